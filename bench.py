@@ -1,0 +1,167 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4 weight-only greedy decode step on one MI355X.
+
+Default workload: the 28-layer Qwen3-VL-2B-shaped text decoder (hidden 2048,
+16/8 heads of 128, SwiGLU 6144, int4 group-128 decoder linears, bf16 lm_head of
+151936 x 2048) at batch 1 with cache_position 700 of a 1024-slot static cache.
+Weights, cache and inputs are seeded synthetic data made on the device.  One
+step = one kmr_decode_step call (embedding, 28 layers, final norm, lm_head,
+argmax); the timed steps repeat the step at the same cache position, rewriting
+the same slot.  `--workload batch4` runs 4 continuous-batching rows (one
+finished) with the token fed back on the device and positions advancing.
+
+Prints one JSON line (see the README of the driver contract in the design doc).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode tok/s + achieved HBM GB/s (% of peak), int4 Qwen3-VL-2B shape, batch 1/4"
+
+
+def algorithmic_bytes(dims, batch, cache_positions, with_lm=True):
+    """Bytes the method must move for one step: int4 codes + (scale, zero) of every
+    decoder linear, norm gains, embedding rows, K/V rows 0..c_b read (the new slot
+    written), bf16 lm_head.  Activations (< 0.1 %) are not counted."""
+    H, D, Hq, Hkv, I, G = dims.hidden, dims.head_dim, dims.n_heads, dims.n_kv_heads, dims.intermediate, dims.group_size
+    lin = [((Hq + 2 * Hkv) * D, H), (H, Hq * D), (2 * I, H), (H, I)]
+    w_layer = sum(n * k // 2 + n * (k // G) * 4 for n, k in lin) + (2 * H + 2 * D) * 2
+    kv_read = sum(2 * Hkv * D * 2 * (int(c) + 1) for c in cache_positions)      # includes the new slot
+    total = dims.n_layers * (w_layer + kv_read)
+    if with_lm:
+        total += dims.vocab * H * 2 + H * 2 + batch * H * 2
+    return total
+
+
+def build(workload_name):
+    import torch
+    from int4_weight_only_gemv_amd import kmr, synth
+    w = synth.WORKLOADS[workload_name]
+    seed = synth.base_seed(w)
+    layers = []
+    for l in range(w.dims.n_layers):
+        layers.append(synth.layer_weights(w.dims, seed, l, where="device", device="cuda"))
+    glob = synth.model_globals(w.dims, seed, where="device", device="cuda")
+    model = kmr.DeviceModel(w.dims, layers, glob)
+    kv = kmr.KVCache(model.cfg, w.batch, w.max_len, zero=False)
+    k, v = synth.kv_cache(w.dims, seed, w.batch, w.max_len, where="device", device="cuda")
+    kv.k.copy_(k)
+    kv.v.copy_(v)
+    del k, v
+    torch.cuda.synchronize()
+    return w, model, kv, layers, glob
+
+
+def cpu_baseline(w, layers, glob, inp, budget_s=20.0):
+    """The oracle as it stands, on this host's cores, over a bounded sample of the
+    same workload: whole decode steps, as many as fit in about budget_s."""
+    import oracle
+    from int4_weight_only_gemv_amd import synth
+    t0 = time.time()
+    host_layers = [{k: oracle.as_u16(v) for k, v in l.items()} for l in layers]
+    ora = oracle.Model(w.dims, host_layers, {k: oracle.as_u16(v) for k, v in glob.items()})
+    del host_layers
+    kh, vh = synth.kv_cache(w.dims, synth.base_seed(w), w.batch, w.max_len, where="device", device="cuda")
+    kh, vh = oracle.as_u16(kh), oracle.as_u16(vh)
+    setup = time.time() - t0
+    times = []
+    while not times or (sum(times) < budget_s and len(times) < 3):
+        t = time.time()
+        ora.decode_step(kh, vh, inp["ids"], inp["positions"].copy(), inp["cache_position"].copy(),
+                        finished=inp["finished"].copy(), want_logits=False)
+        times.append(time.time() - t)
+    sec = float(np.median(times))
+    active = int((inp["finished"] == 0).sum())
+    return {"value": active / sec, "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{len(times)} whole decode step(s) of the same workload (median {sec:.2f} s/step; "
+                      f"oracle setup {setup:.1f} s untimed)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=["step", "batch4"], default="step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this decode step runs on a single MI355X and "
+              "is not sharded across GPUs (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from int4_weight_only_gemv_amd import kmr, synth
+
+    w, model, kv, layers, glob = build(args.workload)
+    inp = synth.step_inputs(w)
+    B = w.batch
+    ws = kmr.Workspace(model.cfg, B, w.max_len)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    ids = [dev(inp["ids"]), torch.zeros(B, dtype=torch.int32, device="cuda")]
+    pos, cpos, fin = dev(inp["positions"]), dev(inp["cache_position"]), dev(inp["finished"])
+    advance = args.workload == "batch4"
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        model.decode_step(kv, ids[i % 2], pos, cpos, ids[(i + 1) % 2], ws, finished=fin,
+                          advance=advance, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if advance:   # restart the timed run from the workload's own state
+        ids[0].copy_(dev(inp["ids"])); pos.copy_(dev(inp["positions"]))
+        cpos.copy_(dev(inp["cache_position"])); fin.copy_(dev(inp["finished"]))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / args.steps
+    status = ws.status()
+    if status:
+        print(f"device status bits set: {status}", file=sys.stderr)
+        sys.exit(3)
+
+    active = int((inp["finished"] == 0).sum())
+    if advance:   # positions advance by one per step for live rows: mean over the run
+        cps = [int(c) + args.steps / 2 for c, f in zip(inp["cache_position"], inp["finished"])]
+    else:
+        cps = [int(c) for c in inp["cache_position"]]
+    nbytes = algorithmic_bytes(w.dims, B, cps)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    tok_s = active * 1000.0 / ms
+    out = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"qwen3vl2b-28L-int4g128-decode-b{B}", "batch": B,
+                   "active_rows": active, "cache_position": [int(c) for c in inp["cache_position"]],
+                   "max_len": w.max_len, "layers": w.dims.n_layers, "vocab": w.dims.vocab},
+        "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": nbytes, "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "whole decode step (kmr_decode_step)"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, layers, glob, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * kmr.h -- C ABI of the int4 weight-only decode step for MI355X (gfx950).
+ *
+ * What the step computes follows the kaminari page ("kaminari - a single-GPU
+ * Qwen3-VL inference engine, explained"):
+ *   - section 04, "3 . decode": one greedy token per call for every batch row,
+ *     from fixed-rank inputs (token ids, 3-axis M-RoPE positions, cache position)
+ *     and the full preallocated KV buffers; the argmax token stays on the device;
+ *     finished rows keep their batch slot and are fed the pad id;
+ *   - section 03 ("State model"): the static KV cache is the one buffer mutated in
+ *     place; section 08 (ContinuousBatchScheduler): each row owns a physical cache
+ *     row, so cache positions are per row here;
+ *   - section 07: only the decoder's attention/MLP linears are int4 weight-only;
+ *     embeddings, lm_head and norms stay bf16; int4 is explicit and never falls
+ *     back silently;
+ *   - attention is softmax(q K^T / sqrt(d)) V ("The Ghost in the Batch", "What
+ *     Attention Does (60 Seconds)"); split partials are merged with the
+ *     log-sum-exp weights stated there ("The merge math").
+ *
+ * Conventions for every entry point:
+ *   - pointers are DEVICE pointers unless marked "host"; all memory is owned by
+ *     the caller; the library never allocates or frees device memory;
+ *   - every argument is checked on the host first; an invalid call returns a
+ *     negative KMR_E* code and launches nothing (kmr_last_error() says why);
+ *   - work is enqueued on the caller's stream, asynchronously; nothing
+ *     synchronises except kmr_status();
+ *   - bf16 values are stored as 16-bit patterns (uint16_t);
+ *   - calls are reentrant given distinct workspaces; calls that share a
+ *     workspace must be ordered on one stream.
+ */
+#ifndef KMR_H
+#define KMR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t (a pointer to the runtime's stream object); NULL is
+ * the null stream.  Declared here so that the header needs no HIP headers. */
+struct ihipStream_t;
+typedef struct ihipStream_t* kmr_stream_t;
+
+enum {
+  KMR_OK = 0,
+  KMR_EINVAL = -1,       /* null pointer, non-positive size, bad index */
+  KMR_ESHAPE = -2,       /* dims the kernels do not support (see kmr_config) */
+  KMR_ENOMEM = -3,       /* caller buffer or workspace smaller than required */
+  KMR_EHIP = -4          /* HIP runtime or launch error */
+};
+
+/* Sticky device-side status bits, read (and cleared) by kmr_status(). */
+enum {
+  KMR_STATUS_CACHE_POS = 1u,  /* a row's cache_position was outside [0, max_len):
+                                 that row wrote nothing and its attention is zero */
+  KMR_STATUS_TOKEN = 2u       /* a token id was outside [0, vocab): that row's
+                                 embedding was taken as zero */
+};
+
+#define KMR_MAX_BATCH 16
+#define KMR_ADVANCE 1u
+
+/*
+ * Model dimensions.  Supported by the kernels: head_dim 64 or 128;
+ * n_heads % n_kv_heads == 0 with n_heads / n_kv_heads <= 8; group_size a multiple
+ * of 32 dividing hidden, n_heads*head_dim and intermediate;
+ * mrope_section[0]+[1]+[2] == head_dim / 2.  Anything else is KMR_ESHAPE.
+ */
+typedef struct {
+  int32_t hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab, n_layers, group_size;
+  float rms_eps;             /* RMSNorm epsilon (1e-6 for the Qwen3 family) */
+  double rope_theta;         /* RoPE base (5e6 for the Qwen3-VL text decoder) */
+  int32_t mrope_section[3];  /* frequency pairs on the t, h, w axes */
+  int32_t mrope_interleaved; /* 1: pair j on h if j%3==1 and j<3*s_h, on w if j%3==2 and
+                                j<3*s_w, else t; 0: contiguous [t | h | w] blocks */
+  int32_t pad_id;            /* token fed to, and emitted by, finished rows */
+  int32_t eos_id;            /* token that finishes a row under KMR_ADVANCE; -1: none */
+} kmr_config;
+
+/* One int4 matrix of N rows by K columns, as written by kmr_quantize_int4:
+ * packed u8 [N][K/2] (byte j of a row holds column 2j in its low nibble and 2j+1
+ * in its high nibble) and sz bf16 [N][K/group][2] (scale, zero). */
+typedef struct {
+  const void* packed;
+  const void* sz;
+  int32_t N, K;
+} kmr_qweight;
+
+/* One decoder layer.  Row order of the fused matrices: qkv = [q heads; k heads;
+ * v heads] (N = (n_heads + 2 n_kv_heads) head_dim, K = hidden); o (N = hidden,
+ * K = n_heads head_dim); gate_up = [gate; up] (N = 2 intermediate, K = hidden);
+ * down (N = hidden, K = intermediate).  Gains are bf16: in_norm/post_norm
+ * [hidden], q_norm/k_norm [head_dim]. */
+typedef struct {
+  const void *in_norm, *q_norm, *k_norm, *post_norm;
+  kmr_qweight qkv, o, gate_up, down;
+} kmr_layer;
+
+/* The whole decoder: bf16 embed [vocab][hidden], final_norm [hidden], untied
+ * lm_head [vocab][hidden]; layers is a HOST array of n_layers entries. */
+typedef struct {
+  const void *embed, *final_norm, *lm_head;
+  const kmr_layer* layers;
+} kmr_model;
+
+/* Static KV cache bound to caller memory: k and v are bf16
+ * [n_layers][batch][n_kv_heads][max_len][head_dim] each. */
+typedef struct {
+  void *k, *v;
+  int32_t n_layers, batch, n_kv_heads, max_len, head_dim;
+  size_t bytes;  /* total bytes of k and v together */
+} kmr_kv;
+
+/*
+ * kmr_kv_alloc -- size or bind a preallocated static KV cache (kaminari section
+ * 03: StaticKVCache, preallocated and slot-addressable).
+ * With buf == NULL only out->bytes is filled (a size query).  Otherwise buf (at
+ * least out->bytes, 256-byte aligned) is split into k and v; zero_fill != 0 clears
+ * it on `stream` with a fill kernel.  Returns KMR_ENOMEM if buf_bytes is short.
+ */
+int kmr_kv_alloc(const kmr_config* cfg, int32_t batch, int32_t max_len, void* buf,
+                 size_t buf_bytes, int32_t zero_fill, kmr_stream_t stream, kmr_kv* out);
+
+/*
+ * kmr_quantize_int4 -- group-wise asymmetric int4 quantization of one bf16
+ * matrix w [N][K] (kaminari section 07: offline weight-only int4 of the decoder
+ * linears; the pages give no formula).  Per row and per group of `group`
+ * consecutive columns, in IEEE fp32 in this order, with no fused multiply-add:
+ *     s = bf16_rne(max((max - min) / 15, 2^-24)),  z = bf16_rne(min + 8 s),
+ *     q = clamp(rne((w - z) / s) + 8, 0, 15),   so that w ~ (q - 8) s + z.
+ * Writes packed [N][K/2] and sz [N][K/group][2] in the kmr_qweight layout.
+ * group must be even and divide K (KMR_ESHAPE otherwise).
+ */
+int kmr_quantize_int4(const void* w_bf16, int32_t N, int32_t K, int32_t group, void* packed,
+                      void* sz, kmr_stream_t stream);
+
+/* Bytes of workspace the decode calls need for this config, batch and max_len. */
+size_t kmr_workspace_bytes(const kmr_config* cfg, int32_t batch, int32_t max_len);
+
+/* Clears a workspace with a fill kernel on `stream`.  Call once after allocating
+ * it and again after any call that returned an error; the decode calls leave
+ * it ready for the next call. */
+int kmr_workspace_init(void* ws, size_t ws_bytes, kmr_stream_t stream);
+
+/*
+ * kmr_decode_layer -- one decoder layer for `batch` rows, in place on
+ * hidden_inout (fp32 [batch][hidden]):
+ *   h = RMSNorm(x; in_norm); [q|k|v] = W_qkv h; per head q, k <- MRoPE(RMSNorm(.; q/k_norm));
+ *   K/V of layer `layer`, row b, slot cache_position[b] <- bf16(k), bf16(v);
+ *   o = attention of each q head over slots 0..cache_position[b] of its kv head
+ *       (q head h reads kv head h / (n_heads / n_kv_heads));
+ *   x += W_o o; x += W_down (silu(gate) * up) with [gate|up] = W_gate_up RMSNorm(x; post_norm).
+ * positions: int32 [3][batch] (t, h, w); cache_position: int32 [batch].
+ * The cache slot cache_position[b] of layer `layer` is the only cache memory
+ * written.  A row whose cache_position is out of range sets KMR_STATUS_CACHE_POS.
+ */
+int kmr_decode_layer(const kmr_config* cfg, const kmr_layer* layer_w, int32_t layer,
+                     const kmr_kv* kv, float* hidden_inout, const int32_t* positions,
+                     const int32_t* cache_position, int32_t batch, void* ws, size_t ws_bytes,
+                     kmr_stream_t stream);
+
+/*
+ * kmr_decode_step -- one greedy decode step of the whole decoder for `batch`
+ * rows (kaminari section 04, "3 . decode"):
+ *   x = embed[id] (id = pad_id for rows with finished[b] != 0), all layers as in
+ *   kmr_decode_layer, RMSNorm(x; final_norm), logits = lm_head x (fp32 accumulate),
+ *   next_ids[b] = lowest index of the largest logit (pad_id for finished rows).
+ * logits: fp32 [batch][vocab] or NULL (written only when given).
+ * finished: uint8 [batch] or NULL (no row finished).
+ * flags & KMR_ADVANCE: on the device, after the argmax, each unfinished row
+ *   whose token is eos_id, or whose cache_position + 1 would reach max_len, is
+ *   marked finished (if `finished` is given); every other unfinished row gets
+ *   cache_position[b] += 1 and all three positions += 1.  This lets the caller
+ *   feed next_ids back as token_ids and replay the step with no host work.
+ * Nothing is synchronised: next_ids is valid once `stream` reaches this point.
+ */
+int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
+                    const int32_t* token_ids, int32_t* positions, int32_t* cache_position,
+                    uint8_t* finished, int32_t batch, int32_t* next_ids, float* logits,
+                    uint32_t flags, void* ws, size_t ws_bytes, kmr_stream_t stream);
+
+/* Synchronises `stream`, returns the sticky KMR_STATUS_* bits of `ws` in
+ * *flags_out (host pointer) and clears them. */
+int kmr_status(void* ws, kmr_stream_t stream, uint32_t* flags_out);
+
+/* Message for a KMR_E* code, and the detail of this thread's last failed call. */
+const char* kmr_strerror(int code);
+const char* kmr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KMR_H */

@@ -1,0 +1,410 @@
+// C ABI of the int4 weight-only decode step (declared in include/kmr.h).
+//
+// Host side: argument checks before any launch, the workspace layout, and the
+// launch sequence of one layer / one step on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kmr.h"
+#include "kmr_kernels.h"
+
+using namespace kmr;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_hip(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KMR_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return KMR_OK;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_config(const kmr_config* c) {
+  if (!c) return fail(KMR_EINVAL, "config is NULL");
+  if (c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->intermediate <= 0 || c->n_layers <= 0 || c->group_size <= 0 || c->vocab < 0)
+    return fail(KMR_EINVAL, "config has a non-positive dimension");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(KMR_ESHAPE, "head_dim %d unsupported (64 or 128)", c->head_dim);
+  if (c->n_heads % c->n_kv_heads != 0)
+    return fail(KMR_ESHAPE, "n_heads %d not a multiple of n_kv_heads %d", c->n_heads, c->n_kv_heads);
+  const int qpg = c->n_heads / c->n_kv_heads;
+  if (qpg != 1 && qpg != 2 && qpg != 4)
+    return fail(KMR_ESHAPE, "n_heads / n_kv_heads = %d unsupported (1, 2 or 4)", qpg);
+  if (c->group_size % 32 != 0)
+    return fail(KMR_ESHAPE, "group_size %d is not a multiple of 32", c->group_size);
+  const int qd = c->n_heads * c->head_dim;
+  if (c->hidden % c->group_size || qd % c->group_size || c->intermediate % c->group_size)
+    return fail(KMR_ESHAPE, "group_size %d must divide hidden, n_heads*head_dim and intermediate",
+                c->group_size);
+  if (c->hidden % 8 != 0) return fail(KMR_ESHAPE, "hidden %d not a multiple of 8", c->hidden);
+  if (c->mrope_section[0] < 0 || c->mrope_section[1] < 0 || c->mrope_section[2] < 0 ||
+      c->mrope_section[0] + c->mrope_section[1] + c->mrope_section[2] != c->head_dim / 2)
+    return fail(KMR_ESHAPE, "mrope_section must be non-negative and sum to head_dim/2");
+  if (!(c->rms_eps >= 0.0f) || !(c->rope_theta > 0.0))
+    return fail(KMR_EINVAL, "rms_eps must be >= 0 and rope_theta > 0");
+  return KMR_OK;
+}
+
+struct WsLayout {
+  size_t status, cnt_attn, cnt_lm, cs, x, qkv, attn_o, act, part_o, part_ml, lm_part, total;
+  int ns, nblk_lm;
+};
+
+WsLayout ws_layout(const kmr_config* c, int B, int M) {
+  WsLayout w{};
+  const int D = c->head_dim, Hq = c->n_heads, Hkv = c->n_kv_heads, qpg = Hq / Hkv;
+  const int nqkv = (Hq + 2 * Hkv) * D;
+  w.ns = (M + kAttnSplit - 1) / kAttnSplit;
+  w.nblk_lm = c->vocab > 0 ? (c->vocab + kLmRowsPerBlock - 1) / kLmRowsPerBlock : 1;
+  size_t o = 0;
+  w.status = o; o += 256;
+  w.cnt_attn = o; o += align256((size_t)B * Hkv * 4);
+  w.cnt_lm = o; o += 256;
+  w.cs = o; o += align256((size_t)B * (D / 2) * 8);
+  w.x = o; o += align256((size_t)B * c->hidden * 4);
+  w.qkv = o; o += align256((size_t)B * nqkv * 4);
+  w.attn_o = o; o += align256((size_t)B * Hq * D * 4);
+  w.act = o; o += align256((size_t)B * c->intermediate * 4);
+  w.part_o = o; o += align256((size_t)B * Hkv * w.ns * qpg * D * 4);
+  w.part_ml = o; o += align256((size_t)B * Hkv * w.ns * qpg * 8);
+  w.lm_part = o; o += align256((size_t)B * w.nblk_lm * 8);
+  w.total = o;
+  return w;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+int check_qweight(const kmr_qweight& q, int N, int K, const char* name) {
+  if (!q.packed || !q.sz) return fail(KMR_EINVAL, "%s: null weight pointer", name);
+  if (q.N != N || q.K != K)
+    return fail(KMR_ESHAPE, "%s: expected %d x %d, got %d x %d", name, N, K, q.N, q.K);
+  return KMR_OK;
+}
+
+int check_layer(const kmr_config* c, const kmr_layer* L) {
+  if (!L) return fail(KMR_EINVAL, "layer is NULL");
+  if (!L->in_norm || !L->q_norm || !L->k_norm || !L->post_norm)
+    return fail(KMR_EINVAL, "layer norm gain is NULL");
+  const int D = c->head_dim, Hq = c->n_heads, Hkv = c->n_kv_heads;
+  int rc;
+  if ((rc = check_qweight(L->qkv, (Hq + 2 * Hkv) * D, c->hidden, "qkv"))) return rc;
+  if ((rc = check_qweight(L->o, c->hidden, Hq * D, "o"))) return rc;
+  if ((rc = check_qweight(L->gate_up, 2 * c->intermediate, c->hidden, "gate_up"))) return rc;
+  if ((rc = check_qweight(L->down, c->hidden, c->intermediate, "down"))) return rc;
+  return KMR_OK;
+}
+
+int check_kv(const kmr_config* c, const kmr_kv* kv, int batch) {
+  if (!kv || !kv->k || !kv->v) return fail(KMR_EINVAL, "kv cache is NULL or unbound");
+  if (kv->n_kv_heads != c->n_kv_heads || kv->head_dim != c->head_dim)
+    return fail(KMR_ESHAPE, "kv cache heads/head_dim do not match the config");
+  if (kv->batch < batch) return fail(KMR_ESHAPE, "kv cache has %d rows, batch is %d", kv->batch, batch);
+  if (kv->max_len <= 0) return fail(KMR_EINVAL, "kv cache max_len must be positive");
+  return KMR_OK;
+}
+
+template <typename F>
+void allow_lds(F* fn, size_t bytes) {
+  if (bytes > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// ---------------------------------------------------------------- GEMV launch
+template <int BT, int EPI>
+void launch_gemv_bt(const GemvArgs& a, hipStream_t st) {
+  const size_t lds = (size_t)BT * (a.K >> 5) * (4 * 16 + 8) + BT * 5 * 4;
+  const int rows_per_block = 4 * kGemvRowsPerWave;
+  dim3 grid((a.N + rows_per_block - 1) / rows_per_block);
+  allow_lds(k_gemv_int4<BT, EPI>, lds);
+  hipLaunchKernelGGL((k_gemv_int4<BT, EPI>), grid, dim3(256), lds, st, a);
+}
+
+template <int EPI>
+void launch_gemv_tile(const GemvArgs& a, hipStream_t st) {
+  switch (a.B) {
+    case 1: launch_gemv_bt<1, EPI>(a, st); break;
+    case 2: launch_gemv_bt<2, EPI>(a, st); break;
+    case 3: case 4: launch_gemv_bt<4, EPI>(a, st); break;
+    case 5: case 6: case 7: case 8: launch_gemv_bt<8, EPI>(a, st); break;
+    default: launch_gemv_bt<16, EPI>(a, st); break;
+  }
+}
+
+// Batch tiles keep the staged input inside the LDS of one CU.
+template <int EPI>
+void launch_gemv(GemvArgs a, hipStream_t st) {
+  const int B = a.B;
+  int tile = 16;
+  while (tile > 1 && (size_t)tile * a.K * 9 / 4 + 1024 > 150 * 1024) tile >>= 1;
+  for (int b0 = 0; b0 < B; b0 += tile) {
+    GemvArgs t = a;
+    t.B = B - b0 < tile ? B - b0 : tile;
+    t.x = a.x + (size_t)b0 * a.ldx;
+    t.y = a.y + (size_t)b0 * a.ldy;
+    launch_gemv_tile<EPI>(t, st);
+  }
+}
+
+int launch_attn(const kmr_config* c, const AttnArgs& a, int B, hipStream_t st) {
+  dim3 grid(a.NS, c->n_kv_heads, B);
+  const int qpg = c->n_heads / c->n_kv_heads;
+#define KMR_ATTN(DD, QQ) hipLaunchKernelGGL((k_attn<DD, QQ>), grid, dim3(256), 0, st, a)
+  if (c->head_dim == 128) {
+    if (qpg == 1) KMR_ATTN(128, 1); else if (qpg == 2) KMR_ATTN(128, 2); else KMR_ATTN(128, 4);
+  } else {
+    if (qpg == 1) KMR_ATTN(64, 1); else if (qpg == 2) KMR_ATTN(64, 2); else KMR_ATTN(64, 4);
+  }
+#undef KMR_ATTN
+  return KMR_OK;
+}
+
+int launch_lmhead(LmArgs a, hipStream_t st) {
+  const size_t lds_of = (size_t)a.K * 4;
+#define KMR_LM(BB)                                                              \
+  do {                                                                          \
+    allow_lds(k_lmhead<BB>, lds_of * BB);                                       \
+    hipLaunchKernelGGL((k_lmhead<BB>), dim3(a.nblk), dim3(256), lds_of * BB, st, a); \
+  } while (0)
+  if (a.B == 1) KMR_LM(1);
+  else if (a.B == 2) KMR_LM(2);
+  else if (a.B <= 4) KMR_LM(4);
+  else if (a.B <= 8) KMR_LM(8);
+  else KMR_LM(16);
+#undef KMR_LM
+  return KMR_OK;
+}
+
+// One decoder layer on x (fp32 [B][H]) using workspace buffers; the RoPE table
+// must already be in ws.cs.
+void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr_kv* kv, float* x,
+                   const int32_t* cpos, int B, void* ws, const WsLayout& w, hipStream_t st) {
+  const int H = c->hidden, D = c->head_dim, Hq = c->n_heads, Hkv = c->n_kv_heads;
+  const int nqkv = (Hq + 2 * Hkv) * D, I = c->intermediate, G = c->group_size;
+  float* qkv = at<float>(ws, w.qkv);
+  float* ao = at<float>(ws, w.attn_o);
+  float* act = at<float>(ws, w.act);
+
+  GemvArgs g{};
+  g.packed = static_cast<const uint8_t*>(L->qkv.packed);
+  g.sz = static_cast<const uint32_t*>(L->qkv.sz);
+  g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->in_norm); g.eps = c->rms_eps;
+  g.y = qkv; g.ldy = nqkv; g.N = nqkv; g.K = H; g.G = G; g.B = B;
+  launch_gemv<EPI_STORE>(g, st);
+
+  AttnArgs a{};
+  const size_t layer_stride = (size_t)kv->batch * Hkv * kv->max_len * D;
+  a.qkv = qkv; a.ldqkv = nqkv;
+  a.q_norm = static_cast<const uint16_t*>(L->q_norm);
+  a.k_norm = static_cast<const uint16_t*>(L->k_norm);
+  a.cs = at<float2>(ws, w.cs);
+  a.kc = static_cast<uint16_t*>(kv->k) + (size_t)layer * layer_stride;
+  a.vc = static_cast<uint16_t*>(kv->v) + (size_t)layer * layer_stride;
+  a.cpos = cpos; a.out = ao;
+  a.part_o = at<float>(ws, w.part_o); a.part_ml = at<float2>(ws, w.part_ml);
+  a.counters = at<uint32_t>(ws, w.cnt_attn); a.status = at<uint32_t>(ws, w.status);
+  a.Hq = Hq; a.Hkv = Hkv; a.M = kv->max_len; a.NS = w.ns; a.eps = c->rms_eps;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  launch_attn(c, a, B, st);
+
+  g = GemvArgs{};
+  g.packed = static_cast<const uint8_t*>(L->o.packed);
+  g.sz = static_cast<const uint32_t*>(L->o.sz);
+  g.x = ao; g.ldx = Hq * D; g.gain = nullptr;
+  g.y = x; g.ldy = H; g.N = H; g.K = Hq * D; g.G = G; g.B = B;
+  launch_gemv<EPI_ADD>(g, st);
+
+  g = GemvArgs{};
+  g.packed = static_cast<const uint8_t*>(L->gate_up.packed);
+  g.sz = static_cast<const uint32_t*>(L->gate_up.sz);
+  g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->post_norm); g.eps = c->rms_eps;
+  g.y = act; g.ldy = I; g.N = I; g.K = H; g.G = G; g.B = B;
+  launch_gemv<EPI_SILU>(g, st);
+
+  g = GemvArgs{};
+  g.packed = static_cast<const uint8_t*>(L->down.packed);
+  g.sz = static_cast<const uint32_t*>(L->down.sz);
+  g.x = act; g.ldx = I; g.gain = nullptr;
+  g.y = x; g.ldy = H; g.N = H; g.K = I; g.G = G; g.B = B;
+  launch_gemv<EPI_ADD>(g, st);
+}
+
+void enqueue_prep(const kmr_config* c, const uint16_t* embed, const int32_t* ids,
+                  const uint8_t* finished, const int32_t* pos, float* x, int B, void* ws,
+                  const WsLayout& w, hipStream_t st) {
+  PrepArgs p{};
+  p.embed = embed; p.ids = ids; p.finished = finished; p.pos = pos; p.x = x;
+  p.cs = at<float2>(ws, w.cs); p.status = at<uint32_t>(ws, w.status);
+  p.B = B; p.H = c->hidden; p.V = c->vocab; p.D = c->head_dim; p.pad_id = c->pad_id;
+  p.theta = c->rope_theta;
+  p.sec0 = c->mrope_section[0]; p.sec1 = c->mrope_section[1]; p.sec2 = c->mrope_section[2];
+  p.interleaved = c->mrope_interleaved;
+  hipLaunchKernelGGL(k_prep, dim3(B), dim3(256), 0, st, p);
+}
+
+void fill_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t words = bytes / 4;
+  if (words) {
+    size_t blocks = (words + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<uint32_t*>(p), words);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kmr_strerror(int code) {
+  switch (code) {
+    case KMR_OK: return "ok";
+    case KMR_EINVAL: return "invalid argument";
+    case KMR_ESHAPE: return "unsupported or mismatched shape";
+    case KMR_ENOMEM: return "buffer or workspace too small";
+    case KMR_EHIP: return "HIP runtime error";
+    default: return "unknown error";
+  }
+}
+
+const char* kmr_last_error(void) { return g_err; }
+
+int kmr_kv_alloc(const kmr_config* cfg, int32_t batch, int32_t max_len, void* buf,
+                 size_t buf_bytes, int32_t zero_fill, kmr_stream_t stream, kmr_kv* out) {
+  int rc;
+  if ((rc = check_config(cfg))) return rc;
+  if (!out) return fail(KMR_EINVAL, "out is NULL");
+  if (batch <= 0 || batch > KMR_MAX_BATCH || max_len <= 0)
+    return fail(KMR_EINVAL, "batch must be in [1, %d] and max_len positive", KMR_MAX_BATCH);
+  const size_t half = (size_t)cfg->n_layers * batch * cfg->n_kv_heads * max_len * cfg->head_dim * 2;
+  const size_t half_al = align256(half);
+  out->bytes = 2 * half_al;
+  out->n_layers = cfg->n_layers; out->batch = batch; out->n_kv_heads = cfg->n_kv_heads;
+  out->max_len = max_len; out->head_dim = cfg->head_dim;
+  out->k = out->v = nullptr;
+  if (!buf) return KMR_OK;
+  if (buf_bytes < out->bytes)
+    return fail(KMR_ENOMEM, "kv buffer has %zu bytes, needs %zu", buf_bytes, out->bytes);
+  if (reinterpret_cast<uintptr_t>(buf) % 256) return fail(KMR_EINVAL, "kv buffer not 256-byte aligned");
+  out->k = buf;
+  out->v = static_cast<char*>(buf) + half_al;
+  if (zero_fill) {
+    fill_zero(buf, out->bytes, reinterpret_cast<hipStream_t>(stream));
+    return check_hip("kv zero fill");
+  }
+  return KMR_OK;
+}
+
+int kmr_quantize_int4(const void* w_bf16, int32_t N, int32_t K, int32_t group, void* packed,
+                      void* sz, kmr_stream_t stream) {
+  if (!w_bf16 || !packed || !sz) return fail(KMR_EINVAL, "null pointer");
+  if (N <= 0 || K <= 0 || group <= 0) return fail(KMR_EINVAL, "N, K and group must be positive");
+  if (group % 2 || K % group) return fail(KMR_ESHAPE, "group %d must be even and divide K %d", group, K);
+  const long long groups = (long long)N * (K / group);
+  const unsigned blocks = (unsigned)((groups + 255) / 256);
+  hipLaunchKernelGGL(k_quantize_int4, dim3(blocks), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint16_t*>(w_bf16),
+                     N, K, group, static_cast<uint8_t*>(packed), static_cast<uint32_t*>(sz));
+  return check_hip("quantize launch");
+}
+
+size_t kmr_workspace_bytes(const kmr_config* cfg, int32_t batch, int32_t max_len) {
+  if (check_config(cfg) || batch <= 0 || batch > KMR_MAX_BATCH || max_len <= 0) return 0;
+  return ws_layout(cfg, batch, max_len).total;
+}
+
+int kmr_workspace_init(void* ws, size_t ws_bytes, kmr_stream_t stream) {
+  if (!ws || !ws_bytes) return fail(KMR_EINVAL, "workspace is NULL or empty");
+  fill_zero(ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  return check_hip("workspace init");
+}
+
+int kmr_decode_layer(const kmr_config* cfg, const kmr_layer* layer_w, int32_t layer,
+                     const kmr_kv* kv, float* hidden_inout, const int32_t* positions,
+                     const int32_t* cache_position, int32_t batch, void* ws, size_t ws_bytes,
+                     kmr_stream_t stream) {
+  int rc;
+  if ((rc = check_config(cfg))) return rc;
+  if ((rc = check_layer(cfg, layer_w))) return rc;
+  if (batch <= 0 || batch > KMR_MAX_BATCH) return fail(KMR_EINVAL, "batch %d out of [1, %d]", batch, KMR_MAX_BATCH);
+  if ((rc = check_kv(cfg, kv, batch))) return rc;
+  if (layer < 0 || layer >= kv->n_layers) return fail(KMR_EINVAL, "layer %d outside the cache", layer);
+  if (!hidden_inout || !positions || !cache_position || !ws)
+    return fail(KMR_EINVAL, "null hidden/positions/cache_position/workspace");
+  const WsLayout w = ws_layout(cfg, batch, kv->max_len);
+  if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  enqueue_prep(cfg, nullptr, nullptr, nullptr, positions, nullptr, batch, ws, w, st);
+  enqueue_layer(cfg, layer_w, layer, kv, hidden_inout, cache_position, batch, ws, w, st);
+  return check_hip("decode_layer launch");
+}
+
+int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
+                    const int32_t* token_ids, int32_t* positions, int32_t* cache_position,
+                    uint8_t* finished, int32_t batch, int32_t* next_ids, float* logits,
+                    uint32_t flags, void* ws, size_t ws_bytes, kmr_stream_t stream) {
+  int rc;
+  if ((rc = check_config(cfg))) return rc;
+  if (cfg->vocab <= 0) return fail(KMR_EINVAL, "vocab must be positive for a full step");
+  if (!model || !model->embed || !model->final_norm || !model->lm_head || !model->layers)
+    return fail(KMR_EINVAL, "model pointers are NULL");
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if ((rc = check_layer(cfg, &model->layers[l]))) return fail(rc, "layer %d: %s", l, g_err);
+  if (batch <= 0 || batch > KMR_MAX_BATCH) return fail(KMR_EINVAL, "batch %d out of [1, %d]", batch, KMR_MAX_BATCH);
+  if ((rc = check_kv(cfg, kv, batch))) return rc;
+  if (kv->n_layers != cfg->n_layers) return fail(KMR_ESHAPE, "kv cache has %d layers, model %d", kv->n_layers, cfg->n_layers);
+  if (!token_ids || !positions || !cache_position || !next_ids || !ws)
+    return fail(KMR_EINVAL, "null token_ids/positions/cache_position/next_ids/workspace");
+  if (flags & ~KMR_ADVANCE) return fail(KMR_EINVAL, "unknown flags 0x%x", flags);
+  const WsLayout w = ws_layout(cfg, batch, kv->max_len);
+  if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* x = at<float>(ws, w.x);
+  enqueue_prep(cfg, static_cast<const uint16_t*>(model->embed), token_ids, finished, positions, x,
+               batch, ws, w, st);
+  for (int l = 0; l < cfg->n_layers; ++l)
+    enqueue_layer(cfg, &model->layers[l], l, kv, x, cache_position, batch, ws, w, st);
+  LmArgs a{};
+  a.x = x; a.gain = static_cast<const uint16_t*>(model->final_norm);
+  a.W = static_cast<const uint16_t*>(model->lm_head);
+  a.logits = logits; a.part = at<float2>(ws, w.lm_part); a.counter = at<uint32_t>(ws, w.cnt_lm);
+  a.finished_in = finished; a.finished = finished; a.next = next_ids;
+  a.cpos = cache_position; a.pos = positions;
+  a.V = cfg->vocab; a.K = cfg->hidden; a.B = batch; a.nblk = w.nblk_lm; a.M = kv->max_len;
+  a.pad_id = cfg->pad_id; a.eos_id = cfg->eos_id; a.flags = flags; a.eps = cfg->rms_eps;
+  launch_lmhead(a, st);
+  return check_hip("decode_step launch");
+}
+
+int kmr_status(void* ws, kmr_stream_t stream, uint32_t* flags_out) {
+  if (!ws || !flags_out) return fail(KMR_EINVAL, "null workspace or flags_out");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, ws, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return check_hip("status read") ? KMR_EHIP : fail(KMR_EHIP, "status read failed");
+  fill_zero(ws, 4, st);
+  *flags_out = v;
+  return check_hip("status clear");
+}
+
+}  // extern "C"

@@ -1,0 +1,702 @@
+// HIP kernels of the int4 weight-only decode step (gfx950, wave64).
+//
+// Decode step as on the kaminari page ("kaminari - a single-GPU Qwen3-VL
+// inference engine, explained", section 04 "3 . decode"; model structure in
+// section 03; int4 weight-only decoder linears in section 07); attention and its
+// split merge as in "The Ghost in the Batch" ("What Attention Does", "The merge
+// math").
+#pragma once
+#include "kmr_device.h"
+
+namespace kmr {
+
+constexpr int kAttnSplit = 64;   // cache positions per attention work-group (fixed, so
+                                 // a row's result never depends on the batch size)
+constexpr int kGemvRowsPerWave = 2;
+constexpr int kLmRowsPerWave = 4;
+constexpr int kLmRowsPerBlock = 4 * kLmRowsPerWave;
+
+struct Status {
+  uint32_t bits;
+};
+
+__device__ __forceinline__ void raise_status(uint32_t* st, uint32_t bit) {
+  __hip_atomic_fetch_or(st, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ fill
+
+__global__ void k_fill_zero(uint32_t* __restrict__ p, size_t words) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < words; i += stride) p[i] = 0u;
+}
+
+// ------------------------------------------------------------------ int4 quantizer
+// Per (row, group): s = bf16(max((hi-lo)/15, 2^-24)), z = bf16(lo + 8 s),
+// q = clamp(rne((w - z)/s) + 8, 0, 15); IEEE fp32, each operation rounded on its
+// own (no contraction), divisions correctly rounded.  One thread per group: this
+// runs once per model and is not on the decode path.
+__global__ void k_quantize_int4(const uint16_t* __restrict__ w, int N, int K, int G,
+                                uint8_t* __restrict__ packed, uint32_t* __restrict__ sz) {
+#pragma clang fp contract(off)
+  const int ng = K / G;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)N * ng) return;
+  const int n = (int)(idx / ng), g = (int)(idx % ng);
+  const uint16_t* src = w + (size_t)n * K + (size_t)g * G;
+  float lo = bf16_to_f32(src[0]), hi = lo;
+  for (int i = 1; i < G; ++i) {
+    float v = bf16_to_f32(src[i]);
+    lo = v < lo ? v : lo;
+    hi = v > hi ? v : hi;
+  }
+  float range = hi - lo;
+  float s32 = range / 15.0f;
+  if (!(s32 >= 0x1p-24f)) s32 = 0x1p-24f;
+  const uint16_t sb = f32_to_bf16(s32);
+  const float s = bf16_to_f32(sb);
+  const float eight_s = 8.0f * s;
+  const float z32 = lo + eight_s;
+  const uint16_t zb = f32_to_bf16(z32);
+  const float z = bf16_to_f32(zb);
+  sz[idx] = (uint32_t)sb | ((uint32_t)zb << 16);
+  uint8_t* dst = packed + (size_t)n * (K / 2) + (size_t)g * (G / 2);
+  for (int i = 0; i < G; i += 2) {
+    int q2[2];
+    for (int t = 0; t < 2; ++t) {
+      float diff = bf16_to_f32(src[i + t]) - z;
+      float r = __builtin_rintf(diff / s);
+      int q = (int)r + 8;
+      q2[t] = q < 0 ? 0 : (q > 15 ? 15 : q);
+    }
+    dst[i / 2] = (uint8_t)(q2[0] | (q2[1] << 4));
+  }
+}
+
+// ------------------------------------------------------------------ step prologue
+// Embedding gather (bf16 row -> fp32 residual stream; finished rows read pad_id)
+// and the RoPE cos/sin of each row's three-axis position, in fp64 then rounded
+// to fp32: pair j uses axis(j) and angle pos[axis] * theta^(-2j/D).
+struct PrepArgs {
+  const uint16_t* embed;   // [V][H] or null (layer-only call)
+  const int32_t* ids;      // [B]
+  const uint8_t* finished; // [B] or null
+  const int32_t* pos;      // [3][B]
+  float* x;                // [B][H]
+  float2* cs;              // [B][D/2]
+  uint32_t* status;
+  int B, H, V, D, pad_id;
+  double theta;
+  int sec0, sec1, sec2, interleaved;
+};
+
+__device__ __forceinline__ int mrope_axis(int j, int s0, int s1, int s2, int interleaved) {
+  if (interleaved) {
+    if (j % 3 == 1 && j < 3 * s1) return 1;
+    if (j % 3 == 2 && j < 3 * s2) return 2;
+    return 0;
+  }
+  (void)s2;
+  return j < s0 ? 0 : (j < s0 + s1 ? 1 : 2);
+}
+
+__global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (a.embed) {
+    int id = (a.finished && a.finished[b]) ? a.pad_id : a.ids[b];
+    const bool ok = id >= 0 && id < a.V;
+    if (!ok && tid == 0) raise_status(a.status, 2u);
+    const uint16_t* row = a.embed + (size_t)(ok ? id : 0) * a.H;
+    for (int k = tid; k < a.H; k += blockDim.x) a.x[(size_t)b * a.H + k] = ok ? bf16_to_f32(row[k]) : 0.0f;
+  }
+  const int half = a.D / 2;
+  for (int j = tid; j < half; j += blockDim.x) {
+    const int ax = mrope_axis(j, a.sec0, a.sec1, a.sec2, a.interleaved);
+    const double p = (double)a.pos[ax * a.B + b];
+    const double inv_freq = pow(a.theta, -2.0 * (double)j / (double)a.D);
+    double sn, cn;
+    sincos(p * inv_freq, &sn, &cn);
+    a.cs[(size_t)b * half + j] = make_float2((float)cn, (float)sn);
+  }
+}
+
+// ------------------------------------------------------------------ int4 GEMV
+// y[b][n] = sum_k w_hat[n][k] x[b][k] with w_hat = (q - 8) s + z per (row, group),
+// for batch rows b < B (compile-time tile BT >= B).  Optional RMSNorm prologue
+// (x <- x / sqrt(mean x^2 + eps) * gain) and three epilogues.
+//
+// Dequantization stays in registers: a 32-bit word of 8 codes becomes four fp16
+// pairs with one shift and four and-or operations, using the exponent of 1024
+// as a magic bias (0x6400 | q is 1024 + q; codes in bits 4..7 of a half read as
+// 1024 + 16 q).  The input vector is staged in LDS as matching fp16 pairs (odd
+// columns pre-divided by 16), so v_dot2_f32_f16 accumulates sum q x plus a known
+// bias in fp32; per 32-column chunk the bias and sum x are precomputed, which
+// folds scale and zero into two multiply-adds per chunk:
+//     sum_k (q_k - 8 + z/s) s x_k = s (dot - C1) + z C2.
+enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SILU = 2 };
+
+struct GemvArgs {
+  const uint8_t* packed;  // [rows][K/2]
+  const uint32_t* sz;     // [rows][K/G] (scale | zero << 16)
+  const float* x;         // [B][ldx]
+  const uint16_t* gain;   // [K] or null
+  float* y;               // [B][ldy]
+  int N;                  // outputs per batch row (EPI_SILU: weight rows are 2N)
+  int K, G, B, ldx, ldy;
+  float eps;
+};
+
+template <int BT, int EPI>
+__global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int K = a.K, CH = K >> 5, NG = K / a.G, B = a.B;
+  uint4* xs = reinterpret_cast<uint4*>(smem);                    // [BT][4][CH]
+  float2* cc = reinterpret_cast<float2*>(xs + BT * 4 * CH);      // [BT][CH]
+  float* red = reinterpret_cast<float*>(cc + BT * CH);           // [BT][4]
+  float* sinv = red + BT * 4;                                    // [BT]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  if (a.gain) {
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      float ss = 0.f;
+      if (b < B)
+        for (int k = tid * 4; k < K; k += 1024) {
+          float4 v = *reinterpret_cast<const float4*>(a.x + (size_t)b * a.ldx + k);
+          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+      ss = wave_sum(ss);
+      if (lane == 0) red[b * 4 + wave] = ss;
+    }
+    __syncthreads();
+    if (tid < BT) {
+      float ss = (red[tid * 4 + 0] + red[tid * 4 + 1]) + (red[tid * 4 + 2] + red[tid * 4 + 3]);
+      sinv[tid] = 1.0f / sqrtf(ss / (float)K + a.eps);
+    }
+    __syncthreads();
+  }
+
+  for (int idx = tid; idx < BT * CH; idx += 256) {
+    const int b = idx / CH, c = idx - b * CH;
+    float e[32];
+    if (b < B) {
+      const float4* src = reinterpret_cast<const float4*>(a.x + (size_t)b * a.ldx + 32 * c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float4 v = src[i];
+        e[4 * i] = v.x; e[4 * i + 1] = v.y; e[4 * i + 2] = v.z; e[4 * i + 3] = v.w;
+      }
+      if (a.gain) {
+        const float iv = sinv[b];
+        const uint32_t* gw = reinterpret_cast<const uint32_t*>(a.gain + 32 * c);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          uint32_t gg = gw[i];
+          e[2 * i] = (e[2 * i] * iv) * bf16_lo(gg);
+          e[2 * i + 1] = (e[2 * i + 1] * iv) * bf16_hi(gg);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) e[i] = 0.f;
+    }
+    float bsum = 0.f, usum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* f = e + 8 * j;
+      _Float16 h0 = (_Float16)f[0], h4 = (_Float16)f[4], h2 = (_Float16)f[2], h6 = (_Float16)f[6];
+      _Float16 h1 = (_Float16)(f[1] * 0.0625f), h5 = (_Float16)(f[5] * 0.0625f);
+      _Float16 h3 = (_Float16)(f[3] * 0.0625f), h7 = (_Float16)(f[7] * 0.0625f);
+      uint4 pk;
+      pk.x = __builtin_bit_cast(uint32_t, half2_t{h0, h4});
+      pk.y = __builtin_bit_cast(uint32_t, half2_t{h1, h5});
+      pk.z = __builtin_bit_cast(uint32_t, half2_t{h2, h6});
+      pk.w = __builtin_bit_cast(uint32_t, half2_t{h3, h7});
+      xs[(b * 4 + j) * CH + c] = pk;
+      const float ev = ((float)h0 + (float)h4) + ((float)h2 + (float)h6);
+      const float od = ((float)h1 + (float)h5) + ((float)h3 + (float)h7);
+      bsum += ev + od;
+      usum += ev + 16.0f * od;
+    }
+    cc[b * CH + c] = make_float2(1024.0f * bsum + 8.0f * usum, usum);
+  }
+  __syncthreads();
+
+  constexpr int RPW = kGemvRowsPerWave;
+  constexpr int NR = (EPI == EPI_SILU ? 2 : 1) * RPW;
+  const int n0 = (blockIdx.x * 4 + wave) * RPW;
+  int wrow[NR];
+  bool ok[NR];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int n = n0 + r;
+    ok[r] = n < a.N;
+    wrow[r] = ok[r] ? n : 0;
+    if (EPI == EPI_SILU) {
+      ok[RPW + r] = ok[r];
+      wrow[RPW + r] = ok[r] ? n + a.N : 0;
+    }
+  }
+  float acc[NR][BT];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int b = 0; b < BT; ++b) acc[i][b] = 0.f;
+
+  for (int c = lane; c < CH; c += 64) {
+    uint4 w[NR];
+    uint32_t sw[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      if (ok[i]) {
+        w[i] = *reinterpret_cast<const uint4*>(a.packed + (size_t)wrow[i] * (K / 2) + 16 * c);
+        sw[i] = a.sz[(size_t)wrow[i] * NG + (32 * c) / a.G];
+      } else {
+        w[i] = make_uint4(0, 0, 0, 0);
+        sw[i] = 0;
+      }
+    }
+    uint32_t p[NR][16];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t t = ww[j] >> 8;
+        p[i][4 * j + 0] = (ww[j] & 0x000F000Fu) | 0x64006400u;
+        p[i][4 * j + 1] = (ww[j] & 0x00F000F0u) | 0x64006400u;
+        p[i][4 * j + 2] = (t & 0x000F000Fu) | 0x64006400u;
+        p[i][4 * j + 3] = (t & 0x00F000F0u) | 0x64006400u;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      uint4 xv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv[j] = xs[(b * 4 + j) * CH + c];
+      const float2 C = cc[b * CH + c];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        float d = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          d = fdot2(p[i][4 * j + 0], xv[j].x, d);
+          d = fdot2(p[i][4 * j + 1], xv[j].y, d);
+          d = fdot2(p[i][4 * j + 2], xv[j].z, d);
+          d = fdot2(p[i][4 * j + 3], xv[j].w, d);
+        }
+        acc[i][b] += bf16_lo(sw[i]) * (d - C.x) + bf16_hi(sw[i]) * C.y;
+      }
+    }
+  }
+
+  float v[NR][BT];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int b = 0; b < BT; ++b) v[i][b] = wave_sum(acc[i][b]);
+
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      if (!ok[r]) continue;
+      const int n = n0 + r;
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        if (b >= B) break;
+        float* dst = a.y + (size_t)b * a.ldy + n;
+        if (EPI == EPI_STORE) {
+          *dst = v[r][b];
+        } else if (EPI == EPI_ADD) {
+          *dst += v[r][b];
+        } else {
+          const float g = v[r][b], u = v[RPW + r][b];
+          *dst = g / (1.0f + expf(-g)) * u;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ attention
+// One work-group per (split of kAttnSplit positions, kv head g, batch row b).
+// Prologue (fused): per-head RMSNorm of q and k over head_dim, M-RoPE on both,
+// bf16 rounding of the new k and v (their storage precision); the group owning
+// slot cache_position writes them to the cache and attends to them directly.
+// Main loop: each 16-lane row of a wave takes one position per step (head_dim/16
+// dims per lane, so four rows read four consecutive cache rows, coalesced),
+// keeping an online softmax per q head of the GQA group.  Partials (m, l, o) of
+// the 16 rows are merged in LDS; the groups of one (b, g) merge through global
+// partials with log-sum-exp weights, done by the last group to finish, in fixed
+// split order.
+struct AttnArgs {
+  const float* qkv;        // [B][ldqkv]
+  const uint16_t* q_norm;  // [D]
+  const uint16_t* k_norm;  // [D]
+  const float2* cs;        // [B][D/2]
+  uint16_t* kc;            // layer slice [cacheB][Hkv][M][D]
+  uint16_t* vc;
+  const int32_t* cpos;     // [B]
+  float* out;              // [B][Hq*D]
+  float* part_o;           // [B][Hkv][NS][QPG][D]
+  float2* part_ml;         // [B][Hkv][NS][QPG]
+  uint32_t* counters;      // [B][Hkv]
+  uint32_t* status;
+  int ldqkv, Hq, Hkv, M, NS;
+  float eps, scale_log2;   // log2(e) / sqrt(D)
+};
+
+template <int D, int QPG>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+  constexpr int DPL = D / 16;   // dims per lane
+  constexpr int HALF = D / 2;
+  __shared__ float s_o[16][QPG][D];
+  __shared__ float s_m[16][QPG];
+  __shared__ float s_l[16][QPG];
+  __shared__ int s_last;
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rr = lane >> 4, li = lane & 15;
+  const int row = wave * 4 + rr;    // 0..15
+  const int d0 = li * DPL;
+  const int c = a.cpos[b];
+  const size_t head_base = ((size_t)b * a.Hkv + g) * a.M;   // in rows of D
+
+  if (c < 0 || c >= a.M) {
+    if (s == 0) {
+      if (tid == 0 && g == 0) raise_status(a.status, 1u);
+      for (int i = tid; i < QPG * D; i += 256) a.out[(size_t)b * a.Hq * D + (size_t)g * QPG * D + i] = 0.f;
+    }
+    return;
+  }
+  if (s * kAttnSplit > c) return;
+  const int ns = c / kAttnSplit + 1;
+
+  // ---- prologue: q', k', v of the current token for this lane's dims
+  const float* qrow = a.qkv + (size_t)b * a.ldqkv;
+  float q[QPG][DPL], kf[DPL], vf[DPL];
+#pragma unroll
+  for (int h = 0; h < QPG; ++h)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) q[h][e] = qrow[(g * QPG + h) * D + d0 + e];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    kf[e] = qrow[(a.Hq + g) * D + d0 + e];
+    vf[e] = qrow[(a.Hq + a.Hkv + g) * D + d0 + e];
+  }
+  float cs_c[DPL], cs_s[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    const float2 t = a.cs[(size_t)b * HALF + ((d0 + e) % HALF)];
+    cs_c[e] = t.x;
+    cs_s[e] = (d0 < HALF) ? -t.y : t.y;   // lower half: x c - x' s; upper: x c + x' s
+  }
+  auto norm_rope = [&](float* vals, const uint16_t* gain) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) ss += vals[e] * vals[e];
+    ss = row16_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) vals[e] = (vals[e] * inv) * bf16_to_f32(gain[d0 + e]);
+    float other[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) other[e] = row16_swap8(vals[e]);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) vals[e] = vals[e] * cs_c[e] + other[e] * cs_s[e];
+  };
+#pragma unroll
+  for (int h = 0; h < QPG; ++h) norm_rope(q[h], a.q_norm);
+  norm_rope(kf, a.k_norm);
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    kf[e] = round_bf16(kf[e]);
+    vf[e] = round_bf16(vf[e]);
+  }
+  if (s == ns - 1 && row == 0) {
+    uint16_t* kd = a.kc + (head_base + c) * D + d0;
+    uint16_t* vd = a.vc + (head_base + c) * D + d0;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      kd[e] = f32_to_bf16(kf[e]);
+      vd[e] = f32_to_bf16(vf[e]);
+    }
+  }
+
+  // ---- main loop over this split's positions
+  float m[QPG], l[QPG], o[QPG][DPL];
+#pragma unroll
+  for (int h = 0; h < QPG; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
+  }
+  constexpr int PER_WAVE = kAttnSplit / 4;
+#pragma unroll
+  for (int it = 0; it < PER_WAVE / 4; ++it) {
+    const int p = s * kAttnSplit + wave * PER_WAVE + it * 4 + rr;
+    const bool valid = p <= c;
+    float kk[DPL], vv[DPL];
+    if (valid && p != c) {
+      const uint16_t* ks = a.kc + (head_base + p) * D + d0;
+      const uint16_t* vs = a.vc + (head_base + p) * D + d0;
+#pragma unroll
+      for (int e = 0; e < DPL; e += 2) {
+        const uint32_t kw = *reinterpret_cast<const uint32_t*>(ks + e);
+        const uint32_t vw = *reinterpret_cast<const uint32_t*>(vs + e);
+        kk[e] = bf16_lo(kw); kk[e + 1] = bf16_hi(kw);
+        vv[e] = bf16_lo(vw); vv[e + 1] = bf16_hi(vw);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        kk[e] = valid ? kf[e] : 0.f;
+        vv[e] = valid ? vf[e] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < QPG; ++h) {
+      float sc = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sc += q[h][e] * kk[e];
+      sc = row16_sum(sc) * a.scale_log2;
+      if (valid) {
+        const float mn = fmaxf(m[h], sc);
+        const float corr = exp2f(m[h] - mn);
+        const float pe = exp2f(sc - mn);
+        l[h] = l[h] * corr + pe;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[h][e] = o[h][e] * corr + pe * vv[e];
+        m[h] = mn;
+      }
+    }
+  }
+
+  // ---- merge the 16 row states of this group
+#pragma unroll
+  for (int h = 0; h < QPG; ++h) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) s_o[row][h][d0 + e] = o[h][e];
+    if (li == 0) {
+      s_m[row][h] = m[h];
+      s_l[row][h] = l[h];
+    }
+  }
+  __syncthreads();
+  const size_t pidx = ((size_t)b * a.Hkv + g) * a.NS + s;   // partial slot
+  for (int i = tid; i < QPG * D; i += 256) {
+    const int h = i / D, d = i - h * D;
+    float M = -INFINITY;
+    for (int r = 0; r < 16; ++r) M = fmaxf(M, s_m[r][h]);
+    float L = 0.f, O = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      const float wgt = exp2f(s_m[r][h] - M);   // rows that saw nothing have m = -inf
+      L += wgt * s_l[r][h];
+      O += wgt * s_o[r][h][d];
+    }
+    if (ns == 1) {
+      a.out[(size_t)b * a.Hq * D + (size_t)(g * QPG + h) * D + d] = O / L;
+    } else {
+      a.part_o[(pidx * QPG + h) * D + d] = O;
+      if (d == 0) a.part_ml[pidx * QPG + h] = make_float2(M, L);
+    }
+  }
+  if (ns == 1) return;
+
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = atomicAdd(&a.counters[b * a.Hkv + g], 1u);
+    s_last = (prev == (uint32_t)(ns - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const size_t base = ((size_t)b * a.Hkv + g) * a.NS;
+  for (int i = tid; i < QPG * D; i += 256) {
+    const int h = i / D, d = i - h * D;
+    float M = -INFINITY;
+    for (int t = 0; t < ns; ++t) M = fmaxf(M, a.part_ml[(base + t) * QPG + h].x);
+    float L = 0.f, O = 0.f;
+    for (int t = 0; t < ns; ++t) {
+      const float2 ml = a.part_ml[(base + t) * QPG + h];
+      const float wgt = exp2f(ml.x - M);
+      L += wgt * ml.y;
+      O += wgt * a.part_o[((base + t) * QPG + h) * D + d];
+    }
+    a.out[(size_t)b * a.Hq * D + (size_t)(g * QPG + h) * D + d] = O / L;
+  }
+  if (tid == 0) a.counters[b * a.Hkv + g] = 0u;
+}
+
+// ------------------------------------------------------------------ lm_head + argmax
+// logits[b][n] = sum_k W[n][k] h[b][k] with h = RMSNorm(x; final_norm), bf16 W
+// widened to fp32 in registers, fp32 accumulation.  Each group keeps the best
+// (value, lowest index) per batch row; the last group to finish reduces the
+// partials, writes next_ids, and applies the finished/advance rules.
+struct LmArgs {
+  const float* x;            // [B][K]
+  const uint16_t* gain;      // [K]
+  const uint16_t* W;         // [V][K]
+  float* logits;             // [B][V] or null
+  float2* part;              // [B][nblk] (value, index as float bits)
+  uint32_t* counter;
+  const uint8_t* finished_in;
+  uint8_t* finished;         // may be null
+  int32_t* next;
+  int32_t* cpos;
+  int32_t* pos;              // [3][B]
+  int V, K, B, nblk, M, pad_id, eos_id;
+  uint32_t flags;
+  float eps;
+};
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+template <int BT>
+__global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* hs = reinterpret_cast<float*>(smem);       // [BT][K]
+  __shared__ float red[BT * 4];
+  __shared__ float s_bv[4][BT];
+  __shared__ int s_bi[4][BT];
+  __shared__ int s_last;
+  const int K = a.K, B = a.B;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+    float ss = 0.f;
+    if (b < B)
+      for (int k = tid * 4; k < K; k += 1024) {
+        float4 v = *reinterpret_cast<const float4*>(a.x + (size_t)b * K + k);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+    ss = wave_sum(ss);
+    if (lane == 0) red[b * 4 + wave] = ss;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+    const float ss = (red[b * 4 + 0] + red[b * 4 + 1]) + (red[b * 4 + 2] + red[b * 4 + 3]);
+    const float inv = 1.0f / sqrtf(ss / (float)K + a.eps);
+    for (int k = tid; k < K; k += 256)
+      hs[b * K + k] = b < B ? (a.x[(size_t)b * K + k] * inv) * bf16_to_f32(a.gain[k]) : 0.f;
+  }
+  __syncthreads();
+
+  constexpr int RPW = kLmRowsPerWave;
+  const int n0 = blockIdx.x * kLmRowsPerBlock + wave * RPW;
+  const int CH = K >> 3;   // 8-column chunks
+  float acc[RPW][BT];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
+  for (int c = lane; c < CH; c += 64) {
+    uint4 w[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int n = n0 + r;
+      w[r] = n < a.V ? *reinterpret_cast<const uint4*>(a.W + (size_t)n * K + 8 * c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      const float4 h0 = *reinterpret_cast<const float4*>(hs + b * K + 8 * c);
+      const float4 h1 = *reinterpret_cast<const float4*>(hs + b * K + 8 * c + 4);
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        float t = acc[r][b];
+        t += bf16_lo(w[r].x) * h0.x; t += bf16_hi(w[r].x) * h0.y;
+        t += bf16_lo(w[r].y) * h0.z; t += bf16_hi(w[r].y) * h0.w;
+        t += bf16_lo(w[r].z) * h1.x; t += bf16_hi(w[r].z) * h1.y;
+        t += bf16_lo(w[r].w) * h1.z; t += bf16_hi(w[r].w) * h1.w;
+        acc[r][b] = t;
+      }
+    }
+  }
+  float bv[BT];
+  int bi[BT];
+#pragma unroll
+  for (int b = 0; b < BT; ++b) { bv[b] = -INFINITY; bi[b] = 0x7fffffff; }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int n = n0 + r;
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      const float v = wave_sum(acc[r][b]);
+      if (n < a.V && b < B) {
+        if (a.logits && lane == 0) a.logits[(size_t)b * a.V + n] = v;
+        if (better(v, n, bv[b], bi[b])) { bv[b] = v; bi[b] = n; }
+      }
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int b = 0; b < BT; ++b) { s_bv[wave][b] = bv[b]; s_bi[wave][b] = bi[b]; }
+  }
+  __syncthreads();
+  if (tid < B) {
+    float v = s_bv[0][tid];
+    int i = s_bi[0][tid];
+    for (int w = 1; w < 4; ++w)
+      if (better(s_bv[w][tid], s_bi[w][tid], v, i)) { v = s_bv[w][tid]; i = s_bi[w][tid]; }
+    a.part[(size_t)tid * a.nblk + blockIdx.x] = make_float2(v, __int_as_float(i));
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = atomicAdd(a.counter, 1u);
+    s_last = (prev == (uint32_t)(gridDim.x - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int b = 0; b < B; ++b) {
+    float v = -INFINITY;
+    int i = 0x7fffffff;
+    for (int t = tid; t < a.nblk; t += 256) {
+      const float2 pv = a.part[(size_t)b * a.nblk + t];
+      if (better(pv.x, __float_as_int(pv.y), v, i)) { v = pv.x; i = __float_as_int(pv.y); }
+    }
+    // block argmax: exchange through LDS in a fixed tree order
+    __shared__ float t_v[256];
+    __shared__ int t_i[256];
+    t_v[tid] = v;
+    t_i[tid] = i;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (tid < w && better(t_v[tid + w], t_i[tid + w], t_v[tid], t_i[tid])) {
+        t_v[tid] = t_v[tid + w];
+        t_i[tid] = t_i[tid + w];
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      const int best = t_i[0];
+      const int fin = a.finished_in ? a.finished_in[b] : 0;
+      a.next[b] = fin ? a.pad_id : best;
+      if ((a.flags & 1u) && !fin) {
+        if (a.eos_id >= 0 && best == a.eos_id) {
+          if (a.finished) a.finished[b] = 1;
+        } else if (a.cpos[b] + 1 >= a.M) {
+          if (a.finished) a.finished[b] = 1;
+        } else {
+          a.cpos[b] += 1;
+          a.pos[0 * B + b] += 1;
+          a.pos[1 * B + b] += 1;
+          a.pos[2 * B + b] += 1;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) *a.counter = 0u;
+}
+
+}  // namespace kmr

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (set by the arithmetic: bf16 storage, fp16 GEMV inputs, fp32 accumulation
+against an fp64 oracle): packed int4 codes and scale/zero bit-exact; cache bytes
+outside the written slots bit-identical; next-token ids equal wherever the
+oracle's top-2 logit margin exceeds 1e-2; hidden states, logits and written K/V
+within max relative error 2e-2 (largest absolute error over the largest
+reference magnitude, per row).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from int4_weight_only_gemv_amd import synth
+from tests.gpu_util import (MARGIN, TOL, bf16_host, build_pair, log, make_caches, max_rel,
+                            to_device_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kmr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from int4_weight_only_gemv_amd import kmr as k
+    return k
+
+
+# ------------------------------------------------------------------ quantizer
+
+def _crafted_groups(G):
+    ties = [0.0, 15 / 64] + [(j + 0.5) / 64 for j in range(15)]
+    ties += [0.0] * (G - len(ties))
+    scale_tie = list(np.linspace(-15 / 256, 15, G))
+    scale_tie[0], scale_tie[-1] = -15 / 256, 15.0
+    return np.array([ties, scale_tie, [0.37109375] * G, [0.0] * G, [-2.5] * G], np.float32)
+
+
+@pytest.mark.parametrize("N,K,G,std", [
+    (512, 256, 64, 0.02), (256, 768, 64, 0.02), (37, 384, 128, 1.0),
+    (4096, 2048, 128, 0.02), (2048, 6144, 128, 0.02), (64, 512, 128, 300.0), (5, 2, 2, 1.0),
+])
+def test_quantize_bit_exact(kmr, N, K, G, std):
+    log(f"quantize N={N} K={K} G={G} std={std}")
+    r = np.random.default_rng(N * 7 + K)
+    w = (r.standard_normal((N, K)).astype(np.float32) * np.float32(std))
+    if K % G == 0 and G >= 32 and N >= 5:
+        c = _crafted_groups(G)
+        w[:5, :G] = c
+    wb = torch.from_numpy(w).to(torch.bfloat16)
+    p_ref, s_ref = oracle.quantize_int4(oracle.as_u16(wb), G)
+    p, s = kmr.quantize_int4(wb.cuda(), G)
+    torch.cuda.synchronize()
+    assert np.array_equal(p.cpu().numpy(), p_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), s_ref)
+
+
+# ------------------------------------------------------------------ one layer
+
+def _layer_case(kmr, dims, seed, batch, M, cpos, pos, x0):
+    pair = build_pair(dims, seed, "host", with_globals=False)
+    kv, kh, vh = make_caches(dims, seed, batch, M, "host")
+    k0, v0 = kh.copy(), vh.copy()
+    cfg = kmr.make_config(dims)
+    ws = kmr.Workspace(cfg, batch, M)
+    x_dev = torch.from_numpy(x0.astype(np.float32)).cuda()
+    pos_d = torch.from_numpy(pos).cuda()
+    cpos_d = torch.from_numpy(cpos).cuda()
+    pair.dev.decode_layer(0, kv, x_dev, pos_d, cpos_d, ws)
+    torch.cuda.synchronize()
+    assert ws.status() == 0
+    x_ref = x0.astype(np.float32).astype(np.float64).copy()
+    pair.ora.decode_layer(0, kh, vh, x_ref, pos, cpos)
+    x_got = x_dev.cpu().numpy()
+    err = max_rel(x_got, x_ref)
+    kg = oracle.as_u16(kv.k)
+    vg = oracle.as_u16(kv.v)
+    mask = np.zeros(kg.shape, bool)
+    for b in range(batch):
+        mask[:, b, :, cpos[b], :] = True
+    kerr = max_rel(bf16_host(kg[mask]).reshape(-1, dims.head_dim), bf16_host(kh[mask]).reshape(-1, dims.head_dim))
+    verr = max_rel(bf16_host(vg[mask]).reshape(-1, dims.head_dim), bf16_host(vh[mask]).reshape(-1, dims.head_dim))
+    log(f"  hidden max_rel={err:.3e}  k={kerr:.3e}  v={verr:.3e}")
+    assert err <= TOL and kerr <= TOL and verr <= TOL
+    assert np.array_equal(kg[~mask], k0[~mask]) and np.array_equal(vg[~mask], v0[~mask])
+    return err
+
+
+@pytest.mark.parametrize("cpos", [0, 1, 16, 63, 64, 65, 127])
+def test_decode_layer_tiny(kmr, cpos):
+    w = synth.WORKLOADS["tiny"]
+    log(f"decode_layer tiny cache_position={cpos}")
+    pos = np.array([[cpos], [3], [60]], np.int32)
+    x0 = synth.hidden_input(w.dims, 5, 1).numpy()
+    _layer_case(kmr, w.dims, synth.base_seed(w), 1, w.max_len, np.array([cpos], np.int32), pos, x0)
+
+
+def test_decode_layer_tiny_ragged_batch(kmr):
+    w = synth.WORKLOADS["tiny"]
+    log("decode_layer tiny batch 3 ragged")
+    cpos = np.array([0, 77, 127], np.int32)
+    pos = np.array([[0, 77, 127], [5, 1, 2], [9, 9, 9]], np.int32)
+    x0 = synth.hidden_input(w.dims, 6, 3).numpy()
+    _layer_case(kmr, w.dims, synth.base_seed(w), 3, w.max_len, cpos, pos, x0)
+
+
+def test_decode_layer_full_size(kmr):
+    w = synth.WORKLOADS["layer"]
+    inp = synth.step_inputs(w)
+    log(f"decode_layer full size cache_position={inp['cache_position']}")
+    x0 = synth.hidden_input(w.dims, synth.base_seed(w), 1).numpy()
+    _layer_case(kmr, w.dims, synth.base_seed(w), 1, w.max_len, inp["cache_position"],
+                inp["positions"], x0)
+
+
+def test_decode_layer_full_size_edges(kmr):
+    w = synth.WORKLOADS["layer"]
+    log("decode_layer full size, batch 4 at split edges")
+    cpos = np.array([0, 63, 64, 1023], np.int32)
+    pos = np.array([[0, 63, 64, 1023], [0, 1, 2, 3], [7, 7, 7, 7]], np.int32)
+    x0 = synth.hidden_input(w.dims, 9, 4).numpy()
+    _layer_case(kmr, w.dims, synth.base_seed(w), 4, w.max_len, cpos, pos, x0)
+
+
+# ------------------------------------------------------------------ whole step
+
+def _check_step(got_next, got_logits, ref, label):
+    lerr = max_rel(got_logits, ref["logits"])
+    agree = got_next == ref["next"]
+    decisive = ref["margin"] > MARGIN
+    log(f"  {label}: logits max_rel={lerr:.3e} tokens={got_next.tolist()} ref={ref['next'].tolist()} "
+        f"margins={np.round(ref['margin'], 4).tolist()}")
+    assert lerr <= TOL
+    assert np.all(agree | ~decisive)
+
+
+def _step_case(kmr, pair, kv, kh, vh, inp, M, steps=1, advance=False):
+    dims = pair.dims
+    B = len(inp["ids"])
+    cfg = pair.dev.cfg
+    ws = kmr.Workspace(cfg, B, M)
+    ids = inp["ids"].copy()
+    pos, cpos, fin = inp["positions"].copy(), inp["cache_position"].copy(), inp["finished"].copy()
+    pos_d, cpos_d = torch.from_numpy(pos).cuda(), torch.from_numpy(cpos).cuda()
+    fin_d = torch.from_numpy(fin).cuda()
+    nxt_d = torch.zeros(B, dtype=torch.int32, device="cuda")
+    logits_d = torch.empty((B, dims.vocab), dtype=torch.float32, device="cuda")
+    for step in range(steps):
+        ids_d = torch.from_numpy(ids).cuda()
+        pair.dev.decode_step(kv, ids_d, pos_d, cpos_d, nxt_d, ws, finished=fin_d, logits=logits_d,
+                             advance=advance)
+        torch.cuda.synchronize()
+        ref = pair.ora.decode_step(kh, vh, ids, pos, cpos, finished=fin, advance=advance)
+        _check_step(nxt_d.cpu().numpy(), logits_d.cpu().numpy(), ref, f"step {step}")
+        assert np.array_equal(pos_d.cpu().numpy(), pos)
+        assert np.array_equal(cpos_d.cpu().numpy(), cpos)
+        assert np.array_equal(fin_d.cpu().numpy(), fin)
+        ids = ref["next"].astype(np.int32)        # lockstep: both sides take the oracle's token
+    assert ws.status() == 0
+    return ref
+
+
+def test_decode_step_tiny(kmr):
+    w = synth.WORKLOADS["tiny"]
+    log("decode_step tiny")
+    pair = build_pair(w.dims, synth.base_seed(w), "host", with_globals=True)
+    kv, kh, vh = make_caches(w.dims, synth.base_seed(w), 1, w.max_len, "host")
+    _step_case(kmr, pair, kv, kh, vh, synth.step_inputs(w), w.max_len)
+
+
+def test_decode_step_tiny_batch_advance(kmr):
+    w = synth.WORKLOADS["tiny"]
+    log("decode_step tiny batch 3, finished row, advance to the last slot")
+    pair = build_pair(w.dims, synth.base_seed(w), "host", with_globals=True)
+    kv, kh, vh = make_caches(w.dims, synth.base_seed(w), 3, w.max_len, "host")
+    inp = {"ids": np.array([5, 6, 7], np.int32),
+           "positions": np.array([[10, 125, 3], [11, 1, 3], [12, 2, 3]], np.int32),
+           "cache_position": np.array([10, 125, 3], np.int32),
+           "finished": np.array([0, 0, 1], np.uint8)}
+    _step_case(kmr, pair, kv, kh, vh, inp, w.max_len, steps=4, advance=True)
+
+
+@pytest.fixture(scope="module")
+def full_pair(kmr):
+    w = synth.WORKLOADS["step"]
+    log("building the 28-layer model (device draws, oracle quantizes its host copy)")
+    return build_pair(w.dims, synth.base_seed(w), "device", with_globals=True)
+
+
+def test_decode_step_full(kmr, full_pair):
+    w = synth.WORKLOADS["step"]
+    log("decode_step 28 layers, batch 1, cache_position 700")
+    kv, kh, vh = make_caches(w.dims, synth.base_seed(w), 1, w.max_len, "device")
+    _step_case(kmr, full_pair, kv, kh, vh, synth.step_inputs(w), w.max_len)
+
+
+def test_decode_step_batch4_lockstep(kmr, full_pair):
+    w = synth.WORKLOADS["batch4"]
+    log("decode_step 28 layers, batch 4 (row 3 finished), 6 lockstep steps with advance")
+    kv, kh, vh = make_caches(w.dims, synth.base_seed(w), w.batch, w.max_len, "device")
+    _step_case(kmr, full_pair, kv, kh, vh, synth.step_inputs(w), w.max_len, steps=6, advance=True)
+
+
+def test_decode_step_long16_sampled_rows(kmr, full_pair):
+    w = synth.WORKLOADS["long16"]
+    rows = [0, 11]
+    log(f"decode_step 28 layers, batch 16, max_len 8192; oracle on rows {rows}")
+    inp = synth.step_inputs(w)
+    kv, kh, vh = make_caches(w.dims, synth.base_seed(w), w.batch, w.max_len, "device", host_rows=rows)
+    B = w.batch
+    ws = kmr.Workspace(full_pair.dev.cfg, B, w.max_len)
+    pos_d = torch.from_numpy(inp["positions"]).cuda()
+    cpos_d = torch.from_numpy(inp["cache_position"]).cuda()
+    nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, w.dims.vocab), dtype=torch.float32, device="cuda")
+    full_pair.dev.decode_step(kv, torch.from_numpy(inp["ids"]).cuda(), pos_d, cpos_d, nxt, ws,
+                              logits=logits)
+    torch.cuda.synchronize()
+    ref = full_pair.ora.decode_step(kh, vh, inp["ids"][rows], np.ascontiguousarray(inp["positions"][:, rows]),
+                                    inp["cache_position"][rows].copy())
+    _check_step(nxt.cpu().numpy()[rows], logits.cpu().numpy()[rows], ref, "rows")
+    assert ws.status() == 0
+
+
+# ------------------------------------------------------------------ error paths
+
+def test_out_of_range_cache_position_sets_status_and_writes_nothing(kmr):
+    w = synth.WORKLOADS["tiny"]
+    log("decode_layer with cache_position == max_len")
+    pair = build_pair(w.dims, synth.base_seed(w), "host", with_globals=False)
+    kv, kh, vh = make_caches(w.dims, synth.base_seed(w), 2, w.max_len, "host")
+    ws = kmr.Workspace(pair.dev.cfg, 2, w.max_len)
+    x = torch.ones((2, w.dims.hidden), dtype=torch.float32, device="cuda")
+    pos = torch.zeros((3, 2), dtype=torch.int32, device="cuda")
+    cpos = torch.tensor([w.max_len, 5], dtype=torch.int32, device="cuda")
+    pair.dev.decode_layer(0, kv, x, pos, cpos, ws)
+    assert ws.status() == kmr.KMR_STATUS_CACHE_POS
+    kg = oracle.as_u16(kv.k)
+    assert np.array_equal(kg[:, 0], kh[:, 0])
+    assert ws.status() == 0             # cleared by the read
+
+
+def test_bad_token_sets_status(kmr):
+    w = synth.WORKLOADS["tiny"]
+    log("decode_step with a token id outside the vocabulary")
+    pair = build_pair(w.dims, synth.base_seed(w), "host", with_globals=True)
+    kv, _, _ = make_caches(w.dims, synth.base_seed(w), 1, w.max_len, "host")
+    ws = kmr.Workspace(pair.dev.cfg, 1, w.max_len)
+    nxt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pair.dev.decode_step(kv, torch.tensor([w.dims.vocab], dtype=torch.int32, device="cuda"),
+                         torch.zeros((3, 1), dtype=torch.int32, device="cuda"),
+                         torch.tensor([3], dtype=torch.int32, device="cuda"), nxt, ws)
+    assert ws.status() == kmr.KMR_STATUS_TOKEN
