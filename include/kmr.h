@@ -55,12 +55,17 @@ enum {
 enum {
   KMR_STATUS_CACHE_POS = 1u,  /* a row's cache_position was outside [0, max_len):
                                  that row wrote nothing and its attention is zero */
-  KMR_STATUS_TOKEN = 2u       /* a token id was outside [0, vocab): that row's
+  KMR_STATUS_TOKEN = 2u,      /* a token id was outside [0, vocab): that row's
                                  embedding was taken as zero */
+  KMR_STATUS_TIMEOUT = 4u     /* a wait inside the persistent step kernel gave up
+                                 (no progress for ~1 s): outputs of that call are
+                                 invalid; re-initialise the workspace */
 };
 
 #define KMR_MAX_BATCH 16
 #define KMR_ADVANCE 1u
+#define KMR_MULTI_KERNEL 2u  /* run the step as one kernel per phase instead of the
+                                single persistent kernel (diagnostics, cross-checks) */
 
 /*
  * Model dimensions.  Supported by the kernels: head_dim 64 or 128;

@@ -4,6 +4,7 @@
 // launch sequence of one layer / one step on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -11,6 +12,7 @@
 
 #include "kmr.h"
 #include "kmr_kernels.h"
+#include "kmr_step.h"
 
 using namespace kmr;
 
@@ -52,7 +54,8 @@ int check_config(const kmr_config* c) {
   if (c->hidden % c->group_size || qd % c->group_size || c->intermediate % c->group_size)
     return fail(KMR_ESHAPE, "group_size %d must divide hidden, n_heads*head_dim and intermediate",
                 c->group_size);
-  if (c->hidden % 8 != 0) return fail(KMR_ESHAPE, "hidden %d not a multiple of 8", c->hidden);
+  if (c->hidden > 4096 || qd > 8192 || c->intermediate > 8192)
+    return fail(KMR_ESHAPE, "hidden <= 4096, n_heads*head_dim <= 8192 and intermediate <= 8192 required");
   if (c->mrope_section[0] < 0 || c->mrope_section[1] < 0 || c->mrope_section[2] < 0 ||
       c->mrope_section[0] + c->mrope_section[1] + c->mrope_section[2] != c->head_dim / 2)
     return fail(KMR_ESHAPE, "mrope_section must be non-negative and sum to head_dim/2");
@@ -61,8 +64,11 @@ int check_config(const kmr_config* c) {
   return KMR_OK;
 }
 
+constexpr int kMaxStepGroups = 1024;   // lm_head partial slots of the persistent kernel
+
 struct WsLayout {
-  size_t status, cnt_attn, cnt_lm, cs, x, qkv, attn_o, act, part_o, part_ml, lm_part, total;
+  size_t status, cs, x, qkv, attn_o, act, part_o, part_ml, lm_part, total;
+  size_t step_ctr, lm_cnt, tx, tqkv, to, tact, tpart, lm_part2;
   int ns, nblk_lm;
 };
 
@@ -74,8 +80,6 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
   w.nblk_lm = c->vocab > 0 ? (c->vocab + kLmRowsPerBlock - 1) / kLmRowsPerBlock : 1;
   size_t o = 0;
   w.status = o; o += 256;
-  w.cnt_attn = o; o += align256((size_t)B * Hkv * 4);
-  w.cnt_lm = o; o += 256;
   w.cs = o; o += align256((size_t)B * (D / 2) * 8);
   w.x = o; o += align256((size_t)B * c->hidden * 4);
   w.qkv = o; o += align256((size_t)B * nqkv * 4);
@@ -84,6 +88,14 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
   w.part_o = o; o += align256((size_t)B * Hkv * w.ns * qpg * D * 4);
   w.part_ml = o; o += align256((size_t)B * Hkv * w.ns * qpg * 8);
   w.lm_part = o; o += align256((size_t)B * w.nblk_lm * 8);
+  w.step_ctr = o; o += 256;
+  w.lm_cnt = o; o += 256;
+  w.tx = o; o += align256((size_t)B * c->hidden * 8);
+  w.tqkv = o; o += align256((size_t)B * nqkv * 8);
+  w.to = o; o += align256((size_t)B * Hq * D * 8);
+  w.tact = o; o += align256((size_t)B * c->intermediate * 8);
+  w.tpart = o; o += align256((size_t)B * Hkv * w.ns * qpg * (D + 2) * 8);
+  w.lm_part2 = o; o += align256((size_t)B * kMaxStepGroups * 8);
   w.total = o;
   return w;
 }
@@ -130,42 +142,54 @@ void allow_lds(F* fn, size_t bytes) {
 }
 
 // ---------------------------------------------------------------- GEMV launch
-template <int BT, int EPI>
-void launch_gemv_bt(const GemvArgs& a, hipStream_t st) {
-  const size_t lds = (size_t)BT * (a.K >> 5) * (4 * 16 + 8) + BT * 5 * 4;
+template <int BT, int EPI, int PRO, int CPL>
+void launch_gemv_k(const GemvArgs& a, hipStream_t st) {
+  const size_t lds = gemv_lds(BT, a.K, PRO == PRO_ATTN).total;
   const int rows_per_block = 4 * kGemvRowsPerWave;
   dim3 grid((a.N + rows_per_block - 1) / rows_per_block);
-  allow_lds(k_gemv_int4<BT, EPI>, lds);
-  hipLaunchKernelGGL((k_gemv_int4<BT, EPI>), grid, dim3(256), lds, st, a);
+  allow_lds(k_gemv_int4<BT, EPI, PRO, CPL>, lds);
+  hipLaunchKernelGGL((k_gemv_int4<BT, EPI, PRO, CPL>), grid, dim3(256), lds, st, a);
 }
 
-template <int EPI>
+template <int BT, int EPI, int PRO>
+void launch_gemv_cpl(const GemvArgs& a, hipStream_t st) {
+  switch ((a.K + 2047) / 2048) {
+    case 1: launch_gemv_k<BT, EPI, PRO, 1>(a, st); break;
+    case 2: launch_gemv_k<BT, EPI, PRO, 2>(a, st); break;
+    case 3: launch_gemv_k<BT, EPI, PRO, 3>(a, st); break;
+    default: launch_gemv_k<BT, EPI, PRO, 4>(a, st); break;
+  }
+}
+
+template <int EPI, int PRO>
 void launch_gemv_tile(const GemvArgs& a, hipStream_t st) {
   switch (a.B) {
-    case 1: launch_gemv_bt<1, EPI>(a, st); break;
-    case 2: launch_gemv_bt<2, EPI>(a, st); break;
-    case 3: case 4: launch_gemv_bt<4, EPI>(a, st); break;
-    case 5: case 6: case 7: case 8: launch_gemv_bt<8, EPI>(a, st); break;
-    default: launch_gemv_bt<16, EPI>(a, st); break;
+    case 1: launch_gemv_cpl<1, EPI, PRO>(a, st); break;
+    case 2: launch_gemv_cpl<2, EPI, PRO>(a, st); break;
+    case 3: case 4: launch_gemv_cpl<4, EPI, PRO>(a, st); break;
+    case 5: case 6: case 7: case 8: launch_gemv_cpl<8, EPI, PRO>(a, st); break;
+    default: launch_gemv_cpl<16, EPI, PRO>(a, st); break;
   }
 }
 
 // Batch tiles keep the staged input inside the LDS of one CU.
-template <int EPI>
+template <int EPI, int PRO>
 void launch_gemv(GemvArgs a, hipStream_t st) {
   const int B = a.B;
   int tile = 16;
-  while (tile > 1 && (size_t)tile * a.K * 9 / 4 + 1024 > 150 * 1024) tile >>= 1;
+  const size_t per_row = (size_t)a.K * 9 / 4 + (PRO == PRO_ATTN ? (size_t)a.K * 4 : 0);
+  while (tile > 1 && tile * per_row + 1024 > 150 * 1024) tile >>= 1;
   for (int b0 = 0; b0 < B; b0 += tile) {
     GemvArgs t = a;
     t.B = B - b0 < tile ? B - b0 : tile;
-    t.x = a.x + (size_t)b0 * a.ldx;
+    t.b0 = b0;
+    if (t.x) t.x = a.x + (size_t)b0 * a.ldx;
     t.y = a.y + (size_t)b0 * a.ldy;
-    launch_gemv_tile<EPI>(t, st);
+    launch_gemv_tile<EPI, PRO>(t, st);
   }
 }
 
-int launch_attn(const kmr_config* c, const AttnArgs& a, int B, hipStream_t st) {
+void launch_attn(const kmr_config* c, const AttnArgs& a, int B, hipStream_t st) {
   dim3 grid(a.NS, c->n_kv_heads, B);
   const int qpg = c->n_heads / c->n_kv_heads;
 #define KMR_ATTN(DD, QQ) hipLaunchKernelGGL((k_attn<DD, QQ>), grid, dim3(256), 0, st, a)
@@ -175,24 +199,37 @@ int launch_attn(const kmr_config* c, const AttnArgs& a, int B, hipStream_t st) {
     if (qpg == 1) KMR_ATTN(64, 1); else if (qpg == 2) KMR_ATTN(64, 2); else KMR_ATTN(64, 4);
   }
 #undef KMR_ATTN
-  return KMR_OK;
 }
 
-int launch_lmhead(LmArgs a, hipStream_t st) {
-  const size_t lds_of = (size_t)a.K * 4;
-#define KMR_LM(BB)                                                              \
-  do {                                                                          \
-    allow_lds(k_lmhead<BB>, lds_of * BB);                                       \
-    hipLaunchKernelGGL((k_lmhead<BB>), dim3(a.nblk), dim3(256), lds_of * BB, st, a); \
-  } while (0)
-  if (a.B == 1) KMR_LM(1);
-  else if (a.B == 2) KMR_LM(2);
-  else if (a.B <= 4) KMR_LM(4);
-  else if (a.B <= 8) KMR_LM(8);
-  else KMR_LM(16);
-#undef KMR_LM
-  return KMR_OK;
+template <int BT, int CPL>
+void launch_lm_k(const LmArgs& a, hipStream_t st) {
+  const size_t lds = (size_t)a.K * 4 * BT;
+  allow_lds(k_lmhead<BT, CPL>, lds);
+  hipLaunchKernelGGL((k_lmhead<BT, CPL>), dim3(a.nblk), dim3(256), lds, st, a);
 }
+
+template <int BT>
+void launch_lm_cpl(const LmArgs& a, hipStream_t st) {
+  const int cpl = (a.K + 511) / 512;
+  if (cpl <= 1) launch_lm_k<BT, 1>(a, st);
+  else if (cpl <= 2) launch_lm_k<BT, 2>(a, st);
+  else if (cpl <= 4) launch_lm_k<BT, 4>(a, st);
+  else launch_lm_k<BT, 8>(a, st);
+}
+
+void launch_lmhead(const LmArgs& a, hipStream_t st) {
+  if (a.B == 1) launch_lm_cpl<1>(a, st);
+  else if (a.B == 2) launch_lm_cpl<2>(a, st);
+  else if (a.B <= 4) launch_lm_cpl<4>(a, st);
+  else if (a.B <= 8) launch_lm_cpl<8>(a, st);
+  else launch_lm_cpl<16>(a, st);
+}
+
+// The O projection merges the attention splits in its own prologue when every
+// one of its groups can afford to read all partials (few rows, few splits);
+// otherwise a separate merge kernel writes o first.  Both use merge_head, so the
+// result is the same bits either way; the choice depends on batch * max_len.
+bool fuse_attn_merge(int B, int ns) { return (size_t)B * ns <= 16; }
 
 // One decoder layer on x (fp32 [B][H]) using workspace buffers; the RoPE table
 // must already be in ws.cs.
@@ -209,7 +246,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   g.sz = static_cast<const uint32_t*>(L->qkv.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->in_norm); g.eps = c->rms_eps;
   g.y = qkv; g.ldy = nqkv; g.N = nqkv; g.K = H; g.G = G; g.B = B;
-  launch_gemv<EPI_STORE>(g, st);
+  launch_gemv<EPI_STORE, PRO_RMSNORM>(g, st);
 
   AttnArgs a{};
   const size_t layer_stride = (size_t)kv->batch * Hkv * kv->max_len * D;
@@ -219,33 +256,84 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   a.cs = at<float2>(ws, w.cs);
   a.kc = static_cast<uint16_t*>(kv->k) + (size_t)layer * layer_stride;
   a.vc = static_cast<uint16_t*>(kv->v) + (size_t)layer * layer_stride;
-  a.cpos = cpos; a.out = ao;
+  a.cpos = cpos;
   a.part_o = at<float>(ws, w.part_o); a.part_ml = at<float2>(ws, w.part_ml);
-  a.counters = at<uint32_t>(ws, w.cnt_attn); a.status = at<uint32_t>(ws, w.status);
+  a.status = at<uint32_t>(ws, w.status);
   a.Hq = Hq; a.Hkv = Hkv; a.M = kv->max_len; a.NS = w.ns; a.eps = c->rms_eps;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   launch_attn(c, a, B, st);
 
+  AttnPart ap{};
+  ap.part_o = a.part_o; ap.part_ml = a.part_ml; ap.cpos = cpos;
+  ap.Hkv = Hkv; ap.NS = w.ns; ap.QPG = Hq / Hkv; ap.D = D; ap.M = kv->max_len;
+
   g = GemvArgs{};
   g.packed = static_cast<const uint8_t*>(L->o.packed);
   g.sz = static_cast<const uint32_t*>(L->o.sz);
-  g.x = ao; g.ldx = Hq * D; g.gain = nullptr;
   g.y = x; g.ldy = H; g.N = H; g.K = Hq * D; g.G = G; g.B = B;
-  launch_gemv<EPI_ADD>(g, st);
+  if (fuse_attn_merge(B, w.ns)) {
+    g.ap = ap;
+    launch_gemv<EPI_ADD, PRO_ATTN>(g, st);
+  } else {
+    const int threads = B * Hq * (D / 4);
+    hipLaunchKernelGGL(k_attn_combine, dim3((threads + 255) / 256), dim3(256), 0, st, ap, ao, B, Hq);
+    g.x = ao; g.ldx = Hq * D;
+    launch_gemv<EPI_ADD, PRO_PLAIN>(g, st);
+  }
 
   g = GemvArgs{};
   g.packed = static_cast<const uint8_t*>(L->gate_up.packed);
   g.sz = static_cast<const uint32_t*>(L->gate_up.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->post_norm); g.eps = c->rms_eps;
   g.y = act; g.ldy = I; g.N = I; g.K = H; g.G = G; g.B = B;
-  launch_gemv<EPI_SILU>(g, st);
+  launch_gemv<EPI_SILU, PRO_RMSNORM>(g, st);
 
   g = GemvArgs{};
   g.packed = static_cast<const uint8_t*>(L->down.packed);
   g.sz = static_cast<const uint32_t*>(L->down.sz);
   g.x = act; g.ldx = I; g.gain = nullptr;
   g.y = x; g.ldy = H; g.N = H; g.K = I; g.G = G; g.B = B;
-  launch_gemv<EPI_ADD>(g, st);
+  launch_gemv<EPI_ADD, PRO_PLAIN>(g, st);
+}
+
+// ---------------------------------------------------------------- persistent step
+// Shapes the persistent kernel is built for (one 2048-column chunk per lane for
+// hidden and n_heads*head_dim, three for intermediate, GQA groups of 2).
+bool step_kernel_fits(const kmr_config* c, int B) {
+  return B <= 4 && c->hidden <= 2048 && c->n_heads * c->head_dim <= 2048 &&
+         c->intermediate <= 6144 && c->n_layers <= kMaxStepLayers &&
+         c->n_heads == 2 * c->n_kv_heads && c->vocab > 0;
+}
+
+int device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return check_hip("hipGetDevice");
+  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return check_hip("CU count");
+  if (*cus > kMaxStepGroups) *cus = kMaxStepGroups;
+  return KMR_OK;
+}
+
+template <int BT, int D>
+int launch_step_k(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
+  const int KMAX = std::max(c->hidden, std::max(c->intermediate, c->n_heads * c->head_dim));
+  const int RPBX = (c->hidden + nwg - 1) / nwg;
+  const size_t lds = step_lds(BT, KMAX, RPBX, D, 2).total;
+  auto fn = k_step<BT, D, 2>;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds) != hipSuccess)
+    return check_hip("step kernel LDS attribute");
+  void* args[] = {&a};
+  if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(nwg), dim3(kStepThreads),
+                                 args, (unsigned)lds, st) != hipSuccess)
+    return check_hip("step kernel cooperative launch");
+  return KMR_OK;
+}
+
+int launch_step(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
+  const int B = a.B;
+  if (c->head_dim == 128) return B == 1 ? launch_step_k<1, 128>(c, a, nwg, st) : launch_step_k<4, 128>(c, a, nwg, st);
+  return B == 1 ? launch_step_k<1, 64>(c, a, nwg, st) : launch_step_k<4, 64>(c, a, nwg, st);
 }
 
 void enqueue_prep(const kmr_config* c, const uint16_t* embed, const int32_t* ids,
@@ -287,6 +375,16 @@ const char* kmr_strerror(int code) {
 }
 
 const char* kmr_last_error(void) { return g_err; }
+
+#ifdef KMR_TRACE
+// Diagnostic builds only: route the step kernel's phase timestamps to `buf`
+// (uint64 [groups][64]); NULL turns tracing off.
+int kmr_debug_set_trace(void* buf) {
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_kmr_trace), &buf, sizeof(buf)) != hipSuccess)
+    return check_hip("trace symbol");
+  return KMR_OK;
+}
+#endif
 
 int kmr_kv_alloc(const kmr_config* cfg, int32_t batch, int32_t max_len, void* buf,
                  size_t buf_bytes, int32_t zero_fill, kmr_stream_t stream, kmr_kv* out) {
@@ -374,24 +472,65 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
   if (kv->n_layers != cfg->n_layers) return fail(KMR_ESHAPE, "kv cache has %d layers, model %d", kv->n_layers, cfg->n_layers);
   if (!token_ids || !positions || !cache_position || !next_ids || !ws)
     return fail(KMR_EINVAL, "null token_ids/positions/cache_position/next_ids/workspace");
-  if (flags & ~KMR_ADVANCE) return fail(KMR_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(KMR_ADVANCE | KMR_MULTI_KERNEL)) return fail(KMR_EINVAL, "unknown flags 0x%x", flags);
   const WsLayout w = ws_layout(cfg, batch, kv->max_len);
   if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!(flags & KMR_MULTI_KERNEL) && step_kernel_fits(cfg, batch)) {
+    int nwg = 0;
+    if ((rc = device_cus(&nwg))) return rc;
+    StepArgs a{};
+    a.embed = static_cast<const uint16_t*>(model->embed);
+    a.final_norm = static_cast<const uint16_t*>(model->final_norm);
+    a.lm_head = static_cast<const uint16_t*>(model->lm_head);
+    a.ids = token_ids; a.pos = positions; a.cpos = cache_position; a.finished = finished;
+    a.next = next_ids; a.logits = logits;
+    a.kc = static_cast<uint16_t*>(kv->k); a.vc = static_cast<uint16_t*>(kv->v);
+    a.status = at<uint32_t>(ws, w.status); a.step_ctr = at<uint32_t>(ws, w.step_ctr);
+    a.lm_cnt = at<uint32_t>(ws, w.lm_cnt);
+    a.tx = at<uint64_t>(ws, w.tx); a.tqkv = at<uint64_t>(ws, w.tqkv);
+    a.to = at<uint64_t>(ws, w.to); a.tact = at<uint64_t>(ws, w.tact);
+    a.tpart = at<uint64_t>(ws, w.tpart);
+    a.lm_part = at<float2>(ws, w.lm_part2);
+    a.B = batch; a.H = cfg->hidden; a.Hq = cfg->n_heads; a.Hkv = cfg->n_kv_heads;
+    a.I = cfg->intermediate; a.V = cfg->vocab; a.L = cfg->n_layers; a.G = cfg->group_size;
+    a.M = kv->max_len; a.cacheB = kv->batch; a.NS = w.ns; a.pad_id = cfg->pad_id;
+    a.eos_id = cfg->eos_id; a.flags = flags & KMR_ADVANCE; a.eps = cfg->rms_eps;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg->head_dim));
+    a.theta = cfg->rope_theta;
+    a.sec0 = cfg->mrope_section[0]; a.sec1 = cfg->mrope_section[1]; a.sec2 = cfg->mrope_section[2];
+    a.interleaved = cfg->mrope_interleaved;
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      const kmr_layer& L = model->layers[l];
+      StepLayer& d = a.layers[l];
+      d.in_norm = static_cast<const uint16_t*>(L.in_norm);
+      d.q_norm = static_cast<const uint16_t*>(L.q_norm);
+      d.k_norm = static_cast<const uint16_t*>(L.k_norm);
+      d.post_norm = static_cast<const uint16_t*>(L.post_norm);
+      d.qkv_p = static_cast<const uint8_t*>(L.qkv.packed); d.qkv_s = static_cast<const uint32_t*>(L.qkv.sz);
+      d.o_p = static_cast<const uint8_t*>(L.o.packed); d.o_s = static_cast<const uint32_t*>(L.o.sz);
+      d.gu_p = static_cast<const uint8_t*>(L.gate_up.packed); d.gu_s = static_cast<const uint32_t*>(L.gate_up.sz);
+      d.d_p = static_cast<const uint8_t*>(L.down.packed); d.d_s = static_cast<const uint32_t*>(L.down.sz);
+    }
+    return launch_step(cfg, a, nwg, st);
+  }
   float* x = at<float>(ws, w.x);
   enqueue_prep(cfg, static_cast<const uint16_t*>(model->embed), token_ids, finished, positions, x,
                batch, ws, w, st);
   for (int l = 0; l < cfg->n_layers; ++l)
     enqueue_layer(cfg, &model->layers[l], l, kv, x, cache_position, batch, ws, w, st);
-  LmArgs a{};
-  a.x = x; a.gain = static_cast<const uint16_t*>(model->final_norm);
-  a.W = static_cast<const uint16_t*>(model->lm_head);
-  a.logits = logits; a.part = at<float2>(ws, w.lm_part); a.counter = at<uint32_t>(ws, w.cnt_lm);
-  a.finished_in = finished; a.finished = finished; a.next = next_ids;
-  a.cpos = cache_position; a.pos = positions;
-  a.V = cfg->vocab; a.K = cfg->hidden; a.B = batch; a.nblk = w.nblk_lm; a.M = kv->max_len;
-  a.pad_id = cfg->pad_id; a.eos_id = cfg->eos_id; a.flags = flags; a.eps = cfg->rms_eps;
-  launch_lmhead(a, st);
+  LmArgs la{};
+  la.x = x; la.gain = static_cast<const uint16_t*>(model->final_norm);
+  la.W = static_cast<const uint16_t*>(model->lm_head);
+  la.logits = logits; la.part = at<float2>(ws, w.lm_part);
+  la.V = cfg->vocab; la.K = cfg->hidden; la.B = batch; la.nblk = w.nblk_lm; la.eps = cfg->rms_eps;
+  launch_lmhead(la, st);
+  LmFinishArgs f{};
+  f.part = la.part; f.finished_in = finished; f.finished = finished; f.next = next_ids;
+  f.cpos = cache_position; f.pos = positions;
+  f.B = batch; f.nblk = w.nblk_lm; f.M = kv->max_len; f.pad_id = cfg->pad_id;
+  f.eos_id = cfg->eos_id; f.flags = flags & KMR_ADVANCE;
+  hipLaunchKernelGGL(k_lm_finish, dim3(batch), dim3(256), 0, st, f);
   return check_hip("decode_step launch");
 }
 

@@ -59,6 +59,14 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal: the data is used once).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
                                 false);

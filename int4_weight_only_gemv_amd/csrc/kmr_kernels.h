@@ -16,10 +16,6 @@ constexpr int kGemvRowsPerWave = 2;
 constexpr int kLmRowsPerWave = 4;
 constexpr int kLmRowsPerBlock = 4 * kLmRowsPerWave;
 
-struct Status {
-  uint32_t bits;
-};
-
 __device__ __forceinline__ void raise_status(uint32_t* st, uint32_t bit) {
   __hip_atomic_fetch_or(st, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -121,43 +117,189 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ attention partials
+// A split of kAttnSplit cache positions leaves, per q head, the running max m
+// (log2 domain), the sum l of 2^(s - m) and the unnormalised o~ = sum 2^(s - m) v.
+// Splits merge with log-sum-exp weights, in split order:
+//     o = sum_s 2^(m_s - M) o~_s / sum_s 2^(m_s - M) l_s,   M = max_s m_s.
+// The same device function serves the fused O-projection prologue and the
+// stand-alone combine kernel, so both give identical bits.
+struct AttnPart {
+  const float* part_o;     // [B][Hkv][NS][QPG][D]
+  const float2* part_ml;   // [B][Hkv][NS][QPG]
+  const int32_t* cpos;     // [B]
+  int Hkv, NS, QPG, D, M;
+};
+
+__device__ __forceinline__ int attn_splits(int c, int M) {
+  return (c < 0 || c >= M) ? 1 : c / kAttnSplit + 1;
+}
+
+// Merges dims [d0, d0 + ND) of q head h of batch row b.  Splits are folded in
+// split order with a running maximum (same value as the formula above); the
+// loads of 8 splits are issued together so the merge costs few memory round trips.
+template <int ND>
+__device__ __forceinline__ void merge_head(const AttnPart& p, int b, int h, int d0, float* out) {
+  const int g = h / p.QPG, hh = h - g * p.QPG;
+  const int ns = attn_splits(p.cpos[b], p.M);
+  const size_t base = ((size_t)b * p.Hkv + g) * p.NS;
+  float Mx = -INFINITY, L = 0.f;
+#pragma unroll
+  for (int i = 0; i < ND; ++i) out[i] = 0.f;
+  for (int t0 = 0; t0 < ns; t0 += 8) {
+    float2 ml[8];
+    float4 ov[8][ND / 4];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (t0 + t < ns) {
+        const size_t slot = (base + t0 + t) * p.QPG + hh;
+        ml[t] = p.part_ml[slot];
+        const float4* src = reinterpret_cast<const float4*>(p.part_o + slot * p.D + d0);
+#pragma unroll
+        for (int i = 0; i < ND / 4; ++i) ov[t][i] = src[i];
+      }
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (t0 + t < ns) {
+        const float Mn = fmaxf(Mx, ml[t].x);
+        const float cold = exp2f(Mx - Mn), cnew = exp2f(ml[t].x - Mn);
+        L = L * cold + ml[t].y * cnew;
+#pragma unroll
+        for (int i = 0; i < ND / 4; ++i) {
+          out[4 * i + 0] = out[4 * i + 0] * cold + ov[t][i].x * cnew;
+          out[4 * i + 1] = out[4 * i + 1] * cold + ov[t][i].y * cnew;
+          out[4 * i + 2] = out[4 * i + 2] * cold + ov[t][i].z * cnew;
+          out[4 * i + 3] = out[4 * i + 3] * cold + ov[t][i].w * cnew;
+        }
+        Mx = Mn;
+      }
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int i = 0; i < ND; ++i) out[i] *= inv;
+}
+
+// Stand-alone merge: one thread per (batch row, q head, 4 dims) -> o fp32 [B][Hq*D].
+__global__ __launch_bounds__(256) void k_attn_combine(AttnPart p, float* __restrict__ out, int B,
+                                                      int Hq) {
+  const int quads = p.D / 4;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * Hq * quads) return;
+  const int b = idx / (Hq * quads), r = idx - b * Hq * quads;
+  const int h = r / quads, dq = r - h * quads;
+  float o[4];
+  merge_head<4>(p, b, h, 4 * dq, o);
+  *reinterpret_cast<float4*>(out + (size_t)b * Hq * p.D + h * p.D + 4 * dq) =
+      make_float4(o[0], o[1], o[2], o[3]);
+}
+
 // ------------------------------------------------------------------ int4 GEMV
 // y[b][n] = sum_k w_hat[n][k] x[b][k] with w_hat = (q - 8) s + z per (row, group),
-// for batch rows b < B (compile-time tile BT >= B).  Optional RMSNorm prologue
-// (x <- x / sqrt(mean x^2 + eps) * gain) and three epilogues.
+// for batch rows b < B (compile-time tile BT >= B).  Prologues: plain input,
+// RMSNorm (x <- x / sqrt(mean x^2 + eps) * gain), or the attention merge above
+// (the O projection reads the split partials directly).  Epilogues: store,
+// residual add, SiLU(gate) * up over row pairs (n, n + N).
+//
+// Each wave owns kGemvRowsPerWave rows and lane l covers columns
+// [32 (l + 64 j), +32) for j < CPL; its weight loads are issued before the
+// prologue so that their latency overlaps the input staging.
 //
 // Dequantization stays in registers: a 32-bit word of 8 codes becomes four fp16
 // pairs with one shift and four and-or operations, using the exponent of 1024
 // as a magic bias (0x6400 | q is 1024 + q; codes in bits 4..7 of a half read as
-// 1024 + 16 q).  The input vector is staged in LDS as matching fp16 pairs (odd
-// columns pre-divided by 16), so v_dot2_f32_f16 accumulates sum q x plus a known
-// bias in fp32; per 32-column chunk the bias and sum x are precomputed, which
-// folds scale and zero into two multiply-adds per chunk:
-//     sum_k (q_k - 8 + z/s) s x_k = s (dot - C1) + z C2.
+// 1024 + 16 q).  The input is staged in LDS as matching fp16 pairs (odd columns
+// pre-divided by 16), so v_dot2_f32_f16 accumulates sum q x plus a known bias in
+// fp32; per 32-column chunk the bias and sum x are precomputed, folding scale
+// and zero into two multiply-adds per chunk:
+//     sum_k ((q_k - 8) s + z) x_k = s (dot - C1) + z C2.
 enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SILU = 2 };
+enum { PRO_PLAIN = 0, PRO_RMSNORM = 1, PRO_ATTN = 2 };
 
 struct GemvArgs {
   const uint8_t* packed;  // [rows][K/2]
   const uint32_t* sz;     // [rows][K/G] (scale | zero << 16)
-  const float* x;         // [B][ldx]
-  const uint16_t* gain;   // [K] or null
+  const float* x;         // [B][ldx]   (PRO_PLAIN, PRO_RMSNORM)
+  const uint16_t* gain;   // [K]        (PRO_RMSNORM)
   float* y;               // [B][ldy]
   int N;                  // outputs per batch row (EPI_SILU: weight rows are 2N)
   int K, G, B, ldx, ldy;
   float eps;
+  AttnPart ap;            // PRO_ATTN; ap.cpos is indexed from batch row b0
+  int b0;                 // first batch row of this tile (PRO_ATTN)
 };
 
-template <int BT, int EPI>
+// LDS layout of k_gemv_int4 (byte offsets, 16-byte aligned).
+struct GemvLds {
+  size_t xs, cc, xm, red, total;
+};
+__host__ __device__ inline GemvLds gemv_lds(int BT, int K, bool merged_input) {
+  GemvLds l{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 15) & ~(size_t)15; return r; };
+  const size_t CH = (size_t)K / 32;
+  l.xs = take((size_t)BT * 4 * CH * 16);
+  l.cc = take((size_t)BT * CH * 8);
+  l.xm = take(merged_input ? (size_t)BT * K * 4 : 0);
+  l.red = take((size_t)BT * 5 * 4);
+  l.total = o;
+  return l;
+}
+
+template <int BT, int EPI, int PRO, int CPL>
 __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int K = a.K, CH = K >> 5, NG = K / a.G, B = a.B;
-  uint4* xs = reinterpret_cast<uint4*>(smem);                    // [BT][4][CH]
-  float2* cc = reinterpret_cast<float2*>(xs + BT * 4 * CH);      // [BT][CH]
-  float* red = reinterpret_cast<float*>(cc + BT * CH);           // [BT][4]
-  float* sinv = red + BT * 4;                                    // [BT]
+  const GemvLds lay = gemv_lds(BT, K, PRO == PRO_ATTN);
+  uint4* xs = reinterpret_cast<uint4*>(smem + lay.xs);            // [BT][4][CH]
+  float2* cc = reinterpret_cast<float2*>(smem + lay.cc);          // [BT][CH]
+  float* xm = reinterpret_cast<float*>(smem + lay.xm);            // [BT][K] (PRO_ATTN)
+  float* red = reinterpret_cast<float*>(smem + lay.red);          // [BT][4]
+  float* sinv = red + BT * 4;                                     // [BT]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  if (a.gain) {
+  constexpr int RPW = kGemvRowsPerWave;
+  constexpr int NR = (EPI == EPI_SILU ? 2 : 1) * RPW;
+  const int n0 = (blockIdx.x * 4 + wave) * RPW;
+  int wrow[NR];
+  bool ok[NR];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int n = n0 + r;
+    ok[r] = n < a.N;
+    wrow[r] = ok[r] ? n : 0;
+    if (EPI == EPI_SILU) {
+      ok[RPW + r] = ok[r];
+      wrow[RPW + r] = ok[r] ? n + a.N : 0;
+    }
+  }
+  // ---- weight stream first
+  uint4 w[NR][CPL];
+  uint32_t sw[NR][CPL];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (ok[i] && c < CH) {
+        w[i][j] = load_stream16(a.packed + (size_t)wrow[i] * (K / 2) + 16 * c);
+        sw[i][j] = a.sz[(size_t)wrow[i] * NG + (32 * c) / a.G];
+      } else {
+        w[i][j] = make_uint4(0, 0, 0, 0);
+        sw[i][j] = 0;
+      }
+    }
+
+  // ---- prologue: input staging
+  if (PRO == PRO_ATTN) {
+    for (int idx = tid; idx < BT * (K / 4); idx += 256) {
+      const int b = idx / (K / 4), k4 = 4 * (idx - b * (K / 4));
+      float o4[4] = {0.f, 0.f, 0.f, 0.f};
+      if (b < B) merge_head<4>(a.ap, a.b0 + b, k4 / a.ap.D, k4 % a.ap.D, o4);
+      *reinterpret_cast<float4*>(xm + b * K + k4) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+    }
+    __syncthreads();
+  }
+  if (PRO == PRO_RMSNORM) {
 #pragma unroll
     for (int b = 0; b < BT; ++b) {
       float ss = 0.f;
@@ -176,18 +318,22 @@ __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
     }
     __syncthreads();
   }
-
   for (int idx = tid; idx < BT * CH; idx += 256) {
     const int b = idx / CH, c = idx - b * CH;
     float e[32];
     if (b < B) {
-      const float4* src = reinterpret_cast<const float4*>(a.x + (size_t)b * a.ldx + 32 * c);
+      if (PRO == PRO_ATTN) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float4 v = src[i];
-        e[4 * i] = v.x; e[4 * i + 1] = v.y; e[4 * i + 2] = v.z; e[4 * i + 3] = v.w;
+        for (int i = 0; i < 32; ++i) e[i] = xm[b * K + 32 * c + i];
+      } else {
+        const float4* src = reinterpret_cast<const float4*>(a.x + (size_t)b * a.ldx + 32 * c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float4 v = src[i];
+          e[4 * i] = v.x; e[4 * i + 1] = v.y; e[4 * i + 2] = v.z; e[4 * i + 3] = v.w;
+        }
       }
-      if (a.gain) {
+      if (PRO == PRO_RMSNORM) {
         const float iv = sinv[b];
         const uint32_t* gw = reinterpret_cast<const uint32_t*>(a.gain + 32 * c);
 #pragma unroll
@@ -223,70 +369,47 @@ __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
   }
   __syncthreads();
 
-  constexpr int RPW = kGemvRowsPerWave;
-  constexpr int NR = (EPI == EPI_SILU ? 2 : 1) * RPW;
-  const int n0 = (blockIdx.x * 4 + wave) * RPW;
-  int wrow[NR];
-  bool ok[NR];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int n = n0 + r;
-    ok[r] = n < a.N;
-    wrow[r] = ok[r] ? n : 0;
-    if (EPI == EPI_SILU) {
-      ok[RPW + r] = ok[r];
-      wrow[RPW + r] = ok[r] ? n + a.N : 0;
-    }
-  }
+  // ---- dequantize and multiply
   float acc[NR][BT];
 #pragma unroll
   for (int i = 0; i < NR; ++i)
 #pragma unroll
     for (int b = 0; b < BT; ++b) acc[i][b] = 0.f;
-
-  for (int c = lane; c < CH; c += 64) {
-    uint4 w[NR];
-    uint32_t sw[NR];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      if (ok[i]) {
-        w[i] = *reinterpret_cast<const uint4*>(a.packed + (size_t)wrow[i] * (K / 2) + 16 * c);
-        sw[i] = a.sz[(size_t)wrow[i] * NG + (32 * c) / a.G];
-      } else {
-        w[i] = make_uint4(0, 0, 0, 0);
-        sw[i] = 0;
-      }
-    }
-    uint32_t p[NR][16];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t t = ww[j] >> 8;
-        p[i][4 * j + 0] = (ww[j] & 0x000F000Fu) | 0x64006400u;
-        p[i][4 * j + 1] = (ww[j] & 0x00F000F0u) | 0x64006400u;
-        p[i][4 * j + 2] = (t & 0x000F000Fu) | 0x64006400u;
-        p[i][4 * j + 3] = (t & 0x00F000F0u) | 0x64006400u;
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      uint4 xv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) xv[j] = xs[(b * 4 + j) * CH + c];
-      const float2 C = cc[b * CH + c];
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    if (c < CH) {
+      uint32_t p[NR][16];
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
-        float d = 0.f;
+        const uint32_t ww[4] = {w[i][j].x, w[i][j].y, w[i][j].z, w[i][j].w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          d = fdot2(p[i][4 * j + 0], xv[j].x, d);
-          d = fdot2(p[i][4 * j + 1], xv[j].y, d);
-          d = fdot2(p[i][4 * j + 2], xv[j].z, d);
-          d = fdot2(p[i][4 * j + 3], xv[j].w, d);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t t = ww[q] >> 8;
+          p[i][4 * q + 0] = (ww[q] & 0x000F000Fu) | 0x64006400u;
+          p[i][4 * q + 1] = (ww[q] & 0x00F000F0u) | 0x64006400u;
+          p[i][4 * q + 2] = (t & 0x000F000Fu) | 0x64006400u;
+          p[i][4 * q + 3] = (t & 0x00F000F0u) | 0x64006400u;
         }
-        acc[i][b] += bf16_lo(sw[i]) * (d - C.x) + bf16_hi(sw[i]) * C.y;
+      }
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        uint4 xv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[q] = xs[(b * 4 + q) * CH + c];
+        const float2 C = cc[b * CH + c];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          float d = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            d = fdot2(p[i][4 * q + 0], xv[q].x, d);
+            d = fdot2(p[i][4 * q + 1], xv[q].y, d);
+            d = fdot2(p[i][4 * q + 2], xv[q].z, d);
+            d = fdot2(p[i][4 * q + 3], xv[q].w, d);
+          }
+          acc[i][b] += bf16_lo(sw[i][j]) * (d - C.x) + bf16_hi(sw[i][j]) * C.y;
+        }
       }
     }
   }
@@ -321,15 +444,15 @@ __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
 
 // ------------------------------------------------------------------ attention
 // One work-group per (split of kAttnSplit positions, kv head g, batch row b).
-// Prologue (fused): per-head RMSNorm of q and k over head_dim, M-RoPE on both,
-// bf16 rounding of the new k and v (their storage precision); the group owning
-// slot cache_position writes them to the cache and attends to them directly.
-// Main loop: each 16-lane row of a wave takes one position per step (head_dim/16
-// dims per lane, so four rows read four consecutive cache rows, coalesced),
-// keeping an online softmax per q head of the GQA group.  Partials (m, l, o) of
-// the 16 rows are merged in LDS; the groups of one (b, g) merge through global
-// partials with log-sum-exp weights, done by the last group to finish, in fixed
-// split order.
+// Each 16-lane row of a wave takes one cache position per step (head_dim/16
+// dims per lane, so the four rows of a wave read four consecutive cache rows),
+// and all of a lane's cache reads are issued first, before the prologue:
+// per-head RMSNorm of q and k over head_dim, M-RoPE on both, bf16 rounding of
+// the new k and v (their storage precision).  The group owning slot
+// cache_position writes them to the cache and attends to them directly.  An
+// online softmax per q head of the GQA group runs over the split; the 16 row
+// states merge in LDS into this split's partial (m, l, o~), written to the
+// workspace for merge_head.
 struct AttnArgs {
   const float* qkv;        // [B][ldqkv]
   const uint16_t* q_norm;  // [D]
@@ -338,10 +461,8 @@ struct AttnArgs {
   uint16_t* kc;            // layer slice [cacheB][Hkv][M][D]
   uint16_t* vc;
   const int32_t* cpos;     // [B]
-  float* out;              // [B][Hq*D]
   float* part_o;           // [B][Hkv][NS][QPG][D]
   float2* part_ml;         // [B][Hkv][NS][QPG]
-  uint32_t* counters;      // [B][Hkv]
   uint32_t* status;
   int ldqkv, Hq, Hkv, M, NS;
   float eps, scale_log2;   // log2(e) / sqrt(D)
@@ -351,10 +472,10 @@ template <int D, int QPG>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   constexpr int DPL = D / 16;   // dims per lane
   constexpr int HALF = D / 2;
+  constexpr int IT = kAttnSplit / 16;
   __shared__ float s_o[16][QPG][D];
   __shared__ float s_m[16][QPG];
   __shared__ float s_l[16][QPG];
-  __shared__ int s_last;
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -363,16 +484,37 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int d0 = li * DPL;
   const int c = a.cpos[b];
   const size_t head_base = ((size_t)b * a.Hkv + g) * a.M;   // in rows of D
+  const size_t pidx = ((size_t)b * a.Hkv + g) * a.NS + s;   // partial slot
 
   if (c < 0 || c >= a.M) {
-    if (s == 0) {
+    if (s == 0) {   // zero attention for this row: partial (m, l, o~) = (0, 1, 0)
       if (tid == 0 && g == 0) raise_status(a.status, 1u);
-      for (int i = tid; i < QPG * D; i += 256) a.out[(size_t)b * a.Hq * D + (size_t)g * QPG * D + i] = 0.f;
+      for (int i = tid; i < QPG * D; i += 256) a.part_o[pidx * QPG * D + i] = 0.f;
+      if (tid < QPG) a.part_ml[pidx * QPG + tid] = make_float2(0.f, 1.f);
     }
     return;
   }
   if (s * kAttnSplit > c) return;
   const int ns = c / kAttnSplit + 1;
+
+  // ---- cache reads first
+  uint32_t kr[IT][DPL / 2], vr[IT][DPL / 2];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int p = s * kAttnSplit + wave * (kAttnSplit / 4) + it * 4 + rr;
+    if (p < c) {
+      const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kc + (head_base + p) * D + d0);
+      const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vc + (head_base + p) * D + d0);
+#pragma unroll
+      for (int e = 0; e < DPL / 2; ++e) {
+        kr[it][e] = ks[e];
+        vr[it][e] = vs[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL / 2; ++e) kr[it][e] = vr[it][e] = 0u;
+    }
+  }
 
   // ---- prologue: q', k', v of the current token for this lane's dims
   const float* qrow = a.qkv + (size_t)b * a.ldqkv;
@@ -425,7 +567,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     }
   }
 
-  // ---- main loop over this split's positions
+  // ---- online softmax over this split's positions
   float m[QPG], l[QPG], o[QPG][DPL];
 #pragma unroll
   for (int h = 0; h < QPG; ++h) {
@@ -434,27 +576,19 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
   }
-  constexpr int PER_WAVE = kAttnSplit / 4;
 #pragma unroll
-  for (int it = 0; it < PER_WAVE / 4; ++it) {
-    const int p = s * kAttnSplit + wave * PER_WAVE + it * 4 + rr;
+  for (int it = 0; it < IT; ++it) {
+    const int p = s * kAttnSplit + wave * (kAttnSplit / 4) + it * 4 + rr;
     const bool valid = p <= c;
     float kk[DPL], vv[DPL];
-    if (valid && p != c) {
-      const uint16_t* ks = a.kc + (head_base + p) * D + d0;
-      const uint16_t* vs = a.vc + (head_base + p) * D + d0;
+    if (p == c) {
 #pragma unroll
-      for (int e = 0; e < DPL; e += 2) {
-        const uint32_t kw = *reinterpret_cast<const uint32_t*>(ks + e);
-        const uint32_t vw = *reinterpret_cast<const uint32_t*>(vs + e);
-        kk[e] = bf16_lo(kw); kk[e + 1] = bf16_hi(kw);
-        vv[e] = bf16_lo(vw); vv[e + 1] = bf16_hi(vw);
-      }
+      for (int e = 0; e < DPL; ++e) { kk[e] = kf[e]; vv[e] = vf[e]; }
     } else {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        kk[e] = valid ? kf[e] : 0.f;
-        vv[e] = valid ? vf[e] : 0.f;
+      for (int e = 0; e < DPL / 2; ++e) {
+        kk[2 * e] = bf16_lo(kr[it][e]); kk[2 * e + 1] = bf16_hi(kr[it][e]);
+        vv[2 * e] = bf16_lo(vr[it][e]); vv[2 * e + 1] = bf16_hi(vr[it][e]);
       }
     }
 #pragma unroll
@@ -475,7 +609,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     }
   }
 
-  // ---- merge the 16 row states of this group
+  // ---- merge the 16 row states into this split's partial
 #pragma unroll
   for (int h = 0; h < QPG; ++h) {
 #pragma unroll
@@ -486,7 +620,6 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     }
   }
   __syncthreads();
-  const size_t pidx = ((size_t)b * a.Hkv + g) * a.NS + s;   // partial slot
   for (int i = tid; i < QPG * D; i += 256) {
     const int h = i / D, d = i - h * D;
     float M = -INFINITY;
@@ -497,60 +630,23 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       L += wgt * s_l[r][h];
       O += wgt * s_o[r][h][d];
     }
-    if (ns == 1) {
-      a.out[(size_t)b * a.Hq * D + (size_t)(g * QPG + h) * D + d] = O / L;
-    } else {
-      a.part_o[(pidx * QPG + h) * D + d] = O;
-      if (d == 0) a.part_ml[pidx * QPG + h] = make_float2(M, L);
-    }
+    a.part_o[(pidx * QPG + h) * D + d] = O;
+    if (d == 0) a.part_ml[pidx * QPG + h] = make_float2(M, L);
   }
-  if (ns == 1) return;
-
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(&a.counters[b * a.Hkv + g], 1u);
-    s_last = (prev == (uint32_t)(ns - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const size_t base = ((size_t)b * a.Hkv + g) * a.NS;
-  for (int i = tid; i < QPG * D; i += 256) {
-    const int h = i / D, d = i - h * D;
-    float M = -INFINITY;
-    for (int t = 0; t < ns; ++t) M = fmaxf(M, a.part_ml[(base + t) * QPG + h].x);
-    float L = 0.f, O = 0.f;
-    for (int t = 0; t < ns; ++t) {
-      const float2 ml = a.part_ml[(base + t) * QPG + h];
-      const float wgt = exp2f(ml.x - M);
-      L += wgt * ml.y;
-      O += wgt * a.part_o[((base + t) * QPG + h) * D + d];
-    }
-    a.out[(size_t)b * a.Hq * D + (size_t)(g * QPG + h) * D + d] = O / L;
-  }
-  if (tid == 0) a.counters[b * a.Hkv + g] = 0u;
 }
 
 // ------------------------------------------------------------------ lm_head + argmax
 // logits[b][n] = sum_k W[n][k] h[b][k] with h = RMSNorm(x; final_norm), bf16 W
-// widened to fp32 in registers, fp32 accumulation.  Each group keeps the best
-// (value, lowest index) per batch row; the last group to finish reduces the
-// partials, writes next_ids, and applies the finished/advance rules.
+// widened to fp32 in registers, fp32 accumulation.  Each group leaves the best
+// (value, lowest index) per batch row; k_lm_finish reduces those partials in a
+// fixed order, writes next_ids, and applies the finished/advance rules.
 struct LmArgs {
   const float* x;            // [B][K]
   const uint16_t* gain;      // [K]
   const uint16_t* W;         // [V][K]
   float* logits;             // [B][V] or null
   float2* part;              // [B][nblk] (value, index as float bits)
-  uint32_t* counter;
-  const uint8_t* finished_in;
-  uint8_t* finished;         // may be null
-  int32_t* next;
-  int32_t* cpos;
-  int32_t* pos;              // [3][B]
-  int V, K, B, nblk, M, pad_id, eos_id;
-  uint32_t flags;
+  int V, K, B, nblk;
   float eps;
 };
 
@@ -558,16 +654,28 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-template <int BT>
+template <int BT, int CPL>
 __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* hs = reinterpret_cast<float*>(smem);       // [BT][K]
   __shared__ float red[BT * 4];
   __shared__ float s_bv[4][BT];
   __shared__ int s_bi[4][BT];
-  __shared__ int s_last;
-  const int K = a.K, B = a.B;
+  const int K = a.K, B = a.B, CH = K >> 3;   // 8-column chunks
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int RPW = kLmRowsPerWave;
+  const int n0 = blockIdx.x * kLmRowsPerBlock + wave * RPW;
+
+  uint4 w[RPW][CPL];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int n = n0 + r, c = lane + 64 * j;
+      w[r][j] = (n < a.V && c < CH)
+                    ? load_stream16(a.W + (size_t)n * K + 8 * c)
+                    : make_uint4(0, 0, 0, 0);
+    }
 
 #pragma unroll
   for (int b = 0; b < BT; ++b) {
@@ -590,33 +698,28 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
   }
   __syncthreads();
 
-  constexpr int RPW = kLmRowsPerWave;
-  const int n0 = blockIdx.x * kLmRowsPerBlock + wave * RPW;
-  const int CH = K >> 3;   // 8-column chunks
   float acc[RPW][BT];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
     for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
-  for (int c = lane; c < CH; c += 64) {
-    uint4 w[RPW];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int n = n0 + r;
-      w[r] = n < a.V ? *reinterpret_cast<const uint4*>(a.W + (size_t)n * K + 8 * c) : make_uint4(0, 0, 0, 0);
-    }
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    if (c < CH) {
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      const float4 h0 = *reinterpret_cast<const float4*>(hs + b * K + 8 * c);
-      const float4 h1 = *reinterpret_cast<const float4*>(hs + b * K + 8 * c + 4);
+      for (int b = 0; b < BT; ++b) {
+        const float4 h0 = *reinterpret_cast<const float4*>(hs + b * K + 8 * c);
+        const float4 h1 = *reinterpret_cast<const float4*>(hs + b * K + 8 * c + 4);
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        float t = acc[r][b];
-        t += bf16_lo(w[r].x) * h0.x; t += bf16_hi(w[r].x) * h0.y;
-        t += bf16_lo(w[r].y) * h0.z; t += bf16_hi(w[r].y) * h0.w;
-        t += bf16_lo(w[r].z) * h1.x; t += bf16_hi(w[r].z) * h1.y;
-        t += bf16_lo(w[r].w) * h1.z; t += bf16_hi(w[r].w) * h1.w;
-        acc[r][b] = t;
+        for (int r = 0; r < RPW; ++r) {
+          float t = acc[r][b];
+          t += bf16_lo(w[r][j].x) * h0.x; t += bf16_hi(w[r][j].x) * h0.y;
+          t += bf16_lo(w[r][j].y) * h0.z; t += bf16_hi(w[r][j].y) * h0.w;
+          t += bf16_lo(w[r][j].z) * h1.x; t += bf16_hi(w[r][j].z) * h1.y;
+          t += bf16_lo(w[r][j].w) * h1.z; t += bf16_hi(w[r][j].w) * h1.w;
+          acc[r][b] = t;
+        }
       }
     }
   }
@@ -644,59 +747,62 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
   if (tid < B) {
     float v = s_bv[0][tid];
     int i = s_bi[0][tid];
-    for (int w = 1; w < 4; ++w)
-      if (better(s_bv[w][tid], s_bi[w][tid], v, i)) { v = s_bv[w][tid]; i = s_bi[w][tid]; }
+    for (int w2 = 1; w2 < 4; ++w2)
+      if (better(s_bv[w2][tid], s_bi[w2][tid], v, i)) { v = s_bv[w2][tid]; i = s_bi[w2][tid]; }
     a.part[(size_t)tid * a.nblk + blockIdx.x] = make_float2(v, __int_as_float(i));
   }
-  __threadfence();
+}
+
+struct LmFinishArgs {
+  const float2* part;        // [B][nblk]
+  const uint8_t* finished_in;
+  uint8_t* finished;         // may be null
+  int32_t* next;
+  int32_t* cpos;
+  int32_t* pos;              // [3][B]
+  int B, nblk, M, pad_id, eos_id;
+  uint32_t flags;
+};
+
+// One group per batch row: argmax over the lm_head partials (ties to the lowest
+// index), then the greedy-step bookkeeping of that row.
+__global__ __launch_bounds__(256) void k_lm_finish(LmFinishArgs a) {
+  __shared__ float t_v[256];
+  __shared__ int t_i[256];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  float v = -INFINITY;
+  int i = 0x7fffffff;
+  for (int t = tid; t < a.nblk; t += 256) {
+    const float2 pv = a.part[(size_t)b * a.nblk + t];
+    if (better(pv.x, __float_as_int(pv.y), v, i)) { v = pv.x; i = __float_as_int(pv.y); }
+  }
+  t_v[tid] = v;
+  t_i[tid] = i;
   __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w && better(t_v[tid + w], t_i[tid + w], t_v[tid], t_i[tid])) {
+      t_v[tid] = t_v[tid + w];
+      t_i[tid] = t_i[tid + w];
+    }
+    __syncthreads();
+  }
   if (tid == 0) {
-    const uint32_t prev = atomicAdd(a.counter, 1u);
-    s_last = (prev == (uint32_t)(gridDim.x - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int b = 0; b < B; ++b) {
-    float v = -INFINITY;
-    int i = 0x7fffffff;
-    for (int t = tid; t < a.nblk; t += 256) {
-      const float2 pv = a.part[(size_t)b * a.nblk + t];
-      if (better(pv.x, __float_as_int(pv.y), v, i)) { v = pv.x; i = __float_as_int(pv.y); }
-    }
-    // block argmax: exchange through LDS in a fixed tree order
-    __shared__ float t_v[256];
-    __shared__ int t_i[256];
-    t_v[tid] = v;
-    t_i[tid] = i;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-      if (tid < w && better(t_v[tid + w], t_i[tid + w], t_v[tid], t_i[tid])) {
-        t_v[tid] = t_v[tid + w];
-        t_i[tid] = t_i[tid + w];
-      }
-      __syncthreads();
-    }
-    if (tid == 0) {
-      const int best = t_i[0];
-      const int fin = a.finished_in ? a.finished_in[b] : 0;
-      a.next[b] = fin ? a.pad_id : best;
-      if ((a.flags & 1u) && !fin) {
-        if (a.eos_id >= 0 && best == a.eos_id) {
-          if (a.finished) a.finished[b] = 1;
-        } else if (a.cpos[b] + 1 >= a.M) {
-          if (a.finished) a.finished[b] = 1;
-        } else {
-          a.cpos[b] += 1;
-          a.pos[0 * B + b] += 1;
-          a.pos[1 * B + b] += 1;
-          a.pos[2 * B + b] += 1;
-        }
+    const int best = t_i[0];
+    const int fin = a.finished_in ? a.finished_in[b] : 0;
+    a.next[b] = fin ? a.pad_id : best;
+    if ((a.flags & 1u) && !fin) {
+      if (a.eos_id >= 0 && best == a.eos_id) {
+        if (a.finished) a.finished[b] = 1;
+      } else if (a.cpos[b] + 1 >= a.M) {
+        if (a.finished) a.finished[b] = 1;
+      } else {
+        a.cpos[b] += 1;
+        a.pos[0 * a.B + b] += 1;
+        a.pos[1 * a.B + b] += 1;
+        a.pos[2 * a.B + b] += 1;
       }
     }
-    __syncthreads();
   }
-  if (tid == 0) *a.counter = 0u;
 }
 
 }  // namespace kmr

@@ -14,7 +14,8 @@ from typing import Dict, List, Optional, Sequence
 import torch  # loads the HIP runtime that libkmr.so must share
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkmr.so")
+# KMR_LIBRARY may point at another build of the same library (e.g. a diagnostic build).
+LIB_PATH = os.environ.get("KMR_LIBRARY", os.path.join(HERE, "libkmr.so"))
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m int4_weight_only_gemv_amd.build`")
@@ -30,9 +31,10 @@ if len(_hip_runtimes()) > 1:
     raise ImportError(f"two HIP runtimes are mapped: {_hip_runtimes()}")
 
 KMR_OK, KMR_EINVAL, KMR_ESHAPE, KMR_ENOMEM, KMR_EHIP = 0, -1, -2, -3, -4
-KMR_STATUS_CACHE_POS, KMR_STATUS_TOKEN = 1, 2
+KMR_STATUS_CACHE_POS, KMR_STATUS_TOKEN, KMR_STATUS_TIMEOUT = 1, 2, 4
 KMR_MAX_BATCH = 16
 KMR_ADVANCE = 1
+KMR_MULTI_KERNEL = 2
 
 _i32, _p = C.c_int32, C.c_void_p
 
@@ -224,13 +226,14 @@ class DeviceModel:
     def decode_step(self, kv: KVCache, token_ids: torch.Tensor, positions: torch.Tensor,
                     cache_position: torch.Tensor, next_ids: torch.Tensor, ws: Workspace,
                     finished: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
-                    advance: bool = False, stream=None) -> torch.Tensor:
+                    advance: bool = False, multi_kernel: bool = False, stream=None) -> torch.Tensor:
         B = token_ids.shape[0]
         assert token_ids.dtype == torch.int32 and next_ids.dtype == torch.int32
         assert finished is None or finished.dtype == torch.uint8
         _check(_lib.kmr_decode_step(C.byref(self.cfg), C.byref(self.cmodel), C.byref(kv.desc),
                                     _ptr(token_ids), _ptr(positions), _ptr(cache_position),
                                     _ptr(finished), B, _ptr(next_ids), _ptr(logits),
-                                    KMR_ADVANCE if advance else 0, ws.ptr, ws.nbytes,
+                                    (KMR_ADVANCE if advance else 0) | (KMR_MULTI_KERNEL if multi_kernel else 0),
+                                    ws.ptr, ws.nbytes,
                                     _stream(stream)))
         return next_ids

@@ -137,7 +137,7 @@ def _check_step(got_next, got_logits, ref, label):
     assert np.all(agree | ~decisive)
 
 
-def _step_case(kmr, pair, kv, kh, vh, inp, M, steps=1, advance=False):
+def _step_case(kmr, pair, kv, kh, vh, inp, M, steps=1, advance=False, multi_kernel=False):
     dims = pair.dims
     B = len(inp["ids"])
     cfg = pair.dev.cfg
@@ -151,7 +151,7 @@ def _step_case(kmr, pair, kv, kh, vh, inp, M, steps=1, advance=False):
     for step in range(steps):
         ids_d = torch.from_numpy(ids).cuda()
         pair.dev.decode_step(kv, ids_d, pos_d, cpos_d, nxt_d, ws, finished=fin_d, logits=logits_d,
-                             advance=advance)
+                             advance=advance, multi_kernel=multi_kernel)
         torch.cuda.synchronize()
         ref = pair.ora.decode_step(kh, vh, ids, pos, cpos, finished=fin, advance=advance)
         _check_step(nxt_d.cpu().numpy(), logits_d.cpu().numpy(), ref, f"step {step}")
@@ -163,24 +163,26 @@ def _step_case(kmr, pair, kv, kh, vh, inp, M, steps=1, advance=False):
     return ref
 
 
-def test_decode_step_tiny(kmr):
+@pytest.mark.parametrize("multi_kernel", [False, True])
+def test_decode_step_tiny(kmr, multi_kernel):
     w = synth.WORKLOADS["tiny"]
-    log("decode_step tiny")
+    log(f"decode_step tiny (multi_kernel={multi_kernel})")
     pair = build_pair(w.dims, synth.base_seed(w), "host", with_globals=True)
     kv, kh, vh = make_caches(w.dims, synth.base_seed(w), 1, w.max_len, "host")
-    _step_case(kmr, pair, kv, kh, vh, synth.step_inputs(w), w.max_len)
+    _step_case(kmr, pair, kv, kh, vh, synth.step_inputs(w), w.max_len, multi_kernel=multi_kernel)
 
 
-def test_decode_step_tiny_batch_advance(kmr):
+@pytest.mark.parametrize("multi_kernel", [False, True])
+def test_decode_step_tiny_batch_advance(kmr, multi_kernel):
     w = synth.WORKLOADS["tiny"]
-    log("decode_step tiny batch 3, finished row, advance to the last slot")
+    log(f"decode_step tiny batch 3, finished row, advance to the last slot (multi_kernel={multi_kernel})")
     pair = build_pair(w.dims, synth.base_seed(w), "host", with_globals=True)
     kv, kh, vh = make_caches(w.dims, synth.base_seed(w), 3, w.max_len, "host")
     inp = {"ids": np.array([5, 6, 7], np.int32),
            "positions": np.array([[10, 125, 3], [11, 1, 3], [12, 2, 3]], np.int32),
            "cache_position": np.array([10, 125, 3], np.int32),
            "finished": np.array([0, 0, 1], np.uint8)}
-    _step_case(kmr, pair, kv, kh, vh, inp, w.max_len, steps=4, advance=True)
+    _step_case(kmr, pair, kv, kh, vh, inp, w.max_len, steps=4, advance=True, multi_kernel=multi_kernel)
 
 
 @pytest.fixture(scope="module")
@@ -190,11 +192,44 @@ def full_pair(kmr):
     return build_pair(w.dims, synth.base_seed(w), "device", with_globals=True)
 
 
-def test_decode_step_full(kmr, full_pair):
+@pytest.mark.parametrize("multi_kernel", [False, True])
+def test_decode_step_full(kmr, full_pair, multi_kernel):
     w = synth.WORKLOADS["step"]
-    log("decode_step 28 layers, batch 1, cache_position 700")
+    log(f"decode_step 28 layers, batch 1, cache_position 700 (multi_kernel={multi_kernel})")
     kv, kh, vh = make_caches(w.dims, synth.base_seed(w), 1, w.max_len, "device")
-    _step_case(kmr, full_pair, kv, kh, vh, synth.step_inputs(w), w.max_len)
+    _step_case(kmr, full_pair, kv, kh, vh, synth.step_inputs(w), w.max_len, multi_kernel=multi_kernel)
+
+
+def test_persistent_and_per_phase_paths_agree(kmr, full_pair):
+    w = synth.WORKLOADS["batch4"]
+    log("persistent step kernel vs per-phase kernels, batch 4, 3 advancing steps")
+    inp = synth.step_inputs(w)
+    outs = []
+    for multi in (False, True):
+        kv, _, _ = make_caches(w.dims, synth.base_seed(w), w.batch, w.max_len, "device", host_rows=[0])
+        ws = kmr.Workspace(full_pair.dev.cfg, w.batch, w.max_len)
+        ids = torch.from_numpy(inp["ids"]).cuda()
+        pos, cpos = torch.from_numpy(inp["positions"]).cuda(), torch.from_numpy(inp["cache_position"]).cuda()
+        fin = torch.from_numpy(inp["finished"]).cuda()
+        nxt = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
+        logits = torch.empty((w.batch, w.dims.vocab), dtype=torch.float32, device="cuda")
+        seq = []
+        for _ in range(3):
+            full_pair.dev.decode_step(kv, ids, pos, cpos, nxt, ws, finished=fin, logits=logits,
+                                      advance=True, multi_kernel=multi)
+            seq.append((nxt.clone(), logits.clone()))
+            ids = nxt.clone()
+        torch.cuda.synchronize()
+        assert ws.status() == 0
+        outs.append((seq, kv.k.clone(), kv.v.clone(), pos.cpu(), cpos.cpu(), fin.cpu()))
+        del kv
+    (sa, ka, va, pa, ca, fa), (sb, kb, vb, pb, cb, fb) = outs
+    for (na, la), (nb, lb) in zip(sa, sb):
+        err = max_rel(la.cpu().numpy(), lb.cpu().numpy())
+        log(f"  logits max_rel between paths {err:.3e}; tokens {na.tolist()} vs {nb.tolist()}")
+        assert err <= TOL
+    assert torch.equal(pa, pb) and torch.equal(ca, cb) and torch.equal(fa, fb)
+    assert max_rel(ka.float().cpu().numpy().reshape(-1, 128), kb.float().cpu().numpy().reshape(-1, 128)) <= TOL
 
 
 def test_decode_step_batch4_lockstep(kmr, full_pair):
