@@ -318,7 +318,7 @@ template <int BT, int D>
 int launch_step_k(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
   const int KMAX = std::max(c->hidden, std::max(c->intermediate, c->n_heads * c->head_dim));
   const int RPBX = (c->hidden + nwg - 1) / nwg;
-  const size_t lds = step_lds(BT, KMAX, RPBX, D, 2).total;
+  const size_t lds = step_lds(BT, KMAX, RPBX, c->hidden, D, 2).total;
   auto fn = k_step<BT, D, 2>;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lds) != hipSuccess)

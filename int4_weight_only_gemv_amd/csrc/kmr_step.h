@@ -155,21 +155,133 @@ __device__ __forceinline__ bool gather_tagged(const uint64_t* src, int total, ui
   return !__syncthreads_or(!ok);
 }
 
-// `total` contiguous tagged words into swizzled LDS (rows of a [B][n] buffer
-// are contiguous, so word i of the gather is word i of the buffer).
-template <typename Pre>
-__device__ __forceinline__ bool gather_vec(const uint64_t* src, int total, uint32_t tag, float* dst,
-                                           Pre pre) {
-  auto addr = [](int i) { return (size_t)i; };
-  auto place = [](int i) { return swz(i); };
-  const int rows = 1, n = total;
-  if (rows * n <= kStepThreads * 4) return gather_tagged<4>(src, rows * n, tag, dst, addr, place, pre);
-  return gather_tagged<12>(src, rows * n, tag, dst, addr, place, pre);
-}
-
 struct NoPre {
   __device__ void operator()() const {}
 };
+
+// The pair (value of the lower lane, value of the upper lane) of lanes l and
+// l ^ 16 (BIT = 16) or l ^ 32 (BIT = 32), the same on both lanes.
+template <int BIT>
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = BIT == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+// ------------------------------------------------------------------ GEMV input staging
+// Value of lane l ^ 4 (the other half of an 8-lane group), from two DPP
+// rotations within each 16-lane row: banks 0 and 2 take lane + 4, banks 1 and 3
+// take lane - 4.
+__device__ __forceinline__ float lane_xor4(float v) {
+  const float up = dpp<0x12C, 0xf, 0x5>(v);   // row_ror 12: lane i <- lane i + 4
+  const float dn = dpp<0x124, 0xf, 0xA>(v);   // row_ror 4:  lane i <- lane i - 4
+  return (threadIdx.x & 4) ? dn : up;
+}
+
+// Gathers a tagged [B][K] input (PT words per thread per pass, consecutive lanes
+// polling consecutive words), optionally RMS-normalises it with `gain`, and
+// converts it once per work-group into the LDS layout the dot products read:
+// xs[(b*4 + w)*CH + c] holds the fp16 pairs of word w (8 columns) of 32-column
+// chunk c, and cc[b*CH + c] its (C1, C2) = (1024 sum h + 8 sum x, sum x) over the
+// values actually used (odd columns pre-divided by 16, matching the magic-bias
+// weight pairs).  An 8-column word lives in 8 consecutive lanes (pairs formed
+// with lane ^ 4), a 32-column chunk in 32 consecutive lanes.
+template <int BT, int PT>
+__device__ __forceinline__ bool gather_stage(const uint64_t* src, int K, int B, uint32_t tag,
+                                             const uint16_t* gain, float eps, uint4* xs, float2* cc,
+                                             float* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int CH = K >> 5, total = B * K;
+  uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
+  float inv[BT];
+#pragma unroll
+  for (int b = 0; b < BT; ++b) inv[b] = 1.f;
+  for (int base = 0; base < total; base += kStepThreads * PT) {
+    int idx[PT], wb[PT], wk[PT];
+    bool has[PT];
+    float gv[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      idx[j] = base + kStepThreads * j + tid;
+      has[j] = idx[j] < total;
+      wb[j] = 0;
+#pragma unroll
+      for (int b = 1; b < BT; ++b) wb[j] += idx[j] >= b * K ? 1 : 0;
+      wk[j] = idx[j] - wb[j] * K;
+      gv[j] = (gain && has[j]) ? bf16_to_f32(gain[wk[j]]) : 1.f;
+    }
+    uint64_t v[PT];
+    uint32_t spins = 0;
+    bool fresh, ok = true;
+    do {
+#pragma unroll
+      for (int j = 0; j < PT; ++j)
+        if (has[j]) v[j] = ld_dev64(src + idx[j]);
+      fresh = true;
+#pragma unroll
+      for (int j = 0; j < PT; ++j)
+        if (has[j]) fresh &= (uint32_t)(v[j] >> 32) == tag;
+      if (!fresh) {
+        if (++spins > kSpinLimit) { ok = false; break; }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    } while (!fresh);
+    if (__syncthreads_or(!ok)) return false;
+    float x[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) x[j] = has[j] ? __uint_as_float((uint32_t)v[j]) : 0.f;
+    if (gain) {
+      // one pass holds every value (checked on the host): per-row sum of squares
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < PT; ++j)
+          if (has[j] && wb[j] == b) ss += x[j] * x[j];
+        ss = wave_sum(ss);
+        if (lane == 0) red[b * kStepWaves + wave] = ss;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        float ss = 0.f;
+#pragma unroll
+        for (int w = 0; w < kStepWaves; ++w) ss += red[b * kStepWaves + w];
+        inv[b] = 1.0f / sqrtf(ss / (float)K + eps);
+      }
+    }
+    const int i8 = lane & 7;   // column within the 8-column word
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      float iv = inv[0];
+#pragma unroll
+      for (int b = 1; b < BT; ++b) if (wb[j] == b) iv = inv[b];
+      const float e = gain ? (x[j] * iv) * gv[j] : x[j];
+      const _Float16 h = (_Float16)((i8 & 1) ? e * 0.0625f : e);
+      const float hf = (float)h;
+      const float uf = (i8 & 1) ? 16.0f * hf : hf;
+      const float other = lane_xor4(hf);
+      // chunk sums over the 32 lanes of the chunk
+      float bs = row16_sum(hf), us = row16_sum(uf), blo, bhi, ulo, uhi;
+      lane_pair<16>(bs, blo, bhi);
+      lane_pair<16>(us, ulo, uhi);
+      if (has[j]) {
+        const int c = wk[j] >> 5, w = (wk[j] >> 3) & 3;
+        if (i8 < 4)
+          xs32[((wb[j] * 4 + w) * CH + c) * 4 + i8] =
+              __builtin_bit_cast(uint32_t, half2_t{h, (_Float16)other});
+        if ((lane & 31) == 0) {
+          const float bsum = blo + bhi, usum = ulo + uhi;
+          cc[wb[j] * CH + c] = make_float2(1024.0f * bsum + 8.0f * usum, usum);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  return true;
+}
 
 // ------------------------------------------------------------------ per-wave GEMV pieces
 // NR weight rows for this lane's CPL 32-column chunks (codes and scale/zero).
@@ -213,46 +325,10 @@ __device__ __forceinline__ void dequant16(const uint4 raw, uint32_t (&p)[16]) {
   }
 }
 
-// The 32 gathered floats of chunk cb (a global 32-column chunk index of the
-// swizzled LDS vector), read granule by granule.
-__device__ __forceinline__ void read_chunk(const float* lds, int cb, float* e) {
-#pragma unroll
-  for (int col = 0; col < 8; ++col) {
-    const float4 v = *reinterpret_cast<const float4*>(lds + (((cb << 3) | (col ^ (cb & 7))) << 2));
-    e[4 * col] = v.x; e[4 * col + 1] = v.y; e[4 * col + 2] = v.z; e[4 * col + 3] = v.w;
-  }
-}
-
-// fp16 pairs of 32 input values in the order of the dequantized weight pairs,
-// with C1 = 1024 sum(h) + 8 sum(x used), C2 = sum(x used).
-__device__ __forceinline__ void pack_input(const float* e, uint32_t* xp, float& C1, float& C2) {
-  float bsum = 0.f, usum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float* f = e + 8 * j;
-    _Float16 h0 = (_Float16)f[0], h4 = (_Float16)f[4], h2 = (_Float16)f[2], h6 = (_Float16)f[6];
-    _Float16 h1 = (_Float16)(f[1] * 0.0625f), h5 = (_Float16)(f[5] * 0.0625f);
-    _Float16 h3 = (_Float16)(f[3] * 0.0625f), h7 = (_Float16)(f[7] * 0.0625f);
-    xp[4 * j + 0] = __builtin_bit_cast(uint32_t, half2_t{h0, h4});
-    xp[4 * j + 1] = __builtin_bit_cast(uint32_t, half2_t{h1, h5});
-    xp[4 * j + 2] = __builtin_bit_cast(uint32_t, half2_t{h2, h6});
-    xp[4 * j + 3] = __builtin_bit_cast(uint32_t, half2_t{h3, h7});
-    const float ev = ((float)h0 + (float)h4) + ((float)h2 + (float)h6);
-    const float od = ((float)h1 + (float)h5) + ((float)h3 + (float)h7);
-    bsum += ev + od;
-    usum += ev + 16.0f * od;
-  }
-  C1 = 1024.0f * bsum + 8.0f * usum;
-  C2 = usum;
-}
-
-// out[i][b] = dot of weight row i with input row b (uniform across the wave).
-// With gain: input b is RMS-normalised (the wave computes the norm itself, its
-// lanes covering the whole vector) and scaled by the gain.
+// out[i][b] = dot of weight row i with staged input row b (uniform across the wave).
 template <int BT, int NR, int CPL>
-__device__ __forceinline__ void wave_dot(const WRows<NR, CPL>& w, const float* lds, int K, int B,
-                                         const uint32_t (*gain)[16], float eps,
-                                         float (&out)[NR][BT]) {
+__device__ __forceinline__ void wave_dot(const WRows<NR, CPL>& w, int K, int B, const uint4* xs,
+                                         const float2* cc, float (&out)[NR][BT]) {
   const int lane = threadIdx.x & 63, CH = K >> 5;
   float acc[NR][BT];
 #pragma unroll
@@ -260,48 +336,29 @@ __device__ __forceinline__ void wave_dot(const WRows<NR, CPL>& w, const float* l
 #pragma unroll
     for (int b = 0; b < BT; ++b) acc[i][b] = 0.f;
 #pragma unroll
-  for (int b = 0; b < BT; ++b) {
-    if (b >= B) break;
-    float inv = 1.f;
-    if (gain) {
-      float ss = 0.f;
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    if (c < CH) {
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const int c = lane + 64 * j;
-        if (c < CH) {
-          float e[32];
-          read_chunk(lds, b * CH + c, e);
+      for (int b = 0; b < BT; ++b) {
+        if (b >= B) break;
+        uint4 xv[4];
 #pragma unroll
-          for (int i = 0; i < 32; ++i) ss += e[i] * e[i];
-        }
-      }
-      ss = wave_sum(ss);
-      inv = 1.0f / sqrtf(ss / (float)K + eps);
-    }
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      if (c < CH) {
-        float e[32];
-        read_chunk(lds, b * CH + c, e);
-        if (gain) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            e[2 * i] = (e[2 * i] * inv) * bf16_lo(gain[j][i]);
-            e[2 * i + 1] = (e[2 * i + 1] * inv) * bf16_hi(gain[j][i]);
-          }
-        }
-        uint32_t xp[16];
-        float C1, C2;
-        pack_input(e, xp, C1, C2);
+        for (int q = 0; q < 4; ++q) xv[q] = xs[(b * 4 + q) * CH + c];
+        const float2 C = cc[b * CH + c];
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
           uint32_t p[16];
           dequant16(w.raw[i][j], p);
           float d = 0.f;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) d = fdot2(p[q], xp[q], d);
-          acc[i][b] += bf16_lo(w.sz[i][j]) * (d - C1) + bf16_hi(w.sz[i][j]) * C2;
+          for (int q = 0; q < 4; ++q) {
+            d = fdot2(p[4 * q + 0], xv[q].x, d);
+            d = fdot2(p[4 * q + 1], xv[q].y, d);
+            d = fdot2(p[4 * q + 2], xv[q].z, d);
+            d = fdot2(p[4 * q + 3], xv[q].w, d);
+          }
+          acc[i][b] += bf16_lo(w.sz[i][j]) * (d - C.x) + bf16_hi(w.sz[i][j]) * C.y;
         }
       }
     }
@@ -310,18 +367,6 @@ __device__ __forceinline__ void wave_dot(const WRows<NR, CPL>& w, const float* l
   for (int i = 0; i < NR; ++i)
 #pragma unroll
     for (int b = 0; b < BT; ++b) out[i][b] = wave_sum(acc[i][b]);
-}
-
-template <int CPL>
-__device__ __forceinline__ void load_gain(const uint16_t* gain, int K, uint32_t (&g)[CPL][16]) {
-  const int lane = threadIdx.x & 63, CH = K >> 5;
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = lane + 64 * j;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      g[j][i] = c < CH ? reinterpret_cast<const uint32_t*>(gain + 32 * c)[i] : 0u;
-  }
 }
 
 struct AttnItem {
@@ -373,25 +418,30 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float* o, float m2
   m = M;
 }
 
+
 // LDS layout of the step kernel (dynamic shared memory, byte offsets):
-//   xin   fp32 [BT][KMAX]        gathered input vector (swizzled), also the
-//                                attention scratch (q/k/v, wave states, merge)
-//   xown  fp32 [BT][RPBX]        this group's rows of the residual stream
-//   cs    float2 [BT][D/2]       RoPE cos/sin of each row
+//   xs    uint4 [BT][4][KMAX/32]  staged fp16 input pairs
+//   cc    float2 [BT][KMAX/32]    per-chunk (C1, C2)
+//   xin   fp32 scratch            attention q/k/v, wave states, split merge,
+//                                 lm_head input
+//   xown  fp32 [BT][RPBX]         this group's rows of the residual stream
+//   cs    float2 [BT][D/2]        RoPE cos/sin of each row
 //   red   float [128]
 struct StepLds {
-  size_t xin, xown, cs, red, total;
+  size_t xs, cc, xin, xown, cs, red, total;
 };
 
-__host__ __device__ inline StepLds step_lds(int BT, int KMAX, int RPBX, int D, int QPG) {
+__host__ __device__ inline StepLds step_lds(int BT, int KMAX, int RPBX, int H, int D, int QPG) {
   StepLds s{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 15) & ~(size_t)15; return r; };
   const size_t merge_bytes = (size_t)kMergeChunk * QPG * (D + 2) * 4;
   const size_t attn_bytes = (size_t)kStepWaves * QPG * (D + 2) * 4 + (size_t)(QPG + 2) * D * 4;
-  size_t xin_bytes = (size_t)BT * KMAX * 4;
+  size_t xin_bytes = (size_t)BT * H * 4;
   if (xin_bytes < merge_bytes) xin_bytes = merge_bytes;
   if (xin_bytes < attn_bytes) xin_bytes = attn_bytes;
+  s.xs = take((size_t)BT * 4 * (KMAX / 32) * 16);
+  s.cc = take((size_t)BT * (KMAX / 32) * 8);
   s.xin = take(xin_bytes);
   s.xown = take((size_t)BT * RPBX * 4);
   s.cs = take((size_t)BT * (D / 2) * 8);
@@ -410,7 +460,9 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
   const int NQKV = (Hq + 2 * Hkv) * D, QD = Hq * D;
   const int KMAX = H > I ? (H > QD ? H : QD) : (I > QD ? I : QD);
   const int RPBX = (H + nwg - 1) / nwg;                     // residual rows owned per group
-  const StepLds L = step_lds(BT, KMAX, RPBX, D, QPG);
+  const StepLds L = step_lds(BT, KMAX, RPBX, H, D, QPG);
+  uint4* xs = reinterpret_cast<uint4*>(smem + L.xs);
+  float2* cc = reinterpret_cast<float2*>(smem + L.cc);
   float* xin = reinterpret_cast<float*>(smem + L.xin);
   float* xown = reinterpret_cast<float*>(smem + L.xown);
   float2* cs = reinterpret_cast<float2*>(smem + L.cs);
@@ -464,15 +516,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
           row[i] = ok[i] ? n : 0;
         }
         WRows<NR, 1> w;
-        uint32_t gn[1][16];
         wrows_load(w, Ly.qkv_p, Ly.qkv_s, H, G, row, ok);
-        load_gain<1>(Ly.in_norm, H, gn);
         if (r0 == 0) {
-          if (!gather_vec(a.tx, B * H, tag(ph), xin, NoPre())) { alive = false; break; }
+          if (!gather_stage<BT, 4 * BT>(a.tx, H, B, tag(ph), Ly.in_norm, a.eps, xs, cc, red)) { alive = false; break; }
         }
         KMR_TRACE_MARK(tev + 0);
         float out[NR][BT];
-        wave_dot<BT, NR, 1>(w, xin, H, B, gn, a.eps, out);
+        wave_dot<BT, NR, 1>(w, H, B, xs, cc, out);
         if (lane < B) {
 #pragma unroll
           for (int i = 0; i < NR; ++i)
@@ -604,17 +654,22 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
           }
         }
       }
-      // merge the 4 rows of each wave through lane shuffles (rows r, r^1, then r^2)
+      KMR_TRACE_MARK(l == 1 ? 59 : 64);
+      // merge the 4 rows of each wave: rows (0,1) and (2,3), then (01, 23); both
+      // lanes of a pair merge (lower, upper) in that order, so all rows agree
 #pragma unroll
-      for (int sh = 16; sh <= 32; sh <<= 1) {
+      for (int h = 0; h < QPG; ++h) {
+        float mlo, mhi, llo, lhi, olo[DPL], ohi[DPL];
+        lane_pair<16>(m[h], mlo, mhi);
+        lane_pair<16>(lsum[h], llo, lhi);
 #pragma unroll
-        for (int h = 0; h < QPG; ++h) {
-          const float m2 = __shfl_xor(m[h], sh), l2 = __shfl_xor(lsum[h], sh);
-          float o2[DPL];
+        for (int e = 0; e < DPL; ++e) lane_pair<16>(o[h][e], olo[e], ohi[e]);
+        lse_merge(mlo, llo, olo, mhi, lhi, ohi, DPL);
+        lane_pair<32>(mlo, m[h], mhi);
+        lane_pair<32>(llo, lsum[h], lhi);
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) o2[e] = __shfl_xor(o[h][e], sh);
-          lse_merge(m[h], lsum[h], o[h], m2, l2, o2, DPL);
-        }
+        for (int e = 0; e < DPL; ++e) lane_pair<32>(olo[e], o[h][e], ohi[e]);
+        lse_merge(m[h], lsum[h], o[h], mhi, lhi, ohi, DPL);
       }
       __syncthreads();   // q/k/v scratch is reused below
       float* s_w = xin;                                  // [8 waves][QPG][D + 2]
@@ -649,6 +704,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
         }
       }
       __syncthreads();
+      KMR_TRACE_MARK(l == 1 ? 60 : 64);
     }
     if (__syncthreads_or(!alive)) break;
     // ================= split merge: the group of each head's last split merges all
@@ -685,11 +741,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
         __syncthreads();
       }
       if (!alive) break;
+      KMR_TRACE_MARK(l == 1 ? 61 : 64);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int i = tid + kStepThreads * k;
         if (i < QPG * D) publish(odst + i, tag(ph + 3), Os[k] * (1.0f / Ls[k]));
       }
+      KMR_TRACE_MARK(l == 1 ? 62 : 64);
     }
     if (__syncthreads_or(!alive)) break;
     KMR_TRACE_MARK(tev + 3);
@@ -703,11 +761,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
       WRows<NR, 1> w;
       wrows_load(w, Ly.o_p, Ly.o_s, QD, G, row, ok);
       if (r2 == 0) {
-        if (!gather_vec(a.to, B * QD, tag(ph + 3), xin, NoPre())) { alive = false; break; }
+        if (!gather_stage<BT, 4 * BT>(a.to, QD, B, tag(ph + 3), nullptr, a.eps, xs, cc, red)) { alive = false; break; }
       }
       KMR_TRACE_MARK(tev + 4);
       float out[NR][BT];
-      wave_dot<BT, NR, 1>(w, xin, QD, B, nullptr, a.eps, out);
+      wave_dot<BT, NR, 1>(w, QD, B, xs, cc, out);
       if (lane < B && ok[0]) {
         float v = out[0][0];
 #pragma unroll
@@ -734,15 +792,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
           row[NP + i] = ok[i] ? n + I : 0;
         }
         WRows<2 * NP, 1> w;
-        uint32_t gn[1][16];
         wrows_load(w, Ly.gu_p, Ly.gu_s, H, G, row, ok);
-        load_gain<1>(Ly.post_norm, H, gn);
         if (r0 == 0) {
-          if (!gather_vec(a.tx, B * H, tag(ph + 4), xin, NoPre())) { alive = false; break; }
+          if (!gather_stage<BT, 4 * BT>(a.tx, H, B, tag(ph + 4), Ly.post_norm, a.eps, xs, cc, red)) { alive = false; break; }
         }
         KMR_TRACE_MARK(tev + 6);
         float out[2 * NP][BT];
-        wave_dot<BT, 2 * NP, 1>(w, xin, H, B, gn, a.eps, out);
+        wave_dot<BT, 2 * NP, 1>(w, H, B, xs, cc, out);
         if (lane < B) {
 #pragma unroll
           for (int i = 0; i < NP; ++i)
@@ -768,11 +824,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
       WRows<NR, CPL> w;
       wrows_load(w, Ly.d_p, Ly.d_s, I, G, row, ok);
       if (r2 == 0) {
-        if (!gather_vec(a.tact, B * I, tag(ph + 5), xin, NoPre())) { alive = false; break; }
+        if (!gather_stage<BT, 12>(a.tact, I, B, tag(ph + 5), nullptr, a.eps, xs, cc, red)) { alive = false; break; }
       }
       KMR_TRACE_MARK(tev + 8);
       float out[NR][BT];
-      wave_dot<BT, NR, CPL>(w, xin, I, B, nullptr, a.eps, out);
+      wave_dot<BT, NR, CPL>(w, I, B, xs, cc, out);
       if (lane < B && ok[0]) {
         float v = out[0][0];
 #pragma unroll
