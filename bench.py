@@ -15,14 +15,19 @@ Prints one JSON line (see the README of the driver contract in the design doc).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "int4_weight_only_gemv_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "decode tok/s + achieved HBM GB/s (% of peak), int4 Qwen3-VL-2B shape, batch 1/4"
 
 
@@ -38,6 +43,57 @@ def algorithmic_bytes(dims, batch, cache_positions, with_lm=True):
     if with_lm:
         total += dims.vocab * H * 2 + H * 2 + batch * H * 2
     return total
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources (name + bytes, sorted): identifies the kernel
+    build that a stored counter summary was taken from."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".h", ".hip")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+PROFILE_TAG = {"step": "qwen3vl2b_b1", "batch4": "qwen3vl2b_b4"}
+
+
+def stored_traffic(workload_name):
+    """HBM bytes per launch of the step kernel from the committed rocprofv3 PMC
+    summary of this workload (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
+    calibration factor), or None when there is none or the kernel sources changed
+    since it was taken."""
+    path = os.path.join(PROFILES, f"k_step_{PROFILE_TAG[workload_name]}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^([a-z_0-9]+):\s*(\S+)", line.strip())
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib):
+    """A plain device copy of `mib` MiB (torch's copy kernel), launched three times,
+    for scaling the FETCH_SIZE / WRITE_SIZE counters of a PMC run."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def build(workload_name):
@@ -91,6 +147,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=["step", "batch4"], default="step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this decode step runs on a single MI355X and "
@@ -100,6 +158,8 @@ def main():
     import torch
     from int4_weight_only_gemv_amd import kmr, synth
 
+    if args.calibrate_copy_mib > 0:
+        copy_calibration(args.calibrate_copy_mib)
     w, model, kv, layers, glob = build(args.workload)
     inp = synth.step_inputs(w)
     B = w.batch
@@ -130,6 +190,20 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(stop) / args.steps
+    # The step kernel's own average launch duration: events on the launch stream
+    # right around each launch, in a second timed pass of the same steps.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    if advance:
+        ids[0].copy_(dev(inp["ids"])); pos.copy_(dev(inp["positions"]))
+        cpos.copy_(dev(inp["cache_position"])); fin.copy_(dev(inp["finished"]))
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     status = ws.status()
     if status:
         print(f"device status bits set: {status}", file=sys.stderr)
@@ -142,6 +216,7 @@ def main():
         cps = [int(c) for c in inp["cache_position"]]
     nbytes = algorithmic_bytes(w.dims, B, cps)
     gbps = nbytes / (ms * 1e-3) / 1e9
+    kernel_gbps = nbytes / (kernel_ms * 1e-3) / 1e9
     tok_s = active * 1000.0 / ms
     out = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1,
@@ -153,9 +228,13 @@ def main():
                    "max_len": w.max_len, "layers": w.dims.n_layers, "vocab": w.dims.vocab},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": nbytes, "wall_s_timed": round(wall, 4),
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "whole decode step (kmr_decode_step)"},
+        # One launch of the persistent step kernel per step (k_step: all layers,
+        # final norm, lm_head and argmax), so its algorithmic bytes per launch are
+        # the step's; its average launch duration comes from per-launch events.
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(args.workload),
+                     "kernel": "k_step", "launches_per_step": 1,
+                     "kernel_us_per_launch": round(kernel_ms * 1000, 1)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
