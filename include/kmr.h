@@ -57,19 +57,24 @@ enum {
                                  that row wrote nothing and its attention is zero */
   KMR_STATUS_TOKEN = 2u,      /* a token id was outside [0, vocab): that row's
                                  embedding was taken as zero */
-  KMR_STATUS_TIMEOUT = 4u     /* a wait inside the persistent step kernel gave up
+  KMR_STATUS_TIMEOUT = 4u,    /* a wait inside the persistent step kernel gave up
                                  (no progress for ~1 s): outputs of that call are
                                  invalid; re-initialise the workspace */
+  KMR_STATUS_TOPOLOGY = 8u    /* a work-group of the XCD-local step kernel found itself
+                                 on another XCD than the placement probe reported
+                                 (diagnostic; such a call may also time out) */
 };
 
 #define KMR_MAX_BATCH 16
 #define KMR_ADVANCE 1u
 #define KMR_MULTI_KERNEL 2u  /* run the step as one kernel per phase instead of the
                                 single persistent kernel (diagnostics, cross-checks) */
+#define KMR_DEVICE_WIDE 4u   /* persistent kernel with every hand-off device-wide,
+                                instead of the XCD-local one (diagnostics, cross-checks) */
 
 /*
  * Model dimensions.  Supported by the kernels: head_dim 64 or 128;
- * n_heads % n_kv_heads == 0 with n_heads / n_kv_heads <= 8; group_size a multiple
+ * n_heads % n_kv_heads == 0 with n_heads / n_kv_heads in {1, 2, 4}; group_size a multiple
  * of 32 dividing hidden, n_heads*head_dim and intermediate;
  * mrope_section[0]+[1]+[2] == head_dim / 2.  Anything else is KMR_ESHAPE.
  */
@@ -146,7 +151,9 @@ size_t kmr_workspace_bytes(const kmr_config* cfg, int32_t batch, int32_t max_len
 
 /* Clears a workspace with a fill kernel on `stream`.  Call once after allocating
  * it and again after any call that returned an error; the decode calls leave
- * it ready for the next call. */
+ * it ready for the next call.  The first call on a device also records where
+ * the device places the work-groups of a one-group-per-CU grid (a small probe
+ * kernel into the workspace and a synchronous copy of one word per CU). */
 int kmr_workspace_init(void* ws, size_t ws_bytes, kmr_stream_t stream);
 
 /*
@@ -179,7 +186,15 @@ int kmr_decode_layer(const kmr_config* cfg, const kmr_layer* layer_w, int32_t la
  *   marked finished (if `finished` is given); every other unfinished row gets
  *   cache_position[b] += 1 and all three positions += 1.  This lets the caller
  *   feed next_ids back as token_ids and replay the step with no host work.
- * Nothing is synchronised: next_ids is valid once `stream` reaches this point.
+ * Nothing is synchronised: next_ids is valid once `stream` reaches this point,
+ * except that a device's first decode call that picks the XCD-local persistent
+ * kernel runs the placement probe of kmr_workspace_init (synchronising `stream`
+ * once) if no kmr_workspace_init ran on that device; under stream capture the
+ * probe is skipped and the kernel keeps every hand-off device-wide.
+ * Paths: batch <= 4 with the model shapes the persistent kernels cover runs as one
+ * cooperative launch (XCD-local hand-offs when n_kv_heads is a multiple of 8, else
+ * or with KMR_DEVICE_WIDE device-wide ones); otherwise, or with KMR_MULTI_KERNEL,
+ * as one kernel per phase.
  */
 int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
                     const int32_t* token_ids, int32_t* positions, int32_t* cache_position,

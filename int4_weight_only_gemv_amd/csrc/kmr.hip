@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -13,12 +14,16 @@
 #include "kmr.h"
 #include "kmr_kernels.h"
 #include "kmr_step.h"
+#include "kmr_stepx.h"
 
 using namespace kmr;
 
 namespace {
 
 thread_local char g_err[512] = "";
+#ifdef KMR_TRACE
+uint64_t* g_trace = nullptr;   // diagnostic builds: phase timestamps of the step kernels
+#endif
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -69,6 +74,8 @@ constexpr int kMaxStepGroups = 1024;   // lm_head partial slots of the persisten
 struct WsLayout {
   size_t status, cs, x, qkv, attn_o, act, part_o, part_ml, lm_part, total;
   size_t step_ctr, lm_cnt, tx, tqkv, to, tact, tpart, lm_part2;
+  size_t lx, lqkv, lpart, lact, pO, pD, probe;
+  StepXSizes xz;
   int ns, nblk_lm;
 };
 
@@ -96,6 +103,16 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
   w.tact = o; o += align256((size_t)B * c->intermediate * 8);
   w.tpart = o; o += align256((size_t)B * Hkv * w.ns * qpg * (D + 2) * 8);
   w.lm_part2 = o; o += align256((size_t)B * kMaxStepGroups * 8);
+  // XCD-local step kernel: per-XCD regions, then the device-wide partials
+  o = (o + 4095) & ~(size_t)4095;
+  w.xz = stepx_sizes(B, c->hidden, Hkv, D, qpg, c->intermediate, M);
+  w.lx = o; o += (size_t)kXcds * w.xz.lx * 8;
+  w.lqkv = o; o += (size_t)kXcds * w.xz.lqkv * 8;
+  w.lpart = o; o += (size_t)kXcds * w.xz.lpart * 8;
+  w.lact = o; o += (size_t)kXcds * w.xz.lact * 8;
+  w.pO = o; o += align256((size_t)kXcds * B * c->hidden * 8);
+  w.pD = o; o += align256((size_t)kXcds * B * c->hidden * 8);
+  w.probe = o; o += align256((size_t)kMaxStepGroups * 4);
   w.total = o;
   return w;
 }
@@ -305,6 +322,51 @@ bool step_kernel_fits(const kmr_config* c, int B) {
          c->n_heads == 2 * c->n_kv_heads && c->vocab > 0;
 }
 
+// The XCD-local step kernel: shapes its fixed per-group work split covers.
+bool stepx_fits(const kmr_config* c, int B, int nwg) {
+  if (!step_kernel_fits(c, B) || nwg % kXcds != 0 || c->n_kv_heads % kXcds != 0) return false;
+  const int WPX = nwg / kXcds, D = c->head_dim, QPG = c->n_heads / c->n_kv_heads;
+  const int GPX = c->n_kv_heads / kXcds, QX = GPX * (QPG + 2) * D, OX = GPX * QPG * D;
+  if (c->intermediate % (kXcds * 32) != 0) return false;
+  const int IX = c->intermediate / kXcds, H = c->hidden;
+  const int RPW = (H + WPX - 1) / WPX, RQ = (QX + WPX - 1) / WPX, RA = (IX + WPX - 1) / WPX;
+  if (OX > 512 || OX > H || OX / 32 > 8 * kXNarrowCpl || IX > H || IX / 32 > 8 * kXNarrowCpl) return false;
+  if (RPW > 8 * kStepWaves || RQ > 2 * kStepWaves || RA > 3 * kStepWaves) return false;
+  // every group owns residual rows and act values (the hand-off order relies on it)
+  if (RPW * (WPX - 1) >= H || RA * (WPX - 1) >= IX) return false;
+  const size_t lds = stepx_lds(4, H, RPW, D, QPG, GPX).total;
+  return lds <= 160 * 1024;
+}
+
+__global__ void k_xcc_probe(uint32_t* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u;
+}
+
+// Whether work-group g of a one-group-per-CU grid runs on XCD g % 8 on the current
+// device: probed once per device (a small kernel on `st`, a synchronous copy of
+// nwg words through `scratch`), then cached.  Not probed while `st` is capturing.
+std::atomic<int> g_topology[64];   // 0 unknown, 1 verified, 2 other placement
+
+bool xcd_placement_ok(void* scratch, size_t scratch_bytes, int nwg, hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  const int known = g_topology[dev].load();
+  if (known) return known == 1;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return false;
+  if (nwg <= 0 || nwg > kMaxStepGroups || scratch_bytes < (size_t)nwg * 4) return false;
+  uint32_t ids[kMaxStepGroups];
+  hipLaunchKernelGGL(k_xcc_probe, dim3(nwg), dim3(64), 0, st, static_cast<uint32_t*>(scratch));
+  if (hipGetLastError() != hipSuccess) return false;
+  if (hipMemcpyAsync(ids, scratch, (size_t)nwg * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return false;
+  bool ok = nwg % kXcds == 0;
+  for (int g = 0; g < nwg && ok; ++g) ok = (int)(ids[g] % kXcds) == g % kXcds;
+  g_topology[dev].store(ok ? 1 : 2);
+  return ok;
+}
+
 int device_cus(int* cus) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return check_hip("hipGetDevice");
@@ -328,6 +390,27 @@ int launch_step_k(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
                                  args, (unsigned)lds, st) != hipSuccess)
     return check_hip("step kernel cooperative launch");
   return KMR_OK;
+}
+
+template <int BT, int D>
+int launch_stepx_k(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
+  const int WPX = nwg / kXcds, RPW = (c->hidden + WPX - 1) / WPX;
+  const size_t lds = stepx_lds(BT, c->hidden, RPW, D, 2, c->n_kv_heads / kXcds).total;
+  auto fn = k_stepx<BT, D, 2>;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds) != hipSuccess)
+    return check_hip("XCD step kernel LDS attribute");
+  void* args[] = {&a};
+  if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(nwg), dim3(kStepThreads),
+                                 args, (unsigned)lds, st) != hipSuccess)
+    return check_hip("XCD step kernel cooperative launch");
+  return KMR_OK;
+}
+
+int launch_stepx(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
+  const int B = a.B;
+  if (c->head_dim == 128) return B == 1 ? launch_stepx_k<1, 128>(c, a, nwg, st) : launch_stepx_k<4, 128>(c, a, nwg, st);
+  return B == 1 ? launch_stepx_k<1, 64>(c, a, nwg, st) : launch_stepx_k<4, 64>(c, a, nwg, st);
 }
 
 int launch_step(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
@@ -380,8 +463,7 @@ const char* kmr_last_error(void) { return g_err; }
 // Diagnostic builds only: route the step kernel's phase timestamps to `buf`
 // (uint64 [groups][64]); NULL turns tracing off.
 int kmr_debug_set_trace(void* buf) {
-  if (hipMemcpyToSymbol(HIP_SYMBOL(g_kmr_trace), &buf, sizeof(buf)) != hipSuccess)
-    return check_hip("trace symbol");
+  g_trace = static_cast<uint64_t*>(buf);
   return KMR_OK;
 }
 #endif
@@ -432,7 +514,10 @@ size_t kmr_workspace_bytes(const kmr_config* cfg, int32_t batch, int32_t max_len
 
 int kmr_workspace_init(void* ws, size_t ws_bytes, kmr_stream_t stream) {
   if (!ws || !ws_bytes) return fail(KMR_EINVAL, "workspace is NULL or empty");
-  fill_zero(ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int nwg = 0;
+  if (device_cus(&nwg) == KMR_OK) xcd_placement_ok(ws, ws_bytes, nwg, st);
+  fill_zero(ws, ws_bytes, st);
   return check_hip("workspace init");
 }
 
@@ -472,7 +557,7 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
   if (kv->n_layers != cfg->n_layers) return fail(KMR_ESHAPE, "kv cache has %d layers, model %d", kv->n_layers, cfg->n_layers);
   if (!token_ids || !positions || !cache_position || !next_ids || !ws)
     return fail(KMR_EINVAL, "null token_ids/positions/cache_position/next_ids/workspace");
-  if (flags & ~(KMR_ADVANCE | KMR_MULTI_KERNEL)) return fail(KMR_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(KMR_ADVANCE | KMR_MULTI_KERNEL | KMR_DEVICE_WIDE)) return fail(KMR_EINVAL, "unknown flags 0x%x", flags);
   const WsLayout w = ws_layout(cfg, batch, kv->max_len);
   if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -492,6 +577,13 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
     a.to = at<uint64_t>(ws, w.to); a.tact = at<uint64_t>(ws, w.tact);
     a.tpart = at<uint64_t>(ws, w.tpart);
     a.lm_part = at<float2>(ws, w.lm_part2);
+#ifdef KMR_TRACE
+    a.trace = g_trace;
+#endif
+    a.lx = at<uint64_t>(ws, w.lx); a.lqkv = at<uint64_t>(ws, w.lqkv);
+    a.lpart = at<uint64_t>(ws, w.lpart); a.lact = at<uint64_t>(ws, w.lact);
+    a.pO = at<uint64_t>(ws, w.pO); a.pD = at<uint64_t>(ws, w.pD);
+    a.x_lx = w.xz.lx; a.x_lqkv = w.xz.lqkv; a.x_lpart = w.xz.lpart; a.x_lact = w.xz.lact;
     a.B = batch; a.H = cfg->hidden; a.Hq = cfg->n_heads; a.Hkv = cfg->n_kv_heads;
     a.I = cfg->intermediate; a.V = cfg->vocab; a.L = cfg->n_layers; a.G = cfg->group_size;
     a.M = kv->max_len; a.cacheB = kv->batch; a.NS = w.ns; a.pad_id = cfg->pad_id;
@@ -511,6 +603,10 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
       d.o_p = static_cast<const uint8_t*>(L.o.packed); d.o_s = static_cast<const uint32_t*>(L.o.sz);
       d.gu_p = static_cast<const uint8_t*>(L.gate_up.packed); d.gu_s = static_cast<const uint32_t*>(L.gate_up.sz);
       d.d_p = static_cast<const uint8_t*>(L.down.packed); d.d_s = static_cast<const uint32_t*>(L.down.sz);
+    }
+    if (!(flags & KMR_DEVICE_WIDE) && stepx_fits(cfg, batch, nwg)) {
+      a.intra_plain = xcd_placement_ok(at<void>(ws, w.probe), (size_t)kMaxStepGroups * 4, nwg, st) ? 1 : 0;
+      return launch_stepx(cfg, a, nwg, st);
     }
     return launch_step(cfg, a, nwg, st);
   }

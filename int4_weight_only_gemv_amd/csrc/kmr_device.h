@@ -40,6 +40,10 @@ __device__ __forceinline__ float row16_sum(float v) {
 __device__ __forceinline__ float row16_swap8(float v) { return dpp<0x128>(v); }
 
 // Sum over the 64-lane wave, returned uniform (from lane 63).
+// 1/sqrt(x) with the hardware reciprocal square root (within 1 ulp); used for
+// RMSNorm scales, whose inputs are at least epsilon.
+__device__ __forceinline__ float rsqrt_f(float x) { return __builtin_amdgcn_rsqf(x); }
+
 __device__ __forceinline__ float wave_sum(float v) {
   v = row16_sum(v);
   v += dpp<0x142, 0xa>(v);  // row_bcast 15 into rows 1 and 3

@@ -31,6 +31,9 @@
 
 namespace kmr {
 
+#ifndef KMR_POLL_SLEEP
+#define KMR_POLL_SLEEP 2   // s_sleep units (64 clocks) between polls of a tagged buffer
+#endif
 constexpr int kStepThreads = 512;
 constexpr int kStepWaves = kStepThreads / 64;
 constexpr int kMaxStepLayers = 32;
@@ -40,11 +43,11 @@ constexpr int kMergeChunk = 16;   // attention splits merged per gather
 
 #ifdef KMR_TRACE
 // Diagnostic builds only: per-group timestamps of phase boundaries.
-__device__ uint64_t* g_kmr_trace = nullptr;
+// (a.trace is a kernel argument: recording a mark waits on nothing but the clock)
 #define KMR_TRACE_MARK(ev)                                                              \
   do {                                                                                   \
-    if (g_kmr_trace && threadIdx.x == 0 && (ev) < 64)                                    \
-      g_kmr_trace[(size_t)blockIdx.x * 64 + (ev)] = wall_clock64();                      \
+    if (a.trace && threadIdx.x == 0 && (ev) < 64)                                        \
+      a.trace[(size_t)blockIdx.x * 64 + (ev)] = wall_clock64();                          \
   } while (0)
 #else
 #define KMR_TRACE_MARK(ev) do { } while (0)
@@ -78,9 +81,20 @@ struct StepArgs {
   uint64_t* tact;           // [B][I]
   uint64_t* tpart;          // [B][Hkv][NS][QPG][D+2]  split partials (o~, m, l)
   float2* lm_part;          // [B][nwg]
+  // XCD-local exchange buffers (k_stepx only); "per XCD" regions are strided by
+  // the x_* strides (in 64-bit words)
+  uint64_t* lx;             // per XCD [B][H]          residual stream copy
+  uint64_t* lqkv;           // per XCD [B][QX]         q/k/v of the XCD's kv heads
+  uint64_t* lpart;          // per XCD [B][GPX][NSX][PW] attention split partials
+  uint64_t* lact;           // per XCD [B][IX]         SiLU(gate)*up of the XCD's slice
+  uint64_t* pO;             // [NX][B][H]              O split-K partials
+  uint64_t* pD;             // [NX][B][H]              down split-K partials
+  long long x_lx, x_lqkv, x_lpart, x_lact;
+  int intra_plain;          // 1: XCD-local stores stay in the XCD's L2 (placement verified)
   // dims
   int B, H, Hq, Hkv, I, V, L, G, M, cacheB, NS, pad_id, eos_id;
   uint32_t flags;
+  uint64_t* trace;          // per-group phase timestamps (diagnostic builds only) or null
   float eps, scale_log2;
   double theta;
   int sec0, sec1, sec2, interleaved;
@@ -143,7 +157,7 @@ __device__ __forceinline__ bool gather_tagged(const uint64_t* src, int total, ui
         if (idx[j] < total) fresh &= (uint32_t)(v[j] >> 32) == tag;
       if (!fresh) {
         if (++spins > kSpinLimit) { ok = false; break; }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(KMR_POLL_SLEEP);
       }
     } while (!fresh);
     if (ok)
@@ -180,28 +194,59 @@ __device__ __forceinline__ float lane_xor4(float v) {
   return (threadIdx.x & 4) ? dn : up;
 }
 
+// Converts this thread's PT values of a [B][K] input (value j is element
+// base + 512 j + tid, row wb[j], column wk[j]) into the LDS layout the dot
+// products read: xs[(b*4 + w)*CH + c] holds the fp16 pairs of word w (8 columns)
+// of 32-column chunk c, and cc[b*CH + c] its (C1, C2) = (1024 sum h + 8 sum x,
+// sum x) over the values actually used (odd columns pre-divided by 16, matching
+// the magic-bias weight pairs).  An 8-column word lives in 8 consecutive lanes
+// (pairs formed with lane ^ 4), a 32-column chunk in 32 consecutive lanes, so K
+// must be a multiple of 32.  Every lane of the wave must call this (DPP).
+template <int PT>
+__device__ __forceinline__ void stage_values(const float (&e)[PT], const bool (&has)[PT],
+                                             const int (&wb)[PT], const int (&wk)[PT], int K,
+                                             uint4* xs, float2* cc) {
+  const int lane = threadIdx.x & 63, CH = K >> 5, i8 = lane & 7;
+  uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
+#pragma unroll
+  for (int j = 0; j < PT; ++j) {
+    const _Float16 h = (_Float16)((i8 & 1) ? e[j] * 0.0625f : e[j]);
+    const float hf = (float)h;
+    const float uf = (i8 & 1) ? 16.0f * hf : hf;
+    const float other = lane_xor4(hf);
+    // chunk sums over the 32 lanes of the chunk
+    float bs = row16_sum(hf), us = row16_sum(uf), blo, bhi, ulo, uhi;
+    lane_pair<16>(bs, blo, bhi);
+    lane_pair<16>(us, ulo, uhi);
+    if (has[j]) {
+      const int c = wk[j] >> 5, w = (wk[j] >> 3) & 3;
+      if (i8 < 4)
+        xs32[((wb[j] * 4 + w) * CH + c) * 4 + i8] =
+            __builtin_bit_cast(uint32_t, half2_t{h, (_Float16)other});
+      if ((lane & 31) == 0) {
+        const float bsum = blo + bhi, usum = ulo + uhi;
+        cc[wb[j] * CH + c] = make_float2(1024.0f * bsum + 8.0f * usum, usum);
+      }
+    }
+  }
+}
+
 // Gathers a tagged [B][K] input (PT words per thread per pass, consecutive lanes
 // polling consecutive words), optionally RMS-normalises it with `gain`, and
-// converts it once per work-group into the LDS layout the dot products read:
-// xs[(b*4 + w)*CH + c] holds the fp16 pairs of word w (8 columns) of 32-column
-// chunk c, and cc[b*CH + c] its (C1, C2) = (1024 sum h + 8 sum x, sum x) over the
-// values actually used (odd columns pre-divided by 16, matching the magic-bias
-// weight pairs).  An 8-column word lives in 8 consecutive lanes (pairs formed
-// with lane ^ 4), a 32-column chunk in 32 consecutive lanes.
+// stages it with stage_values.
 template <int BT, int PT>
 __device__ __forceinline__ bool gather_stage(const uint64_t* src, int K, int B, uint32_t tag,
                                              const uint16_t* gain, float eps, uint4* xs, float2* cc,
                                              float* red) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int CH = K >> 5, total = B * K;
-  uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int total = B * K;
   float inv[BT];
 #pragma unroll
   for (int b = 0; b < BT; ++b) inv[b] = 1.f;
   for (int base = 0; base < total; base += kStepThreads * PT) {
     int idx[PT], wb[PT], wk[PT];
     bool has[PT];
-    float gv[PT];
+    uint16_t graw[PT];
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       idx[j] = base + kStepThreads * j + tid;
@@ -210,7 +255,12 @@ __device__ __forceinline__ bool gather_stage(const uint64_t* src, int K, int B, 
 #pragma unroll
       for (int b = 1; b < BT; ++b) wb[j] += idx[j] >= b * K ? 1 : 0;
       wk[j] = idx[j] - wb[j] * K;
-      gv[j] = (gain && has[j]) ? bf16_to_f32(gain[wk[j]]) : 1.f;
+    }
+    if (gain) {
+      // raw loads with in-range addresses and no use before the polls below, so
+      // nothing waits on them until the values are needed
+#pragma unroll
+      for (int j = 0; j < PT; ++j) graw[j] = gain[wk[j] < K ? wk[j] : K - 1];
     }
     uint64_t v[PT];
     uint32_t spins = 0;
@@ -225,7 +275,7 @@ __device__ __forceinline__ bool gather_stage(const uint64_t* src, int K, int B, 
         if (has[j]) fresh &= (uint32_t)(v[j] >> 32) == tag;
       if (!fresh) {
         if (++spins > kSpinLimit) { ok = false; break; }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(KMR_POLL_SLEEP);
       }
     } while (!fresh);
     if (__syncthreads_or(!ok)) return false;
@@ -249,35 +299,18 @@ __device__ __forceinline__ bool gather_stage(const uint64_t* src, int K, int B, 
         float ss = 0.f;
 #pragma unroll
         for (int w = 0; w < kStepWaves; ++w) ss += red[b * kStepWaves + w];
-        inv[b] = 1.0f / sqrtf(ss / (float)K + eps);
+        inv[b] = rsqrt_f(ss / (float)K + eps);
       }
     }
-    const int i8 = lane & 7;   // column within the 8-column word
+    float e[PT];
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       float iv = inv[0];
 #pragma unroll
       for (int b = 1; b < BT; ++b) if (wb[j] == b) iv = inv[b];
-      const float e = gain ? (x[j] * iv) * gv[j] : x[j];
-      const _Float16 h = (_Float16)((i8 & 1) ? e * 0.0625f : e);
-      const float hf = (float)h;
-      const float uf = (i8 & 1) ? 16.0f * hf : hf;
-      const float other = lane_xor4(hf);
-      // chunk sums over the 32 lanes of the chunk
-      float bs = row16_sum(hf), us = row16_sum(uf), blo, bhi, ulo, uhi;
-      lane_pair<16>(bs, blo, bhi);
-      lane_pair<16>(us, ulo, uhi);
-      if (has[j]) {
-        const int c = wk[j] >> 5, w = (wk[j] >> 3) & 3;
-        if (i8 < 4)
-          xs32[((wb[j] * 4 + w) * CH + c) * 4 + i8] =
-              __builtin_bit_cast(uint32_t, half2_t{h, (_Float16)other});
-        if ((lane & 31) == 0) {
-          const float bsum = blo + bhi, usum = ulo + uhi;
-          cc[wb[j] * CH + c] = make_float2(1024.0f * bsum + 8.0f * usum, usum);
-        }
-      }
+      e[j] = gain ? (x[j] * iv) * bf16_to_f32(graw[j]) : x[j];
     }
+    stage_values<PT>(e, has, wb, wk, K, xs, cc);
   }
   __syncthreads();
   return true;
@@ -397,7 +430,7 @@ __device__ __forceinline__ void norm_rope(float (&vals)[DPL], const float (&gain
 #pragma unroll
   for (int e = 0; e < DPL; ++e) ss += vals[e] * vals[e];
   ss = row16_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+  const float inv = rsqrt_f(ss / (float)D + eps);
 #pragma unroll
   for (int e = 0; e < DPL; ++e) vals[e] = (vals[e] * inv) * gain[e];
   float other[DPL];
@@ -450,11 +483,172 @@ __host__ __device__ inline StepLds step_lds(int BT, int KMAX, int RPBX, int H, i
   return s;
 }
 
+// Final RMSNorm, lm_head rows of this group with the argmax of each batch row,
+// and (in the last group to finish) the argmax over all groups, the greedy-step
+// bookkeeping and the step counter.  xin holds the gathered fp32 [B][H] input.
+template <int BT>
+__device__ __forceinline__ void step_tail(const StepArgs& a, float* xin, float* red, int* s_last_p,
+                                          uint32_t step) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int B = a.B, M = a.M, K = a.H;
+  int& s_last = *s_last_p;
+  {
+    // h = RMSNorm(x; final_norm), same association order as k_lmhead
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      float ss = 0.f;
+      if (tid < 256 && b < B)
+        for (int k = tid * 4; k < K; k += 1024) {
+          const float4 v = *reinterpret_cast<const float4*>(xin + b * K + k);
+          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+      ss = wave_sum(ss);
+      if ((tid & 63) == 0 && tid < 256) red[b * 4 + (tid >> 6)] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      const float ss = (red[b * 4 + 0] + red[b * 4 + 1]) + (red[b * 4 + 2] + red[b * 4 + 3]);
+      const float inv = rsqrt_f(ss / (float)K + a.eps);
+      for (int k = tid; k < K; k += kStepThreads)
+        xin[b * K + k] = b < B ? (xin[b * K + k] * inv) * bf16_to_f32(a.final_norm[k]) : 0.f;
+    }
+    __syncthreads();
+  }
+  constexpr int LR = 4;            // rows per wave per pass
+  constexpr int LCPL = 4;          // 8-column chunks per lane (K <= 2048)
+  const int RPBL = (a.V + nwg - 1) / nwg;
+  const int CH8 = K >> 3;
+  float bv[BT]; int bi[BT];
+#pragma unroll
+  for (int b = 0; b < BT; ++b) { bv[b] = -INFINITY; bi[b] = 0x7fffffff; }
+  for (int r0 = wave * LR; r0 < RPBL; r0 += kStepWaves * LR) {
+    uint4 w[LR][LCPL];
+#pragma unroll
+    for (int r = 0; r < LR; ++r)
+#pragma unroll
+      for (int j = 0; j < LCPL; ++j) {
+        const int rr = r0 + r, n = wg * RPBL + rr, c = lane + 64 * j;
+        w[r][j] = (rr < RPBL && n < a.V && c < CH8) ? load_stream16(a.lm_head + (size_t)n * K + 8 * c)
+                                                    : make_uint4(0, 0, 0, 0);
+      }
+    float acc[LR][BT];
+#pragma unroll
+    for (int r = 0; r < LR; ++r)
+#pragma unroll
+      for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
+#pragma unroll
+    for (int j = 0; j < LCPL; ++j) {
+      const int c = lane + 64 * j;
+      if (c < CH8) {
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          const float4 h0 = *reinterpret_cast<const float4*>(xin + b * K + 8 * c);
+          const float4 h1 = *reinterpret_cast<const float4*>(xin + b * K + 8 * c + 4);
+#pragma unroll
+          for (int r = 0; r < LR; ++r) {
+            float t = acc[r][b];
+            t += bf16_lo(w[r][j].x) * h0.x; t += bf16_hi(w[r][j].x) * h0.y;
+            t += bf16_lo(w[r][j].y) * h0.z; t += bf16_hi(w[r][j].y) * h0.w;
+            t += bf16_lo(w[r][j].z) * h1.x; t += bf16_hi(w[r][j].z) * h1.y;
+            t += bf16_lo(w[r][j].w) * h1.z; t += bf16_hi(w[r][j].w) * h1.w;
+            acc[r][b] = t;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < LR; ++r) {
+      const int rr = r0 + r, n = wg * RPBL + rr;
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        const float v = wave_sum(acc[r][b]);
+        if (rr < RPBL && n < a.V && b < B) {
+          if (a.logits && lane == 0) a.logits[(size_t)b * a.V + n] = v;
+          if (better(v, n, bv[b], bi[b])) { bv[b] = v; bi[b] = n; }
+        }
+      }
+    }
+  }
+  KMR_TRACE_MARK(57);
+  float* s_bv = red;                                  // [8][BT]
+  int* s_bi = reinterpret_cast<int*>(red + 64);       // [8][BT]
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int b = 0; b < BT; ++b) { s_bv[wave * BT + b] = bv[b]; s_bi[wave * BT + b] = bi[b]; }
+  }
+  __syncthreads();
+  if (tid < B) {
+    float v = s_bv[tid];
+    int i = s_bi[tid];
+    for (int w2 = 1; w2 < kStepWaves; ++w2)
+      if (better(s_bv[w2 * BT + tid], s_bi[w2 * BT + tid], v, i)) { v = s_bv[w2 * BT + tid]; i = s_bi[w2 * BT + tid]; }
+    st_devf(&a.lm_part[(size_t)tid * nwg + wg].x, v);
+    st_devf(&a.lm_part[(size_t)tid * nwg + wg].y, __int_as_float(i));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(a.lm_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (uint32_t)(nwg - 1);
+  }
+  __syncthreads();
+  KMR_TRACE_MARK(58);
+  if (!s_last) return;
+  // last group: argmax over all groups' partials (fixed tree order), then the
+  // greedy-step bookkeeping, then the step counter
+  float* t_v = xin;
+  int* t_i = reinterpret_cast<int*>(xin + kStepThreads);
+  for (int b = 0; b < B; ++b) {
+    float v = -INFINITY;
+    int i = 0x7fffffff;
+    for (int t = tid; t < nwg; t += kStepThreads) {
+      const float pv = ld_devf(&a.lm_part[(size_t)b * nwg + t].x);
+      const int pi = __float_as_int(ld_devf(&a.lm_part[(size_t)b * nwg + t].y));
+      if (better(pv, pi, v, i)) { v = pv; i = pi; }
+    }
+    __syncthreads();
+    t_v[tid] = v;
+    t_i[tid] = i;
+    __syncthreads();
+    for (int wdt = kStepThreads / 2; wdt > 0; wdt >>= 1) {
+      if (tid < wdt && better(t_v[tid + wdt], t_i[tid + wdt], t_v[tid], t_i[tid])) {
+        t_v[tid] = t_v[tid + wdt];
+        t_i[tid] = t_i[tid + wdt];
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      const int best = t_i[0];
+      const int fin = a.finished ? a.finished[b] : 0;
+      a.next[b] = fin ? a.pad_id : best;
+      if ((a.flags & 1u) && !fin) {
+        if (a.eos_id >= 0 && best == a.eos_id) {
+          if (a.finished) a.finished[b] = 1;
+        } else if (a.cpos[b] + 1 >= M) {
+          if (a.finished) a.finished[b] = 1;
+        } else {
+          a.cpos[b] += 1;
+          a.pos[0 * B + b] += 1;
+          a.pos[1 * B + b] += 1;
+          a.pos[2 * B + b] += 1;
+        }
+      }
+    }
+  }
+  if (tid == 0) {
+    __hip_atomic_store(a.lm_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.step_ctr[0] = step;
+  }
+}
+
 template <int BT, int D, int QPG>
 __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int DPL = D / 16, HALF = D / 2, PW = QPG * (D + 2);   // partial words per split
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x, nwg = gridDim.x;
   const int B = a.B, H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, G = a.G, M = a.M;
   const int NQKV = (Hq + 2 * Hkv) * D, QD = Hq * D;
@@ -862,155 +1056,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
     }
   }
   KMR_TRACE_MARK(56);
-  {
-    // h = RMSNorm(x; final_norm), same association order as k_lmhead
-#pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      float ss = 0.f;
-      if (tid < 256 && b < B)
-        for (int k = tid * 4; k < K; k += 1024) {
-          const float4 v = *reinterpret_cast<const float4*>(xin + b * K + k);
-          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        }
-      ss = wave_sum(ss);
-      if ((tid & 63) == 0 && tid < 256) red[b * 4 + (tid >> 6)] = ss;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      const float ss = (red[b * 4 + 0] + red[b * 4 + 1]) + (red[b * 4 + 2] + red[b * 4 + 3]);
-      const float inv = 1.0f / sqrtf(ss / (float)K + a.eps);
-      for (int k = tid; k < K; k += kStepThreads)
-        xin[b * K + k] = b < B ? (xin[b * K + k] * inv) * bf16_to_f32(a.final_norm[k]) : 0.f;
-    }
-    __syncthreads();
-  }
-  constexpr int LR = 4;            // rows per wave per pass
-  constexpr int LCPL = 4;          // 8-column chunks per lane (K <= 2048)
-  const int RPBL = (a.V + nwg - 1) / nwg;
-  const int CH8 = K >> 3;
-  float bv[BT]; int bi[BT];
-#pragma unroll
-  for (int b = 0; b < BT; ++b) { bv[b] = -INFINITY; bi[b] = 0x7fffffff; }
-  for (int r0 = wave * LR; r0 < RPBL; r0 += kStepWaves * LR) {
-    uint4 w[LR][LCPL];
-#pragma unroll
-    for (int r = 0; r < LR; ++r)
-#pragma unroll
-      for (int j = 0; j < LCPL; ++j) {
-        const int rr = r0 + r, n = wg * RPBL + rr, c = lane + 64 * j;
-        w[r][j] = (rr < RPBL && n < a.V && c < CH8) ? load_stream16(a.lm_head + (size_t)n * K + 8 * c)
-                                                    : make_uint4(0, 0, 0, 0);
-      }
-    float acc[LR][BT];
-#pragma unroll
-    for (int r = 0; r < LR; ++r)
-#pragma unroll
-      for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
-#pragma unroll
-    for (int j = 0; j < LCPL; ++j) {
-      const int c = lane + 64 * j;
-      if (c < CH8) {
-#pragma unroll
-        for (int b = 0; b < BT; ++b) {
-          const float4 h0 = *reinterpret_cast<const float4*>(xin + b * K + 8 * c);
-          const float4 h1 = *reinterpret_cast<const float4*>(xin + b * K + 8 * c + 4);
-#pragma unroll
-          for (int r = 0; r < LR; ++r) {
-            float t = acc[r][b];
-            t += bf16_lo(w[r][j].x) * h0.x; t += bf16_hi(w[r][j].x) * h0.y;
-            t += bf16_lo(w[r][j].y) * h0.z; t += bf16_hi(w[r][j].y) * h0.w;
-            t += bf16_lo(w[r][j].z) * h1.x; t += bf16_hi(w[r][j].z) * h1.y;
-            t += bf16_lo(w[r][j].w) * h1.z; t += bf16_hi(w[r][j].w) * h1.w;
-            acc[r][b] = t;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < LR; ++r) {
-      const int rr = r0 + r, n = wg * RPBL + rr;
-#pragma unroll
-      for (int b = 0; b < BT; ++b) {
-        const float v = wave_sum(acc[r][b]);
-        if (rr < RPBL && n < a.V && b < B) {
-          if (a.logits && lane == 0) a.logits[(size_t)b * a.V + n] = v;
-          if (better(v, n, bv[b], bi[b])) { bv[b] = v; bi[b] = n; }
-        }
-      }
-    }
-  }
-  KMR_TRACE_MARK(57);
-  float* s_bv = red;                                  // [8][BT]
-  int* s_bi = reinterpret_cast<int*>(red + 64);       // [8][BT]
-  __syncthreads();
-  if (lane == 0) {
-#pragma unroll
-    for (int b = 0; b < BT; ++b) { s_bv[wave * BT + b] = bv[b]; s_bi[wave * BT + b] = bi[b]; }
-  }
-  __syncthreads();
-  if (tid < B) {
-    float v = s_bv[tid];
-    int i = s_bi[tid];
-    for (int w2 = 1; w2 < kStepWaves; ++w2)
-      if (better(s_bv[w2 * BT + tid], s_bi[w2 * BT + tid], v, i)) { v = s_bv[w2 * BT + tid]; i = s_bi[w2 * BT + tid]; }
-    st_devf(&a.lm_part[(size_t)tid * nwg + wg].x, v);
-    st_devf(&a.lm_part[(size_t)tid * nwg + wg].y, __int_as_float(i));
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(a.lm_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (uint32_t)(nwg - 1);
-  }
-  __syncthreads();
-  KMR_TRACE_MARK(58);
-  if (!s_last) return;
-  // last group: argmax over all groups' partials (fixed tree order), then the
-  // greedy-step bookkeeping, then the step counter
-  float* t_v = xin;
-  int* t_i = reinterpret_cast<int*>(xin + kStepThreads);
-  for (int b = 0; b < B; ++b) {
-    float v = -INFINITY;
-    int i = 0x7fffffff;
-    for (int t = tid; t < nwg; t += kStepThreads) {
-      const float pv = ld_devf(&a.lm_part[(size_t)b * nwg + t].x);
-      const int pi = __float_as_int(ld_devf(&a.lm_part[(size_t)b * nwg + t].y));
-      if (better(pv, pi, v, i)) { v = pv; i = pi; }
-    }
-    __syncthreads();
-    t_v[tid] = v;
-    t_i[tid] = i;
-    __syncthreads();
-    for (int wdt = kStepThreads / 2; wdt > 0; wdt >>= 1) {
-      if (tid < wdt && better(t_v[tid + wdt], t_i[tid + wdt], t_v[tid], t_i[tid])) {
-        t_v[tid] = t_v[tid + wdt];
-        t_i[tid] = t_i[tid + wdt];
-      }
-      __syncthreads();
-    }
-    if (tid == 0) {
-      const int best = t_i[0];
-      const int fin = a.finished ? a.finished[b] : 0;
-      a.next[b] = fin ? a.pad_id : best;
-      if ((a.flags & 1u) && !fin) {
-        if (a.eos_id >= 0 && best == a.eos_id) {
-          if (a.finished) a.finished[b] = 1;
-        } else if (a.cpos[b] + 1 >= M) {
-          if (a.finished) a.finished[b] = 1;
-        } else {
-          a.cpos[b] += 1;
-          a.pos[0 * B + b] += 1;
-          a.pos[1 * B + b] += 1;
-          a.pos[2 * B + b] += 1;
-        }
-      }
-    }
-  }
-  if (tid == 0) {
-    __hip_atomic_store(a.lm_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.step_ctr[0] = step;
-  }
+  step_tail<BT>(a, xin, red, &s_last, step);
 }
 
 }  // namespace kmr

@@ -1,0 +1,718 @@
+// kmr_stepx.h -- the persistent decode step with XCD-local exchanges.
+//
+// Same computation as k_step (kaminari page, section 04 "3 . decode": one greedy
+// token per row from fixed-rank inputs and the static KV buffers), arranged
+// around the chip's 8 XCDs instead of treating the 256 work-groups as one pool.
+// Work-group g runs on XCD g % 8 (checked on the host before this kernel is
+// chosen, and again by every group, which raises a status bit on a mismatch);
+// the 32 groups of one XCD share its L2, where a hand-off costs about half of a
+// device-wide one.  Per layer, with XCD x owning kv heads [x*GPX, (x+1)*GPX) and
+// the intermediate slice [x*IX, (x+1)*IX):
+//   QKV      every XCD holds the whole residual stream x; its groups compute the
+//            q/k/v rows of its own kv heads                       (XCD-local)
+//   attn     split-KV items (row, kv head, 128-position split) of those heads,
+//            partials published inside the XCD                    (XCD-local)
+//   O        every group merges all split partials of its XCD (log-sum-exp, the
+//            merge of "The Ghost in the Batch", "The merge math"), then computes
+//            its RPW rows of W_o over the XCD's head columns only (split-K)
+//   RS_O     each group sums the 8 XCD partials of its RPW rows (fixed order),
+//            adds them to its residual rows, and publishes them   (device-wide)
+//   GU       gate/up rows of the XCD's intermediate slice         (XCD-local x)
+//   down     W_down rows of the group over the XCD's slice columns (split-K,
+//            XCD-local act), then RS_D as RS_O                    (device-wide)
+// so two of the six hand-offs of a layer cross XCDs.  Every XCD keeps its own
+// bit-identical copy of the residual stream: the same sums in the same order.
+#pragma once
+
+#include "kmr_step.h"
+
+namespace kmr {
+
+constexpr int kXcds = 8;            // XCDs of the device; group g runs on XCD g % 8
+constexpr int kXSplit = 128;        // attention positions per split item
+constexpr int kXMergeChunk = 8;     // split partials merged per LDS pass
+constexpr int kXNarrowCpl = 3;      // max 32-column chunks per lane in the split-K GEMVs
+constexpr uint32_t kStatusTopology = 8u;
+
+// Store of a tagged word that only groups of this XCD read.  A work-group-scope
+// store stays in the XCD's L2, where the device-scope polls of the XCD's other
+// groups find it; without verified placement the device-scope store is used,
+// which every group sees wherever it runs.
+__device__ __forceinline__ void publish_l(uint64_t* p, uint32_t tag, float v, int plain) {
+  const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
+  if (plain)
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else
+    st_dev64(p, w);
+}
+
+// ------------------------------------------------------------------ split-K GEMV
+// One weight row per 8-lane group, restricted to a KS-column slice: lane
+// (lane & 7) of the group takes 32-column chunks (lane & 7) + 8 t, t < kXNarrowCpl.
+struct WNarrow {
+  uint4 raw[kXNarrowCpl];
+  uint32_t sz[kXNarrowCpl];
+};
+
+__device__ __forceinline__ void wnarrow_load(WNarrow& w, const uint8_t* packed, const uint32_t* sz,
+                                             int K, int G, int k0, int KS, int row, bool ok) {
+  const int sub = threadIdx.x & 7, CHs = KS >> 5, NG = K / G;
+#pragma unroll
+  for (int t = 0; t < kXNarrowCpl; ++t) {
+    const int c = sub + 8 * t;
+    if (ok && c < CHs) {
+      w.raw[t] = load_stream16(packed + (size_t)row * (K / 2) + (k0 >> 1) + 16 * c);
+      w.sz[t] = sz[(size_t)row * NG + (k0 + 32 * c) / G];
+    } else {
+      w.raw[t] = make_uint4(0, 0, 0, 0);
+      w.sz[t] = 0;
+    }
+  }
+}
+
+// out[b] = dot of the group's row with staged input row b over the slice; every
+// lane of the 8-lane group receives the sums.
+template <int BT>
+__device__ __forceinline__ void narrow_dot(const WNarrow& w, int KS, int B, const uint4* xs,
+                                           const float2* cc, float (&out)[BT]) {
+  const int sub = threadIdx.x & 7, CHs = KS >> 5;
+  float acc[BT];
+#pragma unroll
+  for (int b = 0; b < BT; ++b) acc[b] = 0.f;
+#pragma unroll
+  for (int t = 0; t < kXNarrowCpl; ++t) {
+    const int c = sub + 8 * t;
+    if (c < CHs) {
+      uint32_t p[16];
+      dequant16(w.raw[t], p);
+      const float s = bf16_lo(w.sz[t]), z = bf16_hi(w.sz[t]);
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        if (b >= B) break;
+        uint4 xv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[q] = xs[(b * 4 + q) * CHs + c];
+        const float2 C = cc[b * CHs + c];
+        float d = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          d = fdot2(p[4 * q + 0], xv[q].x, d);
+          d = fdot2(p[4 * q + 1], xv[q].y, d);
+          d = fdot2(p[4 * q + 2], xv[q].z, d);
+          d = fdot2(p[4 * q + 3], xv[q].w, d);
+        }
+        acc[b] += s * (d - C.x) + z * C.y;
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+    float v = acc[b];
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+    v += lane_xor4(v);
+    out[b] = v;
+  }
+}
+
+// ------------------------------------------------------------------ reduce-scatter
+// Sums the kXcds split-K partials of this group's RPW residual rows in XCD order
+// 0..7, adds the sum to the owned rows, and publishes the new rows to this XCD's
+// copy of the residual stream.  Returns false, for the whole group, on timeout.
+__device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag, int B, int H,
+                                            int RPW, int row0, float* xown, float* buf,
+                                            uint64_t* lxx, uint32_t xtag, int plain) {
+  constexpr int PT = 4;
+  const int tid = threadIdx.x, per = B * RPW, words = kXcds * per;
+  bool ok = true;
+  for (int base = 0; base < words && ok; base += kStepThreads * PT) {
+    uint64_t v[PT];
+    uint32_t off[PT];
+    bool has[PT];
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int i = base + kStepThreads * q + tid;
+      const int y = i / per, rem = i - y * per, b = rem / RPW, r = rem - b * RPW;
+      has[q] = i < words && row0 + r < H;
+      off[q] = has[q] ? (uint32_t)((y * B + b) * H + row0 + r) : 0u;
+    }
+    uint32_t spins = 0;
+    bool fresh;
+    do {
+#pragma unroll
+      for (int q = 0; q < PT; ++q)
+        if (has[q]) v[q] = ld_dev64(part + off[q]);
+      fresh = true;
+#pragma unroll
+      for (int q = 0; q < PT; ++q)
+        if (has[q]) fresh &= (uint32_t)(v[q] >> 32) == ptag;
+      if (!fresh) {
+        if (++spins > kSpinLimit) { ok = false; break; }
+        __builtin_amdgcn_s_sleep(KMR_POLL_SLEEP);
+      }
+    } while (!fresh);
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int i = base + kStepThreads * q + tid;
+      if (i < words) buf[i] = has[q] ? __uint_as_float((uint32_t)v[q]) : 0.f;
+    }
+  }
+  if (__syncthreads_or(!ok)) return false;
+  for (int i = tid; i < per; i += kStepThreads) {
+    const int b = i / RPW, r = i - b * RPW, n = row0 + r;
+    if (n >= H) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int y = 0; y < kXcds; ++y) sum += buf[(y * B + b) * RPW + r];
+    const float xn = xown[b * RPW + r] + sum;
+    xown[b * RPW + r] = xn;
+    publish_l(lxx + (size_t)b * H + n, xtag, xn, plain);
+  }
+  __syncthreads();
+  return true;
+}
+
+// ------------------------------------------------------------------ LDS layout
+//   xs    uint4 [BT][4][H/32]   staged fp16 input pairs (every GEMV input <= H)
+//   cc    float2 [BT][H/32]     per-chunk (C1, C2)
+//   xin   fp32 scratch          attention q/k/v and wave states, split merge,
+//                               reduce-scatter partials, lm_head input
+//   xown  fp32 [BT][RPW]        this group's rows of the residual stream
+//   cs    float2 [BT][D/2]      RoPE cos/sin of each row
+//   red   float [128]
+struct StepXLds {
+  size_t xs, cc, xin, xown, cs, red, total;
+};
+
+__host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int QPG, int GPX) {
+  StepXLds s{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 15) & ~(size_t)15; return r; };
+  const size_t pw = (size_t)QPG * (D + 2);
+  size_t xin = (size_t)kStepWaves * pw * 4 + (size_t)(QPG + 2) * D * 4;
+  const size_t merge = (size_t)BT * GPX * kXMergeChunk * pw * 4 +
+                       (size_t)BT * GPX * QPG * (kXMergeChunk + 2) * 4;
+  const size_t rs = (size_t)kXcds * BT * RPW * 4;
+  const size_t lm = (size_t)BT * H * 4;
+  if (xin < merge) xin = merge;
+  if (xin < rs) xin = rs;
+  if (xin < lm) xin = lm;
+  s.xs = take((size_t)BT * 4 * (H / 32) * 16);
+  s.cc = take((size_t)BT * (H / 32) * 8);
+  s.xin = take(xin);
+  s.xown = take((size_t)BT * RPW * 4);
+  s.cs = take((size_t)BT * (D / 2) * 8);
+  s.red = take(128 * 4);
+  s.total = o;
+  return s;
+}
+
+// XCD-local buffer strides (64-bit words per XCD region, 4 KB aligned).
+struct StepXSizes {
+  long long lx, lqkv, lpart, lact;
+};
+
+__host__ __device__ inline long long xalign(long long words) { return (words + 511) & ~511LL; }
+
+__host__ __device__ inline StepXSizes stepx_sizes(int B, int H, int Hkv, int D, int QPG, int I, int M) {
+  const int GPX = Hkv / kXcds, NSX = (M + kXSplit - 1) / kXSplit;
+  StepXSizes z{};
+  z.lx = xalign((long long)2 * B * H);   // two copies: x entering the layer, x after O
+  z.lqkv = xalign((long long)B * GPX * (QPG + 2) * D);
+  z.lpart = xalign((long long)B * GPX * NSX * QPG * (D + 2));
+  z.lact = xalign((long long)B * (I / kXcds));
+  return z;
+}
+
+template <int BT, int D, int QPG>
+__global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int DPL = D / 16, HALF = D / 2, PW = QPG * (D + 2);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int x = wg % kXcds, j = wg / kXcds, WPX = nwg / kXcds;
+  const int B = a.B, H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, G = a.G, M = a.M;
+  const int GPX = Hkv / kXcds, QX = GPX * (QPG + 2) * D, OX = GPX * QPG * D, IX = I / kXcds;
+  const int RPW = (H + WPX - 1) / WPX, RQ = (QX + WPX - 1) / WPX, RA = (IX + WPX - 1) / WPX;
+  const int NSX = (M + kXSplit - 1) / kXSplit;
+  const int plain = a.intra_plain;
+  const StepXLds Ld = stepx_lds(BT, H, RPW, D, QPG, GPX);
+  uint4* xs = reinterpret_cast<uint4*>(smem + Ld.xs);
+  float2* cc = reinterpret_cast<float2*>(smem + Ld.cc);
+  float* xin = reinterpret_cast<float*>(smem + Ld.xin);
+  float* xown = reinterpret_cast<float*>(smem + Ld.xown);
+  float2* cs = reinterpret_cast<float2*>(smem + Ld.cs);
+  float* red = reinterpret_cast<float*>(smem + Ld.red);
+  uint64_t* lx0 = a.lx + (size_t)x * a.x_lx;          // x entering a layer
+  uint64_t* lx1 = lx0 + (size_t)B * H;                // x after the O projection
+  uint64_t* lqkv = a.lqkv + (size_t)x * a.x_lqkv;
+  uint64_t* lpart = a.lpart + (size_t)x * a.x_lpart;
+  uint64_t* lact = a.lact + (size_t)x * a.x_lact;
+  __shared__ int s_last;
+  __shared__ int s_c[16];
+  __shared__ int s_ns[16];
+
+  const uint32_t step = (a.step_ctr[0] + 1u) & 0x7fffffu;
+  auto tag = [&](int phase) -> uint32_t { return (step << 9) | (uint32_t)phase; };
+  bool alive = true;
+
+  // ---- step prologue: placement check, cache positions, RoPE tables, embedding
+  if (tid == 0 && plain) {
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u;
+    if ((int)(xcc % kXcds) != x) raise_status(a.status, kStatusTopology);
+  }
+  if (tid < B) {
+    const int c = a.cpos[tid];
+    s_c[tid] = c;
+    s_ns[tid] = (c >= 0 && c < M) ? (c + kXSplit) / kXSplit : 0;
+    if (wg == 0 && (c < 0 || c >= M)) raise_status(a.status, 1u);
+  }
+  for (int i = tid; i < B * HALF; i += kStepThreads) {
+    const int b = i / HALF, jj = i - b * HALF;
+    const int ax = mrope_axis(jj, a.sec0, a.sec1, a.sec2, a.interleaved);
+    const double p = (double)a.pos[ax * B + b];
+    const double inv_freq = pow(a.theta, -2.0 * (double)jj / (double)D);
+    double sn, cn;
+    sincos(p * inv_freq, &sn, &cn);
+    cs[b * HALF + jj] = make_float2((float)cn, (float)sn);
+  }
+  for (int i = tid; i < B * RPW; i += kStepThreads) {
+    const int b = i / RPW, r = i - b * RPW, n = j * RPW + r;
+    if (n >= H) continue;
+    const int id = (a.finished && a.finished[b]) ? a.pad_id : a.ids[b];
+    const bool ok = id >= 0 && id < a.V;
+    if (!ok && n == 0 && x == 0) raise_status(a.status, 2u);
+    const float v = ok ? bf16_to_f32(a.embed[(size_t)id * H + n]) : 0.f;
+    xown[b * RPW + r] = v;
+    publish_l(lx0 + (size_t)b * H + n, tag(1), v, plain);
+  }
+  __syncthreads();
+  KMR_TRACE_MARK(0);
+
+  for (int l = 0; l < a.L && alive; ++l) {
+    const StepLayer& Ly = a.layers[l];
+    const int ph = 1 + 6 * l;   // tags: ph x (lx0), +1 qkv, +2 partials, +3 O partials,
+                                // +4 x after O (lx1), +5 act, +6 down partials and next x
+    [[maybe_unused]] const int tev = l < 5 ? 1 + 11 * l : 64;
+    // ================= QKV rows of this XCD's kv heads: RQ rows per group, 2 per wave
+    {
+      constexpr int NR = 2;
+      int row[NR], lr[NR];
+      bool ok[NR];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int rr = wave * NR + i;
+        lr[i] = j * RQ + rr;
+        ok[i] = rr < RQ && lr[i] < QX;
+        row[i] = 0;
+        if (ok[i]) {
+          const int gl = lr[i] / ((QPG + 2) * D), t = lr[i] - gl * (QPG + 2) * D, g = x * GPX + gl;
+          row[i] = t < QPG * D ? g * QPG * D + t
+                 : t < (QPG + 1) * D ? Hq * D + g * D + (t - QPG * D)
+                                     : Hq * D + Hkv * D + g * D + (t - (QPG + 1) * D);
+        }
+      }
+      WRows<NR, 1> w;
+      wrows_load(w, Ly.qkv_p, Ly.qkv_s, H, G, row, ok);
+      if (!gather_stage<BT, 4 * BT>(lx0, H, B, tag(ph), Ly.in_norm, a.eps, xs, cc, red)) {
+        alive = false;
+        break;
+      }
+      KMR_TRACE_MARK(tev + 0);
+      float out[NR][BT];
+      wave_dot<BT, NR, 1>(w, H, B, xs, cc, out);
+      if (lane < B) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+          if (ok[i]) {
+            float v = out[i][0];
+#pragma unroll
+            for (int b = 1; b < BT; ++b) if (lane == b) v = out[i][b];
+            publish_l(lqkv + (size_t)lane * QX + lr[i], tag(ph + 1), v, plain);
+          }
+      }
+    }
+    KMR_TRACE_MARK(tev + 1);
+    const int orow = j * RPW + wave * 8 + (lane >> 3);   // O and down rows of this lane group
+    const bool ook = wave * 8 + (lane >> 3) < RPW && orow < H;
+    // ================= attention items (row, local kv head, split) of this XCD
+    {
+      uint16_t* kc = a.kc + (size_t)l * a.cacheB * Hkv * M * D;
+      uint16_t* vc = a.vc + (size_t)l * a.cacheB * Hkv * M * D;
+      int total = 0;
+      for (int b = 0; b < B; ++b) total += GPX * s_ns[b];
+      for (int item = j; item < total; item += WPX) {
+        int b = 0, rem = item;
+        while (rem >= GPX * s_ns[b]) { rem -= GPX * s_ns[b]; ++b; }
+        const int ns = s_ns[b], gl = rem / ns, s = rem - gl * ns, g = x * GPX + gl, c = s_c[b];
+        const int rr = lane >> 4, li = lane & 15, row = wave * 4 + rr, d0 = li * DPL;
+        const size_t head_base = ((size_t)b * Hkv + g) * M;
+        // cache reads first: row `row` takes positions s*128 + 4*row + {0..3}
+        uint32_t kr[4][DPL / 2], vr[4][DPL / 2];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int p = s * kXSplit + 4 * row + it;
+          if (p < c) {
+            const uint32_t* ks = reinterpret_cast<const uint32_t*>(kc + (head_base + p) * D + d0);
+            const uint32_t* vs = reinterpret_cast<const uint32_t*>(vc + (head_base + p) * D + d0);
+#pragma unroll
+            for (int e = 0; e < DPL / 2; ++e) { kr[it][e] = ks[e]; vr[it][e] = vs[e]; }
+          } else {
+#pragma unroll
+            for (int e = 0; e < DPL / 2; ++e) kr[it][e] = vr[it][e] = 0u;
+          }
+        }
+        float gq[DPL], gk[DPL];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+          gq[e] = bf16_to_f32(Ly.q_norm[d0 + e]);
+          gk[e] = bf16_to_f32(Ly.k_norm[d0 + e]);
+        }
+        // q heads of kv head g (contiguous), then k, then v: one gather
+        float* qv = xin;
+        {
+          auto addr = [](int i) { return (size_t)i; };
+          auto place = [](int i) { return i; };
+          if (!gather_tagged<(QPG + 2) * D / kStepThreads + 1>(
+                  lqkv + (size_t)b * QX + (size_t)gl * (QPG + 2) * D, (QPG + 2) * D, tag(ph + 1), qv,
+                  addr, place, NoPre())) {
+            alive = false;
+            break;
+          }
+        }
+        KMR_TRACE_MARK(tev + 2);
+        float q[QPG][DPL], kf[DPL], vf[DPL];
+#pragma unroll
+        for (int h = 0; h < QPG; ++h)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) q[h][e] = qv[h * D + d0 + e];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+          kf[e] = qv[QPG * D + d0 + e];
+          vf[e] = qv[(QPG + 1) * D + d0 + e];
+        }
+        float cs_c[DPL], cs_s[DPL];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+          const float2 t = cs[b * HALF + ((d0 + e) % HALF)];
+          cs_c[e] = t.x;
+          cs_s[e] = (d0 < HALF) ? -t.y : t.y;
+        }
+#pragma unroll
+        for (int h = 0; h < QPG; ++h) norm_rope<DPL>(q[h], gq, cs_c, cs_s, D, a.eps);
+        norm_rope<DPL>(kf, gk, cs_c, cs_s, D, a.eps);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) { kf[e] = round_bf16(kf[e]); vf[e] = round_bf16(vf[e]); }
+        KMR_TRACE_MARK(l == 1 ? 59 : 64);
+        if (s == ns - 1 && row == 0) {
+          uint16_t* kd = kc + (head_base + c) * D + d0;
+          uint16_t* vd = vc + (head_base + c) * D + d0;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) { kd[e] = f32_to_bf16(kf[e]); vd[e] = f32_to_bf16(vf[e]); }
+        }
+        float m[QPG], lsum[QPG], o[QPG][DPL];
+#pragma unroll
+        for (int h = 0; h < QPG; ++h) {
+          m[h] = -INFINITY;
+          lsum[h] = 0.f;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int p = s * kXSplit + 4 * row + it;
+          const bool valid = p <= c;
+          float kk[DPL], vv[DPL];
+          if (p == c) {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) { kk[e] = kf[e]; vv[e] = vf[e]; }
+          } else {
+#pragma unroll
+            for (int e = 0; e < DPL / 2; ++e) {
+              kk[2 * e] = bf16_lo(kr[it][e]); kk[2 * e + 1] = bf16_hi(kr[it][e]);
+              vv[2 * e] = bf16_lo(vr[it][e]); vv[2 * e + 1] = bf16_hi(vr[it][e]);
+            }
+          }
+#pragma unroll
+          for (int h = 0; h < QPG; ++h) {
+            float sc = 0.f;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) sc += q[h][e] * kk[e];
+            sc = row16_sum(sc) * a.scale_log2;
+            if (valid) {
+              const float mn = fmaxf(m[h], sc);
+              const float corr = exp2f(m[h] - mn);
+              const float pe = exp2f(sc - mn);
+              lsum[h] = lsum[h] * corr + pe;
+#pragma unroll
+              for (int e = 0; e < DPL; ++e) o[h][e] = o[h][e] * corr + pe * vv[e];
+              m[h] = mn;
+            }
+          }
+        }
+        KMR_TRACE_MARK(l == 1 ? 60 : 64);
+        // merge the 4 rows of each wave: rows (0,1) and (2,3), then (01, 23)
+#pragma unroll
+        for (int h = 0; h < QPG; ++h) {
+          float mlo, mhi, llo, lhi, olo[DPL], ohi[DPL];
+          lane_pair<16>(m[h], mlo, mhi);
+          lane_pair<16>(lsum[h], llo, lhi);
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) lane_pair<16>(o[h][e], olo[e], ohi[e]);
+          lse_merge(mlo, llo, olo, mhi, lhi, ohi, DPL);
+          lane_pair<32>(mlo, m[h], mhi);
+          lane_pair<32>(llo, lsum[h], lhi);
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) lane_pair<32>(olo[e], o[h][e], ohi[e]);
+          lse_merge(m[h], lsum[h], o[h], mhi, lhi, ohi, DPL);
+        }
+        KMR_TRACE_MARK(l == 1 ? 61 : 64);
+        __syncthreads();   // q/k/v scratch is reused below
+        float* s_w = xin;  // [8 waves][QPG][D + 2]
+        if (rr == 0) {
+#pragma unroll
+          for (int h = 0; h < QPG; ++h) {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) s_w[(wave * QPG + h) * (D + 2) + d0 + e] = o[h][e];
+            if (li == 0) {
+              s_w[(wave * QPG + h) * (D + 2) + D] = m[h];
+              s_w[(wave * QPG + h) * (D + 2) + D + 1] = lsum[h];
+            }
+          }
+        }
+        __syncthreads();
+        // merge the 8 wave states of each head: the log-sum-exp weights are
+        // computed once per (wave, head), then each output is 8 multiply-adds
+        float* s_e = s_w + kStepWaves * QPG * (D + 2);   // [8][QPG] weights, [QPG] max, [QPG] sum
+        if (tid < QPG) {
+          float Mx = -INFINITY;
+#pragma unroll
+          for (int wv = 0; wv < kStepWaves; ++wv) Mx = fmaxf(Mx, s_w[(wv * QPG + tid) * (D + 2) + D]);
+          float Ls = 0.f;
+#pragma unroll
+          for (int wv = 0; wv < kStepWaves; ++wv) {
+            const float mw = s_w[(wv * QPG + tid) * (D + 2) + D];
+            const float e = mw == -INFINITY ? 0.f : exp2f(mw - Mx);
+            s_e[wv * QPG + tid] = e;
+            Ls += e * s_w[(wv * QPG + tid) * (D + 2) + D + 1];
+          }
+          s_e[kStepWaves * QPG + tid] = Mx;
+          s_e[(kStepWaves + 1) * QPG + tid] = Ls;
+        }
+        __syncthreads();
+        KMR_TRACE_MARK(l == 1 ? 62 : 64);
+        uint64_t* pdst = lpart + (((size_t)b * GPX + gl) * NSX + s) * PW;
+        for (int i = tid; i < QPG * D; i += kStepThreads) {
+          const int h = i / D, d = i - h * D;
+          float Os = 0.f;
+#pragma unroll
+          for (int wv = 0; wv < kStepWaves; ++wv) Os += s_e[wv * QPG + h] * s_w[(wv * QPG + h) * (D + 2) + d];
+          publish_l(pdst + h * (D + 2) + d, tag(ph + 2), Os, plain);
+          if (d == 0) {
+            publish_l(pdst + h * (D + 2) + D, tag(ph + 2), s_e[kStepWaves * QPG + h], plain);
+            publish_l(pdst + h * (D + 2) + D + 1, tag(ph + 2), s_e[(kStepWaves + 1) * QPG + h], plain);
+          }
+        }
+        __syncthreads();
+      }
+      if (__syncthreads_or(!alive)) break;
+    }
+    KMR_TRACE_MARK(tev + 3);
+    // O weights of this group (rows j*RPW + 8 wave + lane/8, the XCD's head columns),
+    // in flight while the partials are gathered
+    WNarrow wo;
+    wnarrow_load(wo, Ly.o_p, Ly.o_s, Hq * D, G, x * OX, OX, ook ? orow : 0, ook);
+    // ================= merge every split of the XCD's heads; o -> staged O input
+    {
+      constexpr int PTM = BT;   // B * OX <= 512 * BT (OX <= 512, checked on the host)
+      float mM[PTM], mL[PTM], mO[PTM];
+#pragma unroll
+      for (int q = 0; q < PTM; ++q) { mM[q] = -INFINITY; mL[q] = 0.f; mO[q] = 0.f; }
+      int maxns = 0;
+      for (int b = 0; b < B; ++b) maxns = s_ns[b] > maxns ? s_ns[b] : maxns;
+      const int CW = kXMergeChunk * PW, words = B * GPX * CW;
+      for (int t0 = 0; t0 < maxns && alive; t0 += kXMergeChunk) {
+        constexpr int PG = 8;
+        bool ok = true;
+        for (int base = 0; base < words && ok; base += kStepThreads * PG) {
+          uint64_t v[PG];
+          uint32_t off[PG];
+          bool hv[PG];
+#pragma unroll
+          for (int q = 0; q < PG; ++q) {
+            const int i = base + kStepThreads * q + tid;
+            const int seg = i / CW, r1 = i - seg * CW, sl = r1 / PW, k = r1 - sl * PW;
+            hv[q] = i < words && t0 + sl < s_ns[seg / GPX];
+            off[q] = hv[q] ? (uint32_t)((seg * NSX + t0 + sl) * PW + k) : 0u;
+          }
+          uint32_t spins = 0;
+          bool fresh;
+          do {
+#pragma unroll
+            for (int q = 0; q < PG; ++q)
+              if (hv[q]) v[q] = ld_dev64(lpart + off[q]);
+            fresh = true;
+#pragma unroll
+            for (int q = 0; q < PG; ++q)
+              if (hv[q]) fresh &= (uint32_t)(v[q] >> 32) == tag(ph + 2);
+            if (!fresh) {
+              if (++spins > kSpinLimit) { ok = false; break; }
+              __builtin_amdgcn_s_sleep(KMR_POLL_SLEEP);
+            }
+          } while (!fresh);
+#pragma unroll
+          for (int q = 0; q < PG; ++q) {
+            const int i = base + kStepThreads * q + tid;
+            if (hv[q]) xin[i] = __uint_as_float((uint32_t)v[q]);
+          }
+        }
+        if (__syncthreads_or(!ok)) { alive = false; break; }
+        // log-sum-exp weights of this chunk's splits, once per (row, kv head, q head)
+        float* s_wt = xin + words;   // [B*GPX][QPG][kXMergeChunk + 2]: weights, max, sum
+        if (tid < B * GPX * QPG) {
+          const int seg = tid / QPG, h = tid - seg * QPG, b = seg / GPX;
+          const int n = s_ns[b] - t0 < kXMergeChunk ? s_ns[b] - t0 : kXMergeChunk;
+          float* wt = s_wt + tid * (kXMergeChunk + 2);
+          float Mc = -INFINITY, Lc = 0.f;
+          for (int t = 0; t < n; ++t) Mc = fmaxf(Mc, xin[((size_t)seg * kXMergeChunk + t) * PW + h * (D + 2) + D]);
+          for (int t = 0; t < n; ++t) {
+            const float* pt = xin + ((size_t)seg * kXMergeChunk + t) * PW + h * (D + 2);
+            const float e = pt[D] == -INFINITY ? 0.f : exp2f(pt[D] - Mc);
+            wt[t] = e;
+            Lc += e * pt[D + 1];
+          }
+          wt[kXMergeChunk] = Mc;
+          wt[kXMergeChunk + 1] = Lc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < PTM; ++q) {
+          const int idx = kStepThreads * q + tid;
+          if (idx >= B * OX) continue;
+          const int b = idx / OX, k = idx - b * OX, gl = k / (QPG * D), hd = k - gl * QPG * D;
+          const int h = hd / D, d = hd - h * D, seg = b * GPX + gl;
+          const int n = s_ns[b] - t0 < kXMergeChunk ? s_ns[b] - t0 : kXMergeChunk;
+          if (n <= 0) continue;
+          const float* wt = s_wt + (seg * QPG + h) * (kXMergeChunk + 2);
+          float Oc = 0.f;
+          for (int t = 0; t < n; ++t) Oc += wt[t] * xin[((size_t)seg * kXMergeChunk + t) * PW + h * (D + 2) + d];
+          lse_merge(mM[q], mL[q], &mO[q], wt[kXMergeChunk], wt[kXMergeChunk + 1], &Oc, 1);
+        }
+        __syncthreads();
+      }
+      if (!alive) break;
+      float e[PTM];
+      int eb[PTM], ek[PTM];
+      bool has[PTM];
+#pragma unroll
+      for (int q = 0; q < PTM; ++q) {
+        const int idx = kStepThreads * q + tid;
+        has[q] = idx < B * OX;
+        eb[q] = has[q] ? idx / OX : 0;
+        ek[q] = idx - eb[q] * OX;
+        e[q] = (has[q] && mL[q] > 0.f) ? mO[q] * (1.0f / mL[q]) : 0.f;
+      }
+      stage_values<PTM>(e, has, eb, ek, OX, xs, cc);
+      __syncthreads();
+    }
+    KMR_TRACE_MARK(tev + 4);
+    // ================= O split-K partial of this group's rows over the XCD's heads
+    {
+      float out[BT];
+      narrow_dot<BT>(wo, OX, B, xs, cc, out);
+      const int sub = lane & 7;
+      if (ook && sub < B) {
+        float v = out[0];
+#pragma unroll
+        for (int b = 1; b < BT; ++b) if (sub == b) v = out[b];
+        publish(a.pO + ((size_t)x * B + sub) * H + orow, tag(ph + 3), v);
+      }
+    }
+    KMR_TRACE_MARK(tev + 5);
+    // gate/up weights of this group (act rows j*RA + 3 wave + i of the XCD's slice)
+    constexpr int NP = 3;
+    int grow[2 * NP], gla[NP];
+    bool gok[2 * NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int la = wave * NP + i;
+      gla[i] = j * RA + la;
+      gok[i] = gok[NP + i] = la < RA && gla[i] < IX;
+      grow[i] = gok[i] ? x * IX + gla[i] : 0;
+      grow[NP + i] = gok[i] ? x * IX + gla[i] + I : 0;
+    }
+    WRows<2 * NP, 1> wgu;
+    wrows_load(wgu, Ly.gu_p, Ly.gu_s, H, G, grow, gok);
+    // ================= RS_O: x rows after O, published to the XCD's copy
+    if (!reduce_rows(a.pO, tag(ph + 3), B, H, RPW, j * RPW, xown, xin, lx1, tag(ph + 4), plain)) {
+      alive = false;
+      break;
+    }
+    KMR_TRACE_MARK(tev + 6);
+    // ================= gate-up + SiLU over the XCD's slice
+    {
+      if (!gather_stage<BT, 4 * BT>(lx1, H, B, tag(ph + 4), Ly.post_norm, a.eps, xs, cc, red)) {
+        alive = false;
+        break;
+      }
+      KMR_TRACE_MARK(tev + 7);
+      float out[2 * NP][BT];
+      wave_dot<BT, 2 * NP, 1>(wgu, H, B, xs, cc, out);
+      if (lane < B) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+          if (gok[i]) {
+            float gt = out[i][0], up = out[NP + i][0];
+#pragma unroll
+            for (int b = 1; b < BT; ++b) if (lane == b) { gt = out[i][b]; up = out[NP + i][b]; }
+            publish_l(lact + (size_t)lane * IX + gla[i], tag(ph + 5), gt / (1.0f + expf(-gt)) * up, plain);
+          }
+      }
+    }
+    KMR_TRACE_MARK(tev + 8);
+    // ================= down split-K over the XCD's slice, then RS_D
+    {
+      WNarrow wd;
+      wnarrow_load(wd, Ly.d_p, Ly.d_s, I, G, x * IX, IX, ook ? orow : 0, ook);
+      if (!gather_stage<BT, 2 * BT>(lact, IX, B, tag(ph + 5), nullptr, a.eps, xs, cc, red)) {
+        alive = false;
+        break;
+      }
+      KMR_TRACE_MARK(tev + 9);
+      float out[BT];
+      narrow_dot<BT>(wd, IX, B, xs, cc, out);
+      const int sub = lane & 7;
+      if (ook && sub < B) {
+        float v = out[0];
+#pragma unroll
+        for (int b = 1; b < BT; ++b) if (sub == b) v = out[b];
+        publish(a.pD + ((size_t)x * B + sub) * H + orow, tag(ph + 6), v);
+      }
+    }
+    if (!reduce_rows(a.pD, tag(ph + 6), B, H, RPW, j * RPW, xown, xin, lx0, tag(ph + 6), plain)) {
+      alive = false;
+      break;
+    }
+    KMR_TRACE_MARK(tev + 10);
+  }
+
+  if (!alive) {
+    if (tid == 0) raise_status(a.status, kStatusTimeout);
+    return;
+  }
+  {
+    auto addr = [](int i) { return (size_t)i; };
+    auto place = [](int i) { return i; };
+    const bool ok = B * H <= kStepThreads * 4
+                        ? gather_tagged<4>(lx0, B * H, tag(1 + 6 * a.L), xin, addr, place, NoPre())
+                        : gather_tagged<16>(lx0, B * H, tag(1 + 6 * a.L), xin, addr, place, NoPre());
+    if (!ok) {
+      if (tid == 0) raise_status(a.status, kStatusTimeout);
+      return;
+    }
+  }
+  KMR_TRACE_MARK(56);
+  step_tail<BT>(a, xin, red, &s_last, step);
+}
+
+}  // namespace kmr

@@ -31,10 +31,11 @@ if len(_hip_runtimes()) > 1:
     raise ImportError(f"two HIP runtimes are mapped: {_hip_runtimes()}")
 
 KMR_OK, KMR_EINVAL, KMR_ESHAPE, KMR_ENOMEM, KMR_EHIP = 0, -1, -2, -3, -4
-KMR_STATUS_CACHE_POS, KMR_STATUS_TOKEN, KMR_STATUS_TIMEOUT = 1, 2, 4
+KMR_STATUS_CACHE_POS, KMR_STATUS_TOKEN, KMR_STATUS_TIMEOUT, KMR_STATUS_TOPOLOGY = 1, 2, 4, 8
 KMR_MAX_BATCH = 16
 KMR_ADVANCE = 1
 KMR_MULTI_KERNEL = 2
+KMR_DEVICE_WIDE = 4
 
 _i32, _p = C.c_int32, C.c_void_p
 
@@ -226,14 +227,16 @@ class DeviceModel:
     def decode_step(self, kv: KVCache, token_ids: torch.Tensor, positions: torch.Tensor,
                     cache_position: torch.Tensor, next_ids: torch.Tensor, ws: Workspace,
                     finished: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
-                    advance: bool = False, multi_kernel: bool = False, stream=None) -> torch.Tensor:
+                    advance: bool = False, multi_kernel: bool = False, device_wide: bool = False,
+                    stream=None) -> torch.Tensor:
         B = token_ids.shape[0]
         assert token_ids.dtype == torch.int32 and next_ids.dtype == torch.int32
         assert finished is None or finished.dtype == torch.uint8
         _check(_lib.kmr_decode_step(C.byref(self.cfg), C.byref(self.cmodel), C.byref(kv.desc),
                                     _ptr(token_ids), _ptr(positions), _ptr(cache_position),
                                     _ptr(finished), B, _ptr(next_ids), _ptr(logits),
-                                    (KMR_ADVANCE if advance else 0) | (KMR_MULTI_KERNEL if multi_kernel else 0),
+                                    (KMR_ADVANCE if advance else 0) | (KMR_MULTI_KERNEL if multi_kernel else 0)
+                                    | (KMR_DEVICE_WIDE if device_wide else 0),
                                     ws.ptr, ws.nbytes,
                                     _stream(stream)))
         return next_ids

@@ -14,6 +14,9 @@ decoder):
   step      28-layer decoder + bf16 lm_head, batch 1, cache_position 700
   batch4    same model, 4 continuous-batching rows, one finished, 64 steps
   long16    same model, 16 rows, 8192-slot cache, 2048..8000 cached positions
+  kv8       a reduced 2-layer decoder with the full model's head layout (16 q / 8
+            kv heads, GQA 2) at head_dim 64, for parity runs of the kernels that
+            give each XCD its own kv head
 
 Two generators exist:
   * ``where="host"``: numpy PCG64 streams keyed by SeedSequence(base, spawn_key),
@@ -56,6 +59,8 @@ class Dims:
 
 TINY = Dims(hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=768,
             vocab=1024, n_layers=1, group_size=64, mrope_section=(12, 10, 10))
+KV8 = Dims(hidden=512, n_heads=16, n_kv_heads=8, head_dim=64, intermediate=2048,
+           vocab=2048, n_layers=2, group_size=64, mrope_section=(12, 10, 10))
 QWEN3VL_2B = Dims(hidden=2048, n_heads=16, n_kv_heads=8, head_dim=128,
                   intermediate=6144, vocab=151936, n_layers=28, group_size=128,
                   mrope_section=(24, 20, 20))
@@ -83,6 +88,8 @@ WORKLOADS: Dict[str, Workload] = {
                        "28 layers, 4 slots (row 3 finished), 64 greedy steps"),
     "long16": Workload("long16", 4, QWEN3VL_2B, 16, 8192, 32,
                        "28 layers, 16 slots, 8192-slot cache, 2048..8000 cached positions"),
+    "kv8": Workload("kv8", 5, KV8, 4, 384, 4,
+                    "reduced 2-layer decoder with 8 kv heads, 4 slots, 384-slot cache"),
 }
 
 
@@ -208,6 +215,10 @@ def step_inputs(w: Workload) -> Dict[str, np.ndarray]:
     elif w.name == "long16":
         cpos = rng_c.integers(2048, 8001, size=B).astype(np.int32)
         pos = np.stack([cpos, cpos, cpos]).astype(np.int32)
+    elif w.name == "kv8":
+        # split edges of 128-position attention splits, and the last slot
+        cpos = np.array([0, 127, 128, 383], np.int32)[:B]
+        pos = np.stack([rng_pos.integers(0, int(c) + 1, size=3) for c in cpos], axis=1).astype(np.int32)
     else:
         raise ValueError(w.name)
     return {"ids": ids, "positions": np.ascontiguousarray(pos), "cache_position": cpos,

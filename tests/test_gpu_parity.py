@@ -137,7 +137,14 @@ def _check_step(got_next, got_logits, ref, label):
     assert np.all(agree | ~decisive)
 
 
-def _step_case(kmr, pair, kv, kh, vh, inp, M, steps=1, advance=False, multi_kernel=False):
+PATHS = ["persistent", "device_wide", "multi_kernel"]
+
+
+def _path_flags(path):
+    return {"multi_kernel": path == "multi_kernel", "device_wide": path == "device_wide"}
+
+
+def _step_case(kmr, pair, kv, kh, vh, inp, M, steps=1, advance=False, path="persistent"):
     dims = pair.dims
     B = len(inp["ids"])
     cfg = pair.dev.cfg
@@ -148,10 +155,12 @@ def _step_case(kmr, pair, kv, kh, vh, inp, M, steps=1, advance=False, multi_kern
     fin_d = torch.from_numpy(fin).cuda()
     nxt_d = torch.zeros(B, dtype=torch.int32, device="cuda")
     logits_d = torch.empty((B, dims.vocab), dtype=torch.float32, device="cuda")
+    written = set()
     for step in range(steps):
         ids_d = torch.from_numpy(ids).cuda()
+        written.update((b, int(c)) for b, c in enumerate(cpos) if 0 <= c < M)
         pair.dev.decode_step(kv, ids_d, pos_d, cpos_d, nxt_d, ws, finished=fin_d, logits=logits_d,
-                             advance=advance, multi_kernel=multi_kernel)
+                             advance=advance, **_path_flags(path))
         torch.cuda.synchronize()
         ref = pair.ora.decode_step(kh, vh, ids, pos, cpos, finished=fin, advance=advance)
         _check_step(nxt_d.cpu().numpy(), logits_d.cpu().numpy(), ref, f"step {step}")
@@ -160,29 +169,73 @@ def _step_case(kmr, pair, kv, kh, vh, inp, M, steps=1, advance=False, multi_kern
         assert np.array_equal(fin_d.cpu().numpy(), fin)
         ids = ref["next"].astype(np.int32)        # lockstep: both sides take the oracle's token
     assert ws.status() == 0
+    if kh.shape[1] == B:
+        _check_cache(kv, kh, vh, written)
     return ref
 
 
-@pytest.mark.parametrize("multi_kernel", [False, True])
-def test_decode_step_tiny(kmr, multi_kernel):
+def _check_cache(kv, kh, vh, written):
+    """Only the slots the steps wrote may differ from the oracle's cache (bytes);
+    those hold the same K/V within tolerance."""
+    for dev_t, ref in ((kv.k, kh), (kv.v, vh)):
+        got = oracle.as_u16(dev_t)
+        diff = np.any(got != ref, axis=-1)                 # [L][B][Hkv][M]
+        for l, b, g, m in zip(*np.nonzero(diff)):
+            assert (int(b), int(m)) in written, f"slot {(l, b, g, m)} changed but was not written"
+        for b, m in written:
+            err = max_rel(bf16_host(got[:, b, :, m, :]).reshape(-1, got.shape[-1]),
+                          bf16_host(ref[:, b, :, m, :]).reshape(-1, got.shape[-1]))
+            assert err <= TOL, f"row {b} slot {m}: K/V max_rel {err:.3e}"
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_decode_step_tiny(kmr, path):
     w = synth.WORKLOADS["tiny"]
-    log(f"decode_step tiny (multi_kernel={multi_kernel})")
+    log(f"decode_step tiny ({path})")
     pair = build_pair(w.dims, synth.base_seed(w), "host", with_globals=True)
     kv, kh, vh = make_caches(w.dims, synth.base_seed(w), 1, w.max_len, "host")
-    _step_case(kmr, pair, kv, kh, vh, synth.step_inputs(w), w.max_len, multi_kernel=multi_kernel)
+    _step_case(kmr, pair, kv, kh, vh, synth.step_inputs(w), w.max_len, path=path)
 
 
-@pytest.mark.parametrize("multi_kernel", [False, True])
-def test_decode_step_tiny_batch_advance(kmr, multi_kernel):
+@pytest.mark.parametrize("path", PATHS)
+def test_decode_step_tiny_batch_advance(kmr, path):
     w = synth.WORKLOADS["tiny"]
-    log(f"decode_step tiny batch 3, finished row, advance to the last slot (multi_kernel={multi_kernel})")
+    log(f"decode_step tiny batch 3, finished row, advance to the last slot ({path})")
     pair = build_pair(w.dims, synth.base_seed(w), "host", with_globals=True)
     kv, kh, vh = make_caches(w.dims, synth.base_seed(w), 3, w.max_len, "host")
     inp = {"ids": np.array([5, 6, 7], np.int32),
            "positions": np.array([[10, 125, 3], [11, 1, 3], [12, 2, 3]], np.int32),
            "cache_position": np.array([10, 125, 3], np.int32),
            "finished": np.array([0, 0, 1], np.uint8)}
-    _step_case(kmr, pair, kv, kh, vh, inp, w.max_len, steps=4, advance=True, multi_kernel=multi_kernel)
+    _step_case(kmr, pair, kv, kh, vh, inp, w.max_len, steps=4, advance=True, path=path)
+
+
+@pytest.fixture(scope="module")
+def kv8_pair(kmr):
+    w = synth.WORKLOADS["kv8"]
+    return build_pair(w.dims, synth.base_seed(w), "host", with_globals=True)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_decode_step_kv8_batch4_advance(kmr, kv8_pair, path):
+    """8 kv heads (one per XCD): cache positions on split edges and the last slot."""
+    w = synth.WORKLOADS["kv8"]
+    log(f"decode_step kv8 batch 4, c = 0/127/128/383, 4 advancing steps ({path})")
+    kv, kh, vh = make_caches(w.dims, synth.base_seed(w), w.batch, w.max_len, "host")
+    _step_case(kmr, kv8_pair, kv, kh, vh, synth.step_inputs(w), w.max_len, steps=4, advance=True,
+               path=path)
+
+
+@pytest.mark.parametrize("batch,cpos", [(1, [255]), (2, [3, 250]), (3, [129, 0, 300])])
+def test_decode_step_kv8_small_batches(kmr, kv8_pair, batch, cpos):
+    w = synth.WORKLOADS["kv8"]
+    log(f"decode_step kv8 batch {batch}, c = {cpos}, 3 advancing steps (persistent)")
+    kv, kh, vh = make_caches(w.dims, synth.base_seed(w) + batch, batch, w.max_len, "host")
+    c = np.array(cpos, np.int32)
+    inp = {"ids": np.arange(batch, dtype=np.int32) * 37 + 5,
+           "positions": np.stack([c, c // 2, c // 3]).astype(np.int32),
+           "cache_position": c, "finished": np.zeros(batch, np.uint8)}
+    _step_case(kmr, kv8_pair, kv, kh, vh, inp, w.max_len, steps=3, advance=True)
 
 
 @pytest.fixture(scope="module")
@@ -192,20 +245,20 @@ def full_pair(kmr):
     return build_pair(w.dims, synth.base_seed(w), "device", with_globals=True)
 
 
-@pytest.mark.parametrize("multi_kernel", [False, True])
-def test_decode_step_full(kmr, full_pair, multi_kernel):
+@pytest.mark.parametrize("path", PATHS)
+def test_decode_step_full(kmr, full_pair, path):
     w = synth.WORKLOADS["step"]
-    log(f"decode_step 28 layers, batch 1, cache_position 700 (multi_kernel={multi_kernel})")
+    log(f"decode_step 28 layers, batch 1, cache_position 700 ({path})")
     kv, kh, vh = make_caches(w.dims, synth.base_seed(w), 1, w.max_len, "device")
-    _step_case(kmr, full_pair, kv, kh, vh, synth.step_inputs(w), w.max_len, multi_kernel=multi_kernel)
+    _step_case(kmr, full_pair, kv, kh, vh, synth.step_inputs(w), w.max_len, path=path)
 
 
 def test_persistent_and_per_phase_paths_agree(kmr, full_pair):
     w = synth.WORKLOADS["batch4"]
-    log("persistent step kernel vs per-phase kernels, batch 4, 3 advancing steps")
+    log("persistent step kernels vs per-phase kernels, batch 4, 3 advancing steps")
     inp = synth.step_inputs(w)
     outs = []
-    for multi in (False, True):
+    for path in PATHS:
         kv, _, _ = make_caches(w.dims, synth.base_seed(w), w.batch, w.max_len, "device", host_rows=[0])
         ws = kmr.Workspace(full_pair.dev.cfg, w.batch, w.max_len)
         ids = torch.from_numpy(inp["ids"]).cuda()
@@ -216,20 +269,23 @@ def test_persistent_and_per_phase_paths_agree(kmr, full_pair):
         seq = []
         for _ in range(3):
             full_pair.dev.decode_step(kv, ids, pos, cpos, nxt, ws, finished=fin, logits=logits,
-                                      advance=True, multi_kernel=multi)
+                                      advance=True, **_path_flags(path))
             seq.append((nxt.clone(), logits.clone()))
             ids = nxt.clone()
         torch.cuda.synchronize()
         assert ws.status() == 0
         outs.append((seq, kv.k.clone(), kv.v.clone(), pos.cpu(), cpos.cpu(), fin.cpu()))
         del kv
-    (sa, ka, va, pa, ca, fa), (sb, kb, vb, pb, cb, fb) = outs
-    for (na, la), (nb, lb) in zip(sa, sb):
-        err = max_rel(la.cpu().numpy(), lb.cpu().numpy())
-        log(f"  logits max_rel between paths {err:.3e}; tokens {na.tolist()} vs {nb.tolist()}")
-        assert err <= TOL
-    assert torch.equal(pa, pb) and torch.equal(ca, cb) and torch.equal(fa, fb)
-    assert max_rel(ka.float().cpu().numpy().reshape(-1, 128), kb.float().cpu().numpy().reshape(-1, 128)) <= TOL
+    sa, ka, va, pa, ca, fa = outs[-1]          # per-phase kernels as the reference
+    for sb, kb, vb, pb, cb, fb in outs[:-1]:
+        for (na, la), (nb, lb) in zip(sa, sb):
+            err = max_rel(la.cpu().numpy(), lb.cpu().numpy())
+            log(f"  logits max_rel between paths {err:.3e}; tokens {na.tolist()} vs {nb.tolist()}")
+            assert err <= TOL
+        assert torch.equal(pa, pb) and torch.equal(ca, cb) and torch.equal(fa, fb)
+        for xa, xb in ((ka, kb), (va, vb)):
+            assert max_rel(xa.float().cpu().numpy().reshape(-1, 128),
+                           xb.float().cpu().numpy().reshape(-1, 128)) <= TOL
 
 
 def test_decode_step_batch4_lockstep(kmr, full_pair):
