@@ -74,7 +74,7 @@ constexpr int kMaxStepGroups = 1024;   // lm_head partial slots of the persisten
 struct WsLayout {
   size_t status, cs, x, qkv, attn_o, act, part_o, part_ml, lm_part, total;
   size_t step_ctr, lm_cnt, tx, tqkv, to, tact, tpart, lm_part2;
-  size_t lx, lqkv, lpart, lact, pO, pD, probe;
+  size_t lx, sx, lqkv, lpart, lact, pO, pD, probe;
   StepXSizes xz;
   int ns, nblk_lm;
 };
@@ -107,6 +107,7 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
   o = (o + 4095) & ~(size_t)4095;
   w.xz = stepx_sizes(B, c->hidden, Hkv, D, qpg, c->intermediate, M);
   w.lx = o; o += (size_t)kXcds * w.xz.lx * 8;
+  w.sx = o; o += (size_t)kXcds * w.xz.sx * 8;
   w.lqkv = o; o += (size_t)kXcds * w.xz.lqkv * 8;
   w.lpart = o; o += (size_t)kXcds * w.xz.lpart * 8;
   w.lact = o; o += (size_t)kXcds * w.xz.lact * 8;
@@ -334,6 +335,8 @@ bool stepx_fits(const kmr_config* c, int B, int nwg) {
   if (RPW > 8 * kStepWaves || RQ > 2 * kStepWaves || RA > 3 * kStepWaves) return false;
   // every group owns residual rows and act values (the hand-off order relies on it)
   if (RPW * (WPX - 1) >= H || RA * (WPX - 1) >= IX) return false;
+  // staged vectors: 8-column words owned whole, one element per thread, <= 64 producers
+  if (RPW % 8 != 0 || RA % 8 != 0 || RA > 32 || 4 * RPW > kStepThreads || WPX > kXMaxPerXcd) return false;
   const size_t lds = stepx_lds(4, H, RPW, D, QPG, GPX).total;
   return lds <= 160 * 1024;
 }
@@ -583,7 +586,9 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
     a.lx = at<uint64_t>(ws, w.lx); a.lqkv = at<uint64_t>(ws, w.lqkv);
     a.lpart = at<uint64_t>(ws, w.lpart); a.lact = at<uint64_t>(ws, w.lact);
     a.pO = at<uint64_t>(ws, w.pO); a.pD = at<uint64_t>(ws, w.pD);
+    a.sx = at<uint64_t>(ws, w.sx);
     a.x_lx = w.xz.lx; a.x_lqkv = w.xz.lqkv; a.x_lpart = w.xz.lpart; a.x_lact = w.xz.lact;
+    a.x_sx = w.xz.sx; a.srow_x = w.xz.srow_x; a.srow_a = w.xz.srow_a;
     a.B = batch; a.H = cfg->hidden; a.Hq = cfg->n_heads; a.Hkv = cfg->n_kv_heads;
     a.I = cfg->intermediate; a.V = cfg->vocab; a.L = cfg->n_layers; a.G = cfg->group_size;
     a.M = kv->max_len; a.cacheB = kv->batch; a.NS = w.ns; a.pad_id = cfg->pad_id;

@@ -40,6 +40,15 @@ __device__ __forceinline__ float row16_sum(float v) {
 __device__ __forceinline__ float row16_swap8(float v) { return dpp<0x128>(v); }
 
 // Sum over the 64-lane wave, returned uniform (from lane 63).
+// threadIdx.x behind an empty asm barrier: values derived from it are recomputed
+// where they are used instead of being hoisted out of long loops and kept live
+// (the persistent kernels run out of registers otherwise).
+__device__ __forceinline__ int otid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // 1/sqrt(x) with the hardware reciprocal square root (within 1 ulp); used for
 // RMSNorm scales, whose inputs are at least epsilon.
 __device__ __forceinline__ float rsqrt_f(float x) { return __builtin_amdgcn_rsqf(x); }

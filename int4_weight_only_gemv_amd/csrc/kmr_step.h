@@ -83,13 +83,14 @@ struct StepArgs {
   float2* lm_part;          // [B][nwg]
   // XCD-local exchange buffers (k_stepx only); "per XCD" regions are strided by
   // the x_* strides (in 64-bit words)
-  uint64_t* lx;             // per XCD [B][H]          residual stream copy
+  uint64_t* lx;             // per XCD [B][H]          x after the last layer
+  uint64_t* sx;             // per XCD [2][B][srow_x]  staged x: entering a layer, after O
   uint64_t* lqkv;           // per XCD [B][QX]         q/k/v of the XCD's kv heads
   uint64_t* lpart;          // per XCD [B][GPX][NSX][PW] attention split partials
-  uint64_t* lact;           // per XCD [B][IX]         SiLU(gate)*up of the XCD's slice
+  uint64_t* lact;           // per XCD [B][srow_a]     staged SiLU(gate)*up of the XCD's slice
   uint64_t* pO;             // [NX][B][H]              O split-K partials
   uint64_t* pD;             // [NX][B][H]              down split-K partials
-  long long x_lx, x_lqkv, x_lpart, x_lact;
+  long long x_lx, x_sx, x_lqkv, x_lpart, x_lact, srow_x, srow_a;
   int intra_plain;          // 1: XCD-local stores stay in the XCD's L2 (placement verified)
   // dims
   int B, H, Hq, Hkv, I, V, L, G, M, cacheB, NS, pad_id, eos_id;
@@ -130,17 +131,17 @@ __device__ __forceinline__ int swz(int i) {
 // its loads of a pass before checking any, so a poll costs one memory round
 // trip; `pre` runs after the first loads are issued (to overlap other work with
 // them).  Returns false, for the whole work-group, on timeout.
-template <int PT, typename Addr, typename Place, typename Pre>
+template <int PT, typename Addr, typename Place, typename Pre, int NT = kStepThreads>
 __device__ __forceinline__ bool gather_tagged(const uint64_t* src, int total, uint32_t tag,
                                               float* dst, Addr addr, Place place, Pre pre) {
-  const int tid = threadIdx.x;
+  const int tid = otid();
   bool ok = true;
   bool first = true;
-  for (int base = 0; base < total && ok; base += kStepThreads * PT) {
+  for (int base = 0; base < total && ok; base += NT * PT) {
     uint64_t v[PT];
     int idx[PT];
 #pragma unroll
-    for (int j = 0; j < PT; ++j) idx[j] = base + tid + kStepThreads * j;
+    for (int j = 0; j < PT; ++j) idx[j] = base + tid + NT * j;
     uint32_t spins = 0;
     bool fresh;
     do {
@@ -191,7 +192,7 @@ __device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
 __device__ __forceinline__ float lane_xor4(float v) {
   const float up = dpp<0x12C, 0xf, 0x5>(v);   // row_ror 12: lane i <- lane i + 4
   const float dn = dpp<0x124, 0xf, 0xA>(v);   // row_ror 4:  lane i <- lane i - 4
-  return (threadIdx.x & 4) ? dn : up;
+  return (otid() & 4) ? dn : up;
 }
 
 // Converts this thread's PT values of a [B][K] input (value j is element
@@ -206,7 +207,7 @@ template <int PT>
 __device__ __forceinline__ void stage_values(const float (&e)[PT], const bool (&has)[PT],
                                              const int (&wb)[PT], const int (&wk)[PT], int K,
                                              uint4* xs, float2* cc) {
-  const int lane = threadIdx.x & 63, CH = K >> 5, i8 = lane & 7;
+  const int lane = otid() & 63, CH = K >> 5, i8 = lane & 7;
   uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
 #pragma unroll
   for (int j = 0; j < PT; ++j) {
@@ -234,22 +235,22 @@ __device__ __forceinline__ void stage_values(const float (&e)[PT], const bool (&
 // Gathers a tagged [B][K] input (PT words per thread per pass, consecutive lanes
 // polling consecutive words), optionally RMS-normalises it with `gain`, and
 // stages it with stage_values.
-template <int BT, int PT>
+template <int BT, int PT, int NT = kStepThreads>
 __device__ __forceinline__ bool gather_stage(const uint64_t* src, int K, int B, uint32_t tag,
                                              const uint16_t* gain, float eps, uint4* xs, float2* cc,
                                              float* red) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int total = B * K;
   float inv[BT];
 #pragma unroll
   for (int b = 0; b < BT; ++b) inv[b] = 1.f;
-  for (int base = 0; base < total; base += kStepThreads * PT) {
+  for (int base = 0; base < total; base += NT * PT) {
     int idx[PT], wb[PT], wk[PT];
     bool has[PT];
     uint16_t graw[PT];
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      idx[j] = base + kStepThreads * j + tid;
+      idx[j] = base + NT * j + tid;
       has[j] = idx[j] < total;
       wb[j] = 0;
 #pragma unroll
@@ -291,14 +292,14 @@ __device__ __forceinline__ bool gather_stage(const uint64_t* src, int K, int B, 
         for (int j = 0; j < PT; ++j)
           if (has[j] && wb[j] == b) ss += x[j] * x[j];
         ss = wave_sum(ss);
-        if (lane == 0) red[b * kStepWaves + wave] = ss;
+        if (lane == 0) red[b * (NT / 64) + wave] = ss;
       }
       __syncthreads();
 #pragma unroll
       for (int b = 0; b < BT; ++b) {
         float ss = 0.f;
 #pragma unroll
-        for (int w = 0; w < kStepWaves; ++w) ss += red[b * kStepWaves + w];
+        for (int w = 0; w < (NT / 64); ++w) ss += red[b * (NT / 64) + w];
         inv[b] = rsqrt_f(ss / (float)K + eps);
       }
     }
@@ -328,7 +329,7 @@ template <int NR, int CPL>
 __device__ __forceinline__ void wrows_load(WRows<NR, CPL>& w, const uint8_t* packed,
                                            const uint32_t* sz, int K, int G, const int* row,
                                            const bool* ok) {
-  const int lane = threadIdx.x & 63, CH = K >> 5, NG = K / G;
+  const int lane = otid() & 63, CH = K >> 5, NG = K / G;
 #pragma unroll
   for (int i = 0; i < NR; ++i)
 #pragma unroll
@@ -362,7 +363,7 @@ __device__ __forceinline__ void dequant16(const uint4 raw, uint32_t (&p)[16]) {
 template <int BT, int NR, int CPL>
 __device__ __forceinline__ void wave_dot(const WRows<NR, CPL>& w, int K, int B, const uint4* xs,
                                          const float2* cc, float (&out)[NR][BT]) {
-  const int lane = threadIdx.x & 63, CH = K >> 5;
+  const int lane = otid() & 63, CH = K >> 5;
   float acc[NR][BT];
 #pragma unroll
   for (int i = 0; i < NR; ++i)
@@ -486,10 +487,10 @@ __host__ __device__ inline StepLds step_lds(int BT, int KMAX, int RPBX, int H, i
 // Final RMSNorm, lm_head rows of this group with the argmax of each batch row,
 // and (in the last group to finish) the argmax over all groups, the greedy-step
 // bookkeeping and the step counter.  xin holds the gathered fp32 [B][H] input.
-template <int BT>
+template <int BT, int NT = kStepThreads>
 __device__ __forceinline__ void step_tail(const StepArgs& a, float* xin, float* red, int* s_last_p,
                                           uint32_t step) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x, nwg = gridDim.x;
   const int B = a.B, M = a.M, K = a.H;
   int& s_last = *s_last_p;
@@ -511,7 +512,7 @@ __device__ __forceinline__ void step_tail(const StepArgs& a, float* xin, float* 
     for (int b = 0; b < BT; ++b) {
       const float ss = (red[b * 4 + 0] + red[b * 4 + 1]) + (red[b * 4 + 2] + red[b * 4 + 3]);
       const float inv = rsqrt_f(ss / (float)K + a.eps);
-      for (int k = tid; k < K; k += kStepThreads)
+      for (int k = tid; k < K; k += NT)
         xin[b * K + k] = b < B ? (xin[b * K + k] * inv) * bf16_to_f32(a.final_norm[k]) : 0.f;
     }
     __syncthreads();
@@ -523,7 +524,7 @@ __device__ __forceinline__ void step_tail(const StepArgs& a, float* xin, float* 
   float bv[BT]; int bi[BT];
 #pragma unroll
   for (int b = 0; b < BT; ++b) { bv[b] = -INFINITY; bi[b] = 0x7fffffff; }
-  for (int r0 = wave * LR; r0 < RPBL; r0 += kStepWaves * LR) {
+  for (int r0 = wave * LR; r0 < RPBL; r0 += (NT / 64) * LR) {
     uint4 w[LR][LCPL];
 #pragma unroll
     for (int r = 0; r < LR; ++r)
@@ -583,7 +584,7 @@ __device__ __forceinline__ void step_tail(const StepArgs& a, float* xin, float* 
   if (tid < B) {
     float v = s_bv[tid];
     int i = s_bi[tid];
-    for (int w2 = 1; w2 < kStepWaves; ++w2)
+    for (int w2 = 1; w2 < (NT / 64); ++w2)
       if (better(s_bv[w2 * BT + tid], s_bi[w2 * BT + tid], v, i)) { v = s_bv[w2 * BT + tid]; i = s_bi[w2 * BT + tid]; }
     st_devf(&a.lm_part[(size_t)tid * nwg + wg].x, v);
     st_devf(&a.lm_part[(size_t)tid * nwg + wg].y, __int_as_float(i));
@@ -600,11 +601,11 @@ __device__ __forceinline__ void step_tail(const StepArgs& a, float* xin, float* 
   // last group: argmax over all groups' partials (fixed tree order), then the
   // greedy-step bookkeeping, then the step counter
   float* t_v = xin;
-  int* t_i = reinterpret_cast<int*>(xin + kStepThreads);
+  int* t_i = reinterpret_cast<int*>(xin + NT);
   for (int b = 0; b < B; ++b) {
     float v = -INFINITY;
     int i = 0x7fffffff;
-    for (int t = tid; t < nwg; t += kStepThreads) {
+    for (int t = tid; t < nwg; t += NT) {
       const float pv = ld_devf(&a.lm_part[(size_t)b * nwg + t].x);
       const int pi = __float_as_int(ld_devf(&a.lm_part[(size_t)b * nwg + t].y));
       if (better(pv, pi, v, i)) { v = pv; i = pi; }
@@ -613,7 +614,7 @@ __device__ __forceinline__ void step_tail(const StepArgs& a, float* xin, float* 
     t_v[tid] = v;
     t_i[tid] = i;
     __syncthreads();
-    for (int wdt = kStepThreads / 2; wdt > 0; wdt >>= 1) {
+    for (int wdt = NT / 2; wdt > 0; wdt >>= 1) {
       if (tid < wdt && better(t_v[tid + wdt], t_i[tid + wdt], t_v[tid], t_i[tid])) {
         t_v[tid] = t_v[tid + wdt];
         t_i[tid] = t_i[tid + wdt];
@@ -648,7 +649,7 @@ template <int BT, int D, int QPG>
 __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int DPL = D / 16, HALF = D / 2, PW = QPG * (D + 2);   // partial words per split
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x, nwg = gridDim.x;
   const int B = a.B, H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, G = a.G, M = a.M;
   const int NQKV = (Hq + 2 * Hkv) * D, QD = Hq * D;

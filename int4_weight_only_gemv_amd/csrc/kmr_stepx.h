@@ -33,6 +33,8 @@ constexpr int kXSplit = 128;        // attention positions per split item
 constexpr int kXMergeChunk = 8;     // split partials merged per LDS pass
 constexpr int kXNarrowCpl = 3;      // max 32-column chunks per lane in the split-K GEMVs
 constexpr uint32_t kStatusTopology = 8u;
+constexpr int kXMaxPerXcd = 64;
+constexpr int kXGuRows = 6;        // gate/up rows per wave (3 act values)   // work-groups per XCD (sums-of-squares slots of a staged row)
 
 // Store of a tagged word that only groups of this XCD read.  A work-group-scope
 // store stays in the XCD's L2, where the device-scope polls of the XCD's other
@@ -46,6 +48,29 @@ __device__ __forceinline__ void publish_l(uint64_t* p, uint32_t tag, float v, in
     st_dev64(p, w);
 }
 
+// Per-head RMSNorm over head_dim (16 lanes x DPL dims, gains as bf16 pairs) then
+// rotate-half RoPE with the row's cos/sin table in LDS; the partner dim sits 8
+// lanes away in the same 16-lane row.
+template <int DPL>
+__device__ __forceinline__ void norm_rope_lds(float (&vals)[DPL], const uint32_t (&gp)[DPL / 2],
+                                              const float2* csb, int d0, int D, float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) ss += vals[e] * vals[e];
+  ss = row16_sum(ss);
+  const float inv = rsqrt_f(ss / (float)D + eps);
+#pragma unroll
+  for (int e = 0; e < DPL; ++e)
+    vals[e] = (vals[e] * inv) * ((e & 1) ? bf16_hi(gp[e >> 1]) : bf16_lo(gp[e >> 1]));
+  const int half = D >> 1;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    const float other = row16_swap8(vals[e]);
+    const float2 t = csb[(d0 + e) % half];
+    vals[e] = vals[e] * t.x + other * ((d0 < half) ? -t.y : t.y);
+  }
+}
+
 // ------------------------------------------------------------------ split-K GEMV
 // One weight row per 8-lane group, restricted to a KS-column slice: lane
 // (lane & 7) of the group takes 32-column chunks (lane & 7) + 8 t, t < kXNarrowCpl.
@@ -56,7 +81,7 @@ struct WNarrow {
 
 __device__ __forceinline__ void wnarrow_load(WNarrow& w, const uint8_t* packed, const uint32_t* sz,
                                              int K, int G, int k0, int KS, int row, bool ok) {
-  const int sub = threadIdx.x & 7, CHs = KS >> 5, NG = K / G;
+  const int sub = otid() & 7, CHs = KS >> 5, NG = K / G;
 #pragma unroll
   for (int t = 0; t < kXNarrowCpl; ++t) {
     const int c = sub + 8 * t;
@@ -75,7 +100,7 @@ __device__ __forceinline__ void wnarrow_load(WNarrow& w, const uint8_t* packed, 
 template <int BT>
 __device__ __forceinline__ void narrow_dot(const WNarrow& w, int KS, int B, const uint4* xs,
                                            const float2* cc, float (&out)[BT]) {
-  const int sub = threadIdx.x & 7, CHs = KS >> 5;
+  const int sub = otid() & 7, CHs = KS >> 5;
   float acc[BT];
 #pragma unroll
   for (int b = 0; b < BT; ++b) acc[b] = 0.f;
@@ -117,13 +142,14 @@ __device__ __forceinline__ void narrow_dot(const WNarrow& w, int KS, int B, cons
 
 // ------------------------------------------------------------------ reduce-scatter
 // Sums the kXcds split-K partials of this group's RPW residual rows in XCD order
-// 0..7, adds the sum to the owned rows, and publishes the new rows to this XCD's
-// copy of the residual stream.  Returns false, for the whole group, on timeout.
+// 0..7 and adds the sum to the owned rows.  Thread i < B*RPW gets element
+// (b, r) = (i / RPW, i % RPW) in xn (has: a row below H).  Returns false, for the
+// whole group, on timeout.
 __device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag, int B, int H,
-                                            int RPW, int row0, float* xown, float* buf,
-                                            uint64_t* lxx, uint32_t xtag, int plain) {
+                                            int RPW, int row0, float* xown, float* buf, float& xn,
+                                            bool& has_x) {
   constexpr int PT = 4;
-  const int tid = threadIdx.x, per = B * RPW, words = kXcds * per;
+  const int tid = otid(), per = B * RPW, words = kXcds * per;
   bool ok = true;
   for (int base = 0; base < words && ok; base += kStepThreads * PT) {
     uint64_t v[PT];
@@ -158,18 +184,175 @@ __device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag,
     }
   }
   if (__syncthreads_or(!ok)) return false;
-  for (int i = tid; i < per; i += kStepThreads) {
-    const int b = i / RPW, r = i - b * RPW, n = row0 + r;
-    if (n >= H) continue;
+  // per <= kStepThreads (checked on the host): one element per thread
+  const int b = tid / RPW, r = tid - b * RPW;
+  has_x = tid < per && row0 + r < H;
+  xn = 0.f;
+  if (has_x) {
     float sum = 0.f;
 #pragma unroll
     for (int y = 0; y < kXcds; ++y) sum += buf[(y * B + b) * RPW + r];
-    const float xn = xown[b * RPW + r] + sum;
+    xn = xown[b * RPW + r] + sum;
     xown[b * RPW + r] = xn;
-    publish_l(lxx + (size_t)b * H + n, xtag, xn, plain);
   }
   __syncthreads();
   return true;
+}
+
+// ------------------------------------------------------------------ staged vectors
+// A GEMV input published already in the layout the dot products read, so that
+// each consumer only copies it: per row b of K columns, at src + b * stride,
+//   [0, K/2)        fp16 pairs: word 4w + i (i < 4) of 8-column word w holds
+//                   (h[8w + i], h[8w + i + 4]), h = fp16(u) for even columns and
+//                   fp16(u / 16) for odd ones (matching the magic-bias weight pairs)
+//   [K/2, 3K/4)     per 8-column word: sum of h, then sum of the used values
+//                   (16 h for odd columns)
+//   [3K/4, 3K/4+n)  optional sums of squares of the unscaled input, one per producer
+// For an RMSNorm input, u = x * gain and the consumer scales its dot products by
+// 1/sqrt(sum of squares / K + eps): the norm's scale is common to the row.
+__device__ __forceinline__ void publish_lb(uint64_t* p, uint32_t tag, uint32_t bits, int plain) {
+  const uint64_t w = ((uint64_t)tag << 32) | bits;
+  if (plain)
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else
+    st_dev64(p, w);
+}
+
+// This lane's value u of column n (has: valid) of a staged row at dst.  The 8
+// lanes of an aligned group hold 8 consecutive columns starting at a multiple of
+// 8 (n & 7 == lane & 7).  Every lane of the wave must call this (DPP).
+__device__ __forceinline__ void stage_publish(uint64_t* dst, int K, int n, float u, bool has,
+                                              uint32_t tag, int plain) {
+  const int i8 = otid() & 7;
+  const _Float16 h = (_Float16)((i8 & 1) ? u * 0.0625f : u);
+  const float hf = (float)h;
+  const float uf = (i8 & 1) ? 16.0f * hf : hf;
+  const float other = lane_xor4(hf);
+  float sh = hf, su = uf;
+  sh += dpp<0xB1>(sh);
+  su += dpp<0xB1>(su);
+  sh += dpp<0x4E>(sh);
+  su += dpp<0x4E>(su);
+  sh += lane_xor4(sh);
+  su += lane_xor4(su);
+  if (has) {
+    const int w = n >> 3;
+    if (i8 < 4)
+      publish_lb(dst + 4 * w + i8, tag, __builtin_bit_cast(uint32_t, half2_t{h, (_Float16)other}), plain);
+    if (i8 == 0) {
+      publish_lb(dst + (K >> 1) + 2 * w, tag, __float_as_uint(sh), plain);
+      publish_lb(dst + (K >> 1) + 2 * w + 1, tag, __float_as_uint(su), plain);
+    }
+  }
+}
+
+// Gathers B staged rows of K columns (plus nss sums of squares each) into the
+// dot-product LDS layout (xs, cc) and, with nss > 0, s_inv[b] = 1/sqrt(ss/K + eps).
+// tmp: LDS scratch of BT*(K/4 + nss) floats.  Returns false, for the whole group,
+// on timeout.
+template <int BT, int PT>
+__device__ __forceinline__ bool gather_staged(const uint64_t* src, long long stride, int K, int B,
+                                              int nss, uint32_t tag, float eps, uint4* xs,
+                                              float2* cc, float* tmp, float* s_inv) {
+  const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int CH = K >> 5, K2 = K >> 1, K4 = K >> 2, per = K2 + K4 + nss, total = B * per;
+  uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
+  float* s_sum = tmp;              // [B][K/4]
+  float* s_ss = tmp + BT * K4;     // [B][nss]
+  bool ok = true;
+  for (int base = 0; base < total && ok; base += kStepThreads * PT) {
+    uint64_t v[PT];
+    int kk[PT], bb[PT];
+    bool has[PT];
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int i = base + kStepThreads * q + tid;
+      has[q] = i < total;
+      int b = 0;
+#pragma unroll
+      for (int t = 1; t < BT; ++t) b += i >= t * per ? 1 : 0;
+      bb[q] = b;
+      kk[q] = i - b * per;
+    }
+    uint32_t spins = 0;
+    bool fresh;
+    do {
+#pragma unroll
+      for (int q = 0; q < PT; ++q)
+        if (has[q]) v[q] = ld_dev64(src + (size_t)bb[q] * stride + kk[q]);
+      fresh = true;
+#pragma unroll
+      for (int q = 0; q < PT; ++q)
+        if (has[q]) fresh &= (uint32_t)(v[q] >> 32) == tag;
+      if (!fresh) {
+        if (++spins > kSpinLimit) { ok = false; break; }
+        __builtin_amdgcn_s_sleep(KMR_POLL_SLEEP);
+      }
+    } while (!fresh);
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      if (!has[q]) continue;
+      const int k = kk[q], b = bb[q];
+      const uint32_t bits = (uint32_t)v[q];
+      if (k < K2) {
+        const int w8 = k >> 2, i = k & 3;
+        xs32[((b * 4 + (w8 & 3)) * CH + (w8 >> 2)) * 4 + i] = bits;
+      } else if (k < K2 + K4) {
+        s_sum[b * K4 + (k - K2)] = __uint_as_float(bits);
+      } else {
+        s_ss[b * nss + (k - K2 - K4)] = __uint_as_float(bits);
+      }
+    }
+  }
+  if (__syncthreads_or(!ok)) return false;
+  for (int t = tid; t < B * CH; t += kStepThreads) {
+    int b = 0;
+#pragma unroll
+    for (int u = 1; u < BT; ++u) b += t >= u * CH ? 1 : 0;
+    const int c = t - b * CH;
+    const float* ws = s_sum + b * K4 + 8 * c;   // 4 words x (sum h, sum used)
+    const float sh = (ws[0] + ws[2]) + (ws[4] + ws[6]);
+    const float su = (ws[1] + ws[3]) + (ws[5] + ws[7]);
+    cc[b * CH + c] = make_float2(1024.0f * sh + 8.0f * su, su);
+  }
+  if (nss > 0 && wave == 0) {
+    // nss <= 64 (checked on the host)
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      const float ss = wave_sum((b < B && lane < nss) ? s_ss[b * nss + lane] : 0.f);
+      if (lane == 0 && b < B) s_inv[b] = rsqrt_f(ss / (float)K + eps);
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
+// Publishes x rows (element i = tid: row b = i / RPW, column row0 + i % RPW, valid
+// if has) of a staged RMSNorm input: u = x * gain, and this group's sum of squares
+// of each row at slot `slot` of the row's sums-of-squares area.  Every thread of
+// the group must call this.
+template <int BT>
+__device__ __forceinline__ void publish_staged_x(uint64_t* dst, long long stride, int H, int B,
+                                                 int RPW, int row0, float xn, bool has,
+                                                 const uint16_t* gain, int slot, uint32_t tag,
+                                                 int plain, float* red) {
+  const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = tid / RPW, n = row0 + (tid - b * RPW);
+  const float u = has ? xn * bf16_to_f32(gain[n]) : 0.f;
+  stage_publish(dst + (size_t)(has ? b : 0) * stride, H, n, u, has, tag, plain);
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb) {
+    const float ss = wave_sum((has && b == bb) ? xn * xn : 0.f);
+    if (lane == 0) red[bb * kStepWaves + wave] = ss;
+  }
+  __syncthreads();
+  if (tid < B) {
+    float ss = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStepWaves; ++w) ss += red[tid * kStepWaves + w];
+    publish_l(dst + (size_t)tid * stride + (H >> 1) + (H >> 2) + slot, tag, ss, plain);
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------ LDS layout
@@ -181,7 +364,7 @@ __device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag,
 //   cs    float2 [BT][D/2]      RoPE cos/sin of each row
 //   red   float [128]
 struct StepXLds {
-  size_t xs, cc, xin, xown, cs, red, total;
+  size_t xs, cc, xin, xown, cs, red, wgu, total;
 };
 
 __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int QPG, int GPX) {
@@ -203,13 +386,38 @@ __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int
   s.xown = take((size_t)BT * RPW * 4);
   s.cs = take((size_t)BT * (D / 2) * 8);
   s.red = take(128 * 4);
+  s.wgu = take((size_t)kStepWaves * kXGuRows * 64 * 20);   // gate/up codes (16 B) + scale/zero (4 B)
   s.total = o;
   return s;
 }
 
-// XCD-local buffer strides (64-bit words per XCD region, 4 KB aligned).
+// Streams this wave's gate/up weight rows straight into LDS (no registers held
+// while they are in flight): row i of the wave, lane l takes 32-column chunk l
+// (16 bytes of codes at codes + (i*64 + l)*16, its scale/zero word at szw + i*64 + l).
+// The data is in LDS once this wave's vector-memory count has drained.
+__device__ __forceinline__ void wrows_to_lds(const uint8_t* packed, const uint32_t* sz, int K, int G,
+                                             const int* row, uint4* codes, uint32_t* szw) {
+  const int lane = otid() & 63, NG = K / G;
+#pragma unroll
+  for (int i = 0; i < kXGuRows; ++i) {
+    __builtin_amdgcn_global_load_lds(packed + (size_t)row[i] * (K / 2) + 16 * lane, codes + i * 64, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(sz + (size_t)row[i] * NG + (32 * lane) / G, szw + i * 64, 4, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wrows_from_lds(WRows<kXGuRows, 1>& w, const uint4* codes, const uint32_t* szw) {
+  const int lane = otid() & 63;
+#pragma unroll
+  for (int i = 0; i < kXGuRows; ++i) {
+    w.raw[i][0] = codes[i * 64 + lane];
+    w.sz[i][0] = szw[i * 64 + lane];
+  }
+}
+
+// XCD-local buffer strides (64-bit words per XCD region, 4 KB aligned), and the
+// per-row strides of the staged vectors.
 struct StepXSizes {
-  long long lx, lqkv, lpart, lact;
+  long long lx, lqkv, lpart, lact, sx, srow_x, srow_a;
 };
 
 __host__ __device__ inline long long xalign(long long words) { return (words + 511) & ~511LL; }
@@ -217,10 +425,14 @@ __host__ __device__ inline long long xalign(long long words) { return (words + 5
 __host__ __device__ inline StepXSizes stepx_sizes(int B, int H, int Hkv, int D, int QPG, int I, int M) {
   const int GPX = Hkv / kXcds, NSX = (M + kXSplit - 1) / kXSplit;
   StepXSizes z{};
-  z.lx = xalign((long long)2 * B * H);   // two copies: x entering the layer, x after O
+  const int IX = I / kXcds;
+  z.srow_x = ((long long)(H / 2 + H / 4 + kXMaxPerXcd) + 63) & ~63LL;
+  z.srow_a = ((long long)(IX / 2 + IX / 4) + 63) & ~63LL;
+  z.lx = xalign((long long)B * H);             // fp32 x after the last layer (lm_head input)
+  z.sx = xalign((long long)2 * B * z.srow_x);  // staged x: entering the layer, after O
   z.lqkv = xalign((long long)B * GPX * (QPG + 2) * D);
   z.lpart = xalign((long long)B * GPX * NSX * QPG * (D + 2));
-  z.lact = xalign((long long)B * (I / kXcds));
+  z.lact = xalign((long long)B * z.srow_a);    // staged SiLU(gate)*up
   return z;
 }
 
@@ -228,7 +440,7 @@ template <int BT, int D, int QPG>
 __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int DPL = D / 16, HALF = D / 2, PW = QPG * (D + 2);
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x, nwg = gridDim.x;
   const int x = wg % kXcds, j = wg / kXcds, WPX = nwg / kXcds;
   const int B = a.B, H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, G = a.G, M = a.M;
@@ -243,14 +455,17 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   float* xown = reinterpret_cast<float*>(smem + Ld.xown);
   float2* cs = reinterpret_cast<float2*>(smem + Ld.cs);
   float* red = reinterpret_cast<float*>(smem + Ld.red);
-  uint64_t* lx0 = a.lx + (size_t)x * a.x_lx;          // x entering a layer
-  uint64_t* lx1 = lx0 + (size_t)B * H;                // x after the O projection
+  uint64_t* lx0 = a.lx + (size_t)x * a.x_lx;          // x after the last layer
+  uint64_t* sx0 = a.sx + (size_t)x * a.x_sx;          // staged x entering a layer
+  uint64_t* sx1 = sx0 + (size_t)B * a.srow_x;         // staged x after the O projection
+  const long long SX = a.srow_x, SA = a.srow_a;
   uint64_t* lqkv = a.lqkv + (size_t)x * a.x_lqkv;
   uint64_t* lpart = a.lpart + (size_t)x * a.x_lpart;
   uint64_t* lact = a.lact + (size_t)x * a.x_lact;
   __shared__ int s_last;
   __shared__ int s_c[16];
   __shared__ int s_ns[16];
+  __shared__ float s_inv[4];
 
   const uint32_t step = (a.step_ctr[0] + 1u) & 0x7fffffu;
   auto tag = [&](int phase) -> uint32_t { return (step << 9) | (uint32_t)phase; };
@@ -276,23 +491,27 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     sincos(p * inv_freq, &sn, &cn);
     cs[b * HALF + jj] = make_float2((float)cn, (float)sn);
   }
-  for (int i = tid; i < B * RPW; i += kStepThreads) {
-    const int b = i / RPW, r = i - b * RPW, n = j * RPW + r;
-    if (n >= H) continue;
-    const int id = (a.finished && a.finished[b]) ? a.pad_id : a.ids[b];
-    const bool ok = id >= 0 && id < a.V;
-    if (!ok && n == 0 && x == 0) raise_status(a.status, 2u);
-    const float v = ok ? bf16_to_f32(a.embed[(size_t)id * H + n]) : 0.f;
-    xown[b * RPW + r] = v;
-    publish_l(lx0 + (size_t)b * H + n, tag(1), v, plain);
+  {
+    // embedding rows of this group (B * RPW <= kStepThreads), published staged
+    // for the first layer's input norm
+    const int b = tid / RPW, r = tid - b * RPW, n = j * RPW + r;
+    const bool has = tid < B * RPW && n < H;
+    float v = 0.f;
+    if (has) {
+      const int id = (a.finished && a.finished[b]) ? a.pad_id : a.ids[b];
+      const bool ok = id >= 0 && id < a.V;
+      if (!ok && n == 0 && x == 0) raise_status(a.status, 2u);
+      v = ok ? bf16_to_f32(a.embed[(size_t)id * H + n]) : 0.f;
+      xown[b * RPW + r] = v;
+    }
+    publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, v, has, a.layers[0].in_norm, j, tag(1), plain, red);
   }
-  __syncthreads();
   KMR_TRACE_MARK(0);
 
   for (int l = 0; l < a.L && alive; ++l) {
     const StepLayer& Ly = a.layers[l];
-    const int ph = 1 + 6 * l;   // tags: ph x (lx0), +1 qkv, +2 partials, +3 O partials,
-                                // +4 x after O (lx1), +5 act, +6 down partials and next x
+    const int ph = 1 + 6 * l;   // tags: ph x (sx0), +1 qkv, +2 partials, +3 O partials,
+                                // +4 x after O (sx1), +5 act, +6 down partials and next x
     [[maybe_unused]] const int tev = l < 5 ? 1 + 11 * l : 64;
     // ================= QKV rows of this XCD's kv heads: RQ rows per group, 2 per wave
     {
@@ -314,7 +533,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       }
       WRows<NR, 1> w;
       wrows_load(w, Ly.qkv_p, Ly.qkv_s, H, G, row, ok);
-      if (!gather_stage<BT, 4 * BT>(lx0, H, B, tag(ph), Ly.in_norm, a.eps, xs, cc, red)) {
+      if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, WPX, tag(ph), a.eps, xs, cc, xin, s_inv)) {
         alive = false;
         break;
       }
@@ -322,13 +541,14 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       float out[NR][BT];
       wave_dot<BT, NR, 1>(w, H, B, xs, cc, out);
       if (lane < B) {
+        const float inv = s_inv[lane];
 #pragma unroll
         for (int i = 0; i < NR; ++i)
           if (ok[i]) {
             float v = out[i][0];
 #pragma unroll
             for (int b = 1; b < BT; ++b) if (lane == b) v = out[i][b];
-            publish_l(lqkv + (size_t)lane * QX + lr[i], tag(ph + 1), v, plain);
+            publish_l(lqkv + (size_t)lane * QX + lr[i], tag(ph + 1), v * inv, plain);
           }
       }
     }
@@ -362,11 +582,12 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
             for (int e = 0; e < DPL / 2; ++e) kr[it][e] = vr[it][e] = 0u;
           }
         }
-        float gq[DPL], gk[DPL];
+        // q/k norm gains of this lane's dims as bf16 pairs (d0 is a multiple of 8)
+        uint32_t gq[DPL / 2], gk[DPL / 2];
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) {
-          gq[e] = bf16_to_f32(Ly.q_norm[d0 + e]);
-          gk[e] = bf16_to_f32(Ly.k_norm[d0 + e]);
+        for (int e = 0; e < DPL / 2; ++e) {
+          gq[e] = reinterpret_cast<const uint32_t*>(Ly.q_norm + d0)[e];
+          gk[e] = reinterpret_cast<const uint32_t*>(Ly.k_norm + d0)[e];
         }
         // q heads of kv head g (contiguous), then k, then v: one gather
         float* qv = xin;
@@ -391,16 +612,9 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           kf[e] = qv[QPG * D + d0 + e];
           vf[e] = qv[(QPG + 1) * D + d0 + e];
         }
-        float cs_c[DPL], cs_s[DPL];
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) {
-          const float2 t = cs[b * HALF + ((d0 + e) % HALF)];
-          cs_c[e] = t.x;
-          cs_s[e] = (d0 < HALF) ? -t.y : t.y;
-        }
-#pragma unroll
-        for (int h = 0; h < QPG; ++h) norm_rope<DPL>(q[h], gq, cs_c, cs_s, D, a.eps);
-        norm_rope<DPL>(kf, gk, cs_c, cs_s, D, a.eps);
+        for (int h = 0; h < QPG; ++h) norm_rope_lds<DPL>(q[h], gq, cs + b * HALF, d0, D, a.eps);
+        norm_rope_lds<DPL>(kf, gk, cs + b * HALF, d0, D, a.eps);
 #pragma unroll
         for (int e = 0; e < DPL; ++e) { kf[e] = round_bf16(kf[e]); vf[e] = round_bf16(vf[e]); }
         KMR_TRACE_MARK(l == 1 ? 59 : 64);
@@ -641,40 +855,63 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       grow[i] = gok[i] ? x * IX + gla[i] : 0;
       grow[NP + i] = gok[i] ? x * IX + gla[i] + I : 0;
     }
-    WRows<2 * NP, 1> wgu;
-    wrows_load(wgu, Ly.gu_p, Ly.gu_s, H, G, grow, gok);
-    // ================= RS_O: x rows after O, published to the XCD's copy
-    if (!reduce_rows(a.pO, tag(ph + 3), B, H, RPW, j * RPW, xown, xin, lx1, tag(ph + 4), plain)) {
-      alive = false;
-      break;
+    // (K = H = 64 chunks of 32 columns: one chunk per lane, checked on the host)
+    uint4* gu_codes = reinterpret_cast<uint4*>(smem + Ld.wgu) + wave * kXGuRows * 64;
+    uint32_t* gu_sz = reinterpret_cast<uint32_t*>(smem + Ld.wgu + (size_t)kStepWaves * kXGuRows * 64 * 16) +
+                      wave * kXGuRows * 64;
+    wrows_to_lds(Ly.gu_p, Ly.gu_s, H, G, grow, gu_codes, gu_sz);
+    // ================= RS_O: x rows after O, published staged for post_norm
+    {
+      float xn;
+      bool hx;
+      if (!reduce_rows(a.pO, tag(ph + 3), B, H, RPW, j * RPW, xown, xin, xn, hx)) {
+        alive = false;
+        break;
+      }
+      publish_staged_x<BT>(sx1, SX, H, B, RPW, j * RPW, xn, hx, Ly.post_norm, j, tag(ph + 4), plain, red);
     }
     KMR_TRACE_MARK(tev + 6);
     // ================= gate-up + SiLU over the XCD's slice
     {
-      if (!gather_stage<BT, 4 * BT>(lx1, H, B, tag(ph + 4), Ly.post_norm, a.eps, xs, cc, red)) {
+      if (!gather_staged<BT, 4 * BT>(sx1, SX, H, B, WPX, tag(ph + 4), a.eps, xs, cc, xin, s_inv)) {
         alive = false;
         break;
       }
       KMR_TRACE_MARK(tev + 7);
       float out[2 * NP][BT];
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gate/up rows are in LDS
+      WRows<2 * NP, 1> wgu;
+      wrows_from_lds(wgu, gu_codes, gu_sz);
       wave_dot<BT, 2 * NP, 1>(wgu, H, B, xs, cc, out);
+      // act values of this group into LDS [b][32], then published staged
+      float* s_act = xin;
       if (lane < B) {
+        const float inv = s_inv[lane];
 #pragma unroll
-        for (int i = 0; i < NP; ++i)
-          if (gok[i]) {
-            float gt = out[i][0], up = out[NP + i][0];
+        for (int i = 0; i < NP; ++i) {
+          float gt = out[i][0], up = out[NP + i][0];
 #pragma unroll
-            for (int b = 1; b < BT; ++b) if (lane == b) { gt = out[i][b]; up = out[NP + i][b]; }
-            publish_l(lact + (size_t)lane * IX + gla[i], tag(ph + 5), gt / (1.0f + expf(-gt)) * up, plain);
-          }
+          for (int b = 1; b < BT; ++b) if (lane == b) { gt = out[i][b]; up = out[NP + i][b]; }
+          gt *= inv;
+          up *= inv;
+          if (gok[i]) s_act[lane * 32 + wave * NP + i] = gt / (1.0f + expf(-gt)) * up;
+        }
       }
+      __syncthreads();
+      {
+        const int b = tid >> 5, t = tid & 31;
+        const bool has = b < B && t < RA && j * RA + t < IX;
+        stage_publish(lact + (size_t)(has ? b : 0) * SA, IX, j * RA + t, has ? s_act[tid] : 0.f, has,
+                      tag(ph + 5), plain);
+      }
+      __syncthreads();   // s_act is LDS scratch of the next gather
     }
     KMR_TRACE_MARK(tev + 8);
     // ================= down split-K over the XCD's slice, then RS_D
     {
       WNarrow wd;
       wnarrow_load(wd, Ly.d_p, Ly.d_s, I, G, x * IX, IX, ook ? orow : 0, ook);
-      if (!gather_stage<BT, 2 * BT>(lact, IX, B, tag(ph + 5), nullptr, a.eps, xs, cc, red)) {
+      if (!gather_staged<BT, 4 * BT>(lact, SA, IX, B, 0, tag(ph + 5), a.eps, xs, cc, xin, s_inv)) {
         alive = false;
         break;
       }
@@ -689,9 +926,20 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         publish(a.pD + ((size_t)x * B + sub) * H + orow, tag(ph + 6), v);
       }
     }
-    if (!reduce_rows(a.pD, tag(ph + 6), B, H, RPW, j * RPW, xown, xin, lx0, tag(ph + 6), plain)) {
-      alive = false;
-      break;
+    {
+      float xn;
+      bool hx;
+      if (!reduce_rows(a.pD, tag(ph + 6), B, H, RPW, j * RPW, xown, xin, xn, hx)) {
+        alive = false;
+        break;
+      }
+      if (l + 1 < a.L) {
+        publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, a.layers[l + 1].in_norm, j, tag(ph + 6),
+                             plain, red);
+      } else if (hx) {
+        const int b = tid / RPW;
+        publish_l(lx0 + (size_t)b * H + j * RPW + (tid - b * RPW), tag(ph + 6), xn, plain);
+      }
     }
     KMR_TRACE_MARK(tev + 10);
   }
