@@ -71,6 +71,35 @@ __device__ __forceinline__ void norm_rope_lds(float (&vals)[DPL], const uint32_t
   }
 }
 
+// K/V rows of attention item `item` (row b, local kv head, 128-position split):
+// 16-lane row `row` of wave `wave` takes positions s*128 + 4*row + {0..3}, this
+// lane DPL dims of each; slots at or past the row's cache position read as zero
+// (the new slot's k/v come from the QKV phase).
+template <int DPL>
+__device__ __forceinline__ void attn_load_kv(uint32_t (&kr)[4][DPL / 2], uint32_t (&vr)[4][DPL / 2],
+                                             const uint16_t* kc, const uint16_t* vc, int item,
+                                             const int* s_ns, const int* s_c, int GPX, int x, int Hkv,
+                                             int M, int D, int wave) {
+  int b = 0, rem = item;
+  while (rem >= GPX * s_ns[b]) { rem -= GPX * s_ns[b]; ++b; }
+  const int ns = s_ns[b], gl = rem / ns, s = rem - gl * ns, g = x * GPX + gl, c = s_c[b];
+  const int lane = otid() & 63, row = wave * 4 + (lane >> 4), d0 = (lane & 15) * DPL;
+  const size_t head_base = ((size_t)b * Hkv + g) * M;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int p = s * kXSplit + 4 * row + it;
+    if (p < c) {
+      const uint32_t* ks = reinterpret_cast<const uint32_t*>(kc + (head_base + p) * D + d0);
+      const uint32_t* vs = reinterpret_cast<const uint32_t*>(vc + (head_base + p) * D + d0);
+#pragma unroll
+      for (int e = 0; e < DPL / 2; ++e) { kr[it][e] = ks[e]; vr[it][e] = vs[e]; }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL / 2; ++e) kr[it][e] = vr[it][e] = 0u;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ split-K GEMV
 // One weight row per 8-lane group, restricted to a KS-column slice: lane
 // (lane & 7) of the group takes 32-column chunks (lane & 7) + 8 t, t < kXNarrowCpl.
@@ -562,26 +591,14 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       int total = 0;
       for (int b = 0; b < B; ++b) total += GPX * s_ns[b];
       for (int item = j; item < total; item += WPX) {
+        uint32_t kr[4][DPL / 2], vr[4][DPL / 2];
+        attn_load_kv<DPL>(kr, vr, kc, vc, item, s_ns, s_c, GPX, x, Hkv, M, D, wave);
         int b = 0, rem = item;
         while (rem >= GPX * s_ns[b]) { rem -= GPX * s_ns[b]; ++b; }
         const int ns = s_ns[b], gl = rem / ns, s = rem - gl * ns, g = x * GPX + gl, c = s_c[b];
         const int rr = lane >> 4, li = lane & 15, row = wave * 4 + rr, d0 = li * DPL;
         const size_t head_base = ((size_t)b * Hkv + g) * M;
-        // cache reads first: row `row` takes positions s*128 + 4*row + {0..3}
-        uint32_t kr[4][DPL / 2], vr[4][DPL / 2];
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int p = s * kXSplit + 4 * row + it;
-          if (p < c) {
-            const uint32_t* ks = reinterpret_cast<const uint32_t*>(kc + (head_base + p) * D + d0);
-            const uint32_t* vs = reinterpret_cast<const uint32_t*>(vc + (head_base + p) * D + d0);
-#pragma unroll
-            for (int e = 0; e < DPL / 2; ++e) { kr[it][e] = ks[e]; vr[it][e] = vs[e]; }
-          } else {
-#pragma unroll
-            for (int e = 0; e < DPL / 2; ++e) kr[it][e] = vr[it][e] = 0u;
-          }
-        }
+
         // q/k norm gains of this lane's dims as bf16 pairs (d0 is a multiple of 8)
         uint32_t gq[DPL / 2], gk[DPL / 2];
 #pragma unroll
@@ -698,20 +715,24 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         // merge the 8 wave states of each head: the log-sum-exp weights are
         // computed once per (wave, head), then each output is 8 multiply-adds
         float* s_e = s_w + kStepWaves * QPG * (D + 2);   // [8][QPG] weights, [QPG] max, [QPG] sum
-        if (tid < QPG) {
-          float Mx = -INFINITY;
-#pragma unroll
-          for (int wv = 0; wv < kStepWaves; ++wv) Mx = fmaxf(Mx, s_w[(wv * QPG + tid) * (D + 2) + D]);
-          float Ls = 0.f;
-#pragma unroll
-          for (int wv = 0; wv < kStepWaves; ++wv) {
-            const float mw = s_w[(wv * QPG + tid) * (D + 2) + D];
-            const float e = mw == -INFINITY ? 0.f : exp2f(mw - Mx);
-            s_e[wv * QPG + tid] = e;
-            Ls += e * s_w[(wv * QPG + tid) * (D + 2) + D + 1];
+        static_assert(kStepWaves * QPG == 16, "one 16-lane row holds every (wave, head) state");
+        if (wave == 0 && lane < 16) {
+          // lane t = wave * QPG + head: the states of one head sit at lane ^ 2, ^ 4, ^ 8
+          const float mw = s_w[lane * (D + 2) + D], lw = s_w[lane * (D + 2) + D + 1];
+          float Mx = mw;
+          Mx = fmaxf(Mx, dpp<0x4E>(Mx));        // lane ^ 2
+          Mx = fmaxf(Mx, lane_xor4(Mx));        // lane ^ 4
+          Mx = fmaxf(Mx, row16_swap8(Mx));      // lane ^ 8
+          const float e = mw == -INFINITY ? 0.f : exp2f(mw - Mx);
+          float Ls = e * lw;
+          Ls += dpp<0x4E>(Ls);
+          Ls += lane_xor4(Ls);
+          Ls += row16_swap8(Ls);
+          s_e[lane] = e;
+          if (lane < QPG) {
+            s_e[kStepWaves * QPG + lane] = Mx;
+            s_e[(kStepWaves + 1) * QPG + lane] = Ls;
           }
-          s_e[kStepWaves * QPG + tid] = Mx;
-          s_e[(kStepWaves + 1) * QPG + tid] = Ls;
         }
         __syncthreads();
         KMR_TRACE_MARK(l == 1 ? 62 : 64);
@@ -783,20 +804,31 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         if (__syncthreads_or(!ok)) { alive = false; break; }
         // log-sum-exp weights of this chunk's splits, once per (row, kv head, q head)
         float* s_wt = xin + words;   // [B*GPX][QPG][kXMergeChunk + 2]: weights, max, sum
-        if (tid < B * GPX * QPG) {
-          const int seg = tid / QPG, h = tid - seg * QPG, b = seg / GPX;
-          const int n = s_ns[b] - t0 < kXMergeChunk ? s_ns[b] - t0 : kXMergeChunk;
-          float* wt = s_wt + tid * (kXMergeChunk + 2);
-          float Mc = -INFINITY, Lc = 0.f;
-          for (int t = 0; t < n; ++t) Mc = fmaxf(Mc, xin[((size_t)seg * kXMergeChunk + t) * PW + h * (D + 2) + D]);
-          for (int t = 0; t < n; ++t) {
-            const float* pt = xin + ((size_t)seg * kXMergeChunk + t) * PW + h * (D + 2);
-            const float e = pt[D] == -INFINITY ? 0.f : exp2f(pt[D] - Mc);
+        static_assert(kXMergeChunk == 8, "one 8-lane group per (row, kv head, q head)");
+        if (wave == 0) {
+          // lane = 8 * (seg * QPG + h) + t: split t of the chunk (B * GPX * QPG <= 8, host-checked)
+          const int sh = lane >> 3, t = lane & 7, seg = sh / QPG, h = sh - seg * QPG;
+          const bool live = seg < B * GPX;
+          const int n = live ? (s_ns[seg / GPX] - t0 < kXMergeChunk ? s_ns[seg / GPX] - t0 : kXMergeChunk) : 0;
+          const float* pt = xin + ((size_t)seg * kXMergeChunk + t) * PW + h * (D + 2);
+          const float mt = t < n ? pt[D] : -INFINITY, lt = t < n ? pt[D + 1] : 0.f;
+          float Mc = mt;
+          Mc = fmaxf(Mc, dpp<0xB1>(Mc));   // lane ^ 1
+          Mc = fmaxf(Mc, dpp<0x4E>(Mc));   // lane ^ 2
+          Mc = fmaxf(Mc, lane_xor4(Mc));   // lane ^ 4
+          const float e = mt == -INFINITY ? 0.f : exp2f(mt - Mc);
+          float Lc = e * lt;
+          Lc += dpp<0xB1>(Lc);
+          Lc += dpp<0x4E>(Lc);
+          Lc += lane_xor4(Lc);
+          if (live) {
+            float* wt = s_wt + sh * (kXMergeChunk + 2);
             wt[t] = e;
-            Lc += e * pt[D + 1];
+            if (t == 0) {
+              wt[kXMergeChunk] = Mc;
+              wt[kXMergeChunk + 1] = Lc;
+            }
           }
-          wt[kXMergeChunk] = Mc;
-          wt[kXMergeChunk + 1] = Lc;
         }
         __syncthreads();
 #pragma unroll
