@@ -48,54 +48,37 @@ __device__ __forceinline__ void publish_l(uint64_t* p, uint32_t tag, float v, in
     st_dev64(p, w);
 }
 
-// Per-head RMSNorm over head_dim (16 lanes x DPL dims, gains as bf16 pairs) then
-// rotate-half RoPE with the row's cos/sin table in LDS; the partner dim sits 8
-// lanes away in the same 16-lane row.
-template <int DPL>
-__device__ __forceinline__ void norm_rope_lds(float (&vals)[DPL], const uint32_t (&gp)[DPL / 2],
-                                              const float2* csb, int d0, int D, float eps) {
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) ss += vals[e] * vals[e];
-  ss = row16_sum(ss);
-  const float inv = rsqrt_f(ss / (float)D + eps);
-#pragma unroll
-  for (int e = 0; e < DPL; ++e)
-    vals[e] = (vals[e] * inv) * ((e & 1) ? bf16_hi(gp[e >> 1]) : bf16_lo(gp[e >> 1]));
-  const int half = D >> 1;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    const float other = row16_swap8(vals[e]);
-    const float2 t = csb[(d0 + e) % half];
-    vals[e] = vals[e] * t.x + other * ((d0 < half) ? -t.y : t.y);
-  }
-}
-
 // K/V rows of attention item `item` (row b, local kv head, 128-position split):
 // 16-lane row `row` of wave `wave` takes positions s*128 + 4*row + {0..3}, this
-// lane DPL dims of each; slots at or past the row's cache position read as zero
-// (the new slot's k/v come from the QKV phase).
+// lane DPL dims of each.  The loads are unconditional (slot clamped into the
+// cache) so that nothing waits for them here; the attention loop ignores slots
+// past the row's cache position and takes the new slot's k/v from the QKV phase.
 template <int DPL>
 __device__ __forceinline__ void attn_load_kv(uint32_t (&kr)[4][DPL / 2], uint32_t (&vr)[4][DPL / 2],
                                              const uint16_t* kc, const uint16_t* vc, int item,
                                              const int* s_ns, const int* s_c, int GPX, int x, int Hkv,
                                              int M, int D, int wave) {
+  static_assert(DPL == 4 || DPL == 8, "head_dim 64 or 128");
   int b = 0, rem = item;
   while (rem >= GPX * s_ns[b]) { rem -= GPX * s_ns[b]; ++b; }
-  const int ns = s_ns[b], gl = rem / ns, s = rem - gl * ns, g = x * GPX + gl, c = s_c[b];
+  const int ns = s_ns[b], gl = rem / ns, s = rem - gl * ns, g = x * GPX + gl;
   const int lane = otid() & 63, row = wave * 4 + (lane >> 4), d0 = (lane & 15) * DPL;
   const size_t head_base = ((size_t)b * Hkv + g) * M;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int p = s * kXSplit + 4 * row + it;
-    if (p < c) {
-      const uint32_t* ks = reinterpret_cast<const uint32_t*>(kc + (head_base + p) * D + d0);
-      const uint32_t* vs = reinterpret_cast<const uint32_t*>(vc + (head_base + p) * D + d0);
-#pragma unroll
-      for (int e = 0; e < DPL / 2; ++e) { kr[it][e] = ks[e]; vr[it][e] = vs[e]; }
+    int p = s * kXSplit + 4 * row + it;
+    p = p < M ? p : M - 1;
+    // DPL bf16 = DPL * 2 bytes per lane, aligned to that size (d0 = lane * DPL)
+    if constexpr (DPL == 8) {
+      const uint4 k4 = *reinterpret_cast<const uint4*>(kc + (head_base + p) * D + d0);
+      const uint4 v4 = *reinterpret_cast<const uint4*>(vc + (head_base + p) * D + d0);
+      kr[it][0] = k4.x; kr[it][1] = k4.y; kr[it][2] = k4.z; kr[it][3] = k4.w;
+      vr[it][0] = v4.x; vr[it][1] = v4.y; vr[it][2] = v4.z; vr[it][3] = v4.w;
     } else {
-#pragma unroll
-      for (int e = 0; e < DPL / 2; ++e) kr[it][e] = vr[it][e] = 0u;
+      const uint2 k2 = *reinterpret_cast<const uint2*>(kc + (head_base + p) * D + d0);
+      const uint2 v2 = *reinterpret_cast<const uint2*>(vc + (head_base + p) * D + d0);
+      kr[it][0] = k2.x; kr[it][1] = k2.y;
+      vr[it][0] = v2.x; vr[it][1] = v2.y;
     }
   }
 }
@@ -356,18 +339,25 @@ __device__ __forceinline__ bool gather_staged(const uint64_t* src, long long str
   return true;
 }
 
+// The norm gain of this thread's column in publish_staged_x, requested early (an
+// in-range address, no use here) so that nothing waits on it before it is needed.
+__device__ __forceinline__ uint16_t staged_gain(const uint16_t* gain, int H, int RPW, int row0) {
+  const int tid = otid(), b = tid / RPW;
+  const int n = row0 + (tid - b * RPW);
+  return gain[n < H ? n : H - 1];
+}
+
 // Publishes x rows (element i = tid: row b = i / RPW, column row0 + i % RPW, valid
-// if has) of a staged RMSNorm input: u = x * gain, and this group's sum of squares
-// of each row at slot `slot` of the row's sums-of-squares area.  Every thread of
-// the group must call this.
+// if has) of a staged RMSNorm input: u = x * gain (g: this column's bf16 gain from
+// staged_gain), and this group's sum of squares of each row at slot `slot` of the
+// row's sums-of-squares area.  Every thread of the group must call this.
 template <int BT>
 __device__ __forceinline__ void publish_staged_x(uint64_t* dst, long long stride, int H, int B,
-                                                 int RPW, int row0, float xn, bool has,
-                                                 const uint16_t* gain, int slot, uint32_t tag,
-                                                 int plain, float* red) {
+                                                 int RPW, int row0, float xn, bool has, uint16_t g,
+                                                 int slot, uint32_t tag, int plain, float* red) {
   const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = tid / RPW, n = row0 + (tid - b * RPW);
-  const float u = has ? xn * bf16_to_f32(gain[n]) : 0.f;
+  const float u = has ? xn * bf16_to_f32(g) : 0.f;
   stage_publish(dst + (size_t)(has ? b : 0) * stride, H, n, u, has, tag, plain);
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) {
@@ -533,7 +523,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       v = ok ? bf16_to_f32(a.embed[(size_t)id * H + n]) : 0.f;
       xown[b * RPW + r] = v;
     }
-    publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, v, has, a.layers[0].in_norm, j, tag(1), plain, red);
+    publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, v, has, staged_gain(a.layers[0].in_norm, H, RPW, j * RPW),
+                         j, tag(1), plain, red);
   }
   KMR_TRACE_MARK(0);
 
@@ -542,6 +533,11 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     const int ph = 1 + 6 * l;   // tags: ph x (sx0), +1 qkv, +2 partials, +3 O partials,
                                 // +4 x after O (sx1), +5 act, +6 down partials and next x
     [[maybe_unused]] const int tev = l < 5 ? 1 + 11 * l : 64;
+    uint16_t* kc = a.kc + (size_t)l * a.cacheB * Hkv * M * D;
+    uint16_t* vc = a.vc + (size_t)l * a.cacheB * Hkv * M * D;
+    int total = 0;
+    for (int b = 0; b < B; ++b) total += GPX * s_ns[b];
+    uint32_t kr[4][DPL / 2], vr[4][DPL / 2];
     // ================= QKV rows of this XCD's kv heads: RQ rows per group, 2 per wave
     {
       constexpr int NR = 2;
@@ -562,6 +558,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       }
       WRows<NR, 1> w;
       wrows_load(w, Ly.qkv_p, Ly.qkv_s, H, G, row, ok);
+      asm volatile("" ::: "memory");   // keep the weight requests ahead of the polls
       if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, WPX, tag(ph), a.eps, xs, cc, xin, s_inv)) {
         alive = false;
         break;
@@ -581,31 +578,23 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           }
       }
     }
+    // K/V rows of this group's first attention item: requested right after its
+    // q/k/v rows are out, so that their latency overlaps the hand-off
+    asm volatile("" ::: "memory");   // not ahead of the q/k/v stores
+    if (j < total) attn_load_kv<DPL>(kr, vr, kc, vc, j, s_ns, s_c, GPX, x, Hkv, M, D, wave);
     KMR_TRACE_MARK(tev + 1);
     const int orow = j * RPW + wave * 8 + (lane >> 3);   // O and down rows of this lane group
     const bool ook = wave * 8 + (lane >> 3) < RPW && orow < H;
     // ================= attention items (row, local kv head, split) of this XCD
     {
-      uint16_t* kc = a.kc + (size_t)l * a.cacheB * Hkv * M * D;
-      uint16_t* vc = a.vc + (size_t)l * a.cacheB * Hkv * M * D;
-      int total = 0;
-      for (int b = 0; b < B; ++b) total += GPX * s_ns[b];
       for (int item = j; item < total; item += WPX) {
-        uint32_t kr[4][DPL / 2], vr[4][DPL / 2];
-        attn_load_kv<DPL>(kr, vr, kc, vc, item, s_ns, s_c, GPX, x, Hkv, M, D, wave);
+        if (item != j) attn_load_kv<DPL>(kr, vr, kc, vc, item, s_ns, s_c, GPX, x, Hkv, M, D, wave);
         int b = 0, rem = item;
         while (rem >= GPX * s_ns[b]) { rem -= GPX * s_ns[b]; ++b; }
         const int ns = s_ns[b], gl = rem / ns, s = rem - gl * ns, g = x * GPX + gl, c = s_c[b];
         const int rr = lane >> 4, li = lane & 15, row = wave * 4 + rr, d0 = li * DPL;
         const size_t head_base = ((size_t)b * Hkv + g) * M;
 
-        // q/k norm gains of this lane's dims as bf16 pairs (d0 is a multiple of 8)
-        uint32_t gq[DPL / 2], gk[DPL / 2];
-#pragma unroll
-        for (int e = 0; e < DPL / 2; ++e) {
-          gq[e] = reinterpret_cast<const uint32_t*>(Ly.q_norm + d0)[e];
-          gk[e] = reinterpret_cast<const uint32_t*>(Ly.k_norm + d0)[e];
-        }
         // q heads of kv head g (contiguous), then k, then v: one gather
         float* qv = xin;
         {
@@ -619,6 +608,35 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           }
         }
         KMR_TRACE_MARK(tev + 2);
+        // per-head RMSNorm + RoPE of the q heads and k, and bf16 rounding of k and
+        // v, once per group: wave h takes head h (q heads, then k, then v), lane l
+        // the rotate-half pair of dims (l, l + D/2), in place in LDS
+        if (wave <= QPG + 1) {
+          float* hv = qv + wave * D;
+          const bool act = lane < HALF;
+          float x0 = act ? hv[lane] : 0.f, x1 = act ? hv[lane + HALF] : 0.f;
+          if (wave <= QPG) {
+            const uint16_t* gn = wave < QPG ? Ly.q_norm : Ly.k_norm;
+            const float ss = wave_sum(x0 * x0 + x1 * x1);
+            const float inv = rsqrt_f(ss / (float)D + a.eps);
+            if (act) {
+              const float y0 = (x0 * inv) * bf16_to_f32(gn[lane]);
+              const float y1 = (x1 * inv) * bf16_to_f32(gn[lane + HALF]);
+              const float2 t = cs[b * HALF + lane];
+              x0 = y0 * t.x - y1 * t.y;
+              x1 = y1 * t.x + y0 * t.y;
+            }
+          }
+          if (wave >= QPG && act) {
+            x0 = round_bf16(x0);
+            x1 = round_bf16(x1);
+          }
+          if (act) {
+            hv[lane] = x0;
+            hv[lane + HALF] = x1;
+          }
+        }
+        __syncthreads();
         float q[QPG][DPL], kf[DPL], vf[DPL];
 #pragma unroll
         for (int h = 0; h < QPG; ++h)
@@ -629,11 +647,6 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           kf[e] = qv[QPG * D + d0 + e];
           vf[e] = qv[(QPG + 1) * D + d0 + e];
         }
-#pragma unroll
-        for (int h = 0; h < QPG; ++h) norm_rope_lds<DPL>(q[h], gq, cs + b * HALF, d0, D, a.eps);
-        norm_rope_lds<DPL>(kf, gk, cs + b * HALF, d0, D, a.eps);
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) { kf[e] = round_bf16(kf[e]); vf[e] = round_bf16(vf[e]); }
         KMR_TRACE_MARK(l == 1 ? 59 : 64);
         if (s == ns - 1 && row == 0) {
           uint16_t* kd = kc + (head_base + c) * D + d0;
@@ -887,6 +900,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       grow[i] = gok[i] ? x * IX + gla[i] : 0;
       grow[NP + i] = gok[i] ? x * IX + gla[i] + I : 0;
     }
+    const uint16_t g_post = staged_gain(Ly.post_norm, H, RPW, j * RPW);
     // (K = H = 64 chunks of 32 columns: one chunk per lane, checked on the host)
     uint4* gu_codes = reinterpret_cast<uint4*>(smem + Ld.wgu) + wave * kXGuRows * 64;
     uint32_t* gu_sz = reinterpret_cast<uint32_t*>(smem + Ld.wgu + (size_t)kStepWaves * kXGuRows * 64 * 16) +
@@ -900,7 +914,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         alive = false;
         break;
       }
-      publish_staged_x<BT>(sx1, SX, H, B, RPW, j * RPW, xn, hx, Ly.post_norm, j, tag(ph + 4), plain, red);
+      publish_staged_x<BT>(sx1, SX, H, B, RPW, j * RPW, xn, hx, g_post, j, tag(ph + 4), plain, red);
     }
     KMR_TRACE_MARK(tev + 6);
     // ================= gate-up + SiLU over the XCD's slice
@@ -940,7 +954,9 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     }
     KMR_TRACE_MARK(tev + 8);
     // ================= down split-K over the XCD's slice, then RS_D
+    uint16_t g_next;
     {
+      g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
       WNarrow wd;
       wnarrow_load(wd, Ly.d_p, Ly.d_s, I, G, x * IX, IX, ook ? orow : 0, ook);
       if (!gather_staged<BT, 4 * BT>(lact, SA, IX, B, 0, tag(ph + 5), a.eps, xs, cc, xin, s_inv)) {
@@ -966,8 +982,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         break;
       }
       if (l + 1 < a.L) {
-        publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, a.layers[l + 1].in_norm, j, tag(ph + 6),
-                             plain, red);
+        publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, g_next, j, tag(ph + 6), plain, red);
       } else if (hx) {
         const int b = tid / RPW;
         publish_l(lx0 + (size_t)b * H + j * RPW + (tid - b * RPW), tag(ph + 6), xn, plain);
