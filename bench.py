@@ -58,6 +58,9 @@ def kernel_source_hash():
 
 
 PROFILE_TAG = {"step": "qwen3vl2b_b1", "batch4": "qwen3vl2b_b4"}
+# The kernel a step of these workloads runs: the persistent XCD-local step kernel
+# (batch <= 4, 8 kv heads), one launch per step.
+STEP_KERNEL = "k_stepx"
 
 
 def stored_traffic(workload_name):
@@ -65,7 +68,7 @@ def stored_traffic(workload_name):
     summary of this workload (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
     calibration factor), or None when there is none or the kernel sources changed
     since it was taken."""
-    path = os.path.join(PROFILES, f"k_step_{PROFILE_TAG[workload_name]}_pmc.txt")
+    path = os.path.join(PROFILES, f"{STEP_KERNEL}_{PROFILE_TAG[workload_name]}_pmc.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -228,12 +231,12 @@ def main():
                    "max_len": w.max_len, "layers": w.dims.n_layers, "vocab": w.dims.vocab},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": nbytes, "wall_s_timed": round(wall, 4),
-        # One launch of the persistent step kernel per step (k_step: all layers,
+        # One launch of the persistent step kernel per step (all layers,
         # final norm, lm_head and argmax), so its algorithmic bytes per launch are
         # the step's; its average launch duration comes from per-launch events.
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(args.workload),
-                     "kernel": "k_step", "launches_per_step": 1,
+                     "kernel": STEP_KERNEL, "launches_per_step": 1,
                      "kernel_us_per_launch": round(kernel_ms * 1000, 1)},
         "cpu_baseline": None,
     }
