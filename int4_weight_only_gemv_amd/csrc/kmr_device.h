@@ -49,6 +49,15 @@ __device__ __forceinline__ int otid() {
   return t;
 }
 
+// Marks a loaded value as used here, so that the compiler waits for its load at
+// this point (right after a poll, where every earlier load has already
+// completed and the wait is free) rather than at its first real use, where the
+// wait would also cover loads issued in between.
+template <typename T>
+__device__ __forceinline__ void settle(T v) {
+  asm volatile("" ::"v"(v));
+}
+
 // 1/sqrt(x) with the hardware reciprocal square root (within 1 ulp); used for
 // RMSNorm scales, whose inputs are at least epsilon.
 __device__ __forceinline__ float rsqrt_f(float x) { return __builtin_amdgcn_rsqf(x); }

@@ -33,8 +33,8 @@ constexpr int kXSplit = 128;        // attention positions per split item
 constexpr int kXMergeChunk = 8;     // split partials merged per LDS pass
 constexpr int kXNarrowCpl = 3;      // max 32-column chunks per lane in the split-K GEMVs
 constexpr uint32_t kStatusTopology = 8u;
-constexpr int kXMaxPerXcd = 64;
-constexpr int kXGuRows = 6;        // gate/up rows per wave (3 act values)   // work-groups per XCD (sums-of-squares slots of a staged row)
+constexpr int kXMaxPerXcd = 64;     // work-groups per XCD (sums-of-squares slots of a staged row)
+constexpr int kXGuRows = 6;         // gate/up rows per wave (3 act values)
 
 // Store of a tagged word that only groups of this XCD read.  A work-group-scope
 // store stays in the XCD's L2, where the device-scope polls of the XCD's other
@@ -528,6 +528,38 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   }
   KMR_TRACE_MARK(0);
 
+  // QKV rows of this group: 2 per wave, of the XCD's kv heads (q heads, k, v)
+  constexpr int NRQ = 2;
+  auto qkv_rows = [&](int (&row)[NRQ], int (&lr)[NRQ], bool (&ok)[NRQ]) {
+    const int wv = __builtin_amdgcn_readfirstlane(otid() >> 6);
+#pragma unroll
+    for (int i = 0; i < NRQ; ++i) {
+      const int rr = wv * NRQ + i;
+      lr[i] = j * RQ + rr;
+      ok[i] = rr < RQ && lr[i] < QX;
+      row[i] = 0;
+      if (ok[i]) {
+        const int gl = lr[i] / ((QPG + 2) * D), t = lr[i] - gl * (QPG + 2) * D, g = x * GPX + gl;
+        row[i] = t < QPG * D ? g * QPG * D + t
+               : t < (QPG + 1) * D ? Hq * D + g * D + (t - QPG * D)
+                                   : Hq * D + Hkv * D + g * D + (t - (QPG + 1) * D);
+      }
+    }
+  };
+  // At batch 1 the QKV and down weight rows are requested one phase early, right
+  // after the preceding phase's input has arrived: a poll waits for every load
+  // its wave issued before it, so rows requested just ahead of a poll would delay
+  // it by a memory latency.  (At larger batches the registers held meanwhile cost
+  // more than the latency saved.)
+  constexpr bool kAhead = BT == 1;
+  WRows<NRQ, 1> wq;
+  if constexpr (kAhead) {
+    int row[NRQ], lr[NRQ];
+    bool ok[NRQ];
+    qkv_rows(row, lr, ok);
+    wrows_load(wq, a.layers[0].qkv_p, a.layers[0].qkv_s, H, G, row, ok);
+  }
+
   for (int l = 0; l < a.L && alive; ++l) {
     const StepLayer& Ly = a.layers[l];
     const int ph = 1 + 6 * l;   // tags: ph x (sx0), +1 qkv, +2 partials, +3 O partials,
@@ -540,32 +572,21 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     uint32_t kr[4][DPL / 2], vr[4][DPL / 2];
     // ================= QKV rows of this XCD's kv heads: RQ rows per group, 2 per wave
     {
-      constexpr int NR = 2;
+      constexpr int NR = NRQ;
       int row[NR], lr[NR];
       bool ok[NR];
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const int rr = wave * NR + i;
-        lr[i] = j * RQ + rr;
-        ok[i] = rr < RQ && lr[i] < QX;
-        row[i] = 0;
-        if (ok[i]) {
-          const int gl = lr[i] / ((QPG + 2) * D), t = lr[i] - gl * (QPG + 2) * D, g = x * GPX + gl;
-          row[i] = t < QPG * D ? g * QPG * D + t
-                 : t < (QPG + 1) * D ? Hq * D + g * D + (t - QPG * D)
-                                     : Hq * D + Hkv * D + g * D + (t - (QPG + 1) * D);
-        }
+      qkv_rows(row, lr, ok);
+      if constexpr (!kAhead) {
+        wrows_load(wq, Ly.qkv_p, Ly.qkv_s, H, G, row, ok);
+        asm volatile("" ::: "memory");   // keep the weight requests ahead of the polls
       }
-      WRows<NR, 1> w;
-      wrows_load(w, Ly.qkv_p, Ly.qkv_s, H, G, row, ok);
-      asm volatile("" ::: "memory");   // keep the weight requests ahead of the polls
       if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, WPX, tag(ph), a.eps, xs, cc, xin, s_inv)) {
         alive = false;
         break;
       }
       KMR_TRACE_MARK(tev + 0);
       float out[NR][BT];
-      wave_dot<BT, NR, 1>(w, H, B, xs, cc, out);
+      wave_dot<BT, NR, 1>(wq, H, B, xs, cc, out);
       if (lane < B) {
         const float inv = s_inv[lane];
 #pragma unroll
@@ -918,6 +939,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     }
     KMR_TRACE_MARK(tev + 6);
     // ================= gate-up + SiLU over the XCD's slice
+    WNarrow wd;
+    uint16_t g_next;
     {
       if (!gather_staged<BT, 4 * BT>(sx1, SX, H, B, WPX, tag(ph + 4), a.eps, xs, cc, xin, s_inv)) {
         alive = false;
@@ -926,6 +949,10 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       KMR_TRACE_MARK(tev + 7);
       float out[2 * NP][BT];
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gate/up rows are in LDS
+      if constexpr (kAhead) {
+        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, G, x * IX, IX, ook ? orow : 0, ook);
+        g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
+      }
       WRows<2 * NP, 1> wgu;
       wrows_from_lds(wgu, gu_codes, gu_sz);
       wave_dot<BT, 2 * NP, 1>(wgu, H, B, xs, cc, out);
@@ -954,15 +981,16 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     }
     KMR_TRACE_MARK(tev + 8);
     // ================= down split-K over the XCD's slice, then RS_D
-    uint16_t g_next;
     {
-      g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
-      WNarrow wd;
-      wnarrow_load(wd, Ly.d_p, Ly.d_s, I, G, x * IX, IX, ook ? orow : 0, ook);
+      if constexpr (!kAhead) {
+        g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
+        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, G, x * IX, IX, ook ? orow : 0, ook);
+      }
       if (!gather_staged<BT, 4 * BT>(lact, SA, IX, B, 0, tag(ph + 5), a.eps, xs, cc, xin, s_inv)) {
         alive = false;
         break;
       }
+      settle(g_next);
       KMR_TRACE_MARK(tev + 9);
       float out[BT];
       narrow_dot<BT>(wd, IX, B, xs, cc, out);
@@ -982,6 +1010,12 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         break;
       }
       if (l + 1 < a.L) {
+        if constexpr (kAhead) {
+          int row[NRQ], lr[NRQ];
+          bool ok[NRQ];
+          qkv_rows(row, lr, ok);
+          wrows_load(wq, a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, G, row, ok);
+        }
         publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, g_next, j, tag(ph + 6), plain, red);
       } else if (hx) {
         const int b = tid / RPW;
