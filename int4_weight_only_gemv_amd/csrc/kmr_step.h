@@ -373,26 +373,34 @@ __device__ __forceinline__ void wave_dot(const WRows<NR, CPL>& w, int K, int B, 
   for (int j = 0; j < CPL; ++j) {
     const int c = lane + 64 * j;
     if (c < CH) {
+      // the input chunk of every row first, then one row of weights at a time:
+      // each row is dequantized once and only its 16 words are live
+      uint4 xv[BT][4];
+      float2 C[BT];
 #pragma unroll
       for (int b = 0; b < BT; ++b) {
-        if (b >= B) break;
-        uint4 xv[4];
+        const int bb = b < B ? b : 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xv[q] = xs[(b * 4 + q) * CH + c];
-        const float2 C = cc[b * CH + c];
+        for (int q = 0; q < 4; ++q) xv[b][q] = xs[(bb * 4 + q) * CH + c];
+        C[b] = cc[bb * CH + c];
+      }
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-          uint32_t p[16];
-          dequant16(w.raw[i][j], p);
+      for (int i = 0; i < NR; ++i) {
+        uint32_t p[16];
+        dequant16(w.raw[i][j], p);
+        const float s = bf16_lo(w.sz[i][j]), z = bf16_hi(w.sz[i][j]);
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          if (b >= B) break;
           float d = 0.f;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            d = fdot2(p[4 * q + 0], xv[q].x, d);
-            d = fdot2(p[4 * q + 1], xv[q].y, d);
-            d = fdot2(p[4 * q + 2], xv[q].z, d);
-            d = fdot2(p[4 * q + 3], xv[q].w, d);
+            d = fdot2(p[4 * q + 0], xv[b][q].x, d);
+            d = fdot2(p[4 * q + 1], xv[b][q].y, d);
+            d = fdot2(p[4 * q + 2], xv[b][q].z, d);
+            d = fdot2(p[4 * q + 3], xv[b][q].w, d);
           }
-          acc[i][b] += bf16_lo(w.sz[i][j]) * (d - C.x) + bf16_hi(w.sz[i][j]) * C.y;
+          acc[i][b] += s * (d - C[b].x) + z * C[b].y;
         }
       }
     }
