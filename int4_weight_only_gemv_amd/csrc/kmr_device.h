@@ -57,6 +57,12 @@ template <typename T>
 __device__ __forceinline__ void settle(T v) {
   asm volatile("" ::"v"(v));
 }
+__device__ __forceinline__ void settle(uint4 v) {
+  settle(v.x);
+  settle(v.y);
+  settle(v.z);
+  settle(v.w);
+}
 
 // 1/sqrt(x) with the hardware reciprocal square root (within 1 ulp); used for
 // RMSNorm scales, whose inputs are at least epsilon.

@@ -585,6 +585,17 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         break;
       }
       KMR_TRACE_MARK(tev + 0);
+      // at batch 1 the K/V rows of the first attention item are requested now,
+      // to be in flight during the QKV rows and their hand-off (the QKV rows,
+      // requested a phase ago, are settled first)
+      if constexpr (kAhead) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          settle(wq.raw[i][0]);
+          settle(wq.sz[i][0]);
+        }
+        if (j < total) attn_load_kv<DPL>(kr, vr, kc, vc, j, s_ns, s_c, GPX, x, Hkv, M, D, wave);
+      }
       float out[NR][BT];
       wave_dot<BT, NR, 1>(wq, H, B, xs, cc, out);
       if (lane < B) {
@@ -602,7 +613,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     // K/V rows of this group's first attention item: requested right after its
     // q/k/v rows are out, so that their latency overlaps the hand-off
     asm volatile("" ::: "memory");   // not ahead of the q/k/v stores
-    if (j < total) attn_load_kv<DPL>(kr, vr, kc, vc, j, s_ns, s_c, GPX, x, Hkv, M, D, wave);
+    if constexpr (!kAhead)
+      if (j < total) attn_load_kv<DPL>(kr, vr, kc, vc, j, s_ns, s_c, GPX, x, Hkv, M, D, wave);
     KMR_TRACE_MARK(tev + 1);
     const int orow = j * RPW + wave * 8 + (lane >> 3);   // O and down rows of this lane group
     const bool ook = wave * 8 + (lane >> 3) < RPW && orow < H;
@@ -637,10 +649,10 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           const bool act = lane < HALF;
           float x0 = act ? hv[lane] : 0.f, x1 = act ? hv[lane + HALF] : 0.f;
           if (wave <= QPG) {
-            const uint16_t* gn = wave < QPG ? Ly.q_norm : Ly.k_norm;
             const float ss = wave_sum(x0 * x0 + x1 * x1);
             const float inv = rsqrt_f(ss / (float)D + a.eps);
             if (act) {
+              const uint16_t* gn = wave < QPG ? Ly.q_norm : Ly.k_norm;
               const float y0 = (x0 * inv) * bf16_to_f32(gn[lane]);
               const float y1 = (x1 * inv) * bf16_to_f32(gn[lane + HALF]);
               const float2 t = cs[b * HALF + lane];
