@@ -126,6 +126,25 @@ __device__ __forceinline__ int swz(int i) {
   return (((c << 3) | (col ^ (c & 7))) << 2) | (i & 3);
 }
 
+// Whether any thread of the work-group failed a bounded wait, with one barrier:
+// a failing thread sets a flag in LDS before the barrier and every thread reads
+// it after.  The flag is cleared once at kernel start (group_fail_reset, followed
+// by a barrier) and never again: a failure ends the group, and any wave that sees
+// it leaves (a wave that has ended no longer holds up the others' barriers).
+__device__ __forceinline__ int* group_fail_flag() {
+  __shared__ int flag;
+  return &flag;
+}
+__device__ __forceinline__ void group_fail_reset() {
+  if (threadIdx.x == 0) *group_fail_flag() = 0;
+}
+__device__ __forceinline__ bool group_failed(bool bad) {
+  int* f = group_fail_flag();
+  if (bad) *f = 1;
+  __syncthreads();
+  return *f != 0;
+}
+
 // Polls `total` tagged words until all carry `tag`, then stores their values in
 // LDS at dst[place(i)].  Word i lives at src + addr(i).  Each thread issues all
 // its loads of a pass before checking any, so a poll costs one memory round
@@ -167,7 +186,7 @@ __device__ __forceinline__ bool gather_tagged(const uint64_t* src, int total, ui
         if (idx[j] < total) dst[place(idx[j])] = __uint_as_float((uint32_t)v[j]);
   }
   if (first) pre();
-  return !__syncthreads_or(!ok);
+  return !group_failed(!ok);
 }
 
 struct NoPre {
@@ -279,7 +298,7 @@ __device__ __forceinline__ bool gather_stage(const uint64_t* src, int K, int B, 
         __builtin_amdgcn_s_sleep(KMR_POLL_SLEEP);
       }
     } while (!fresh);
-    if (__syncthreads_or(!ok)) return false;
+    if (group_failed(!ok)) return false;
     float x[PT];
 #pragma unroll
     for (int j = 0; j < PT; ++j) x[j] = has[j] ? __uint_as_float((uint32_t)v[j]) : 0.f;
@@ -664,6 +683,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
   const int KMAX = H > I ? (H > QD ? H : QD) : (I > QD ? I : QD);
   const int RPBX = (H + nwg - 1) / nwg;                     // residual rows owned per group
   const StepLds L = step_lds(BT, KMAX, RPBX, H, D, QPG);
+  group_fail_reset();
+  __syncthreads();
   uint4* xs = reinterpret_cast<uint4*>(smem + L.xs);
   float2* cc = reinterpret_cast<float2*>(smem + L.cc);
   float* xin = reinterpret_cast<float*>(smem + L.xin);
@@ -738,7 +759,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
         }
         if (RPB <= kStepWaves * NR) break;
       }
-      if (__syncthreads_or(!alive)) break;
+      if (group_failed(!alive)) break;
     }
     KMR_TRACE_MARK(tev + 1);
     // ================= attention splits: items (b, g, split)
@@ -909,7 +930,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
       __syncthreads();
       KMR_TRACE_MARK(l == 1 ? 60 : 64);
     }
-    if (__syncthreads_or(!alive)) break;
+    if (group_failed(!alive)) break;
     // ================= split merge: the group of each head's last split merges all
     for (int item = wg; item < total && alive; item += nwg) {
       const AttnItem it_ = attn_item(item, s_c, B, Hkv, M);
@@ -952,7 +973,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
       }
       KMR_TRACE_MARK(l == 1 ? 62 : 64);
     }
-    if (__syncthreads_or(!alive)) break;
+    if (group_failed(!alive)) break;
     KMR_TRACE_MARK(tev + 3);
     // ================= O projection + residual: this group's RPBX rows of x
     for (int r2 = 0; r2 < RPBX || r2 == 0; r2 += kStepWaves) {
@@ -979,7 +1000,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
       }
       if (RPBX <= kStepWaves) break;
     }
-    if (__syncthreads_or(!alive)) break;
+    if (group_failed(!alive)) break;
     KMR_TRACE_MARK(tev + 5);
     // ================= gate-up + SiLU: RPB pairs per group, NP per wave
     {
@@ -1014,7 +1035,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
         }
         if (RPB <= kStepWaves * NP) break;
       }
-      if (__syncthreads_or(!alive)) break;
+      if (group_failed(!alive)) break;
     }
     KMR_TRACE_MARK(tev + 7);
     // ================= down + residual
@@ -1042,7 +1063,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
       }
       if (RPBX <= kStepWaves) break;
     }
-    if (__syncthreads_or(!alive)) break;
+    if (group_failed(!alive)) break;
     KMR_TRACE_MARK(tev + 9);
   }
 

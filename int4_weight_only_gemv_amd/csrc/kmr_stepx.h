@@ -195,7 +195,7 @@ __device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag,
       if (i < words) buf[i] = has[q] ? __uint_as_float((uint32_t)v[q]) : 0.f;
     }
   }
-  if (__syncthreads_or(!ok)) return false;
+  if (group_failed(!ok)) return false;
   // per <= kStepThreads (checked on the host): one element per thread
   const int b = tid / RPW, r = tid - b * RPW;
   has_x = tid < per && row0 + r < H;
@@ -316,7 +316,7 @@ __device__ __forceinline__ bool gather_staged(const uint64_t* src, long long str
       }
     }
   }
-  if (__syncthreads_or(!ok)) return false;
+  if (group_failed(!ok)) return false;
   for (int t = tid; t < B * CH; t += kStepThreads) {
     int b = 0;
 #pragma unroll
@@ -468,6 +468,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   const int NSX = (M + kXSplit - 1) / kXSplit;
   const int plain = a.intra_plain;
   const StepXLds Ld = stepx_lds(BT, H, RPW, D, QPG, GPX);
+  group_fail_reset();
+  __syncthreads();
   uint4* xs = reinterpret_cast<uint4*>(smem + Ld.xs);
   float2* cc = reinterpret_cast<float2*>(smem + Ld.cc);
   float* xin = reinterpret_cast<float*>(smem + Ld.xin);
@@ -796,7 +798,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         }
         __syncthreads();
       }
-      if (__syncthreads_or(!alive)) break;
+      if (group_failed(!alive)) break;
     }
     KMR_TRACE_MARK(tev + 3);
     // O weights of this group (rows j*RPW + 8 wave + lane/8, the XCD's head columns),
@@ -847,7 +849,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
             if (hv[q]) xin[i] = __uint_as_float((uint32_t)v[q]);
           }
         }
-        if (__syncthreads_or(!ok)) { alive = false; break; }
+        if (group_failed(!ok)) { alive = false; break; }
         // log-sum-exp weights of this chunk's splits, once per (row, kv head, q head)
         float* s_wt = xin + words;   // [B*GPX][QPG][kXMergeChunk + 2]: weights, max, sum
         static_assert(kXMergeChunk == 8, "one 8-lane group per (row, kv head, q head)");
