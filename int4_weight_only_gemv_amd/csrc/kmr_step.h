@@ -378,10 +378,30 @@ __device__ __forceinline__ void dequant16(const uint4 raw, uint32_t (&p)[16]) {
   }
 }
 
+// Per-chunk constants (C1, C2) = (1024 sum(h) + 8 sum(u), sum(u)) of a staged input
+// row, from a precomputed array ...
+struct ChunkCC {
+  const float2* cc;
+  int CH;   // chunks per row
+  __device__ float2 get(int b, int c) const { return cc[b * CH + c]; }
+};
+// ... or from the per-8-column-word sums (sum h, sum u) of a staged vector, 16-byte
+// aligned rows of K/4 floats
+struct ChunkSums {
+  const float* sum;
+  int K4;
+  __device__ float2 get(int b, int c) const {
+    const float4* p = reinterpret_cast<const float4*>(sum + b * K4 + 8 * c);
+    const float4 lo = p[0], hi = p[1];
+    const float sh = (lo.x + lo.z) + (hi.x + hi.z), su = (lo.y + lo.w) + (hi.y + hi.w);
+    return make_float2(1024.0f * sh + 8.0f * su, su);
+  }
+};
+
 // out[i][b] = dot of weight row i with staged input row b (uniform across the wave).
-template <int BT, int NR, int CPL>
-__device__ __forceinline__ void wave_dot(const WRows<NR, CPL>& w, int K, int B, const uint4* xs,
-                                         const float2* cc, float (&out)[NR][BT]) {
+template <int BT, int NR, int CPL, typename CS>
+__device__ __forceinline__ void wave_dot_c(const WRows<NR, CPL>& w, int K, int B, const uint4* xs,
+                                           const CS& cs, float (&out)[NR][BT]) {
   const int lane = otid() & 63, CH = K >> 5;
   float acc[NR][BT];
 #pragma unroll
@@ -401,7 +421,7 @@ __device__ __forceinline__ void wave_dot(const WRows<NR, CPL>& w, int K, int B, 
         const int bb = b < B ? b : 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) xv[b][q] = xs[(bb * 4 + q) * CH + c];
-        C[b] = cc[bb * CH + c];
+        C[b] = cs.get(bb, c);
       }
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
@@ -428,6 +448,12 @@ __device__ __forceinline__ void wave_dot(const WRows<NR, CPL>& w, int K, int B, 
   for (int i = 0; i < NR; ++i)
 #pragma unroll
     for (int b = 0; b < BT; ++b) out[i][b] = wave_sum(acc[i][b]);
+}
+
+template <int BT, int NR, int CPL>
+__device__ __forceinline__ void wave_dot(const WRows<NR, CPL>& w, int K, int B, const uint4* xs,
+                                         const float2* cc, float (&out)[NR][BT]) {
+  wave_dot_c<BT, NR, CPL>(w, K, B, xs, ChunkCC{cc, K >> 5}, out);
 }
 
 struct AttnItem {

@@ -109,9 +109,9 @@ __device__ __forceinline__ void wnarrow_load(WNarrow& w, const uint8_t* packed, 
 
 // out[b] = dot of the group's row with staged input row b over the slice; every
 // lane of the 8-lane group receives the sums.
-template <int BT>
+template <int BT, typename CS>
 __device__ __forceinline__ void narrow_dot(const WNarrow& w, int KS, int B, const uint4* xs,
-                                           const float2* cc, float (&out)[BT]) {
+                                           const CS& cs, float (&out)[BT]) {
   const int sub = otid() & 7, CHs = KS >> 5;
   float acc[BT];
 #pragma unroll
@@ -129,7 +129,7 @@ __device__ __forceinline__ void narrow_dot(const WNarrow& w, int KS, int B, cons
         uint4 xv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) xv[q] = xs[(b * 4 + q) * CHs + c];
-        const float2 C = cc[b * CHs + c];
+        const float2 C = cs.get(b, c);
         float d = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -259,18 +259,19 @@ __device__ __forceinline__ void stage_publish(uint64_t* dst, int K, int n, float
 }
 
 // Gathers B staged rows of K columns (plus nss sums of squares each) into the
-// dot-product LDS layout (xs, cc) and, with nss > 0, s_inv[b] = 1/sqrt(ss/K + eps).
-// tmp: LDS scratch of BT*(K/4 + nss) floats.  Returns false, for the whole group,
-// on timeout.
+// dot-product LDS layout: pairs into xs, and the per-word sums into sums ([BT][K/4],
+// read through ChunkSums) followed by the sums of squares ([BT][nss], read by
+// staged_inv).  One barrier: the data is in LDS for every wave on return.  The
+// buffers must not be rewritten before a barrier that follows their last reader.
+// Returns false, for the whole group, on timeout.
 template <int BT, int PT>
 __device__ __forceinline__ bool gather_staged(const uint64_t* src, long long stride, int K, int B,
-                                              int nss, uint32_t tag, float eps, uint4* xs,
-                                              float2* cc, float* tmp, float* s_inv) {
-  const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+                                              int nss, uint32_t tag, uint4* xs, float* sums) {
+  const int tid = otid();
   const int CH = K >> 5, K2 = K >> 1, K4 = K >> 2, per = K2 + K4 + nss, total = B * per;
   uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
-  float* s_sum = tmp;              // [B][K/4]
-  float* s_ss = tmp + BT * K4;     // [B][nss]
+  float* s_sum = sums;             // [B][K/4]
+  float* s_ss = sums + BT * K4;    // [B][nss]
   bool ok = true;
   for (int base = 0; base < total && ok; base += kStepThreads * PT) {
     uint64_t v[PT];
@@ -316,27 +317,30 @@ __device__ __forceinline__ bool gather_staged(const uint64_t* src, long long str
       }
     }
   }
-  if (group_failed(!ok)) return false;
-  for (int t = tid; t < B * CH; t += kStepThreads) {
-    int b = 0;
+  return !group_failed(!ok);
+}
+
+// 1/sqrt(sum of squares / K + eps) of staged row b from its nss (<= 64) partial
+// sums in LDS; every lane of the calling wave gets it.
+__device__ __forceinline__ float staged_inv(const float* s_ss, int b, int nss, int K, float eps) {
+  const int lane = otid() & 63;
+  const float ss = wave_sum(lane < nss ? s_ss[b * nss + lane] : 0.f);
+  return rsqrt_f(ss / (float)K + eps);
+}
+
+// Lane b < B: staged_inv of row b (the others get 1).  Every lane of the wave must
+// call this.
+template <int BT>
+__device__ __forceinline__ float row_inv(const float* s_ss, int B, int nss, int K, float eps) {
+  const int lane = otid() & 63;
+  float r = 1.f;
 #pragma unroll
-    for (int u = 1; u < BT; ++u) b += t >= u * CH ? 1 : 0;
-    const int c = t - b * CH;
-    const float* ws = s_sum + b * K4 + 8 * c;   // 4 words x (sum h, sum used)
-    const float sh = (ws[0] + ws[2]) + (ws[4] + ws[6]);
-    const float su = (ws[1] + ws[3]) + (ws[5] + ws[7]);
-    cc[b * CH + c] = make_float2(1024.0f * sh + 8.0f * su, su);
+  for (int b = 0; b < BT; ++b) {
+    if (b >= B) break;
+    const float v = staged_inv(s_ss, b, nss, K, eps);
+    if (lane == b) r = v;
   }
-  if (nss > 0 && wave == 0) {
-    // nss <= 64 (checked on the host)
-#pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      const float ss = wave_sum((b < B && lane < nss) ? s_ss[b * nss + lane] : 0.f);
-      if (lane == 0 && b < B) s_inv[b] = rsqrt_f(ss / (float)K + eps);
-    }
-  }
-  __syncthreads();
-  return true;
+  return r;
 }
 
 // The norm gain of this thread's column in publish_staged_x, requested early (an
@@ -376,14 +380,16 @@ __device__ __forceinline__ void publish_staged_x(uint64_t* dst, long long stride
 
 // ------------------------------------------------------------------ LDS layout
 //   xs    uint4 [BT][4][H/32]   staged fp16 input pairs (every GEMV input <= H)
-//   cc    float2 [BT][H/32]     per-chunk (C1, C2)
+//   cc    float2 [BT][H/32]     per-chunk (C1, C2) of the O input
+//   sums  fp32 [BT][H/4], [BT][64]  per-word sums and sums of squares of a
+//                               gathered staged vector
 //   xin   fp32 scratch          attention q/k/v and wave states, split merge,
 //                               reduce-scatter partials, lm_head input
 //   xown  fp32 [BT][RPW]        this group's rows of the residual stream
 //   cs    float2 [BT][D/2]      RoPE cos/sin of each row
 //   red   float [128]
 struct StepXLds {
-  size_t xs, cc, xin, xown, cs, red, wgu, total;
+  size_t xs, cc, sums, xin, xown, cs, red, wgu, total;
 };
 
 __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int QPG, int GPX) {
@@ -401,6 +407,7 @@ __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int
   if (xin < lm) xin = lm;
   s.xs = take((size_t)BT * 4 * (H / 32) * 16);
   s.cc = take((size_t)BT * (H / 32) * 8);
+  s.sums = take((size_t)BT * (H / 4 + kXMaxPerXcd) * 4);
   s.xin = take(xin);
   s.xown = take((size_t)BT * RPW * 4);
   s.cs = take((size_t)BT * (D / 2) * 8);
@@ -472,6 +479,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   __syncthreads();
   uint4* xs = reinterpret_cast<uint4*>(smem + Ld.xs);
   float2* cc = reinterpret_cast<float2*>(smem + Ld.cc);
+  float* sums = reinterpret_cast<float*>(smem + Ld.sums);
   float* xin = reinterpret_cast<float*>(smem + Ld.xin);
   float* xown = reinterpret_cast<float*>(smem + Ld.xown);
   float2* cs = reinterpret_cast<float2*>(smem + Ld.cs);
@@ -486,7 +494,6 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   __shared__ int s_last;
   __shared__ int s_c[16];
   __shared__ int s_ns[16];
-  __shared__ float s_inv[4];
 
   const uint32_t step = (a.step_ctr[0] + 1u) & 0x7fffffu;
   auto tag = [&](int phase) -> uint32_t { return (step << 9) | (uint32_t)phase; };
@@ -582,7 +589,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         wrows_load(wq, Ly.qkv_p, Ly.qkv_s, H, G, row, ok);
         asm volatile("" ::: "memory");   // keep the weight requests ahead of the polls
       }
-      if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, WPX, tag(ph), a.eps, xs, cc, xin, s_inv)) {
+      if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, WPX, tag(ph), xs, sums)) {
         alive = false;
         break;
       }
@@ -599,9 +606,9 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         if (j < total) attn_load_kv<DPL>(kr, vr, kc, vc, j, s_ns, s_c, GPX, x, Hkv, M, D, wave);
       }
       float out[NR][BT];
-      wave_dot<BT, NR, 1>(wq, H, B, xs, cc, out);
+      wave_dot_c<BT, NR, 1>(wq, H, B, xs, ChunkSums{sums, H / 4}, out);
+      const float inv = row_inv<BT>(sums + BT * (H / 4), B, WPX, H, a.eps);
       if (lane < B) {
-        const float inv = s_inv[lane];
 #pragma unroll
         for (int i = 0; i < NR; ++i)
           if (ok[i]) {
@@ -913,7 +920,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     // ================= O split-K partial of this group's rows over the XCD's heads
     {
       float out[BT];
-      narrow_dot<BT>(wo, OX, B, xs, cc, out);
+      narrow_dot<BT>(wo, OX, B, xs, ChunkCC{cc, OX >> 5}, out);
       const int sub = lane & 7;
       if (ook && sub < B) {
         float v = out[0];
@@ -956,7 +963,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     WNarrow wd;
     uint16_t g_next;
     {
-      if (!gather_staged<BT, 4 * BT>(sx1, SX, H, B, WPX, tag(ph + 4), a.eps, xs, cc, xin, s_inv)) {
+      if (!gather_staged<BT, 4 * BT>(sx1, SX, H, B, WPX, tag(ph + 4), xs, sums)) {
         alive = false;
         break;
       }
@@ -969,11 +976,11 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       }
       WRows<2 * NP, 1> wgu;
       wrows_from_lds(wgu, gu_codes, gu_sz);
-      wave_dot<BT, 2 * NP, 1>(wgu, H, B, xs, cc, out);
+      wave_dot_c<BT, 2 * NP, 1>(wgu, H, B, xs, ChunkSums{sums, H / 4}, out);
+      const float inv = row_inv<BT>(sums + BT * (H / 4), B, WPX, H, a.eps);
       // act values of this group into LDS [b][32], then published staged
       float* s_act = xin;
       if (lane < B) {
-        const float inv = s_inv[lane];
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           float gt = out[i][0], up = out[NP + i][0];
@@ -1000,14 +1007,14 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
         wnarrow_load(wd, Ly.d_p, Ly.d_s, I, G, x * IX, IX, ook ? orow : 0, ook);
       }
-      if (!gather_staged<BT, 4 * BT>(lact, SA, IX, B, 0, tag(ph + 5), a.eps, xs, cc, xin, s_inv)) {
+      if (!gather_staged<BT, 4 * BT>(lact, SA, IX, B, 0, tag(ph + 5), xs, sums)) {
         alive = false;
         break;
       }
       settle(g_next);
       KMR_TRACE_MARK(tev + 9);
       float out[BT];
-      narrow_dot<BT>(wd, IX, B, xs, cc, out);
+      narrow_dot<BT>(wd, IX, B, xs, ChunkSums{sums, IX / 4}, out);
       const int sub = lane & 7;
       if (ook && sub < B) {
         float v = out[0];
