@@ -337,6 +337,8 @@ bool stepx_fits(const kmr_config* c, int B, int nwg) {
   if (RPW * (WPX - 1) >= H || RA * (WPX - 1) >= IX) return false;
   // staged vectors: 8-column words owned whole, one element per thread, <= 64 producers
   if (RPW % 8 != 0 || RA % 8 != 0 || RA > 32 || 4 * RPW > kStepThreads || WPX > kXMaxPerXcd) return false;
+  // a residual row starts at a wave boundary or lies within one wave
+  if (RPW <= 64 ? 64 % RPW != 0 : RPW % 64 != 0) return false;
   if (4 * GPX * QPG > 8 || QPG != 2) return false;   // split-merge weights in one wave
   const size_t lds = stepx_lds(4, H, RPW, D, QPG, GPX).total;
   return lds <= 160 * 1024;

@@ -33,7 +33,8 @@ constexpr int kXSplit = 128;        // attention positions per split item
 constexpr int kXMergeChunk = 8;     // split partials merged per LDS pass
 constexpr int kXNarrowCpl = 3;      // max 32-column chunks per lane in the split-K GEMVs
 constexpr uint32_t kStatusTopology = 8u;
-constexpr int kXMaxPerXcd = 64;     // work-groups per XCD (sums-of-squares slots of a staged row)
+constexpr int kXMaxPerXcd = 64;     // work-groups per XCD
+constexpr int kXSsSlots = kXMaxPerXcd * 2;   // sums-of-squares slots of a staged row (<= 2 per group)
 constexpr int kXGuRows = 6;         // gate/up rows per wave (3 act values)
 
 // Store of a tagged word that only groups of this XCD read.  A work-group-scope
@@ -207,7 +208,6 @@ __device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag,
     xn = xown[b * RPW + r] + sum;
     xown[b * RPW + r] = xn;
   }
-  __syncthreads();
   return true;
 }
 
@@ -320,12 +320,13 @@ __device__ __forceinline__ bool gather_staged(const uint64_t* src, long long str
   return !group_failed(!ok);
 }
 
-// 1/sqrt(sum of squares / K + eps) of staged row b from its nss (<= 64) partial
-// sums in LDS; every lane of the calling wave gets it.
+// 1/sqrt(sum of squares / K + eps) of staged row b from its nss (<= kXSsSlots)
+// partial sums in LDS; every lane of the calling wave gets it.
 __device__ __forceinline__ float staged_inv(const float* s_ss, int b, int nss, int K, float eps) {
   const int lane = otid() & 63;
-  const float ss = wave_sum(lane < nss ? s_ss[b * nss + lane] : 0.f);
-  return rsqrt_f(ss / (float)K + eps);
+  float part = 0.f;
+  for (int i = lane; i < nss; i += 64) part += s_ss[b * nss + i];
+  return rsqrt_f(wave_sum(part) / (float)K + eps);
 }
 
 // Lane b < B: staged_inv of row b (the others get 1).  Every lane of the wave must
@@ -353,29 +354,31 @@ __device__ __forceinline__ uint16_t staged_gain(const uint16_t* gain, int H, int
 
 // Publishes x rows (element i = tid: row b = i / RPW, column row0 + i % RPW, valid
 // if has) of a staged RMSNorm input: u = x * gain (g: this column's bf16 gain from
-// staged_gain), and this group's sum of squares of each row at slot `slot` of the
-// row's sums-of-squares area.  Every thread of the group must call this.
+// staged_gain), and the sum of squares of each row from each wave that holds part
+// of it, at slot WPR * slot + (wave - first wave of the row), WPR = max(1, RPW / 64)
+// (a row starts at a wave boundary or within one wave: 64 % RPW == 0 or
+// RPW % 64 == 0, checked on the host).  Every thread of the group must call this;
+// it has no barrier.
 template <int BT>
 __device__ __forceinline__ void publish_staged_x(uint64_t* dst, long long stride, int H, int B,
                                                  int RPW, int row0, float xn, bool has, uint16_t g,
-                                                 int slot, uint32_t tag, int plain, float* red) {
+                                                 int slot, uint32_t tag, int plain) {
   const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = tid / RPW, n = row0 + (tid - b * RPW);
   const float u = has ? xn * bf16_to_f32(g) : 0.f;
   stage_publish(dst + (size_t)(has ? b : 0) * stride, H, n, u, has, tag, plain);
+  const int WPR = RPW >= 64 ? RPW >> 6 : 1;
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) {
-    const float ss = wave_sum((has && b == bb) ? xn * xn : 0.f);
-    if (lane == 0) red[bb * kStepWaves + wave] = ss;
+    if (bb >= B) break;
+    const int w0 = (bb * RPW) >> 6, w1 = ((bb + 1) * RPW - 1) >> 6;
+    if (wave >= w0 && wave <= w1) {
+      const float ss = wave_sum((has && b == bb) ? xn * xn : 0.f);
+      if (lane == 0)
+        publish_l(dst + (size_t)bb * stride + (H >> 1) + (H >> 2) + WPR * slot + (wave - w0), tag, ss,
+                  plain);
+    }
   }
-  __syncthreads();
-  if (tid < B) {
-    float ss = 0.f;
-#pragma unroll
-    for (int w = 0; w < kStepWaves; ++w) ss += red[tid * kStepWaves + w];
-    publish_l(dst + (size_t)tid * stride + (H >> 1) + (H >> 2) + slot, tag, ss, plain);
-  }
-  __syncthreads();
 }
 
 // ------------------------------------------------------------------ LDS layout
@@ -407,7 +410,7 @@ __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int
   if (xin < lm) xin = lm;
   s.xs = take((size_t)BT * 4 * (H / 32) * 16);
   s.cc = take((size_t)BT * (H / 32) * 8);
-  s.sums = take((size_t)BT * (H / 4 + kXMaxPerXcd) * 4);
+  s.sums = take((size_t)BT * (H / 4 + kXSsSlots) * 4);
   s.xin = take(xin);
   s.xown = take((size_t)BT * RPW * 4);
   s.cs = take((size_t)BT * (D / 2) * 8);
@@ -452,7 +455,7 @@ __host__ __device__ inline StepXSizes stepx_sizes(int B, int H, int Hkv, int D, 
   const int GPX = Hkv / kXcds, NSX = (M + kXSplit - 1) / kXSplit;
   StepXSizes z{};
   const int IX = I / kXcds;
-  z.srow_x = ((long long)(H / 2 + H / 4 + kXMaxPerXcd) + 63) & ~63LL;
+  z.srow_x = ((long long)(H / 2 + H / 4 + kXSsSlots) + 63) & ~63LL;
   z.srow_a = ((long long)(IX / 2 + IX / 4) + 63) & ~63LL;
   z.lx = xalign((long long)B * H);             // fp32 x after the last layer (lm_head input)
   z.sx = xalign((long long)2 * B * z.srow_x);  // staged x: entering the layer, after O
@@ -473,6 +476,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   const int GPX = Hkv / kXcds, QX = GPX * (QPG + 2) * D, OX = GPX * QPG * D, IX = I / kXcds;
   const int RPW = (H + WPX - 1) / WPX, RQ = (QX + WPX - 1) / WPX, RA = (IX + WPX - 1) / WPX;
   const int NSX = (M + kXSplit - 1) / kXSplit;
+  const int NSS = WPX * (RPW >= 64 ? RPW >> 6 : 1);   // sums-of-squares slots of a staged row
   const int plain = a.intra_plain;
   const StepXLds Ld = stepx_lds(BT, H, RPW, D, QPG, GPX);
   group_fail_reset();
@@ -533,8 +537,9 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       xown[b * RPW + r] = v;
     }
     publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, v, has, staged_gain(a.layers[0].in_norm, H, RPW, j * RPW),
-                         j, tag(1), plain, red);
+                         j, tag(1), plain);
   }
+  __syncthreads();   // cache positions, split counts and RoPE tables are in LDS
   KMR_TRACE_MARK(0);
 
   // QKV rows of this group: 2 per wave, of the XCD's kv heads (q heads, k, v)
@@ -589,7 +594,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         wrows_load(wq, Ly.qkv_p, Ly.qkv_s, H, G, row, ok);
         asm volatile("" ::: "memory");   // keep the weight requests ahead of the polls
       }
-      if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, WPX, tag(ph), xs, sums)) {
+      if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, NSS, tag(ph), xs, sums)) {
         alive = false;
         break;
       }
@@ -607,7 +612,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       }
       float out[NR][BT];
       wave_dot_c<BT, NR, 1>(wq, H, B, xs, ChunkSums{sums, H / 4}, out);
-      const float inv = row_inv<BT>(sums + BT * (H / 4), B, WPX, H, a.eps);
+      const float inv = row_inv<BT>(sums + BT * (H / 4), B, NSS, H, a.eps);
       if (lane < B) {
 #pragma unroll
         for (int i = 0; i < NR; ++i)
@@ -956,14 +961,14 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         alive = false;
         break;
       }
-      publish_staged_x<BT>(sx1, SX, H, B, RPW, j * RPW, xn, hx, g_post, j, tag(ph + 4), plain, red);
+      publish_staged_x<BT>(sx1, SX, H, B, RPW, j * RPW, xn, hx, g_post, j, tag(ph + 4), plain);
     }
     KMR_TRACE_MARK(tev + 6);
     // ================= gate-up + SiLU over the XCD's slice
     WNarrow wd;
     uint16_t g_next;
     {
-      if (!gather_staged<BT, 4 * BT>(sx1, SX, H, B, WPX, tag(ph + 4), xs, sums)) {
+      if (!gather_staged<BT, 4 * BT>(sx1, SX, H, B, NSS, tag(ph + 4), xs, sums)) {
         alive = false;
         break;
       }
@@ -977,7 +982,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       WRows<2 * NP, 1> wgu;
       wrows_from_lds(wgu, gu_codes, gu_sz);
       wave_dot_c<BT, 2 * NP, 1>(wgu, H, B, xs, ChunkSums{sums, H / 4}, out);
-      const float inv = row_inv<BT>(sums + BT * (H / 4), B, WPX, H, a.eps);
+      const float inv = row_inv<BT>(sums + BT * (H / 4), B, NSS, H, a.eps);
       // act values of this group into LDS [b][32], then published staged
       float* s_act = xin;
       if (lane < B) {
@@ -1037,7 +1042,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           qkv_rows(row, lr, ok);
           wrows_load(wq, a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, G, row, ok);
         }
-        publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, g_next, j, tag(ph + 6), plain, red);
+        publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, g_next, j, tag(ph + 6), plain);
       } else if (hx) {
         const int b = tid / RPW;
         publish_l(lx0 + (size_t)b * H + j * RPW + (tid - b * RPW), tag(ph + 6), xn, plain);
