@@ -400,7 +400,8 @@ __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 15) & ~(size_t)15; return r; };
   const size_t pw = (size_t)QPG * (D + 2);
-  size_t xin = (size_t)kStepWaves * pw * 4 + (size_t)(QPG + 2) * D * 4;
+  // attention: q/k/v, then the wave states and their merge weights (disjoint)
+  size_t xin = (size_t)(QPG + 2) * D * 4 + (size_t)kStepWaves * pw * 4 + (size_t)(kStepWaves + 2) * QPG * 4;
   const size_t merge = (size_t)BT * GPX * kXMergeChunk * pw * 4 +
                        (size_t)BT * GPX * QPG * (kXMergeChunk + 2) * 4;
   const size_t rs = (size_t)kXcds * BT * RPW * 4;
@@ -758,8 +759,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           lse_merge(m[h], lsum[h], o[h], mhi, lhi, ohi, DPL);
         }
         KMR_TRACE_MARK(l == 1 ? 61 : 64);
-        __syncthreads();   // q/k/v scratch is reused below
-        float* s_w = xin;  // [8 waves][QPG][D + 2]
+        float* s_w = xin + (QPG + 2) * D;  // [8 waves][QPG][D + 2], after q/k/v
         if (rr == 0) {
 #pragma unroll
           for (int h = 0; h < QPG; ++h) {
@@ -810,7 +810,10 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         }
         __syncthreads();
       }
-      if (group_failed(!alive)) break;
+      // (a failed gather leaves the item loop in every thread; the barrier keeps the
+      // group's waves together ahead of the merge, which measured faster)
+      __syncthreads();
+      if (!alive) break;
     }
     KMR_TRACE_MARK(tev + 3);
     // O weights of this group (rows j*RPW + 8 wave + lane/8, the XCD's head columns),
@@ -904,7 +907,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           for (int t = 0; t < n; ++t) Oc += wt[t] * xin[((size_t)seg * kXMergeChunk + t) * PW + h * (D + 2) + d];
           lse_merge(mM[q], mL[q], &mO[q], wt[kXMergeChunk], wt[kXMergeChunk + 1], &Oc, 1);
         }
-        __syncthreads();
+        __syncthreads();   // xin is rewritten by the next chunk, xs by the staging below
       }
       if (!alive) break;
       float e[PTM];
