@@ -996,7 +996,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           for (int b = 1; b < BT; ++b) if (lane == b) { gt = out[i][b]; up = out[NP + i][b]; }
           gt *= inv;
           up *= inv;
-          if (gok[i]) s_act[lane * 32 + wave * NP + i] = gt / (1.0f + expf(-gt)) * up;
+          // SiLU(gate) * up with the hardware exp and reciprocal (a few ulp)
+          if (gok[i]) s_act[lane * 32 + wave * NP + i] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
         }
       }
       __syncthreads();
@@ -1006,7 +1007,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         stage_publish(lact + (size_t)(has ? b : 0) * SA, IX, j * RA + t, has ? s_act[tid] : 0.f, has,
                       tag(ph + 5), plain);
       }
-      __syncthreads();   // s_act is LDS scratch of the next gather
+      // (s_act in xin is next rewritten by the down reduce-scatter, after the
+      // barrier of the act gather)
     }
     KMR_TRACE_MARK(tev + 8);
     // ================= down split-K over the XCD's slice, then RS_D
