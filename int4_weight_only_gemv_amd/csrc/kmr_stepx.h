@@ -631,8 +631,12 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     if constexpr (!kAhead)
       if (j < total) attn_load_kv<DPL>(kr, vr, kc, vc, j, s_ns, s_c, GPX, x, Hkv, M, D, wave);
     KMR_TRACE_MARK(tev + 1);
-    const int orow = j * RPW + wave * 8 + (lane >> 3);   // O and down rows of this lane group
-    const bool ook = wave * 8 + (lane >> 3) < RPW && orow < H;
+    // O and down rows of this lane group (at larger batches recomputed where used:
+    // held across the attention they would be spilled)
+    const int orow_l = j * RPW + wave * 8 + (lane >> 3);
+    const bool ook_l = wave * 8 + (lane >> 3) < RPW && orow_l < H;
+    auto orow_at = [&]() { return kAhead ? orow_l : j * RPW + wave * 8 + ((otid() & 63) >> 3); };
+    auto ook_at = [&](int r) { return kAhead ? ook_l : (r - j * RPW < RPW && r < H); };
     // ================= attention items (row, local kv head, split) of this XCD
     {
       for (int item = j; item < total; item += WPX) {
@@ -819,7 +823,11 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     // O weights of this group (rows j*RPW + 8 wave + lane/8, the XCD's head columns),
     // in flight while the partials are gathered
     WNarrow wo;
-    wnarrow_load(wo, Ly.o_p, Ly.o_s, Hq * D, G, x * OX, OX, ook ? orow : 0, ook);
+    {
+      const int orow = orow_at();
+      const bool ook = ook_at(orow);
+      wnarrow_load(wo, Ly.o_p, Ly.o_s, Hq * D, G, x * OX, OX, ook ? orow : 0, ook);
+    }
     // ================= merge every split of the XCD's heads; o -> staged O input
     {
       constexpr int PTM = BT;   // B * OX <= 512 * BT (OX <= 512, checked on the host)
@@ -930,7 +938,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       float out[BT];
       narrow_dot<BT>(wo, OX, B, xs, ChunkCC{cc, OX >> 5}, out);
       const int sub = lane & 7;
-      if (ook && sub < B) {
+      const int orow = orow_at();
+      if (ook_at(orow) && sub < B) {
         float v = out[0];
 #pragma unroll
         for (int b = 1; b < BT; ++b) if (sub == b) v = out[b];
@@ -979,6 +988,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       float out[2 * NP][BT];
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gate/up rows are in LDS
       if constexpr (kAhead) {
+        const int orow = orow_at();
+        const bool ook = ook_at(orow);
         wnarrow_load(wd, Ly.d_p, Ly.d_s, I, G, x * IX, IX, ook ? orow : 0, ook);
         g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
       }
@@ -997,7 +1008,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           gt *= inv;
           up *= inv;
           // SiLU(gate) * up with the hardware exp and reciprocal (a few ulp)
-          if (gok[i]) s_act[lane * 32 + wave * NP + i] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+          if (gok[i]) s_act[(kAhead ? lane : (otid() & 63)) * 32 + wave * NP + i] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
         }
       }
       __syncthreads();
@@ -1015,6 +1026,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     {
       if constexpr (!kAhead) {
         g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
+        const int orow = orow_at();
+        const bool ook = ook_at(orow);
         wnarrow_load(wd, Ly.d_p, Ly.d_s, I, G, x * IX, IX, ook ? orow : 0, ook);
       }
       if (!gather_staged<BT, 4 * BT>(lact, SA, IX, B, 0, tag(ph + 5), xs, sums)) {
@@ -1026,7 +1039,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       float out[BT];
       narrow_dot<BT>(wd, IX, B, xs, ChunkSums{sums, IX / 4}, out);
       const int sub = lane & 7;
-      if (ook && sub < B) {
+      const int orow = orow_at();
+      if (ook_at(orow) && sub < B) {
         float v = out[0];
 #pragma unroll
         for (int b = 1; b < BT; ++b) if (sub == b) v = out[b];
