@@ -32,7 +32,7 @@
 namespace kmr {
 
 #ifndef KMR_POLL_SLEEP
-#define KMR_POLL_SLEEP 2   // s_sleep units (64 clocks) between polls of a tagged buffer
+#define KMR_POLL_SLEEP 1   // s_sleep units (64 clocks) between polls of a tagged buffer
 #endif
 constexpr int kStepThreads = 512;
 constexpr int kStepWaves = kStepThreads / 64;
