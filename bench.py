@@ -9,6 +9,8 @@ step = one kmr_decode_step call (embedding, 28 layers, final norm, lm_head,
 argmax); the timed steps repeat the step at the same cache position, rewriting
 the same slot.  `--workload batch4` runs 4 continuous-batching rows (one
 finished) with the token fed back on the device and positions advancing.
+`--workload kv_copy` times the continuous-batching slot copy instead
+(kmr_kv_copy_row of a full 1024-position row of the same model's cache).
 
 Prints one JSON line (see the README of the driver contract in the design doc).
 """
@@ -143,12 +145,63 @@ def cpu_baseline(w, layers, glob, inp, budget_s=10.0):
                       f"oracle setup {setup:.1f} s untimed)"}
 
 
+def bench_kv_copy(args):
+    """Slot copy of a continuous-batching cache: row 0 of a batch-1 cache -> row 2 of
+    a batch-4 cache, positions [0, 1024), every layer and kv head, K and V, at the
+    28-layer model's cache shape (bf16 [28][B][8][1024][128])."""
+    import torch
+    from int4_weight_only_gemv_amd import kmr, synth
+    dims = synth.WORKLOADS["step"].dims
+    cfg = kmr.make_config(dims)
+    M, n = 1024, 1024
+    src = kmr.KVCache(cfg, 1, M, zero=False)
+    dst = kmr.KVCache(cfg, 4, M, zero=True)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    for t_ in (src.k, src.v):
+        t_.copy_(torch.randn(t_.shape, generator=g, device="cuda").to(torch.bfloat16))
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        kmr.kv_copy_row(dst, 2, src, 0, n, stream=stream)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        kmr.kv_copy_row(dst, 2, src, 0, n, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) * 1000 / args.steps
+    assert torch.equal(dst.k[:, 2], src.k[:, 0]) and torch.equal(dst.v[:, 2], src.v[:, 0])
+    moved = 2 * 2 * dims.n_layers * dims.n_kv_heads * n * dims.head_dim * 2   # K and V, read + write
+    gbps = moved / (us * 1e-6) / 1e9
+    out = {"metric": "KV slot copy GB/s (read + write), Qwen3-VL-2B cache shape", "value": round(gbps, 1),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(us / 1000, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "kv-row-copy-28L-8kv-128d-1024pos", "positions": n, "layers": dims.n_layers},
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_kv_copy_row",
+                        "launches_per_step": 1, "kernel_us_per_launch": round(us, 2)},
+           "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        from oracle import slots
+        sk, sv = src.k.cpu().view(torch.int16).numpy(), src.v.cpu().view(torch.int16).numpy()
+        dk, dv = dst.k.cpu().view(torch.int16).numpy(), dst.v.cpu().view(torch.int16).numpy()
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 3.0 or reps < 3:
+            slots.kv_copy_row(dk, dv, 2, sk, sv, 0, n)
+            reps += 1
+        sec = (time.perf_counter() - t0) / reps
+        out["cpu_baseline"] = {"value": round(moved / sec / 1e9, 2), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{reps} whole row copies (numpy, one thread)"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["step", "batch4"], default="step")
+    ap.add_argument("--workload", choices=["step", "batch4", "kv_copy"], default="step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
@@ -163,6 +216,9 @@ def main():
 
     if args.calibrate_copy_mib > 0:
         copy_calibration(args.calibrate_copy_mib)
+    if args.workload == "kv_copy":
+        bench_kv_copy(args)
+        return
     w, model, kv, layers, glob = build(args.workload)
     inp = synth.step_inputs(w)
     B = w.batch

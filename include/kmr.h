@@ -201,6 +201,47 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
                     uint8_t* finished, int32_t batch, int32_t* next_ids, float* logits,
                     uint32_t flags, void* ws, size_t ws_bytes, kmr_stream_t stream);
 
+/*
+ * Slot operations of a continuous-batching scheduler (kaminari section 08: the
+ * ContinuousBatchScheduler admits requests into free DecodeSlots, each pinned to a
+ * physical row of one shared static cache, ticks the active slots one token at a
+ * time and finalizes a row the moment it finishes; copy_row_from moves a row's KV
+ * state into another row).  All three run on `stream` without a host round trip
+ * and allocate nothing.
+ *
+ * kmr_kv_copy_row -- for every layer and kv head, copies positions
+ * [0, n_positions) of row src_row of `src` (K and V) to row dst_row of `dst`,
+ * bit for bit; every other position and row of dst is left unchanged.  dst and
+ * src may be the same cache (rows must then differ) or two caches with equal
+ * n_layers, n_kv_heads and head_dim (batch and max_len may differ).
+ * KMR_EINVAL: null pointers, a row outside its cache, n_positions outside
+ * [0, min(dst->max_len, src->max_len)], unequal dims, or a row copied onto
+ * itself.  n_positions == 0 launches nothing.
+ */
+int kmr_kv_copy_row(const kmr_kv* dst, int32_t dst_row, const kmr_kv* src, int32_t src_row,
+                    int32_t n_positions, kmr_stream_t stream);
+
+/*
+ * kmr_slot_admit -- makes row `row` of a batch of `batch` live for the next
+ * kmr_decode_step: token_ids[row] = token, positions[a * batch + row] = pos[a] for
+ * the t, h, w axes a = 0, 1, 2 (pos is a HOST array of 3), cache_position[row] =
+ * cache_pos, finished[row] = 0.  The cache row itself is not touched (fill it
+ * with a prefill or kmr_kv_copy_row first).  KMR_EINVAL: null pointers, row
+ * outside [0, batch), batch outside [1, KMR_MAX_BATCH], a negative cache_pos or
+ * position.  (A cache_pos at or past the cache's max_len is caught by the step,
+ * which raises KMR_STATUS_CACHE_POS.)
+ */
+int kmr_slot_admit(int32_t* token_ids, int32_t* positions, int32_t* cache_position,
+                   uint8_t* finished, int32_t batch, int32_t row, int32_t token,
+                   const int32_t* pos, int32_t cache_pos, kmr_stream_t stream);
+
+/*
+ * kmr_slot_retire -- finished[row] = 1: from the next step on the row is fed the
+ * pad id, emits the pad id and keeps its cache position and positions frozen.
+ * KMR_EINVAL: null pointer, row outside [0, batch), batch outside [1, KMR_MAX_BATCH].
+ */
+int kmr_slot_retire(uint8_t* finished, int32_t batch, int32_t row, kmr_stream_t stream);
+
 /* Synchronises `stream`, returns the sticky KMR_STATUS_* bits of `ws` in
  * *flags_out (host pointer) and clears them. */
 int kmr_status(void* ws, kmr_stream_t stream, uint32_t* flags_out);

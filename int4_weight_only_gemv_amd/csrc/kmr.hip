@@ -638,6 +638,58 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
   return check_hip("decode_step launch");
 }
 
+int kmr_kv_copy_row(const kmr_kv* dst, int32_t dst_row, const kmr_kv* src, int32_t src_row,
+                    int32_t n_positions, kmr_stream_t stream) {
+  if (!dst || !src || !dst->k || !dst->v || !src->k || !src->v) return fail(KMR_EINVAL, "null cache");
+  if (dst->n_layers != src->n_layers || dst->n_kv_heads != src->n_kv_heads || dst->head_dim != src->head_dim)
+    return fail(KMR_EINVAL, "caches differ in layers, kv heads or head_dim");
+  if (dst->n_layers <= 0 || dst->n_kv_heads <= 0 || dst->head_dim <= 0 || dst->head_dim % 8)
+    return fail(KMR_EINVAL, "bad cache dims");
+  if (dst_row < 0 || dst_row >= dst->batch || src_row < 0 || src_row >= src->batch)
+    return fail(KMR_EINVAL, "row outside its cache (dst %d of %d, src %d of %d)", dst_row, dst->batch,
+                src_row, src->batch);
+  const int lim = dst->max_len < src->max_len ? dst->max_len : src->max_len;
+  if (n_positions < 0 || n_positions > lim)
+    return fail(KMR_EINVAL, "n_positions %d outside [0, %d]", n_positions, lim);
+  if (dst->k == src->k && dst_row == src_row) return fail(KMR_EINVAL, "row copied onto itself");
+  if (n_positions == 0) return KMR_OK;
+  KvCopyArgs a{};
+  a.sk = static_cast<const uint16_t*>(src->k); a.sv = static_cast<const uint16_t*>(src->v);
+  a.dk = static_cast<uint16_t*>(dst->k); a.dv = static_cast<uint16_t*>(dst->v);
+  a.Hkv = dst->n_kv_heads; a.D = dst->head_dim; a.n = n_positions;
+  a.sB = src->batch; a.sM = src->max_len; a.srow = src_row;
+  a.dB = dst->batch; a.dM = dst->max_len; a.drow = dst_row;
+  const size_t words = (size_t)n_positions * a.D / 8;
+  const unsigned bx = (unsigned)std::min<size_t>((words + 255) / 256, 64);
+  hipLaunchKernelGGL(k_kv_copy_row, dim3(bx, 2 * dst->n_layers * dst->n_kv_heads), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), a);
+  return check_hip("kv row copy launch");
+}
+
+int kmr_slot_admit(int32_t* token_ids, int32_t* positions, int32_t* cache_position,
+                   uint8_t* finished, int32_t batch, int32_t row, int32_t token,
+                   const int32_t* pos, int32_t cache_pos, kmr_stream_t stream) {
+  if (!token_ids || !positions || !cache_position || !finished || !pos) return fail(KMR_EINVAL, "null pointer");
+  if (batch <= 0 || batch > KMR_MAX_BATCH || row < 0 || row >= batch)
+    return fail(KMR_EINVAL, "row %d outside batch %d (at most %d)", row, batch, KMR_MAX_BATCH);
+  if (cache_pos < 0 || pos[0] < 0 || pos[1] < 0 || pos[2] < 0)
+    return fail(KMR_EINVAL, "negative cache position or position");
+  hipLaunchKernelGGL(k_slot_set, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), token_ids,
+                     positions, cache_position, finished, batch, row, 1, token, pos[0], pos[1], pos[2],
+                     cache_pos);
+  return check_hip("slot admit launch");
+}
+
+int kmr_slot_retire(uint8_t* finished, int32_t batch, int32_t row, kmr_stream_t stream) {
+  if (!finished) return fail(KMR_EINVAL, "null pointer");
+  if (batch <= 0 || batch > KMR_MAX_BATCH || row < 0 || row >= batch)
+    return fail(KMR_EINVAL, "row %d outside batch %d (at most %d)", row, batch, KMR_MAX_BATCH);
+  hipLaunchKernelGGL(k_slot_set, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr),
+                     static_cast<int32_t*>(nullptr), finished, batch, row, 0, 0, 0, 0, 0, 0);
+  return check_hip("slot retire launch");
+}
+
 int kmr_status(void* ws, kmr_stream_t stream, uint32_t* flags_out) {
   if (!ws || !flags_out) return fail(KMR_EINVAL, "null workspace or flags_out");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

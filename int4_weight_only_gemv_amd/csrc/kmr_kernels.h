@@ -28,6 +28,44 @@ __global__ void k_fill_zero(uint32_t* __restrict__ p, size_t words) {
   for (; i < words; i += stride) p[i] = 0u;
 }
 
+// ------------------------------------------------------------------ slots
+// One cache row copy: blockIdx.y = 2 * (layer * Hkv + head) + (0: K, 1: V) picks a
+// contiguous run of n * D bf16 in each cache; 16-byte words along x.
+struct KvCopyArgs {
+  const uint16_t *sk, *sv;
+  uint16_t *dk, *dv;
+  int Hkv, D, n;
+  int sB, sM, srow, dB, dM, drow;
+};
+
+__global__ __launch_bounds__(256) void k_kv_copy_row(KvCopyArgs a) {
+  const int s = blockIdx.y >> 1, which = blockIdx.y & 1;
+  const int l = s / a.Hkv, g = s - l * a.Hkv;
+  const uint4* src = reinterpret_cast<const uint4*>(
+      (which ? a.sv : a.sk) + (((size_t)l * a.sB + a.srow) * a.Hkv + g) * a.sM * a.D);
+  uint4* dst = reinterpret_cast<uint4*>((which ? a.dv : a.dk) +
+                                        (((size_t)l * a.dB + a.drow) * a.Hkv + g) * a.dM * a.D);
+  const size_t words = (size_t)a.n * a.D / 8;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256)
+    dst[i] = src[i];
+}
+
+// Admit (admit != 0) or retire one slot: single-thread stores of its step state.
+__global__ void k_slot_set(int32_t* ids, int32_t* pos, int32_t* cpos, uint8_t* fin, int B, int row,
+                           int admit, int token, int p0, int p1, int p2, int c) {
+  if (threadIdx.x != 0) return;
+  if (admit) {
+    ids[row] = token;
+    pos[row] = p0;
+    pos[B + row] = p1;
+    pos[2 * B + row] = p2;
+    cpos[row] = c;
+    fin[row] = 0;
+  } else {
+    fin[row] = 1;
+  }
+}
+
 // ------------------------------------------------------------------ int4 quantizer
 // Per (row, group): s = bf16(max((hi-lo)/15, 2^-24)), z = bf16(lo + 8 s),
 // q = clamp(rne((w - z)/s) + 8, 0, 15); IEEE fp32, each operation rounded on its

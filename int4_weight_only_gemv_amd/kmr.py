@@ -75,11 +75,15 @@ _lib.kmr_decode_layer.argtypes = [C.POINTER(Config), C.POINTER(Layer), _i32, C.P
 _lib.kmr_decode_step.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(KV), _p, _p, _p, _p,
                                  _i32, _p, _p, C.c_uint32, _p, C.c_size_t, _p]
 _lib.kmr_status.argtypes = [_p, _p, C.POINTER(C.c_uint32)]
+_lib.kmr_kv_copy_row.argtypes = [C.POINTER(KV), _i32, C.POINTER(KV), _i32, _i32, _p]
+_lib.kmr_slot_admit.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, C.POINTER(_i32), _i32, _p]
+_lib.kmr_slot_retire.argtypes = [_p, _i32, _i32, _p]
 _lib.kmr_strerror.restype = C.c_char_p
 _lib.kmr_last_error.restype = C.c_char_p
 
-EXPORTED = ["kmr_kv_alloc", "kmr_quantize_int4", "kmr_workspace_bytes", "kmr_workspace_init",
-            "kmr_decode_layer", "kmr_decode_step", "kmr_status", "kmr_strerror", "kmr_last_error"]
+EXPORTED = ["kmr_kv_alloc", "kmr_kv_copy_row", "kmr_quantize_int4", "kmr_workspace_bytes",
+            "kmr_workspace_init", "kmr_decode_layer", "kmr_decode_step", "kmr_slot_admit",
+            "kmr_slot_retire", "kmr_status", "kmr_strerror", "kmr_last_error"]
 
 
 class KmrError(RuntimeError):
@@ -171,6 +175,28 @@ class KVCache:
         half = self.desc.bytes // 2
         self.k = self.buf[:half].view(torch.bfloat16)[:n].view(shape)
         self.v = self.buf[half:].view(torch.bfloat16)[:n].view(shape)
+
+
+def kv_copy_row(dst: "KVCache", dst_row: int, src: "KVCache", src_row: int, n_positions: int,
+                stream=None) -> None:
+    """Positions [0, n_positions) of cache row src_row of src -> row dst_row of dst
+    (every layer and kv head, K and V)."""
+    _check(_lib.kmr_kv_copy_row(C.byref(dst.desc), dst_row, C.byref(src.desc), src_row, n_positions,
+                                _stream(stream)))
+
+
+def slot_admit(token_ids: torch.Tensor, positions: torch.Tensor, cache_position: torch.Tensor,
+               finished: torch.Tensor, row: int, token: int, pos, cache_pos: int, stream=None) -> None:
+    """Row `row` becomes live: its token id, three positions (t, h, w), cache position,
+    and a cleared finished flag, set on the device."""
+    p3 = (_i32 * 3)(*[int(v) for v in pos])
+    _check(_lib.kmr_slot_admit(_ptr(token_ids), _ptr(positions), _ptr(cache_position), _ptr(finished),
+                               int(token_ids.numel()), row, token, p3, cache_pos, _stream(stream)))
+
+
+def slot_retire(finished: torch.Tensor, row: int, stream=None) -> None:
+    """Row `row` is finished from the next step on."""
+    _check(_lib.kmr_slot_retire(_ptr(finished), int(finished.numel()), row, _stream(stream)))
 
 
 def _qweight(packed: torch.Tensor, sz: torch.Tensor) -> QWeight:

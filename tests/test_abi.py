@@ -123,3 +123,34 @@ def test_bad_calls_are_rejected_before_launch(kmr):
                                    fake, 1 << 30, None)
     assert rc == kmr.KMR_EINVAL and b"norm" in kmr._lib.kmr_last_error()
     assert kmr._lib.kmr_strerror(kmr.KMR_ENOMEM) == b"buffer or workspace too small"
+
+
+def test_bad_slot_calls_are_rejected_before_launch(kmr):
+    import ctypes as C
+    fake = C.c_void_p(0x1000)
+
+    def kv(batch, max_len, layers=2, heads=8, dim=128):
+        d = kmr.KV()
+        d.k, d.v = 0x1000, 0x2000
+        d.n_layers, d.batch, d.n_kv_heads, d.max_len, d.head_dim = layers, batch, heads, max_len, dim
+        return d
+
+    a, b = kv(4, 64), kv(2, 32)
+    copy = kmr._lib.kmr_kv_copy_row
+    assert copy(C.byref(a), 4, C.byref(b), 0, 8, None) == kmr.KMR_EINVAL        # dst row
+    assert copy(C.byref(a), 0, C.byref(b), 2, 8, None) == kmr.KMR_EINVAL        # src row
+    assert copy(C.byref(a), 0, C.byref(b), 1, 33, None) == kmr.KMR_EINVAL       # past src max_len
+    assert copy(C.byref(a), 0, C.byref(b), 1, -1, None) == kmr.KMR_EINVAL
+    assert copy(C.byref(a), 1, C.byref(a), 1, 8, None) == kmr.KMR_EINVAL        # onto itself
+    c = kv(2, 32, heads=4)
+    assert copy(C.byref(a), 0, C.byref(c), 1, 8, None) == kmr.KMR_EINVAL        # unequal dims
+    assert b"kv heads" in kmr._lib.kmr_last_error()
+    assert copy(C.byref(a), 0, C.byref(b), 1, 0, None) == kmr.KMR_OK            # nothing to copy
+    p3 = (C.c_int32 * 3)(1, 2, 3)
+    admit = kmr._lib.kmr_slot_admit
+    assert admit(fake, fake, fake, fake, 4, 4, 7, p3, 5, None) == kmr.KMR_EINVAL
+    assert admit(fake, fake, fake, fake, 17, 0, 7, p3, 5, None) == kmr.KMR_EINVAL
+    assert admit(fake, fake, fake, fake, 4, 0, 7, p3, -1, None) == kmr.KMR_EINVAL
+    assert admit(None, fake, fake, fake, 4, 0, 7, p3, 5, None) == kmr.KMR_EINVAL
+    assert kmr._lib.kmr_slot_retire(fake, 4, -1, None) == kmr.KMR_EINVAL
+    assert kmr._lib.kmr_slot_retire(None, 4, 0, None) == kmr.KMR_EINVAL
