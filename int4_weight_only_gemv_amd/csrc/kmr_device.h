@@ -64,6 +64,11 @@ __device__ __forceinline__ void settle(uint4 v) {
   settle(v.w);
 }
 
+// 2^x with the hardware exponential (about 1 ulp; results below the smallest
+// normal float may flush to zero): for softmax and log-sum-exp weights, where such
+// terms are negligible against the largest weight of 1.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // 1/sqrt(x) with the hardware reciprocal square root (within 1 ulp); used for
 // RMSNorm scales, whose inputs are at least epsilon.
 __device__ __forceinline__ float rsqrt_f(float x) { return __builtin_amdgcn_rsqf(x); }

@@ -498,8 +498,8 @@ __device__ __forceinline__ void norm_rope(float (&vals)[DPL], const float (&gain
 __device__ __forceinline__ void lse_merge(float& m, float& l, float* o, float m2, float l2,
                                           const float* o2, int n) {
   const float M = fmaxf(m, m2);
-  const float c1 = m == -INFINITY ? 0.f : exp2f(m - M);
-  const float c2 = m2 == -INFINITY ? 0.f : exp2f(m2 - M);
+  const float c1 = m == -INFINITY ? 0.f : exp2_fast(m - M);
+  const float c2 = m2 == -INFINITY ? 0.f : exp2_fast(m2 - M);
   l = l * c1 + l2 * c2;
   for (int i = 0; i < n; ++i) o[i] = o[i] * c1 + o2[i] * c2;
   m = M;
@@ -895,8 +895,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
           sc = row16_sum(sc) * a.scale_log2;
           if (valid) {
             const float mn = fmaxf(m[h], sc);
-            const float corr = exp2f(m[h] - mn);
-            const float pe = exp2f(sc - mn);
+            const float corr = exp2_fast(m[h] - mn);
+            const float pe = exp2_fast(sc - mn);
             lsum[h] = lsum[h] * corr + pe;
 #pragma unroll
             for (int e = 0; e < DPL; ++e) o[h][e] = o[h][e] * corr + pe * vv[e];

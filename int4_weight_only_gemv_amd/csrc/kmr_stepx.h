@@ -737,8 +737,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
             sc = row16_sum(sc) * a.scale_log2;
             if (valid) {
               const float mn = fmaxf(m[h], sc);
-              const float corr = exp2f(m[h] - mn);
-              const float pe = exp2f(sc - mn);
+              const float corr = exp2_fast(m[h] - mn);
+              const float pe = exp2_fast(sc - mn);
               lsum[h] = lsum[h] * corr + pe;
 #pragma unroll
               for (int e = 0; e < DPL; ++e) o[h][e] = o[h][e] * corr + pe * vv[e];
@@ -787,7 +787,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           Mx = fmaxf(Mx, dpp<0x4E>(Mx));        // lane ^ 2
           Mx = fmaxf(Mx, lane_xor4(Mx));        // lane ^ 4
           Mx = fmaxf(Mx, row16_swap8(Mx));      // lane ^ 8
-          const float e = mw == -INFINITY ? 0.f : exp2f(mw - Mx);
+          const float e = mw == -INFINITY ? 0.f : exp2_fast(mw - Mx);
           float Ls = e * lw;
           Ls += dpp<0x4E>(Ls);
           Ls += lane_xor4(Ls);
@@ -887,7 +887,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           Mc = fmaxf(Mc, dpp<0xB1>(Mc));   // lane ^ 1
           Mc = fmaxf(Mc, dpp<0x4E>(Mc));   // lane ^ 2
           Mc = fmaxf(Mc, lane_xor4(Mc));   // lane ^ 4
-          const float e = mt == -INFINITY ? 0.f : exp2f(mt - Mc);
+          const float e = mt == -INFINITY ? 0.f : exp2_fast(mt - Mc);
           float Lc = e * lt;
           Lc += dpp<0xB1>(Lc);
           Lc += dpp<0x4E>(Lc);
