@@ -275,8 +275,10 @@ __device__ __forceinline__ bool gather_staged(const uint64_t* src, long long str
   bool ok = true;
   for (int base = 0; base < total && ok; base += kStepThreads * PT) {
     uint64_t v[PT];
-    int kk[PT], bb[PT];
+    const uint64_t* sp[PT];
+    uint32_t* dp[PT];
     bool has[PT];
+    // source and LDS destination of every word, worked out before the first poll
 #pragma unroll
     for (int q = 0; q < PT; ++q) {
       const int i = base + kStepThreads * q + tid;
@@ -284,15 +286,18 @@ __device__ __forceinline__ bool gather_staged(const uint64_t* src, long long str
       int b = 0;
 #pragma unroll
       for (int t = 1; t < BT; ++t) b += i >= t * per ? 1 : 0;
-      bb[q] = b;
-      kk[q] = i - b * per;
+      const int k = i - b * per, w8 = k >> 2;
+      sp[q] = src + (size_t)b * stride + k;
+      dp[q] = k < K2 ? xs32 + ((b * 4 + (w8 & 3)) * CH + (w8 >> 2)) * 4 + (k & 3)
+            : k < K2 + K4 ? reinterpret_cast<uint32_t*>(s_sum) + b * K4 + (k - K2)
+                          : reinterpret_cast<uint32_t*>(s_ss) + b * nss + (k - K2 - K4);
     }
     uint32_t spins = 0;
     bool fresh;
     do {
 #pragma unroll
       for (int q = 0; q < PT; ++q)
-        if (has[q]) v[q] = ld_dev64(src + (size_t)bb[q] * stride + kk[q]);
+        if (has[q]) v[q] = ld_dev64(sp[q]);
       fresh = true;
 #pragma unroll
       for (int q = 0; q < PT; ++q)
@@ -303,19 +308,8 @@ __device__ __forceinline__ bool gather_staged(const uint64_t* src, long long str
       }
     } while (!fresh);
 #pragma unroll
-    for (int q = 0; q < PT; ++q) {
-      if (!has[q]) continue;
-      const int k = kk[q], b = bb[q];
-      const uint32_t bits = (uint32_t)v[q];
-      if (k < K2) {
-        const int w8 = k >> 2, i = k & 3;
-        xs32[((b * 4 + (w8 & 3)) * CH + (w8 >> 2)) * 4 + i] = bits;
-      } else if (k < K2 + K4) {
-        s_sum[b * K4 + (k - K2)] = __uint_as_float(bits);
-      } else {
-        s_ss[b * nss + (k - K2 - K4)] = __uint_as_float(bits);
-      }
-    }
+    for (int q = 0; q < PT; ++q)
+      if (has[q]) *dp[q] = (uint32_t)v[q];
   }
   return !group_failed(!ok);
 }
