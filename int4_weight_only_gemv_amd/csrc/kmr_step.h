@@ -430,7 +430,7 @@ __device__ __forceinline__ void wave_dot_c(const WRows<NR, CPL>& w, int K, int B
         const float s = bf16_lo(w.sz[i][j]), z = bf16_hi(w.sz[i][j]);
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
-          if (b >= B) break;
+          if (BT > 1 && b >= B) break;   // (a batch-1 instantiation runs only at B == 1)
           float d = 0.f;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {

@@ -126,7 +126,7 @@ __device__ __forceinline__ void narrow_dot(const WNarrow& w, int KS, int B, cons
       const float s = bf16_lo(w.sz[t]), z = bf16_hi(w.sz[t]);
 #pragma unroll
       for (int b = 0; b < BT; ++b) {
-        if (b >= B) break;
+        if (BT > 1 && b >= B) break;   // (a batch-1 instantiation runs only at B == 1)
         uint4 xv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) xv[q] = xs[(b * 4 + q) * CHs + c];
@@ -331,7 +331,7 @@ __device__ __forceinline__ float row_inv(const float* s_ss, int B, int nss, int 
   float r = 1.f;
 #pragma unroll
   for (int b = 0; b < BT; ++b) {
-    if (b >= B) break;
+    if (BT > 1 && b >= B) break;
     const float v = staged_inv(s_ss, b, nss, K, eps);
     if (lane == b) r = v;
   }
@@ -364,7 +364,7 @@ __device__ __forceinline__ void publish_staged_x(uint64_t* dst, long long stride
   const int WPR = RPW >= 64 ? RPW >> 6 : 1;
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) {
-    if (bb >= B) break;
+    if (BT > 1 && bb >= B) break;
     const int w0 = (bb * RPW) >> 6, w1 = ((bb + 1) * RPW - 1) >> 6;
     if (wave >= w0 && wave <= w1) {
       const float ss = wave_sum((has && b == bb) ? xn * xn : 0.f);
