@@ -704,7 +704,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
   constexpr int DPL = D / 16, HALF = D / 2, PW = QPG * (D + 2);   // partial words per split
   const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x, nwg = gridDim.x;
-  const int B = a.B, H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, G = a.G, M = a.M;
+  const int B = BT == 1 ? 1 : a.B;   // (a batch-1 instantiation runs only at B == 1)
+  const int H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, G = a.G, M = a.M;
   const int NQKV = (Hq + 2 * Hkv) * D, QD = Hq * D;
   const int KMAX = H > I ? (H > QD ? H : QD) : (I > QD ? I : QD);
   const int RPBX = (H + nwg - 1) / nwg;                     // residual rows owned per group

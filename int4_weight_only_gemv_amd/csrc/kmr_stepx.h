@@ -467,7 +467,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x, nwg = gridDim.x;
   const int x = wg % kXcds, j = wg / kXcds, WPX = nwg / kXcds;
-  const int B = a.B, H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, G = a.G, M = a.M;
+  const int B = BT == 1 ? 1 : a.B;   // (a batch-1 instantiation runs only at B == 1)
+  const int H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, G = a.G, M = a.M;
   const int GPX = Hkv / kXcds, QX = GPX * (QPG + 2) * D, OX = GPX * QPG * D, IX = I / kXcds;
   const int RPW = (H + WPX - 1) / WPX, RQ = (QX + WPX - 1) / WPX, RA = (IX + WPX - 1) / WPX;
   const int NSX = (M + kXSplit - 1) / kXSplit;
