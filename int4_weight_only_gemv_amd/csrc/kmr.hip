@@ -318,7 +318,8 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
 // Shapes the persistent kernel is built for (one 2048-column chunk per lane for
 // hidden and n_heads*head_dim, three for intermediate, GQA groups of 2).
 bool step_kernel_fits(const kmr_config* c, int B) {
-  return B <= 4 && c->hidden <= 2048 && c->n_heads * c->head_dim <= 2048 &&
+  return B <= 4 && (c->group_size & (c->group_size - 1)) == 0 && c->hidden <= 2048 &&
+         c->n_heads * c->head_dim <= 2048 &&
          c->intermediate <= 6144 && c->n_layers <= kMaxStepLayers &&
          c->n_heads == 2 * c->n_kv_heads && c->vocab > 0;
 }
@@ -594,6 +595,8 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
     a.x_sx = w.xz.sx; a.srow_x = w.xz.srow_x; a.srow_a = w.xz.srow_a;
     a.B = batch; a.H = cfg->hidden; a.Hq = cfg->n_heads; a.Hkv = cfg->n_kv_heads;
     a.I = cfg->intermediate; a.V = cfg->vocab; a.L = cfg->n_layers; a.G = cfg->group_size;
+    a.lgG = 0;
+    while ((1 << a.lgG) < a.G) ++a.lgG;
     a.M = kv->max_len; a.cacheB = kv->batch; a.NS = w.ns; a.pad_id = cfg->pad_id;
     a.eos_id = cfg->eos_id; a.flags = flags & KMR_ADVANCE; a.eps = cfg->rms_eps;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg->head_dim));

@@ -93,7 +93,7 @@ struct StepArgs {
   long long x_lx, x_sx, x_lqkv, x_lpart, x_lact, srow_x, srow_a;
   int intra_plain;          // 1: XCD-local stores stay in the XCD's L2 (placement verified)
   // dims
-  int B, H, Hq, Hkv, I, V, L, G, M, cacheB, NS, pad_id, eos_id;
+  int B, H, Hq, Hkv, I, V, L, G, lgG, M, cacheB, NS, pad_id, eos_id;   // lgG = log2(G)
   uint32_t flags;
   uint64_t* trace;          // per-group phase timestamps (diagnostic builds only) or null
   float eps, scale_log2;
@@ -346,9 +346,9 @@ struct WRows {
 
 template <int NR, int CPL>
 __device__ __forceinline__ void wrows_load(WRows<NR, CPL>& w, const uint8_t* packed,
-                                           const uint32_t* sz, int K, int G, const int* row,
+                                           const uint32_t* sz, int K, int lgG, const int* row,
                                            const bool* ok) {
-  const int lane = otid() & 63, CH = K >> 5, NG = K / G;
+  const int lane = otid() & 63, CH = K >> 5, NG = K >> lgG;
 #pragma unroll
   for (int i = 0; i < NR; ++i)
 #pragma unroll
@@ -356,7 +356,7 @@ __device__ __forceinline__ void wrows_load(WRows<NR, CPL>& w, const uint8_t* pac
       const int c = lane + 64 * j;
       if (ok[i] && c < CH) {
         w.raw[i][j] = load_stream16(packed + (size_t)row[i] * (K / 2) + 16 * c);
-        w.sz[i][j] = sz[(size_t)row[i] * NG + (32 * c) / G];
+        w.sz[i][j] = sz[(size_t)row[i] * NG + ((32 * c) >> lgG)];
       } else {
         w.raw[i][j] = make_uint4(0, 0, 0, 0);
         w.sz[i][j] = 0;
@@ -705,7 +705,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
   const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x, nwg = gridDim.x;
   const int B = BT == 1 ? 1 : a.B;   // (a batch-1 instantiation runs only at B == 1)
-  const int H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, G = a.G, M = a.M;
+  const int H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, M = a.M;
   const int NQKV = (Hq + 2 * Hkv) * D, QD = Hq * D;
   const int KMAX = H > I ? (H > QD ? H : QD) : (I > QD ? I : QD);
   const int RPBX = (H + nwg - 1) / nwg;                     // residual rows owned per group
@@ -767,7 +767,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
           row[i] = ok[i] ? n : 0;
         }
         WRows<NR, 1> w;
-        wrows_load(w, Ly.qkv_p, Ly.qkv_s, H, G, row, ok);
+        wrows_load(w, Ly.qkv_p, Ly.qkv_s, H, a.lgG, row, ok);
         if (r0 == 0) {
           if (!gather_stage<BT, 4 * BT>(a.tx, H, B, tag(ph), Ly.in_norm, a.eps, xs, cc, red)) { alive = false; break; }
         }
@@ -1010,7 +1010,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
       bool ok[NR] = {rr < RPBX && n < H};
       if (ok[0]) row[0] = n;
       WRows<NR, 1> w;
-      wrows_load(w, Ly.o_p, Ly.o_s, QD, G, row, ok);
+      wrows_load(w, Ly.o_p, Ly.o_s, QD, a.lgG, row, ok);
       if (r2 == 0) {
         if (!gather_stage<BT, 4 * BT>(a.to, QD, B, tag(ph + 3), nullptr, a.eps, xs, cc, red)) { alive = false; break; }
       }
@@ -1043,7 +1043,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
           row[NP + i] = ok[i] ? n + I : 0;
         }
         WRows<2 * NP, 1> w;
-        wrows_load(w, Ly.gu_p, Ly.gu_s, H, G, row, ok);
+        wrows_load(w, Ly.gu_p, Ly.gu_s, H, a.lgG, row, ok);
         if (r0 == 0) {
           if (!gather_stage<BT, 4 * BT>(a.tx, H, B, tag(ph + 4), Ly.post_norm, a.eps, xs, cc, red)) { alive = false; break; }
         }
@@ -1073,7 +1073,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
       bool ok[NR] = {rr < RPBX && n < H};
       if (ok[0]) row[0] = n;
       WRows<NR, CPL> w;
-      wrows_load(w, Ly.d_p, Ly.d_s, I, G, row, ok);
+      wrows_load(w, Ly.d_p, Ly.d_s, I, a.lgG, row, ok);
       if (r2 == 0) {
         if (!gather_stage<BT, 12>(a.tact, I, B, tag(ph + 5), nullptr, a.eps, xs, cc, red)) { alive = false; break; }
       }

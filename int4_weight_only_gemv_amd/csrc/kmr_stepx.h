@@ -93,14 +93,14 @@ struct WNarrow {
 };
 
 __device__ __forceinline__ void wnarrow_load(WNarrow& w, const uint8_t* packed, const uint32_t* sz,
-                                             int K, int G, int k0, int KS, int row, bool ok) {
-  const int sub = otid() & 7, CHs = KS >> 5, NG = K / G;
+                                             int K, int lgG, int k0, int KS, int row, bool ok) {
+  const int sub = otid() & 7, CHs = KS >> 5, NG = K >> lgG;
 #pragma unroll
   for (int t = 0; t < kXNarrowCpl; ++t) {
     const int c = sub + 8 * t;
     if (ok && c < CHs) {
       w.raw[t] = load_stream16(packed + (size_t)row * (K / 2) + (k0 >> 1) + 16 * c);
-      w.sz[t] = sz[(size_t)row * NG + (k0 + 32 * c) / G];
+      w.sz[t] = sz[(size_t)row * NG + ((k0 + 32 * c) >> lgG)];
     } else {
       w.raw[t] = make_uint4(0, 0, 0, 0);
       w.sz[t] = 0;
@@ -419,13 +419,13 @@ __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int
 // while they are in flight): row i of the wave, lane l takes 32-column chunk l
 // (16 bytes of codes at codes + (i*64 + l)*16, its scale/zero word at szw + i*64 + l).
 // The data is in LDS once this wave's vector-memory count has drained.
-__device__ __forceinline__ void wrows_to_lds(const uint8_t* packed, const uint32_t* sz, int K, int G,
+__device__ __forceinline__ void wrows_to_lds(const uint8_t* packed, const uint32_t* sz, int K, int lgG,
                                              const int* row, uint4* codes, uint32_t* szw) {
-  const int lane = otid() & 63, NG = K / G;
+  const int lane = otid() & 63, NG = K >> lgG;
 #pragma unroll
   for (int i = 0; i < kXGuRows; ++i) {
     __builtin_amdgcn_global_load_lds(packed + (size_t)row[i] * (K / 2) + 16 * lane, codes + i * 64, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(sz + (size_t)row[i] * NG + (32 * lane) / G, szw + i * 64, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(sz + (size_t)row[i] * NG + ((32 * lane) >> lgG), szw + i * 64, 4, 0, 0);
   }
 }
 
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   const int wg = blockIdx.x, nwg = gridDim.x;
   const int x = wg % kXcds, j = wg / kXcds, WPX = nwg / kXcds;
   const int B = BT == 1 ? 1 : a.B;   // (a batch-1 instantiation runs only at B == 1)
-  const int H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, G = a.G, M = a.M;
+  const int H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, M = a.M;
   const int GPX = Hkv / kXcds, QX = GPX * (QPG + 2) * D, OX = GPX * QPG * D, IX = I / kXcds;
   const int RPW = (H + WPX - 1) / WPX, RQ = (QX + WPX - 1) / WPX, RA = (IX + WPX - 1) / WPX;
   const int NSX = (M + kXSplit - 1) / kXSplit;
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     int row[NRQ], lr[NRQ];
     bool ok[NRQ];
     qkv_rows(row, lr, ok);
-    wrows_load(wq, a.layers[0].qkv_p, a.layers[0].qkv_s, H, G, row, ok);
+    wrows_load(wq, a.layers[0].qkv_p, a.layers[0].qkv_s, H, a.lgG, row, ok);
   }
 
   for (int l = 0; l < a.L && alive; ++l) {
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       bool ok[NR];
       qkv_rows(row, lr, ok);
       if constexpr (!kAhead) {
-        wrows_load(wq, Ly.qkv_p, Ly.qkv_s, H, G, row, ok);
+        wrows_load(wq, Ly.qkv_p, Ly.qkv_s, H, a.lgG, row, ok);
         asm volatile("" ::: "memory");   // keep the weight requests ahead of the polls
       }
       if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, NSS, tag(ph), xs, sums)) {
@@ -821,7 +821,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     {
       const int orow = orow_at();
       const bool ook = ook_at(orow);
-      wnarrow_load(wo, Ly.o_p, Ly.o_s, Hq * D, G, x * OX, OX, ook ? orow : 0, ook);
+      wnarrow_load(wo, Ly.o_p, Ly.o_s, Hq * D, a.lgG, x * OX, OX, ook ? orow : 0, ook);
     }
     // ================= merge every split of the XCD's heads; o -> staged O input
     {
@@ -959,7 +959,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     uint4* gu_codes = reinterpret_cast<uint4*>(smem + Ld.wgu) + wave * kXGuRows * 64;
     uint32_t* gu_sz = reinterpret_cast<uint32_t*>(smem + Ld.wgu + (size_t)kStepWaves * kXGuRows * 64 * 16) +
                       wave * kXGuRows * 64;
-    wrows_to_lds(Ly.gu_p, Ly.gu_s, H, G, grow, gu_codes, gu_sz);
+    wrows_to_lds(Ly.gu_p, Ly.gu_s, H, a.lgG, grow, gu_codes, gu_sz);
     // ================= RS_O: x rows after O, published staged for post_norm
     {
       float xn;
@@ -985,7 +985,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       if constexpr (kAhead) {
         const int orow = orow_at();
         const bool ook = ook_at(orow);
-        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, G, x * IX, IX, ook ? orow : 0, ook);
+        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, a.lgG, x * IX, IX, ook ? orow : 0, ook);
         g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
       }
       WRows<2 * NP, 1> wgu;
@@ -1023,7 +1023,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
         const int orow = orow_at();
         const bool ook = ook_at(orow);
-        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, G, x * IX, IX, ook ? orow : 0, ook);
+        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, a.lgG, x * IX, IX, ook ? orow : 0, ook);
       }
       if (!gather_staged<BT, 4 * BT>(lact, SA, IX, B, 0, tag(ph + 5), xs, sums)) {
         alive = false;
@@ -1054,7 +1054,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           int row[NRQ], lr[NRQ];
           bool ok[NRQ];
           qkv_rows(row, lr, ok);
-          wrows_load(wq, a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, G, row, ok);
+          wrows_load(wq, a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, a.lgG, row, ok);
         }
         publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, g_next, j, tag(ph + 6), plain);
       } else if (hx) {
