@@ -341,6 +341,7 @@ bool stepx_fits(const kmr_config* c, int B, int nwg) {
   // a residual row starts at a wave boundary or lies within one wave
   if (RPW <= 64 ? 64 % RPW != 0 : RPW % 64 != 0) return false;
   if (4 * GPX * QPG > 8 || QPG != 2) return false;   // split-merge weights in one wave
+  if (GPX & (GPX - 1)) return false;                  // kv heads per XCD: a power of two
   const size_t lds = stepx_lds(4, H, RPW, D, QPG, GPX).total;
   return lds <= 160 * 1024;
 }

@@ -158,11 +158,13 @@ __device__ __forceinline__ void narrow_dot(const WNarrow& w, int KS, int B, cons
 // 0..7 and adds the sum to the owned rows.  Thread i < B*RPW gets element
 // (b, r) = (i / RPW, i % RPW) in xn (has: a row below H).  Returns false, for the
 // whole group, on timeout.
+// RPW is a power of two (checked on the host): row and column by shifts.
+template <int BT>
 __device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag, int B, int H,
                                             int RPW, int row0, float* xown, float* buf, float& xn,
                                             bool& has_x) {
   constexpr int PT = 4;
-  const int tid = otid(), per = B * RPW, words = kXcds * per;
+  const int tid = otid(), per = B * RPW, words = kXcds * per, lgR = __builtin_ctz((unsigned)RPW);
   bool ok = true;
   for (int base = 0; base < words && ok; base += kStepThreads * PT) {
     uint64_t v[PT];
@@ -171,7 +173,7 @@ __device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag,
 #pragma unroll
     for (int q = 0; q < PT; ++q) {
       const int i = base + kStepThreads * q + tid;
-      const int y = i / per, rem = i - y * per, b = rem / RPW, r = rem - b * RPW;
+      const int y = BT == 1 ? i >> lgR : i / per, rem = i - y * per, b = rem >> lgR, r = rem & (RPW - 1);
       has[q] = i < words && row0 + r < H;
       off[q] = has[q] ? (uint32_t)((y * B + b) * H + row0 + r) : 0u;
     }
@@ -198,7 +200,7 @@ __device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag,
   }
   if (group_failed(!ok)) return false;
   // per <= kStepThreads (checked on the host): one element per thread
-  const int b = tid / RPW, r = tid - b * RPW;
+  const int b = tid >> lgR, r = tid & (RPW - 1);
   has_x = tid < per && row0 + r < H;
   xn = 0.f;
   if (has_x) {
@@ -341,8 +343,8 @@ __device__ __forceinline__ float row_inv(const float* s_ss, int B, int nss, int 
 // The norm gain of this thread's column in publish_staged_x, requested early (an
 // in-range address, no use here) so that nothing waits on it before it is needed.
 __device__ __forceinline__ uint16_t staged_gain(const uint16_t* gain, int H, int RPW, int row0) {
-  const int tid = otid(), b = tid / RPW;
-  const int n = row0 + (tid - b * RPW);
+  const int tid = otid();
+  const int n = row0 + (tid & (RPW - 1));   // RPW: a power of two
   return gain[n < H ? n : H - 1];
 }
 
@@ -358,7 +360,7 @@ __device__ __forceinline__ void publish_staged_x(uint64_t* dst, long long stride
                                                  int RPW, int row0, float xn, bool has, uint16_t g,
                                                  int slot, uint32_t tag, int plain) {
   const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = tid / RPW, n = row0 + (tid - b * RPW);
+  const int b = tid >> __builtin_ctz((unsigned)RPW), n = row0 + (tid & (RPW - 1));   // RPW: a power of two
   const float u = has ? xn * bf16_to_f32(g) : 0.f;
   stage_publish(dst + (size_t)(has ? b : 0) * stride, H, n, u, has, tag, plain);
   const int WPR = RPW >= 64 ? RPW >> 6 : 1;
@@ -472,6 +474,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   const int GPX = Hkv / kXcds, QX = GPX * (QPG + 2) * D, OX = GPX * QPG * D, IX = I / kXcds;
   const int RPW = (H + WPX - 1) / WPX, RQ = (QX + WPX - 1) / WPX, RA = (IX + WPX - 1) / WPX;
   const int NSX = (M + kXSplit - 1) / kXSplit;
+  const int lgGPX = __builtin_ctz((unsigned)GPX);   // GPX: a power of two (checked on the host)
   const int NSS = WPX * (RPW >= 64 ? RPW >> 6 : 1);   // sums-of-squares slots of a staged row
   const int plain = a.intra_plain;
   const StepXLds Ld = stepx_lds(BT, H, RPW, D, QPG, GPX);
@@ -843,7 +846,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           for (int q = 0; q < PG; ++q) {
             const int i = base + kStepThreads * q + tid;
             const int seg = i / CW, r1 = i - seg * CW, sl = r1 / PW, k = r1 - sl * PW;
-            hv[q] = i < words && t0 + sl < s_ns[seg / GPX];
+            hv[q] = i < words && t0 + sl < s_ns[seg >> lgGPX];
             off[q] = hv[q] ? (uint32_t)((seg * NSX + t0 + sl) * PW + k) : 0u;
           }
           uint32_t spins = 0;
@@ -875,7 +878,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           // lane = 8 * (seg * QPG + h) + t: split t of the chunk (B * GPX * QPG <= 8, host-checked)
           const int sh = lane >> 3, t = lane & 7, seg = sh / QPG, h = sh - seg * QPG;
           const bool live = seg < B * GPX;
-          const int n = live ? (s_ns[seg / GPX] - t0 < kXMergeChunk ? s_ns[seg / GPX] - t0 : kXMergeChunk) : 0;
+          const int n = live ? (s_ns[seg >> lgGPX] - t0 < kXMergeChunk ? s_ns[seg >> lgGPX] - t0 : kXMergeChunk) : 0;
           const float* pt = xin + ((size_t)seg * kXMergeChunk + t) * PW + h * (D + 2);
           const float mt = t < n ? pt[D] : -INFINITY, lt = t < n ? pt[D + 1] : 0.f;
           float Mc = mt;
@@ -964,7 +967,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     {
       float xn;
       bool hx;
-      if (!reduce_rows(a.pO, tag(ph + 3), B, H, RPW, j * RPW, xown, xin, xn, hx)) {
+      if (!reduce_rows<BT>(a.pO, tag(ph + 3), B, H, RPW, j * RPW, xown, xin, xn, hx)) {
         alive = false;
         break;
       }
@@ -1045,7 +1048,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     {
       float xn;
       bool hx;
-      if (!reduce_rows(a.pD, tag(ph + 6), B, H, RPW, j * RPW, xown, xin, xn, hx)) {
+      if (!reduce_rows<BT>(a.pD, tag(ph + 6), B, H, RPW, j * RPW, xown, xin, xn, hx)) {
         alive = false;
         break;
       }
