@@ -475,6 +475,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   const int RPW = (H + WPX - 1) / WPX, RQ = (QX + WPX - 1) / WPX, RA = (IX + WPX - 1) / WPX;
   const int NSX = (M + kXSplit - 1) / kXSplit;
   const int lgGPX = __builtin_ctz((unsigned)GPX);   // GPX: a power of two (checked on the host)
+  const int lgOX = __builtin_ctz((unsigned)OX);     // OX = GPX * 2 * D: a power of two too
   const int NSS = WPX * (RPW >= 64 ? RPW >> 6 : 1);   // sums-of-squares slots of a staged row
   const int plain = a.intra_plain;
   const StepXLds Ld = stepx_lds(BT, H, RPW, D, QPG, GPX);
@@ -904,7 +905,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         for (int q = 0; q < PTM; ++q) {
           const int idx = kStepThreads * q + tid;
           if (idx >= B * OX) continue;
-          const int b = idx / OX, k = idx - b * OX, gl = k / (QPG * D), hd = k - gl * QPG * D;
+          const int b = idx >> lgOX, k = idx & (OX - 1), gl = k / (QPG * D), hd = k - gl * QPG * D;
           const int h = hd / D, d = hd - h * D, seg = b * GPX + gl;
           const int n = s_ns[b] - t0 < kXMergeChunk ? s_ns[b] - t0 : kXMergeChunk;
           if (n <= 0) continue;
@@ -923,7 +924,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       for (int q = 0; q < PTM; ++q) {
         const int idx = kStepThreads * q + tid;
         has[q] = idx < B * OX;
-        eb[q] = has[q] ? idx / OX : 0;
+        eb[q] = has[q] ? idx >> lgOX : 0;
         ek[q] = idx - eb[q] * OX;
         e[q] = (has[q] && mL[q] > 0.f) ? mO[q] * (1.0f / mL[q]) : 0.f;
       }
