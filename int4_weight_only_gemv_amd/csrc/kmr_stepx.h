@@ -49,6 +49,17 @@ __device__ __forceinline__ void publish_l(uint64_t* p, uint32_t tag, float v, in
     st_dev64(p, w);
 }
 
+// Row b, local kv head gl and split s of attention item `item` (items run row by
+// row, then kv head, then split); s_ns in LDS holds each row's split count.
+__device__ __forceinline__ void xitem(int item, const int* s_ns, int GPX, int& b, int& gl, int& s) {
+  int rem = item;
+  b = 0;
+  while (rem >= GPX * s_ns[b]) { rem -= GPX * s_ns[b]; ++b; }
+  const int ns = s_ns[b];
+  gl = GPX == 1 ? 0 : rem / ns;   // one kv head per XCD: no division
+  s = rem - gl * ns;
+}
+
 // K/V rows of attention item `item` (row b, local kv head, 128-position split):
 // 16-lane row `row` of wave `wave` takes positions s*128 + 4*row + {0..3}, this
 // lane DPL dims of each.  The loads are unconditional (slot clamped into the
@@ -60,9 +71,9 @@ __device__ __forceinline__ void attn_load_kv(uint32_t (&kr)[4][DPL / 2], uint32_
                                              const int* s_ns, const int* s_c, int GPX, int x, int Hkv,
                                              int M, int D, int wave) {
   static_assert(DPL == 4 || DPL == 8, "head_dim 64 or 128");
-  int b = 0, rem = item;
-  while (rem >= GPX * s_ns[b]) { rem -= GPX * s_ns[b]; ++b; }
-  const int ns = s_ns[b], gl = rem / ns, s = rem - gl * ns, g = x * GPX + gl;
+  int b, gl, s;
+  xitem(item, s_ns, GPX, b, gl, s);
+  const int g = x * GPX + gl;
   const int lane = otid() & 63, row = wave * 4 + (lane >> 4), d0 = (lane & 15) * DPL;
   const size_t head_base = ((size_t)b * Hkv + g) * M;
 #pragma unroll
@@ -640,9 +651,9 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     {
       for (int item = j; item < total; item += WPX) {
         if (item != j) attn_load_kv<DPL>(kr, vr, kc, vc, item, s_ns, s_c, GPX, x, Hkv, M, D, wave);
-        int b = 0, rem = item;
-        while (rem >= GPX * s_ns[b]) { rem -= GPX * s_ns[b]; ++b; }
-        const int ns = s_ns[b], gl = rem / ns, s = rem - gl * ns, g = x * GPX + gl, c = s_c[b];
+        int b, gl, s;
+        xitem(item, s_ns, GPX, b, gl, s);
+        const int ns = s_ns[b], g = x * GPX + gl, c = s_c[b];
         const int rr = lane >> 4, li = lane & 15, row = wave * 4 + rr, d0 = li * DPL;
         const size_t head_base = ((size_t)b * Hkv + g) * M;
 
