@@ -404,7 +404,13 @@ template <int BT, int D>
 int launch_stepx_k(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
   const int WPX = nwg / kXcds, RPW = (c->hidden + WPX - 1) / WPX;
   const size_t lds = stepx_lds(BT, c->hidden, RPW, D, 2, c->n_kv_heads / kXcds).total;
-  auto fn = k_stepx<BT, D, 2>;
+  // the constant-size instantiation for the shape it was compiled for
+  auto fn = k_stepx<BT, D, 2, false>;
+  if constexpr (D == 128) {
+    if (c->hidden == kFixH && c->n_kv_heads == kFixHkv && c->n_heads == 2 * kFixHkv &&
+        c->intermediate == kFixI && c->group_size == (1 << kFixLgG) && nwg == kFixNwg)
+      fn = k_stepx<BT, D, 2, true>;
+  }
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lds) != hipSuccess)
     return check_hip("XCD step kernel LDS attribute");

@@ -473,15 +473,21 @@ __host__ __device__ inline StepXSizes stepx_sizes(int B, int H, int Hkv, int D, 
   return z;
 }
 
-template <int BT, int D, int QPG>
+// Sizes of the Qwen3-VL-2B text decoder on a 256-group grid: an instantiation with
+// FIXED set takes them as constants (the host launches it only when they match),
+// so that indices and LDS offsets fold at compile time.
+constexpr int kFixH = 2048, kFixHkv = 8, kFixI = 6144, kFixLgG = 7, kFixNwg = 256;
+
+template <int BT, int D, int QPG, bool FIXED = false>
 __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int DPL = D / 16, HALF = D / 2, PW = QPG * (D + 2);
   const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int wg = blockIdx.x, nwg = FIXED ? kFixNwg : (int)gridDim.x;
   const int x = wg % kXcds, j = wg / kXcds, WPX = nwg / kXcds;
   const int B = BT == 1 ? 1 : a.B;   // (a batch-1 instantiation runs only at B == 1)
-  const int H = a.H, Hq = a.Hq, Hkv = a.Hkv, I = a.I, M = a.M;
+  const int H = FIXED ? kFixH : a.H, Hkv = FIXED ? kFixHkv : a.Hkv, Hq = FIXED ? kFixHkv * QPG : a.Hq;
+  const int I = FIXED ? kFixI : a.I, M = a.M, lgG = FIXED ? kFixLgG : a.lgG;
   const int GPX = Hkv / kXcds, QX = GPX * (QPG + 2) * D, OX = GPX * QPG * D, IX = I / kXcds;
   const int RPW = (H + WPX - 1) / WPX, RQ = (QX + WPX - 1) / WPX, RA = (IX + WPX - 1) / WPX;
   const int NSX = (M + kXSplit - 1) / kXSplit;
@@ -582,7 +588,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     int row[NRQ], lr[NRQ];
     bool ok[NRQ];
     qkv_rows(row, lr, ok);
-    wrows_load(wq, a.layers[0].qkv_p, a.layers[0].qkv_s, H, a.lgG, row, ok);
+    wrows_load(wq, a.layers[0].qkv_p, a.layers[0].qkv_s, H, lgG, row, ok);
   }
 
   for (int l = 0; l < a.L && alive; ++l) {
@@ -602,7 +608,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       bool ok[NR];
       qkv_rows(row, lr, ok);
       if constexpr (!kAhead) {
-        wrows_load(wq, Ly.qkv_p, Ly.qkv_s, H, a.lgG, row, ok);
+        wrows_load(wq, Ly.qkv_p, Ly.qkv_s, H, lgG, row, ok);
         asm volatile("" ::: "memory");   // keep the weight requests ahead of the polls
       }
       if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, NSS, tag(ph), xs, sums)) {
@@ -836,7 +842,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     {
       const int orow = orow_at();
       const bool ook = ook_at(orow);
-      wnarrow_load(wo, Ly.o_p, Ly.o_s, Hq * D, a.lgG, x * OX, OX, ook ? orow : 0, ook);
+      wnarrow_load(wo, Ly.o_p, Ly.o_s, Hq * D, lgG, x * OX, OX, ook ? orow : 0, ook);
     }
     // ================= merge every split of the XCD's heads; o -> staged O input
     {
@@ -974,7 +980,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     uint4* gu_codes = reinterpret_cast<uint4*>(smem + Ld.wgu) + wave * kXGuRows * 64;
     uint32_t* gu_sz = reinterpret_cast<uint32_t*>(smem + Ld.wgu + (size_t)kStepWaves * kXGuRows * 64 * 16) +
                       wave * kXGuRows * 64;
-    wrows_to_lds(Ly.gu_p, Ly.gu_s, H, a.lgG, grow, gu_codes, gu_sz);
+    wrows_to_lds(Ly.gu_p, Ly.gu_s, H, lgG, grow, gu_codes, gu_sz);
     // ================= RS_O: x rows after O, published staged for post_norm
     {
       float xn;
@@ -1000,7 +1006,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       if constexpr (kAhead) {
         const int orow = orow_at();
         const bool ook = ook_at(orow);
-        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, a.lgG, x * IX, IX, ook ? orow : 0, ook);
+        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, lgG, x * IX, IX, ook ? orow : 0, ook);
         g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
       }
       WRows<2 * NP, 1> wgu;
@@ -1038,7 +1044,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
         const int orow = orow_at();
         const bool ook = ook_at(orow);
-        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, a.lgG, x * IX, IX, ook ? orow : 0, ook);
+        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, lgG, x * IX, IX, ook ? orow : 0, ook);
       }
       if (!gather_staged<BT, 4 * BT>(lact, SA, IX, B, 0, tag(ph + 5), xs, sums)) {
         alive = false;
@@ -1069,7 +1075,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           int row[NRQ], lr[NRQ];
           bool ok[NRQ];
           qkv_rows(row, lr, ok);
-          wrows_load(wq, a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, a.lgG, row, ok);
+          wrows_load(wq, a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, lgG, row, ok);
         }
         publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, g_next, j, tag(ph + 6), plain);
       } else if (hx) {
