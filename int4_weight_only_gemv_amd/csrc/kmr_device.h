@@ -105,6 +105,17 @@ __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
                                 false);
 }
 
+// Matrix-core product of a 16 x 32 fp16 tile a with a 32 x 16 fp16 tile b, added to
+// c.  Lane l supplies a[l % 16][8 (l / 16) + e] and b[8 (l / 16) + e][l % 16] as
+// element e of its 8 halves (4 words), and holds c[4 (l / 16) + e][l % 16] as
+// element e of its 4 floats (the gfx950 layout of v_mfma_f32_16x16x32_f16).
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4 a, const uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
+                                                c, 0, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
   half2_t h = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, h);

@@ -451,6 +451,94 @@ __device__ __forceinline__ void wrows_from_lds(WRows<kXGuRows, 1>& w, const uint
   }
 }
 
+// Matrix-core form of the gate/up product, for K = 2048 columns in quantization
+// groups of 128 and 24 act rows per group: the group's 48 weight rows (local row r:
+// gate of act row r for r < 24, up of act row r - 24 after) form three 16-row tiles,
+// and wave w takes all of them over its 256 columns [256 w, 256 w + 256), two
+// groups of four 32-column chunks.  The codes stream into LDS a whole 128-byte line
+// per row and load: load i, lane l takes local row 8 i + l / 8, chunk 8 w + l % 8,
+// into slot i*64 + l.  The scale/zero words of the wave's 96 (row, group) pairs
+// follow in two loads: slot p = 2 r + h holds local row r, group 2 w + h.
+constexpr int kGuMfmaK = 2048, kGuMfmaRows = 24;
+__device__ __forceinline__ void gu_tiles_to_lds(const uint8_t* packed, const uint32_t* sz, int lgG,
+                                                const int (&row)[6], const int (&zrow)[2], uint4* codes,
+                                                uint32_t* szw) {
+  const int lane = otid() & 63, wave = otid() >> 6, NG = kGuMfmaK >> lgG;
+#pragma unroll
+  for (int i = 0; i < kXGuRows; ++i)
+    __builtin_amdgcn_global_load_lds(packed + (size_t)row[i] * (kGuMfmaK / 2) + 16 * (8 * wave + (lane & 7)),
+                                     codes + i * 64, 16, 0, 0);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    __builtin_amdgcn_global_load_lds(sz + (size_t)zrow[u] * NG + ((256 * wave + 128 * (lane & 1)) >> lgG),
+                                     szw + u * 64, 4, 0, 0);
+}
+
+// This wave's part of the 48 gate/up dot products of each staged row b < B, over its
+// 256 columns, into part[(wave * BT + b) * 48 + local row].  Per tile and group the
+// four chunk products go through the matrix cores with the staged rows as the first
+// operand (row b of it; lanes of higher rows repeat row 0) and the weight tile as
+// the second, so lane n < 16 receives every batch row of weight row n.  The group's
+// scale and zero point then apply as in wave_dot_c, s (d - C1) + z C2, with the
+// staged constants of row b summed over the group's four chunks.
+template <int BT>
+__device__ __forceinline__ void gu_mfma_part(const uint4* codes, const uint32_t* szw, const uint4* xs,
+                                             const float* sums, int B, float* part) {
+  constexpr int CH = kGuMfmaK / 32;
+  const int lane = otid() & 63, wave = otid() >> 6, n = lane & 15, gq = lane >> 4;
+  const int bn = (BT > 1 && n < B) ? n : 0;
+  const ChunkSums cs{sums, kGuMfmaK / 4};
+  float acc[3][BT];
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int e = 0; e < BT; ++e) acc[t][e] = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c0 = 8 * wave + 4 * h;
+    uint4 xv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[q] = xs[(bn * 4 + q) * CH + c0 + gq];
+    // group constants of row bn in lane bn, then those of every row, wave-uniform
+    float2 Cl = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const float2 v = cs.get(bn, c0 + cc);
+      Cl.x += v.x;
+      Cl.y += v.y;
+    }
+    float C1[BT], C2[BT];
+#pragma unroll
+    for (int e = 0; e < BT; ++e) {
+      C1[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Cl.x), e));
+      C2[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Cl.y), e));
+    }
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      // weight operand: local row 16 t + n, chunk c0 + gq (load 2 t + n / 8, lane 8 (n % 8) + 4 h + gq)
+      uint32_t p[16];
+      dequant16(codes[(2 * t + (n >> 3)) * 64 + 8 * (n & 7) + 4 * h + gq], p);
+      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        d = mfma16x16x32(xv[kt], make_uint4(p[4 * kt], p[4 * kt + 1], p[4 * kt + 2], p[4 * kt + 3]), d);
+      // lanes n < 16 hold rows b = e of weight row 16 t + n
+      const uint32_t zz = szw[2 * (16 * t + n) + h];
+      const float sc = bf16_lo(zz), zp = bf16_hi(zz);
+#pragma unroll
+      for (int e = 0; e < BT; ++e) acc[t][e] += __builtin_fmaf(sc, d[e] - C1[e], zp * C2[e]);
+    }
+  }
+  if (gq == 0) {
+#pragma unroll
+    for (int e = 0; e < BT; ++e) {
+      if (BT > 1 && e >= B) break;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) part[(wave * BT + e) * 48 + 16 * t + n] = acc[t][e];
+    }
+  }
+}
+
 // XCD-local buffer strides (64-bit words per XCD region, 4 KB aligned), and the
 // per-row strides of the staged vectors.
 struct StepXSizes {
@@ -980,7 +1068,24 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     uint4* gu_codes = reinterpret_cast<uint4*>(smem + Ld.wgu) + wave * kXGuRows * 64;
     uint32_t* gu_sz = reinterpret_cast<uint32_t*>(smem + Ld.wgu + (size_t)kStepWaves * kXGuRows * 64 * 16) +
                       wave * kXGuRows * 64;
-    wrows_to_lds(Ly.gu_p, Ly.gu_s, H, lgG, grow, gu_codes, gu_sz);
+    if constexpr (FIXED) {
+      // matrix-core tiles: local row 16 t + lane % 16 of the group's gate/up rows
+      auto grow_of = [&](int r) {   // weight row of local row r (gate rows, then up rows)
+        const int ar = r < kGuMfmaRows ? r : r - kGuMfmaRows;
+        return x * IX + j * kGuMfmaRows + ar + (r < kGuMfmaRows ? 0 : I);
+      };
+      int trow[kXGuRows], zrow[2];
+#pragma unroll
+      for (int i = 0; i < kXGuRows; ++i) trow[i] = grow_of(8 * i + (lane >> 3));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int p = 64 * u + lane;   // (row, group) pair p < 96; the rest repeat pair 0
+        zrow[u] = grow_of(p < 96 ? p >> 1 : 0);
+      }
+      gu_tiles_to_lds(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, gu_codes, gu_sz);
+    } else {
+      wrows_to_lds(Ly.gu_p, Ly.gu_s, H, lgG, grow, gu_codes, gu_sz);
+    }
     // ================= RS_O: x rows after O, published staged for post_norm
     {
       float xn;
@@ -1001,7 +1106,6 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         break;
       }
       KMR_TRACE_MARK(tev + 7);
-      float out[2 * NP][BT];
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gate/up rows are in LDS
       if constexpr (kAhead) {
         const int orow = orow_at();
@@ -1009,30 +1113,56 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         wnarrow_load(wd, Ly.d_p, Ly.d_s, I, lgG, x * IX, IX, ook ? orow : 0, ook);
         g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
       }
-      WRows<2 * NP, 1> wgu;
-      wrows_from_lds(wgu, gu_codes, gu_sz);
-      wave_dot_c<BT, 2 * NP, 1>(wgu, H, B, xs, ChunkSums{sums, H / 4}, out);
-      const float inv = row_inv<BT>(sums + BT * (H / 4), B, NSS, H, a.eps);
-      // act values of this group into LDS [b][32], then published staged
-      float* s_act = xin;
-      if (lane < B) {
+      if constexpr (FIXED) {
+        // wave partials [8][BT][48] in LDS, then wave b sums batch row b's act rows
+        float* part = xin;
+        gu_mfma_part<BT>(gu_codes, gu_sz, xs, sums, B, part);
+        __syncthreads();
+        if (wave < B) {
+          const float inv = staged_inv(sums + BT * (H / 4), wave, NSS, H, a.eps);
+          const bool has = lane < kGuMfmaRows;
+          float gt = 0.f, up = 0.f;
+          if (has) {
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          float gt = out[i][0], up = out[NP + i][0];
-#pragma unroll
-          for (int b = 1; b < BT; ++b) if (lane == b) { gt = out[i][b]; up = out[NP + i][b]; }
+            for (int w = 0; w < kStepWaves; ++w) {
+              gt += part[(w * BT + wave) * 48 + lane];
+              up += part[(w * BT + wave) * 48 + kGuMfmaRows + lane];
+            }
+          }
           gt *= inv;
           up *= inv;
           // SiLU(gate) * up with the hardware exp and reciprocal (a few ulp)
-          if (gok[i]) s_act[(kAhead ? lane : (otid() & 63)) * 32 + wave * NP + i] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+          const float act = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+          stage_publish(lact + (size_t)wave * SA, IX, j * kGuMfmaRows + lane, has ? act : 0.f, has, tag(ph + 5),
+                        plain);
         }
-      }
-      __syncthreads();
-      {
-        const int b = tid >> 5, t = tid & 31;
-        const bool has = b < B && t < RA && j * RA + t < IX;
-        stage_publish(lact + (size_t)(has ? b : 0) * SA, IX, j * RA + t, has ? s_act[tid] : 0.f, has,
-                      tag(ph + 5), plain);
+      } else {
+        float out[2 * NP][BT];
+        WRows<2 * NP, 1> wgu;
+        wrows_from_lds(wgu, gu_codes, gu_sz);
+        wave_dot_c<BT, 2 * NP, 1>(wgu, H, B, xs, ChunkSums{sums, H / 4}, out);
+        const float inv = row_inv<BT>(sums + BT * (H / 4), B, NSS, H, a.eps);
+        // act values of this group into LDS [b][32], then published staged
+        float* s_act = xin;
+        if (lane < B) {
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            float gt = out[i][0], up = out[NP + i][0];
+#pragma unroll
+            for (int b = 1; b < BT; ++b) if (lane == b) { gt = out[i][b]; up = out[NP + i][b]; }
+            gt *= inv;
+            up *= inv;
+            // SiLU(gate) * up with the hardware exp and reciprocal (a few ulp)
+            if (gok[i]) s_act[(kAhead ? lane : (otid() & 63)) * 32 + wave * NP + i] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+          }
+        }
+        __syncthreads();
+        {
+          const int b = tid >> 5, t = tid & 31;
+          const bool has = b < B && t < RA && j * RA + t < IX;
+          stage_publish(lact + (size_t)(has ? b : 0) * SA, IX, j * RA + t, has ? s_act[tid] : 0.f, has,
+                        tag(ph + 5), plain);
+        }
       }
       // (s_act in xin is next rewritten by the down reduce-scatter, after the
       // barrier of the act gather)
