@@ -116,6 +116,19 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4 a, const uint4 b, f3
                                                 c, 0, 0, 0);
 }
 
+// (a & mask) | bias as one v_and_or_b32.  A three-source VALU instruction takes no
+// 32-bit literal on this architecture, so with literal constants the compiler splits
+// it into v_and_b32 + v_or_b32.  The empty asm statements only hide the constants'
+// values: the mask then lives in a scalar register and the bias in a vector register
+// (both set once, outside the loops that use them), and the compiler still emits
+// and tracks the instruction itself (its wait states before a matrix-core read of
+// the result included).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bias) {
+  asm("" : "+s"(mask));
+  asm("" : "+v"(bias));
+  return (a & mask) | bias;
+}
+
 __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
   half2_t h = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, h);

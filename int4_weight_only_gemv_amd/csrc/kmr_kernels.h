@@ -424,10 +424,10 @@ __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t t = ww[q] >> 8;
-          p[i][4 * q + 0] = (ww[q] & 0x000F000Fu) | 0x64006400u;
-          p[i][4 * q + 1] = (ww[q] & 0x00F000F0u) | 0x64006400u;
-          p[i][4 * q + 2] = (t & 0x000F000Fu) | 0x64006400u;
-          p[i][4 * q + 3] = (t & 0x00F000F0u) | 0x64006400u;
+          p[i][4 * q + 0] = and_or(ww[q], 0x000F000Fu, 0x64006400u);
+          p[i][4 * q + 1] = and_or(ww[q], 0x00F000F0u, 0x64006400u);
+          p[i][4 * q + 2] = and_or(t, 0x000F000Fu, 0x64006400u);
+          p[i][4 * q + 3] = and_or(t, 0x00F000F0u, 0x64006400u);
         }
       }
 #pragma unroll

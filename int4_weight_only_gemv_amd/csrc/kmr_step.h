@@ -371,10 +371,10 @@ __device__ __forceinline__ void dequant16(const uint4 raw, uint32_t (&p)[16]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t t = ww[q] >> 8;
-    p[4 * q + 0] = (ww[q] & 0x000F000Fu) | 0x64006400u;
-    p[4 * q + 1] = (ww[q] & 0x00F000F0u) | 0x64006400u;
-    p[4 * q + 2] = (t & 0x000F000Fu) | 0x64006400u;
-    p[4 * q + 3] = (t & 0x00F000F0u) | 0x64006400u;
+    p[4 * q + 0] = and_or(ww[q], 0x000F000Fu, 0x64006400u);
+    p[4 * q + 1] = and_or(ww[q], 0x00F000F0u, 0x64006400u);
+    p[4 * q + 2] = and_or(t, 0x000F000Fu, 0x64006400u);
+    p[4 * q + 3] = and_or(t, 0x00F000F0u, 0x64006400u);
   }
 }
 
