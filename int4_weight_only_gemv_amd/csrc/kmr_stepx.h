@@ -751,6 +751,14 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         const int rr = lane >> 4, li = lane & 15, row = wave * 4 + rr, d0 = li * DPL;
         const size_t head_base = ((size_t)b * Hkv + g) * M;
 
+        // the q/k norm gains of this wave's head, requested ahead of the poll so that
+        // they are in registers when the q/k/v rows arrive
+        uint16_t gn0 = 0, gn1 = 0;
+        if (wave <= QPG && lane < HALF) {
+          const uint16_t* gn = wave < QPG ? Ly.q_norm : Ly.k_norm;
+          gn0 = gn[lane];
+          gn1 = gn[lane + HALF];
+        }
         // q heads of kv head g (contiguous), then k, then v: one gather
         float* qv = xin;
         {
@@ -775,9 +783,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
             const float ss = wave_sum(x0 * x0 + x1 * x1);
             const float inv = rsqrt_f(ss / (float)D + a.eps);
             if (act) {
-              const uint16_t* gn = wave < QPG ? Ly.q_norm : Ly.k_norm;
-              const float y0 = (x0 * inv) * bf16_to_f32(gn[lane]);
-              const float y1 = (x1 * inv) * bf16_to_f32(gn[lane + HALF]);
+              const float y0 = (x0 * inv) * bf16_to_f32(gn0);
+              const float y1 = (x1 * inv) * bf16_to_f32(gn1);
               const float2 t = cs[b * HALF + lane];
               x0 = y0 * t.x - y1 * t.y;
               x1 = y1 * t.x + y0 * t.y;
