@@ -825,36 +825,58 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
 #pragma unroll
           for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
         }
+        // the row's 4 positions as one block: their scores (log2 units; -inf past
+        // the cache position), then one update of the running max and one rescale
+        // of the state per head, then the 4 weighted value rows
+        float sc[QPG][4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           const int p = s * kXSplit + 4 * row + it;
-          const bool valid = p <= c;
-          float kk[DPL], vv[DPL];
+          float kk[DPL];
           if (p == c) {
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) { kk[e] = kf[e]; vv[e] = vf[e]; }
+            for (int e = 0; e < DPL; ++e) kk[e] = kf[e];
           } else {
 #pragma unroll
-            for (int e = 0; e < DPL / 2; ++e) {
-              kk[2 * e] = bf16_lo(kr[it][e]); kk[2 * e + 1] = bf16_hi(kr[it][e]);
-              vv[2 * e] = bf16_lo(vr[it][e]); vv[2 * e + 1] = bf16_hi(vr[it][e]);
-            }
+            for (int e = 0; e < DPL / 2; ++e) { kk[2 * e] = bf16_lo(kr[it][e]); kk[2 * e + 1] = bf16_hi(kr[it][e]); }
           }
 #pragma unroll
           for (int h = 0; h < QPG; ++h) {
-            float sc = 0.f;
+            float t = 0.f;
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) sc += q[h][e] * kk[e];
-            sc = row16_sum(sc) * a.scale_log2;
-            if (valid) {
-              const float mn = fmaxf(m[h], sc);
-              const float corr = exp2_fast(m[h] - mn);
-              const float pe = exp2_fast(sc - mn);
-              lsum[h] = lsum[h] * corr + pe;
+            for (int e = 0; e < DPL; ++e) t += q[h][e] * kk[e];
+            t = row16_sum(t) * a.scale_log2;
+            sc[h][it] = p <= c ? t : -INFINITY;
+          }
+        }
+        float mb[QPG];
 #pragma unroll
-              for (int e = 0; e < DPL; ++e) o[h][e] = o[h][e] * corr + pe * vv[e];
-              m[h] = mn;
-            }
+        for (int h = 0; h < QPG; ++h) {
+          mb[h] = fmaxf(fmaxf(m[h], fmaxf(sc[h][0], sc[h][1])), fmaxf(sc[h][2], sc[h][3]));
+          // (-inf: no valid position yet, the state stays empty)
+          const float corr = mb[h] != -INFINITY ? exp2_fast(m[h] - mb[h]) : 1.f;
+          lsum[h] *= corr;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) o[h][e] *= corr;
+          m[h] = mb[h];
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int p = s * kXSplit + 4 * row + it;
+          float vv[DPL];
+          if (p == c) {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) vv[e] = vf[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < DPL / 2; ++e) { vv[2 * e] = bf16_lo(vr[it][e]); vv[2 * e + 1] = bf16_hi(vr[it][e]); }
+          }
+#pragma unroll
+          for (int h = 0; h < QPG; ++h) {
+            const float pe = sc[h][it] != -INFINITY ? exp2_fast(sc[h][it] - mb[h]) : 0.f;
+            lsum[h] += pe;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) o[h][e] += pe * vv[e];
           }
         }
         KMR_TRACE_MARK(l == 1 ? 60 : 64);
