@@ -179,8 +179,31 @@ void launch_gemv_cpl(const GemvArgs& a, hipStream_t st) {
   }
 }
 
+// Batch tiles of 9..16 rows go to the matrix cores when the group size and K are
+// multiples of 128 (one scale/zero per 128-column block), K <= 8192 (16 blocks per
+// wave) and the wave partials fit where the staged input was (K >= 256 per
+// 16-row weight tile).  The rule depends on the shapes and the tile size only.
+// (8-row tiles measured slower there than on the VALU: half of each product is
+// padding, and a 16-row block leaves half the CUs idle when N = 2048.)
+template <int BT, int EPI, int PRO>
+void launch_gemv_mfma(const GemvArgs& a, hipStream_t st) {
+  const size_t lds = gemv_lds(BT, a.K, PRO == PRO_ATTN).total;
+  allow_lds(k_gemv_int4_mfma<BT, EPI, PRO>, lds);
+  hipLaunchKernelGGL((k_gemv_int4_mfma<BT, EPI, PRO>), dim3((a.N + 15) / 16), dim3(256), lds, st, a);
+}
+
+inline bool gemv_mfma_fits(const GemvArgs& a, int EPI) {
+  const int nt = EPI == EPI_SILU ? 2 : 1;
+  return a.B >= 9 && a.G % 128 == 0 && a.K % 128 == 0 && a.K <= 4 * kMfmaBlocksPerWave * 128 &&
+         a.K >= 256 * nt;
+}
+
 template <int EPI, int PRO>
 void launch_gemv_tile(const GemvArgs& a, hipStream_t st) {
+  if (gemv_mfma_fits(a, EPI)) {
+    launch_gemv_mfma<16, EPI, PRO>(a, st);
+    return;
+  }
   switch (a.B) {
     case 1: launch_gemv_cpl<1, EPI, PRO>(a, st); break;
     case 2: launch_gemv_cpl<2, EPI, PRO>(a, st); break;

@@ -129,6 +129,20 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b
   return (a & mask) | bias;
 }
 
+// One 16-byte word group of codes -> the fp16 magic-bias pairs of k_gemv_int4
+// (1024 + q for codes in bits 0..3 of a half, 1024 + 16 q for bits 4..7).
+__device__ __forceinline__ void dequant16(const uint4 raw, uint32_t (&p)[16]) {
+  const uint32_t ww[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t t = ww[q] >> 8;
+    p[4 * q + 0] = and_or(ww[q], 0x000F000Fu, 0x64006400u);
+    p[4 * q + 1] = and_or(ww[q], 0x00F000F0u, 0x64006400u);
+    p[4 * q + 2] = and_or(t, 0x000F000Fu, 0x64006400u);
+    p[4 * q + 3] = and_or(t, 0x00F000F0u, 0x64006400u);
+  }
+}
+
 __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
   half2_t h = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, h);

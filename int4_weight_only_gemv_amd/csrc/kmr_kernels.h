@@ -283,10 +283,14 @@ __host__ __device__ inline GemvLds gemv_lds(int BT, int K, bool merged_input) {
   return l;
 }
 
-template <int BT, int EPI, int PRO, int CPL>
-__global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int K = a.K, CH = K >> 5, NG = K / a.G, B = a.B;
+// Stages the B <= BT input rows of a GEMV in LDS after its prologue (plain input,
+// RMSNorm of it, or the attention merge): the fp16 magic-bias pairs xs [BT][4][CH]
+// (h[8w+i], h[8w+i+4]) with odd columns divided by 16, and the per-chunk constants
+// cc [BT][CH] = (1024 sum h + 8 sum u, sum u).  Rows b >= B are zero.  Every
+// thread of the block must call this; the data is in LDS for all on return.
+template <int BT, int PRO>
+__device__ __forceinline__ void gemv_stage(const GemvArgs& a, unsigned char* smem) {
+  const int K = a.K, CH = K >> 5, B = a.B;
   const GemvLds lay = gemv_lds(BT, K, PRO == PRO_ATTN);
   uint4* xs = reinterpret_cast<uint4*>(smem + lay.xs);            // [BT][4][CH]
   float2* cc = reinterpret_cast<float2*>(smem + lay.cc);          // [BT][CH]
@@ -294,40 +298,6 @@ __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
   float* red = reinterpret_cast<float*>(smem + lay.red);          // [BT][4]
   float* sinv = red + BT * 4;                                     // [BT]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  constexpr int RPW = kGemvRowsPerWave;
-  constexpr int NR = (EPI == EPI_SILU ? 2 : 1) * RPW;
-  const int n0 = (blockIdx.x * 4 + wave) * RPW;
-  int wrow[NR];
-  bool ok[NR];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int n = n0 + r;
-    ok[r] = n < a.N;
-    wrow[r] = ok[r] ? n : 0;
-    if (EPI == EPI_SILU) {
-      ok[RPW + r] = ok[r];
-      wrow[RPW + r] = ok[r] ? n + a.N : 0;
-    }
-  }
-  // ---- weight stream first
-  uint4 w[NR][CPL];
-  uint32_t sw[NR][CPL];
-#pragma unroll
-  for (int i = 0; i < NR; ++i)
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      if (ok[i] && c < CH) {
-        w[i][j] = load_stream16(a.packed + (size_t)wrow[i] * (K / 2) + 16 * c);
-        sw[i][j] = a.sz[(size_t)wrow[i] * NG + (32 * c) / a.G];
-      } else {
-        w[i][j] = make_uint4(0, 0, 0, 0);
-        sw[i][j] = 0;
-      }
-    }
-
-  // ---- prologue: input staging
   if (PRO == PRO_ATTN) {
     for (int idx = tid; idx < BT * (K / 4); idx += 256) {
       const int b = idx / (K / 4), k4 = 4 * (idx - b * (K / 4));
@@ -407,6 +377,52 @@ __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
   }
   __syncthreads();
 
+}
+
+template <int BT, int EPI, int PRO, int CPL>
+__global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int K = a.K, CH = K >> 5, NG = K / a.G, B = a.B;
+  const GemvLds lay = gemv_lds(BT, K, PRO == PRO_ATTN);
+  uint4* xs = reinterpret_cast<uint4*>(smem + lay.xs);            // [BT][4][CH]
+  float2* cc = reinterpret_cast<float2*>(smem + lay.cc);          // [BT][CH]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  constexpr int RPW = kGemvRowsPerWave;
+  constexpr int NR = (EPI == EPI_SILU ? 2 : 1) * RPW;
+  const int n0 = (blockIdx.x * 4 + wave) * RPW;
+  int wrow[NR];
+  bool ok[NR];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int n = n0 + r;
+    ok[r] = n < a.N;
+    wrow[r] = ok[r] ? n : 0;
+    if (EPI == EPI_SILU) {
+      ok[RPW + r] = ok[r];
+      wrow[RPW + r] = ok[r] ? n + a.N : 0;
+    }
+  }
+  // ---- weight stream first
+  uint4 w[NR][CPL];
+  uint32_t sw[NR][CPL];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (ok[i] && c < CH) {
+        w[i][j] = load_stream16(a.packed + (size_t)wrow[i] * (K / 2) + 16 * c);
+        sw[i][j] = a.sz[(size_t)wrow[i] * NG + (32 * c) / a.G];
+      } else {
+        w[i][j] = make_uint4(0, 0, 0, 0);
+        sw[i][j] = 0;
+      }
+    }
+
+  // ---- prologue: input staging
+  gemv_stage<BT, PRO>(a, smem);
+
   // ---- dequantize and multiply
   float acc[NR][BT];
 #pragma unroll
@@ -475,6 +491,122 @@ __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
           const float g = v[r][b], u = v[RPW + r][b];
           *dst = g / (1.0f + expf(-g)) * u;
         }
+      }
+    }
+  }
+}
+
+// Batch tiles of up to BT = 16 rows on the matrix cores (group size a multiple of
+// 128).  A block takes 16 weight rows (EPI_SILU: 16 gate rows and their 16 up
+// rows) and its 4 waves split K by 128-column blocks (wave w: blocks w, w + 4, ...).
+// Per block, lane (n, gq) = (lane % 16, lane / 16) holds the codes of weight row n
+// over chunk 4 kb + gq and the staged batch row n over the same chunk; four
+// v_mfma_f32_16x16x32_f16 with the staged rows as the first operand leave in lane
+// (n, gq) the dots of batch rows 4 gq + e with weight row n, and the block's scale
+// and zero point apply as s (d - C1) + z C2 with the staged constants summed over
+// its four chunks (the same algebra as k_gemv_int4, per 128 columns instead of 32).
+// Wave partials are summed through LDS in wave order before the epilogue.
+constexpr int kMfmaBlocksPerWave = 16;   // K <= 4 * 16 * 128 = 8192
+template <int BT, int EPI, int PRO>
+__global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
+  static_assert(BT == 16, "one 16-row operand of batch rows");
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NT = EPI == EPI_SILU ? 2 : 1;   // 16-row weight tiles per block
+  const int K = a.K, CH = K >> 5, NG = K / a.G, NB = K >> 7, B = a.B;
+  const GemvLds lay = gemv_lds(BT, K, PRO == PRO_ATTN);
+  const uint4* xs = reinterpret_cast<const uint4*>(smem + lay.xs);     // [BT][4][CH]
+  const float2* cc = reinterpret_cast<const float2*>(smem + lay.cc);   // [BT][CH]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, gq = lane >> 4;
+  const int r0 = blockIdx.x * 16;
+  const bool rok = r0 + n < a.N;
+  const int nbw = NB > wave ? (NB - wave + 3) >> 2 : 0;   // this wave's 128-column blocks
+
+  // ---- weight stream first (in flight while the input is staged)
+  uint4 w[NT][kMfmaBlocksPerWave];
+  uint32_t sw[NT][kMfmaBlocksPerWave];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int row = rok ? r0 + n + t * a.N : 0;
+#pragma unroll
+    for (int i = 0; i < kMfmaBlocksPerWave; ++i) {
+      const int kb = wave + 4 * i;
+      if (i < nbw && rok) {
+        w[t][i] = load_stream16(a.packed + (size_t)row * (K / 2) + 16 * (4 * kb + gq));
+        sw[t][i] = a.sz[(size_t)row * NG + ((kb << 7) / a.G)];
+      } else {
+        w[t][i] = make_uint4(0, 0, 0, 0);
+        sw[t][i] = 0;
+      }
+    }
+  }
+  gemv_stage<BT, PRO>(a, smem);
+
+  // ---- dequantize and multiply
+  const int bn = n < B ? n : 0;   // staged row of this lane's operand (padding repeats row 0)
+  float acc[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[t][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMfmaBlocksPerWave; ++i) {
+    if (i >= nbw) break;
+    const int kb = wave + 4 * i, c = 4 * kb + gq;
+    uint4 xv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[q] = xs[(bn * 4 + q) * CH + c];
+    // the block's constants of batch rows 4 gq + e
+    float C1[4], C2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int b = 4 * gq + e < BT ? 4 * gq + e : 0;
+      const float2* cp = cc + b * CH + 4 * kb;
+      const float2 c0 = cp[0], c1 = cp[1], c2 = cp[2], c3 = cp[3];
+      C1[e] = (c0.x + c1.x) + (c2.x + c3.x);
+      C2[e] = (c0.y + c1.y) + (c2.y + c3.y);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint32_t p[16];
+      dequant16(w[t][i], p);
+      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        d = mfma16x16x32(xv[kt], make_uint4(p[4 * kt], p[4 * kt + 1], p[4 * kt + 2], p[4 * kt + 3]), d);
+      const float sc = bf16_lo(sw[t][i]), zp = bf16_hi(sw[t][i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][e] += __builtin_fmaf(sc, d[e] - C1[e], zp * C2[e]);
+    }
+  }
+
+  // ---- wave partials -> LDS [4 waves][NT][16 batch rows][16 weight rows], then the epilogue
+  __syncthreads();   // the staged input is no longer read: its space takes the partials
+  float* part = reinterpret_cast<float*>(smem + lay.xs);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * gq + e < BT) part[((wave * NT + t) * 16 + 4 * gq + e) * 16 + n] = acc[t][e];
+  __syncthreads();
+  {
+    const int b = tid >> 4, r = tid & 15, nr = r0 + r;
+    if (b < B && nr < a.N) {
+      float v[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float s = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) s += part[((wv * NT + t) * 16 + b) * 16 + r];
+        v[t] = s;
+      }
+      float* dst = a.y + (size_t)b * a.ldy + nr;
+      if (EPI == EPI_STORE) {
+        *dst = v[0];
+      } else if (EPI == EPI_ADD) {
+        *dst += v[0];
+      } else {
+        const float g = v[0], u = v[NT - 1];
+        *dst = g / (1.0f + expf(-g)) * u;
       }
     }
   }

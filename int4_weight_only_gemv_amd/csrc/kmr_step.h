@@ -364,20 +364,6 @@ __device__ __forceinline__ void wrows_load(WRows<NR, CPL>& w, const uint8_t* pac
     }
 }
 
-// One 16-byte word group of codes -> the fp16 magic-bias pairs of k_gemv_int4
-// (1024 + q for codes in bits 0..3 of a half, 1024 + 16 q for bits 4..7).
-__device__ __forceinline__ void dequant16(const uint4 raw, uint32_t (&p)[16]) {
-  const uint32_t ww[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t t = ww[q] >> 8;
-    p[4 * q + 0] = and_or(ww[q], 0x000F000Fu, 0x64006400u);
-    p[4 * q + 1] = and_or(ww[q], 0x00F000F0u, 0x64006400u);
-    p[4 * q + 2] = and_or(t, 0x000F000Fu, 0x64006400u);
-    p[4 * q + 3] = and_or(t, 0x00F000F0u, 0x64006400u);
-  }
-}
-
 // Per-chunk constants (C1, C2) = (1024 sum(h) + 8 sum(u), sum(u)) of a staged input
 // row, from a precomputed array ...
 struct ChunkCC {

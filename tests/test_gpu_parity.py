@@ -125,6 +125,21 @@ def test_decode_layer_full_size_edges(kmr):
     _layer_case(kmr, w.dims, synth.base_seed(w), 4, w.max_len, cpos, pos, x0)
 
 
+@pytest.mark.parametrize("batch", [11, 16])
+def test_decode_layer_full_size_matrix_core_tiles(kmr, batch):
+    """Batch tiles of 9..16 rows with group 128 take the matrix-core GEMV (the QKV and
+    gate-up products; O and down run in 8-row tiles on the VALU): a padded tile
+    (B = 11, with an 8 + 3-row split of the others) and a full one (B = 16)."""
+    w = synth.WORKLOADS["layer"]
+    log(f"decode_layer full size, batch {batch} (matrix-core GEMV tiles)")
+    rng = np.random.default_rng(500 + batch)
+    cpos = rng.integers(0, w.max_len, batch).astype(np.int32)
+    cpos[0], cpos[-1] = 0, w.max_len - 1
+    pos = np.stack([cpos, cpos // 2, cpos // 3]).astype(np.int32)
+    x0 = synth.hidden_input(w.dims, 40 + batch, batch).numpy()
+    _layer_case(kmr, w.dims, synth.base_seed(w), batch, w.max_len, cpos, pos, x0)
+
+
 # ------------------------------------------------------------------ whole step
 
 def _check_step(got_next, got_logits, ref, label):
