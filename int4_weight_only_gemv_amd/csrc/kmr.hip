@@ -246,7 +246,10 @@ template <int BT, int CPL>
 void launch_lm_k(const LmArgs& a, hipStream_t st) {
   const size_t lds = (size_t)a.K * 4 * BT;
   allow_lds(k_lmhead<BT, CPL>, lds);
-  hipLaunchKernelGGL((k_lmhead<BT, CPL>), dim3(a.nblk), dim3(256), lds, st, a);
+  // at most 4 groups per CU of 256: each normalizes the input once and loops over
+  // row blocks (the normalization re-done per 16-row block dominated at B = 16)
+  const int grid = a.nblk < 1024 ? a.nblk : 1024;
+  hipLaunchKernelGGL((k_lmhead<BT, CPL>), dim3(grid), dim3(256), lds, st, a);
 }
 
 template <int BT>

@@ -834,19 +834,9 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
   const int K = a.K, B = a.B, CH = K >> 3;   // 8-column chunks
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int RPW = kLmRowsPerWave;
-  const int n0 = blockIdx.x * kLmRowsPerBlock + wave * RPW;
 
-  uint4 w[RPW][CPL];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int n = n0 + r, c = lane + 64 * j;
-      w[r][j] = (n < a.V && c < CH)
-                    ? load_stream16(a.W + (size_t)n * K + 8 * c)
-                    : make_uint4(0, 0, 0, 0);
-    }
-
+  // h = RMSNorm(x; gain) into LDS once per group; the group then takes row blocks
+  // blockIdx.x, blockIdx.x + gridDim.x, ... (one argmax partial per row block)
 #pragma unroll
   for (int b = 0; b < BT; ++b) {
     float ss = 0.f;
@@ -868,58 +858,72 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
   }
   __syncthreads();
 
-  float acc[RPW][BT];
+  for (int blk = blockIdx.x; blk < a.nblk; blk += gridDim.x) {
+    const int n0 = blk * kLmRowsPerBlock + wave * RPW;
+    uint4 w[RPW][CPL];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r)
+    for (int r = 0; r < RPW; ++r)
 #pragma unroll
-    for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
+      for (int j = 0; j < CPL; ++j) {
+        const int n = n0 + r, c = lane + 64 * j;
+        w[r][j] = (n < a.V && c < CH)
+                      ? load_stream16(a.W + (size_t)n * K + 8 * c)
+                      : make_uint4(0, 0, 0, 0);
+      }
+    float acc[RPW][BT];
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = lane + 64 * j;
-    if (c < CH) {
+    for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int b = 0; b < BT; ++b) {
-        const float4 h0 = *reinterpret_cast<const float4*>(hs + b * K + 8 * c);
-        const float4 h1 = *reinterpret_cast<const float4*>(hs + b * K + 8 * c + 4);
+      for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          float t = acc[r][b];
-          t += bf16_lo(w[r][j].x) * h0.x; t += bf16_hi(w[r][j].x) * h0.y;
-          t += bf16_lo(w[r][j].y) * h0.z; t += bf16_hi(w[r][j].y) * h0.w;
-          t += bf16_lo(w[r][j].z) * h1.x; t += bf16_hi(w[r][j].z) * h1.y;
-          t += bf16_lo(w[r][j].w) * h1.z; t += bf16_hi(w[r][j].w) * h1.w;
-          acc[r][b] = t;
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (c < CH) {
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          const float4 h0 = *reinterpret_cast<const float4*>(hs + b * K + 8 * c);
+          const float4 h1 = *reinterpret_cast<const float4*>(hs + b * K + 8 * c + 4);
+#pragma unroll
+          for (int r = 0; r < RPW; ++r) {
+            float t = acc[r][b];
+            t += bf16_lo(w[r][j].x) * h0.x; t += bf16_hi(w[r][j].x) * h0.y;
+            t += bf16_lo(w[r][j].y) * h0.z; t += bf16_hi(w[r][j].y) * h0.w;
+            t += bf16_lo(w[r][j].z) * h1.x; t += bf16_hi(w[r][j].z) * h1.y;
+            t += bf16_lo(w[r][j].w) * h1.z; t += bf16_hi(w[r][j].w) * h1.w;
+            acc[r][b] = t;
+          }
         }
       }
     }
-  }
-  float bv[BT];
-  int bi[BT];
+    float bv[BT];
+    int bi[BT];
 #pragma unroll
-  for (int b = 0; b < BT; ++b) { bv[b] = -INFINITY; bi[b] = 0x7fffffff; }
+    for (int b = 0; b < BT; ++b) { bv[b] = -INFINITY; bi[b] = 0x7fffffff; }
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int n = n0 + r;
+    for (int r = 0; r < RPW; ++r) {
+      const int n = n0 + r;
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      const float v = wave_sum(acc[r][b]);
-      if (n < a.V && b < B) {
-        if (a.logits && lane == 0) a.logits[(size_t)b * a.V + n] = v;
-        if (better(v, n, bv[b], bi[b])) { bv[b] = v; bi[b] = n; }
+      for (int b = 0; b < BT; ++b) {
+        const float v = wave_sum(acc[r][b]);
+        if (n < a.V && b < B) {
+          if (a.logits && lane == 0) a.logits[(size_t)b * a.V + n] = v;
+          if (better(v, n, bv[b], bi[b])) { bv[b] = v; bi[b] = n; }
+        }
       }
     }
-  }
-  if (lane == 0) {
+    if (lane == 0) {
 #pragma unroll
-    for (int b = 0; b < BT; ++b) { s_bv[wave][b] = bv[b]; s_bi[wave][b] = bi[b]; }
-  }
-  __syncthreads();
-  if (tid < B) {
-    float v = s_bv[0][tid];
-    int i = s_bi[0][tid];
-    for (int w2 = 1; w2 < 4; ++w2)
-      if (better(s_bv[w2][tid], s_bi[w2][tid], v, i)) { v = s_bv[w2][tid]; i = s_bi[w2][tid]; }
-    a.part[(size_t)tid * a.nblk + blockIdx.x] = make_float2(v, __int_as_float(i));
+      for (int b = 0; b < BT; ++b) { s_bv[wave][b] = bv[b]; s_bi[wave][b] = bi[b]; }
+    }
+    __syncthreads();
+    if (tid < B) {
+      float v = s_bv[0][tid];
+      int i = s_bi[0][tid];
+      for (int w2 = 1; w2 < 4; ++w2)
+        if (better(s_bv[w2][tid], s_bi[w2][tid], v, i)) { v = s_bv[w2][tid]; i = s_bi[w2][tid]; }
+      a.part[(size_t)tid * a.nblk + blk] = make_float2(v, __int_as_float(i));
+    }
+    __syncthreads();   // s_bv / s_bi are rewritten by the next row block
   }
 }
 
