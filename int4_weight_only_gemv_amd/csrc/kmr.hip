@@ -75,6 +75,7 @@ struct WsLayout {
   size_t status, cs, x, qkv, attn_o, act, part_o, part_ml, lm_part, total;
   size_t step_ctr, lm_cnt, tx, tqkv, to, tact, tpart, lm_part2;
   size_t lx, sx, lqkv, lpart, lact, pO, pD, probe;
+  size_t xst, xst_cc;   // staged input of a 16-row GEMV tile: [16][4][Kmax/32] x 16 B, [16][Kmax/32] x 8 B
   StepXSizes xz;
   int ns, nblk_lm;
 };
@@ -103,6 +104,12 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
   w.tact = o; o += align256((size_t)B * c->intermediate * 8);
   w.tpart = o; o += align256((size_t)B * Hkv * w.ns * qpg * (D + 2) * 8);
   w.lm_part2 = o; o += align256((size_t)B * kMaxStepGroups * 8);
+  {
+    int kmax = c->hidden > Hq * D ? c->hidden : Hq * D;
+    kmax = kmax > c->intermediate ? kmax : c->intermediate;
+    w.xst = o; o += align256((size_t)16 * 4 * (kmax / 32) * 16);
+    w.xst_cc = o; o += align256((size_t)16 * (kmax / 32) * 8);
+  }
   // XCD-local step kernel: per-XCD regions, then the device-wide partials
   o = (o + 4095) & ~(size_t)4095;
   w.xz = stepx_sizes(B, c->hidden, Hkv, D, qpg, c->intermediate, M);
@@ -180,28 +187,36 @@ void launch_gemv_cpl(const GemvArgs& a, hipStream_t st) {
 }
 
 // Batch tiles of 9..16 rows go to the matrix cores when the group size and K are
-// multiples of 128 (one scale/zero per 128-column block), K <= 8192 (16 blocks per
-// wave) and the wave partials fit where the staged input was (K >= 256 per
+// multiples of 128 (one scale/zero per 128-column block) and K <= 8192 (16 blocks
+// per wave).  With a staging buffer (plain or RMSNorm input) the tile's input is
+// staged once by k_gemv_stage16 and every group reads it from memory; otherwise each
+// group stages it in LDS, where the wave partials must then fit (K >= 256 per
 // 16-row weight tile).  The rule depends on the shapes and the tile size only.
 // (8-row tiles measured slower there than on the VALU: half of each product is
 // padding, and a 16-row block leaves half the CUs idle when N = 2048.)
-template <int BT, int EPI, int PRO>
-void launch_gemv_mfma(const GemvArgs& a, hipStream_t st) {
-  const size_t lds = gemv_lds(BT, a.K, PRO == PRO_ATTN).total;
-  allow_lds(k_gemv_int4_mfma<BT, EPI, PRO>, lds);
-  hipLaunchKernelGGL((k_gemv_int4_mfma<BT, EPI, PRO>), dim3((a.N + 15) / 16), dim3(256), lds, st, a);
+template <int EPI, int PRO>
+inline bool gemv_mfma_shape(const GemvArgs& a) {
+  return a.G % 128 == 0 && a.K % 128 == 0 && a.K <= 4 * kMfmaBlocksPerWave * 128;
 }
-
-inline bool gemv_mfma_fits(const GemvArgs& a, int EPI) {
-  const int nt = EPI == EPI_SILU ? 2 : 1;
-  return a.B >= 9 && a.G % 128 == 0 && a.K % 128 == 0 && a.K <= 4 * kMfmaBlocksPerWave * 128 &&
-         a.K >= 256 * nt;
+template <int EPI, int PRO>
+inline bool gemv_mfma_staged(const GemvArgs& a) {
+  return PRO != PRO_ATTN && a.xsg && a.ccg && gemv_mfma_shape<EPI, PRO>(a);
 }
 
 template <int EPI, int PRO>
 void launch_gemv_tile(const GemvArgs& a, hipStream_t st) {
-  if (gemv_mfma_fits(a, EPI)) {
-    launch_gemv_mfma<16, EPI, PRO>(a, st);
+  if (a.B >= 9 && gemv_mfma_staged<EPI, PRO>(a)) {
+    if constexpr (PRO != PRO_ATTN) {
+      hipLaunchKernelGGL((k_gemv_stage16<PRO>), dim3(16), dim3(256), 0, st, a);
+      const size_t lds = (size_t)4 * (EPI == EPI_SILU ? 2 : 1) * 256 * 4;   // wave partials
+      hipLaunchKernelGGL((k_gemv_int4_mfma<16, EPI, PRO, true>), dim3((a.N + 15) / 16), dim3(256), lds, st, a);
+    }
+    return;
+  }
+  if (a.B >= 9 && gemv_mfma_shape<EPI, PRO>(a) && a.K >= 256 * (EPI == EPI_SILU ? 2 : 1)) {
+    const size_t lds = gemv_lds(16, a.K, PRO == PRO_ATTN).total;
+    allow_lds(k_gemv_int4_mfma<16, EPI, PRO, false>, lds);
+    hipLaunchKernelGGL((k_gemv_int4_mfma<16, EPI, PRO, false>), dim3((a.N + 15) / 16), dim3(256), lds, st, a);
     return;
   }
   switch (a.B) {
@@ -219,7 +234,8 @@ void launch_gemv(GemvArgs a, hipStream_t st) {
   const int B = a.B;
   int tile = 16;
   const size_t per_row = (size_t)a.K * 9 / 4 + (PRO == PRO_ATTN ? (size_t)a.K * 4 : 0);
-  while (tile > 1 && tile * per_row + 1024 > 150 * 1024) tile >>= 1;
+  if (!(B >= 9 && gemv_mfma_staged<EPI, PRO>(a)))   // (staged in memory: no LDS bound)
+    while (tile > 1 && tile * per_row + 1024 > 150 * 1024) tile >>= 1;
   for (int b0 = 0; b0 < B; b0 += tile) {
     GemvArgs t = a;
     t.B = B - b0 < tile ? B - b0 : tile;
@@ -285,7 +301,10 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   float* ao = at<float>(ws, w.attn_o);
   float* act = at<float>(ws, w.act);
 
+  uint4* xsg = at<uint4>(ws, w.xst);
+  float2* ccg = at<float2>(ws, w.xst_cc);
   GemvArgs g{};
+  g.xsg = xsg; g.ccg = ccg;
   g.packed = static_cast<const uint8_t*>(L->qkv.packed);
   g.sz = static_cast<const uint32_t*>(L->qkv.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->in_norm); g.eps = c->rms_eps;
@@ -312,6 +331,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   ap.Hkv = Hkv; ap.NS = w.ns; ap.QPG = Hq / Hkv; ap.D = D; ap.M = kv->max_len;
 
   g = GemvArgs{};
+  g.xsg = xsg; g.ccg = ccg;
   g.packed = static_cast<const uint8_t*>(L->o.packed);
   g.sz = static_cast<const uint32_t*>(L->o.sz);
   g.y = x; g.ldy = H; g.N = H; g.K = Hq * D; g.G = G; g.B = B;
@@ -326,6 +346,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   }
 
   g = GemvArgs{};
+  g.xsg = xsg; g.ccg = ccg;
   g.packed = static_cast<const uint8_t*>(L->gate_up.packed);
   g.sz = static_cast<const uint32_t*>(L->gate_up.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->post_norm); g.eps = c->rms_eps;
@@ -333,6 +354,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   launch_gemv<EPI_SILU, PRO_RMSNORM>(g, st);
 
   g = GemvArgs{};
+  g.xsg = xsg; g.ccg = ccg;
   g.packed = static_cast<const uint8_t*>(L->down.packed);
   g.sz = static_cast<const uint32_t*>(L->down.sz);
   g.x = act; g.ldx = I; g.gain = nullptr;

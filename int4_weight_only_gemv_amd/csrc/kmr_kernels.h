@@ -264,6 +264,8 @@ struct GemvArgs {
   float eps;
   AttnPart ap;            // PRO_ATTN; ap.cpos is indexed from batch row b0
   int b0;                 // first batch row of this tile (PRO_ATTN)
+  uint4* xsg;             // staged input of a 16-row tile in memory: [16][4][K/32] ...
+  float2* ccg;            // ... and its chunk constants [16][K/32] (k_gemv_stage16)
 };
 
 // LDS layout of k_gemv_int4 (byte offsets, 16-byte aligned).
@@ -281,6 +283,31 @@ __host__ __device__ inline GemvLds gemv_lds(int BT, int K, bool merged_input) {
   l.red = take((size_t)BT * 5 * 4);
   l.total = o;
   return l;
+}
+
+// One 32-column chunk e of a staged GEMV input: its four 16-byte words of fp16
+// magic-bias pairs (h[8j+i], h[8j+i+4]), odd columns divided by 16, to dst[j * CH]
+// for j < 4, and the chunk constants (1024 sum h + 8 sum u, sum u) returned.
+__device__ __forceinline__ float2 stage_chunk(const float (&e)[32], uint4* dst, int CH) {
+  float bsum = 0.f, usum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float* f = e + 8 * j;
+    _Float16 h0 = (_Float16)f[0], h4 = (_Float16)f[4], h2 = (_Float16)f[2], h6 = (_Float16)f[6];
+    _Float16 h1 = (_Float16)(f[1] * 0.0625f), h5 = (_Float16)(f[5] * 0.0625f);
+    _Float16 h3 = (_Float16)(f[3] * 0.0625f), h7 = (_Float16)(f[7] * 0.0625f);
+    uint4 pk;
+    pk.x = __builtin_bit_cast(uint32_t, half2_t{h0, h4});
+    pk.y = __builtin_bit_cast(uint32_t, half2_t{h1, h5});
+    pk.z = __builtin_bit_cast(uint32_t, half2_t{h2, h6});
+    pk.w = __builtin_bit_cast(uint32_t, half2_t{h3, h7});
+    dst[j * CH] = pk;
+    const float ev = ((float)h0 + (float)h4) + ((float)h2 + (float)h6);
+    const float od = ((float)h1 + (float)h5) + ((float)h3 + (float)h7);
+    bsum += ev + od;
+    usum += ev + 16.0f * od;
+  }
+  return make_float2(1024.0f * bsum + 8.0f * usum, usum);
 }
 
 // Stages the B <= BT input rows of a GEMV in LDS after its prologue (plain input,
@@ -355,25 +382,7 @@ __device__ __forceinline__ void gemv_stage(const GemvArgs& a, unsigned char* sme
 #pragma unroll
       for (int i = 0; i < 32; ++i) e[i] = 0.f;
     }
-    float bsum = 0.f, usum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float* f = e + 8 * j;
-      _Float16 h0 = (_Float16)f[0], h4 = (_Float16)f[4], h2 = (_Float16)f[2], h6 = (_Float16)f[6];
-      _Float16 h1 = (_Float16)(f[1] * 0.0625f), h5 = (_Float16)(f[5] * 0.0625f);
-      _Float16 h3 = (_Float16)(f[3] * 0.0625f), h7 = (_Float16)(f[7] * 0.0625f);
-      uint4 pk;
-      pk.x = __builtin_bit_cast(uint32_t, half2_t{h0, h4});
-      pk.y = __builtin_bit_cast(uint32_t, half2_t{h1, h5});
-      pk.z = __builtin_bit_cast(uint32_t, half2_t{h2, h6});
-      pk.w = __builtin_bit_cast(uint32_t, half2_t{h3, h7});
-      xs[(b * 4 + j) * CH + c] = pk;
-      const float ev = ((float)h0 + (float)h4) + ((float)h2 + (float)h6);
-      const float od = ((float)h1 + (float)h5) + ((float)h3 + (float)h7);
-      bsum += ev + od;
-      usum += ev + 16.0f * od;
-    }
-    cc[b * CH + c] = make_float2(1024.0f * bsum + 8.0f * usum, usum);
+    cc[b * CH + c] = stage_chunk(e, xs + b * 4 * CH + c, CH);
   }
   __syncthreads();
 
@@ -496,6 +505,55 @@ __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
   }
 }
 
+// The staged input of a 16-row batch tile written once to memory (a.xsg, a.ccg), in
+// the layout gemv_stage gives LDS, for k_gemv_int4_mfma with GS set: one group per
+// batch row (rows b >= B are zero), plain input or its RMSNorm.
+template <int PRO>
+__global__ __launch_bounds__(256) void k_gemv_stage16(GemvArgs a) {
+  static_assert(PRO == PRO_PLAIN || PRO == PRO_RMSNORM, "plain or RMSNorm input");
+  __shared__ float red[4];
+  const int b = blockIdx.x, K = a.K, CH = K >> 5, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool live = b < a.B;
+  const float* xr = a.x + (size_t)(live ? b : 0) * a.ldx;
+  float iv = 1.f;
+  if (PRO == PRO_RMSNORM) {
+    float ss = 0.f;
+    if (live)
+      for (int k = tid * 4; k < K; k += 1024) {
+        const float4 v = *reinterpret_cast<const float4*>(xr + k);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    iv = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)K + a.eps);
+  }
+  for (int c = tid; c < CH; c += 256) {
+    float e[32];
+    if (live) {
+      const float4* src = reinterpret_cast<const float4*>(xr + 32 * c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 v = src[i];
+        e[4 * i] = v.x; e[4 * i + 1] = v.y; e[4 * i + 2] = v.z; e[4 * i + 3] = v.w;
+      }
+      if (PRO == PRO_RMSNORM) {
+        const uint32_t* gw = reinterpret_cast<const uint32_t*>(a.gain + 32 * c);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t gg = gw[i];
+          e[2 * i] = (e[2 * i] * iv) * bf16_lo(gg);
+          e[2 * i + 1] = (e[2 * i + 1] * iv) * bf16_hi(gg);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) e[i] = 0.f;
+    }
+    a.ccg[b * CH + c] = stage_chunk(e, a.xsg + b * 4 * CH + c, CH);
+  }
+}
+
 // Batch tiles of up to BT = 16 rows on the matrix cores (group size a multiple of
 // 128).  A block takes 16 weight rows (EPI_SILU: 16 gate rows and their 16 up
 // rows) and its 4 waves split K by 128-column blocks (wave w: blocks w, w + 4, ...).
@@ -507,15 +565,17 @@ __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
 // its four chunks (the same algebra as k_gemv_int4, per 128 columns instead of 32).
 // Wave partials are summed through LDS in wave order before the epilogue.
 constexpr int kMfmaBlocksPerWave = 16;   // K <= 4 * 16 * 128 = 8192
-template <int BT, int EPI, int PRO>
+// GS: the staged input comes from memory (k_gemv_stage16) instead of being built in
+// this group's LDS.
+template <int BT, int EPI, int PRO, bool GS>
 __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
   static_assert(BT == 16, "one 16-row operand of batch rows");
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NT = EPI == EPI_SILU ? 2 : 1;   // 16-row weight tiles per block
   const int K = a.K, CH = K >> 5, NG = K / a.G, NB = K >> 7, B = a.B;
   const GemvLds lay = gemv_lds(BT, K, PRO == PRO_ATTN);
-  const uint4* xs = reinterpret_cast<const uint4*>(smem + lay.xs);     // [BT][4][CH]
-  const float2* cc = reinterpret_cast<const float2*>(smem + lay.cc);   // [BT][CH]
+  const uint4* xs = GS ? a.xsg : reinterpret_cast<const uint4*>(smem + lay.xs);      // [BT][4][CH]
+  const float2* cc = GS ? a.ccg : reinterpret_cast<const float2*>(smem + lay.cc);    // [BT][CH]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, gq = lane >> 4;
   const int r0 = blockIdx.x * 16;
   const bool rok = r0 + n < a.N;
@@ -539,7 +599,7 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
       }
     }
   }
-  gemv_stage<BT, PRO>(a, smem);
+  if constexpr (!GS) gemv_stage<BT, PRO>(a, smem);
 
   // ---- dequantize and multiply
   const int bn = n < B ? n : 0;   // staged row of this lane's operand (padding repeats row 0)
@@ -580,8 +640,8 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
   }
 
   // ---- wave partials -> LDS [4 waves][NT][16 batch rows][16 weight rows], then the epilogue
-  __syncthreads();   // the staged input is no longer read: its space takes the partials
-  float* part = reinterpret_cast<float*>(smem + lay.xs);
+  __syncthreads();   // (LDS staging: the input is no longer read, its space takes the partials)
+  float* part = reinterpret_cast<float*>(smem + (GS ? 0 : lay.xs));
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
