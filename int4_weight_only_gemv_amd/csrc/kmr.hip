@@ -75,7 +75,8 @@ struct WsLayout {
   size_t status, cs, x, qkv, attn_o, act, part_o, part_ml, lm_part, total;
   size_t step_ctr, lm_cnt, tx, tqkv, to, tact, tpart, lm_part2;
   size_t lx, sx, lqkv, lpart, lact, pO, pD, probe;
-  size_t xst, xst_cc;   // staged input of a 16-row GEMV tile: [16][4][Kmax/32] x 16 B, [16][Kmax/32] x 8 B
+  size_t xst, xst_cc, xst_cb;   // staged 16-row GEMV tile: [16][4][Kmax/32] x 16 B, [16][Kmax/32] x 8 B,
+                                // [16][Kmax/128] x 8 B
   StepXSizes xz;
   int ns, nblk_lm;
 };
@@ -109,6 +110,7 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
     kmax = kmax > c->intermediate ? kmax : c->intermediate;
     w.xst = o; o += align256((size_t)16 * 4 * (kmax / 32) * 16);
     w.xst_cc = o; o += align256((size_t)16 * (kmax / 32) * 8);
+    w.xst_cb = o; o += align256((size_t)16 * (kmax / 128) * 8);
   }
   // XCD-local step kernel: per-XCD regions, then the device-wide partials
   o = (o + 4095) & ~(size_t)4095;
@@ -200,14 +202,14 @@ inline bool gemv_mfma_shape(const GemvArgs& a) {
 }
 template <int EPI, int PRO>
 inline bool gemv_mfma_staged(const GemvArgs& a) {
-  return PRO != PRO_ATTN && a.xsg && a.ccg && gemv_mfma_shape<EPI, PRO>(a);
+  return PRO != PRO_ATTN && a.xsg && a.ccg && a.cbg && gemv_mfma_shape<EPI, PRO>(a);
 }
 
 template <int EPI, int PRO>
 void launch_gemv_tile(const GemvArgs& a, hipStream_t st) {
   if (a.B >= 9 && gemv_mfma_staged<EPI, PRO>(a)) {
     if constexpr (PRO != PRO_ATTN) {
-      hipLaunchKernelGGL((k_gemv_stage16<PRO>), dim3(16), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemv_stage16<PRO>), dim3(16, (a.K + 2047) / 2048), dim3(64), 0, st, a);
       const size_t lds = (size_t)4 * (EPI == EPI_SILU ? 2 : 1) * 256 * 4;   // wave partials
       hipLaunchKernelGGL((k_gemv_int4_mfma<16, EPI, PRO, true>), dim3((a.N + 15) / 16), dim3(256), lds, st, a);
     }
@@ -303,8 +305,9 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
 
   uint4* xsg = at<uint4>(ws, w.xst);
   float2* ccg = at<float2>(ws, w.xst_cc);
+  float2* cbg = at<float2>(ws, w.xst_cb);
   GemvArgs g{};
-  g.xsg = xsg; g.ccg = ccg;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg;
   g.packed = static_cast<const uint8_t*>(L->qkv.packed);
   g.sz = static_cast<const uint32_t*>(L->qkv.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->in_norm); g.eps = c->rms_eps;
@@ -331,7 +334,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   ap.Hkv = Hkv; ap.NS = w.ns; ap.QPG = Hq / Hkv; ap.D = D; ap.M = kv->max_len;
 
   g = GemvArgs{};
-  g.xsg = xsg; g.ccg = ccg;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg;
   g.packed = static_cast<const uint8_t*>(L->o.packed);
   g.sz = static_cast<const uint32_t*>(L->o.sz);
   g.y = x; g.ldy = H; g.N = H; g.K = Hq * D; g.G = G; g.B = B;
@@ -346,7 +349,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   }
 
   g = GemvArgs{};
-  g.xsg = xsg; g.ccg = ccg;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg;
   g.packed = static_cast<const uint8_t*>(L->gate_up.packed);
   g.sz = static_cast<const uint32_t*>(L->gate_up.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->post_norm); g.eps = c->rms_eps;
@@ -354,7 +357,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   launch_gemv<EPI_SILU, PRO_RMSNORM>(g, st);
 
   g = GemvArgs{};
-  g.xsg = xsg; g.ccg = ccg;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg;
   g.packed = static_cast<const uint8_t*>(L->down.packed);
   g.sz = static_cast<const uint32_t*>(L->down.sz);
   g.x = act; g.ldx = I; g.gain = nullptr;

@@ -265,7 +265,8 @@ struct GemvArgs {
   AttnPart ap;            // PRO_ATTN; ap.cpos is indexed from batch row b0
   int b0;                 // first batch row of this tile (PRO_ATTN)
   uint4* xsg;             // staged input of a 16-row tile in memory: [16][4][K/32] ...
-  float2* ccg;            // ... and its chunk constants [16][K/32] (k_gemv_stage16)
+  float2* ccg;            // ... its chunk constants [16][K/32] ...
+  float2* cbg;            // ... and their sums per 128-column block [16][K/128] (k_gemv_stage16)
 };
 
 // LDS layout of k_gemv_int4 (byte offsets, 16-byte aligned).
@@ -505,53 +506,51 @@ __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
   }
 }
 
-// The staged input of a 16-row batch tile written once to memory (a.xsg, a.ccg), in
-// the layout gemv_stage gives LDS, for k_gemv_int4_mfma with GS set: one group per
-// batch row (rows b >= B are zero), plain input or its RMSNorm.
+// The staged input of a 16-row batch tile written once to memory (a.xsg, a.ccg, and
+// the chunk constants summed per 128-column block in a.cbg), in the layout
+// gemv_stage gives LDS, for k_gemv_int4_mfma with GS set.  Grid (16 rows, K/2048):
+// one wave per row and 64 chunks, lane = chunk; rows b >= B are zero.  Plain input
+// or its RMSNorm (each wave sums the squares of its whole row).
 template <int PRO>
-__global__ __launch_bounds__(256) void k_gemv_stage16(GemvArgs a) {
+__global__ __launch_bounds__(64) void k_gemv_stage16(GemvArgs a) {
   static_assert(PRO == PRO_PLAIN || PRO == PRO_RMSNORM, "plain or RMSNorm input");
-  __shared__ float red[4];
-  const int b = blockIdx.x, K = a.K, CH = K >> 5, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x, K = a.K, CH = K >> 5, lane = threadIdx.x, c = blockIdx.y * 64 + lane;
   const bool live = b < a.B;
   const float* xr = a.x + (size_t)(live ? b : 0) * a.ldx;
-  float iv = 1.f;
+  // this lane's chunk (and gains) first, in flight during the sum of squares
+  float e[32];
+  uint32_t gw[16];
+  const bool own = live && c < CH;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = own ? reinterpret_cast<const float4*>(xr + 32 * c)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    e[4 * i] = v.x; e[4 * i + 1] = v.y; e[4 * i + 2] = v.z; e[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    gw[i] = (PRO == PRO_RMSNORM && own) ? reinterpret_cast<const uint32_t*>(a.gain + 32 * c)[i] : 0u;
   if (PRO == PRO_RMSNORM) {
     float ss = 0.f;
     if (live)
-      for (int k = tid * 4; k < K; k += 1024) {
+      for (int k = lane * 4; k < K; k += 256) {
         const float4 v = *reinterpret_cast<const float4*>(xr + k);
         ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
       }
-    ss = wave_sum(ss);
-    if (lane == 0) red[wave] = ss;
-    __syncthreads();
-    iv = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)K + a.eps);
-  }
-  for (int c = tid; c < CH; c += 256) {
-    float e[32];
-    if (live) {
-      const float4* src = reinterpret_cast<const float4*>(xr + 32 * c);
+    const float iv = 1.0f / sqrtf(wave_sum(ss) / (float)K + a.eps);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 v = src[i];
-        e[4 * i] = v.x; e[4 * i + 1] = v.y; e[4 * i + 2] = v.z; e[4 * i + 3] = v.w;
-      }
-      if (PRO == PRO_RMSNORM) {
-        const uint32_t* gw = reinterpret_cast<const uint32_t*>(a.gain + 32 * c);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t gg = gw[i];
-          e[2 * i] = (e[2 * i] * iv) * bf16_lo(gg);
-          e[2 * i + 1] = (e[2 * i + 1] * iv) * bf16_hi(gg);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) e[i] = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      e[2 * i] = (e[2 * i] * iv) * bf16_lo(gw[i]);
+      e[2 * i + 1] = (e[2 * i + 1] * iv) * bf16_hi(gw[i]);
     }
-    a.ccg[b * CH + c] = stage_chunk(e, a.xsg + b * 4 * CH + c, CH);
   }
+  uint4 scratch[4];
+  const float2 C = stage_chunk(e, c < CH ? a.xsg + b * 4 * CH + c : scratch, c < CH ? CH : 1);
+  if (c < CH) a.ccg[b * CH + c] = C;
+  // block constants: the 4 chunks of a 128-column block are lanes 4m .. 4m + 3
+  float c1 = C.x, c2 = C.y;
+  c1 += dpp<0xB1>(c1); c2 += dpp<0xB1>(c2);   // lane ^ 1
+  c1 += dpp<0x4E>(c1); c2 += dpp<0x4E>(c2);   // lane ^ 2
+  if ((lane & 3) == 0 && c < CH) a.cbg[b * (CH >> 2) + (c >> 2)] = make_float2(c1, c2);
 }
 
 // Batch tiles of up to BT = 16 rows on the matrix cores (group size a multiple of
@@ -620,10 +619,16 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int b = 4 * gq + e < BT ? 4 * gq + e : 0;
-      const float2* cp = cc + b * CH + 4 * kb;
-      const float2 c0 = cp[0], c1 = cp[1], c2 = cp[2], c3 = cp[3];
-      C1[e] = (c0.x + c1.x) + (c2.x + c3.x);
-      C2[e] = (c0.y + c1.y) + (c2.y + c3.y);
+      if constexpr (GS) {
+        const float2 cb = a.cbg[b * NB + kb];
+        C1[e] = cb.x;
+        C2[e] = cb.y;
+      } else {
+        const float2* cp = cc + b * CH + 4 * kb;
+        const float2 c0 = cp[0], c1 = cp[1], c2 = cp[2], c3 = cp[3];
+        C1[e] = (c0.x + c1.x) + (c2.x + c3.x);
+        C2[e] = (c0.y + c1.y) + (c2.y + c3.y);
+      }
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
