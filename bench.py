@@ -9,6 +9,9 @@ step = one kmr_decode_step call (embedding, 28 layers, final norm, lm_head,
 argmax); the timed steps repeat the step at the same cache position, rewriting
 the same slot.  `--workload batch4` runs 4 continuous-batching rows (one
 finished) with the token fed back on the device and positions advancing.
+`--workload long16` runs 16 rows with caches of 2048..8000 positions (of 8192):
+a batch that the per-phase kernels serve, with the matrix-core int4 GEMV for
+its 16-row tiles; its roofline figure covers the whole step (many launches).
 `--workload kv_copy` times the continuous-batching slot copy instead
 (kmr_kv_copy_row of a full 1024-position row of the same model's cache).
 
@@ -70,6 +73,8 @@ def stored_traffic(workload_name):
     summary of this workload (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
     calibration factor), or None when there is none or the kernel sources changed
     since it was taken."""
+    if workload_name not in PROFILE_TAG:
+        return None
     path = os.path.join(PROFILES, f"{STEP_KERNEL}_{PROFILE_TAG[workload_name]}_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -201,7 +206,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["step", "batch4", "kv_copy"], default="step")
+    ap.add_argument("--workload", choices=["step", "batch4", "long16", "kv_copy"], default="step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
@@ -290,10 +295,14 @@ def main():
         # One launch of the persistent step kernel per step (all layers,
         # final norm, lm_head and argmax), so its algorithmic bytes per launch are
         # the step's; its average launch duration comes from per-launch events.
+        # (long16: the per-phase kernels, so the figure covers the whole step.)
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(args.workload),
-                     "kernel": STEP_KERNEL, "launches_per_step": 1,
-                     "kernel_us_per_launch": round(kernel_ms * 1000, 1)},
+                     "kernel": STEP_KERNEL if B <= 4 else "per-phase step kernels (k_gemv_int4_mfma, k_attn, "
+                                                          "k_lmhead, ...)",
+                     "launches_per_step": 1 if B <= 4 else None,
+                     "kernel_us_per_launch": round(kernel_ms * 1000, 1) if B <= 4 else None,
+                     "step_us": round(kernel_ms * 1000, 1)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
