@@ -342,7 +342,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
     g.ap = ap;
     launch_gemv<EPI_ADD, PRO_ATTN>(g, st);
   } else {
-    const int threads = B * Hq * (D / 4);
+    const int threads = 8 * B * Hq * (D / 4);   // 8 lanes per 4 output dims
     hipLaunchKernelGGL(k_attn_combine, dim3((threads + 255) / 256), dim3(256), 0, st, ap, ao, B, Hq);
     g.x = ao; g.ldx = Hq * D;
     launch_gemv<EPI_ADD, PRO_PLAIN>(g, st);

@@ -173,62 +173,101 @@ __device__ __forceinline__ int attn_splits(int c, int M) {
   return (c < 0 || c >= M) ? 1 : c / kAttnSplit + 1;
 }
 
-// Merges dims [d0, d0 + ND) of q head h of batch row b.  Splits are folded in
-// split order with a running maximum (same value as the formula above); the
-// loads of 8 splits are issued together so the merge costs few memory round trips.
+// Log-sum-exp merge of two partial states (m, l, o[ND]) into the first; an empty
+// state has m = -inf.  The fused multiply-adds are explicit so that every caller
+// rounds alike; `a` is always the state of the lower split class.
 template <int ND>
-__device__ __forceinline__ void merge_head(const AttnPart& p, int b, int h, int d0, float* out) {
+__device__ __forceinline__ void lse_pair(float& ma, float& la, float* oa, float mb, float lb, const float* ob) {
+  if (mb == -INFINITY) return;
+  if (ma == -INFINITY) {
+    ma = mb;
+    la = lb;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) oa[i] = ob[i];
+    return;
+  }
+  const float mn = fmaxf(ma, mb), ca = exp2f(ma - mn), cb = exp2f(mb - mn);
+  la = __builtin_fmaf(la, ca, lb * cb);
+#pragma unroll
+  for (int i = 0; i < ND; ++i) oa[i] = __builtin_fmaf(oa[i], ca, ob[i] * cb);
+  ma = mn;
+}
+
+// Partial state of split class j (splits t = j, j + 8, ... in order) of dims
+// [d0, d0 + ND) of q head h of batch row b.
+template <int ND>
+__device__ __forceinline__ void merge_class(const AttnPart& p, int b, int h, int d0, int j, float& m, float& l,
+                                            float* o) {
   const int g = h / p.QPG, hh = h - g * p.QPG;
   const int ns = attn_splits(p.cpos[b], p.M);
   const size_t base = ((size_t)b * p.Hkv + g) * p.NS;
-  float Mx = -INFINITY, L = 0.f;
+  m = -INFINITY;
+  l = 0.f;
 #pragma unroll
-  for (int i = 0; i < ND; ++i) out[i] = 0.f;
-  for (int t0 = 0; t0 < ns; t0 += 8) {
-    float2 ml[8];
-    float4 ov[8][ND / 4];
+  for (int i = 0; i < ND; ++i) o[i] = 0.f;
+  for (int t = j; t < ns; t += 8) {
+    const size_t slot = (base + t) * p.QPG + hh;
+    const float2 ml = p.part_ml[slot];
+    float ov[ND];
+    const float4* src = reinterpret_cast<const float4*>(p.part_o + slot * p.D + d0);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      if (t0 + t < ns) {
-        const size_t slot = (base + t0 + t) * p.QPG + hh;
-        ml[t] = p.part_ml[slot];
-        const float4* src = reinterpret_cast<const float4*>(p.part_o + slot * p.D + d0);
-#pragma unroll
-        for (int i = 0; i < ND / 4; ++i) ov[t][i] = src[i];
-      }
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      if (t0 + t < ns) {
-        const float Mn = fmaxf(Mx, ml[t].x);
-        const float cold = exp2f(Mx - Mn), cnew = exp2f(ml[t].x - Mn);
-        L = L * cold + ml[t].y * cnew;
-#pragma unroll
-        for (int i = 0; i < ND / 4; ++i) {
-          out[4 * i + 0] = out[4 * i + 0] * cold + ov[t][i].x * cnew;
-          out[4 * i + 1] = out[4 * i + 1] * cold + ov[t][i].y * cnew;
-          out[4 * i + 2] = out[4 * i + 2] * cold + ov[t][i].z * cnew;
-          out[4 * i + 3] = out[4 * i + 3] * cold + ov[t][i].w * cnew;
-        }
-        Mx = Mn;
-      }
+    for (int i = 0; i < ND / 4; ++i) {
+      const float4 v = src[i];
+      ov[4 * i] = v.x; ov[4 * i + 1] = v.y; ov[4 * i + 2] = v.z; ov[4 * i + 3] = v.w;
+    }
+    lse_pair<ND>(m, l, o, ml.x, ml.y, ov);
   }
-  const float inv = 1.0f / L;
-#pragma unroll
-  for (int i = 0; i < ND; ++i) out[i] *= inv;
 }
 
-// Stand-alone merge: one thread per (batch row, q head, 4 dims) -> o fp32 [B][Hq*D].
+// Merges dims [d0, d0 + ND) of q head h of batch row b: the 8 split classes, then
+// the fixed tree ((0 1)(2 3))((4 5)(6 7)).  k_attn_combine runs the classes on 8
+// lanes and the tree with lane exchanges: the same operations in the same order.
+template <int ND>
+__device__ __forceinline__ void merge_head(const AttnPart& p, int b, int h, int d0, float* out) {
+  float m[8], l[8], o[8][ND];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) merge_class<ND>(p, b, h, d0, j, m[j], l[j], o[j]);
+#pragma unroll
+  for (int k = 1; k < 8; k <<= 1)
+#pragma unroll
+    for (int j = 0; j < 8; j += 2 * k) lse_pair<ND>(m[j], l[j], o[j], m[j + k], l[j + k], o[j + k]);
+  const float inv = 1.0f / l[0];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) out[i] = o[0][i] * inv;
+}
+
+// Stand-alone merge: 8 lanes per (batch row, q head, 4 dims), lane j taking split
+// class j -> o fp32 [B][Hq*D].
 __global__ __launch_bounds__(256) void k_attn_combine(AttnPart p, float* __restrict__ out, int B,
                                                       int Hq) {
   const int quads = p.D / 4;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= B * Hq * quads) return;
-  const int b = idx / (Hq * quads), r = idx - b * Hq * quads;
-  const int h = r / quads, dq = r - h * quads;
-  float o[4];
-  merge_head<4>(p, b, h, 4 * dq, o);
-  *reinterpret_cast<float4*>(out + (size_t)b * Hq * p.D + h * p.D + 4 * dq) =
-      make_float4(o[0], o[1], o[2], o[3]);
+  const int t = blockIdx.x * blockDim.x + threadIdx.x, j = t & 7, idx = t >> 3;
+  const bool live = idx < B * Hq * quads;   // (whole 8-lane groups: live is uniform in a group)
+  const int b = live ? idx / (Hq * quads) : 0, r = idx - b * Hq * quads;
+  const int h = live ? r / quads : 0, dq = live ? r - h * quads : 0;
+  float m, l, o[4];
+  merge_class<4>(p, b, h, 4 * dq, j, m, l, o);
+#pragma unroll
+  for (int k = 1; k < 8; k <<= 1) {
+    const float mp = __shfl_xor(m, k), lp = __shfl_xor(l, k);
+    float op[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) op[i] = __shfl_xor(o[i], k);
+    if (j & k) {   // the partner holds the lower class: it is the first operand
+      float ml = mp, ll = lp, ol[4] = {op[0], op[1], op[2], op[3]};
+      lse_pair<4>(ml, ll, ol, m, l, o);
+      m = ml; l = ll;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = ol[i];
+    } else {
+      lse_pair<4>(m, l, o, mp, lp, op);
+    }
+  }
+  if (live && j == 0) {
+    const float inv = 1.0f / l;
+    *reinterpret_cast<float4*>(out + (size_t)b * Hq * p.D + h * p.D + 4 * dq) =
+        make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  }
 }
 
 // ------------------------------------------------------------------ int4 GEMV
