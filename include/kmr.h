@@ -65,7 +65,7 @@ enum {
                                  (diagnostic; such a call may also time out) */
 };
 
-#define KMR_MAX_BATCH 16
+#define KMR_MAX_BATCH 64
 #define KMR_ADVANCE 1u
 #define KMR_MULTI_KERNEL 2u  /* run the step as one kernel per phase instead of the
                                 single persistent kernel (diagnostics, cross-checks) */

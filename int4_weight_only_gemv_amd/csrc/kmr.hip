@@ -279,12 +279,24 @@ void launch_lm_cpl(const LmArgs& a, hipStream_t st) {
   else launch_lm_k<BT, 8>(a, st);
 }
 
-void launch_lmhead(const LmArgs& a, hipStream_t st) {
+void launch_lmhead_tile(const LmArgs& a, hipStream_t st) {
   if (a.B == 1) launch_lm_cpl<1>(a, st);
   else if (a.B == 2) launch_lm_cpl<2>(a, st);
   else if (a.B <= 4) launch_lm_cpl<4>(a, st);
   else if (a.B <= 8) launch_lm_cpl<8>(a, st);
   else launch_lm_cpl<16>(a, st);
+}
+
+// Batch tiles of at most 16 rows (input rows, logits rows and argmax partials offset).
+void launch_lmhead(const LmArgs& a, hipStream_t st) {
+  for (int b0 = 0; b0 < a.B; b0 += 16) {
+    LmArgs t = a;
+    t.B = a.B - b0 < 16 ? a.B - b0 : 16;
+    t.x = a.x + (size_t)b0 * a.K;
+    t.logits = a.logits ? a.logits + (size_t)b0 * a.V : nullptr;
+    t.part = a.part + (size_t)b0 * a.nblk;
+    launch_lmhead_tile(t, st);
+  }
 }
 
 // The O projection merges the attention splits in its own prologue when every

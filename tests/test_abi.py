@@ -91,7 +91,7 @@ def test_workspace_and_kv_sizes(kmr):
     n16 = kmr.workspace_bytes(cfg, 16, 8192)
     assert 0 < n1 < n16
     assert kmr.workspace_bytes(cfg, 0, 1024) == 0
-    assert kmr.workspace_bytes(cfg, 17, 1024) == 0
+    assert kmr.workspace_bytes(cfg, kmr.KMR_MAX_BATCH + 1, 1024) == 0
 
 
 @pytest.mark.parametrize("over,code", [
@@ -149,7 +149,7 @@ def test_bad_slot_calls_are_rejected_before_launch(kmr):
     p3 = (C.c_int32 * 3)(1, 2, 3)
     admit = kmr._lib.kmr_slot_admit
     assert admit(fake, fake, fake, fake, 4, 4, 7, p3, 5, None) == kmr.KMR_EINVAL
-    assert admit(fake, fake, fake, fake, 17, 0, 7, p3, 5, None) == kmr.KMR_EINVAL
+    assert admit(fake, fake, fake, fake, kmr.KMR_MAX_BATCH + 1, 0, 7, p3, 5, None) == kmr.KMR_EINVAL
     assert admit(fake, fake, fake, fake, 4, 0, 7, p3, -1, None) == kmr.KMR_EINVAL
     assert admit(None, fake, fake, fake, 4, 0, 7, p3, 5, None) == kmr.KMR_EINVAL
     assert kmr._lib.kmr_slot_retire(fake, 4, -1, None) == kmr.KMR_EINVAL

@@ -331,6 +331,29 @@ def test_decode_step_long16_sampled_rows(kmr, full_pair):
     assert ws.status() == 0
 
 
+def test_decode_step_batch40_sampled_rows(kmr, full_pair):
+    """Batches above 16 run in 16-row tiles (here 16 + 16 + 8, the last tile on the
+    VALU GEMV and a ragged lm_head tile); the oracle checks rows from each tile."""
+    dims = full_pair.dims
+    B, M, rows = 40, 1024, [0, 17, 39]
+    log(f"decode_step 28 layers, batch {B}, max_len {M}; oracle on rows {rows}")
+    rng = np.random.default_rng(4040)
+    cpos = rng.integers(0, M - 1, B).astype(np.int32)
+    ids = rng.integers(0, dims.vocab, B).astype(np.int32)
+    pos = np.stack([cpos, cpos // 2, cpos // 3]).astype(np.int32)
+    kv, kh, vh = make_caches(dims, synth.base_seed(synth.WORKLOADS["step"]), B, M, "device", host_rows=rows)
+    ws = kmr.Workspace(full_pair.dev.cfg, B, M)
+    nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, dims.vocab), dtype=torch.float32, device="cuda")
+    full_pair.dev.decode_step(kv, torch.from_numpy(ids).cuda(), torch.from_numpy(pos).cuda(),
+                              torch.from_numpy(cpos).cuda(), nxt, ws, logits=logits)
+    torch.cuda.synchronize()
+    assert ws.status() == 0
+    ref = full_pair.ora.decode_step(kh, vh, ids[rows], np.ascontiguousarray(pos[:, rows]), cpos[rows].copy())
+    _check_step(nxt.cpu().numpy()[rows], logits.cpu().numpy()[rows], ref, "rows")
+    del kv
+
+
 # ------------------------------------------------------------------ error paths
 
 def test_out_of_range_cache_position_sets_status_and_writes_nothing(kmr):
