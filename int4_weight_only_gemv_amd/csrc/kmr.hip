@@ -287,6 +287,17 @@ void launch_lmhead_tile(const LmArgs& a, hipStream_t st) {
   else launch_lm_cpl<16>(a, st);
 }
 
+// Tiles of 9..16 rows with hidden 2048 take the matrix-core lm_head: 256 groups
+// (one per CU: the staged input fills most of the LDS), each wave at most
+// ceil(V / 16 / 1024) vocabulary blocks.
+bool lmhead_mfma_fits(const LmArgs& a) { return a.B >= 9 && a.K == 2048 && a.nblk == (a.V + 15) / 16; }
+
+void launch_lmhead_mfma(const LmArgs& a, hipStream_t st) {
+  const size_t lds = (size_t)2 * 16 * (2048 + 8) * 2;
+  allow_lds(k_lmhead_mfma<64>, lds);
+  hipLaunchKernelGGL((k_lmhead_mfma<64>), dim3(256), dim3(256), lds, st, a);
+}
+
 // Batch tiles of at most 16 rows (input rows, logits rows and argmax partials offset).
 void launch_lmhead(const LmArgs& a, hipStream_t st) {
   for (int b0 = 0; b0 < a.B; b0 += 16) {
@@ -295,7 +306,8 @@ void launch_lmhead(const LmArgs& a, hipStream_t st) {
     t.x = a.x + (size_t)b0 * a.K;
     t.logits = a.logits ? a.logits + (size_t)b0 * a.V : nullptr;
     t.part = a.part + (size_t)b0 * a.nblk;
-    launch_lmhead_tile(t, st);
+    if (lmhead_mfma_fits(t)) launch_lmhead_mfma(t, st);
+    else launch_lmhead_tile(t, st);
   }
 }
 

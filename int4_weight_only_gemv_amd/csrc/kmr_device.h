@@ -115,6 +115,12 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4 a, const uint4 b, f3
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
                                                 c, 0, 0, 0);
 }
+// The same product with bf16 operands (same lane layout).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4_t mfma16x16x32_bf16(const uint4 a, const uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
 
 // (a & mask) | bias as one v_and_or_b32.  A three-source VALU instruction takes no
 // 32-bit literal on this architecture, so with literal constants the compiler splits

@@ -1031,6 +1031,104 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
   }
 }
 
+// The lm_head of a 9..16-row batch tile on the matrix cores, for K = 32 NK.  Each
+// group stages h = RMSNorm(x; gain) of the tile once in LDS as bf16 h_hi = bf16(h)
+// and h_lo = bf16(h - h_hi) (rows padded by 16 bytes: the 16 rows of an operand
+// read fall in distinct banks); bf16 weights times both parts are exact in fp32,
+// so two v_mfma_f32_16x16x32_bf16 per 32 columns give the fp32 product to about
+// 2^-16 of |h|.  Each wave takes 16-row vocabulary blocks (block t = rows 16 t..)
+// in a grid-stride loop, streaming its lane's 16-byte weight pieces through a
+// ring of kLmRing loads over the unrolled K loop; lane (n, gq) receives batch rows
+// 4 gq + e of vocabulary row 16 t + n.  The argmax of each batch row is kept per
+// lane over all of the wave's blocks and written, with empty entries for its other
+// blocks, after the loop (a store in flight would make every later load wait).
+constexpr int kLmRing = 16;
+template <int NK>
+__global__ __launch_bounds__(256) void k_lmhead_mfma(LmArgs a) {
+  constexpr int K = 32 * NK, KS = K + 8;   // LDS row stride in bf16
+  static_assert(NK >= kLmRing, "the ring is filled from the first K columns");
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* hhi = reinterpret_cast<uint16_t*>(smem);   // [16][KS]
+  uint16_t* hlo = hhi + 16 * KS;                        // [16][KS]
+  __shared__ float s_inv[16];
+  const int B = a.B, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, gq = lane >> 4;
+
+  // ---- h of the tile's rows (rows >= B zero), split into two bf16 parts
+  for (int b = wave; b < 16; b += 4) {
+    float ss = 0.f;
+    if (b < B)
+      for (int k = lane * 4; k < K; k += 256) {
+        const float4 v = *reinterpret_cast<const float4*>(a.x + (size_t)b * K + k);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+    ss = wave_sum(ss);
+    if (lane == 0) s_inv[b] = b < B ? 1.0f / sqrtf(ss / (float)K + a.eps) : 0.f;
+  }
+  __syncthreads();
+  for (int i = tid; i < 16 * K; i += 256) {
+    const int b = i / K, k = i - b * K;
+    const float h = b < B ? (a.x[(size_t)b * K + k] * s_inv[b]) * bf16_to_f32(a.gain[k]) : 0.f;
+    const uint16_t hi = f32_to_bf16(h);
+    hhi[b * KS + k] = hi;
+    hlo[b * KS + k] = f32_to_bf16(h - bf16_to_f32(hi));
+  }
+  __syncthreads();
+
+  const int ntile = (a.V + 15) >> 4;
+  float bv[4];
+  int bi[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { bv[e] = -INFINITY; bi[e] = 0x7fffffff; }
+  const uint16_t* ahi = hhi + n * KS + 8 * gq;
+  const uint16_t* alo = hlo + n * KS + 8 * gq;
+  for (int t = blockIdx.x * 4 + wave; t < ntile; t += gridDim.x * 4) {
+    const int r = 16 * t + n;
+    const bool rok = r < a.V;
+    const uint16_t* wr = a.W + (size_t)(rok ? r : 0) * K + 8 * gq;
+    uint4 ring[kLmRing];
+#pragma unroll
+    for (int i = 0; i < kLmRing; ++i) ring[i] = load_stream16(wr + 32 * i);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < NK; ++kt) {
+      const uint4 w = ring[kt % kLmRing];
+      if (kt + kLmRing < NK) ring[kt % kLmRing] = load_stream16(wr + 32 * (kt + kLmRing));
+      const uint4 xh = *reinterpret_cast<const uint4*>(ahi + 32 * kt);
+      const uint4 xl = *reinterpret_cast<const uint4*>(alo + 32 * kt);
+      acc = mfma16x16x32_bf16(xh, w, acc);
+      acc = mfma16x16x32_bf16(xl, w, acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int b = 4 * gq + e;
+      if (b < B && rok) {
+        if (a.logits) a.logits[(size_t)b * a.V + r] = acc[e];
+        if (better(acc[e], r, bv[e], bi[e])) { bv[e] = acc[e]; bi[e] = r; }
+      }
+    }
+  }
+  // best of each batch row over the 16 lanes of a row group, then the partials:
+  // the wave's first block holds its best, its other blocks empty entries
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const float ov = __shfl_xor(bv[e], off);
+      const int oi = __shfl_xor(bi[e], off);
+      if (better(ov, oi, bv[e], bi[e])) { bv[e] = ov; bi[e] = oi; }
+    }
+  const int t0 = blockIdx.x * 4 + wave;
+  for (int t = t0; t < ntile; t += gridDim.x * 4)
+    if (n == 0)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int b = 4 * gq + e;
+        if (b < B)
+          a.part[(size_t)b * a.nblk + t] = t == t0 ? make_float2(bv[e], __int_as_float(bi[e]))
+                                                   : make_float2(-INFINITY, __int_as_float(0x7fffffff));
+      }
+}
+
 struct LmFinishArgs {
   const float2* part;        // [B][nblk]
   const uint8_t* finished_in;
