@@ -294,8 +294,13 @@ bool lmhead_mfma_fits(const LmArgs& a) { return a.B >= 9 && a.K == 2048 && a.nbl
 
 void launch_lmhead_mfma(const LmArgs& a, hipStream_t st) {
   const size_t lds = (size_t)2 * 16 * (2048 + 8) * 2;
-  allow_lds(k_lmhead_mfma<64>, lds);
-  hipLaunchKernelGGL((k_lmhead_mfma<64>), dim3(256), dim3(256), lds, st, a);
+  if (a.logits) {
+    allow_lds(k_lmhead_mfma<64, true>, lds);
+    hipLaunchKernelGGL((k_lmhead_mfma<64, true>), dim3(256), dim3(256), lds, st, a);
+  } else {
+    allow_lds(k_lmhead_mfma<64, false>, lds);
+    hipLaunchKernelGGL((k_lmhead_mfma<64, false>), dim3(256), dim3(256), lds, st, a);
+  }
 }
 
 // Batch tiles of at most 16 rows (input rows, logits rows and argmax partials offset).

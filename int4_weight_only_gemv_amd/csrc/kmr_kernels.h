@@ -1041,9 +1041,10 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
 // ring of kLmRing loads over the unrolled K loop; lane (n, gq) receives batch rows
 // 4 gq + e of vocabulary row 16 t + n.  The argmax of each batch row is kept per
 // lane over all of the wave's blocks and written, with empty entries for its other
-// blocks, after the loop (a store in flight would make every later load wait).
+// blocks, after the loop (a store in flight would make every later load wait; so
+// the logits stores are a separate instantiation, LG, used only when asked for).
 constexpr int kLmRing = 16;
-template <int NK>
+template <int NK, bool LG>
 __global__ __launch_bounds__(256) void k_lmhead_mfma(LmArgs a) {
   constexpr int K = 32 * NK, KS = K + 8;   // LDS row stride in bf16
   static_assert(NK >= kLmRing, "the ring is filled from the first K columns");
@@ -1065,12 +1066,39 @@ __global__ __launch_bounds__(256) void k_lmhead_mfma(LmArgs a) {
     if (lane == 0) s_inv[b] = b < B ? 1.0f / sqrtf(ss / (float)K + a.eps) : 0.f;
   }
   __syncthreads();
-  for (int i = tid; i < 16 * K; i += 256) {
-    const int b = i / K, k = i - b * K;
-    const float h = b < B ? (a.x[(size_t)b * K + k] * s_inv[b]) * bf16_to_f32(a.gain[k]) : 0.f;
-    const uint16_t hi = f32_to_bf16(h);
-    hhi[b * KS + k] = hi;
-    hlo[b * KS + k] = f32_to_bf16(h - bf16_to_f32(hi));
+  // 8 consecutive columns per thread and step, the loads of 4 steps issued together
+  constexpr int STEPS = 16 * K / (8 * 256), SB = 4;
+  static_assert(STEPS % SB == 0, "whole batches of steps");
+  for (int j0 = 0; j0 < STEPS; j0 += SB) {
+  float4 xv[SB][2];
+  uint4 gv[SB];
+#pragma unroll
+  for (int jj = 0; jj < SB; ++jj) {
+    const int j = j0 + jj, i = (j * 256 + tid) * 8, b = i / K, k = i - b * K;
+    const float* xp = a.x + (size_t)(b < B ? b : 0) * K + k;
+    xv[jj][0] = *reinterpret_cast<const float4*>(xp);
+    xv[jj][1] = *reinterpret_cast<const float4*>(xp + 4);
+    gv[jj] = *reinterpret_cast<const uint4*>(a.gain + k);
+  }
+#pragma unroll
+  for (int jj = 0; jj < SB; ++jj) {
+    const int j = j0 + jj, i = (j * 256 + tid) * 8, b = i / K, k = i - b * K;
+    const float xs[8] = {xv[jj][0].x, xv[jj][0].y, xv[jj][0].z, xv[jj][0].w,
+                         xv[jj][1].x, xv[jj][1].y, xv[jj][1].z, xv[jj][1].w};
+    const uint32_t gw[4] = {gv[jj].x, gv[jj].y, gv[jj].z, gv[jj].w};
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float h0 = (xs[2 * q] * s_inv[b]) * bf16_lo(gw[q]);
+      float h1 = (xs[2 * q + 1] * s_inv[b]) * bf16_hi(gw[q]);
+      if (b >= B) h0 = h1 = 0.f;
+      const uint16_t a0 = f32_to_bf16(h0), a1 = f32_to_bf16(h1);
+      ph[q] = (uint32_t)a0 | ((uint32_t)a1 << 16);
+      pl[q] = (uint32_t)f32_to_bf16(h0 - bf16_to_f32(a0)) | ((uint32_t)f32_to_bf16(h1 - bf16_to_f32(a1)) << 16);
+    }
+    *reinterpret_cast<uint4*>(hhi + b * KS + k) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+    *reinterpret_cast<uint4*>(hlo + b * KS + k) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+  }
   }
   __syncthreads();
 
@@ -1097,12 +1125,15 @@ __global__ __launch_bounds__(256) void k_lmhead_mfma(LmArgs a) {
       const uint4 xl = *reinterpret_cast<const uint4*>(alo + 32 * kt);
       acc = mfma16x16x32_bf16(xh, w, acc);
       acc = mfma16x16x32_bf16(xl, w, acc);
+      // keeps each step's loads in its step: the ring's loads stay kLmRing steps
+      // ahead of their use instead of being moved next to it
+      asm volatile("" ::: "memory");
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int b = 4 * gq + e;
       if (b < B && rok) {
-        if (a.logits) a.logits[(size_t)b * a.V + r] = acc[e];
+        if constexpr (LG) a.logits[(size_t)b * a.V + r] = acc[e];
         if (better(acc[e], r, bv[e], bi[e])) { bv[e] = acc[e]; bi[e] = r; }
       }
     }
