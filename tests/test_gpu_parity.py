@@ -354,6 +354,32 @@ def test_decode_step_batch40_sampled_rows(kmr, full_pair):
     del kv
 
 
+@pytest.mark.parametrize("batch", [1, 4, 16])
+def test_decode_step_tokens_without_logits_buffer(kmr, full_pair, batch):
+    """Without a logits buffer the lm_head loops take their store-free form; the
+    tokens must be those of the run that also writes the logits (same arithmetic)."""
+    dims, M = full_pair.dims, 1024
+    log(f"decode_step batch {batch}: tokens with and without a logits buffer")
+    rng = np.random.default_rng(7000 + batch)
+    cpos = rng.integers(0, M - 1, batch).astype(np.int32)
+    ids = rng.integers(0, dims.vocab, batch).astype(np.int32)
+    pos = np.stack([cpos, cpos // 2, cpos // 3]).astype(np.int32)
+    got = []
+    for with_logits in (True, False):
+        kv, _, _ = make_caches(dims, synth.base_seed(synth.WORKLOADS["step"]), batch, M, "device", host_rows=[])
+        ws = kmr.Workspace(full_pair.dev.cfg, batch, M)
+        nxt = torch.zeros(batch, dtype=torch.int32, device="cuda")
+        logits = torch.empty((batch, dims.vocab), dtype=torch.float32, device="cuda") if with_logits else None
+        full_pair.dev.decode_step(kv, torch.from_numpy(ids).cuda(), torch.from_numpy(pos).cuda(),
+                                  torch.from_numpy(cpos).cuda(), nxt, ws, logits=logits)
+        torch.cuda.synchronize()
+        assert ws.status() == 0
+        got.append(nxt.cpu().numpy())
+        del kv
+    log(f"  tokens {got[0].tolist()} vs {got[1].tolist()}")
+    assert np.array_equal(got[0], got[1])
+
+
 # ------------------------------------------------------------------ error paths
 
 def test_out_of_range_cache_position_sets_status_and_writes_nothing(kmr):
