@@ -850,36 +850,54 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
   }
+  // the row's IT positions as one block: their scores (log2 units; -inf past the
+  // cache position), one running-max update and rescale per head, then the
+  // weighted value rows (hardware exp2)
+  float sc[QPG][IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int p = s * kAttnSplit + wave * (kAttnSplit / 4) + it * 4 + rr;
-    const bool valid = p <= c;
-    float kk[DPL], vv[DPL];
+    float kk[DPL];
     if (p == c) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) { kk[e] = kf[e]; vv[e] = vf[e]; }
+      for (int e = 0; e < DPL; ++e) kk[e] = kf[e];
     } else {
 #pragma unroll
-      for (int e = 0; e < DPL / 2; ++e) {
-        kk[2 * e] = bf16_lo(kr[it][e]); kk[2 * e + 1] = bf16_hi(kr[it][e]);
-        vv[2 * e] = bf16_lo(vr[it][e]); vv[2 * e + 1] = bf16_hi(vr[it][e]);
-      }
+      for (int e = 0; e < DPL / 2; ++e) { kk[2 * e] = bf16_lo(kr[it][e]); kk[2 * e + 1] = bf16_hi(kr[it][e]); }
     }
 #pragma unroll
     for (int h = 0; h < QPG; ++h) {
-      float sc = 0.f;
+      float t = 0.f;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) sc += q[h][e] * kk[e];
-      sc = row16_sum(sc) * a.scale_log2;
-      if (valid) {
-        const float mn = fmaxf(m[h], sc);
-        const float corr = exp2f(m[h] - mn);
-        const float pe = exp2f(sc - mn);
-        l[h] = l[h] * corr + pe;
+      for (int e = 0; e < DPL; ++e) t += q[h][e] * kk[e];
+      t = row16_sum(t) * a.scale_log2;
+      sc[h][it] = p <= c ? t : -INFINITY;
+    }
+  }
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o[h][e] = o[h][e] * corr + pe * vv[e];
-        m[h] = mn;
-      }
+  for (int h = 0; h < QPG; ++h) {
+    float mb = m[h];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) mb = fmaxf(mb, sc[h][it]);
+    m[h] = mb;   // (-inf: no valid position, the state stays empty)
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int p = s * kAttnSplit + wave * (kAttnSplit / 4) + it * 4 + rr;
+    float vv[DPL];
+    if (p == c) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) vv[e] = vf[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL / 2; ++e) { vv[2 * e] = bf16_lo(vr[it][e]); vv[2 * e + 1] = bf16_hi(vr[it][e]); }
+    }
+#pragma unroll
+    for (int h = 0; h < QPG; ++h) {
+      const float pe = sc[h][it] != -INFINITY ? exp2_fast(sc[h][it] - m[h]) : 0.f;
+      l[h] += pe;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[h][e] += pe * vv[e];
     }
   }
 
@@ -894,18 +912,32 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     }
   }
   __syncthreads();
+  // the log-sum-exp weight of each (row, head) once, by the first wave: lane
+  // 16 h + r holds row r of head h (QPG <= 4); rows that saw nothing have m = -inf
+  __shared__ float s_w[QPG][16], s_ML[QPG][2];
+  if (wave == 0) {
+    const int h = lane >> 4, r = lane & 15;
+    const float mr = h < QPG ? s_m[r][h] : -INFINITY;
+    float M = mr;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = mr == -INFINITY ? 0.f : exp2_fast(mr - M);
+    float L = h < QPG ? w * s_l[r][h] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) L += __shfl_xor(L, off);
+    if (h < QPG) {
+      s_w[h][r] = w;
+      if (r == 0) { s_ML[h][0] = M; s_ML[h][1] = L; }
+    }
+  }
+  __syncthreads();
   for (int i = tid; i < QPG * D; i += 256) {
     const int h = i / D, d = i - h * D;
-    float M = -INFINITY;
-    for (int r = 0; r < 16; ++r) M = fmaxf(M, s_m[r][h]);
-    float L = 0.f, O = 0.f;
-    for (int r = 0; r < 16; ++r) {
-      const float wgt = exp2f(s_m[r][h] - M);   // rows that saw nothing have m = -inf
-      L += wgt * s_l[r][h];
-      O += wgt * s_o[r][h][d];
-    }
+    float O = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O += s_w[h][r] * s_o[r][h][d];
     a.part_o[(pidx * QPG + h) * D + d] = O;
-    if (d == 0) a.part_ml[pidx * QPG + h] = make_float2(M, L);
+    if (d == 0) a.part_ml[pidx * QPG + h] = make_float2(s_ML[h][0], s_ML[h][1]);
   }
 }
 
