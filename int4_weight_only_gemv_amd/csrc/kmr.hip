@@ -78,7 +78,7 @@ struct WsLayout {
   size_t xst, xst_cc, xst_cb;   // staged 16-row GEMV tile: [16][4][Kmax/32] x 16 B, [16][Kmax/32] x 8 B,
                                 // [16][Kmax/128] x 8 B
   StepXSizes xz;
-  int ns, nblk_lm;
+  int ns, ns_pp, nblk_lm;   // attention splits: persistent device-wide kernel, per-phase kernels
 };
 
 WsLayout ws_layout(const kmr_config* c, int B, int M) {
@@ -86,6 +86,7 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
   const int D = c->head_dim, Hq = c->n_heads, Hkv = c->n_kv_heads, qpg = Hq / Hkv;
   const int nqkv = (Hq + 2 * Hkv) * D;
   w.ns = (M + kAttnSplit - 1) / kAttnSplit;
+  w.ns_pp = (M + kAttnSplitPP - 1) / kAttnSplitPP;
   w.nblk_lm = c->vocab > 0 ? (c->vocab + kLmRowsPerBlock - 1) / kLmRowsPerBlock : 1;
   size_t o = 0;
   w.status = o; o += 256;
@@ -94,8 +95,8 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
   w.qkv = o; o += align256((size_t)B * nqkv * 4);
   w.attn_o = o; o += align256((size_t)B * Hq * D * 4);
   w.act = o; o += align256((size_t)B * c->intermediate * 4);
-  w.part_o = o; o += align256((size_t)B * Hkv * w.ns * qpg * D * 4);
-  w.part_ml = o; o += align256((size_t)B * Hkv * w.ns * qpg * 8);
+  w.part_o = o; o += align256((size_t)B * Hkv * w.ns_pp * qpg * D * 4);
+  w.part_ml = o; o += align256((size_t)B * Hkv * w.ns_pp * qpg * 8);
   w.lm_part = o; o += align256((size_t)B * w.nblk_lm * 8);
   w.step_ctr = o; o += 256;
   w.lm_cnt = o; o += 256;
@@ -354,20 +355,20 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   a.cpos = cpos;
   a.part_o = at<float>(ws, w.part_o); a.part_ml = at<float2>(ws, w.part_ml);
   a.status = at<uint32_t>(ws, w.status);
-  a.Hq = Hq; a.Hkv = Hkv; a.M = kv->max_len; a.NS = w.ns; a.eps = c->rms_eps;
+  a.Hq = Hq; a.Hkv = Hkv; a.M = kv->max_len; a.NS = w.ns_pp; a.eps = c->rms_eps;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   launch_attn(c, a, B, st);
 
   AttnPart ap{};
   ap.part_o = a.part_o; ap.part_ml = a.part_ml; ap.cpos = cpos;
-  ap.Hkv = Hkv; ap.NS = w.ns; ap.QPG = Hq / Hkv; ap.D = D; ap.M = kv->max_len;
+  ap.Hkv = Hkv; ap.NS = w.ns_pp; ap.QPG = Hq / Hkv; ap.D = D; ap.M = kv->max_len;
 
   g = GemvArgs{};
   g.xsg = xsg; g.ccg = ccg; g.cbg = cbg;
   g.packed = static_cast<const uint8_t*>(L->o.packed);
   g.sz = static_cast<const uint32_t*>(L->o.sz);
   g.y = x; g.ldy = H; g.N = H; g.K = Hq * D; g.G = G; g.B = B;
-  if (fuse_attn_merge(B, w.ns)) {
+  if (fuse_attn_merge(B, w.ns_pp)) {
     g.ap = ap;
     launch_gemv<EPI_ADD, PRO_ATTN>(g, st);
   } else {

@@ -10,8 +10,10 @@
 
 namespace kmr {
 
-constexpr int kAttnSplit = 64;   // cache positions per attention work-group (fixed, so
-                                 // a row's result never depends on the batch size)
+constexpr int kAttnSplit = 64;     // cache positions per attention item of the device-wide
+                                   // persistent kernel, and ...
+constexpr int kAttnSplitPP = 128;  // ... per work-group of the per-phase kernels (both fixed,
+                                   // so a row's result never depends on the batch size)
 constexpr int kGemvRowsPerWave = 2;
 constexpr int kLmRowsPerWave = 4;
 constexpr int kLmRowsPerBlock = 4 * kLmRowsPerWave;
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
 }
 
 // ------------------------------------------------------------------ attention partials
-// A split of kAttnSplit cache positions leaves, per q head, the running max m
+// A split of kAttnSplitPP cache positions leaves, per q head, the running max m
 // (log2 domain), the sum l of 2^(s - m) and the unnormalised o~ = sum 2^(s - m) v.
 // Splits merge with log-sum-exp weights, in split order:
 //     o = sum_s 2^(m_s - M) o~_s / sum_s 2^(m_s - M) l_s,   M = max_s m_s.
@@ -171,6 +173,9 @@ struct AttnPart {
 
 __device__ __forceinline__ int attn_splits(int c, int M) {
   return (c < 0 || c >= M) ? 1 : c / kAttnSplit + 1;
+}
+__device__ __forceinline__ int attn_splits_pp(int c, int M) {
+  return (c < 0 || c >= M) ? 1 : c / kAttnSplitPP + 1;
 }
 
 // Log-sum-exp merge of two partial states (m, l, o[ND]) into the first; an empty
@@ -199,7 +204,7 @@ template <int ND>
 __device__ __forceinline__ void merge_class(const AttnPart& p, int b, int h, int d0, int j, float& m, float& l,
                                             float* o) {
   const int g = h / p.QPG, hh = h - g * p.QPG;
-  const int ns = attn_splits(p.cpos[b], p.M);
+  const int ns = attn_splits_pp(p.cpos[b], p.M);
   const size_t base = ((size_t)b * p.Hkv + g) * p.NS;
   m = -INFINITY;
   l = 0.f;
@@ -717,7 +722,7 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
 }
 
 // ------------------------------------------------------------------ attention
-// One work-group per (split of kAttnSplit positions, kv head g, batch row b).
+// One work-group per (split of kAttnSplitPP positions, kv head g, batch row b).
 // Each 16-lane row of a wave takes one cache position per step (head_dim/16
 // dims per lane, so the four rows of a wave read four consecutive cache rows),
 // and all of a lane's cache reads are issued first, before the prologue:
@@ -746,7 +751,7 @@ template <int D, int QPG>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   constexpr int DPL = D / 16;   // dims per lane
   constexpr int HALF = D / 2;
-  constexpr int IT = kAttnSplit / 16;
+  constexpr int IT = kAttnSplitPP / 16;
   __shared__ float s_o[16][QPG][D];
   __shared__ float s_m[16][QPG];
   __shared__ float s_l[16][QPG];
@@ -768,14 +773,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     }
     return;
   }
-  if (s * kAttnSplit > c) return;
-  const int ns = c / kAttnSplit + 1;
+  if (s * kAttnSplitPP > c) return;
+  const int ns = c / kAttnSplitPP + 1;
 
   // ---- cache reads first
   uint32_t kr[IT][DPL / 2], vr[IT][DPL / 2];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int p = s * kAttnSplit + wave * (kAttnSplit / 4) + it * 4 + rr;
+    const int p = s * kAttnSplitPP + wave * (kAttnSplitPP / 4) + it * 4 + rr;
     if (p < c) {
       const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kc + (head_base + p) * D + d0);
       const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vc + (head_base + p) * D + d0);
@@ -856,7 +861,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   float sc[QPG][IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int p = s * kAttnSplit + wave * (kAttnSplit / 4) + it * 4 + rr;
+    const int p = s * kAttnSplitPP + wave * (kAttnSplitPP / 4) + it * 4 + rr;
     float kk[DPL];
     if (p == c) {
 #pragma unroll
@@ -883,7 +888,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int p = s * kAttnSplit + wave * (kAttnSplit / 4) + it * 4 + rr;
+    const int p = s * kAttnSplitPP + wave * (kAttnSplitPP / 4) + it * 4 + rr;
     float vv[DPL];
     if (p == c) {
 #pragma unroll
