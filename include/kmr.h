@@ -194,7 +194,10 @@ int kmr_decode_layer(const kmr_config* cfg, const kmr_layer* layer_w, int32_t la
  * Paths: batch <= 4 with the model shapes the persistent kernels cover runs as one
  * cooperative launch (XCD-local hand-offs when n_kv_heads is a multiple of 8, else
  * or with KMR_DEVICE_WIDE device-wide ones); otherwise, or with KMR_MULTI_KERNEL,
- * as one kernel per phase.
+ * as one kernel per phase, in batch tiles of at most 16 rows (batch up to
+ * KMR_MAX_BATCH).  A tile of 9..16 rows takes the matrix-core int4 GEMV when the
+ * group size is a multiple of 128, and the matrix-core lm_head when hidden is
+ * 2048; the choice depends on the shapes and the tile size only.
  */
 int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
                     const int32_t* token_ids, int32_t* positions, int32_t* cache_position,
