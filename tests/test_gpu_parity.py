@@ -331,13 +331,15 @@ def test_decode_step_long16_sampled_rows(kmr, full_pair):
     assert ws.status() == 0
 
 
-def test_decode_step_batch40_sampled_rows(kmr, full_pair):
-    """Batches above 16 run in 16-row tiles (here 16 + 16 + 8, the last tile on the
-    VALU GEMV and a ragged lm_head tile); the oracle checks rows from each tile."""
+@pytest.mark.parametrize("B,rows", [(40, [0, 17, 39]), (64, [0, 33, 63])])
+def test_decode_step_large_batch_sampled_rows(kmr, full_pair, B, rows):
+    """Batches above 16 run in 16-row tiles (40 = 16 + 16 + 8, the last tile on the
+    VALU GEMV and a ragged lm_head tile; 64 = KMR_MAX_BATCH, four full tiles); the
+    oracle checks rows from different tiles."""
     dims = full_pair.dims
-    B, M, rows = 40, 1024, [0, 17, 39]
+    M = 1024
     log(f"decode_step 28 layers, batch {B}, max_len {M}; oracle on rows {rows}")
-    rng = np.random.default_rng(4040)
+    rng = np.random.default_rng(4000 + B)
     cpos = rng.integers(0, M - 1, B).astype(np.int32)
     ids = rng.integers(0, dims.vocab, B).astype(np.int32)
     pos = np.stack([cpos, cpos // 2, cpos // 3]).astype(np.int32)
