@@ -205,6 +205,27 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
                     uint32_t flags, void* ws, size_t ws_bytes, kmr_stream_t stream);
 
 /*
+ * kmr_decode_step_prefix -- kmr_decode_step with shared-prefix (cascade) attention
+ * ("The Ghost in the Batch", cascade attention: a prefix common to many requests
+ * is read once for all of them, then merged with each request's own suffix).
+ * The caller promises that every row holds the same K/V in cache positions
+ * [0, shared_prefix) of every layer (row 0 is the one read).  The step runs on the
+ * per-phase kernels; the attention splits of 128 positions that lie wholly inside
+ * the prefix are computed once per (split, kv head) for every row whose
+ * cache_position is past them, with the same operations as the plain path, so
+ * next_ids, logits and the cache are bit for bit those of kmr_decode_step with
+ * KMR_MULTI_KERNEL; only the prefix K/V reads shrink.  It is an explicit call:
+ * the library never switches to it by itself.  shared_prefix = 0 is the plain
+ * per-phase step.  KMR_EINVAL: shared_prefix outside [0, kv->max_len], and every
+ * error of kmr_decode_step.
+ */
+int kmr_decode_step_prefix(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
+                           const int32_t* token_ids, int32_t* positions, int32_t* cache_position,
+                           uint8_t* finished, int32_t batch, int32_t* next_ids, float* logits,
+                           uint32_t flags, int32_t shared_prefix, void* ws, size_t ws_bytes,
+                           kmr_stream_t stream);
+
+/*
  * Slot operations of a continuous-batching scheduler (kaminari section 08: the
  * ContinuousBatchScheduler admits requests into free DecodeSlots, each pinned to a
  * physical row of one shared static cache, ticks the active slots one token at a

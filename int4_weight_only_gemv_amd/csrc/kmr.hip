@@ -259,6 +259,16 @@ void launch_attn(const kmr_config* c, const AttnArgs& a, int B, hipStream_t st) 
     if (qpg == 1) KMR_ATTN(64, 1); else if (qpg == 2) KMR_ATTN(64, 2); else KMR_ATTN(64, 4);
   }
 #undef KMR_ATTN
+  if (a.first_split > 0) {   // the shared-prefix splits, once per (split, kv head, row group)
+    dim3 pgrid(a.first_split, c->n_kv_heads, (B + kPrefixRows - 1) / kPrefixRows);
+#define KMR_ATTNP(DD, QQ) hipLaunchKernelGGL((k_attn_prefix<DD, QQ>), pgrid, dim3(256), 0, st, a)
+    if (c->head_dim == 128) {
+      if (qpg == 1) KMR_ATTNP(128, 1); else if (qpg == 2) KMR_ATTNP(128, 2); else KMR_ATTNP(128, 4);
+    } else {
+      if (qpg == 1) KMR_ATTNP(64, 1); else if (qpg == 2) KMR_ATTNP(64, 2); else KMR_ATTNP(64, 4);
+    }
+#undef KMR_ATTNP
+  }
 }
 
 template <int BT, int CPL>
@@ -326,7 +336,8 @@ bool fuse_attn_merge(int B, int ns) { return (size_t)B * ns <= 16; }
 // One decoder layer on x (fp32 [B][H]) using workspace buffers; the RoPE table
 // must already be in ws.cs.
 void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr_kv* kv, float* x,
-                   const int32_t* cpos, int B, void* ws, const WsLayout& w, hipStream_t st) {
+                   const int32_t* cpos, int B, void* ws, const WsLayout& w, hipStream_t st,
+                   int prefix_splits = 0) {
   const int H = c->hidden, D = c->head_dim, Hq = c->n_heads, Hkv = c->n_kv_heads;
   const int nqkv = (Hq + 2 * Hkv) * D, I = c->intermediate, G = c->group_size;
   float* qkv = at<float>(ws, w.qkv);
@@ -357,6 +368,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   a.status = at<uint32_t>(ws, w.status);
   a.Hq = Hq; a.Hkv = Hkv; a.M = kv->max_len; a.NS = w.ns_pp; a.eps = c->rms_eps;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  a.B = B; a.first_split = prefix_splits; a.prefix_row = 0;
   launch_attn(c, a, B, st);
 
   AttnPart ap{};
@@ -636,10 +648,10 @@ int kmr_decode_layer(const kmr_config* cfg, const kmr_layer* layer_w, int32_t la
   return check_hip("decode_layer launch");
 }
 
-int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
-                    const int32_t* token_ids, int32_t* positions, int32_t* cache_position,
-                    uint8_t* finished, int32_t batch, int32_t* next_ids, float* logits,
-                    uint32_t flags, void* ws, size_t ws_bytes, kmr_stream_t stream) {
+static int decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
+                       const int32_t* token_ids, int32_t* positions, int32_t* cache_position,
+                       uint8_t* finished, int32_t batch, int32_t* next_ids, float* logits,
+                       uint32_t flags, void* ws, size_t ws_bytes, kmr_stream_t stream, int prefix_splits) {
   int rc;
   if ((rc = check_config(cfg))) return rc;
   if (cfg->vocab <= 0) return fail(KMR_EINVAL, "vocab must be positive for a full step");
@@ -656,7 +668,7 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
   const WsLayout w = ws_layout(cfg, batch, kv->max_len);
   if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (!(flags & KMR_MULTI_KERNEL) && step_kernel_fits(cfg, batch)) {
+  if (!(flags & KMR_MULTI_KERNEL) && prefix_splits == 0 && step_kernel_fits(cfg, batch)) {
     int nwg = 0;
     if ((rc = device_cus(&nwg))) return rc;
     StepArgs a{};
@@ -713,7 +725,7 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
   enqueue_prep(cfg, static_cast<const uint16_t*>(model->embed), token_ids, finished, positions, x,
                batch, ws, w, st);
   for (int l = 0; l < cfg->n_layers; ++l)
-    enqueue_layer(cfg, &model->layers[l], l, kv, x, cache_position, batch, ws, w, st);
+    enqueue_layer(cfg, &model->layers[l], l, kv, x, cache_position, batch, ws, w, st, prefix_splits);
   LmArgs la{};
   la.x = x; la.gain = static_cast<const uint16_t*>(model->final_norm);
   la.W = static_cast<const uint16_t*>(model->lm_head);
@@ -727,6 +739,26 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
   f.eos_id = cfg->eos_id; f.flags = flags & KMR_ADVANCE;
   hipLaunchKernelGGL(k_lm_finish, dim3(batch), dim3(256), 0, st, f);
   return check_hip("decode_step launch");
+}
+
+int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
+                    const int32_t* token_ids, int32_t* positions, int32_t* cache_position,
+                    uint8_t* finished, int32_t batch, int32_t* next_ids, float* logits,
+                    uint32_t flags, void* ws, size_t ws_bytes, kmr_stream_t stream) {
+  return decode_step(cfg, model, kv, token_ids, positions, cache_position, finished, batch, next_ids, logits,
+                     flags, ws, ws_bytes, stream, 0);
+}
+
+int kmr_decode_step_prefix(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
+                           const int32_t* token_ids, int32_t* positions, int32_t* cache_position,
+                           uint8_t* finished, int32_t batch, int32_t* next_ids, float* logits,
+                           uint32_t flags, int32_t shared_prefix, void* ws, size_t ws_bytes,
+                           kmr_stream_t stream) {
+  if (!kv) return fail(KMR_EINVAL, "kv is NULL");
+  if (shared_prefix < 0 || shared_prefix > kv->max_len)
+    return fail(KMR_EINVAL, "shared_prefix %d outside [0, max_len %d]", shared_prefix, kv->max_len);
+  return decode_step(cfg, model, kv, token_ids, positions, cache_position, finished, batch, next_ids, logits,
+                     flags | KMR_MULTI_KERNEL, ws, ws_bytes, stream, shared_prefix / kAttnSplitPP);
 }
 
 int kmr_kv_copy_row(const kmr_kv* dst, int32_t dst_row, const kmr_kv* src, int32_t src_row,

@@ -653,7 +653,7 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
     for (int e = 0; e < 4; ++e) acc[t][e] = 0.f;
 #pragma unroll
   for (int i = 0; i < kMfmaBlocksPerWave; ++i) {
-    if (i >= nbw) break;
+    if (i >= nbw) continue;   // (not break: the loop unrolls, w and sw stay in registers)
     const int kb = wave + 4 * i, c = 4 * kb + gq;
     uint4 xv[4];
 #pragma unroll
@@ -745,56 +745,35 @@ struct AttnArgs {
   uint32_t* status;
   int ldqkv, Hq, Hkv, M, NS;
   float eps, scale_log2;   // log2(e) / sqrt(D)
+  int B;                   // rows
+  int first_split;         // shared-prefix splits (0: none) ...
+  int prefix_row;          // ... and the cache row that holds the prefix
 };
 
+// The attention of split s of kv head g for batch row b (cache position c), given
+// this lane's K/V words of the split (kr, vr: positions s*kAttnSplitPP + 16 wave +
+// 4 it + lane/16, dims DPL*(lane%16) ..): q/k norm and RoPE of the row's new token,
+// its cache write (last split), the block softmax of each 16-lane row, the 16 row
+// states merged, and the split's partial stored.  Every thread of the group calls
+// this; it ends after the partial stores (a caller that calls it again must first
+// wait at a barrier).
 template <int D, int QPG>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+__device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int g, int s, int c,
+                                           const uint32_t (&kr)[kAttnSplitPP / 16][D / 32],
+                                           const uint32_t (&vr)[kAttnSplitPP / 16][D / 32],
+                                           float (&s_o)[16][QPG][D], float (&s_m)[16][QPG],
+                                           float (&s_l)[16][QPG], float (&s_w)[QPG][16],
+                                           float (&s_ML)[QPG][2]) {
   constexpr int DPL = D / 16;   // dims per lane
   constexpr int HALF = D / 2;
   constexpr int IT = kAttnSplitPP / 16;
-  __shared__ float s_o[16][QPG][D];
-  __shared__ float s_m[16][QPG];
-  __shared__ float s_l[16][QPG];
-
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rr = lane >> 4, li = lane & 15;
   const int row = wave * 4 + rr;    // 0..15
   const int d0 = li * DPL;
-  const int c = a.cpos[b];
+  const int ns = c / kAttnSplitPP + 1;
   const size_t head_base = ((size_t)b * a.Hkv + g) * a.M;   // in rows of D
   const size_t pidx = ((size_t)b * a.Hkv + g) * a.NS + s;   // partial slot
-
-  if (c < 0 || c >= a.M) {
-    if (s == 0) {   // zero attention for this row: partial (m, l, o~) = (0, 1, 0)
-      if (tid == 0 && g == 0) raise_status(a.status, 1u);
-      for (int i = tid; i < QPG * D; i += 256) a.part_o[pidx * QPG * D + i] = 0.f;
-      if (tid < QPG) a.part_ml[pidx * QPG + tid] = make_float2(0.f, 1.f);
-    }
-    return;
-  }
-  if (s * kAttnSplitPP > c) return;
-  const int ns = c / kAttnSplitPP + 1;
-
-  // ---- cache reads first
-  uint32_t kr[IT][DPL / 2], vr[IT][DPL / 2];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int p = s * kAttnSplitPP + wave * (kAttnSplitPP / 4) + it * 4 + rr;
-    if (p < c) {
-      const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kc + (head_base + p) * D + d0);
-      const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vc + (head_base + p) * D + d0);
-#pragma unroll
-      for (int e = 0; e < DPL / 2; ++e) {
-        kr[it][e] = ks[e];
-        vr[it][e] = vs[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < DPL / 2; ++e) kr[it][e] = vr[it][e] = 0u;
-    }
-  }
-
   // ---- prologue: q', k', v of the current token for this lane's dims
   const float* qrow = a.qkv + (size_t)b * a.ldqkv;
   float q[QPG][DPL], kf[DPL], vf[DPL];
@@ -919,7 +898,6 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   __syncthreads();
   // the log-sum-exp weight of each (row, head) once, by the first wave: lane
   // 16 h + r holds row r of head h (QPG <= 4); rows that saw nothing have m = -inf
-  __shared__ float s_w[QPG][16], s_ML[QPG][2];
   if (wave == 0) {
     const int h = lane >> 4, r = lane & 15;
     const float mr = h < QPG ? s_m[r][h] : -INFINITY;
@@ -945,6 +923,100 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     if (d == 0) a.part_ml[pidx * QPG + h] = make_float2(s_ML[h][0], s_ML[h][1]);
   }
 }
+
+// Shared-prefix (cascade) attention: the first a.first_split splits of every row
+// whose cache position is past them, when all rows hold the same K/V there (the
+// caller's promise; row a.prefix_row is read).  One work-group per (prefix split,
+// kv head, kPrefixRows rows) reads the split's K/V once and runs attn_split for each
+// such row, the same operations on the same values as k_attn would, so the partials
+// -- and the step's results -- are bit for bit those of the plain path; only the
+// prefix K/V reads shrink, by up to kPrefixRows.  (A separate launch: folded into
+// k_attn's grid, its code cost every plain work-group registers and occupancy.)
+constexpr int kPrefixRows = 4;
+template <int D, int QPG>
+__global__ __launch_bounds__(256) void k_attn_prefix(AttnArgs a) {
+  constexpr int DPL = D / 16;
+  constexpr int IT = kAttnSplitPP / 16;
+  __shared__ float s_o[16][QPG][D];
+  __shared__ float s_m[16][QPG];
+  __shared__ float s_l[16][QPG];
+  __shared__ float s_w[QPG][16], s_ML[QPG][2];
+  const int s = blockIdx.x, g = blockIdx.y, b0 = blockIdx.z * kPrefixRows;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, rr = lane >> 4, d0 = (lane & 15) * DPL;
+  const size_t head_base = ((size_t)a.prefix_row * a.Hkv + g) * a.M;
+  // every position of a prefix split lies before the cache position of the rows
+  // served here (c >= first_split * kAttnSplitPP), as k_attn's masked loads find
+  uint32_t kr[IT][DPL / 2], vr[IT][DPL / 2];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int p = s * kAttnSplitPP + wave * (kAttnSplitPP / 4) + it * 4 + rr;
+    const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kc + (head_base + p) * D + d0);
+    const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vc + (head_base + p) * D + d0);
+#pragma unroll
+    for (int e = 0; e < DPL / 2; ++e) {
+      kr[it][e] = ks[e];
+      vr[it][e] = vs[e];
+    }
+  }
+  const int b1 = b0 + kPrefixRows < a.B ? b0 + kPrefixRows : a.B;
+  for (int b = b0; b < b1; ++b) {
+    const int c = a.cpos[b];
+    if (c < a.first_split * kAttnSplitPP || c >= a.M) continue;   // (uniform in the group)
+    attn_split<D, QPG>(a, b, g, s, c, kr, vr, s_o, s_m, s_l, s_w, s_ML);
+    __syncthreads();   // s_o and the weights are rewritten for the next row
+  }
+}
+
+template <int D, int QPG>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+  constexpr int DPL = D / 16;   // dims per lane
+  constexpr int IT = kAttnSplitPP / 16;
+  __shared__ float s_o[16][QPG][D];
+  __shared__ float s_m[16][QPG];
+  __shared__ float s_l[16][QPG];
+  __shared__ float s_w[QPG][16], s_ML[QPG][2];
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rr = lane >> 4, li = lane & 15;
+  const int d0 = li * DPL;
+  const int c = a.cpos[b];
+  const size_t head_base = ((size_t)b * a.Hkv + g) * a.M;   // in rows of D
+  const size_t pidx = ((size_t)b * a.Hkv + g) * a.NS + s;   // partial slot
+
+  if (c < 0 || c >= a.M) {
+    if (s == 0) {   // zero attention for this row: partial (m, l, o~) = (0, 1, 0)
+      if (tid == 0 && g == 0) raise_status(a.status, 1u);
+      for (int i = tid; i < QPG * D; i += 256) a.part_o[pidx * QPG * D + i] = 0.f;
+      if (tid < QPG) a.part_ml[pidx * QPG + tid] = make_float2(0.f, 1.f);
+    }
+    return;
+  }
+  if (s * kAttnSplitPP > c) return;
+  // a split of the shared prefix of a row past it: k_attn_prefix writes its partial
+  if (s < a.first_split && c >= a.first_split * kAttnSplitPP) return;
+
+  // ---- cache reads first
+  uint32_t kr[IT][DPL / 2], vr[IT][DPL / 2];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int p = s * kAttnSplitPP + wave * (kAttnSplitPP / 4) + it * 4 + rr;
+    if (p < c) {
+      const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kc + (head_base + p) * D + d0);
+      const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vc + (head_base + p) * D + d0);
+#pragma unroll
+      for (int e = 0; e < DPL / 2; ++e) {
+        kr[it][e] = ks[e];
+        vr[it][e] = vs[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL / 2; ++e) kr[it][e] = vr[it][e] = 0u;
+    }
+  }
+  attn_split<D, QPG>(a, b, g, s, c, kr, vr, s_o, s_m, s_l, s_w, s_ML);
+}
+
 
 // ------------------------------------------------------------------ lm_head + argmax
 // logits[b][n] = sum_k W[n][k] h[b][k] with h = RMSNorm(x; final_norm), bf16 W

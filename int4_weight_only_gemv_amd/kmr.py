@@ -74,6 +74,8 @@ _lib.kmr_decode_layer.argtypes = [C.POINTER(Config), C.POINTER(Layer), _i32, C.P
                                   _p, _i32, _p, C.c_size_t, _p]
 _lib.kmr_decode_step.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(KV), _p, _p, _p, _p,
                                  _i32, _p, _p, C.c_uint32, _p, C.c_size_t, _p]
+_lib.kmr_decode_step_prefix.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(KV), _p, _p, _p, _p,
+                                        _i32, _p, _p, C.c_uint32, _i32, _p, C.c_size_t, _p]
 _lib.kmr_status.argtypes = [_p, _p, C.POINTER(C.c_uint32)]
 _lib.kmr_kv_copy_row.argtypes = [C.POINTER(KV), _i32, C.POINTER(KV), _i32, _i32, _p]
 _lib.kmr_slot_admit.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, C.POINTER(_i32), _i32, _p]
@@ -82,8 +84,8 @@ _lib.kmr_strerror.restype = C.c_char_p
 _lib.kmr_last_error.restype = C.c_char_p
 
 EXPORTED = ["kmr_kv_alloc", "kmr_kv_copy_row", "kmr_quantize_int4", "kmr_workspace_bytes",
-            "kmr_workspace_init", "kmr_decode_layer", "kmr_decode_step", "kmr_slot_admit",
-            "kmr_slot_retire", "kmr_status", "kmr_strerror", "kmr_last_error"]
+            "kmr_workspace_init", "kmr_decode_layer", "kmr_decode_step", "kmr_decode_step_prefix",
+            "kmr_slot_admit", "kmr_slot_retire", "kmr_status", "kmr_strerror", "kmr_last_error"]
 
 
 class KmrError(RuntimeError):
@@ -254,15 +256,18 @@ class DeviceModel:
                     cache_position: torch.Tensor, next_ids: torch.Tensor, ws: Workspace,
                     finished: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
                     advance: bool = False, multi_kernel: bool = False, device_wide: bool = False,
-                    stream=None) -> torch.Tensor:
+                    shared_prefix: int = 0, stream=None) -> torch.Tensor:
+        """shared_prefix > 0: kmr_decode_step_prefix (every row holds the same K/V in
+        cache positions [0, shared_prefix); the per-phase kernels read it once)."""
         B = token_ids.shape[0]
         assert token_ids.dtype == torch.int32 and next_ids.dtype == torch.int32
         assert finished is None or finished.dtype == torch.uint8
-        _check(_lib.kmr_decode_step(C.byref(self.cfg), C.byref(self.cmodel), C.byref(kv.desc),
-                                    _ptr(token_ids), _ptr(positions), _ptr(cache_position),
-                                    _ptr(finished), B, _ptr(next_ids), _ptr(logits),
-                                    (KMR_ADVANCE if advance else 0) | (KMR_MULTI_KERNEL if multi_kernel else 0)
-                                    | (KMR_DEVICE_WIDE if device_wide else 0),
-                                    ws.ptr, ws.nbytes,
-                                    _stream(stream)))
+        flags = ((KMR_ADVANCE if advance else 0) | (KMR_MULTI_KERNEL if multi_kernel else 0)
+                 | (KMR_DEVICE_WIDE if device_wide else 0))
+        args = (C.byref(self.cfg), C.byref(self.cmodel), C.byref(kv.desc), _ptr(token_ids), _ptr(positions),
+                _ptr(cache_position), _ptr(finished), B, _ptr(next_ids), _ptr(logits), flags)
+        if shared_prefix:
+            _check(_lib.kmr_decode_step_prefix(*args, shared_prefix, ws.ptr, ws.nbytes, _stream(stream)))
+        else:
+            _check(_lib.kmr_decode_step(*args, ws.ptr, ws.nbytes, _stream(stream)))
         return next_ids

@@ -382,6 +382,40 @@ def test_decode_step_tokens_without_logits_buffer(kmr, full_pair, batch):
     assert np.array_equal(got[0], got[1])
 
 
+@pytest.mark.parametrize("batch", [6, 16])
+def test_shared_prefix_step_equals_plain_step(kmr, full_pair, batch):
+    """kmr_decode_step_prefix (the prefix's K/V read once for all rows) gives the bits
+    of the plain per-phase step when the rows share that K/V: tokens, logits and the
+    whole cache.  Row 0 sits exactly at the end of the prefix, row 1 inside it (it
+    keeps the plain path), the others past it."""
+    dims, M, P = full_pair.dims, 1024, 512
+    log(f"decode_step batch {batch}: shared prefix of {P} positions vs the plain per-phase step")
+    rng = np.random.default_rng(9000 + batch)
+    cpos = rng.integers(P, M - 1, batch).astype(np.int32)
+    cpos[0], cpos[1] = P, 100
+    ids = rng.integers(0, dims.vocab, batch).astype(np.int32)
+    pos = np.stack([cpos, cpos // 2, cpos // 3]).astype(np.int32)
+    got = []
+    for prefix in (0, P):
+        kv, _, _ = make_caches(dims, synth.base_seed(synth.WORKLOADS["step"]), batch, M, "device", host_rows=[])
+        kv.k[:, :, :, :P] = kv.k[:, 0:1, :, :P].clone()   # [L][B][Hkv][M][D]: every row holds row 0's prefix
+        kv.v[:, :, :, :P] = kv.v[:, 0:1, :, :P].clone()
+        ws = kmr.Workspace(full_pair.dev.cfg, batch, M)
+        nxt = torch.zeros(batch, dtype=torch.int32, device="cuda")
+        logits = torch.empty((batch, dims.vocab), dtype=torch.float32, device="cuda")
+        full_pair.dev.decode_step(kv, torch.from_numpy(ids).cuda(), torch.from_numpy(pos).cuda(),
+                                  torch.from_numpy(cpos).cuda(), nxt, ws, logits=logits, multi_kernel=True,
+                                  shared_prefix=prefix)
+        torch.cuda.synchronize()
+        assert ws.status() == 0
+        got.append((nxt.cpu(), logits.cpu(), kv.k.clone(), kv.v.clone()))
+        del kv
+    (n0, l0, k0, v0), (n1, l1, k1, v1) = got
+    log(f"  tokens {n0.tolist()} vs {n1.tolist()}; logits bitwise equal {torch.equal(l0, l1)}")
+    assert torch.equal(n0, n1) and torch.equal(l0, l1)
+    assert torch.equal(k0, k1) and torch.equal(v0, v1)
+
+
 # ------------------------------------------------------------------ error paths
 
 def test_out_of_range_cache_position_sets_status_and_writes_nothing(kmr):
