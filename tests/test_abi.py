@@ -125,6 +125,21 @@ def test_bad_calls_are_rejected_before_launch(kmr):
     assert kmr._lib.kmr_strerror(kmr.KMR_ENOMEM) == b"buffer or workspace too small"
 
 
+def test_bad_shared_prefix_is_rejected_before_launch(kmr):
+    import ctypes as C
+    cfg = _cfg(kmr)
+    kv = kmr.KV()
+    kv.max_len = 1024
+    fake = C.c_void_p(0x1000)
+    model = kmr.Model()
+    for bad in (-1, 1025):
+        rc = kmr._lib.kmr_decode_step_prefix(C.byref(cfg), C.byref(model), C.byref(kv), fake, fake, fake, None,
+                                             4, fake, None, 0, bad, fake, 1 << 30, None)
+        assert rc == kmr.KMR_EINVAL and b"shared_prefix" in kmr._lib.kmr_last_error()
+    assert kmr._lib.kmr_decode_step_prefix(C.byref(cfg), C.byref(model), None, fake, fake, fake, None, 4, fake,
+                                           None, 0, 0, fake, 1 << 30, None) == kmr.KMR_EINVAL
+
+
 def test_bad_slot_calls_are_rejected_before_launch(kmr):
     import ctypes as C
     fake = C.c_void_p(0x1000)
