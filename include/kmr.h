@@ -60,9 +60,10 @@ enum {
   KMR_STATUS_TIMEOUT = 4u,    /* a wait inside the persistent step kernel gave up
                                  (no progress for ~1 s): outputs of that call are
                                  invalid; re-initialise the workspace */
-  KMR_STATUS_TOPOLOGY = 8u    /* a work-group of the XCD-local step kernel found itself
-                                 on another XCD than the placement probe reported
-                                 (diagnostic; such a call may also time out) */
+  KMR_STATUS_TOPOLOGY = 8u    /* a work-group of the XCD-local step kernel read an XCD
+                                 id above 7 or found more groups on its XCD than the
+                                 grid deals to one (diagnostic; such a call may also
+                                 time out) */
 };
 
 #define KMR_MAX_BATCH 64
@@ -71,6 +72,12 @@ enum {
                                 single persistent kernel (diagnostics, cross-checks) */
 #define KMR_DEVICE_WIDE 4u   /* persistent kernel with every hand-off device-wide,
                                 instead of the XCD-local one (diagnostics, cross-checks) */
+#define KMR_COOPERATIVE 8u   /* launch the persistent kernel with hipLaunchCooperativeKernel,
+                                whose runtime guarantees that all its work-groups run at
+                                once, instead of a plain launch after a host occupancy
+                                check (~20 us more per step; for callers that run other
+                                long kernels on the device concurrently).  Ignored on the
+                                per-phase path. */
 
 /*
  * Model dimensions.  Supported by the kernels: head_dim 64 or 128;
@@ -192,8 +199,10 @@ int kmr_decode_layer(const kmr_config* cfg, const kmr_layer* layer_w, int32_t la
  * once) if no kmr_workspace_init ran on that device; under stream capture the
  * probe is skipped and the kernel keeps every hand-off device-wide.
  * Paths: batch <= 4 with the model shapes the persistent kernels cover runs as one
- * cooperative launch (XCD-local hand-offs when n_kv_heads is a multiple of 8, else
- * or with KMR_DEVICE_WIDE device-wide ones); otherwise, or with KMR_MULTI_KERNEL,
+ * launch of a persistent kernel (XCD-local hand-offs when n_kv_heads is a multiple of
+ * 8, else or with KMR_DEVICE_WIDE device-wide ones; its work-groups wait on each other
+ * with bounded waits, so other work that holds CUs for longer than ~1 s ends the call
+ * with KMR_STATUS_TIMEOUT unless KMR_COOPERATIVE is set); otherwise, or with KMR_MULTI_KERNEL,
  * as one kernel per phase, in batch tiles of at most 16 rows (batch up to
  * KMR_MAX_BATCH).  A tile of 9..16 rows takes the matrix-core int4 GEMV when the
  * group size is a multiple of 128, and the matrix-core lm_head when hidden is

@@ -443,9 +443,11 @@ __global__ void k_xcc_probe(uint32_t* out) {
   if (threadIdx.x == 0) out[blockIdx.x] = __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u;
 }
 
-// Whether work-group g of a one-group-per-CU grid runs on XCD g % 8 on the current
-// device: probed once per device (a small kernel on `st`, a synchronous copy of
-// nwg words through `scratch`), then cached.  Not probed while `st` is capturing.
+// Whether the XCC id register of the current device names 8 XCDs that receive the
+// groups of a grid in turn (group g on XCD (s + g) % 8 for some s: the dispatcher's
+// starting XCD moves with the groups of earlier dispatches): probed once per device
+// (a small kernel on `st`, a synchronous copy of nwg words through `scratch`), then
+// cached.  Not probed while `st` is capturing.
 std::atomic<int> g_topology[64];   // 0 unknown, 1 verified, 2 other placement
 
 bool xcd_placement_ok(void* scratch, size_t scratch_bytes, int nwg, hipStream_t st) {
@@ -463,7 +465,7 @@ bool xcd_placement_ok(void* scratch, size_t scratch_bytes, int nwg, hipStream_t 
       hipStreamSynchronize(st) != hipSuccess)
     return false;
   bool ok = nwg % kXcds == 0;
-  for (int g = 0; g < nwg && ok; ++g) ok = (int)(ids[g] % kXcds) == g % kXcds;
+  for (int g = 0; g < nwg && ok; ++g) ok = ids[g] < (uint32_t)kXcds && (int)ids[g] == ((int)ids[0] + g) % kXcds;
   g_topology[dev].store(ok ? 1 : 2);
   return ok;
 }
@@ -477,24 +479,45 @@ int device_cus(int* cus) {
   return KMR_OK;
 }
 
-template <int BT, int D>
-int launch_step_k(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
-  const int KMAX = std::max(c->hidden, std::max(c->intermediate, c->n_heads * c->head_dim));
-  const int RPBX = (c->hidden + nwg - 1) / nwg;
-  const size_t lds = step_lds(BT, KMAX, RPBX, c->hidden, D, 2).total;
-  auto fn = k_step<BT, D, 2>;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) != hipSuccess)
+// Launches a persistent step kernel: nwg groups that hand work to each other, so all
+// of them must be resident at once.  The default is a plain launch after checking that
+// the device holds nwg groups of this LDS size at once; on an otherwise idle device
+// every group then starts at launch.  Work from other streams or processes can hold
+// groups back, which delays the step, and past the bounded hand-off waits (~1 s) ends
+// it with KMR_STATUS_TIMEOUT; nothing waits on this kernel, so it cannot deadlock.
+// coop asks the runtime for the co-residency guarantee (hipLaunchCooperativeKernel)
+// instead, which costs ~20 us more per launch on gfx950.
+int launch_persistent(const void* fn, int nwg, size_t lds, StepArgs& a, bool coop, hipStream_t st) {
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return check_hip("step kernel LDS attribute");
   void* args[] = {&a};
-  if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(nwg), dim3(kStepThreads),
-                                 args, (unsigned)lds, st) != hipSuccess)
-    return check_hip("step kernel cooperative launch");
+  if (coop) {
+    if (hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(kStepThreads), args, (unsigned)lds, st) != hipSuccess)
+      return check_hip("step kernel cooperative launch");
+    return KMR_OK;
+  }
+  int per_cu = 0, cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStepThreads, lds) != hipSuccess)
+    return check_hip("step kernel occupancy");
+  if ((long)per_cu * cus < nwg)
+    return fail(KMR_EHIP, "step kernel: %d groups do not fit at once (%d per CU, %d CUs)", nwg, per_cu, cus);
+  if (hipLaunchKernel(fn, dim3(nwg), dim3(kStepThreads), args, lds, st) != hipSuccess)
+    return check_hip("step kernel launch");
   return KMR_OK;
 }
 
 template <int BT, int D>
-int launch_stepx_k(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
+int launch_step_k(const kmr_config* c, StepArgs& a, int nwg, bool coop, hipStream_t st) {
+  const int KMAX = std::max(c->hidden, std::max(c->intermediate, c->n_heads * c->head_dim));
+  const int RPBX = (c->hidden + nwg - 1) / nwg;
+  const size_t lds = step_lds(BT, KMAX, RPBX, c->hidden, D, 2).total;
+  return launch_persistent(reinterpret_cast<const void*>(k_step<BT, D, 2>), nwg, lds, a, coop, st);
+}
+
+template <int BT, int D>
+int launch_stepx_k(const kmr_config* c, StepArgs& a, int nwg, bool coop, hipStream_t st) {
   const int WPX = nwg / kXcds, RPW = (c->hidden + WPX - 1) / WPX;
   const size_t lds = stepx_lds(BT, c->hidden, RPW, D, 2, c->n_kv_heads / kXcds).total;
   // the constant-size instantiation for the shape it was compiled for
@@ -504,26 +527,21 @@ int launch_stepx_k(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
         c->intermediate == kFixI && c->group_size == (1 << kFixLgG) && nwg == kFixNwg)
       fn = k_stepx<BT, D, 2, true>;
   }
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) != hipSuccess)
-    return check_hip("XCD step kernel LDS attribute");
-  void* args[] = {&a};
-  if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(nwg), dim3(kStepThreads),
-                                 args, (unsigned)lds, st) != hipSuccess)
-    return check_hip("XCD step kernel cooperative launch");
-  return KMR_OK;
+  return launch_persistent(reinterpret_cast<const void*>(fn), nwg, lds, a, coop, st);
 }
 
-int launch_stepx(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
+int launch_stepx(const kmr_config* c, StepArgs& a, int nwg, bool coop, hipStream_t st) {
   const int B = a.B;
-  if (c->head_dim == 128) return B == 1 ? launch_stepx_k<1, 128>(c, a, nwg, st) : launch_stepx_k<4, 128>(c, a, nwg, st);
-  return B == 1 ? launch_stepx_k<1, 64>(c, a, nwg, st) : launch_stepx_k<4, 64>(c, a, nwg, st);
+  if (c->head_dim == 128)
+    return B == 1 ? launch_stepx_k<1, 128>(c, a, nwg, coop, st) : launch_stepx_k<4, 128>(c, a, nwg, coop, st);
+  return B == 1 ? launch_stepx_k<1, 64>(c, a, nwg, coop, st) : launch_stepx_k<4, 64>(c, a, nwg, coop, st);
 }
 
-int launch_step(const kmr_config* c, StepArgs& a, int nwg, hipStream_t st) {
+int launch_step(const kmr_config* c, StepArgs& a, int nwg, bool coop, hipStream_t st) {
   const int B = a.B;
-  if (c->head_dim == 128) return B == 1 ? launch_step_k<1, 128>(c, a, nwg, st) : launch_step_k<4, 128>(c, a, nwg, st);
-  return B == 1 ? launch_step_k<1, 64>(c, a, nwg, st) : launch_step_k<4, 64>(c, a, nwg, st);
+  if (c->head_dim == 128)
+    return B == 1 ? launch_step_k<1, 128>(c, a, nwg, coop, st) : launch_step_k<4, 128>(c, a, nwg, coop, st);
+  return B == 1 ? launch_step_k<1, 64>(c, a, nwg, coop, st) : launch_step_k<4, 64>(c, a, nwg, coop, st);
 }
 
 void enqueue_prep(const kmr_config* c, const uint16_t* embed, const int32_t* ids,
@@ -664,7 +682,7 @@ static int decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_
   if (kv->n_layers != cfg->n_layers) return fail(KMR_ESHAPE, "kv cache has %d layers, model %d", kv->n_layers, cfg->n_layers);
   if (!token_ids || !positions || !cache_position || !next_ids || !ws)
     return fail(KMR_EINVAL, "null token_ids/positions/cache_position/next_ids/workspace");
-  if (flags & ~(KMR_ADVANCE | KMR_MULTI_KERNEL | KMR_DEVICE_WIDE)) return fail(KMR_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(KMR_ADVANCE | KMR_MULTI_KERNEL | KMR_DEVICE_WIDE | KMR_COOPERATIVE)) return fail(KMR_EINVAL, "unknown flags 0x%x", flags);
   const WsLayout w = ws_layout(cfg, batch, kv->max_len);
   if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -680,6 +698,7 @@ static int decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_
     a.kc = static_cast<uint16_t*>(kv->k); a.vc = static_cast<uint16_t*>(kv->v);
     a.status = at<uint32_t>(ws, w.status); a.step_ctr = at<uint32_t>(ws, w.step_ctr);
     a.lm_cnt = at<uint32_t>(ws, w.lm_cnt);
+    a.xarr = a.lm_cnt + 32;   // 8 counters, 128 bytes past lm_cnt in its 256-byte block
     a.tx = at<uint64_t>(ws, w.tx); a.tqkv = at<uint64_t>(ws, w.tqkv);
     a.to = at<uint64_t>(ws, w.to); a.tact = at<uint64_t>(ws, w.tact);
     a.tpart = at<uint64_t>(ws, w.tpart);
@@ -717,9 +736,9 @@ static int decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_
     }
     if (!(flags & KMR_DEVICE_WIDE) && stepx_fits(cfg, batch, nwg)) {
       a.intra_plain = xcd_placement_ok(at<void>(ws, w.probe), (size_t)kMaxStepGroups * 4, nwg, st) ? 1 : 0;
-      return launch_stepx(cfg, a, nwg, st);
+      return launch_stepx(cfg, a, nwg, (flags & KMR_COOPERATIVE) != 0, st);
     }
-    return launch_step(cfg, a, nwg, st);
+    return launch_step(cfg, a, nwg, (flags & KMR_COOPERATIVE) != 0, st);
   }
   float* x = at<float>(ws, w.x);
   enqueue_prep(cfg, static_cast<const uint16_t*>(model->embed), token_ids, finished, positions, x,

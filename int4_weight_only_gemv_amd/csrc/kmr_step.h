@@ -75,6 +75,7 @@ struct StepArgs {
   uint32_t* status;
   uint32_t* step_ctr;
   uint32_t* lm_cnt;
+  uint32_t* xarr;           // [8] per-XCD arrival counters of the XCD-local kernel
   uint64_t* tx;             // [B][H]       tagged residual stream
   uint64_t* tqkv;           // [B][NQKV]
   uint64_t* to;             // [B][Hq*D]    attention output

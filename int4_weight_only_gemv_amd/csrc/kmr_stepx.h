@@ -3,10 +3,10 @@
 // Same computation as k_step (kaminari page, section 04 "3 . decode": one greedy
 // token per row from fixed-rank inputs and the static KV buffers), arranged
 // around the chip's 8 XCDs instead of treating the 256 work-groups as one pool.
-// Work-group g runs on XCD g % 8 (checked on the host before this kernel is
-// chosen, and again by every group, which raises a status bit on a mismatch);
-// the 32 groups of one XCD share its L2, where a hand-off costs about half of a
-// device-wide one.  Per layer, with XCD x owning kv heads [x*GPX, (x+1)*GPX) and
+// Each work-group reads its XCD from the hardware and takes its index among that
+// XCD's 32 groups from a per-XCD arrival counter, so the arrangement holds however
+// the dispatcher deals the groups out; the 32 groups of one XCD share its L2, where
+// a hand-off costs about half of a device-wide one.  Per layer, with XCD x owning kv heads [x*GPX, (x+1)*GPX) and
 // the intermediate slice [x*IX, (x+1)*IX):
 //   QKV      every XCD holds the whole residual stream x; its groups compute the
 //            q/k/v rows of its own kv heads                       (XCD-local)
@@ -28,7 +28,7 @@
 
 namespace kmr {
 
-constexpr int kXcds = 8;            // XCDs of the device; group g runs on XCD g % 8
+constexpr int kXcds = 8;            // XCDs of the device
 constexpr int kXSplit = 128;        // attention positions per split item
 constexpr int kXMergeChunk = 8;     // split partials merged per LDS pass
 constexpr int kXNarrowCpl = 3;      // max 32-column chunks per lane in the split-K GEMVs
@@ -571,8 +571,22 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int DPL = D / 16, HALF = D / 2, PW = QPG * (D + 2);
   const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wg = blockIdx.x, nwg = FIXED ? kFixNwg : (int)gridDim.x;
-  const int x = wg % kXcds, j = wg / kXcds, WPX = nwg / kXcds;
+  const int nwg = FIXED ? kFixNwg : (int)gridDim.x, WPX = nwg / kXcds;
+  // The group's XCD is read from the hardware, and its index among that XCD's groups
+  // is taken from an arrival counter that wraps at WPX.  The dispatcher deals the
+  // groups out over the XCDs in turn, but not always starting at XCD 0, so every XCD
+  // receives WPX of them and the indices of one launch are a permutation of
+  // 0..WPX-1 on each XCD.
+  __shared__ int s_xj;
+  if (tid == 0) {
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u;
+    const uint32_t k = atomicInc(a.xarr + xcc % kXcds, (unsigned)(WPX - 1));
+    if (xcc >= (uint32_t)kXcds || k >= (uint32_t)WPX) raise_status(a.status, kStatusTopology);
+    s_xj = (int)(xcc % kXcds) | (int)(k < (uint32_t)WPX ? k : 0u) << 4;
+  }
+  __syncthreads();
+  const int xj = __builtin_amdgcn_readfirstlane(s_xj);
+  const int x = xj & 15, j = xj >> 4;
   const int B = BT == 1 ? 1 : a.B;   // (a batch-1 instantiation runs only at B == 1)
   const int H = FIXED ? kFixH : a.H, Hkv = FIXED ? kFixHkv : a.Hkv, Hq = FIXED ? kFixHkv * QPG : a.Hq;
   const int I = FIXED ? kFixI : a.I, M = a.M, lgG = FIXED ? kFixLgG : a.lgG;
@@ -608,16 +622,12 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   auto tag = [&](int phase) -> uint32_t { return (step << 9) | (uint32_t)phase; };
   bool alive = true;
 
-  // ---- step prologue: placement check, cache positions, RoPE tables, embedding
-  if (tid == 0 && plain) {
-    const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u;
-    if ((int)(xcc % kXcds) != x) raise_status(a.status, kStatusTopology);
-  }
+  // ---- step prologue: cache positions, RoPE tables, embedding
   if (tid < B) {
     const int c = a.cpos[tid];
     s_c[tid] = c;
     s_ns[tid] = (c >= 0 && c < M) ? (c + kXSplit) / kXSplit : 0;
-    if (wg == 0 && (c < 0 || c >= M)) raise_status(a.status, 1u);
+    if (blockIdx.x == 0 && (c < 0 || c >= M)) raise_status(a.status, 1u);
   }
   for (int i = tid; i < B * HALF; i += kStepThreads) {
     const int b = i / HALF, jj = i - b * HALF;

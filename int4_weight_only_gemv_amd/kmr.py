@@ -36,6 +36,7 @@ KMR_MAX_BATCH = 64
 KMR_ADVANCE = 1
 KMR_MULTI_KERNEL = 2
 KMR_DEVICE_WIDE = 4
+KMR_COOPERATIVE = 8
 
 _i32, _p = C.c_int32, C.c_void_p
 
@@ -256,14 +257,14 @@ class DeviceModel:
                     cache_position: torch.Tensor, next_ids: torch.Tensor, ws: Workspace,
                     finished: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
                     advance: bool = False, multi_kernel: bool = False, device_wide: bool = False,
-                    shared_prefix: int = 0, stream=None) -> torch.Tensor:
+                    cooperative: bool = False, shared_prefix: int = 0, stream=None) -> torch.Tensor:
         """shared_prefix > 0: kmr_decode_step_prefix (every row holds the same K/V in
         cache positions [0, shared_prefix); the per-phase kernels read it once)."""
         B = token_ids.shape[0]
         assert token_ids.dtype == torch.int32 and next_ids.dtype == torch.int32
         assert finished is None or finished.dtype == torch.uint8
         flags = ((KMR_ADVANCE if advance else 0) | (KMR_MULTI_KERNEL if multi_kernel else 0)
-                 | (KMR_DEVICE_WIDE if device_wide else 0))
+                 | (KMR_DEVICE_WIDE if device_wide else 0) | (KMR_COOPERATIVE if cooperative else 0))
         args = (C.byref(self.cfg), C.byref(self.cmodel), C.byref(kv.desc), _ptr(token_ids), _ptr(positions),
                 _ptr(cache_position), _ptr(finished), B, _ptr(next_ids), _ptr(logits), flags)
         if shared_prefix:

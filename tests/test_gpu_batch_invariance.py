@@ -48,7 +48,7 @@ def _run_model(kmr, dev, vocab, kv, ids, pos, cpos, fin, path):
     dev.decode_step(kv, torch.from_numpy(ids).cuda(), torch.from_numpy(pos).cuda(),
                          torch.from_numpy(cpos).cuda(), nxt, ws, finished=torch.from_numpy(fin).cuda(),
                          logits=logits, multi_kernel=(path == "multi_kernel"),
-                         device_wide=(path == "device_wide"))
+                         device_wide=(path == "device_wide"), cooperative=(path == "cooperative"))
     torch.cuda.synchronize()
     assert ws.status() == 0
     return nxt.cpu().numpy(), logits.cpu()
@@ -109,3 +109,11 @@ def test_row_alone_equals_row_in_batch_full_size(kmr):
         assert same
         assert next1[0] == next4[r]
         assert torch.equal(kv1.k[:, 0], kv4.k[:, r]) and torch.equal(kv1.v[:, 0], kv4.v[:, r])
+    # the same batch under the runtime's cooperative launch: same kernel, same bits
+    kvc = kmr.KVCache(dev.cfg, 4, M, zero=True)
+    kvc.k.copy_(base_k)
+    kvc.v.copy_(base_v)
+    nextc, logitsc = _run_model(kmr, dev, dims.vocab, kvc, ids, pos, cpos, fin, "cooperative")
+    log(f"  cooperative launch: logits bitwise equal to the plain launch: {torch.equal(logitsc, logits4)}")
+    assert torch.equal(logitsc, logits4) and np.array_equal(nextc, next4)
+    assert torch.equal(kvc.k, kv4.k) and torch.equal(kvc.v, kv4.v)

@@ -152,11 +152,12 @@ def _check_step(got_next, got_logits, ref, label):
     assert np.all(agree | ~decisive)
 
 
-PATHS = ["persistent", "device_wide", "multi_kernel"]
+PATHS = ["persistent", "cooperative", "device_wide", "multi_kernel"]
 
 
 def _path_flags(path):
-    return {"multi_kernel": path == "multi_kernel", "device_wide": path == "device_wide"}
+    return {"multi_kernel": path == "multi_kernel", "device_wide": path == "device_wide",
+            "cooperative": path == "cooperative"}
 
 
 def _step_case(kmr, pair, kv, kh, vh, inp, M, steps=1, advance=False, path="persistent"):
