@@ -235,6 +235,30 @@ int kmr_decode_step_prefix(const kmr_config* cfg, const kmr_model* model, const 
                            kmr_stream_t stream);
 
 /*
+ * kmr_prefill -- the prompt of one sequence through the decoder (kaminari page,
+ * section 04: the prompt's forward fills the static cache, and the first generated
+ * token is the argmax of the logits at the last prompt token).
+ * token_ids [n_tokens] and positions [3][n_tokens] (t, h, w axis-major, int32) are
+ * device arrays; token i takes cache position start + i of cache row `row`, so the
+ * call writes that row's K/V slots [start, start + n_tokens) in every layer and
+ * reads its slots [0, start) as an earlier part of the same sequence.  Each token
+ * attends causally to the slots up to its own.  No other slot or row is touched.
+ * next_id [1] receives the argmax at the last token; logits [vocab] fp32 receives
+ * that token's logits if not NULL.
+ * The tokens run in chunks of at most KMR_MAX_BATCH through the per-phase kernels
+ * (every projection of a chunk as one batch; the attention of a chunk in two
+ * passes, the new K/V slots of every token first, then the attention itself).
+ * ws must hold kmr_workspace_bytes(cfg, min(n_tokens, KMR_MAX_BATCH), max_len)
+ * bytes and have been initialised once.  Returns KMR_EINVAL for a row outside the
+ * cache, n_tokens < 1, or start + n_tokens > max_len, before anything is launched;
+ * token ids outside [0, vocab) raise KMR_STATUS_TOKEN as in kmr_decode_step.
+ * Nothing is synchronised.
+ */
+int kmr_prefill(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv, int32_t row,
+                const int32_t* token_ids, const int32_t* positions, int32_t start, int32_t n_tokens,
+                int32_t* next_id, float* logits, void* ws, size_t ws_bytes, kmr_stream_t stream);
+
+/*
  * Slot operations of a continuous-batching scheduler (kaminari section 08: the
  * ContinuousBatchScheduler admits requests into free DecodeSlots, each pinned to a
  * physical row of one shared static cache, ticks the active slots one token at a

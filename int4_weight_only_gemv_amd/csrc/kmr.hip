@@ -74,7 +74,7 @@ constexpr int kMaxStepGroups = 1024;   // lm_head partial slots of the persisten
 struct WsLayout {
   size_t status, cs, x, qkv, attn_o, act, part_o, part_ml, lm_part, total;
   size_t step_ctr, lm_cnt, tx, tqkv, to, tact, tpart, lm_part2;
-  size_t lx, sx, lqkv, lpart, lact, pO, pD, probe;
+  size_t lx, sx, lqkv, lpart, lact, pO, pD, probe, pf;
   size_t xst, xst_cc, xst_cb;   // staged 16-row GEMV tile: [16][4][Kmax/32] x 16 B, [16][Kmax/32] x 8 B,
                                 // [16][Kmax/128] x 8 B
   StepXSizes xz;
@@ -124,6 +124,7 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
   w.pO = o; o += align256((size_t)kXcds * B * c->hidden * 8);
   w.pD = o; o += align256((size_t)kXcds * B * c->hidden * 8);
   w.probe = o; o += align256((size_t)kMaxStepGroups * 4);
+  w.pf = o; o += align256((size_t)4 * KMR_MAX_BATCH * 4);   // prefill: a chunk's [3][C] positions, [C] cache positions
   w.total = o;
   return w;
 }
@@ -335,9 +336,12 @@ bool fuse_attn_merge(int B, int ns) { return (size_t)B * ns <= 16; }
 
 // One decoder layer on x (fp32 [B][H]) using workspace buffers; the RoPE table
 // must already be in ws.cs.
+// fixed_row > 0: every row is a token of one prompt held in cache row fixed_row - 1
+// at its own cache position; the new slots of all rows are written before any row
+// attends (two attention passes), so that each token sees the ones before it.
 void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr_kv* kv, float* x,
                    const int32_t* cpos, int B, void* ws, const WsLayout& w, hipStream_t st,
-                   int prefix_splits = 0) {
+                   int prefix_splits = 0, int fixed_row = 0) {
   const int H = c->hidden, D = c->head_dim, Hq = c->n_heads, Hkv = c->n_kv_heads;
   const int nqkv = (Hq + 2 * Hkv) * D, I = c->intermediate, G = c->group_size;
   float* qkv = at<float>(ws, w.qkv);
@@ -369,6 +373,12 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   a.Hq = Hq; a.Hkv = Hkv; a.M = kv->max_len; a.NS = w.ns_pp; a.eps = c->rms_eps;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   a.B = B; a.first_split = prefix_splits; a.prefix_row = 0;
+  a.fixed_row = fixed_row;
+  if (fixed_row) {
+    a.write_mode = 1;
+    launch_attn(c, a, B, st);
+    a.write_mode = 2;
+  }
   launch_attn(c, a, B, st);
 
   AttnPart ap{};
@@ -778,6 +788,54 @@ int kmr_decode_step_prefix(const kmr_config* cfg, const kmr_model* model, const 
     return fail(KMR_EINVAL, "shared_prefix %d outside [0, max_len %d]", shared_prefix, kv->max_len);
   return decode_step(cfg, model, kv, token_ids, positions, cache_position, finished, batch, next_ids, logits,
                      flags | KMR_MULTI_KERNEL, ws, ws_bytes, stream, shared_prefix / kAttnSplitPP);
+}
+
+int kmr_prefill(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv, int32_t row,
+                const int32_t* token_ids, const int32_t* positions, int32_t start, int32_t n_tokens,
+                int32_t* next_id, float* logits, void* ws, size_t ws_bytes, kmr_stream_t stream) {
+  int rc;
+  if ((rc = check_config(cfg))) return rc;
+  if (cfg->vocab <= 0) return fail(KMR_EINVAL, "vocab must be positive for a prefill");
+  if (!kv) return fail(KMR_EINVAL, "kv cache is NULL");
+  if (row < 0 || row >= kv->batch) return fail(KMR_EINVAL, "cache row %d out of [0, %d)", row, kv->batch);
+  if (n_tokens <= 0 || start < 0 || (long long)start + n_tokens > kv->max_len)
+    return fail(KMR_EINVAL, "tokens [%d, %lld) outside the cache [0, %d)", start, (long long)start + n_tokens,
+                kv->max_len);
+  if ((rc = check_kv(cfg, kv, 1))) return rc;
+  if (kv->n_layers != cfg->n_layers) return fail(KMR_ESHAPE, "kv cache has %d layers, model %d", kv->n_layers, cfg->n_layers);
+  if (!model || !model->embed || !model->final_norm || !model->lm_head || !model->layers)
+    return fail(KMR_EINVAL, "model pointers are NULL");
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if ((rc = check_layer(cfg, &model->layers[l]))) return fail(rc, "layer %d: %s", l, g_err);
+  if (!token_ids || !positions || !next_id || !ws)
+    return fail(KMR_EINVAL, "null token_ids/positions/next_id/workspace");
+  const int C = n_tokens < KMR_MAX_BATCH ? n_tokens : KMR_MAX_BATCH;
+  const WsLayout w = ws_layout(cfg, C, kv->max_len);
+  if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* x = at<float>(ws, w.x);
+  int32_t* pos_c = at<int32_t>(ws, w.pf);
+  int32_t* cpos_c = pos_c + 3 * KMR_MAX_BATCH;
+  int n = 0;
+  for (int t0 = 0; t0 < n_tokens; t0 += n) {
+    n = n_tokens - t0 < C ? n_tokens - t0 : C;
+    hipLaunchKernelGGL(k_prefill_rows, dim3(1), dim3(64), 0, st, positions, n_tokens, t0, n, start, pos_c, cpos_c);
+    enqueue_prep(cfg, static_cast<const uint16_t*>(model->embed), token_ids + t0, nullptr, pos_c, x, n, ws, w, st);
+    for (int l = 0; l < cfg->n_layers; ++l)
+      enqueue_layer(cfg, &model->layers[l], l, kv, x, cpos_c, n, ws, w, st, 0, row + 1);
+  }
+  // the next token from the last prompt token only
+  LmArgs la{};
+  la.x = x + (size_t)(n - 1) * cfg->hidden; la.gain = static_cast<const uint16_t*>(model->final_norm);
+  la.W = static_cast<const uint16_t*>(model->lm_head);
+  la.logits = logits; la.part = at<float2>(ws, w.lm_part);
+  la.V = cfg->vocab; la.K = cfg->hidden; la.B = 1; la.nblk = w.nblk_lm; la.eps = cfg->rms_eps;
+  launch_lmhead(la, st);
+  LmFinishArgs f{};
+  f.part = la.part; f.next = next_id; f.cpos = cpos_c; f.pos = pos_c;
+  f.B = 1; f.nblk = w.nblk_lm; f.M = kv->max_len; f.pad_id = cfg->pad_id; f.eos_id = cfg->eos_id; f.flags = 0;
+  hipLaunchKernelGGL(k_lm_finish, dim3(1), dim3(256), 0, st, f);
+  return check_hip("prefill launch");
 }
 
 int kmr_kv_copy_row(const kmr_kv* dst, int32_t dst_row, const kmr_kv* src, int32_t src_row,

@@ -658,33 +658,40 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
     uint4 xv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) xv[q] = xs[(bn * 4 + q) * CH + c];
-    // the block's constants of batch rows 4 gq + e
-    float C1[4], C2[4];
+    // the block's input sums of batch rows 4 gq + e
+    float C2[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int b = 4 * gq + e < BT ? 4 * gq + e : 0;
       if constexpr (GS) {
-        const float2 cb = a.cbg[b * NB + kb];
-        C1[e] = cb.x;
-        C2[e] = cb.y;
+        C2[e] = a.cbg[b * NB + kb].y;
       } else {
         const float2* cp = cc + b * CH + 4 * kb;
-        const float2 c0 = cp[0], c1 = cp[1], c2 = cp[2], c3 = cp[3];
-        C1[e] = (c0.x + c1.x) + (c2.x + c3.x);
-        C2[e] = (c0.y + c1.y) + (c2.y + c3.y);
+        C2[e] = (cp[0].y + cp[1].y) + (cp[2].y + cp[3].y);
       }
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       uint32_t p[16];
       dequant16(w[t][i], p);
+      // the bias off before the product: even words 1024 + q -> q - 8, odd words
+      // 1024 + 16 q -> 16 (q - 8), all exact in fp16.  The matrix core then never
+      // sums the 1024-sized terms whose cancellation against the block constant
+      // lost ~1e-3 of the result (the VALU path's fp32 sums do not).
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const half2_t h = __builtin_bit_cast(half2_t, p[j]);
+        const _Float16 off = (j & 1) ? (_Float16)1152.0f : (_Float16)1032.0f;
+        p[j] = __builtin_bit_cast(uint32_t, half2_t{h[0] - off, h[1] - off});
+      }
       f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
         d = mfma16x16x32(xv[kt], make_uint4(p[4 * kt], p[4 * kt + 1], p[4 * kt + 2], p[4 * kt + 3]), d);
       const float sc = bf16_lo(sw[t][i]), zp = bf16_hi(sw[t][i]);
+      // a weight is sc (q - 8) + zp: sum x w = sc d + zp sum x, with C2 = sum x
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][e] += __builtin_fmaf(sc, d[e] - C1[e], zp * C2[e]);
+      for (int e = 0; e < 4; ++e) acc[t][e] += __builtin_fmaf(sc, d[e], zp * C2[e]);
     }
   }
 
@@ -748,6 +755,9 @@ struct AttnArgs {
   int B;                   // rows
   int first_split;         // shared-prefix splits (0: none) ...
   int prefix_row;          // ... and the cache row that holds the prefix
+  int fixed_row;           // 0: row b reads and writes cache row b; r + 1: every row uses
+                           // cache row r (the tokens of one prompt, at their own positions)
+  int write_mode;          // 0: write the new slot and attend; 1: only write it; 2: only attend
 };
 
 // The attention of split s of kv head g for batch row b (cache position c), given
@@ -772,8 +782,9 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int g, int 
   const int row = wave * 4 + rr;    // 0..15
   const int d0 = li * DPL;
   const int ns = c / kAttnSplitPP + 1;
-  const size_t head_base = ((size_t)b * a.Hkv + g) * a.M;   // in rows of D
-  const size_t pidx = ((size_t)b * a.Hkv + g) * a.NS + s;   // partial slot
+  const int crow = a.fixed_row ? a.fixed_row - 1 : b;
+  const size_t head_base = ((size_t)crow * a.Hkv + g) * a.M;   // in rows of D
+  const size_t pidx = ((size_t)b * a.Hkv + g) * a.NS + s;      // partial slot
   // ---- prologue: q', k', v of the current token for this lane's dims
   const float* qrow = a.qkv + (size_t)b * a.ldqkv;
   float q[QPG][DPL], kf[DPL], vf[DPL];
@@ -815,7 +826,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int g, int 
     kf[e] = round_bf16(kf[e]);
     vf[e] = round_bf16(vf[e]);
   }
-  if (s == ns - 1 && row == 0) {
+  if (s == ns - 1 && row == 0 && a.write_mode != 2) {
     uint16_t* kd = a.kc + (head_base + c) * D + d0;
     uint16_t* vd = a.vc + (head_base + c) * D + d0;
 #pragma unroll
@@ -824,6 +835,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int g, int 
       vd[e] = f32_to_bf16(vf[e]);
     }
   }
+  if (a.write_mode == 1) return;   // (uniform over the group)
 
   // ---- online softmax over this split's positions
   float m[QPG], l[QPG], o[QPG][DPL];
@@ -981,8 +993,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int rr = lane >> 4, li = lane & 15;
   const int d0 = li * DPL;
   const int c = a.cpos[b];
-  const size_t head_base = ((size_t)b * a.Hkv + g) * a.M;   // in rows of D
-  const size_t pidx = ((size_t)b * a.Hkv + g) * a.NS + s;   // partial slot
+  const int crow = a.fixed_row ? a.fixed_row - 1 : b;
+  const size_t head_base = ((size_t)crow * a.Hkv + g) * a.M;   // in rows of D
+  const size_t pidx = ((size_t)b * a.Hkv + g) * a.NS + s;      // partial slot
 
   if (c < 0 || c >= a.M) {
     if (s == 0) {   // zero attention for this row: partial (m, l, o~) = (0, 1, 0)
@@ -995,13 +1008,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   if (s * kAttnSplitPP > c) return;
   // a split of the shared prefix of a row past it: k_attn_prefix writes its partial
   if (s < a.first_split && c >= a.first_split * kAttnSplitPP) return;
+  if (a.write_mode == 1 && s != c / kAttnSplitPP) return;   // only the new slot's split writes
 
   // ---- cache reads first
   uint32_t kr[IT][DPL / 2], vr[IT][DPL / 2];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int p = s * kAttnSplitPP + wave * (kAttnSplitPP / 4) + it * 4 + rr;
-    if (p < c) {
+    if (p < c && a.write_mode != 1) {
       const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kc + (head_base + p) * D + d0);
       const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vc + (head_base + p) * D + d0);
 #pragma unroll
@@ -1017,6 +1031,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   attn_split<D, QPG>(a, b, g, s, c, kr, vr, s_o, s_m, s_l, s_w, s_ML);
 }
 
+
+// Positions and cache positions of the prompt tokens [t0, t0 + C) in the per-row
+// layouts of the decode kernels: pos_c[a][b] = pos[a][t0 + b] (pos is [3][T]) and
+// cpos_c[b] = start + t0 + b.  One group of 64 threads, C <= 64.
+__global__ void k_prefill_rows(const int32_t* pos, int T, int t0, int C, int start, int32_t* pos_c,
+                               int32_t* cpos_c) {
+  const int b = threadIdx.x;
+  if (b >= C) return;
+#pragma unroll
+  for (int ax = 0; ax < 3; ++ax) pos_c[ax * C + b] = pos[(size_t)ax * T + t0 + b];
+  cpos_c[b] = start + t0 + b;
+}
 
 // ------------------------------------------------------------------ lm_head + argmax
 // logits[b][n] = sum_k W[n][k] h[b][k] with h = RMSNorm(x; final_norm), bf16 W

@@ -431,14 +431,16 @@ __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int
 // Streams this wave's gate/up weight rows straight into LDS (no registers held
 // while they are in flight): row i of the wave, lane l takes 32-column chunk l
 // (16 bytes of codes at codes + (i*64 + l)*16, its scale/zero word at szw + i*64 + l).
+// Rows shorter than 64 chunks (K < 2048): the lanes past the row load its chunk 0
+// again, so that every address stays inside the row; the dot product skips them.
 // The data is in LDS once this wave's vector-memory count has drained.
 __device__ __forceinline__ void wrows_to_lds(const uint8_t* packed, const uint32_t* sz, int K, int lgG,
                                              const int* row, uint4* codes, uint32_t* szw) {
-  const int lane = otid() & 63, NG = K >> lgG;
+  const int lane = otid() & 63, NG = K >> lgG, cl = 32 * lane < K ? lane : 0;
 #pragma unroll
   for (int i = 0; i < kXGuRows; ++i) {
-    __builtin_amdgcn_global_load_lds(packed + (size_t)row[i] * (K / 2) + 16 * lane, codes + i * 64, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(sz + (size_t)row[i] * NG + ((32 * lane) >> lgG), szw + i * 64, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(packed + (size_t)row[i] * (K / 2) + 16 * cl, codes + i * 64, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(sz + (size_t)row[i] * NG + ((32 * cl) >> lgG), szw + i * 64, 4, 0, 0);
   }
 }
 

@@ -77,6 +77,8 @@ _lib.kmr_decode_step.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(
                                  _i32, _p, _p, C.c_uint32, _p, C.c_size_t, _p]
 _lib.kmr_decode_step_prefix.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(KV), _p, _p, _p, _p,
                                         _i32, _p, _p, C.c_uint32, _i32, _p, C.c_size_t, _p]
+_lib.kmr_prefill.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(KV), _i32, _p, _p, _i32, _i32,
+                             _p, _p, _p, C.c_size_t, _p]
 _lib.kmr_status.argtypes = [_p, _p, C.POINTER(C.c_uint32)]
 _lib.kmr_kv_copy_row.argtypes = [C.POINTER(KV), _i32, C.POINTER(KV), _i32, _i32, _p]
 _lib.kmr_slot_admit.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, C.POINTER(_i32), _i32, _p]
@@ -86,6 +88,7 @@ _lib.kmr_last_error.restype = C.c_char_p
 
 EXPORTED = ["kmr_kv_alloc", "kmr_kv_copy_row", "kmr_quantize_int4", "kmr_workspace_bytes",
             "kmr_workspace_init", "kmr_decode_layer", "kmr_decode_step", "kmr_decode_step_prefix",
+            "kmr_prefill",
             "kmr_slot_admit", "kmr_slot_retire", "kmr_status", "kmr_strerror", "kmr_last_error"]
 
 
@@ -272,3 +275,17 @@ class DeviceModel:
         else:
             _check(_lib.kmr_decode_step(*args, ws.ptr, ws.nbytes, _stream(stream)))
         return next_ids
+
+    def prefill(self, kv: KVCache, row: int, token_ids: torch.Tensor, positions: torch.Tensor, start: int,
+                next_id: torch.Tensor, ws: Workspace, logits: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+        """kmr_prefill: token_ids [T] int32, positions [3, T] int32 (contiguous), the
+        tokens at cache positions start..start+T-1 of cache row `row`; ws sized for
+        batch min(T, KMR_MAX_BATCH)."""
+        T = token_ids.shape[0]
+        assert token_ids.dtype == torch.int32 and positions.dtype == torch.int32 and next_id.dtype == torch.int32
+        assert positions.shape == (3, T) and positions.is_contiguous() and token_ids.is_contiguous()
+        _check(_lib.kmr_prefill(C.byref(self.cfg), C.byref(self.cmodel), C.byref(kv.desc), row, _ptr(token_ids),
+                                _ptr(positions), start, T, _ptr(next_id), _ptr(logits), ws.ptr, ws.nbytes,
+                                _stream(stream)))
+        return next_id

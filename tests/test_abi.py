@@ -140,6 +140,23 @@ def test_bad_shared_prefix_is_rejected_before_launch(kmr):
                                            None, 0, 0, fake, 1 << 30, None) == kmr.KMR_EINVAL
 
 
+def test_bad_prefill_calls_are_rejected_before_launch(kmr):
+    import ctypes as C
+    cfg = _cfg(kmr)
+    kv = kmr.KV()
+    kv.k, kv.v = 0x1000, 0x2000
+    kv.n_layers, kv.batch, kv.n_kv_heads, kv.max_len, kv.head_dim = 28, 2, 8, 64, 128
+    fake = C.c_void_p(0x1000)
+    model = kmr.Model()
+    pf = kmr._lib.kmr_prefill
+    for row, start, n, what in ((2, 0, 4, b"cache row"), (-1, 0, 4, b"cache row"), (0, 0, 0, b"outside"),
+                                (0, 60, 5, b"outside"), (0, -1, 4, b"outside")):
+        rc = pf(C.byref(cfg), C.byref(model), C.byref(kv), row, fake, fake, start, n, fake, None, fake, 1 << 30, None)
+        assert rc == kmr.KMR_EINVAL and what in kmr._lib.kmr_last_error(), (row, start, n)
+    rc = pf(C.byref(cfg), C.byref(model), C.byref(kv), 1, fake, fake, 60, 4, fake, None, fake, 1 << 30, None)
+    assert rc == kmr.KMR_EINVAL and b"model" in kmr._lib.kmr_last_error()   # the range itself is fine
+
+
 def test_bad_slot_calls_are_rejected_before_launch(kmr):
     import ctypes as C
     fake = C.c_void_p(0x1000)
