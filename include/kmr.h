@@ -219,7 +219,7 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
  * is read once for all of them, then merged with each request's own suffix).
  * The caller promises that every row holds the same K/V in cache positions
  * [0, shared_prefix) of every layer (row 0 is the one read).  The step runs on the
- * per-phase kernels; the attention splits of 128 positions that lie wholly inside
+ * per-phase kernels; the attention splits of 256 positions that lie wholly inside
  * the prefix are computed once per (split, kv head) for every row whose
  * cache_position is past them, with the same operations as the plain path, so
  * next_ids, logits and the cache are bit for bit those of kmr_decode_step with

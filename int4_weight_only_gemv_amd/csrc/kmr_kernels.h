@@ -12,7 +12,7 @@ namespace kmr {
 
 constexpr int kAttnSplit = 64;     // cache positions per attention item of the device-wide
                                    // persistent kernel, and ...
-constexpr int kAttnSplitPP = 128;  // ... per work-group of the per-phase kernels (both fixed,
+constexpr int kAttnSplitPP = 256;  // ... per work-group of the per-phase kernels (both fixed,
                                    // so a row's result never depends on the batch size)
 constexpr int kGemvRowsPerWave = 2;
 constexpr int kLmRowsPerWave = 4;
@@ -761,8 +761,8 @@ struct AttnArgs {
 };
 
 // The attention of split s of kv head g for batch row b (cache position c), given
-// this lane's K/V words of the split (kr, vr: positions s*kAttnSplitPP + 16 wave +
-// 4 it + lane/16, dims DPL*(lane%16) ..): q/k norm and RoPE of the row's new token,
+// this lane's K/V words of the split (kr, vr: positions s*kAttnSplitPP +
+// (kAttnSplitPP/4) wave + 4 it + lane/16, dims DPL*(lane%16) ..): q/k norm and RoPE of the row's new token,
 // its cache write (last split), the block softmax of each 16-lane row, the 16 row
 // states merged, and the split's partial stored.  Every thread of the group calls
 // this; it ends after the partial stores (a caller that calls it again must first
