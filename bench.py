@@ -14,6 +14,9 @@ a batch that the per-phase kernels serve, with the matrix-core int4 GEMV for
 its 16-row tiles; its roofline figure covers the whole step (many launches).
 `--workload kv_copy` times the continuous-batching slot copy instead
 (kmr_kv_copy_row of a full 1024-position row of the same model's cache).
+`--workload prefill512` times kmr_prefill of a 512-token prompt into row 0 of
+the default workload's cache (8 chunks of 64 tokens through the per-phase
+kernels); its roofline is the matrix cores' fp16 dense peak.
 
 Prints one JSON line (see the README of the driver contract in the design doc).
 """
@@ -201,12 +204,58 @@ def bench_kv_copy(args):
     print(json.dumps(out), flush=True)
 
 
+F16_DENSE_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
+
+
+def bench_prefill(args):
+    """kmr_prefill of a 512-token prompt (token ids U[0, V), text positions t = h = w
+    = 0..511) into row 0 of the 28-layer model's 1024-slot cache, start 0."""
+    import torch
+    from int4_weight_only_gemv_amd import kmr
+    w, model, kv, _, _ = build("step")
+    d, T = w.dims, 512
+    g = torch.Generator(device="cuda").manual_seed(11)
+    ids = torch.randint(0, d.vocab, (T,), generator=g, device="cuda", dtype=torch.int32)
+    pos = torch.arange(T, dtype=torch.int32, device="cuda").repeat(3, 1).contiguous()
+    ws = kmr.Workspace(model.cfg, min(T, kmr.KMR_MAX_BATCH), w.max_len)
+    nxt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        model.prefill(kv, 0, ids, pos, 0, nxt, ws, stream=stream)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        model.prefill(kv, 0, ids, pos, 0, nxt, ws, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    assert ws.status() == 0
+    ms = start.elapsed_time(stop) / args.steps
+    # algorithmic flops: the decoder linears for every token, causal attention
+    # (q k^T and p v over positions 0..t of token t), the lm_head for the last token
+    lin = ((d.n_heads + 2 * d.n_kv_heads) * d.head_dim * d.hidden + d.hidden * d.n_heads * d.head_dim
+           + 3 * d.intermediate * d.hidden)
+    attn = 4 * d.n_heads * d.head_dim * T * (T + 1) // 2
+    flops = d.n_layers * (2 * lin * T + attn) + 2 * d.vocab * d.hidden
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {"metric": "prefill tokens/s, 512-token prompt, Qwen3-VL-2B-shaped int4 decoder", "value": round(T / ms * 1e3, 1),
+           "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "prefill-512-tokens-28L-int4-g128", "tokens": T, "chunk": kmr.KMR_MAX_BATCH},
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": F16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / F16_DENSE_PEAK_TFLOPS, 5), "traffic": None,
+                        "kernel": "per-phase kernels over 64-token chunks", "launches_per_step": None,
+                        "kernel_us_per_launch": None},
+           "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["step", "batch4", "long16", "kv_copy"], default="step")
+    ap.add_argument("--workload", choices=["step", "batch4", "long16", "kv_copy", "prefill512"], default="step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
@@ -223,6 +272,9 @@ def main():
         copy_calibration(args.calibrate_copy_mib)
     if args.workload == "kv_copy":
         bench_kv_copy(args)
+        return
+    if args.workload == "prefill512":
+        bench_prefill(args)
         return
     w, model, kv, layers, glob = build(args.workload)
     inp = synth.step_inputs(w)
