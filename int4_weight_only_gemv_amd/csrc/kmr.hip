@@ -109,9 +109,10 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
   {
     int kmax = c->hidden > Hq * D ? c->hidden : Hq * D;
     kmax = kmax > c->intermediate ? kmax : c->intermediate;
-    w.xst = o; o += align256((size_t)16 * 4 * (kmax / 32) * 16);
-    w.xst_cc = o; o += align256((size_t)16 * (kmax / 32) * 8);
-    w.xst_cb = o; o += align256((size_t)16 * (kmax / 128) * 8);
+    const size_t rows = B > 16 ? (size_t)(B / 16) * 16 : 16;   // the full 16-row tiles, or one tile
+    w.xst = o; o += align256(rows * 4 * (kmax / 32) * 16);
+    w.xst_cc = o; o += align256(rows * (kmax / 32) * 8);
+    w.xst_cb = o; o += align256(rows * (kmax / 128) * 8);
   }
   // XCD-local step kernel: per-XCD regions, then the device-wide partials
   o = (o + 4095) & ~(size_t)4095;
@@ -232,10 +233,29 @@ void launch_gemv_tile(const GemvArgs& a, hipStream_t st) {
   }
 }
 
-// Batch tiles keep the staged input inside the LDS of one CU.
+// Batch tiles keep the staged input inside the LDS of one CU.  With the input
+// staged in memory, all full 16-row tiles run as one launch (the tile is the
+// grid's y index): one staging pass and one product launch instead of one each
+// per tile, and the tiles stream the same weights at the same time.  Every row's
+// result is the same as in a launch of its own tile.
 template <int EPI, int PRO>
 void launch_gemv(GemvArgs a, hipStream_t st) {
-  const int B = a.B;
+  int B = a.B;
+  if constexpr (PRO != PRO_ATTN) {
+    const int full = B / 16;
+    if (full >= 2 && gemv_mfma_staged<EPI, PRO>(a)) {
+      GemvArgs t = a;
+      t.B = 16 * full;
+      hipLaunchKernelGGL((k_gemv_stage16<PRO>), dim3(16 * full, (a.K + 2047) / 2048), dim3(64), 0, st, t);
+      const size_t lds = (size_t)4 * (EPI == EPI_SILU ? 2 : 1) * 256 * 4;   // wave partials
+      hipLaunchKernelGGL((k_gemv_int4_mfma<16, EPI, PRO, true>), dim3((a.N + 15) / 16, full), dim3(256), lds, st, t);
+      if (B == 16 * full) return;
+      a.x += (size_t)16 * full * a.ldx;   // the remaining rows as before
+      a.y += (size_t)16 * full * a.ldy;
+      a.b0 += 16 * full;
+      a.B = B = B - 16 * full;
+    }
+  }
   int tile = 16;
   const size_t per_row = (size_t)a.K * 9 / 4 + (PRO == PRO_ATTN ? (size_t)a.K * 4 : 0);
   if (!(B >= 9 && gemv_mfma_staged<EPI, PRO>(a)))   // (staged in memory: no LDS bound)
@@ -243,7 +263,7 @@ void launch_gemv(GemvArgs a, hipStream_t st) {
   for (int b0 = 0; b0 < B; b0 += tile) {
     GemvArgs t = a;
     t.B = B - b0 < tile ? B - b0 : tile;
-    t.b0 = b0;
+    t.b0 = a.b0 + b0;
     if (t.x) t.x = a.x + (size_t)b0 * a.ldx;
     t.y = a.y + (size_t)b0 * a.ldy;
     launch_gemv_tile<EPI, PRO>(t, st);

@@ -615,10 +615,13 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
   static_assert(BT == 16, "one 16-row operand of batch rows");
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NT = EPI == EPI_SILU ? 2 : 1;   // 16-row weight tiles per block
-  const int K = a.K, CH = K >> 5, NG = K / a.G, NB = K >> 7, B = a.B;
+  // staged in memory (GS): blockIdx.y picks a 16-row tile of the staged rows and of y
+  const int tr = GS ? 16 * (int)blockIdx.y : 0;
+  const int K = a.K, CH = K >> 5, NG = K / a.G, NB = K >> 7;
+  const int B = GS ? (a.B - tr < 16 ? a.B - tr : 16) : a.B;
   const GemvLds lay = gemv_lds(BT, K, PRO == PRO_ATTN);
-  const uint4* xs = GS ? a.xsg : reinterpret_cast<const uint4*>(smem + lay.xs);      // [BT][4][CH]
-  const float2* cc = GS ? a.ccg : reinterpret_cast<const float2*>(smem + lay.cc);    // [BT][CH]
+  const uint4* xs = GS ? a.xsg + (size_t)tr * 4 * CH : reinterpret_cast<const uint4*>(smem + lay.xs);   // [BT][4][CH]
+  const float2* cc = GS ? a.ccg + (size_t)tr * CH : reinterpret_cast<const float2*>(smem + lay.cc);     // [BT][CH]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, gq = lane >> 4;
   const int r0 = blockIdx.x * 16;
   const bool rok = r0 + n < a.N;
@@ -664,7 +667,7 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int b = 4 * gq + e < BT ? 4 * gq + e : 0;
       if constexpr (GS) {
-        C2[e] = a.cbg[b * NB + kb].y;
+        C2[e] = a.cbg[(tr + b) * NB + kb].y;
       } else {
         const float2* cp = cc + b * CH + 4 * kb;
         C2[e] = (cp[0].y + cp[1].y) + (cp[2].y + cp[3].y);
@@ -715,7 +718,7 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
         for (int wv = 0; wv < 4; ++wv) s += part[((wv * NT + t) * 16 + b) * 16 + r];
         v[t] = s;
       }
-      float* dst = a.y + (size_t)b * a.ldy + nr;
+      float* dst = a.y + (size_t)(tr + b) * a.ldy + nr;
       if (EPI == EPI_STORE) {
         *dst = v[0];
       } else if (EPI == EPI_ADD) {
