@@ -269,6 +269,46 @@ def test_decode_step_full(kmr, full_pair, path):
     _step_case(kmr, full_pair, kv, kh, vh, synth.step_inputs(w), w.max_len, path=path)
 
 
+def test_prefill_full_size_matches_oracle_decode(kmr, full_pair):
+    """kmr_prefill of 70 tokens at the full model size (one 64-token chunk on the fused
+    matrix-core tiles, then 6 tokens on the VALU) against the oracle's decode step run
+    token by token over the same cache row (kaminari page, section 04: prefill fills
+    the static cache that decode extends): the last token's logits and token, every
+    written K/V slot, and no other slot."""
+    w = synth.WORKLOADS["step"]
+    dims, M, T = w.dims, w.max_len, 70
+    rng = np.random.default_rng(T)
+    tokens = rng.integers(0, dims.vocab, T).astype(np.int32)
+    pos3 = np.ascontiguousarray(np.arange(T, dtype=np.int32)[None].repeat(3, 0))
+    log(f"prefill {T} tokens, 28 layers, from position 0 (oracle: {T} decode steps)")
+    kv, kh, vh = make_caches(dims, synth.base_seed(w) + T, 1, M, "device")
+    ws = kmr.Workspace(full_pair.dev.cfg, min(T, kmr.KMR_MAX_BATCH), M)
+    nxt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    logits = torch.empty(dims.vocab, dtype=torch.float32, device="cuda")
+    full_pair.dev.prefill(kv, 0, torch.from_numpy(tokens).cuda(), torch.from_numpy(pos3).cuda(), 0, nxt, ws,
+                          logits=logits)
+    torch.cuda.synchronize()
+    assert ws.status() == 0
+    kc, vc = kh.copy(), vh.copy()
+    for t in range(T):
+        ref = full_pair.ora.decode_step(kc, vc, tokens[t:t + 1], np.ascontiguousarray(pos3[:, t:t + 1]),
+                                        np.array([t], np.int32))
+    err = max_rel(logits.cpu().numpy()[None], ref["logits"])
+    got_next = int(nxt.cpu()[0])
+    log(f"  logits max_rel={err:.3e} next={got_next} oracle={int(ref['next'][0])} "
+        f"margin={float(ref['margin'][0]):.4f}")
+    assert err <= TOL
+    if ref["margin"][0] > MARGIN:
+        assert got_next == int(ref["next"][0])
+    D = dims.head_dim
+    for dev_t, want, before in ((kv.k, kc, kh), (kv.v, vc, vh)):
+        got = oracle.as_u16(dev_t)
+        e = max_rel(bf16_host(got[:, 0, :, :T]).reshape(-1, D), bf16_host(want[:, 0, :, :T]).reshape(-1, D))
+        log(f"  written K/V max_rel={e:.3e}")
+        assert e <= TOL
+        assert np.array_equal(got[:, :, :, T:], before[:, :, :, T:])
+
+
 def test_persistent_and_per_phase_paths_agree(kmr, full_pair):
     w = synth.WORKLOADS["batch4"]
     log("persistent step kernels vs per-phase kernels, batch 4, 3 advancing steps")
