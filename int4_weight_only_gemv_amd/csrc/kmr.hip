@@ -74,7 +74,8 @@ constexpr int kMaxStepGroups = 1024;   // lm_head partial slots of the persisten
 struct WsLayout {
   size_t status, cs, x, qkv, attn_o, act, part_o, part_ml, lm_part, total;
   size_t step_ctr, lm_cnt, tx, tqkv, to, tact, tpart, lm_part2;
-  size_t lx, sx, lqkv, lpart, lact, pO, pD, probe, pf;
+  size_t lx, sx, lqkv, lpart, lact, pO, pD, probe, pf, kpart;
+  int kpart_rows;
   size_t xst, xst_cc, xst_cb;   // staged 16-row GEMV tile: [16][4][Kmax/32] x 16 B, [16][Kmax/32] x 8 B,
                                 // [16][Kmax/128] x 8 B
   StepXSizes xz;
@@ -113,6 +114,8 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
     w.xst = o; o += align256(rows * 4 * (kmax / 32) * 16);
     w.xst_cc = o; o += align256(rows * (kmax / 32) * 8);
     w.xst_cb = o; o += align256(rows * (kmax / 128) * 8);
+    w.kpart_rows = (int)rows;
+    w.kpart = o; o += align256((size_t)2 * rows * c->hidden * 4);   // split-K partials of O and down
   }
   // XCD-local step kernel: per-XCD regions, then the device-wide partials
   o = (o + 4095) & ~(size_t)4095;
@@ -208,14 +211,32 @@ inline bool gemv_mfma_staged(const GemvArgs& a) {
   return PRO != PRO_ATTN && a.xsg && a.ccg && a.cbg && gemv_mfma_shape<EPI, PRO>(a);
 }
 
+// The staged matrix-core product over `tiles` 16-row tiles (a.B rows): one staging
+// launch, one product launch.  An accumulating product whose grid would have fewer
+// groups than the chip has CUs (one group per 16 weight rows and tile) splits K in
+// two halves (the grid's z index) into a.kpart, and k_gemv_kreduce adds them to y.
+// (Measured: at 16 rows the O and down products gain; at 64 rows, with 4 tiles, the
+// split only adds the partial traffic and a launch.)
+constexpr int kSplitBelowGroups = 256;   // MI355X compute units
+template <int EPI, int PRO>
+void launch_mfma_staged(const GemvArgs& a, int tiles, hipStream_t st) {
+  hipLaunchKernelGGL((k_gemv_stage16<PRO>), dim3(16 * tiles, (a.K + 2047) / 2048), dim3(64), 0, st, a);
+  const size_t lds = (size_t)4 * (EPI == EPI_SILU ? 2 : 1) * 256 * 4;   // wave partials
+  const bool split = EPI == EPI_ADD && a.kpart && a.N <= a.kpart_n && (a.K / 128) % 2 == 0 &&
+                     a.kpart_rows >= 16 * tiles && ((a.N + 15) / 16) * tiles < kSplitBelowGroups;
+  hipLaunchKernelGGL((k_gemv_int4_mfma<16, EPI, PRO, true>), dim3((a.N + 15) / 16, tiles, split ? 2 : 1),
+                     dim3(256), lds, st, a);
+  if (split) {
+    const int n = a.B * a.N;
+    hipLaunchKernelGGL(k_gemv_kreduce, dim3((n + 255) / 256), dim3(256), 0, st, a.y, a.ldy, a.kpart,
+                       a.kpart_rows, a.N, a.B);
+  }
+}
+
 template <int EPI, int PRO>
 void launch_gemv_tile(const GemvArgs& a, hipStream_t st) {
   if (a.B >= 9 && gemv_mfma_staged<EPI, PRO>(a)) {
-    if constexpr (PRO != PRO_ATTN) {
-      hipLaunchKernelGGL((k_gemv_stage16<PRO>), dim3(16, (a.K + 2047) / 2048), dim3(64), 0, st, a);
-      const size_t lds = (size_t)4 * (EPI == EPI_SILU ? 2 : 1) * 256 * 4;   // wave partials
-      hipLaunchKernelGGL((k_gemv_int4_mfma<16, EPI, PRO, true>), dim3((a.N + 15) / 16), dim3(256), lds, st, a);
-    }
+    if constexpr (PRO != PRO_ATTN) launch_mfma_staged<EPI, PRO>(a, 1, st);
     return;
   }
   if (a.B >= 9 && gemv_mfma_shape<EPI, PRO>(a) && a.K >= 256 * (EPI == EPI_SILU ? 2 : 1)) {
@@ -246,9 +267,7 @@ void launch_gemv(GemvArgs a, hipStream_t st) {
     if (full >= 2 && gemv_mfma_staged<EPI, PRO>(a)) {
       GemvArgs t = a;
       t.B = 16 * full;
-      hipLaunchKernelGGL((k_gemv_stage16<PRO>), dim3(16 * full, (a.K + 2047) / 2048), dim3(64), 0, st, t);
-      const size_t lds = (size_t)4 * (EPI == EPI_SILU ? 2 : 1) * 256 * 4;   // wave partials
-      hipLaunchKernelGGL((k_gemv_int4_mfma<16, EPI, PRO, true>), dim3((a.N + 15) / 16, full), dim3(256), lds, st, t);
+      launch_mfma_staged<EPI, PRO>(t, full, st);
       if (B == 16 * full) return;
       a.x += (size_t)16 * full * a.ldx;   // the remaining rows as before
       a.y += (size_t)16 * full * a.ldy;
@@ -371,8 +390,9 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   uint4* xsg = at<uint4>(ws, w.xst);
   float2* ccg = at<float2>(ws, w.xst_cc);
   float2* cbg = at<float2>(ws, w.xst_cb);
+  float* kpart = at<float>(ws, w.kpart);
   GemvArgs g{};
-  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
   g.packed = static_cast<const uint8_t*>(L->qkv.packed);
   g.sz = static_cast<const uint32_t*>(L->qkv.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->in_norm); g.eps = c->rms_eps;
@@ -406,7 +426,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   ap.Hkv = Hkv; ap.NS = w.ns_pp; ap.QPG = Hq / Hkv; ap.D = D; ap.M = kv->max_len;
 
   g = GemvArgs{};
-  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
   g.packed = static_cast<const uint8_t*>(L->o.packed);
   g.sz = static_cast<const uint32_t*>(L->o.sz);
   g.y = x; g.ldy = H; g.N = H; g.K = Hq * D; g.G = G; g.B = B;
@@ -421,7 +441,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   }
 
   g = GemvArgs{};
-  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
   g.packed = static_cast<const uint8_t*>(L->gate_up.packed);
   g.sz = static_cast<const uint32_t*>(L->gate_up.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->post_norm); g.eps = c->rms_eps;
@@ -429,7 +449,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   launch_gemv<EPI_SILU, PRO_RMSNORM>(g, st);
 
   g = GemvArgs{};
-  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
   g.packed = static_cast<const uint8_t*>(L->down.packed);
   g.sz = static_cast<const uint32_t*>(L->down.sz);
   g.x = act; g.ldx = I; g.gain = nullptr;

@@ -311,6 +311,8 @@ struct GemvArgs {
   uint4* xsg;             // staged input of a 16-row tile in memory: [16][4][K/32] ...
   float2* ccg;            // ... its chunk constants [16][K/32] ...
   float2* cbg;            // ... and their sums per 128-column block [16][K/128] (k_gemv_stage16)
+  float* kpart;           // split-K partials [2][kpart_rows][N] of an EPI_ADD product (or null),
+  int kpart_rows, kpart_n;   // for N <= kpart_n
 };
 
 // LDS layout of k_gemv_int4 (byte offsets, 16-byte aligned).
@@ -625,7 +627,9 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, gq = lane >> 4;
   const int r0 = blockIdx.x * 16;
   const bool rok = r0 + n < a.N;
-  const int nbw = NB > wave ? (NB - wave + 3) >> 2 : 0;   // this wave's 128-column blocks
+  // split K (GS, EPI_ADD): blockIdx.z takes the z-th of gridDim.z equal runs of 128-column blocks
+  const int KZ = GS ? (int)gridDim.z : 1, kz = GS ? (int)blockIdx.z : 0, NBz = NB / KZ, kb0 = kz * NBz;
+  const int nbw = NBz > wave ? (NBz - wave + 3) >> 2 : 0;   // this wave's 128-column blocks
 
   // ---- weight stream first (in flight while the input is staged)
   uint4 w[NT][kMfmaBlocksPerWave];
@@ -635,7 +639,7 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
     const int row = rok ? r0 + n + t * a.N : 0;
 #pragma unroll
     for (int i = 0; i < kMfmaBlocksPerWave; ++i) {
-      const int kb = wave + 4 * i;
+      const int kb = kb0 + wave + 4 * i;
       if (i < nbw && rok) {
         w[t][i] = load_stream16(a.packed + (size_t)row * (K / 2) + 16 * (4 * kb + gq));
         sw[t][i] = a.sz[(size_t)row * NG + ((kb << 7) / a.G)];
@@ -657,7 +661,7 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
 #pragma unroll
   for (int i = 0; i < kMfmaBlocksPerWave; ++i) {
     if (i >= nbw) continue;   // (not break: the loop unrolls, w and sw stay in registers)
-    const int kb = wave + 4 * i, c = 4 * kb + gq;
+    const int kb = kb0 + wave + 4 * i, c = 4 * kb + gq;
     uint4 xv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) xv[q] = xs[(bn * 4 + q) * CH + c];
@@ -719,7 +723,9 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
         v[t] = s;
       }
       float* dst = a.y + (size_t)(tr + b) * a.ldy + nr;
-      if (EPI == EPI_STORE) {
+      if (KZ > 1) {   // (EPI_ADD only) this half's partial; k_gemv_kreduce adds both to y
+        a.kpart[((size_t)kz * a.kpart_rows + tr + b) * a.N + nr] = v[0];
+      } else if (EPI == EPI_STORE) {
         *dst = v[0];
       } else if (EPI == EPI_ADD) {
         *dst += v[0];
@@ -729,6 +735,14 @@ __global__ __launch_bounds__(256) void k_gemv_int4_mfma(GemvArgs a) {
       }
     }
   }
+}
+
+// y[b][n] += (p0 + p1) for the two split-K partials of an EPI_ADD product (fixed order).
+__global__ void k_gemv_kreduce(float* y, int ldy, const float* kpart, int rows, int N, int B) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * N) return;
+  const int b = i / N, n = i - b * N;
+  y[(size_t)b * ldy + n] += kpart[(size_t)b * N + n] + kpart[((size_t)rows + b) * N + n];
 }
 
 // ------------------------------------------------------------------ attention
