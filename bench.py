@@ -18,7 +18,8 @@ its 16-row tiles; its roofline figure covers the whole step (many launches).
 the default workload's cache (8 chunks of 64 tokens through the per-phase
 kernels); its roofline is the matrix cores' fp16 dense peak.
 
-Prints one JSON line (see the README of the driver contract in the design doc).
+Prints one JSON line: metric, value, unit, timing, config, the roofline of the
+dominant kernel and (default workload) the CPU oracle baseline.
 """
 from __future__ import annotations
 
