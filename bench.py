@@ -15,7 +15,7 @@ its 16-row tiles; its roofline figure covers the whole step (many launches).
 `--workload kv_copy` times the continuous-batching slot copy instead
 (kmr_kv_copy_row of a full 1024-position row of the same model's cache).
 `--workload prefill512` times kmr_prefill of a 512-token prompt into row 0 of
-the default workload's cache (8 chunks of 64 tokens through the per-phase
+the default workload's cache (4 chunks of 128 tokens through the per-phase
 kernels); its roofline is the matrix cores' fp16 dense peak.
 
 Prints one JSON line: metric, value, unit, timing, config, the roofline of the
@@ -218,7 +218,7 @@ def bench_prefill(args):
     g = torch.Generator(device="cuda").manual_seed(11)
     ids = torch.randint(0, d.vocab, (T,), generator=g, device="cuda", dtype=torch.int32)
     pos = torch.arange(T, dtype=torch.int32, device="cuda").repeat(3, 1).contiguous()
-    ws = kmr.Workspace(model.cfg, min(T, kmr.KMR_MAX_BATCH), w.max_len)
+    ws = kmr.Workspace.for_prefill(model.cfg, T, w.max_len)
     nxt = torch.zeros(1, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -242,7 +242,7 @@ def bench_prefill(args):
     out = {"metric": "prefill tokens/s, 512-token prompt, Qwen3-VL-2B-shaped int4 decoder", "value": round(T / ms * 1e3, 1),
            "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-           "config": {"workload": "prefill-512-tokens-28L-int4-g128", "tokens": T, "chunk": kmr.KMR_MAX_BATCH},
+           "config": {"workload": "prefill-512-tokens-28L-int4-g128", "tokens": T, "chunk": kmr.KMR_PREFILL_CHUNK},
            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": F16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tflops / F16_DENSE_PEAK_TFLOPS, 5), "traffic": None,
                         "kernel": "per-phase kernels over 64-token chunks", "launches_per_step": None,

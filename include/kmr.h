@@ -67,6 +67,7 @@ enum {
 };
 
 #define KMR_MAX_BATCH 64
+#define KMR_PREFILL_CHUNK 128   /* prompt tokens per chunk of kmr_prefill */
 #define KMR_ADVANCE 1u
 #define KMR_MULTI_KERNEL 2u  /* run the step as one kernel per phase instead of the
                                 single persistent kernel (diagnostics, cross-checks) */
@@ -155,6 +156,9 @@ int kmr_quantize_int4(const void* w_bf16, int32_t N, int32_t K, int32_t group, v
 
 /* Bytes of workspace the decode calls need for this config, batch and max_len. */
 size_t kmr_workspace_bytes(const kmr_config* cfg, int32_t batch, int32_t max_len);
+/* The workspace kmr_prefill needs for a prompt of n_tokens (a chunk of
+ * min(n_tokens, KMR_PREFILL_CHUNK) rows); 0 for an invalid config or size. */
+size_t kmr_prefill_workspace_bytes(const kmr_config* cfg, int32_t n_tokens, int32_t max_len);
 
 /* Clears a workspace with a fill kernel on `stream`.  Call once after allocating
  * it and again after any call that returned an error; the decode calls leave
@@ -245,11 +249,11 @@ int kmr_decode_step_prefix(const kmr_config* cfg, const kmr_model* model, const 
  * attends causally to the slots up to its own.  No other slot or row is touched.
  * next_id [1] receives the argmax at the last token; logits [vocab] fp32 receives
  * that token's logits if not NULL.
- * The tokens run in chunks of at most KMR_MAX_BATCH through the per-phase kernels
+ * The tokens run in chunks of at most KMR_PREFILL_CHUNK through the per-phase kernels
  * (every projection of a chunk as one batch; the attention of a chunk in two
  * passes, the new K/V slots of every token first, then the attention itself).
- * ws must hold kmr_workspace_bytes(cfg, min(n_tokens, KMR_MAX_BATCH), max_len)
- * bytes and have been initialised once.  Returns KMR_EINVAL for a row outside the
+ * ws must hold kmr_prefill_workspace_bytes(cfg, n_tokens, max_len) bytes and
+ * have been initialised once.  Returns KMR_EINVAL for a row outside the
  * cache, n_tokens < 1, or start + n_tokens > max_len, before anything is launched;
  * token ids outside [0, vocab) raise KMR_STATUS_TOKEN as in kmr_decode_step.
  * Nothing is synchronised.

@@ -128,7 +128,7 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
   w.pO = o; o += align256((size_t)kXcds * B * c->hidden * 8);
   w.pD = o; o += align256((size_t)kXcds * B * c->hidden * 8);
   w.probe = o; o += align256((size_t)kMaxStepGroups * 4);
-  w.pf = o; o += align256((size_t)4 * KMR_MAX_BATCH * 4);   // prefill: a chunk's [3][C] positions, [C] cache positions
+  w.pf = o; o += align256((size_t)4 * KMR_PREFILL_CHUNK * 4);   // prefill: a chunk's [3][C] positions, [C] cache positions
   w.total = o;
   return w;
 }
@@ -687,6 +687,11 @@ size_t kmr_workspace_bytes(const kmr_config* cfg, int32_t batch, int32_t max_len
   return ws_layout(cfg, batch, max_len).total;
 }
 
+size_t kmr_prefill_workspace_bytes(const kmr_config* cfg, int32_t n_tokens, int32_t max_len) {
+  if (check_config(cfg) || n_tokens <= 0 || max_len <= 0) return 0;
+  return ws_layout(cfg, n_tokens < KMR_PREFILL_CHUNK ? n_tokens : KMR_PREFILL_CHUNK, max_len).total;
+}
+
 int kmr_workspace_init(void* ws, size_t ws_bytes, kmr_stream_t stream) {
   if (!ws || !ws_bytes) return fail(KMR_EINVAL, "workspace is NULL or empty");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -849,17 +854,18 @@ int kmr_prefill(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
     if ((rc = check_layer(cfg, &model->layers[l]))) return fail(rc, "layer %d: %s", l, g_err);
   if (!token_ids || !positions || !next_id || !ws)
     return fail(KMR_EINVAL, "null token_ids/positions/next_id/workspace");
-  const int C = n_tokens < KMR_MAX_BATCH ? n_tokens : KMR_MAX_BATCH;
+  const int C = n_tokens < KMR_PREFILL_CHUNK ? n_tokens : KMR_PREFILL_CHUNK;
   const WsLayout w = ws_layout(cfg, C, kv->max_len);
   if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float* x = at<float>(ws, w.x);
   int32_t* pos_c = at<int32_t>(ws, w.pf);
-  int32_t* cpos_c = pos_c + 3 * KMR_MAX_BATCH;
+  int32_t* cpos_c = pos_c + 3 * KMR_PREFILL_CHUNK;
   int n = 0;
   for (int t0 = 0; t0 < n_tokens; t0 += n) {
     n = n_tokens - t0 < C ? n_tokens - t0 : C;
-    hipLaunchKernelGGL(k_prefill_rows, dim3(1), dim3(64), 0, st, positions, n_tokens, t0, n, start, pos_c, cpos_c);
+    hipLaunchKernelGGL(k_prefill_rows, dim3(1), dim3(KMR_PREFILL_CHUNK), 0, st, positions, n_tokens, t0, n, start,
+                       pos_c, cpos_c);
     enqueue_prep(cfg, static_cast<const uint16_t*>(model->embed), token_ids + t0, nullptr, pos_c, x, n, ws, w, st);
     for (int l = 0; l < cfg->n_layers; ++l)
       enqueue_layer(cfg, &model->layers[l], l, kv, x, cpos_c, n, ws, w, st, 0, row + 1);

@@ -1051,7 +1051,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 
 // Positions and cache positions of the prompt tokens [t0, t0 + C) in the per-row
 // layouts of the decode kernels: pos_c[a][b] = pos[a][t0 + b] (pos is [3][T]) and
-// cpos_c[b] = start + t0 + b.  One group of 64 threads, C <= 64.
+// cpos_c[b] = start + t0 + b.  One group of KMR_PREFILL_CHUNK threads, C <= that.
 __global__ void k_prefill_rows(const int32_t* pos, int T, int t0, int C, int start, int32_t* pos_c,
                                int32_t* cpos_c) {
   const int b = threadIdx.x;

@@ -33,6 +33,7 @@ if len(_hip_runtimes()) > 1:
 KMR_OK, KMR_EINVAL, KMR_ESHAPE, KMR_ENOMEM, KMR_EHIP = 0, -1, -2, -3, -4
 KMR_STATUS_CACHE_POS, KMR_STATUS_TOKEN, KMR_STATUS_TIMEOUT, KMR_STATUS_TOPOLOGY = 1, 2, 4, 8
 KMR_MAX_BATCH = 64
+KMR_PREFILL_CHUNK = 128
 KMR_ADVANCE = 1
 KMR_MULTI_KERNEL = 2
 KMR_DEVICE_WIDE = 4
@@ -70,6 +71,8 @@ _lib.kmr_kv_alloc.argtypes = [C.POINTER(Config), _i32, _i32, _p, C.c_size_t, _i3
 _lib.kmr_quantize_int4.argtypes = [_p, _i32, _i32, _i32, _p, _p, _p]
 _lib.kmr_workspace_bytes.argtypes = [C.POINTER(Config), _i32, _i32]
 _lib.kmr_workspace_bytes.restype = C.c_size_t
+_lib.kmr_prefill_workspace_bytes.argtypes = [C.POINTER(Config), _i32, _i32]
+_lib.kmr_prefill_workspace_bytes.restype = C.c_size_t
 _lib.kmr_workspace_init.argtypes = [_p, C.c_size_t, _p]
 _lib.kmr_decode_layer.argtypes = [C.POINTER(Config), C.POINTER(Layer), _i32, C.POINTER(KV), _p, _p,
                                   _p, _i32, _p, C.c_size_t, _p]
@@ -87,6 +90,7 @@ _lib.kmr_strerror.restype = C.c_char_p
 _lib.kmr_last_error.restype = C.c_char_p
 
 EXPORTED = ["kmr_kv_alloc", "kmr_kv_copy_row", "kmr_quantize_int4", "kmr_workspace_bytes",
+            "kmr_prefill_workspace_bytes",
             "kmr_workspace_init", "kmr_decode_layer", "kmr_decode_step", "kmr_decode_step_prefix",
             "kmr_prefill",
             "kmr_slot_admit", "kmr_slot_retire", "kmr_status", "kmr_strerror", "kmr_last_error"]
@@ -146,12 +150,18 @@ def workspace_bytes(cfg: Config, batch: int, max_len: int) -> int:
 
 
 class Workspace:
-    def __init__(self, cfg: Config, batch: int, max_len: int, device="cuda", stream=None):
-        n = workspace_bytes(cfg, batch, max_len)
+    def __init__(self, cfg: Config, batch: int, max_len: int, device="cuda", stream=None, nbytes=None):
+        n = workspace_bytes(cfg, batch, max_len) if nbytes is None else nbytes
         if n == 0:
             raise KmrError(KMR_EINVAL)
         self.buf = torch.empty(n, dtype=torch.uint8, device=device)
         _check(_lib.kmr_workspace_init(_ptr(self.buf), n, _stream(stream)))
+
+    @classmethod
+    def for_prefill(cls, cfg: Config, n_tokens: int, max_len: int, device="cuda", stream=None):
+        """The workspace of a kmr_prefill of n_tokens (kmr_prefill_workspace_bytes)."""
+        return cls(cfg, 0, max_len, device, stream,
+                   nbytes=int(_lib.kmr_prefill_workspace_bytes(C.byref(cfg), n_tokens, max_len)))
 
     @property
     def ptr(self):
@@ -281,7 +291,7 @@ class DeviceModel:
                 stream=None) -> torch.Tensor:
         """kmr_prefill: token_ids [T] int32, positions [3, T] int32 (contiguous), the
         tokens at cache positions start..start+T-1 of cache row `row`; ws sized for
-        batch min(T, KMR_MAX_BATCH)."""
+        Workspace.for_prefill(cfg, T, max_len)."""
         T = token_ids.shape[0]
         assert token_ids.dtype == torch.int32 and positions.dtype == torch.int32 and next_id.dtype == torch.int32
         assert positions.shape == (3, T) and positions.is_contiguous() and token_ids.is_contiguous()

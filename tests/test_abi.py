@@ -92,6 +92,10 @@ def test_workspace_and_kv_sizes(kmr):
     assert 0 < n1 < n16
     assert kmr.workspace_bytes(cfg, 0, 1024) == 0
     assert kmr.workspace_bytes(cfg, kmr.KMR_MAX_BATCH + 1, 1024) == 0
+    pf = kmr._lib.kmr_prefill_workspace_bytes
+    assert pf(C.byref(cfg), 0, 1024) == 0 and pf(C.byref(cfg), 8, 0) == 0
+    assert pf(C.byref(cfg), 5, 1024) == kmr.workspace_bytes(cfg, 5, 1024)        # one chunk of 5 rows
+    assert pf(C.byref(cfg), 1000, 1024) == pf(C.byref(cfg), kmr.KMR_PREFILL_CHUNK, 1024) > n16
 
 
 @pytest.mark.parametrize("over,code", [

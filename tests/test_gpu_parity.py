@@ -270,8 +270,8 @@ def test_decode_step_full(kmr, full_pair, path):
 
 
 def test_prefill_full_size_matches_oracle_decode(kmr, full_pair):
-    """kmr_prefill of 70 tokens at the full model size (one 64-token chunk on the fused
-    matrix-core tiles, then 6 tokens on the VALU) against the oracle's decode step run
+    """kmr_prefill of 70 tokens at the full model size (one chunk: four 16-row tiles in
+    one fused matrix-core launch, then 6 rows on the VALU) against the oracle's decode step run
     token by token over the same cache row (kaminari page, section 04: prefill fills
     the static cache that decode extends): the last token's logits and token, every
     written K/V slot, and no other slot."""
@@ -282,7 +282,7 @@ def test_prefill_full_size_matches_oracle_decode(kmr, full_pair):
     pos3 = np.ascontiguousarray(np.arange(T, dtype=np.int32)[None].repeat(3, 0))
     log(f"prefill {T} tokens, 28 layers, from position 0 (oracle: {T} decode steps)")
     kv, kh, vh = make_caches(dims, synth.base_seed(w) + T, 1, M, "device")
-    ws = kmr.Workspace(full_pair.dev.cfg, min(T, kmr.KMR_MAX_BATCH), M)
+    ws = kmr.Workspace.for_prefill(full_pair.dev.cfg, T, M)
     nxt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     logits = torch.empty(dims.vocab, dtype=torch.float32, device="cuda")
     full_pair.dev.prefill(kv, 0, torch.from_numpy(tokens).cuda(), torch.from_numpy(pos3).cuda(), 0, nxt, ws,

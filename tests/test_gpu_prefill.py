@@ -8,7 +8,7 @@ is the argmax at the last prompt token).
   decode step run token by token over the same cache row, which is the same
   computation by the decode/prefill invariant.
 - Token counts cover one token, a single chunk that takes the matrix-core tiles
-  (group size 128), and several chunks of KMR_MAX_BATCH with a ragged last one.
+  (group size 128), and two chunks of KMR_PREFILL_CHUNK tokens with a ragged last one.
 - Only the prompt's slots of the chosen cache row change."""
 import dataclasses
 
@@ -47,7 +47,7 @@ def _np_layers(ora):
 def _run(kmr, pair, kv, row, tokens, pos3, start):
     dims = pair.dims
     T = len(tokens)
-    ws = kmr.Workspace(pair.dev.cfg, min(T, kmr.KMR_MAX_BATCH), kv.k.shape[3])
+    ws = kmr.Workspace.for_prefill(pair.dev.cfg, T, kv.k.shape[3])
     nxt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     logits = torch.empty(dims.vocab, dtype=torch.float32, device="cuda")
     pair.dev.prefill(kv, row, torch.from_numpy(tokens.astype(np.int32)).cuda(),
