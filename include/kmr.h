@@ -58,12 +58,24 @@ enum {
   KMR_STATUS_TOKEN = 2u,      /* a token id was outside [0, vocab): that row's
                                  embedding was taken as zero */
   KMR_STATUS_TIMEOUT = 4u,    /* a wait inside the persistent step kernel gave up
-                                 (no progress for ~1 s): outputs of that call are
-                                 invalid; re-initialise the workspace */
-  KMR_STATUS_TOPOLOGY = 8u    /* a work-group of the XCD-local step kernel read an XCD
+                                 (no progress for ~1 s): that call wrote -1 to every
+                                 next_ids entry and advanced nothing.  The bit is
+                                 sticky: kmr_status reports it without clearing it,
+                                 and every later persistent step on the workspace
+                                 writes -1 again and does nothing else, until
+                                 kmr_workspace_init re-initialises the workspace */
+  KMR_STATUS_TOPOLOGY = 8u,   /* a work-group of the XCD-local step kernel read an XCD
                                  id above 7 or found more groups on its XCD than the
                                  grid deals to one (diagnostic; such a call may also
                                  time out) */
+  KMR_STATUS_RANGE = 16u      /* a GEMV input exceeded the fp16 range in which the int4
+                                 products take their activations (|v| >= 65520): the
+                                 outputs of that call are invalid.  Residual-stream
+                                 and MLP inputs of the XCD-local persistent kernel are
+                                 staged with a power-of-two exponent and never raise
+                                 it; attention outputs and MLP activations elsewhere
+                                 are staged as they are, and normalised inputs are
+                                 bounded by sqrt(K) times the largest norm gain */
 };
 
 #define KMR_MAX_BATCH 64
@@ -79,6 +91,13 @@ enum {
                                 check (~20 us more per step; for callers that run other
                                 long kernels on the device concurrently).  Ignored on the
                                 per-phase path. */
+#define KMR_DEVICE_SCOPE_STORES 32u  /* XCD-local persistent kernel with every hand-off
+                                through device-scope stores, as it runs under stream capture
+                                or without a verified placement (cross-checks) */
+#define KMR_TEST_STALL 256u  /* failure-path tests only: the persistent kernel's consumers
+                                wait for hand-off tags that no producer writes and give up
+                                after 4096 polls, so every work-group exits through its
+                                bounded wait and the call ends with KMR_STATUS_TIMEOUT */
 
 /*
  * Model dimensions.  Supported by the kernels: head_dim 64 or 128;
@@ -161,10 +180,15 @@ size_t kmr_workspace_bytes(const kmr_config* cfg, int32_t batch, int32_t max_len
 size_t kmr_prefill_workspace_bytes(const kmr_config* cfg, int32_t n_tokens, int32_t max_len);
 
 /* Clears a workspace with a fill kernel on `stream`.  Call once after allocating
- * it and again after any call that returned an error; the decode calls leave
- * it ready for the next call.  The first call on a device also records where
- * the device places the work-groups of a one-group-per-CU grid (a small probe
- * kernel into the workspace and a synchronous copy of one word per CU). */
+ * it, and again after a call that returned an error or raised KMR_STATUS_TIMEOUT;
+ * the decode and prefill calls otherwise leave it ready for the next call.  One
+ * workspace may serve calls of any kind and batch size on the same config and
+ * max_len, as long as it is large enough for each: the words that persist between
+ * calls (status, step counter, arrival counters) sit in a fixed header, and the
+ * persistent kernels' exchange buffers at offsets that do not depend on the batch.
+ * The first call on a device also records where the device places the
+ * work-groups of a one-group-per-CU grid (a small probe kernel into the workspace
+ * and a synchronous copy of one word per CU). */
 int kmr_workspace_init(void* ws, size_t ws_bytes, kmr_stream_t stream);
 
 /*
@@ -304,7 +328,8 @@ int kmr_slot_admit(int32_t* token_ids, int32_t* positions, int32_t* cache_positi
 int kmr_slot_retire(uint8_t* finished, int32_t batch, int32_t row, kmr_stream_t stream);
 
 /* Synchronises `stream`, returns the sticky KMR_STATUS_* bits of `ws` in
- * *flags_out (host pointer) and clears them. */
+ * *flags_out (host pointer) and clears them, except KMR_STATUS_TIMEOUT, which
+ * only kmr_workspace_init clears. */
 int kmr_status(void* ws, kmr_stream_t stream, uint32_t* flags_out);
 
 /* Message for a KMR_E* code, and the detail of this thread's last failed call. */

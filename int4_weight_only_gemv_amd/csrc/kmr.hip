@@ -70,10 +70,20 @@ int check_config(const kmr_config* c) {
 }
 
 constexpr int kMaxStepGroups = 1024;   // lm_head partial slots of the persistent kernel
+constexpr int kStepBatchMax = 4;       // largest batch of the persistent kernels
 
+// Workspace layout.  Three parts:
+//   header       status word, step counter, arrival counters and the placement
+//                probe's words, at fixed offsets;
+//   exchange     the persistent kernels' tagged buffers, sized for their largest
+//                batch, at offsets that depend on the config and max_len only;
+//   per-phase    the per-phase kernels' buffers for `batch` rows.
+// So a workspace reused with another batch size or call kind (prefill, per-phase
+// or persistent decode) keeps its counters, and a word a per-phase call wrote never
+// sits where a persistent call polls for a tag.
 struct WsLayout {
   size_t status, cs, x, qkv, attn_o, act, part_o, part_ml, lm_part, total;
-  size_t step_ctr, lm_cnt, tx, tqkv, to, tact, tpart, lm_part2;
+  size_t step_ctr, lm_cnt, xarr, tx, tqkv, to, tact, tpart, lm_part2;
   size_t lx, sx, lqkv, lpart, lact, pO, pD, probe, pf, kpart;
   int kpart_rows;
   size_t xst, xst_cc, xst_cb;   // staged 16-row GEMV tile: [16][4][Kmax/32] x 16 B, [16][Kmax/32] x 8 B,
@@ -85,12 +95,34 @@ struct WsLayout {
 WsLayout ws_layout(const kmr_config* c, int B, int M) {
   WsLayout w{};
   const int D = c->head_dim, Hq = c->n_heads, Hkv = c->n_kv_heads, qpg = Hq / Hkv;
-  const int nqkv = (Hq + 2 * Hkv) * D;
+  const int nqkv = (Hq + 2 * Hkv) * D, PB = kStepBatchMax;
   w.ns = (M + kAttnSplit - 1) / kAttnSplit;
   w.ns_pp = (M + kAttnSplitPP - 1) / kAttnSplitPP;
   w.nblk_lm = c->vocab > 0 ? (c->vocab + kLmRowsPerBlock - 1) / kLmRowsPerBlock : 1;
-  size_t o = 0;
-  w.status = o; o += 256;
+  // header
+  w.status = 0;
+  w.step_ctr = 64;
+  w.lm_cnt = 128;
+  w.xarr = 256;   // 8 per-XCD arrival counters
+  size_t o = 512;
+  w.probe = o; o += align256((size_t)kMaxStepGroups * 4);
+  // exchange buffers of the persistent kernels (batch <= PB)
+  w.tx = o; o += align256((size_t)PB * c->hidden * 8);
+  w.tqkv = o; o += align256((size_t)PB * nqkv * 8);
+  w.to = o; o += align256((size_t)PB * Hq * D * 8);
+  w.tact = o; o += align256((size_t)PB * c->intermediate * 8);
+  w.tpart = o; o += align256((size_t)PB * Hkv * w.ns * qpg * (D + 2) * 8);
+  w.lm_part2 = o; o += align256((size_t)PB * kMaxStepGroups * 8);
+  o = (o + 4095) & ~(size_t)4095;
+  w.xz = stepx_sizes(PB, c->hidden, Hkv, D, qpg, c->intermediate, M);
+  w.lx = o; o += (size_t)kXcds * w.xz.lx * 8;
+  w.sx = o; o += (size_t)kXcds * w.xz.sx * 8;
+  w.lqkv = o; o += (size_t)kXcds * w.xz.lqkv * 8;
+  w.lpart = o; o += (size_t)kXcds * w.xz.lpart * 8;
+  w.lact = o; o += (size_t)kXcds * w.xz.lact * 8;
+  w.pO = o; o += align256((size_t)kXcds * PB * c->hidden * 8);
+  w.pD = o; o += align256((size_t)kXcds * PB * c->hidden * 8);
+  // per-phase buffers for B rows
   w.cs = o; o += align256((size_t)B * (D / 2) * 8);
   w.x = o; o += align256((size_t)B * c->hidden * 4);
   w.qkv = o; o += align256((size_t)B * nqkv * 4);
@@ -99,14 +131,6 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
   w.part_o = o; o += align256((size_t)B * Hkv * w.ns_pp * qpg * D * 4);
   w.part_ml = o; o += align256((size_t)B * Hkv * w.ns_pp * qpg * 8);
   w.lm_part = o; o += align256((size_t)B * w.nblk_lm * 8);
-  w.step_ctr = o; o += 256;
-  w.lm_cnt = o; o += 256;
-  w.tx = o; o += align256((size_t)B * c->hidden * 8);
-  w.tqkv = o; o += align256((size_t)B * nqkv * 8);
-  w.to = o; o += align256((size_t)B * Hq * D * 8);
-  w.tact = o; o += align256((size_t)B * c->intermediate * 8);
-  w.tpart = o; o += align256((size_t)B * Hkv * w.ns * qpg * (D + 2) * 8);
-  w.lm_part2 = o; o += align256((size_t)B * kMaxStepGroups * 8);
   {
     int kmax = c->hidden > Hq * D ? c->hidden : Hq * D;
     kmax = kmax > c->intermediate ? kmax : c->intermediate;
@@ -117,17 +141,6 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
     w.kpart_rows = (int)rows;
     w.kpart = o; o += align256((size_t)2 * rows * c->hidden * 4);   // split-K partials of O and down
   }
-  // XCD-local step kernel: per-XCD regions, then the device-wide partials
-  o = (o + 4095) & ~(size_t)4095;
-  w.xz = stepx_sizes(B, c->hidden, Hkv, D, qpg, c->intermediate, M);
-  w.lx = o; o += (size_t)kXcds * w.xz.lx * 8;
-  w.sx = o; o += (size_t)kXcds * w.xz.sx * 8;
-  w.lqkv = o; o += (size_t)kXcds * w.xz.lqkv * 8;
-  w.lpart = o; o += (size_t)kXcds * w.xz.lpart * 8;
-  w.lact = o; o += (size_t)kXcds * w.xz.lact * 8;
-  w.pO = o; o += align256((size_t)kXcds * B * c->hidden * 8);
-  w.pD = o; o += align256((size_t)kXcds * B * c->hidden * 8);
-  w.probe = o; o += align256((size_t)kMaxStepGroups * 4);
   w.pf = o; o += align256((size_t)4 * KMR_PREFILL_CHUNK * 4);   // prefill: a chunk's [3][C] positions, [C] cache positions
   w.total = o;
   return w;
@@ -392,7 +405,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   float2* cbg = at<float2>(ws, w.xst_cb);
   float* kpart = at<float>(ws, w.kpart);
   GemvArgs g{};
-  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.status = at<uint32_t>(ws, w.status); g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
   g.packed = static_cast<const uint8_t*>(L->qkv.packed);
   g.sz = static_cast<const uint32_t*>(L->qkv.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->in_norm); g.eps = c->rms_eps;
@@ -426,7 +439,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   ap.Hkv = Hkv; ap.NS = w.ns_pp; ap.QPG = Hq / Hkv; ap.D = D; ap.M = kv->max_len;
 
   g = GemvArgs{};
-  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.status = at<uint32_t>(ws, w.status); g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
   g.packed = static_cast<const uint8_t*>(L->o.packed);
   g.sz = static_cast<const uint32_t*>(L->o.sz);
   g.y = x; g.ldy = H; g.N = H; g.K = Hq * D; g.G = G; g.B = B;
@@ -441,7 +454,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   }
 
   g = GemvArgs{};
-  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.status = at<uint32_t>(ws, w.status); g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
   g.packed = static_cast<const uint8_t*>(L->gate_up.packed);
   g.sz = static_cast<const uint32_t*>(L->gate_up.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->post_norm); g.eps = c->rms_eps;
@@ -449,7 +462,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   launch_gemv<EPI_SILU, PRO_RMSNORM>(g, st);
 
   g = GemvArgs{};
-  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
+  g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.status = at<uint32_t>(ws, w.status); g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
   g.packed = static_cast<const uint8_t*>(L->down.packed);
   g.sz = static_cast<const uint32_t*>(L->down.sz);
   g.x = act; g.ldx = I; g.gain = nullptr;
@@ -737,7 +750,9 @@ static int decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_
   if (kv->n_layers != cfg->n_layers) return fail(KMR_ESHAPE, "kv cache has %d layers, model %d", kv->n_layers, cfg->n_layers);
   if (!token_ids || !positions || !cache_position || !next_ids || !ws)
     return fail(KMR_EINVAL, "null token_ids/positions/cache_position/next_ids/workspace");
-  if (flags & ~(KMR_ADVANCE | KMR_MULTI_KERNEL | KMR_DEVICE_WIDE | KMR_COOPERATIVE)) return fail(KMR_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(KMR_ADVANCE | KMR_MULTI_KERNEL | KMR_DEVICE_WIDE | KMR_COOPERATIVE | KMR_DEVICE_SCOPE_STORES |
+                KMR_TEST_STALL))
+    return fail(KMR_EINVAL, "unknown flags 0x%x", flags);
   const WsLayout w = ws_layout(cfg, batch, kv->max_len);
   if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -753,7 +768,7 @@ static int decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_
     a.kc = static_cast<uint16_t*>(kv->k); a.vc = static_cast<uint16_t*>(kv->v);
     a.status = at<uint32_t>(ws, w.status); a.step_ctr = at<uint32_t>(ws, w.step_ctr);
     a.lm_cnt = at<uint32_t>(ws, w.lm_cnt);
-    a.xarr = a.lm_cnt + 32;   // 8 counters, 128 bytes past lm_cnt in its 256-byte block
+    a.xarr = at<uint32_t>(ws, w.xarr);
     a.tx = at<uint64_t>(ws, w.tx); a.tqkv = at<uint64_t>(ws, w.tqkv);
     a.to = at<uint64_t>(ws, w.to); a.tact = at<uint64_t>(ws, w.tact);
     a.tpart = at<uint64_t>(ws, w.tpart);
@@ -773,6 +788,10 @@ static int decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_
     while ((1 << a.lgG) < a.G) ++a.lgG;
     a.M = kv->max_len; a.cacheB = kv->batch; a.NS = w.ns; a.pad_id = cfg->pad_id;
     a.eos_id = cfg->eos_id; a.flags = flags & KMR_ADVANCE; a.eps = cfg->rms_eps;
+    // KMR_TEST_STALL: consumers wait for a phase bit no producer sets (phases stay
+    // below 256), and give up after 4096 polls
+    a.tag_xor = (flags & KMR_TEST_STALL) ? 0x100u : 0u;
+    a.spin_limit = (flags & KMR_TEST_STALL) ? (1u << 12) : kSpinLimit;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg->head_dim));
     a.theta = cfg->rope_theta;
     a.sec0 = cfg->mrope_section[0]; a.sec1 = cfg->mrope_section[1]; a.sec2 = cfg->mrope_section[2];
@@ -790,7 +809,8 @@ static int decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_
       d.d_p = static_cast<const uint8_t*>(L.down.packed); d.d_s = static_cast<const uint32_t*>(L.down.sz);
     }
     if (!(flags & KMR_DEVICE_WIDE) && stepx_fits(cfg, batch, nwg)) {
-      a.intra_plain = xcd_placement_ok(at<void>(ws, w.probe), (size_t)kMaxStepGroups * 4, nwg, st) ? 1 : 0;
+      a.intra_plain = !(flags & KMR_DEVICE_SCOPE_STORES) &&
+                      xcd_placement_ok(at<void>(ws, w.probe), (size_t)kMaxStepGroups * 4, nwg, st);
       return launch_stepx(cfg, a, nwg, (flags & KMR_COOPERATIVE) != 0, st);
     }
     return launch_step(cfg, a, nwg, (flags & KMR_COOPERATIVE) != 0, st);
@@ -943,7 +963,8 @@ int kmr_status(void* ws, kmr_stream_t stream, uint32_t* flags_out) {
   if (hipMemcpyAsync(&v, ws, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess)
     return check_hip("status read") ? KMR_EHIP : fail(KMR_EHIP, "status read failed");
-  fill_zero(ws, 4, st);
+  // every bit but KMR_STATUS_TIMEOUT is cleared; that one stays until kmr_workspace_init
+  hipLaunchKernelGGL(k_status_keep, dim3(1), dim3(1), 0, st, static_cast<uint32_t*>(ws), (uint32_t)KMR_STATUS_TIMEOUT);
   *flags_out = v;
   return check_hip("status clear");
 }

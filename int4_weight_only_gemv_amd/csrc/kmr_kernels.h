@@ -18,11 +18,18 @@ constexpr int kGemvRowsPerWave = 2;
 constexpr int kLmRowsPerWave = 4;
 constexpr int kLmRowsPerBlock = 4 * kLmRowsPerWave;
 
+constexpr uint32_t kStatusRange = 16u;   // a staged GEMV input overflowed fp16
+
 __device__ __forceinline__ void raise_status(uint32_t* st, uint32_t bit) {
   __hip_atomic_fetch_or(st, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ fill
+
+// Clears every status bit outside `keep` (one thread).
+__global__ void k_status_keep(uint32_t* st, uint32_t keep) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *st &= keep;
+}
 
 __global__ void k_fill_zero(uint32_t* __restrict__ p, size_t words) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -313,6 +320,7 @@ struct GemvArgs {
   float2* cbg;            // ... and their sums per 128-column block [16][K/128] (k_gemv_stage16)
   float* kpart;           // split-K partials [2][kpart_rows][N] of an EPI_ADD product (or null),
   int kpart_rows, kpart_n;   // for N <= kpart_n
+  uint32_t* status;       // sticky status word (KMR_STATUS_RANGE when a staged input overflows fp16)
 };
 
 // LDS layout of k_gemv_int4 (byte offsets, 16-byte aligned).
@@ -334,8 +342,10 @@ __host__ __device__ inline GemvLds gemv_lds(int BT, int K, bool merged_input) {
 
 // One 32-column chunk e of a staged GEMV input: its four 16-byte words of fp16
 // magic-bias pairs (h[8j+i], h[8j+i+4]), odd columns divided by 16, to dst[j * CH]
-// for j < 4, and the chunk constants (1024 sum h + 8 sum u, sum u) returned.
-__device__ __forceinline__ float2 stage_chunk(const float (&e)[32], uint4* dst, int CH) {
+// for j < 4, and the chunk constants (1024 sum h + 8 sum u, sum u) returned.  A
+// value past the fp16 range (the sums then turn infinite or NaN) raises
+// KMR_STATUS_RANGE in *status when status is not null.
+__device__ __forceinline__ float2 stage_chunk(const float (&e)[32], uint4* dst, int CH, uint32_t* status) {
   float bsum = 0.f, usum = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -354,6 +364,7 @@ __device__ __forceinline__ float2 stage_chunk(const float (&e)[32], uint4* dst, 
     bsum += ev + od;
     usum += ev + 16.0f * od;
   }
+  if (status && !(fabsf(bsum) + fabsf(usum) <= 3.0e38f)) raise_status(status, kStatusRange);
   return make_float2(1024.0f * bsum + 8.0f * usum, usum);
 }
 
@@ -429,7 +440,7 @@ __device__ __forceinline__ void gemv_stage(const GemvArgs& a, unsigned char* sme
 #pragma unroll
       for (int i = 0; i < 32; ++i) e[i] = 0.f;
     }
-    cc[b * CH + c] = stage_chunk(e, xs + b * 4 * CH + c, CH);
+    cc[b * CH + c] = stage_chunk(e, xs + b * 4 * CH + c, CH, a.status);
   }
   __syncthreads();
 
@@ -590,7 +601,7 @@ __global__ __launch_bounds__(64) void k_gemv_stage16(GemvArgs a) {
     }
   }
   uint4 scratch[4];
-  const float2 C = stage_chunk(e, c < CH ? a.xsg + b * 4 * CH + c : scratch, c < CH ? CH : 1);
+  const float2 C = stage_chunk(e, c < CH ? a.xsg + b * 4 * CH + c : scratch, c < CH ? CH : 1, a.status);
   if (c < CH) a.ccg[b * CH + c] = C;
   // block constants: the 4 chunks of a 128-column block are lanes 4m .. 4m + 3
   float c1 = C.x, c2 = C.y;

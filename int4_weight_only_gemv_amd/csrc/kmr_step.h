@@ -96,6 +96,8 @@ struct StepArgs {
   // dims
   int B, H, Hq, Hkv, I, V, L, G, lgG, M, cacheB, NS, pad_id, eos_id;   // lgG = log2(G)
   uint32_t flags;
+  uint32_t tag_xor;         // 0; a test hook sets a phase bit no producer writes, so every wait gives up
+  uint32_t spin_limit;      // polls before a wait gives up
   uint64_t* trace;          // per-group phase timestamps (diagnostic builds only) or null
   float eps, scale_log2;
   double theta;
@@ -147,13 +149,13 @@ __device__ __forceinline__ bool group_failed(bool bad) {
 }
 
 // Polls `total` tagged words until all carry `tag`, then stores their values in
-// LDS at dst[place(i)].  Word i lives at src + addr(i).  Each thread issues all
+// LDS at dst[place(i)] (at most `lim` polls per pass).  Word i lives at src + addr(i).  Each thread issues all
 // its loads of a pass before checking any, so a poll costs one memory round
 // trip; `pre` runs after the first loads are issued (to overlap other work with
 // them).  Returns false, for the whole work-group, on timeout.
 template <int PT, typename Addr, typename Place, typename Pre, int NT = kStepThreads>
 __device__ __forceinline__ bool gather_tagged(const uint64_t* src, int total, uint32_t tag,
-                                              float* dst, Addr addr, Place place, Pre pre) {
+                                              float* dst, Addr addr, Place place, Pre pre, uint32_t lim) {
   const int tid = otid();
   bool ok = true;
   bool first = true;
@@ -177,7 +179,7 @@ __device__ __forceinline__ bool gather_tagged(const uint64_t* src, int total, ui
       for (int j = 0; j < PT; ++j)
         if (idx[j] < total) fresh &= (uint32_t)(v[j] >> 32) == tag;
       if (!fresh) {
-        if (++spins > kSpinLimit) { ok = false; break; }
+        if (++spins > lim) { ok = false; break; }
         __builtin_amdgcn_s_sleep(KMR_POLL_SLEEP);
       }
     } while (!fresh);
@@ -223,16 +225,20 @@ __device__ __forceinline__ float lane_xor4(float v) {
 // the magic-bias weight pairs).  An 8-column word lives in 8 consecutive lanes
 // (pairs formed with lane ^ 4), a 32-column chunk in 32 consecutive lanes, so K
 // must be a multiple of 32.  Every lane of the wave must call this (DPP).
+// Returns whether one of this thread's values overflowed fp16 (the caller raises
+// KMR_STATUS_RANGE).
 template <int PT>
-__device__ __forceinline__ void stage_values(const float (&e)[PT], const bool (&has)[PT],
+__device__ __forceinline__ bool stage_values(const float (&e)[PT], const bool (&has)[PT],
                                              const int (&wb)[PT], const int (&wk)[PT], int K,
                                              uint4* xs, float2* cc) {
   const int lane = otid() & 63, CH = K >> 5, i8 = lane & 7;
   uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
+  bool over = false;
 #pragma unroll
   for (int j = 0; j < PT; ++j) {
     const _Float16 h = (_Float16)((i8 & 1) ? e[j] * 0.0625f : e[j]);
     const float hf = (float)h;
+    over |= has[j] && !(fabsf(hf) <= 65504.f);
     const float uf = (i8 & 1) ? 16.0f * hf : hf;
     const float other = lane_xor4(hf);
     // chunk sums over the 32 lanes of the chunk
@@ -250,6 +256,7 @@ __device__ __forceinline__ void stage_values(const float (&e)[PT], const bool (&
       }
     }
   }
+  return over;
 }
 
 // Gathers a tagged [B][K] input (PT words per thread per pass, consecutive lanes
@@ -258,7 +265,7 @@ __device__ __forceinline__ void stage_values(const float (&e)[PT], const bool (&
 template <int BT, int PT, int NT = kStepThreads>
 __device__ __forceinline__ bool gather_stage(const uint64_t* src, int K, int B, uint32_t tag,
                                              const uint16_t* gain, float eps, uint4* xs, float2* cc,
-                                             float* red) {
+                                             float* red, uint32_t lim, uint32_t* status) {
   const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int total = B * K;
   float inv[BT];
@@ -295,7 +302,7 @@ __device__ __forceinline__ bool gather_stage(const uint64_t* src, int K, int B, 
       for (int j = 0; j < PT; ++j)
         if (has[j]) fresh &= (uint32_t)(v[j] >> 32) == tag;
       if (!fresh) {
-        if (++spins > kSpinLimit) { ok = false; break; }
+        if (++spins > lim) { ok = false; break; }
         __builtin_amdgcn_s_sleep(KMR_POLL_SLEEP);
       }
     } while (!fresh);
@@ -331,7 +338,7 @@ __device__ __forceinline__ bool gather_stage(const uint64_t* src, int K, int B, 
       for (int b = 1; b < BT; ++b) if (wb[j] == b) iv = inv[b];
       e[j] = gain ? (x[j] * iv) * bf16_to_f32(graw[j]) : x[j];
     }
-    stage_values<PT>(e, has, wb, wk, K, xs, cc);
+    if (stage_values<PT>(e, has, wb, wk, K, xs, cc)) raise_status(status, kStatusRange);
   }
   __syncthreads();
   return true;
@@ -524,6 +531,29 @@ __host__ __device__ inline StepLds step_lds(int BT, int KMAX, int RPBX, int H, i
   return s;
 }
 
+// A step that cannot complete (a wait gave up, or an earlier call on this
+// workspace did): KMR_STATUS_TIMEOUT is raised and every row's next id becomes
+// -1, so a caller that feeds next_ids back without reading the status decodes
+// nothing further.  Cache positions and positions stay unadvanced (the advance
+// belongs to the last group's tail, which no group reaches once one has given
+// up).  Any thread may call this; threads 0..B-1 write.
+__device__ __forceinline__ void step_abandon(const StepArgs& a) {
+  const int tid = threadIdx.x;
+  if (tid == 0) raise_status(a.status, kStatusTimeout);
+  if (tid < a.B) a.next[tid] = -1;
+}
+
+// Whether the workspace carries KMR_STATUS_TIMEOUT from an earlier call: its
+// arrival counter and tags are then stale, and the step refuses to run until the
+// workspace is re-initialised (the bit survives kmr_status).  Called by every
+// thread with the same result: thread 0 reads the word, the barrier shares it.
+__device__ __forceinline__ bool step_refused(const StepArgs& a, int* s_flag) {
+  if (threadIdx.x == 0)
+    *s_flag = (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusTimeout) != 0;
+  __syncthreads();
+  return *s_flag != 0;
+}
+
 // Final RMSNorm, lm_head rows of this group with the argmax of each batch row,
 // and (in the last group to finish) the argmax over all groups, the greedy-step
 // bookkeeping and the step counter.  xin holds the gathered fp32 [B][H] input.
@@ -632,7 +662,9 @@ __device__ __forceinline__ void step_tail(const StepArgs& a, float* xin, float* 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(a.lm_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // release: this group's argmax partial is visible before its arrival counts;
+    // acquire: the last group to arrive then reads every group's partial
+    const uint32_t prev = __hip_atomic_fetch_add(a.lm_cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == (uint32_t)(nwg - 1);
   }
   __syncthreads();
@@ -708,8 +740,15 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
   __shared__ int s_last;
   __shared__ int s_c[16];
 
+  if (step_refused(a, &s_last)) {
+    step_abandon(a);
+    return;
+  }
   const uint32_t step = (a.step_ctr[0] + 1u) & 0x7fffffu;
   auto tag = [&](int phase) -> uint32_t { return (step << 9) | (uint32_t)phase; };
+  // the tag a consumer waits for (the producer's, unless a test hook skews it)
+  auto ctag = [&](int phase) -> uint32_t { return tag(phase) ^ a.tag_xor; };
+  const uint32_t lim = a.spin_limit;
   bool alive = true;
 
   // ---- step prologue: cache positions, RoPE tables, embedding rows of this group
@@ -756,7 +795,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
         WRows<NR, 1> w;
         wrows_load(w, Ly.qkv_p, Ly.qkv_s, H, a.lgG, row, ok);
         if (r0 == 0) {
-          if (!gather_stage<BT, 4 * BT>(a.tx, H, B, tag(ph), Ly.in_norm, a.eps, xs, cc, red)) { alive = false; break; }
+          if (!gather_stage<BT, 4 * BT>(a.tx, H, B, ctag(ph), Ly.in_norm, a.eps, xs, cc, red, lim, a.status)) { alive = false; break; }
         }
         KMR_TRACE_MARK(tev + 0);
         float out[NR][BT];
@@ -818,8 +857,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
         const int qo = g * QPG * D, ko = (Hq + g) * D - QPG * D, vo = (Hq + Hkv + g) * D - (QPG + 1) * D;
         auto addr = [=](int i) { return (size_t)(i < QPG * D ? qo + i : (i < (QPG + 1) * D ? ko + i : vo + i)); };
         auto place = [](int i) { return i; };
-        if (!gather_tagged<(QPG + 2) * D / kStepThreads + 1>(rowp, (QPG + 2) * D, tag(ph + 1), qv, addr,
-                                                            place, NoPre())) {
+        if (!gather_tagged<(QPG + 2) * D / kStepThreads + 1>(rowp, (QPG + 2) * D, ctag(ph + 1), qv, addr,
+                                                            place, NoPre(), lim)) {
           alive = false;
           break;
         }
@@ -960,8 +999,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
         const int nt = ns - t0 < kMergeChunk ? ns - t0 : kMergeChunk;
         auto addr = [=](int i) { return (size_t)t0 * PW + i; };
         auto place = [](int i) { return i; };
-        if (!gather_tagged<kMergeChunk * PW / kStepThreads + 1>(psrc, nt * PW, tag(ph + 2), xin, addr,
-                                                               place, NoPre())) {
+        if (!gather_tagged<kMergeChunk * PW / kStepThreads + 1>(psrc, nt * PW, ctag(ph + 2), xin, addr,
+                                                               place, NoPre(), lim)) {
           alive = false;
           break;
         }
@@ -999,7 +1038,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
       WRows<NR, 1> w;
       wrows_load(w, Ly.o_p, Ly.o_s, QD, a.lgG, row, ok);
       if (r2 == 0) {
-        if (!gather_stage<BT, 4 * BT>(a.to, QD, B, tag(ph + 3), nullptr, a.eps, xs, cc, red)) { alive = false; break; }
+        if (!gather_stage<BT, 4 * BT>(a.to, QD, B, ctag(ph + 3), nullptr, a.eps, xs, cc, red, lim, a.status)) { alive = false; break; }
       }
       KMR_TRACE_MARK(tev + 4);
       float out[NR][BT];
@@ -1032,7 +1071,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
         WRows<2 * NP, 1> w;
         wrows_load(w, Ly.gu_p, Ly.gu_s, H, a.lgG, row, ok);
         if (r0 == 0) {
-          if (!gather_stage<BT, 4 * BT>(a.tx, H, B, tag(ph + 4), Ly.post_norm, a.eps, xs, cc, red)) { alive = false; break; }
+          if (!gather_stage<BT, 4 * BT>(a.tx, H, B, ctag(ph + 4), Ly.post_norm, a.eps, xs, cc, red, lim, a.status)) { alive = false; break; }
         }
         KMR_TRACE_MARK(tev + 6);
         float out[2 * NP][BT];
@@ -1062,7 +1101,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
       WRows<NR, CPL> w;
       wrows_load(w, Ly.d_p, Ly.d_s, I, a.lgG, row, ok);
       if (r2 == 0) {
-        if (!gather_stage<BT, 12>(a.tact, I, B, tag(ph + 5), nullptr, a.eps, xs, cc, red)) { alive = false; break; }
+        if (!gather_stage<BT, 12>(a.tact, I, B, ctag(ph + 5), nullptr, a.eps, xs, cc, red, lim, a.status)) { alive = false; break; }
       }
       KMR_TRACE_MARK(tev + 8);
       float out[NR][BT];
@@ -1082,7 +1121,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
   }
 
   if (!alive) {
-    if (tid == 0) raise_status(a.status, kStatusTimeout);
+    step_abandon(a);
     return;
   }
 
@@ -1092,10 +1131,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a) {
     auto addr = [](int i) { return (size_t)i; };
     auto place = [](int i) { return i; };
     const bool ok = B * K <= kStepThreads * 4
-                        ? gather_tagged<4>(a.tx, B * K, tag(1 + 6 * a.L), xin, addr, place, NoPre())
-                        : gather_tagged<12>(a.tx, B * K, tag(1 + 6 * a.L), xin, addr, place, NoPre());
+                        ? gather_tagged<4>(a.tx, B * K, ctag(1 + 6 * a.L), xin, addr, place, NoPre(), lim)
+                        : gather_tagged<12>(a.tx, B * K, ctag(1 + 6 * a.L), xin, addr, place, NoPre(), lim);
     if (!ok) {
-      if (tid == 0) raise_status(a.status, kStatusTimeout);
+      step_abandon(a);
       return;
     }
   }

@@ -31,13 +31,15 @@ if len(_hip_runtimes()) > 1:
     raise ImportError(f"two HIP runtimes are mapped: {_hip_runtimes()}")
 
 KMR_OK, KMR_EINVAL, KMR_ESHAPE, KMR_ENOMEM, KMR_EHIP = 0, -1, -2, -3, -4
-KMR_STATUS_CACHE_POS, KMR_STATUS_TOKEN, KMR_STATUS_TIMEOUT, KMR_STATUS_TOPOLOGY = 1, 2, 4, 8
+KMR_STATUS_CACHE_POS, KMR_STATUS_TOKEN, KMR_STATUS_TIMEOUT, KMR_STATUS_TOPOLOGY, KMR_STATUS_RANGE = 1, 2, 4, 8, 16
 KMR_MAX_BATCH = 64
 KMR_PREFILL_CHUNK = 128
 KMR_ADVANCE = 1
 KMR_MULTI_KERNEL = 2
 KMR_DEVICE_WIDE = 4
 KMR_COOPERATIVE = 8
+KMR_DEVICE_SCOPE_STORES = 32
+KMR_TEST_STALL = 256
 
 _i32, _p = C.c_int32, C.c_void_p
 
@@ -149,6 +151,10 @@ def workspace_bytes(cfg: Config, batch: int, max_len: int) -> int:
     return int(_lib.kmr_workspace_bytes(C.byref(cfg), batch, max_len))
 
 
+def prefill_workspace_bytes(cfg: Config, n_tokens: int, max_len: int) -> int:
+    return int(_lib.kmr_prefill_workspace_bytes(C.byref(cfg), n_tokens, max_len))
+
+
 class Workspace:
     def __init__(self, cfg: Config, batch: int, max_len: int, device="cuda", stream=None, nbytes=None):
         n = workspace_bytes(cfg, batch, max_len) if nbytes is None else nbytes
@@ -161,7 +167,7 @@ class Workspace:
     def for_prefill(cls, cfg: Config, n_tokens: int, max_len: int, device="cuda", stream=None):
         """The workspace of a kmr_prefill of n_tokens (kmr_prefill_workspace_bytes)."""
         return cls(cfg, 0, max_len, device, stream,
-                   nbytes=int(_lib.kmr_prefill_workspace_bytes(C.byref(cfg), n_tokens, max_len)))
+                   nbytes=prefill_workspace_bytes(cfg, n_tokens, max_len))
 
     @property
     def ptr(self):
@@ -170,6 +176,10 @@ class Workspace:
     @property
     def nbytes(self):
         return self.buf.numel()
+
+    def init(self, stream=None) -> None:
+        """kmr_workspace_init again (after an error or KMR_STATUS_TIMEOUT)."""
+        _check(_lib.kmr_workspace_init(self.ptr, self.nbytes, _stream(stream)))
 
     def status(self, stream=None) -> int:
         v = C.c_uint32(0)
@@ -270,14 +280,17 @@ class DeviceModel:
                     cache_position: torch.Tensor, next_ids: torch.Tensor, ws: Workspace,
                     finished: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
                     advance: bool = False, multi_kernel: bool = False, device_wide: bool = False,
-                    cooperative: bool = False, shared_prefix: int = 0, stream=None) -> torch.Tensor:
+                    cooperative: bool = False, shared_prefix: int = 0, device_scope_stores: bool = False,
+                    extra_flags: int = 0, stream=None) -> torch.Tensor:
         """shared_prefix > 0: kmr_decode_step_prefix (every row holds the same K/V in
-        cache positions [0, shared_prefix); the per-phase kernels read it once)."""
+        cache positions [0, shared_prefix); the per-phase kernels read it once).
+        extra_flags: further KMR_* flag bits, passed through."""
         B = token_ids.shape[0]
         assert token_ids.dtype == torch.int32 and next_ids.dtype == torch.int32
         assert finished is None or finished.dtype == torch.uint8
         flags = ((KMR_ADVANCE if advance else 0) | (KMR_MULTI_KERNEL if multi_kernel else 0)
-                 | (KMR_DEVICE_WIDE if device_wide else 0) | (KMR_COOPERATIVE if cooperative else 0))
+                 | (KMR_DEVICE_WIDE if device_wide else 0) | (KMR_COOPERATIVE if cooperative else 0)
+                 | (KMR_DEVICE_SCOPE_STORES if device_scope_stores else 0) | int(extra_flags))
         args = (C.byref(self.cfg), C.byref(self.cmodel), C.byref(kv.desc), _ptr(token_ids), _ptr(positions),
                 _ptr(cache_position), _ptr(finished), B, _ptr(next_ids), _ptr(logits), flags)
         if shared_prefix:

@@ -345,31 +345,161 @@ def test_persistent_and_per_phase_paths_agree(kmr, full_pair):
 
 
 def test_decode_step_batch4_lockstep(kmr, full_pair):
+    """The batch-4 workload as specified: 64 consecutive greedy steps with on-device
+    advance (row 3 finished throughout; rows whose cache position would reach
+    max_len finish by length), both sides fed the oracle's token every step."""
     w = synth.WORKLOADS["batch4"]
-    log("decode_step 28 layers, batch 4 (row 3 finished), 6 lockstep steps with advance")
+    log(f"decode_step 28 layers, batch 4 (row 3 finished), {w.steps} lockstep steps with advance")
     kv, kh, vh = make_caches(w.dims, synth.base_seed(w), w.batch, w.max_len, "device")
-    _step_case(kmr, full_pair, kv, kh, vh, synth.step_inputs(w), w.max_len, steps=6, advance=True)
+    _step_case(kmr, full_pair, kv, kh, vh, synth.step_inputs(w), w.max_len, steps=w.steps, advance=True)
 
 
-def test_decode_step_long16_sampled_rows(kmr, full_pair):
+def test_decode_step_long16_every_row(kmr, full_pair):
+    """The long-context workload (16 rows, 8192-slot cache, cache positions 2048..8000)
+    over 4 advancing steps, every row checked: the rows go to the oracle in groups of
+    four, each group over all 4 steps on a freshly drawn cache (the oracle holds 4 of
+    the 16 rows at a time).  Rows of the group take the oracle's token; the others
+    take their own."""
     w = synth.WORKLOADS["long16"]
-    rows = [0, 11]
-    log(f"decode_step 28 layers, batch 16, max_len 8192; oracle on rows {rows}")
+    B, M, steps = w.batch, w.max_len, 4
     inp = synth.step_inputs(w)
-    kv, kh, vh = make_caches(w.dims, synth.base_seed(w), w.batch, w.max_len, "device", host_rows=rows)
-    B = w.batch
-    ws = kmr.Workspace(full_pair.dev.cfg, B, w.max_len)
-    pos_d = torch.from_numpy(inp["positions"]).cuda()
-    cpos_d = torch.from_numpy(inp["cache_position"]).cuda()
+    for g in range(B // 4):
+        rows = list(range(4 * g, 4 * g + 4))
+        log(f"decode_step 28 layers, batch 16, max_len 8192, {steps} steps; oracle on rows {rows}")
+        kv, kh, vh = make_caches(w.dims, synth.base_seed(w), B, M, "device", host_rows=rows)
+        ws = kmr.Workspace(full_pair.dev.cfg, B, M)
+        ids = inp["ids"].copy()
+        pos_d = torch.from_numpy(inp["positions"].copy()).cuda()
+        cpos_d = torch.from_numpy(inp["cache_position"].copy()).cuda()
+        rpos = np.ascontiguousarray(inp["positions"][:, rows])
+        rcpos = inp["cache_position"][rows].copy()
+        nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
+        logits = torch.empty((B, w.dims.vocab), dtype=torch.float32, device="cuda")
+        for s in range(steps):
+            full_pair.dev.decode_step(kv, torch.from_numpy(ids).cuda(), pos_d, cpos_d, nxt, ws, logits=logits,
+                                      advance=True)
+            torch.cuda.synchronize()
+            ref = full_pair.ora.decode_step(kh, vh, ids[rows], rpos, rcpos, advance=True)
+            got = nxt.cpu().numpy()
+            _check_step(got[rows], logits.cpu().numpy()[rows], ref, f"step {s}")
+            assert np.array_equal(pos_d.cpu().numpy()[:, rows], rpos)
+            assert np.array_equal(cpos_d.cpu().numpy()[rows], rcpos)
+            ids = got.astype(np.int32)
+            ids[rows] = ref["next"]
+        assert ws.status() == 0
+        del kv, kh, vh
+        torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ graph capture
+
+def _graph_lockstep(kmr, pair, kv, kh, vh, inp, M, flags, replays=16):
+    """One kmr_decode_step with KMR_ADVANCE captured in a HIP graph (through torch's
+    graph capture on a side stream) and replayed `replays` times; before each
+    replay the oracle's token goes into the captured token buffer (lockstep), and
+    after it tokens, logits, positions and cache positions are checked."""
+    B = len(inp["ids"])
+    ws = kmr.Workspace(pair.dev.cfg, B, M)
+    ids = inp["ids"].copy()
+    pos, cpos, fin = inp["positions"].copy(), inp["cache_position"].copy(), inp["finished"].copy()
+    ids_d = torch.from_numpy(ids.copy()).cuda()
+    pos_d, cpos_d = torch.from_numpy(pos.copy()).cuda(), torch.from_numpy(cpos.copy()).cuda()
+    fin_d = torch.from_numpy(fin.copy()).cuda()
     nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
-    logits = torch.empty((B, w.dims.vocab), dtype=torch.float32, device="cuda")
-    full_pair.dev.decode_step(kv, torch.from_numpy(inp["ids"]).cuda(), pos_d, cpos_d, nxt, ws,
-                              logits=logits)
+    logits = torch.empty((B, pair.dims.vocab), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    ref = full_pair.ora.decode_step(kh, vh, inp["ids"][rows], np.ascontiguousarray(inp["positions"][:, rows]),
-                                    inp["cache_position"][rows].copy())
-    _check_step(nxt.cpu().numpy()[rows], logits.cpu().numpy()[rows], ref, "rows")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pair.dev.decode_step(kv, ids_d, pos_d, cpos_d, nxt, ws, finished=fin_d, logits=logits, advance=True,
+                             **flags)
+    torch.cuda.synchronize()
+    # capture runs nothing: state is as before
+    assert np.array_equal(cpos_d.cpu().numpy(), cpos)
+    written = set()
+    for r in range(replays):
+        ids_d.copy_(torch.from_numpy(ids))
+        written.update((b, int(c)) for b, c in enumerate(cpos) if 0 <= c < M)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = pair.ora.decode_step(kh, vh, ids, pos, cpos, finished=fin, advance=True)
+        _check_step(nxt.cpu().numpy(), logits.cpu().numpy(), ref, f"replay {r}")
+        assert np.array_equal(pos_d.cpu().numpy(), pos)
+        assert np.array_equal(cpos_d.cpu().numpy(), cpos)
+        assert np.array_equal(fin_d.cpu().numpy(), fin)
+        ids = ref["next"].astype(np.int32)
     assert ws.status() == 0
+    del graph
+    return written
+
+
+@pytest.mark.parametrize("path", ["persistent", "device_scope_stores"])
+def test_decode_step_full_graph_replay(kmr, full_pair, path):
+    w = synth.WORKLOADS["step"]
+    log(f"decode_step 28 layers, batch 1, captured once, 16 replays in lockstep ({path})")
+    kv, kh, vh = make_caches(w.dims, synth.base_seed(w), 1, w.max_len, "device")
+    flags = {"device_scope_stores": path == "device_scope_stores"}
+    written = _graph_lockstep(kmr, full_pair, kv, kh, vh, synth.step_inputs(w), w.max_len, flags)
+    _check_cache(kv, kh, vh, written)
+
+
+@pytest.mark.parametrize("path", ["persistent", "device_scope_stores", "device_wide", "multi_kernel"])
+def test_decode_step_kv8_graph_replay(kmr, kv8_pair, path):
+    w = synth.WORKLOADS["kv8"]
+    log(f"decode_step kv8 batch 4, captured once, 16 replays in lockstep ({path})")
+    kv, kh, vh = make_caches(w.dims, synth.base_seed(w), w.batch, w.max_len, "host")
+    flags = {"device_scope_stores": path == "device_scope_stores", "device_wide": path == "device_wide",
+             "multi_kernel": path == "multi_kernel"}
+    written = _graph_lockstep(kmr, kv8_pair, kv, kh, vh, synth.step_inputs(w), w.max_len, flags)
+    _check_cache(kv, kh, vh, written)
+
+
+# ------------------------------------------------------------------ full size: failure paths, magnitudes, M-RoPE layout
+
+@pytest.mark.parametrize("wl", ["step", "batch4"])
+def test_full_stalled_step_fails_hard_then_recovers(kmr, full_pair, wl):
+    """The constant-size persistent kernel (batch 1 and batch 4): a stalled step
+    writes -1 and advances nothing, a plain step on the same workspace is refused,
+    and a re-initialised workspace decodes like the oracle."""
+    from tests.test_gpu_robustness import stall_then_recover
+    log(f"decode_step 28 layers, {wl}: stalled step, refusal, re-initialised workspace")
+    stall_then_recover(kmr, full_pair, synth.WORKLOADS[wl], {})
+
+
+def test_full_residual_outliers_1e5(kmr, full_pair):
+    """The constant-size kernel at batch 4 with residual-stream channels of 3e4..1.2e5
+    (embedding columns set to those values for every token), 2 lockstep steps."""
+    w = synth.WORKLOADS["batch4"]
+    log("decode_step 28 layers, batch 4, residual outlier channels up to 1.2e5, 2 steps")
+    outl = {3: 6.0e4, 1000: -1.0e5, 1025: 3.1e4, 2047: 1.2e5}
+    emb_d, emb_h = full_pair.dev.globals["embed"], full_pair.ora.g["embed"]
+    saved = {ch: (emb_d[:, ch].clone(), emb_h[:, ch].copy()) for ch in outl}
+    try:
+        for ch, val in outl.items():
+            emb_d[:, ch] = val
+            emb_h[:, ch] = oracle.as_u16(torch.tensor([val], dtype=torch.bfloat16))[0]
+        kv, kh, vh = make_caches(w.dims, synth.base_seed(w), w.batch, w.max_len, "device")
+        _step_case(kmr, full_pair, kv, kh, vh, synth.step_inputs(w), w.max_len, steps=2, advance=True)
+    finally:
+        for ch, (d, h) in saved.items():
+            emb_d[:, ch] = d
+            emb_h[:, ch] = h
+
+
+def test_full_contiguous_mrope(kmr, full_pair):
+    """The constant-size kernel with the contiguous M-RoPE layout (mrope_interleaved = 0)
+    on the batch-4 workload, whose rows have distinct t, h, w positions."""
+    w = synth.WORKLOADS["batch4"]
+    log("decode_step 28 layers, batch 4, contiguous M-RoPE sections, 2 steps")
+    full_pair.dev.cfg.mrope_interleaved = 0
+    full_pair.ora.cdims.mrope_interleaved = 0
+    try:
+        inp = synth.step_inputs(w)
+        log(f"  positions (t, h, w per row): {inp['positions'].T.tolist()}")
+        kv, kh, vh = make_caches(w.dims, synth.base_seed(w), w.batch, w.max_len, "device")
+        _step_case(kmr, full_pair, kv, kh, vh, inp, w.max_len, steps=2, advance=True)
+    finally:
+        full_pair.dev.cfg.mrope_interleaved = 1
+        full_pair.ora.cdims.mrope_interleaved = 1
 
 
 @pytest.mark.parametrize("B,rows", [(40, [0, 17, 39]), (64, [0, 33, 63])])
