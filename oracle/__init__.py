@@ -68,6 +68,8 @@ def lib() -> C.CDLL:
         L.ora_attend.argtypes = [_p, _p, _p, _i64, _i64, _p]
         L.ora_bf16_round.argtypes = [_f64]
         L.ora_bf16_round.restype = _f64
+        L.ora_silu.argtypes = [_f64]
+        L.ora_silu.restype = _f64
         L.ora_decode_layer.argtypes = [C.POINTER(OraDims), C.POINTER(OraLayer), _i64, _p, _p,
                                        _i64, _i64, _p, _p, _p]
         L.ora_decode_step.argtypes = [C.POINTER(OraDims), C.POINTER(OraModel), _p, _p, _i64, _i64,
@@ -151,6 +153,10 @@ def attend(q: np.ndarray, k_u16: np.ndarray, v_u16: np.ndarray) -> np.ndarray:
 
 def bf16_round(x: float) -> float:
     return float(lib().ora_bf16_round(float(x)))
+
+
+def silu(x: float) -> float:
+    return float(lib().ora_silu(float(x)))
 
 
 def make_dims(dims) -> OraDims:

@@ -260,6 +260,9 @@ void ora_attend(const double* q, const uint16_t* k, const uint16_t* v, int64_t n
 
 static double silu(double a) { return a / (1.0 + exp(-a)); }
 
+/* SiLU as the MLP uses it, exported so that tests can pin it to closed forms. */
+double ora_silu(double a) { return silu(a); }
+
 /* One decoder layer for B independent rows, in place on x [B][H].
  * Order (kaminari section 03: TextAttention with fused QKV, Mrope, MLP; the
  * standard Qwen3 decoder block, which the pages name but do not spell out):

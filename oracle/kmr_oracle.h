@@ -67,6 +67,7 @@ void ora_mrope(double* v, int64_t D, const int32_t* pos3, const int32_t* section
 void ora_attend(const double* q, const uint16_t* k, const uint16_t* v, int64_t n_pos,
                 int64_t D, double* out);
 double ora_bf16_round(double x);
+double ora_silu(double a);   /* a / (1 + e^-a), the MLP's gate activation */
 int ora_decode_layer(const ora_dims* d, const ora_layer* w, int64_t layer,
                      uint16_t* kcache, uint16_t* vcache, int64_t B, int64_t M,
                      double* x, const int32_t* pos, const int32_t* cpos);

@@ -184,3 +184,78 @@ def test_bf16_rounding_ties_and_neighbours():
     ref = torch.from_numpy(r.astype(np.float32)).to(torch.bfloat16).double().numpy()
     got = np.array([oracle.bf16_round(float(np.float32(x))) for x in r])
     assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------ SiLU and the MLP's gate/up order
+# The MLP of a Qwen3 decoder layer is down(silu(gate) * up) with [gate ; up] the rows
+# of the fused gate-up projection (kaminari page, section 05: fused gate-up).  SiLU
+# is x * sigmoid(x); scipy's expit is an independent sigmoid.
+
+@pytest.mark.parametrize("x", [-40.0, -7.5, -1.0, -1e-3, 0.0, 1e-3, 0.5, 1.0, 3.0, 40.0])
+def test_silu_matches_x_times_library_sigmoid(x):
+    assert oracle.silu(x) == pytest.approx(x * float(sps.expit(x)), rel=1e-14, abs=1e-300)
+
+
+def test_silu_closed_forms():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1.0) == pytest.approx(1.0 / (1.0 + np.exp(-1.0)), rel=1e-15)
+    # silu(x) - silu(-x) = x (sigmoid(x) + sigmoid(-x) = 1)
+    for x in (0.3, 2.0, 11.0):
+        assert oracle.silu(x) - oracle.silu(-x) == pytest.approx(x, rel=1e-14)
+    # large |x|: the identity above and the vanishing negative side
+    assert oracle.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert abs(oracle.silu(-40.0)) < 1e-15 and oracle.silu(-40.0) < 0.0
+
+
+def _mlp_only_layer(dims, rng, gate_std, up_std, zero_gate=False):
+    """bf16 source weights of one layer whose O projection is all zero, so that the
+    layer's update of x is its MLP alone."""
+    H, D, I = dims.hidden, dims.head_dim, dims.intermediate
+    bf = lambda a: torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16)
+    wgu = np.concatenate([rng.standard_normal((I, H)) * gate_std, rng.standard_normal((I, H)) * up_std])
+    if zero_gate:
+        wgu[:I] = 0.0
+    return {
+        "in_norm": bf(rng.uniform(0.5, 1.5, H)), "q_norm": bf(rng.uniform(0.5, 1.5, D)),
+        "k_norm": bf(rng.uniform(0.5, 1.5, D)), "post_norm": bf(rng.uniform(0.5, 1.5, H)),
+        "wqkv": bf(rng.standard_normal((dims.qkv_rows, H)) * 0.02),
+        "wo": bf(np.zeros((H, dims.n_heads * D))),
+        "wgu": bf(wgu), "wd": bf(rng.standard_normal((H, I)) * 0.02),
+    }
+
+
+@pytest.mark.parametrize("zero_gate", [False, True])
+def test_layer_mlp_is_down_of_silu_gate_times_up(zero_gate):
+    """Through the oracle's whole layer: x_out - x_in = Wd (silu(g) * u) with
+    [g ; u] = Wgu RMSNorm(x_in; post_norm), from the dequantized weights (pinned by
+    the quantizer tests) and scipy's sigmoid.  Gate rows are drawn larger than up
+    rows, so that silu applied to the up half, or the halves swapped, fails; with
+    the gate rows zero the MLP adds exactly nothing."""
+    from int4_weight_only_gemv_amd import synth
+    dims = synth.TINY
+    rng = np.random.default_rng(404)
+    w = _mlp_only_layer(dims, rng, 0.2, 0.05, zero_gate)
+    model = oracle.Model(dims, [w])
+    q = model.q[0]
+    B, M = 2, 8
+    kc = np.zeros((1, B, dims.n_kv_heads, M, dims.head_dim), np.uint16)
+    vc = np.zeros_like(kc)
+    x_in = rng.standard_normal((B, dims.hidden)) * 3.0
+    x = x_in.copy()
+    model.decode_layer(0, kc, vc, x, np.zeros((3, B), np.int32), np.array([2, 5], np.int32))
+    G, I = dims.group_size, dims.intermediate
+    wgu = oracle.dequant(*q["wgu"], G)
+    wd = oracle.dequant(*q["wd"], G)
+    for b in range(B):
+        h = oracle.rmsnorm(x_in[b], q["post_norm"], dims.rms_eps)
+        gu = wgu @ h
+        g, u = gu[:I], gu[I:]
+        want = wd @ (g * sps.expit(g) * u)
+        got = x[b] - x_in[b]
+        if zero_gate:
+            assert np.all(got == 0.0)
+        else:
+            assert np.max(np.abs(g)) > 2.0     # the nonlinearity is exercised
+            np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-12 * np.abs(want).max())
+            swapped = wd @ (u * sps.expit(u) * g)
+            assert np.abs(swapped - want).max() > 1e-3 * np.abs(want).max()
