@@ -91,6 +91,23 @@ enum {
                                 check (~20 us more per step; for callers that run other
                                 long kernels on the device concurrently).  Ignored on the
                                 per-phase path. */
+#define KMR_BATCH_INVARIANT 16u  /* one arithmetic form for every batch size, so that a
+                                row's next id, logits and cache writes are bit for bit the
+                                same whatever other rows share its batch ("The Ghost in the
+                                Batch", "The Fork in the Code" and "The Fix: Three Options":
+                                a kernel choice that depends on the batch changes a row's
+                                bits).  The step then runs on the per-phase kernels with the
+                                matrix-core int4 GEMV for every 16-row tile (padded; used when
+                                group_size and the GEMV K are multiples of 128, else the VALU
+                                GEMV in 8-row tiles), the matrix-core lm_head for every tile
+                                (hidden 2048; else the VALU lm_head in 8-row tiles), no
+                                split-K and the separate split-merge kernel: the form depends
+                                on the model shapes only.  Without this flag the default
+                                path takes the fastest form for the batch, and a row's
+                                results agree across batch sizes within the parity
+                                tolerance but not bit for bit (the persistent kernel for
+                                batch 1..4, the VALU GEMV tiles for 5..8, the matrix-core
+                                tiles from 9). */
 #define KMR_DEVICE_SCOPE_STORES 32u  /* XCD-local persistent kernel with every hand-off
                                 through device-scope stores, as it runs under stream capture
                                 or without a verified placement (cross-checks) */
@@ -234,7 +251,9 @@ int kmr_decode_layer(const kmr_config* cfg, const kmr_layer* layer_w, int32_t la
  * as one kernel per phase, in batch tiles of at most 16 rows (batch up to
  * KMR_MAX_BATCH).  A tile of 9..16 rows takes the matrix-core int4 GEMV when the
  * group size is a multiple of 128, and the matrix-core lm_head when hidden is
- * 2048; the choice depends on the shapes and the tile size only.
+ * 2048; the choice depends on the shapes and the tile size only.  So the
+ * arithmetic of a row changes where the batch crosses 4/5 and 8/9 (within the
+ * parity tolerance); KMR_BATCH_INVARIANT pins one form for every batch size.
  */
 int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
                     const int32_t* token_ids, int32_t* positions, int32_t* cache_position,

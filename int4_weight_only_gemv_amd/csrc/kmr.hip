@@ -232,10 +232,10 @@ inline bool gemv_mfma_staged(const GemvArgs& a) {
 // split only adds the partial traffic and a launch.)
 constexpr int kSplitBelowGroups = 256;   // MI355X compute units
 template <int EPI, int PRO>
-void launch_mfma_staged(const GemvArgs& a, int tiles, hipStream_t st) {
+void launch_mfma_staged(const GemvArgs& a, int tiles, hipStream_t st, bool inv) {
   hipLaunchKernelGGL((k_gemv_stage16<PRO>), dim3(16 * tiles, (a.K + 2047) / 2048), dim3(64), 0, st, a);
   const size_t lds = (size_t)4 * (EPI == EPI_SILU ? 2 : 1) * 256 * 4;   // wave partials
-  const bool split = EPI == EPI_ADD && a.kpart && a.N <= a.kpart_n && (a.K / 128) % 2 == 0 &&
+  const bool split = !inv && EPI == EPI_ADD && a.kpart && a.N <= a.kpart_n && (a.K / 128) % 2 == 0 &&
                      a.kpart_rows >= 16 * tiles && ((a.N + 15) / 16) * tiles < kSplitBelowGroups;
   hipLaunchKernelGGL((k_gemv_int4_mfma<16, EPI, PRO, true>), dim3((a.N + 15) / 16, tiles, split ? 2 : 1),
                      dim3(256), lds, st, a);
@@ -246,10 +246,21 @@ void launch_mfma_staged(const GemvArgs& a, int tiles, hipStream_t st) {
   }
 }
 
+// inv (KMR_BATCH_INVARIANT): one form for every tile whatever its rows -- the staged
+// matrix-core product (padded to 16 rows, no split K) when the shapes allow it, else
+// the VALU product in its 8-row instantiation -- so a row's bits never depend on
+// the batch.  (The merge prologue never runs in this mode: k_attn_combine merges.)
 template <int EPI, int PRO>
-void launch_gemv_tile(const GemvArgs& a, hipStream_t st) {
+void launch_gemv_tile(const GemvArgs& a, hipStream_t st, bool inv) {
+  if (inv) {
+    if constexpr (PRO != PRO_ATTN) {
+      if (gemv_mfma_staged<EPI, PRO>(a)) launch_mfma_staged<EPI, PRO>(a, 1, st, true);
+      else launch_gemv_cpl<8, EPI, PRO>(a, st);
+    }
+    return;
+  }
   if (a.B >= 9 && gemv_mfma_staged<EPI, PRO>(a)) {
-    if constexpr (PRO != PRO_ATTN) launch_mfma_staged<EPI, PRO>(a, 1, st);
+    if constexpr (PRO != PRO_ATTN) launch_mfma_staged<EPI, PRO>(a, 1, st, false);
     return;
   }
   if (a.B >= 9 && gemv_mfma_shape<EPI, PRO>(a) && a.K >= 256 * (EPI == EPI_SILU ? 2 : 1)) {
@@ -273,14 +284,14 @@ void launch_gemv_tile(const GemvArgs& a, hipStream_t st) {
 // per tile, and the tiles stream the same weights at the same time.  Every row's
 // result is the same as in a launch of its own tile.
 template <int EPI, int PRO>
-void launch_gemv(GemvArgs a, hipStream_t st) {
+void launch_gemv(GemvArgs a, hipStream_t st, bool inv = false) {
   int B = a.B;
   if constexpr (PRO != PRO_ATTN) {
     const int full = B / 16;
     if (full >= 2 && gemv_mfma_staged<EPI, PRO>(a)) {
       GemvArgs t = a;
       t.B = 16 * full;
-      launch_mfma_staged<EPI, PRO>(t, full, st);
+      launch_mfma_staged<EPI, PRO>(t, full, st, inv);
       if (B == 16 * full) return;
       a.x += (size_t)16 * full * a.ldx;   // the remaining rows as before
       a.y += (size_t)16 * full * a.ldy;
@@ -290,15 +301,18 @@ void launch_gemv(GemvArgs a, hipStream_t st) {
   }
   int tile = 16;
   const size_t per_row = (size_t)a.K * 9 / 4 + (PRO == PRO_ATTN ? (size_t)a.K * 4 : 0);
-  if (!(B >= 9 && gemv_mfma_staged<EPI, PRO>(a)))   // (staged in memory: no LDS bound)
+  if (inv) {
+    if (!gemv_mfma_staged<EPI, PRO>(a)) tile = 8;
+  } else if (!(B >= 9 && gemv_mfma_staged<EPI, PRO>(a))) {   // (staged in memory: no LDS bound)
     while (tile > 1 && tile * per_row + 1024 > 150 * 1024) tile >>= 1;
+  }
   for (int b0 = 0; b0 < B; b0 += tile) {
     GemvArgs t = a;
     t.B = B - b0 < tile ? B - b0 : tile;
     t.b0 = a.b0 + b0;
     if (t.x) t.x = a.x + (size_t)b0 * a.ldx;
     t.y = a.y + (size_t)b0 * a.ldy;
-    launch_gemv_tile<EPI, PRO>(t, st);
+    launch_gemv_tile<EPI, PRO>(t, st, inv);
   }
 }
 
@@ -368,15 +382,25 @@ void launch_lmhead_mfma(const LmArgs& a, hipStream_t st) {
 }
 
 // Batch tiles of at most 16 rows (input rows, logits rows and argmax partials offset).
-void launch_lmhead(const LmArgs& a, hipStream_t st) {
-  for (int b0 = 0; b0 < a.B; b0 += 16) {
+// inv (KMR_BATCH_INVARIANT): the matrix-core lm_head for every tile when hidden is
+// 2048, else the VALU lm_head in its 8-row instantiation over tiles of 8 rows.
+void launch_lmhead(const LmArgs& a, hipStream_t st, bool inv = false) {
+  const bool mfma = a.K == 2048 && a.nblk == (a.V + 15) / 16;
+  const int tile = inv && !mfma ? 8 : 16;
+  for (int b0 = 0; b0 < a.B; b0 += tile) {
     LmArgs t = a;
-    t.B = a.B - b0 < 16 ? a.B - b0 : 16;
+    t.B = a.B - b0 < tile ? a.B - b0 : tile;
     t.x = a.x + (size_t)b0 * a.K;
     t.logits = a.logits ? a.logits + (size_t)b0 * a.V : nullptr;
     t.part = a.part + (size_t)b0 * a.nblk;
-    if (lmhead_mfma_fits(t)) launch_lmhead_mfma(t, st);
-    else launch_lmhead_tile(t, st);
+    if (inv) {
+      if (mfma) launch_lmhead_mfma(t, st);
+      else launch_lm_cpl<8>(t, st);
+    } else if (lmhead_mfma_fits(t)) {
+      launch_lmhead_mfma(t, st);
+    } else {
+      launch_lmhead_tile(t, st);
+    }
   }
 }
 
@@ -393,7 +417,7 @@ bool fuse_attn_merge(int B, int ns) { return (size_t)B * ns <= 16; }
 // attends (two attention passes), so that each token sees the ones before it.
 void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr_kv* kv, float* x,
                    const int32_t* cpos, int B, void* ws, const WsLayout& w, hipStream_t st,
-                   int prefix_splits = 0, int fixed_row = 0) {
+                   int prefix_splits = 0, int fixed_row = 0, bool inv = false) {
   const int H = c->hidden, D = c->head_dim, Hq = c->n_heads, Hkv = c->n_kv_heads;
   const int nqkv = (Hq + 2 * Hkv) * D, I = c->intermediate, G = c->group_size;
   float* qkv = at<float>(ws, w.qkv);
@@ -410,7 +434,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   g.sz = static_cast<const uint32_t*>(L->qkv.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->in_norm); g.eps = c->rms_eps;
   g.y = qkv; g.ldy = nqkv; g.N = nqkv; g.K = H; g.G = G; g.B = B;
-  launch_gemv<EPI_STORE, PRO_RMSNORM>(g, st);
+  launch_gemv<EPI_STORE, PRO_RMSNORM>(g, st, inv);
 
   AttnArgs a{};
   const size_t layer_stride = (size_t)kv->batch * Hkv * kv->max_len * D;
@@ -443,14 +467,14 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   g.packed = static_cast<const uint8_t*>(L->o.packed);
   g.sz = static_cast<const uint32_t*>(L->o.sz);
   g.y = x; g.ldy = H; g.N = H; g.K = Hq * D; g.G = G; g.B = B;
-  if (fuse_attn_merge(B, w.ns_pp)) {
+  if (!inv && fuse_attn_merge(B, w.ns_pp)) {
     g.ap = ap;
     launch_gemv<EPI_ADD, PRO_ATTN>(g, st);
   } else {
     const int threads = 8 * B * Hq * (D / 4);   // 8 lanes per 4 output dims
     hipLaunchKernelGGL(k_attn_combine, dim3((threads + 255) / 256), dim3(256), 0, st, ap, ao, B, Hq);
     g.x = ao; g.ldx = Hq * D;
-    launch_gemv<EPI_ADD, PRO_PLAIN>(g, st);
+    launch_gemv<EPI_ADD, PRO_PLAIN>(g, st, inv);
   }
 
   g = GemvArgs{};
@@ -459,7 +483,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   g.sz = static_cast<const uint32_t*>(L->gate_up.sz);
   g.x = x; g.ldx = H; g.gain = static_cast<const uint16_t*>(L->post_norm); g.eps = c->rms_eps;
   g.y = act; g.ldy = I; g.N = I; g.K = H; g.G = G; g.B = B;
-  launch_gemv<EPI_SILU, PRO_RMSNORM>(g, st);
+  launch_gemv<EPI_SILU, PRO_RMSNORM>(g, st, inv);
 
   g = GemvArgs{};
   g.xsg = xsg; g.ccg = ccg; g.cbg = cbg; g.status = at<uint32_t>(ws, w.status); g.kpart = kpart; g.kpart_rows = w.kpart_rows; g.kpart_n = H;
@@ -467,7 +491,7 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   g.sz = static_cast<const uint32_t*>(L->down.sz);
   g.x = act; g.ldx = I; g.gain = nullptr;
   g.y = x; g.ldy = H; g.N = H; g.K = I; g.G = G; g.B = B;
-  launch_gemv<EPI_ADD, PRO_PLAIN>(g, st);
+  launch_gemv<EPI_ADD, PRO_PLAIN>(g, st, inv);
 }
 
 // ---------------------------------------------------------------- persistent step
@@ -600,11 +624,12 @@ int launch_stepx(const kmr_config* c, StepArgs& a, int nwg, bool coop, hipStream
   return B == 1 ? launch_stepx_k<1, 64>(c, a, nwg, coop, st) : launch_stepx_k<4, 64>(c, a, nwg, coop, st);
 }
 
+// The device-wide kernel runs its 4-row instantiation at every batch of 1..4, so
+// that a row's bits do not depend on the batch it is in (its 1-row instantiation
+// compiled to different arithmetic for some products).
 int launch_step(const kmr_config* c, StepArgs& a, int nwg, bool coop, hipStream_t st) {
-  const int B = a.B;
-  if (c->head_dim == 128)
-    return B == 1 ? launch_step_k<1, 128>(c, a, nwg, coop, st) : launch_step_k<4, 128>(c, a, nwg, coop, st);
-  return B == 1 ? launch_step_k<1, 64>(c, a, nwg, coop, st) : launch_step_k<4, 64>(c, a, nwg, coop, st);
+  if (c->head_dim == 128) return launch_step_k<4, 128>(c, a, nwg, coop, st);
+  return launch_step_k<4, 64>(c, a, nwg, coop, st);
 }
 
 void enqueue_prep(const kmr_config* c, const uint16_t* embed, const int32_t* ids,
@@ -751,12 +776,13 @@ static int decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_
   if (!token_ids || !positions || !cache_position || !next_ids || !ws)
     return fail(KMR_EINVAL, "null token_ids/positions/cache_position/next_ids/workspace");
   if (flags & ~(KMR_ADVANCE | KMR_MULTI_KERNEL | KMR_DEVICE_WIDE | KMR_COOPERATIVE | KMR_DEVICE_SCOPE_STORES |
-                KMR_TEST_STALL))
+                KMR_BATCH_INVARIANT | KMR_TEST_STALL))
     return fail(KMR_EINVAL, "unknown flags 0x%x", flags);
   const WsLayout w = ws_layout(cfg, batch, kv->max_len);
   if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (!(flags & KMR_MULTI_KERNEL) && prefix_splits == 0 && step_kernel_fits(cfg, batch)) {
+  const bool inv = (flags & KMR_BATCH_INVARIANT) != 0;
+  if (!(flags & KMR_MULTI_KERNEL) && !inv && prefix_splits == 0 && step_kernel_fits(cfg, batch)) {
     int nwg = 0;
     if ((rc = device_cus(&nwg))) return rc;
     StepArgs a{};
@@ -819,13 +845,13 @@ static int decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_
   enqueue_prep(cfg, static_cast<const uint16_t*>(model->embed), token_ids, finished, positions, x,
                batch, ws, w, st);
   for (int l = 0; l < cfg->n_layers; ++l)
-    enqueue_layer(cfg, &model->layers[l], l, kv, x, cache_position, batch, ws, w, st, prefix_splits);
+    enqueue_layer(cfg, &model->layers[l], l, kv, x, cache_position, batch, ws, w, st, prefix_splits, 0, inv);
   LmArgs la{};
   la.x = x; la.gain = static_cast<const uint16_t*>(model->final_norm);
   la.W = static_cast<const uint16_t*>(model->lm_head);
   la.logits = logits; la.part = at<float2>(ws, w.lm_part);
   la.V = cfg->vocab; la.K = cfg->hidden; la.B = batch; la.nblk = w.nblk_lm; la.eps = cfg->rms_eps;
-  launch_lmhead(la, st);
+  launch_lmhead(la, st, inv);
   LmFinishArgs f{};
   f.part = la.part; f.finished_in = finished; f.finished = finished; f.next = next_ids;
   f.cpos = cache_position; f.pos = positions;

@@ -529,7 +529,8 @@ __global__ __launch_bounds__(256) void k_gemv_int4(GemvArgs a) {
             d = fdot2(p[i][4 * q + 2], xv[q].z, d);
             d = fdot2(p[i][4 * q + 3], xv[q].w, d);
           }
-          acc[i][b] += bf16_lo(sw[i][j]) * (d - C.x) + bf16_hi(sw[i][j]) * C.y;
+          // explicit fused ops: the same arithmetic in every instantiation and row
+          acc[i][b] = __builtin_fmaf(bf16_lo(sw[i][j]), d - C.x, __builtin_fmaf(bf16_hi(sw[i][j]), C.y, acc[i][b]));
         }
       }
     }
@@ -1153,10 +1154,10 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
 #pragma unroll
           for (int r = 0; r < RPW; ++r) {
             float t = acc[r][b];
-            t += bf16_lo(w[r][j].x) * h0.x; t += bf16_hi(w[r][j].x) * h0.y;
-            t += bf16_lo(w[r][j].y) * h0.z; t += bf16_hi(w[r][j].y) * h0.w;
-            t += bf16_lo(w[r][j].z) * h1.x; t += bf16_hi(w[r][j].z) * h1.y;
-            t += bf16_lo(w[r][j].w) * h1.z; t += bf16_hi(w[r][j].w) * h1.w;
+            t = __builtin_fmaf(bf16_lo(w[r][j].x), h0.x, t); t = __builtin_fmaf(bf16_hi(w[r][j].x), h0.y, t);
+            t = __builtin_fmaf(bf16_lo(w[r][j].y), h0.z, t); t = __builtin_fmaf(bf16_hi(w[r][j].y), h0.w, t);
+            t = __builtin_fmaf(bf16_lo(w[r][j].z), h1.x, t); t = __builtin_fmaf(bf16_hi(w[r][j].z), h1.y, t);
+            t = __builtin_fmaf(bf16_lo(w[r][j].w), h1.z, t); t = __builtin_fmaf(bf16_hi(w[r][j].w), h1.w, t);
             acc[r][b] = t;
           }
         }

@@ -433,7 +433,8 @@ __device__ __forceinline__ void wave_dot_c(const WRows<NR, CPL>& w, int K, int B
             d = fdot2(p[4 * q + 2], xv[b][q].z, d);
             d = fdot2(p[4 * q + 3], xv[b][q].w, d);
           }
-          acc[i][b] += s * (d - C[b].x) + z * C[b].y;
+          // explicit fused ops: the same arithmetic in every instantiation and row
+          acc[i][b] = __builtin_fmaf(s, d - C[b].x, __builtin_fmaf(z, C[b].y, acc[i][b]));
         }
       }
     }
@@ -620,10 +621,10 @@ __device__ __forceinline__ void step_tail(const StepArgs& a, float* xin, float* 
 #pragma unroll
           for (int r = 0; r < LR; ++r) {
             float t = acc[r][b];
-            t += bf16_lo(w[r][j].x) * h0.x; t += bf16_hi(w[r][j].x) * h0.y;
-            t += bf16_lo(w[r][j].y) * h0.z; t += bf16_hi(w[r][j].y) * h0.w;
-            t += bf16_lo(w[r][j].z) * h1.x; t += bf16_hi(w[r][j].z) * h1.y;
-            t += bf16_lo(w[r][j].w) * h1.z; t += bf16_hi(w[r][j].w) * h1.w;
+            t = __builtin_fmaf(bf16_lo(w[r][j].x), h0.x, t); t = __builtin_fmaf(bf16_hi(w[r][j].x), h0.y, t);
+            t = __builtin_fmaf(bf16_lo(w[r][j].y), h0.z, t); t = __builtin_fmaf(bf16_hi(w[r][j].y), h0.w, t);
+            t = __builtin_fmaf(bf16_lo(w[r][j].z), h1.x, t); t = __builtin_fmaf(bf16_hi(w[r][j].z), h1.y, t);
+            t = __builtin_fmaf(bf16_lo(w[r][j].w), h1.z, t); t = __builtin_fmaf(bf16_hi(w[r][j].w), h1.w, t);
             acc[r][b] = t;
           }
         }

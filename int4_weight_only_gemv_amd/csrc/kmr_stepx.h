@@ -150,7 +150,7 @@ __device__ __forceinline__ void narrow_dot(const WNarrow& w, int KS, int B, cons
           d = fdot2(p[4 * q + 2], xv[q].z, d);
           d = fdot2(p[4 * q + 3], xv[q].w, d);
         }
-        acc[b] += s * (d - C.x) + z * C.y;
+        acc[b] = __builtin_fmaf(s, d - C.x, __builtin_fmaf(z, C.y, acc[b]));
       }
     }
   }

@@ -38,6 +38,7 @@ KMR_ADVANCE = 1
 KMR_MULTI_KERNEL = 2
 KMR_DEVICE_WIDE = 4
 KMR_COOPERATIVE = 8
+KMR_BATCH_INVARIANT = 16
 KMR_DEVICE_SCOPE_STORES = 32
 KMR_TEST_STALL = 256
 
@@ -281,7 +282,7 @@ class DeviceModel:
                     finished: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
                     advance: bool = False, multi_kernel: bool = False, device_wide: bool = False,
                     cooperative: bool = False, shared_prefix: int = 0, device_scope_stores: bool = False,
-                    extra_flags: int = 0, stream=None) -> torch.Tensor:
+                    batch_invariant: bool = False, extra_flags: int = 0, stream=None) -> torch.Tensor:
         """shared_prefix > 0: kmr_decode_step_prefix (every row holds the same K/V in
         cache positions [0, shared_prefix); the per-phase kernels read it once).
         extra_flags: further KMR_* flag bits, passed through."""
@@ -290,7 +291,8 @@ class DeviceModel:
         assert finished is None or finished.dtype == torch.uint8
         flags = ((KMR_ADVANCE if advance else 0) | (KMR_MULTI_KERNEL if multi_kernel else 0)
                  | (KMR_DEVICE_WIDE if device_wide else 0) | (KMR_COOPERATIVE if cooperative else 0)
-                 | (KMR_DEVICE_SCOPE_STORES if device_scope_stores else 0) | int(extra_flags))
+                 | (KMR_DEVICE_SCOPE_STORES if device_scope_stores else 0)
+                 | (KMR_BATCH_INVARIANT if batch_invariant else 0) | int(extra_flags))
         args = (C.byref(self.cfg), C.byref(self.cmodel), C.byref(kv.desc), _ptr(token_ids), _ptr(positions),
                 _ptr(cache_position), _ptr(finished), B, _ptr(next_ids), _ptr(logits), flags)
         if shared_prefix:

@@ -1,23 +1,28 @@
 """Batch invariance of the decode step, bit for bit ("The Ghost in the Batch":
-the result of a row must not depend on which other rows share its batch).
+the result of a row must not depend on which other rows share its batch; "The Fork
+in the Code" and "The Fix: Three Options": a kernel choice made by batch size
+changes a row's bits).
 
-A row decoded alone (batch 1) and the same row decoded among three others
-(batch 4) must give identical logits, next token and cache writes.  The splits of
-the attention depend on the row's own cache position only and every reduction
-runs in a fixed order, so the two runs take the same arithmetic steps even though
-they use different kernel instantiations.  This holds for the XCD-local
-persistent kernel (the default) and for the per-phase kernels; the device-wide
-persistent kernel agrees with them within the parity tolerance only.  At the
-Qwen3-VL-2B text-decoder size the XCD-local kernel runs its constant-size form,
-whose gate/up product goes through the matrix cores at every batch size; that case
-is checked on the full 28-layer model.
+Default path.  A row decoded alone (batch 1) and the same row decoded among three
+others (batch 4) give identical logits, next token and cache writes on every
+persistent kernel and on the per-phase kernels: attention splits depend on the
+row's own cache position only, every reduction runs in a fixed order, and the
+device-wide kernel runs one instantiation for every batch of 1..4.  Across 4/5 and
+8/9 the default path changes kernels, and rows then agree within the parity
+tolerance only.
+
+KMR_BATCH_INVARIANT.  One arithmetic form for every batch size: the same row at
+batch 1, 4, 5, 9, 16 and 64 (full size) gives the same bits, and that form matches
+the oracle within the parity tolerance.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
+
 from int4_weight_only_gemv_amd import synth
-from tests.gpu_util import build_pair, log, make_caches
+from tests.gpu_util import MARGIN, TOL, build_pair, log, make_caches, max_rel
 
 pytestmark = pytest.mark.gpu
 
@@ -46,15 +51,16 @@ def _run_model(kmr, dev, vocab, kv, ids, pos, cpos, fin, path):
     nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
     logits = torch.empty((B, vocab), dtype=torch.float32, device="cuda")
     dev.decode_step(kv, torch.from_numpy(ids).cuda(), torch.from_numpy(pos).cuda(),
-                         torch.from_numpy(cpos).cuda(), nxt, ws, finished=torch.from_numpy(fin).cuda(),
-                         logits=logits, multi_kernel=(path == "multi_kernel"),
-                         device_wide=(path == "device_wide"), cooperative=(path == "cooperative"))
+                    torch.from_numpy(cpos).cuda(), nxt, ws, finished=torch.from_numpy(fin).cuda(),
+                    logits=logits, multi_kernel=(path == "multi_kernel"),
+                    device_wide=(path == "device_wide"), cooperative=(path == "cooperative"),
+                    batch_invariant=(path == "batch_invariant"))
     torch.cuda.synchronize()
     assert ws.status() == 0
     return nxt.cpu().numpy(), logits.cpu()
 
 
-@pytest.mark.parametrize("path", ["persistent", "multi_kernel"])
+@pytest.mark.parametrize("path", ["persistent", "device_wide", "multi_kernel", "batch_invariant"])
 def test_row_alone_equals_row_in_batch(kmr, kv8_pair, path):
     w = synth.WORKLOADS["kv8"]
     M = w.max_len
@@ -117,3 +123,73 @@ def test_row_alone_equals_row_in_batch_full_size(kmr):
     log(f"  cooperative launch: logits bitwise equal to the plain launch: {torch.equal(logitsc, logits4)}")
     assert torch.equal(logitsc, logits4) and np.array_equal(nextc, next4)
     assert torch.equal(kvc.k, kv4.k) and torch.equal(kvc.v, kv4.v)
+
+
+def _row_in_batches(kmr, dev, dims, seed, M, batches, target, place, vocab):
+    """Decodes the row `target` (id, (t, h, w), cache position) with
+    KMR_BATCH_INVARIANT inside batches of the given sizes, at batch row place(B),
+    the other rows drawn at random; returns per batch size (next id, logits row,
+    K and V written at the row's cache position)."""
+    tid, tpos, tc = target
+    base, _, _ = make_caches(dims, seed, 1, M, "device", host_rows=[])
+    out = {}
+    for B in batches:
+        r = place(B)
+        rng = np.random.default_rng(31 * B)
+        cpos = rng.integers(0, M - 1, B).astype(np.int32)
+        ids = rng.integers(0, vocab, B).astype(np.int32)
+        pos = np.stack([cpos, cpos // 2, cpos // 3]).astype(np.int32)
+        cpos[r], ids[r], pos[:, r] = tc, tid, tpos
+        kv, _, _ = make_caches(dims, seed + B, B, M, "device", host_rows=[])
+        kv.k[:, r:r + 1].copy_(base.k)
+        kv.v[:, r:r + 1].copy_(base.v)
+        nxt, logits = _run_model(kmr, dev, vocab, kv, ids, np.ascontiguousarray(pos), cpos,
+                                 np.zeros(B, np.uint8), "batch_invariant")
+        out[B] = (int(nxt[r]), logits[r].clone(), kv.k[:, r, :, tc].clone(), kv.v[:, r, :, tc].clone())
+        del kv
+        torch.cuda.empty_cache()
+    return out, base
+
+
+def _assert_same_bits(out, label):
+    ref_b = min(out)
+    n0, l0, k0, v0 = out[ref_b]
+    for B, (n, l, k, v) in out.items():
+        same = torch.equal(l, l0) and torch.equal(k, k0) and torch.equal(v, v0) and n == n0
+        log(f"  {label}: batch {B}: next {n}, logits/K/V bitwise equal to batch {ref_b}: {same}"
+            + ("" if same else f", max logits diff {float((l - l0).abs().max()):.3e}"))
+        assert same
+
+
+def test_batch_invariant_flag_kv8(kmr, kv8_pair):
+    """kv8 (group 64, hidden 512): the VALU GEMV and lm_head forms in 8-row tiles."""
+    w = synth.WORKLOADS["kv8"]
+    log("KMR_BATCH_INVARIANT, kv8: one row at batch 1, 3, 4, 5, 9, 16")
+    target = (37, np.array([200, 100, 66], np.int32), 200)
+    out, _ = _row_in_batches(kmr, kv8_pair.dev, w.dims, synth.base_seed(w), w.max_len, [1, 3, 4, 5, 9, 16],
+                             target, lambda B: B - 1, w.dims.vocab)
+    _assert_same_bits(out, "kv8")
+
+
+def test_batch_invariant_flag_full_size(kmr):
+    """The 28-layer model: the matrix-core GEMV and lm_head forms for every tile.
+    The row sits at a different batch row each time (first, inside a tile, last);
+    the form is checked against the oracle at batch 1."""
+    w = synth.WORKLOADS["step"]
+    dims, seed, M = w.dims, synth.base_seed(w), w.max_len
+    log("KMR_BATCH_INVARIANT at full size: building the 28-layer model and its oracle copy")
+    pair = build_pair(dims, seed, "device", with_globals=True)
+    target = (151, np.array([700, 350, 233], np.int32), 700)
+    places = {1: 0, 4: 3, 5: 2, 9: 8, 16: 9, 64: 37}
+    out, base = _row_in_batches(kmr, pair.dev, dims, seed, M, [1, 4, 5, 9, 16, 64], target,
+                                lambda B: places[B], dims.vocab)
+    _assert_same_bits(out, "full size")
+    # the invariant form against the oracle (batch 1, cache row as before the step)
+    kh, vh = oracle.as_u16(base.k), oracle.as_u16(base.v)
+    ref = pair.ora.decode_step(kh, vh, np.array([target[0]], np.int32), target[1].reshape(3, 1).copy(),
+                               np.array([target[2]], np.int32))
+    n1, l1, _, _ = out[1]
+    err = max_rel(l1.numpy()[None], ref["logits"])
+    log(f"  oracle: logits max_rel {err:.3e}, next {n1} vs {int(ref['next'][0])} (margin {float(ref['margin'][0]):.4f})")
+    assert err <= TOL
+    assert ref["margin"][0] <= MARGIN or n1 == int(ref["next"][0])
