@@ -79,6 +79,7 @@ enum {
 };
 
 #define KMR_MAX_BATCH 64
+#define KMR_STATIC_WORKSPACE_BYTES (48u << 20)  /* the array kmr_decode_step_static uses */
 #define KMR_PREFILL_CHUNK 128   /* prompt tokens per chunk of kmr_prefill */
 #define KMR_ADVANCE 1u
 #define KMR_MULTI_KERNEL 2u  /* run the step as one kernel per phase instead of the
@@ -111,6 +112,10 @@ enum {
 #define KMR_DEVICE_SCOPE_STORES 32u  /* XCD-local persistent kernel with every hand-off
                                 through device-scope stores, as it runs under stream capture
                                 or without a verified placement (cross-checks) */
+#define KMR_CLEAR_WORKSPACE 64u  /* kmr_decode_step_static only: clear its static array
+                                (a fill kernel) before the step, as kmr_workspace_init clears a
+                                workspace; needed after a step that wrote -1 (KMR_EINVAL on the
+                                calls that take a workspace) */
 #define KMR_TEST_STALL 256u  /* failure-path tests only: the persistent kernel's consumers
                                 wait for hand-off tags that no producer writes and give up
                                 after 4096 polls, so every work-group exits through its
@@ -259,6 +264,29 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
                     const int32_t* token_ids, int32_t* positions, int32_t* cache_position,
                     uint8_t* finished, int32_t batch, int32_t* next_ids, float* logits,
                     uint32_t flags, void* ws, size_t ws_bytes, kmr_stream_t stream);
+
+/*
+ * kmr_decode_step_static -- kmr_decode_step without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The workspace is a static array of
+ * KMR_STATIC_WORKSPACE_BYTES in the library's device code, one per device, held
+ * until the process ends; this call allocates nothing.  Same arguments, kernels
+ * and results as kmr_decode_step.  KMR_ENOMEM when kmr_workspace_bytes(cfg, batch,
+ * kv->max_len) exceeds the array (48 MiB: every batch up to KMR_MAX_BATCH at
+ * max_len 8192 for the Qwen3-VL-2B text decoder).  The array keeps the last call's
+ * contents: when the layout (config, max_len or batch-dependent size) differs from
+ * the previous call's on the device, the call first clears it with a fill kernel
+ * on `stream` (recorded too if the call is captured).  All calls on one device
+ * share the array, so calls that overlap in time on one device race and must be
+ * ordered by the caller (one stream).  Its status bits are not readable; a step
+ * whose waits gave up writes -1 to next_ids, as kmr_decode_step does, and so do
+ * later persistent steps until a call with KMR_CLEAR_WORKSPACE (or another layout)
+ * clears the array.
+ */
+int kmr_decode_step_static(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
+                           const int32_t* token_ids, int32_t* positions, int32_t* cache_position,
+                           uint8_t* finished, int32_t batch, int32_t* next_ids, float* logits,
+                           uint32_t flags, kmr_stream_t stream);
 
 /*
  * kmr_decode_step_prefix -- kmr_decode_step with shared-prefix (cascade) attention

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kmr.h"
 #include "kmr_kernels.h"
@@ -655,6 +656,48 @@ void fill_zero(void* p, size_t bytes, hipStream_t st) {
   }
 }
 
+// ---------------------------------------------------------------- static workspace
+// The workspace of kmr_decode_step_static: one array per device, held until the
+// process ends.  In host code `scratch` is only a stand-in for the symbol; its
+// device address comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) unsigned char scratch[KMR_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices];           // device address of `scratch` on each device
+size_t g_static_sig[kMaxDevices][4];       // layout of the last call on each device
+
+// The current device's static workspace for a call whose layout is w: its address
+// (set up on the device's first call), and a fill kernel on `st` when the layout
+// differs from the previous call's on this device (the first call included), so
+// that the header's counters start at zero and no word of another layout can be
+// taken for a tag.  Calls with one layout reuse the contents, as a caller-owned
+// workspace is reused.
+int static_workspace(const kmr_config* c, const WsLayout& w, int M, bool clear, hipStream_t st, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return check_hip("hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KMR_EINVAL, "device %d outside [0, %d)", dev, kMaxDevices);
+  if (w.total > (size_t)KMR_STATIC_WORKSPACE_BYTES)
+    return fail(KMR_ENOMEM, "this batch and max_len need a %zu-byte workspace; the static one holds %zu",
+                w.total, (size_t)KMR_STATIC_WORKSPACE_BYTES);
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(KMR_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_static_ptr[dev] = p;
+  }
+  const size_t sig[4] = {w.total, w.lx, (size_t)M,
+                         ((size_t)c->hidden << 40) ^ ((size_t)c->intermediate << 20) ^
+                             ((size_t)c->n_kv_heads << 8) ^ (size_t)c->head_dim};
+  if (clear || memcmp(sig, g_static_sig[dev], sizeof sig) != 0) {
+    fill_zero(g_static_ptr[dev], w.total, st);
+    memcpy(g_static_sig[dev], sig, sizeof sig);
+  }
+  *out = g_static_ptr[dev];
+  return check_hip("static workspace fill");
+}
+
 }  // namespace
 
 extern "C" {
@@ -867,6 +910,23 @@ int kmr_decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_kv*
                     uint32_t flags, void* ws, size_t ws_bytes, kmr_stream_t stream) {
   return decode_step(cfg, model, kv, token_ids, positions, cache_position, finished, batch, next_ids, logits,
                      flags, ws, ws_bytes, stream, 0);
+}
+
+int kmr_decode_step_static(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
+                           const int32_t* token_ids, int32_t* positions, int32_t* cache_position,
+                           uint8_t* finished, int32_t batch, int32_t* next_ids, float* logits,
+                           uint32_t flags, kmr_stream_t stream) {
+  int rc;
+  if ((rc = check_config(cfg))) return rc;
+  if (!kv) return fail(KMR_EINVAL, "kv cache is NULL");
+  if (batch <= 0 || batch > KMR_MAX_BATCH) return fail(KMR_EINVAL, "batch %d out of [1, %d]", batch, KMR_MAX_BATCH);
+  if (kv->max_len <= 0) return fail(KMR_EINVAL, "kv cache max_len must be positive");
+  const WsLayout w = ws_layout(cfg, batch, kv->max_len);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((rc = static_workspace(cfg, w, kv->max_len, (flags & KMR_CLEAR_WORKSPACE) != 0, st, &ws))) return rc;
+  return decode_step(cfg, model, kv, token_ids, positions, cache_position, finished, batch, next_ids, logits,
+                     flags & ~KMR_CLEAR_WORKSPACE, ws, (size_t)KMR_STATIC_WORKSPACE_BYTES, stream, 0);
 }
 
 int kmr_decode_step_prefix(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,

@@ -40,6 +40,8 @@ KMR_DEVICE_WIDE = 4
 KMR_COOPERATIVE = 8
 KMR_BATCH_INVARIANT = 16
 KMR_DEVICE_SCOPE_STORES = 32
+KMR_CLEAR_WORKSPACE = 64
+KMR_STATIC_WORKSPACE_BYTES = 48 << 20
 KMR_TEST_STALL = 256
 
 _i32, _p = C.c_int32, C.c_void_p
@@ -81,6 +83,8 @@ _lib.kmr_decode_layer.argtypes = [C.POINTER(Config), C.POINTER(Layer), _i32, C.P
                                   _p, _i32, _p, C.c_size_t, _p]
 _lib.kmr_decode_step.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(KV), _p, _p, _p, _p,
                                  _i32, _p, _p, C.c_uint32, _p, C.c_size_t, _p]
+_lib.kmr_decode_step_static.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(KV), _p, _p, _p, _p,
+                                        _i32, _p, _p, C.c_uint32, _p]
 _lib.kmr_decode_step_prefix.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(KV), _p, _p, _p, _p,
                                         _i32, _p, _p, C.c_uint32, _i32, _p, C.c_size_t, _p]
 _lib.kmr_prefill.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(KV), _i32, _p, _p, _i32, _i32,
@@ -94,7 +98,8 @@ _lib.kmr_last_error.restype = C.c_char_p
 
 EXPORTED = ["kmr_kv_alloc", "kmr_kv_copy_row", "kmr_quantize_int4", "kmr_workspace_bytes",
             "kmr_prefill_workspace_bytes",
-            "kmr_workspace_init", "kmr_decode_layer", "kmr_decode_step", "kmr_decode_step_prefix",
+            "kmr_workspace_init", "kmr_decode_layer", "kmr_decode_step", "kmr_decode_step_static",
+            "kmr_decode_step_prefix",
             "kmr_prefill",
             "kmr_slot_admit", "kmr_slot_retire", "kmr_status", "kmr_strerror", "kmr_last_error"]
 
@@ -299,6 +304,20 @@ class DeviceModel:
             _check(_lib.kmr_decode_step_prefix(*args, shared_prefix, ws.ptr, ws.nbytes, _stream(stream)))
         else:
             _check(_lib.kmr_decode_step(*args, ws.ptr, ws.nbytes, _stream(stream)))
+        return next_ids
+
+    def decode_step_static(self, kv: KVCache, token_ids: torch.Tensor, positions: torch.Tensor,
+                           cache_position: torch.Tensor, next_ids: torch.Tensor,
+                           finished: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                           advance: bool = False, flags: int = 0, stream=None) -> torch.Tensor:
+        """kmr_decode_step_static: the step with the library's static workspace (no
+        workspace argument, nothing allocated).  flags: further KMR_* bits."""
+        B = token_ids.shape[0]
+        assert token_ids.dtype == torch.int32 and next_ids.dtype == torch.int32
+        f = (KMR_ADVANCE if advance else 0) | int(flags)
+        _check(_lib.kmr_decode_step_static(C.byref(self.cfg), C.byref(self.cmodel), C.byref(kv.desc),
+                                           _ptr(token_ids), _ptr(positions), _ptr(cache_position), _ptr(finished),
+                                           B, _ptr(next_ids), _ptr(logits), f, _stream(stream)))
         return next_ids
 
     def prefill(self, kv: KVCache, row: int, token_ids: torch.Tensor, positions: torch.Tensor, start: int,
