@@ -69,13 +69,14 @@ enum {
                                  grid deals to one (diagnostic; such a call may also
                                  time out) */
   KMR_STATUS_RANGE = 16u      /* a GEMV input exceeded the fp16 range in which the int4
-                                 products take their activations (|v| >= 65520): the
-                                 outputs of that call are invalid.  Residual-stream
-                                 and MLP inputs of the XCD-local persistent kernel are
-                                 staged with a power-of-two exponent and never raise
-                                 it; attention outputs and MLP activations elsewhere
-                                 are staged as they are, and normalised inputs are
-                                 bounded by sqrt(K) times the largest norm gain */
+                                 products take their activations: the outputs of that
+                                 call are invalid.  The XCD-local persistent kernel
+                                 stages residual-stream and MLP inputs scaled by 2^-3,
+                                 so they reach it past |x * norm gain| or |SiLU(gate) up|
+                                 of about 5.2e5; attention outputs, and the per-phase
+                                 kernels' MLP activations, are staged unscaled (past
+                                 65504); normalised inputs are bounded by sqrt(K)
+                                 times the largest norm gain */
 };
 
 #define KMR_MAX_BATCH 64
@@ -373,6 +374,15 @@ int kmr_slot_admit(int32_t* token_ids, int32_t* positions, int32_t* cache_positi
  * KMR_EINVAL: null pointer, row outside [0, batch), batch outside [1, KMR_MAX_BATCH].
  */
 int kmr_slot_retire(uint8_t* finished, int32_t batch, int32_t row, kmr_stream_t stream);
+
+/* Measurement: reads `bytes` (a positive multiple of 16; buf 16-byte aligned) of
+ * device memory with the 16-byte non-temporal loads the int4 GEMVs stream their
+ * weights with, on a grid of KMR_READ_PROBE_THREADS threads, each writing one word
+ * to sink (uint32 [KMR_READ_PROBE_THREADS]).  Timed over a buffer much larger than
+ * the 256 MB Infinity Cache, it gives the device's achievable streaming-read rate,
+ * the practical ceiling of the bandwidth-bound decode step. */
+#define KMR_READ_PROBE_THREADS (256 * 8 * 256)
+int kmr_read_probe(const void* buf, size_t bytes, uint32_t* sink, kmr_stream_t stream);
 
 /* Synchronises `stream`, returns the sticky KMR_STATUS_* bits of `ws` in
  * *flags_out (host pointer) and clears them, except KMR_STATUS_TIMEOUT, which

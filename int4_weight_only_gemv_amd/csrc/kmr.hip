@@ -1042,6 +1042,15 @@ int kmr_slot_retire(uint8_t* finished, int32_t batch, int32_t row, kmr_stream_t 
   return check_hip("slot retire launch");
 }
 
+int kmr_read_probe(const void* buf, size_t bytes, uint32_t* sink, kmr_stream_t stream) {
+  if (!buf || !sink) return fail(KMR_EINVAL, "null pointer");
+  if (bytes < 16 || bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
+    return fail(KMR_EINVAL, "buffer must be 16-byte aligned and a positive multiple of 16 bytes");
+  hipLaunchKernelGGL(k_read_probe, dim3(KMR_READ_PROBE_THREADS / 256), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint4*>(buf), bytes / 16, sink);
+  return check_hip("read probe launch");
+}
+
 int kmr_status(void* ws, kmr_stream_t stream, uint32_t* flags_out) {
   if (!ws || !flags_out) return fail(KMR_EINVAL, "null workspace or flags_out");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -24,6 +24,29 @@ __device__ __forceinline__ void raise_status(uint32_t* st, uint32_t bit) {
   __hip_atomic_fetch_or(st, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------------ read probe
+// Streams `words` 16-byte words with the 16-byte non-temporal loads the GEMVs use,
+// eight loads in flight per thread, and writes one XOR word per thread so that no
+// load can be dropped: the achievable streaming-read rate of the device.
+__global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ src, size_t words,
+                                                    uint32_t* __restrict__ sink) {
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x, nt = (size_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  size_t i = tid;
+  for (; i + 7 * nt < words; i += 8 * nt) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = load_stream16(src + i + u * nt);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < words; i += nt) {
+    const uint4 v = load_stream16(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  sink[tid] = acc;
+}
+
 // ------------------------------------------------------------------ fill
 
 // Clears every status bit outside `keep` (one thread).

@@ -664,9 +664,10 @@ __device__ __forceinline__ void step_tail(const StepArgs& a, float* xin, float* 
   __syncthreads();
   if (tid == 0) {
     // release: this group's argmax partial is visible before its arrival counts;
-    // acquire: the last group to arrive then reads every group's partial
-    const uint32_t prev = __hip_atomic_fetch_add(a.lm_cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    // the last group to arrive acquires (the fence) before it reads every partial
+    const uint32_t prev = __hip_atomic_fetch_add(a.lm_cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == (uint32_t)(nwg - 1);
+    if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   KMR_TRACE_MARK(58);

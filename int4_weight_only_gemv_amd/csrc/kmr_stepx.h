@@ -234,42 +234,28 @@ __device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag,
 //                   (16 h for odd columns)
 //   [3K/4, 3K/4+n)  optional sums of squares of the unscaled input, one per producer
 //                   part (a wave's share of the row)
-//   [ex, ex+n)      the exponent e >= 0 of each producer part: the part's fp16 pairs
-//                   and word sums hold u * 2^-e (ex = 3K/4 + kXSsSlots for an RMSNorm
-//                   input, 3K/4 for the act rows)
 // For an RMSNorm input, u = x * gain and the consumer scales its dot products by
 // 1/sqrt(sum of squares / K + eps): the norm's scale is common to the row.
-// Residual-stream values are not normalised before staging, so a part whose
-// largest |u| reaches 2^15 is staged scaled by 2^-e to keep its fp16 form finite;
-// a consumer that finds a nonzero exponent rescales the row's parts to the row's
-// largest exponent E and multiplies its dot products by 2^E.  With every e = 0
-// (all |u| < 2^15) nothing is rescaled and the arithmetic is unchanged.
+// Residual-stream and MLP values are not normalised before staging, so they are
+// staged as u * 2^-3 (kStageScale, an exact power of two) and the consumers
+// multiply their dot products back by 2^3: the fp16 pairs then stay finite for
+// |u| < 65504 * 8 (about 5.2e5; even columns, the narrower ones).  A producer
+// that meets a larger or non-finite value raises KMR_STATUS_RANGE.
+constexpr float kStageScale = 0.125f, kStageUnscale = 8.0f;
+
+// Raises KMR_STATUS_RANGE (once per wave) when some lane's staged value u (already
+// scaled by kStageScale) is outside the fp16 range.  Every lane of the wave calls this.
+__device__ __forceinline__ void stage_range_check(float u, uint32_t* status) {
+  if (__builtin_amdgcn_ballot_w64(!(fabsf(u) < 65504.f)) != 0 && (otid() & 63) == 0)
+    raise_status(status, kStatusRange);
+}
+
 __device__ __forceinline__ void publish_lb(uint64_t* p, uint32_t tag, uint32_t bits, int plain) {
   const uint64_t w = ((uint64_t)tag << 32) | bits;
   if (plain)
     __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   else
     st_dev64(p, w);
-}
-
-// The exponent e >= 0 that brings a staged part with largest magnitude mx below
-// 2^15 (mx = m 2^k with m in [0.5, 1), so mx 2^-(k-15) < 2^15); 0 for mx < 2^15
-// and for a non-finite mx, which no scaling can fix.
-__device__ __forceinline__ int stage_exponent(float mx) {
-  const int k = __builtin_amdgcn_frexp_expf(mx);
-  return (mx >= 32768.f && mx <= 3.0e38f) ? k - 15 : 0;
-}
-
-// Largest value over each aligned 32-lane half of the wave (every lane of the
-// half receives it).
-__device__ __forceinline__ float half_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));   // lane ^ 1
-  v = fmaxf(v, dpp<0x4E>(v));   // lane ^ 2
-  v = fmaxf(v, dpp<0x124>(v));  // row_ror 4
-  v = fmaxf(v, dpp<0x128>(v));  // row_ror 8
-  float lo, hi;
-  lane_pair<16>(v, lo, hi);
-  return fmaxf(lo, hi);
 }
 
 // This lane's value u of column n (has: valid) of a staged row at dst.  The 8
@@ -300,20 +286,17 @@ __device__ __forceinline__ void stage_publish(uint64_t* dst, int K, int n, float
   }
 }
 
-// Gathers B staged rows of K columns (plus nss sums of squares and nex part
-// exponents each, the exponents at word ex of the row) into the dot-product LDS
-// layout: pairs into xs, and the per-word sums into sums ([BT][K/4], read through
-// ChunkSums) followed by the sums of squares ([BT][nss] at sums + BT * K/4, read by
-// staged_inv); the exponents go to ex ([BT][nex], read by staged_exps).  One
-// barrier: the data is in LDS for every wave on return.  The buffers must not be
-// rewritten before a barrier that follows their last reader.  Returns false, for
-// the whole group, on timeout.
+// Gathers B staged rows of K columns (plus nss sums of squares each) into the
+// dot-product LDS layout: pairs into xs, and the per-word sums into sums ([BT][K/4],
+// read through ChunkSums) followed by the sums of squares ([BT][nss], read by
+// staged_inv).  One barrier: the data is in LDS for every wave on return.  The
+// buffers must not be rewritten before a barrier that follows their last reader.
+// Returns false, for the whole group, on timeout.
 template <int BT, int PT>
 __device__ __forceinline__ bool gather_staged(const uint64_t* src, long long stride, int K, int B,
-                                              int nss, int nex, int exw, uint32_t tag, uint4* xs, float* sums,
-                                              int* ex, uint32_t lim) {
+                                              int nss, uint32_t tag, uint4* xs, float* sums, uint32_t lim) {
   const int tid = otid();
-  const int CH = K >> 5, K2 = K >> 1, K4 = K >> 2, KS = K2 + K4 + nss, per = KS + nex, total = B * per;
+  const int CH = K >> 5, K2 = K >> 1, K4 = K >> 2, per = K2 + K4 + nss, total = B * per;
   uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
   float* s_sum = sums;             // [B][K/4]
   float* s_ss = sums + BT * K4;    // [B][nss]
@@ -332,11 +315,10 @@ __device__ __forceinline__ bool gather_staged(const uint64_t* src, long long str
 #pragma unroll
       for (int t = 1; t < BT; ++t) b += i >= t * per ? 1 : 0;
       const int k = i - b * per, w8 = k >> 2;
-      sp[q] = src + (size_t)b * stride + (k < KS ? k : exw + (k - KS));
+      sp[q] = src + (size_t)b * stride + k;
       dp[q] = k < K2 ? xs32 + ((b * 4 + (w8 & 3)) * CH + (w8 >> 2)) * 4 + (k & 3)
             : k < K2 + K4 ? reinterpret_cast<uint32_t*>(s_sum) + b * K4 + (k - K2)
-            : k < KS      ? reinterpret_cast<uint32_t*>(s_ss) + b * nss + (k - K2 - K4)
-                          : reinterpret_cast<uint32_t*>(ex) + b * nex + (k - KS);
+                          : reinterpret_cast<uint32_t*>(s_ss) + b * nss + (k - K2 - K4);
     }
     uint32_t spins = 0;
     bool fresh;
@@ -360,79 +342,26 @@ __device__ __forceinline__ bool gather_staged(const uint64_t* src, long long str
   return !group_failed(!ok);
 }
 
-// E[b] = the largest part exponent of gathered row b (wave-uniform; 0 for b >= B).
-// Returns whether any is nonzero, the same answer in every wave of the group.
-template <int BT>
-__device__ __forceinline__ bool staged_exps(const int* ex, int B, int nex, int (&E)[BT]) {
-  const int lane = otid() & 63;
-  int any = 0;
-#pragma unroll
-  for (int b = 0; b < BT; ++b) {
-    E[b] = 0;
-    if (BT > 1 && b >= B) continue;
-    int m = 0;
-    for (int i = lane; i < nex; i += 64) m = max(m, ex[b * nex + i]);
-    E[b] = (int)wave_max((float)m);
-    any |= E[b];
-  }
-  return any != 0;
-}
-
-// Rescales every part of the gathered rows to its row's exponent E[b] (parts with
-// exponent e hold u 2^-e; they become u 2^-E by an exact power-of-two scaling, up
-// to the fp16 rounding of values that turn subnormal) and recomputes their word
-// sums from the rescaled values.  The part of 8-column word w8 is word 8 w8 / seg
-// of the row's exponents.  Every thread of the group calls this; one barrier.
-template <int BT>
-__device__ __noinline__ void staged_harmonize(int K, int B, const int (&E)[BT], int nex, int seg, uint4* xs,
-                                               float* sums, const int* ex) {
-  const int tid = otid(), CH = K >> 5, K8 = K >> 3, K4 = K >> 2;
-  uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
-  for (int i = tid; i < B * K8; i += kStepThreads) {
-    const int b = i / K8, w8 = i - b * K8;
-    int eb = E[0];
-#pragma unroll
-    for (int t = 1; t < BT; ++t) if (b == t) eb = E[t];
-    const int ep = ex[b * nex + (8 * w8) / seg];
-    if (ep == eb) continue;
-    const float f = ldexpf(1.0f, ep - eb);
-    uint32_t* p = xs32 + ((b * 4 + (w8 & 3)) * CH + (w8 >> 2)) * 4;
-    float sh = 0.f, su = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const half2_t h = __builtin_bit_cast(half2_t, p[q]);
-      const _Float16 a0 = (_Float16)((float)h[0] * f), a1 = (_Float16)((float)h[1] * f);
-      p[q] = __builtin_bit_cast(uint32_t, half2_t{a0, a1});
-      const float t = (float)a0 + (float)a1;
-      sh += t;
-      su += (q & 1) ? 16.0f * t : t;   // pair word q holds columns q, q + 4 of the word
-    }
-    sums[b * K4 + 2 * w8] = sh;
-    sums[b * K4 + 2 * w8 + 1] = su;
-  }
-  __syncthreads();
-}
-
 // 1/sqrt(sum of squares / K + eps) of staged row b from its nss (<= kXSsSlots)
-// partial sums in LDS; every lane of the calling wave gets it.
-// Times 2^E for a row staged at exponent E.
-__device__ __forceinline__ float staged_inv(const float* s_ss, int b, int nss, int K, float eps, int E = 0) {
+// partial sums in LDS, times kStageUnscale (the row was staged scaled by
+// kStageScale); every lane of the calling wave gets it.
+__device__ __forceinline__ float staged_inv(const float* s_ss, int b, int nss, int K, float eps) {
   const int lane = otid() & 63;
   float part = 0.f;
   for (int i = lane; i < nss; i += 64) part += s_ss[b * nss + i];
-  return ldexpf(rsqrt_f(wave_sum(part) / (float)K + eps), E);
+  return rsqrt_f(wave_sum(part) / (float)K + eps) * kStageUnscale;
 }
 
 // Lane b < B: staged_inv of row b (the others get 1).  Every lane of the wave must
 // call this.
 template <int BT>
-__device__ __forceinline__ float row_inv(const float* s_ss, int B, int nss, int K, float eps, const int (&E)[BT]) {
+__device__ __forceinline__ float row_inv(const float* s_ss, int B, int nss, int K, float eps) {
   const int lane = otid() & 63;
   float r = 1.f;
 #pragma unroll
   for (int b = 0; b < BT; ++b) {
     if (BT > 1 && b >= B) break;
-    const float v = staged_inv(s_ss, b, nss, K, eps, E[b]);
+    const float v = staged_inv(s_ss, b, nss, K, eps);
     if (lane == b) r = v;
   }
   return r;
@@ -447,39 +376,33 @@ __device__ __forceinline__ uint16_t staged_gain(const uint16_t* gain, int H, int
 }
 
 // Publishes x rows (element i = tid: row b = i / RPW, column row0 + i % RPW, valid
-// if has) of a staged RMSNorm input: u = x * gain (g: this column's bf16 gain from
-// staged_gain), and, from each wave that holds part of a row, that part's sum of
-// squares of x and its exponent (stage_exponent of its largest |u|), at slot
-// WPR * slot + (wave - first wave of the row), WPR = max(1, RPW / 64) (a row starts
-// at a wave boundary or within one wave: 64 % RPW == 0 or RPW % 64 == 0, checked on
-// the host); the part's pairs and word sums hold u * 2^-e.  Every thread of the
-// group must call this; it has no barrier.
+// if has) of a staged RMSNorm input: u = x * gain * kStageScale (g: this column's
+// bf16 gain from staged_gain), and the sum of squares of x of each row from each
+// wave that holds part of it, at slot WPR * slot + (wave - first wave of the row),
+// WPR = max(1, RPW / 64) (a row starts at a wave boundary or within one wave:
+// 64 % RPW == 0 or RPW % 64 == 0, checked on the host).  Every thread of the group
+// must call this; it has no barrier.
 template <int BT>
 __device__ __forceinline__ void publish_staged_x(uint64_t* dst, long long stride, int H, int B,
                                                  int RPW, int row0, float xn, bool has, uint16_t g,
-                                                 int slot, uint32_t tag, int plain) {
+                                                 int slot, uint32_t tag, int plain, uint32_t* status) {
   const int tid = otid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = tid >> __builtin_ctz((unsigned)RPW), n = row0 + (tid & (RPW - 1));   // RPW: a power of two
-  const float u = has ? xn * bf16_to_f32(g) : 0.f;
+  const float u = has ? xn * (bf16_to_f32(g) * kStageScale) : 0.f;
+  stage_range_check(u, status);
+  stage_publish(dst + (size_t)(has ? b : 0) * stride, H, n, u, has, tag, plain);
   const int WPR = RPW >= 64 ? RPW >> 6 : 1;
-  int e = 0;   // the exponent of this lane's part
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) {
     if (BT > 1 && bb >= B) break;
     const int w0 = (bb * RPW) >> 6, w1 = ((bb + 1) * RPW - 1) >> 6;
     if (wave >= w0 && wave <= w1) {
-      const bool mine = has && b == bb;
-      const float ss = wave_sum(mine ? xn * xn : 0.f);
-      const int eb = stage_exponent(wave_max(mine ? fabsf(u) : 0.f));
-      if (b == bb) e = eb;
-      if (lane == 0) {
-        uint64_t* sp = dst + (size_t)bb * stride + (H >> 1) + (H >> 2) + WPR * slot + (wave - w0);
-        publish_l(sp, tag, ss, plain);
-        publish_lb(sp + kXSsSlots, tag, (uint32_t)eb, plain);
-      }
+      const float ss = wave_sum((has && b == bb) ? xn * xn : 0.f);
+      if (lane == 0)
+        publish_l(dst + (size_t)bb * stride + (H >> 1) + (H >> 2) + WPR * slot + (wave - w0), tag, ss,
+                  plain);
     }
   }
-  stage_publish(dst + (size_t)(has ? b : 0) * stride, H, n, ldexpf(u, -e), has, tag, plain);
 }
 
 // ------------------------------------------------------------------ LDS layout
@@ -487,14 +410,13 @@ __device__ __forceinline__ void publish_staged_x(uint64_t* dst, long long stride
 //   cc    float2 [BT][H/32]     per-chunk (C1, C2) of the O input
 //   sums  fp32 [BT][H/4], [BT][64]  per-word sums and sums of squares of a
 //                               gathered staged vector
-//   ex    int [BT][kXSsSlots]   its part exponents
 //   xin   fp32 scratch          attention q/k/v and wave states, split merge,
 //                               reduce-scatter partials, lm_head input
 //   xown  fp32 [BT][RPW]        this group's rows of the residual stream
 //   cs    float2 [BT][D/2]      RoPE cos/sin of each row
 //   red   float [128]
 struct StepXLds {
-  size_t xs, cc, sums, ex, xin, xown, cs, red, wgu, total;
+  size_t xs, cc, sums, xin, xown, cs, red, wgu, total;
 };
 
 __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int QPG, int GPX) {
@@ -514,7 +436,6 @@ __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int
   s.xs = take((size_t)BT * 4 * (H / 32) * 16);
   s.cc = take((size_t)BT * (H / 32) * 8);
   s.sums = take((size_t)BT * (H / 4 + kXSsSlots) * 4);
-  s.ex = take((size_t)BT * kXSsSlots * 4);
   s.xin = take(xin);
   s.xown = take((size_t)BT * RPW * 4);
   s.cs = take((size_t)BT * (D / 2) * 8);
@@ -649,8 +570,8 @@ __host__ __device__ inline StepXSizes stepx_sizes(int B, int H, int Hkv, int D, 
   const int GPX = Hkv / kXcds, NSX = (M + kXSplit - 1) / kXSplit;
   StepXSizes z{};
   const int IX = I / kXcds;
-  z.srow_x = ((long long)(H / 2 + H / 4 + 2 * kXSsSlots) + 63) & ~63LL;   // + sums of squares, exponents
-  z.srow_a = ((long long)(IX / 2 + IX / 4 + kXMaxPerXcd) + 63) & ~63LL;    // + exponents
+  z.srow_x = ((long long)(H / 2 + H / 4 + kXSsSlots) + 63) & ~63LL;
+  z.srow_a = ((long long)(IX / 2 + IX / 4) + 63) & ~63LL;
   z.lx = xalign((long long)B * H);             // fp32 x after the last layer (lm_head input)
   z.sx = xalign((long long)2 * B * z.srow_x);  // staged x: entering the layer, after O
   z.lqkv = xalign((long long)B * GPX * (QPG + 2) * D);
@@ -694,9 +615,6 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   const int lgGPX = __builtin_ctz((unsigned)GPX);   // GPX: a power of two (checked on the host)
   const int lgOX = __builtin_ctz((unsigned)OX);     // OX = GPX * 2 * D: a power of two too
   const int NSS = WPX * (RPW >= 64 ? RPW >> 6 : 1);   // sums-of-squares slots of a staged row
-  const int XEX = (H >> 1) + (H >> 2) + kXSsSlots;    // its exponents (one per slot)
-  const int XSEG = RPW < 64 ? RPW : 64;               // columns per slot
-  const int AEX = (IX >> 1) + (IX >> 2);              // exponents of an act row (one per group)
   const int plain = a.intra_plain;
   const StepXLds Ld = stepx_lds(BT, H, RPW, D, QPG, GPX);
   group_fail_reset();
@@ -704,7 +622,6 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   uint4* xs = reinterpret_cast<uint4*>(smem + Ld.xs);
   float2* cc = reinterpret_cast<float2*>(smem + Ld.cc);
   float* sums = reinterpret_cast<float*>(smem + Ld.sums);
-  int* sex = reinterpret_cast<int*>(smem + Ld.ex);
   float* xin = reinterpret_cast<float*>(smem + Ld.xin);
   float* xown = reinterpret_cast<float*>(smem + Ld.xown);
   float2* cs = reinterpret_cast<float2*>(smem + Ld.cs);
@@ -761,7 +678,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       xown[b * RPW + r] = v;
     }
     publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, v, has, staged_gain(a.layers[0].in_norm, H, RPW, j * RPW),
-                         j, tag(1), plain);
+                         j, tag(1), plain, a.status);
   }
   __syncthreads();   // cache positions, split counts and RoPE tables are in LDS
   KMR_TRACE_MARK(0);
@@ -818,12 +735,10 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         wrows_load(wq, Ly.qkv_p, Ly.qkv_s, H, lgG, row, ok);
         asm volatile("" ::: "memory");   // keep the weight requests ahead of the polls
       }
-      if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, NSS, NSS, XEX, ctag(ph), xs, sums, sex, lim)) {
+      if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, NSS, ctag(ph), xs, sums, lim)) {
         alive = false;
         break;
       }
-      int E[BT];
-      if (staged_exps<BT>(sex, B, NSS, E)) staged_harmonize<BT>(H, B, E, NSS, XSEG, xs, sums, sex);
       KMR_TRACE_MARK(tev + 0);
       // at batch 1 the K/V rows of the first attention item are requested now,
       // to be in flight during the QKV rows and their hand-off (the QKV rows,
@@ -838,7 +753,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       }
       float out[NR][BT];
       wave_dot_c<BT, NR, 1>(wq, H, B, xs, ChunkSums{sums, H / 4}, out);
-      const float inv = row_inv<BT>(sums + BT * (H / 4), B, NSS, H, a.eps, E);
+      const float inv = row_inv<BT>(sums + BT * (H / 4), B, NSS, H, a.eps);
       if (lane < B) {
 #pragma unroll
         for (int i = 0; i < NR; ++i)
@@ -1244,19 +1159,17 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         alive = false;
         break;
       }
-      publish_staged_x<BT>(sx1, SX, H, B, RPW, j * RPW, xn, hx, g_post, j, tag(ph + 4), plain);
+      publish_staged_x<BT>(sx1, SX, H, B, RPW, j * RPW, xn, hx, g_post, j, tag(ph + 4), plain, a.status);
     }
     KMR_TRACE_MARK(tev + 6);
     // ================= gate-up + SiLU over the XCD's slice
     WNarrow wd;
     uint16_t g_next;
     {
-      if (!gather_staged<BT, 4 * BT>(sx1, SX, H, B, NSS, NSS, XEX, ctag(ph + 4), xs, sums, sex, lim)) {
+      if (!gather_staged<BT, 4 * BT>(sx1, SX, H, B, NSS, ctag(ph + 4), xs, sums, lim)) {
         alive = false;
         break;
       }
-      int E[BT];
-      if (staged_exps<BT>(sex, B, NSS, E)) staged_harmonize<BT>(H, B, E, NSS, XSEG, xs, sums, sex);
       KMR_TRACE_MARK(tev + 7);
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gate/up rows are in LDS
       if constexpr (kAhead) {
@@ -1271,10 +1184,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         gu_mfma_part<BT>(gu_codes, gu_sz, xs, sums, B, part);
         __syncthreads();
         if (wave < B) {
-          int Ew = E[0];
-#pragma unroll
-          for (int b = 1; b < BT; ++b) if (wave == b) Ew = E[b];
-          const float inv = staged_inv(sums + BT * (H / 4), wave, NSS, H, a.eps, Ew);
+          const float inv = staged_inv(sums + BT * (H / 4), wave, NSS, H, a.eps);
           const bool has = lane < kGuMfmaRows;
           float gt = 0.f, up = 0.f;
           if (has) {
@@ -1287,18 +1197,17 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           gt *= inv;
           up *= inv;
           // SiLU(gate) * up with the hardware exp and reciprocal (a few ulp)
-          const float act = has ? gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up : 0.f;
-          const int ea = stage_exponent(wave_max(fabsf(act)));
-          stage_publish(lact + (size_t)wave * SA, IX, j * kGuMfmaRows + lane, ldexpf(act, -ea), has, tag(ph + 5),
-                        plain);
-          if (lane == 0) publish_lb(lact + (size_t)wave * SA + AEX + j, tag(ph + 5), (uint32_t)ea, plain);
+          // (staged scaled by kStageScale: the down product multiplies back)
+          const float act = has ? gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * (up * kStageScale) : 0.f;
+          stage_range_check(act, a.status);
+          stage_publish(lact + (size_t)wave * SA, IX, j * kGuMfmaRows + lane, act, has, tag(ph + 5), plain);
         }
       } else {
         float out[2 * NP][BT];
         WRows<2 * NP, 1> wgu;
         wrows_from_lds(wgu, gu_codes, gu_sz);
         wave_dot_c<BT, 2 * NP, 1>(wgu, H, B, xs, ChunkSums{sums, H / 4}, out);
-        const float inv = row_inv<BT>(sums + BT * (H / 4), B, NSS, H, a.eps, E);
+        const float inv = row_inv<BT>(sums + BT * (H / 4), B, NSS, H, a.eps);
         // act values of this group into LDS [b][32], then published staged
         float* s_act = xin;
         if (lane < B) {
@@ -1309,20 +1218,20 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
             for (int b = 1; b < BT; ++b) if (lane == b) { gt = out[i][b]; up = out[NP + i][b]; }
             gt *= inv;
             up *= inv;
-            // SiLU(gate) * up with the hardware exp and reciprocal (a few ulp)
-            if (gok[i]) s_act[(kAhead ? lane : (otid() & 63)) * 32 + wave * NP + i] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+            // SiLU(gate) * up with the hardware exp and reciprocal (a few ulp), staged
+            // scaled by kStageScale (the down product multiplies back)
+            if (gok[i])
+              s_act[(kAhead ? lane : (otid() & 63)) * 32 + wave * NP + i] =
+                  gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * (up * kStageScale);
           }
         }
         __syncthreads();
         {
-          // (a 32-lane half of a wave holds one row's part)
           const int b = tid >> 5, t = tid & 31;
           const bool has = b < B && t < RA && j * RA + t < IX;
           const float av = has ? s_act[tid] : 0.f;
-          const int ea = stage_exponent(half_max(fabsf(av)));
-          stage_publish(lact + (size_t)(has ? b : 0) * SA, IX, j * RA + t, ldexpf(av, -ea), has,
-                        tag(ph + 5), plain);
-          if (t == 0 && b < B) publish_lb(lact + (size_t)b * SA + AEX + j, tag(ph + 5), (uint32_t)ea, plain);
+          stage_range_check(av, a.status);
+          stage_publish(lact + (size_t)(has ? b : 0) * SA, IX, j * RA + t, av, has, tag(ph + 5), plain);
         }
       }
       // (s_act in xin is next rewritten by the down reduce-scatter, after the
@@ -1337,25 +1246,21 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         const bool ook = ook_at(orow);
         wnarrow_load(wd, Ly.d_p, Ly.d_s, I, lgG, x * IX, IX, ook ? orow : 0, ook);
       }
-      if (!gather_staged<BT, 4 * BT>(lact, SA, IX, B, 0, WPX, AEX, ctag(ph + 5), xs, sums, sex, lim)) {
+      if (!gather_staged<BT, 4 * BT>(lact, SA, IX, B, 0, ctag(ph + 5), xs, sums, lim)) {
         alive = false;
         break;
       }
-      int E[BT];
-      if (staged_exps<BT>(sex, B, WPX, E)) staged_harmonize<BT>(IX, B, E, WPX, RA, xs, sums, sex);
       settle(g_next);
       KMR_TRACE_MARK(tev + 9);
       float out[BT];
       narrow_dot<BT>(wd, IX, B, xs, ChunkSums{sums, IX / 4}, out);
-#pragma unroll
-      for (int b = 0; b < BT; ++b) out[b] = ldexpf(out[b], E[b]);
       const int sub = lane & 7;
       const int orow = orow_at();
       if (ook_at(orow) && sub < B) {
         float v = out[0];
 #pragma unroll
         for (int b = 1; b < BT; ++b) if (sub == b) v = out[b];
-        publish(a.pD + ((size_t)x * B + sub) * H + orow, tag(ph + 6), v);
+        publish(a.pD + ((size_t)x * B + sub) * H + orow, tag(ph + 6), v * kStageUnscale);
       }
     }
     {
@@ -1372,7 +1277,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           qkv_rows(row, lr, ok);
           wrows_load(wq, a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, lgG, row, ok);
         }
-        publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, g_next, j, tag(ph + 6), plain);
+        publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, g_next, j, tag(ph + 6), plain, a.status);
       } else if (hx) {
         const int b = tid / RPW;
         publish_l(lx0 + (size_t)b * H + j * RPW + (tid - b * RPW), tag(ph + 6), xn, plain);

@@ -90,6 +90,7 @@ _lib.kmr_decode_step_prefix.argtypes = [C.POINTER(Config), C.POINTER(Model), C.P
 _lib.kmr_prefill.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(KV), _i32, _p, _p, _i32, _i32,
                              _p, _p, _p, C.c_size_t, _p]
 _lib.kmr_status.argtypes = [_p, _p, C.POINTER(C.c_uint32)]
+_lib.kmr_read_probe.argtypes = [_p, C.c_size_t, _p, _p]
 _lib.kmr_kv_copy_row.argtypes = [C.POINTER(KV), _i32, C.POINTER(KV), _i32, _i32, _p]
 _lib.kmr_slot_admit.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, C.POINTER(_i32), _i32, _p]
 _lib.kmr_slot_retire.argtypes = [_p, _i32, _i32, _p]
@@ -101,7 +102,16 @@ EXPORTED = ["kmr_kv_alloc", "kmr_kv_copy_row", "kmr_quantize_int4", "kmr_workspa
             "kmr_workspace_init", "kmr_decode_layer", "kmr_decode_step", "kmr_decode_step_static",
             "kmr_decode_step_prefix",
             "kmr_prefill",
-            "kmr_slot_admit", "kmr_slot_retire", "kmr_status", "kmr_strerror", "kmr_last_error"]
+            "kmr_slot_admit", "kmr_slot_retire", "kmr_status", "kmr_read_probe", "kmr_strerror",
+            "kmr_last_error"]
+KMR_READ_PROBE_THREADS = 256 * 8 * 256
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """kmr_read_probe: stream every byte of buf (device, contiguous) with 16-byte
+    non-temporal loads; sink: uint32/int32 device tensor of KMR_READ_PROBE_THREADS."""
+    assert sink.numel() >= KMR_READ_PROBE_THREADS and sink.element_size() == 4
+    _check(_lib.kmr_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 class KmrError(RuntimeError):
