@@ -499,14 +499,36 @@ __device__ __forceinline__ void gu_tiles_to_lds(const uint8_t* packed, const uin
 // operand (row b of it; lanes of higher rows repeat row 0) and the weight tile as
 // the second, so lane n < 16 receives every batch row of weight row n.  The group's
 // scale and zero point then apply as in wave_dot_c, s (d - C1) + z C2, with the
-// staged constants of row b summed over the group's four chunks.
+// staged constants of row b summed over the group's 16 eight-column words.
 template <int BT>
 __device__ __forceinline__ void gu_mfma_part(const uint4* codes, const uint32_t* szw, const uint4* xs,
                                              const float* sums, int B, float* part) {
-  constexpr int CH = kGuMfmaK / 32;
+  constexpr int CH = kGuMfmaK / 32, K4 = kGuMfmaK / 4;
   const int lane = otid() & 63, wave = otid() >> 6, n = lane & 15, gq = lane >> 4;
   const int bn = (BT > 1 && n < B) ? n : 0;
-  const ChunkSums cs{sums, kGuMfmaK / 4};
+  // The group constants of every staged row b over this wave's two groups, from one
+  // LDS read per lane: lane l takes float l of the row's 64 per-word sums of the
+  // wave's 256 columns (group h = l / 32; the word's sum of h if l is even, of the
+  // used values if odd), and the 16 lanes of one parity in each 32-lane half are
+  // added (lane ^ 2, ^ 4, ^ 8, ^ 16).  Wave-uniform results.
+  float C1[BT][2], C2[BT][2];
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+    float v = (BT == 1 || b < B) ? sums[b * K4 + 64 * wave + lane] : 0.f;
+    v += dpp<0x4E>(v);     // lane ^ 2
+    v += lane_xor4(v);     // lane ^ 4
+    v += row16_swap8(v);   // lane ^ 8
+    float lo, hi;
+    lane_pair<16>(v, lo, hi);
+    v = lo + hi;           // lane ^ 16
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float sh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32 * h));
+      const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32 * h + 1));
+      C1[b][h] = __builtin_fmaf(1024.0f, sh, 8.0f * su);
+      C2[b][h] = su;
+    }
+  }
   float acc[3][BT];
 #pragma unroll
   for (int t = 0; t < 3; ++t)
@@ -515,37 +537,30 @@ __device__ __forceinline__ void gu_mfma_part(const uint4* codes, const uint32_t*
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int c0 = 8 * wave + 4 * h;
-    uint4 xv[4];
+    // every LDS read of this group first: the staged rows, then the three tiles'
+    // codes (local row 16 t + n, chunk c0 + gq: load 2 t + n / 8, lane 8 (n % 8) + 4 h + gq)
+    // and scale/zero words
+    uint4 xv[4], cw[3];
+    uint32_t zz[3];
 #pragma unroll
     for (int q = 0; q < 4; ++q) xv[q] = xs[(bn * 4 + q) * CH + c0 + gq];
-    // group constants of row bn in lane bn, then those of every row, wave-uniform
-    float2 Cl = make_float2(0.f, 0.f);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const float2 v = cs.get(bn, c0 + cc);
-      Cl.x += v.x;
-      Cl.y += v.y;
-    }
-    float C1[BT], C2[BT];
-#pragma unroll
-    for (int e = 0; e < BT; ++e) {
-      C1[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Cl.x), e));
-      C2[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Cl.y), e));
+    for (int t = 0; t < 3; ++t) {
+      cw[t] = codes[(2 * t + (n >> 3)) * 64 + 8 * (n & 7) + 4 * h + gq];
+      zz[t] = szw[2 * (16 * t + n) + h];
     }
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
-      // weight operand: local row 16 t + n, chunk c0 + gq (load 2 t + n / 8, lane 8 (n % 8) + 4 h + gq)
       uint32_t p[16];
-      dequant16(codes[(2 * t + (n >> 3)) * 64 + 8 * (n & 7) + 4 * h + gq], p);
+      dequant16(cw[t], p);
       f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
         d = mfma16x16x32(xv[kt], make_uint4(p[4 * kt], p[4 * kt + 1], p[4 * kt + 2], p[4 * kt + 3]), d);
       // lanes n < 16 hold rows b = e of weight row 16 t + n
-      const uint32_t zz = szw[2 * (16 * t + n) + h];
-      const float sc = bf16_lo(zz), zp = bf16_hi(zz);
+      const float sc = bf16_lo(zz[t]), zp = bf16_hi(zz[t]);
 #pragma unroll
-      for (int e = 0; e < BT; ++e) acc[t][e] += __builtin_fmaf(sc, d[e] - C1[e], zp * C2[e]);
+      for (int e = 0; e < BT; ++e) acc[t][e] += __builtin_fmaf(sc, d[e] - C1[e][h], zp * C2[e][h]);
     }
   }
   if (gq == 0) {
