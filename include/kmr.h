@@ -81,7 +81,7 @@ enum {
 
 #define KMR_MAX_BATCH 64
 #define KMR_STATIC_WORKSPACE_BYTES (48u << 20)  /* the array kmr_decode_step_static uses */
-#define KMR_PREFILL_CHUNK 128   /* prompt tokens per chunk of kmr_prefill */
+#define KMR_PREFILL_CHUNK 512   /* largest prompt chunk of kmr_prefill (tokens) */
 #define KMR_ADVANCE 1u
 #define KMR_MULTI_KERNEL 2u  /* run the step as one kernel per phase instead of the
                                 single persistent kernel (diagnostics, cross-checks) */

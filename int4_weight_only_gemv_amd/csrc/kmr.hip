@@ -14,6 +14,7 @@
 
 #include "kmr.h"
 #include "kmr_kernels.h"
+#include "kmr_prefill.h"
 #include "kmr_step.h"
 #include "kmr_stepx.h"
 
@@ -87,6 +88,7 @@ struct WsLayout {
   size_t step_ctr, lm_cnt, xarr, tx, tqkv, to, tact, tpart, lm_part2;
   size_t lx, sx, lqkv, lpart, lact, pO, pD, probe, pf, kpart;
   int kpart_rows;
+  size_t pxs, pc2;              // prefill GEMM input of B tokens: [B][Kmax/32][4] x 16 B, [B][Kmax/128] x 4 B
   size_t xst, xst_cc, xst_cb;   // staged 16-row GEMV tile: [16][4][Kmax/32] x 16 B, [16][Kmax/32] x 8 B,
                                 // [16][Kmax/128] x 8 B
   StepXSizes xz;
@@ -141,6 +143,8 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
     w.xst_cb = o; o += align256(rows * (kmax / 128) * 8);
     w.kpart_rows = (int)rows;
     w.kpart = o; o += align256((size_t)2 * rows * c->hidden * 4);   // split-K partials of O and down
+    w.pxs = o; o += align256((size_t)B * (kmax / 32) * 4 * 16);
+    w.pc2 = o; o += align256((size_t)B * (kmax / 128) * 4);
   }
   w.pf = o; o += align256((size_t)4 * KMR_PREFILL_CHUNK * 4);   // prefill: a chunk's [3][C] positions, [C] cache positions
   w.total = o;
@@ -493,6 +497,110 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   g.x = act; g.ldx = I; g.gain = nullptr;
   g.y = x; g.ldy = H; g.N = H; g.K = I; g.G = G; g.B = B;
   launch_gemv<EPI_ADD, PRO_PLAIN>(g, st, inv);
+}
+
+// ---------------------------------------------------------------- prefill
+// The matrix-core GEMM takes a linear when its group size is a multiple of 128 and
+// its input width a multiple of 512 (whole 4-block zero-point steps).
+bool pf_gemm_fits(const kmr_config* c) {
+  return c->group_size % 128 == 0 && c->hidden % 512 == 0 && (c->n_heads * c->head_dim) % 512 == 0 &&
+         c->intermediate % 512 == 0;
+}
+
+template <int PRO>
+void launch_pf_stage(const float* x, int ldx, const uint16_t* gain, int K, int M, float eps, void* ws,
+                     const WsLayout& w, hipStream_t st) {
+  PfStageArgs s{};
+  s.x = x; s.ldx = ldx; s.gain = gain; s.eps = eps; s.K = K; s.M = M;
+  s.xs = at<uint4>(ws, w.pxs); s.c2 = at<float>(ws, w.pc2); s.status = at<uint32_t>(ws, w.status);
+  hipLaunchKernelGGL(k_pf_stage<PRO>, dim3(M, (K / 32 + 63) / 64), dim3(64), 0, st, s);
+}
+
+template <int EPI>
+void launch_pf_gemm(const kmr_qweight& q, float* y, int ldy, int N, int K, int G, int M, void* ws,
+                    const WsLayout& w, hipStream_t st) {
+  PfGemmArgs g{};
+  g.xs = at<const uint4>(ws, w.pxs); g.c2 = at<const float>(ws, w.pc2);
+  g.packed = static_cast<const uint8_t*>(q.packed); g.sz = static_cast<const uint32_t*>(q.sz);
+  g.y = y; g.ldy = ldy; g.M = M; g.N = N; g.K = K; g.G = G;
+  const int rows = EPI == EPI_SILU ? kPfTileN / 2 : kPfTileN;
+  allow_lds(k_pf_gemm<EPI>, pf_gemm_lds());
+  hipLaunchKernelGGL(k_pf_gemm<EPI>, dim3((N + rows - 1) / rows, (M + kPfTileM - 1) / kPfTileM), dim3(256),
+                     pf_gemm_lds(), st, g);
+}
+
+// One decoder layer over the M tokens of a prompt chunk (cache row crow, cache
+// positions cpos, consecutive).  The linears run as matrix-core GEMMs over the whole
+// chunk when pf_gemm_fits (else as the decode path's GEMV tiles); the chunk's q/k/v
+// are normalized, rotated and written to the cache first, then every token attends
+// causally over slots 0 .. its own.
+void enqueue_prefill_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr_kv* kv, float* x,
+                           const int32_t* cpos, int M, int crow, void* ws, const WsLayout& w, hipStream_t st) {
+  const int H = c->hidden, D = c->head_dim, Hq = c->n_heads, Hkv = c->n_kv_heads;
+  const int nqkv = (Hq + 2 * Hkv) * D, I = c->intermediate, G = c->group_size;
+  const bool mm = pf_gemm_fits(c);
+  float* qkv = at<float>(ws, w.qkv);
+  float* ao = at<float>(ws, w.attn_o);
+  float* act = at<float>(ws, w.act);
+  auto gemv = [&](const kmr_qweight& q, const float* in, int ldx, const uint16_t* gain, float* y, int ldy, int N,
+                  int K) {
+    GemvArgs g{};
+    g.xsg = at<uint4>(ws, w.xst); g.ccg = at<float2>(ws, w.xst_cc); g.cbg = at<float2>(ws, w.xst_cb);
+    g.status = at<uint32_t>(ws, w.status); g.kpart = at<float>(ws, w.kpart); g.kpart_rows = w.kpart_rows;
+    g.kpart_n = H;
+    g.packed = static_cast<const uint8_t*>(q.packed); g.sz = static_cast<const uint32_t*>(q.sz);
+    g.x = in; g.ldx = ldx; g.gain = gain; g.eps = c->rms_eps;
+    g.y = y; g.ldy = ldy; g.N = N; g.K = K; g.G = G; g.B = M;
+    return g;
+  };
+  // q, k, v
+  if (mm) {
+    launch_pf_stage<PRO_RMSNORM>(x, H, static_cast<const uint16_t*>(L->in_norm), H, M, c->rms_eps, ws, w, st);
+    launch_pf_gemm<EPI_STORE>(L->qkv, qkv, nqkv, nqkv, H, G, M, ws, w, st);
+  } else {
+    launch_gemv<EPI_STORE, PRO_RMSNORM>(gemv(L->qkv, x, H, static_cast<const uint16_t*>(L->in_norm), qkv, nqkv,
+                                             nqkv, H), st);
+  }
+  const size_t layer_stride = (size_t)kv->batch * Hkv * kv->max_len * D;
+  uint16_t* kc = static_cast<uint16_t*>(kv->k) + (size_t)layer * layer_stride;
+  uint16_t* vc = static_cast<uint16_t*>(kv->v) + (size_t)layer * layer_stride;
+  PfQkArgs qa{};
+  qa.qkv = qkv; qa.q_norm = static_cast<const uint16_t*>(L->q_norm); qa.k_norm = static_cast<const uint16_t*>(L->k_norm);
+  qa.cs = at<float2>(ws, w.cs); qa.kc = kc; qa.vc = vc; qa.cpos = cpos;
+  qa.M = M; qa.ldqkv = nqkv; qa.Hq = Hq; qa.Hkv = Hkv; qa.D = D; qa.max_len = kv->max_len; qa.crow = crow;
+  qa.eps = c->rms_eps;
+  hipLaunchKernelGGL(k_pf_qk, dim3((Hq + 2 * Hkv + 3) / 4, M), dim3(256), 0, st, qa);
+  PfAttnArgs aa{};
+  aa.q = qkv; aa.ldq = nqkv; aa.kc = kc; aa.vc = vc; aa.cpos = cpos; aa.o = ao; aa.ldo = Hq * D;
+  aa.M = M; aa.Hkv = Hkv; aa.max_len = kv->max_len; aa.crow = crow;
+  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  const int qpg = Hq / Hkv, tq = 64 / qpg;
+  const dim3 agrid((M + tq - 1) / tq, Hkv);
+#define KMR_PFATTN(DD, QQ) hipLaunchKernelGGL((k_pf_attn<DD, QQ>), agrid, dim3(256), 0, st, aa)
+  if (D == 128) {
+    if (qpg == 1) KMR_PFATTN(128, 1); else if (qpg == 2) KMR_PFATTN(128, 2); else KMR_PFATTN(128, 4);
+  } else {
+    if (qpg == 1) KMR_PFATTN(64, 1); else if (qpg == 2) KMR_PFATTN(64, 2); else KMR_PFATTN(64, 4);
+  }
+#undef KMR_PFATTN
+  // o projection (+ residual)
+  if (mm) {
+    launch_pf_stage<PRO_PLAIN>(ao, Hq * D, nullptr, Hq * D, M, c->rms_eps, ws, w, st);
+    launch_pf_gemm<EPI_ADD>(L->o, x, H, H, Hq * D, G, M, ws, w, st);
+  } else {
+    launch_gemv<EPI_ADD, PRO_PLAIN>(gemv(L->o, ao, Hq * D, nullptr, x, H, H, Hq * D), st);
+  }
+  // MLP
+  if (mm) {
+    launch_pf_stage<PRO_RMSNORM>(x, H, static_cast<const uint16_t*>(L->post_norm), H, M, c->rms_eps, ws, w, st);
+    launch_pf_gemm<EPI_SILU>(L->gate_up, act, I, I, H, G, M, ws, w, st);
+    launch_pf_stage<PRO_PLAIN>(act, I, nullptr, I, M, c->rms_eps, ws, w, st);
+    launch_pf_gemm<EPI_ADD>(L->down, x, H, H, I, G, M, ws, w, st);
+  } else {
+    launch_gemv<EPI_SILU, PRO_RMSNORM>(gemv(L->gate_up, x, H, static_cast<const uint16_t*>(L->post_norm), act, I,
+                                            I, H), st);
+    launch_gemv<EPI_ADD, PRO_PLAIN>(gemv(L->down, act, I, nullptr, x, H, H, I), st);
+  }
 }
 
 // ---------------------------------------------------------------- persistent step
@@ -960,9 +1068,17 @@ int kmr_prefill(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
     if ((rc = check_layer(cfg, &model->layers[l]))) return fail(rc, "layer %d: %s", l, g_err);
   if (!token_ids || !positions || !next_id || !ws)
     return fail(KMR_EINVAL, "null token_ids/positions/next_id/workspace");
-  const int C = n_tokens < KMR_PREFILL_CHUNK ? n_tokens : KMR_PREFILL_CHUNK;
+  // chunk: min(n_tokens, KMR_PREFILL_CHUNK) tokens, or the largest of 256, 128, .., 16
+  // below that whose layout the workspace holds
+  int C = n_tokens < KMR_PREFILL_CHUNK ? n_tokens : KMR_PREFILL_CHUNK;
+  const size_t need = ws_layout(cfg, C, kv->max_len).total;
+  while (ws_bytes < ws_layout(cfg, C, kv->max_len).total && C > 16) {
+    int h = KMR_PREFILL_CHUNK / 2;
+    while (h >= C) h /= 2;
+    C = h;
+  }
   const WsLayout w = ws_layout(cfg, C, kv->max_len);
-  if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  if (ws_bytes < w.total) return fail(KMR_ENOMEM, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float* x = at<float>(ws, w.x);
   int32_t* pos_c = at<int32_t>(ws, w.pf);
@@ -974,7 +1090,7 @@ int kmr_prefill(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
                        pos_c, cpos_c);
     enqueue_prep(cfg, static_cast<const uint16_t*>(model->embed), token_ids + t0, nullptr, pos_c, x, n, ws, w, st);
     for (int l = 0; l < cfg->n_layers; ++l)
-      enqueue_layer(cfg, &model->layers[l], l, kv, x, cpos_c, n, ws, w, st, 0, row + 1);
+      enqueue_prefill_layer(cfg, &model->layers[l], l, kv, x, cpos_c, n, row, ws, w, st);
   }
   // the next token from the last prompt token only
   LmArgs la{};

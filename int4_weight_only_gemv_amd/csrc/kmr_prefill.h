@@ -1,0 +1,496 @@
+// Prefill kernels: the decoder linears of a prompt chunk as int4 x fp16 matrix-core
+// GEMMs that read each weight once per 128 tokens, and causal attention over the
+// static cache on the matrix cores with each K/V block shared by the queries of a
+// tile (kaminari page, section 04 "Request lifecycle", stage 2: one forward over the
+// prompt fills the cache; the first token is the argmax at the last prompt token).
+#pragma once
+#include "kmr_kernels.h"
+
+namespace kmr {
+
+// ------------------------------------------------------------------ staging
+// A chunk's GEMM input, token-major: row t of x (plain, or its RMSNorm with `gain`)
+// as fp16 magic-bias pairs (h[8w+i], h[8w+i+4]) with odd columns divided by 16,
+// xs[t][K/32][4] (16-byte words; the four words of a 32-column chunk together, so
+// the 128 columns of a quantization block are 256 contiguous bytes per token), and
+// the per-token sums of the staged values over each 128-column block,
+// c2[t][K/128] (the zero-point term's input).  Grid (M tokens, ceil(K/2048)), one
+// wave: lane = 32-column chunk.
+struct PfStageArgs {
+  const float* x;         // [M][ldx]
+  const uint16_t* gain;   // [K] (PRO_RMSNORM)
+  uint4* xs;              // [M][K/32][4]
+  float* c2;              // [M][K/128]
+  uint32_t* status;       // KMR_STATUS_RANGE when a staged value leaves the fp16 range
+  int M, K, ldx;
+  float eps;
+};
+
+template <int PRO>
+__global__ __launch_bounds__(64) void k_pf_stage(PfStageArgs a) {
+  static_assert(PRO == PRO_PLAIN || PRO == PRO_RMSNORM, "plain or RMSNorm input");
+  const int t = blockIdx.x, K = a.K, CH = K >> 5, lane = threadIdx.x, c = blockIdx.y * 64 + lane;
+  const float* xr = a.x + (size_t)t * a.ldx;
+  const bool own = c < CH;
+  float e[32];
+  uint32_t gw[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = own ? reinterpret_cast<const float4*>(xr + 32 * c)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    e[4 * i] = v.x; e[4 * i + 1] = v.y; e[4 * i + 2] = v.z; e[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    gw[i] = (PRO == PRO_RMSNORM && own) ? reinterpret_cast<const uint32_t*>(a.gain + 32 * c)[i] : 0u;
+  if (PRO == PRO_RMSNORM) {
+    float ss = 0.f;
+    for (int k = lane * 4; k < K; k += 256) {
+      const float4 v = *reinterpret_cast<const float4*>(xr + k);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    const float iv = 1.0f / sqrtf(wave_sum(ss) / (float)K + a.eps);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      e[2 * i] = (e[2 * i] * iv) * bf16_lo(gw[i]);
+      e[2 * i + 1] = (e[2 * i + 1] * iv) * bf16_hi(gw[i]);
+    }
+  }
+  uint4 spare[4];
+  const float2 C = stage_chunk(e, own ? a.xs + ((size_t)t * CH + c) * 4 : spare, 1, a.status);
+  // the 4 chunks of a 128-column block are lanes 4m .. 4m + 3
+  float s = C.y;
+  s += dpp<0xB1>(s);   // lane ^ 1
+  s += dpp<0x4E>(s);   // lane ^ 2
+  if ((lane & 3) == 0 && own) a.c2[(size_t)t * (CH >> 2) + (c >> 2)] = s;
+}
+
+// ------------------------------------------------------------------ GEMM
+// y[t][r] (EPI) = sum_k x[t][k] w[r][k] for the M tokens of a chunk, w = s (q - 8) + z
+// per group of G columns (G a multiple of 128).
+//
+// Work-group tile: 128 tokens x 64 weight rows (EPI_SILU: 32 gate rows and their 32
+// up rows), four waves in a 2 x 2 grid, each 64 tokens x two 16-row blocks (for
+// EPI_SILU the gate block and the up block of the same 16 outputs).  The K loop runs
+// over 128-column blocks: the tile's staged input block (128 tokens x 256 bytes)
+// goes to LDS, double-buffered, the next block's loads in flight during this one's
+// products; each lane dequantizes the codes of its weight row over chunk 4 kb + gq to
+// exact operands (even words q - 8, odd words 16 (q - 8), the odd input columns
+// being staged / 16), and 4 x 4 x 2 v_mfma_f32_16x16x32_f16 per block give the
+// block's dots d; acc += s d per block.  The zero-point term sum_kb z[r][kb] c2[t][kb]
+// is one more product over the K/128 blocks, on the fp32 matrix path
+// (v_mfma_f32_16x16x4_f32, four blocks per instruction), after the loop.
+// Each weight is thus read once per 128 tokens; a token's input once per 64 rows.
+constexpr int kPfTileM = 128;
+constexpr int kPfTileN = 64;
+
+struct PfGemmArgs {
+  const uint4* xs;         // staged input [M][K/32][4] (k_pf_stage)
+  const float* c2;         // [M][K/128]
+  const uint8_t* packed;   // [rows][K/2]
+  const uint32_t* sz;      // [rows][K/G] (scale | zero << 16, bf16)
+  float* y;                // [M][ldy]
+  int M, N, K, G, ldy;     // N outputs per token (EPI_SILU: weight rows are 2N)
+};
+
+__host__ __device__ inline size_t pf_gemm_lds() { return (size_t)2 * kPfTileM * 16 * 16; }
+
+__device__ __forceinline__ f32x4_t mfma16x16x4_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void k_pf_gemm(PfGemmArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  // [2][128 tokens][16 slots]: slot j of token t at t * 16 + (j ^ (t & 15))
+  uint4* sA = reinterpret_cast<uint4*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, gq = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int K = a.K, CH = K >> 5, NB = K >> 7, NG = K / a.G;
+  const int m0 = blockIdx.y * kPfTileM;
+  int wrow[2];
+  bool wok[2];
+  if (EPI == EPI_SILU) {
+    const int o = blockIdx.x * (kPfTileN / 2) + 16 * wn + n;
+    wok[0] = wok[1] = o < a.N;
+    wrow[0] = wok[0] ? o : 0;
+    wrow[1] = wok[0] ? a.N + o : 0;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = blockIdx.x * kPfTileN + 32 * wn + 16 * j + n;
+      wok[j] = r < a.N;
+      wrow[j] = wok[j] ? r : 0;
+    }
+  }
+  // staging: thread tid moves slot lj of tokens lt + 16 i (i < 8) of the tile
+  const int lj = tid & 15, lt = tid >> 4;
+  auto load_a = [&](int kb, uint4 (&r)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = m0 + lt + 16 * i;
+      r[i] = t < a.M ? a.xs[((size_t)t * CH + 4 * kb) * 4 + lj] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_a = [&](int buf, const uint4 (&r)[8]) {
+    uint4* d = sA + buf * (kPfTileM * 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[(lt + 16 * i) * 16 + (lj ^ lt)] = r[i];
+  };
+  auto load_b = [&](int kb, uint4 (&cw)[2], uint32_t (&sw)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      cw[j] = wok[j] ? *reinterpret_cast<const uint4*>(a.packed + (size_t)wrow[j] * (K / 2) + 16 * (4 * kb + gq))
+                     : make_uint4(0, 0, 0, 0);
+      sw[j] = wok[j] ? a.sz[(size_t)wrow[j] * NG + ((kb << 7) / a.G)] : 0u;
+    }
+  };
+
+  f32x4_t acc[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[mb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 ar[8], cw[2];
+  uint32_t sw[2];
+  load_a(0, ar);
+  load_b(0, cw, sw);
+  store_a(0, ar);
+  __syncthreads();
+  for (int kb = 0; kb < NB; ++kb) {
+    const int buf = kb & 1;
+    const bool more = kb + 1 < NB;
+    uint4 ncw[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    uint32_t nsw[2] = {0u, 0u};
+    if (more) {
+      load_a(kb + 1, ar);
+      load_b(kb + 1, ncw, nsw);
+    }
+    uint32_t p[2][16];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      dequant16(cw[j], p[j]);
+      // the bias off: even words 1024 + q -> q - 8, odd words 1024 + 16 q -> 16 (q - 8)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const half2_t h = __builtin_bit_cast(half2_t, p[j][i]);
+        const _Float16 off = (i & 1) ? (_Float16)1152.0f : (_Float16)1032.0f;
+        p[j][i] = __builtin_bit_cast(uint32_t, half2_t{h[0] - off, h[1] - off});
+      }
+    }
+    const uint4* At = sA + buf * (kPfTileM * 16) + (64 * wm) * 16;
+    f32x4_t d[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) d[mb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const uint4 xv = At[(16 * mb + n) * 16 + ((4 * gq + kt) ^ n)];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          d[mb][j] = mfma16x16x32(xv, make_uint4(p[j][4 * kt], p[j][4 * kt + 1], p[j][4 * kt + 2], p[j][4 * kt + 3]),
+                                  d[mb][j]);
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float sc = bf16_lo(sw[j]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mb][j][e] = __builtin_fmaf(sc, d[mb][j][e], acc[mb][j][e]);
+    }
+    if (more) {
+      store_a(buf ^ 1, ar);
+      cw[0] = ncw[0]; cw[1] = ncw[1];
+      sw[0] = nsw[0]; sw[1] = nsw[1];
+    }
+    __syncthreads();
+  }
+  // zero points: acc[t][r] += sum_kb c2[t][kb] z[r][kb], four blocks per product
+  // (lane (n, gq) supplies c2 of token n and z of weight row n at block 4 s + gq)
+  for (int s = 0; s < NB; s += 4) {
+    float zb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) zb[j] = wok[j] ? bf16_hi(a.sz[(size_t)wrow[j] * NG + (((s + gq) << 7) / a.G)]) : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int t = m0 + 64 * wm + 16 * mb + n;
+      const float za = a.c2[(size_t)(t < a.M ? t : a.M - 1) * NB + s + gq];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[mb][j] = mfma16x16x4_f32(za, zb[j], acc[mb][j]);
+    }
+  }
+  // epilogue: lane (n, gq) holds tokens 16 mb + 4 gq + e of its wave for weight row n
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = m0 + 64 * wm + 16 * mb + 4 * gq + e;
+      if (t >= a.M) continue;
+      float* yr = a.y + (size_t)t * a.ldy;
+      if (EPI == EPI_SILU) {
+        if (wok[0]) {
+          const float g = acc[mb][0][e], u = acc[mb][1][e];
+          yr[wrow[0]] = g / (1.0f + expf(-g)) * u;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (wok[j]) {
+            if (EPI == EPI_STORE) yr[wrow[j]] = acc[mb][j][e];
+            else yr[wrow[j]] += acc[mb][j][e];
+          }
+      }
+    }
+}
+
+// ------------------------------------------------------------------ q/k/v of a chunk
+// Per token and head (one wave; lane i < D/2 holds dims i and i + D/2): q heads and
+// k heads RMSNorm over head_dim with their gains, then M-RoPE from the chunk's
+// cos/sin table (rotate-half pairs (i, i + D/2)); q is written back in place (fp32),
+// k and v (bf16, their storage precision) go to the token's cache slot.
+struct PfQkArgs {
+  float* qkv;              // [M][ldqkv]: Hq q heads, Hkv k heads, Hkv v heads of D
+  const uint16_t* q_norm;  // [D]
+  const uint16_t* k_norm;  // [D]
+  const float2* cs;        // [M][D/2]
+  uint16_t* kc;            // layer slice [cache rows][Hkv][max_len][D]
+  uint16_t* vc;
+  const int32_t* cpos;     // [M]
+  int M, ldqkv, Hq, Hkv, D, max_len, crow;
+  float eps;
+};
+
+__global__ __launch_bounds__(256) void k_pf_qk(PfQkArgs a) {
+  const int lane = threadIdx.x & 63, h = blockIdx.x * 4 + (threadIdx.x >> 6), t = blockIdx.y;
+  if (h >= a.Hq + 2 * a.Hkv) return;
+  const int half = a.D >> 1;
+  const bool on = lane < half;
+  float* row = a.qkv + (size_t)t * a.ldqkv + (size_t)h * a.D;
+  float lo = on ? row[lane] : 0.f, hi = on ? row[lane + half] : 0.f;
+  const int c = a.cpos[t];
+  if (h >= a.Hq + a.Hkv) {   // v
+    const int g = h - a.Hq - a.Hkv;
+    uint16_t* vd = a.vc + (((size_t)a.crow * a.Hkv + g) * a.max_len + c) * a.D;
+    if (on) {
+      vd[lane] = f32_to_bf16(lo);
+      vd[lane + half] = f32_to_bf16(hi);
+    }
+    return;
+  }
+  const bool isq = h < a.Hq;
+  const uint16_t* gain = isq ? a.q_norm : a.k_norm;
+  const float inv = 1.0f / sqrtf(wave_sum(lo * lo + hi * hi) / (float)a.D + a.eps);
+  if (!on) return;
+  lo = (lo * inv) * bf16_to_f32(gain[lane]);
+  hi = (hi * inv) * bf16_to_f32(gain[lane + half]);
+  const float2 r = a.cs[(size_t)t * half + lane];
+  const float nlo = lo * r.x - hi * r.y, nhi = hi * r.x + lo * r.y;
+  if (isq) {
+    row[lane] = nlo;
+    row[lane + half] = nhi;
+  } else {
+    uint16_t* kd = a.kc + (((size_t)a.crow * a.Hkv + (h - a.Hq)) * a.max_len + c) * a.D;
+    kd[lane] = f32_to_bf16(nlo);
+    kd[lane + half] = f32_to_bf16(nhi);
+  }
+}
+
+// ------------------------------------------------------------------ attention
+// Causal attention of a chunk's tokens (cache positions consecutive, cpos[t]) over
+// slots 0 .. cpos[t] of cache row crow, after k_pf_qk wrote the chunk's slots.
+// Work-group: kv head g and 16 (4 / QPG) tokens, four waves, wave = one q head of
+// the GQA group x 16 tokens.  K/V blocks of 32 slots go to LDS once for all four
+// waves (double-buffered; V transposed).  Per block, S^T = K Q^T on the matrix
+// cores leaves lane (n, gq) the scores of token n at slots 16 pb + 4 gq + e, so
+// each lane's running max, sum and output column belong to one token; the online
+// softmax rescales by 2^(m - m'), and O^T += V^T P^T takes the lane's own
+// probabilities as its operand (the product's k order is the slots the lane holds).
+// Operands are bf16 (the cache's precision for K and V); q and the probabilities
+// enter as a bf16 high part plus a bf16 low part, two products each, so that their
+// rounding stays near fp32.  Output o[t][h D + d] fp32, divided by the softmax sum.
+constexpr int kPfKvBlock = 32;
+
+struct PfAttnArgs {
+  const float* q;          // [M][ldq], q head h at h * D (after k_pf_qk)
+  const uint16_t* kc;      // layer slice
+  const uint16_t* vc;
+  const int32_t* cpos;     // [M], consecutive
+  float* o;                // [M][ldo]
+  int M, ldq, ldo, Hkv, max_len, crow;
+  float scale_log2;        // log2(e) / sqrt(D)
+};
+
+__device__ __forceinline__ void split_bf16(float f, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(f);
+  lo = f32_to_bf16(f - bf16_to_f32(hi));
+}
+
+template <int D, int QPG>
+__global__ __launch_bounds__(256) void k_pf_attn(PfAttnArgs a) {
+  constexpr int WPH = 4 / QPG;          // waves per q head
+  constexpr int TQ = 16 * WPH;          // tokens per work-group
+  constexpr int SL = D / 8;             // 16-byte slots per K row
+  constexpr int KS = D / 32;            // k steps of S^T
+  constexpr int DB = D / 16;            // 16-dim blocks of O^T
+  constexpr int VS = kPfKvBlock + 4;    // V^T row stride (bf16): 8-byte reads of 16 rows hit distinct banks
+  constexpr int KI = kPfKvBlock * SL / 256;   // K staging words per thread (2 or 1)
+  __shared__ __align__(16) uint4 sK[2][kPfKvBlock * SL];
+  __shared__ __align__(16) uint16_t sV[2][D * VS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, gq = lane >> 4;
+  const int g = blockIdx.y, hq = g * QPG + wave / WPH;
+  const int t0 = blockIdx.x * TQ, tq = t0 + (wave % WPH) * 16 + n;
+  const bool qok = tq < a.M;
+  const int cq = a.cpos[qok ? tq : a.M - 1];
+  const int cmax = a.cpos[(t0 + TQ < a.M ? t0 + TQ : a.M) - 1];
+  const int nblk = cmax / kPfKvBlock + 1;
+  const size_t head = ((size_t)a.crow * a.Hkv + g) * a.max_len;   // cache row of slot 0 of this kv head
+
+  // q of token tq, head hq: dims 32 ks + 8 gq + i as bf16 high and low parts
+  uint4 qh[KS], ql[KS];
+  {
+    const float* qr = a.q + (size_t)(qok ? tq : 0) * a.ldq + (size_t)hq * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 f0 = *reinterpret_cast<const float4*>(qr + 32 * ks + 8 * gq);
+      const float4 f1 = *reinterpret_cast<const float4*>(qr + 32 * ks + 8 * gq + 4);
+      const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+      uint32_t wh[4], wl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint16_t h0, l0, h1, l1;
+        split_bf16(f[2 * i], h0, l0);
+        split_bf16(f[2 * i + 1], h1, l1);
+        wh[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        wl[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      qh[ks] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+      ql[ks] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    }
+  }
+
+  // staging of block kb: K rows as 16-byte slots (slot c of slot row p at
+  // p * SL + (c ^ (p % SL))); V transposed, two slots per 32-bit word.  Slots past
+  // cmax are zero (they may hold anything, and 0 * NaN would reach the sums).
+  uint4 kr[KI], vr[2];
+  auto load_kv = [&](int kb) {
+    const int p0 = kb * kPfKvBlock;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int it = tid + 256 * i, p = it / SL, c = it % SL;
+      kr[i] = p0 + p <= cmax ? *reinterpret_cast<const uint4*>(a.kc + (head + p0 + p) * D + 8 * c)
+                             : make_uint4(0, 0, 0, 0);
+    }
+    const int pp = tid / SL, c = tid % SL;   // slot pair pp (2 pp, 2 pp + 1), dims 8 c ..
+    if (pp < kPfKvBlock / 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int p = p0 + 2 * pp + u;
+        vr[u] = p <= cmax ? *reinterpret_cast<const uint4*>(a.vc + (head + p) * D + 8 * c) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_kv = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int it = tid + 256 * i, p = it / SL, c = it % SL;
+      sK[buf][p * SL + (c ^ (p % SL))] = kr[i];
+    }
+    const int pp = tid / SL, c = tid % SL;
+    if (pp < kPfKvBlock / 2) {
+      const uint32_t a0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
+      const uint32_t a1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<uint32_t*>(&sV[buf][(8 * c + 2 * i) * VS + 2 * pp]) = (a0[i] & 0xffffu) | (a1[i] << 16);
+        *reinterpret_cast<uint32_t*>(&sV[buf][(8 * c + 2 * i + 1) * VS + 2 * pp]) = (a0[i] >> 16) | (a1[i] & 0xffff0000u);
+      }
+    }
+  };
+
+  float m = -INFINITY, l = 0.f;
+  f32x4_t ot[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) ot[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  load_kv(0);
+  store_kv(0);
+  __syncthreads();
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int buf = kb & 1;
+    const bool more = kb + 1 < nblk;
+    if (more) load_kv(kb + 1);
+    // S^T = K Q^T: lane (n, gq) gets slots 16 pb + 4 gq + e of token n
+    f32x4_t st[2];
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      st[pb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int p = 16 * pb + n;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 kf = sK[buf][p * SL + ((4 * ks + gq) ^ (p % SL))];
+        st[pb] = mfma16x16x32_bf16(kf, qh[ks], st[pb]);
+        st[pb] = mfma16x16x32_bf16(kf, ql[ks], st[pb]);
+      }
+    }
+    const int p0 = kb * kPfKvBlock;
+    float s[2][4], bm = -INFINITY;
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = p0 + 16 * pb + 4 * gq + e;
+        s[pb][e] = p <= cq ? st[pb][e] * a.scale_log2 : -INFINITY;
+        bm = fmaxf(bm, s[pb][e]);
+      }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);   // finite from the first block on (slot 0 <= cq)
+    const float al = exp2_fast(m - mn);
+    m = mn;
+    l *= al;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ot[db][e] *= al;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float e0 = exp2_fast(s[pb][2 * i] - mn), e1 = exp2_fast(s[pb][2 * i + 1] - mn);
+        l += e0 + e1;
+        uint16_t h0, l0, h1, l1;
+        split_bf16(e0, h0, l0);
+        split_bf16(e1, h1, l1);
+        ph[2 * pb + i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        pl[2 * pb + i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+    const uint4 PH = make_uint4(ph[0], ph[1], ph[2], ph[3]), PL = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+    // O^T += V^T P^T: lane (n, gq) supplies V^T row 16 db + n at slots 4 gq .. + 3, 16 + 4 gq .. + 3
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint16_t* vrow = &sV[buf][(16 * db + n) * VS];
+      const uint2 w0 = *reinterpret_cast<const uint2*>(vrow + 4 * gq);
+      const uint2 w1 = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * gq);
+      const uint4 vf = make_uint4(w0.x, w0.y, w1.x, w1.y);
+      ot[db] = mfma16x16x32_bf16(vf, PH, ot[db]);
+      ot[db] = mfma16x16x32_bf16(vf, PL, ot[db]);
+    }
+    if (more) store_kv(buf ^ 1);
+    __syncthreads();
+  }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (qok) {
+    const float il = 1.0f / l;
+    float* orow = a.o + (size_t)tq * a.ldo + (size_t)hq * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<float4*>(orow + 16 * db + 4 * gq) =
+          make_float4(ot[db][0] * il, ot[db][1] * il, ot[db][2] * il, ot[db][3] * il);
+  }
+}
+
+}  // namespace kmr

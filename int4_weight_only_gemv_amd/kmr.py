@@ -33,7 +33,7 @@ if len(_hip_runtimes()) > 1:
 KMR_OK, KMR_EINVAL, KMR_ESHAPE, KMR_ENOMEM, KMR_EHIP = 0, -1, -2, -3, -4
 KMR_STATUS_CACHE_POS, KMR_STATUS_TOKEN, KMR_STATUS_TIMEOUT, KMR_STATUS_TOPOLOGY, KMR_STATUS_RANGE = 1, 2, 4, 8, 16
 KMR_MAX_BATCH = 64
-KMR_PREFILL_CHUNK = 128
+KMR_PREFILL_CHUNK = 512
 KMR_ADVANCE = 1
 KMR_MULTI_KERNEL = 2
 KMR_DEVICE_WIDE = 4

@@ -270,8 +270,9 @@ def test_decode_step_full(kmr, full_pair, path):
 
 
 def test_prefill_full_size_matches_oracle_decode(kmr, full_pair):
-    """kmr_prefill of 70 tokens at the full model size (one chunk: four 16-row tiles in
-    one fused matrix-core launch, then 6 rows on the VALU) against the oracle's decode step run
+    """kmr_prefill of 70 tokens at the full model size (one chunk: one ragged 128-token
+    tile of each matrix-core GEMM, one ragged attention tile per kv head and 32 tokens)
+    against the oracle's decode step run
     token by token over the same cache row (kaminari page, section 04: prefill fills
     the static cache that decode extends): the last token's logits and token, every
     written K/V slot, and no other slot."""

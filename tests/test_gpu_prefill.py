@@ -7,8 +7,9 @@ is the argmax at the last prompt token).
 - After an earlier part of the sequence (start > 0) they match the oracle's own
   decode step run token by token over the same cache row, which is the same
   computation by the decode/prefill invariant.
-- Token counts cover one token, a single chunk that takes the matrix-core tiles
-  (group size 128), and two chunks of KMR_PREFILL_CHUNK tokens with a ragged last one.
+- Token counts cover one token, a single chunk (group size 128: the matrix-core
+  GEMM tiles, ragged; group size 64: the decode path's GEMV tiles), and, with a
+  workspace sized for 128 tokens, two chunks with a ragged last one.
 - Only the prompt's slots of the chosen cache row change."""
 import dataclasses
 
@@ -44,10 +45,10 @@ def _np_layers(ora):
             for q in ora.q]
 
 
-def _run(kmr, pair, kv, row, tokens, pos3, start):
+def _run(kmr, pair, kv, row, tokens, pos3, start, chunk=None):
     dims = pair.dims
     T = len(tokens)
-    ws = kmr.Workspace.for_prefill(pair.dev.cfg, T, kv.k.shape[3])
+    ws = kmr.Workspace.for_prefill(pair.dev.cfg, chunk or T, kv.k.shape[3])
     nxt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     logits = torch.empty(dims.vocab, dtype=torch.float32, device="cuda")
     pair.dev.prefill(kv, row, torch.from_numpy(tokens.astype(np.int32)).cuda(),
@@ -76,16 +77,17 @@ def _check_cache(kv, kh, vh, row, lo, hi, want_k, want_v):
         assert err <= TOL, f"K/V max_rel {err:.3e}"
 
 
-@pytest.mark.parametrize("T", [1, 13, 150])
-def test_prefill_from_empty_matches_causal_forward(kmr, pair, T):
+@pytest.mark.parametrize("T,chunk", [(1, None), (13, None), (150, None), (150, 128)])
+def test_prefill_from_empty_matches_causal_forward(kmr, pair, T, chunk):
     dims = pair.dims
     w = synth.WORKLOADS["kv8"]
     rng = np.random.default_rng(T)
     tokens = rng.integers(0, dims.vocab, T)
     pos3 = np.sort(rng.integers(0, 300, size=(3, T)), axis=1).astype(np.int32)
-    log(f"prefill {T} tokens from position 0 into cache row 1 (group size {dims.group_size})")
+    log(f"prefill {T} tokens from position 0 into cache row 1 (group size {dims.group_size}, "
+        f"workspace for {chunk or T} tokens)")
     kv, kh, vh = make_caches(dims, synth.base_seed(w) + T, 2, w.max_len, "host")
-    got_next, got_logits = _run(kmr, pair, kv, 1, tokens, pos3, 0)
+    got_next, got_logits = _run(kmr, pair, kv, 1, tokens, pos3, 0, chunk)
 
     x0 = prefill.bf16_values(pair.ora.g["embed"][tokens])
     x_full, kvs = prefill.forward(dims, _np_layers(pair.ora), x0, pos3)
