@@ -88,7 +88,8 @@ struct WsLayout {
   size_t step_ctr, lm_cnt, xarr, tx, tqkv, to, tact, tpart, lm_part2;
   size_t lx, sx, lqkv, lpart, lact, pO, pD, probe, pf, kpart;
   int kpart_rows;
-  size_t pxs, pc2;              // prefill GEMM input of B tokens: [B][Kmax/32][4] x 16 B, [B][Kmax/128] x 4 B
+  size_t pxs, pc2, pkp;         // prefill GEMM input of B tokens: [B][Kmax/32][4] x 16 B, [B][Kmax/128] x 4 B;
+                                // split-K partials [2][B][hidden] x 4 B
   size_t xst, xst_cc, xst_cb;   // staged 16-row GEMV tile: [16][4][Kmax/32] x 16 B, [16][Kmax/32] x 8 B,
                                 // [16][Kmax/128] x 8 B
   StepXSizes xz;
@@ -145,6 +146,7 @@ WsLayout ws_layout(const kmr_config* c, int B, int M) {
     w.kpart = o; o += align256((size_t)2 * rows * c->hidden * 4);   // split-K partials of O and down
     w.pxs = o; o += align256((size_t)B * (kmax / 32) * 4 * 16);
     w.pc2 = o; o += align256((size_t)B * (kmax / 128) * 4);
+    w.pkp = o; o += align256((size_t)2 * B * c->hidden * 4);
   }
   w.pf = o; o += align256((size_t)4 * KMR_PREFILL_CHUNK * 4);   // prefill: a chunk's [3][C] positions, [C] cache positions
   w.total = o;
@@ -516,17 +518,24 @@ void launch_pf_stage(const float* x, int ldx, const uint16_t* gain, int K, int M
   hipLaunchKernelGGL(k_pf_stage<PRO>, dim3(M, (K / 32 + 63) / 64), dim3(64), 0, st, s);
 }
 
+// An EPI_ADD product whose tiles number fewer than two per compute unit's worth of
+// groups (512) splits K in two when each half keeps whole 4-block zero-point steps;
+// its partials go to the workspace and k_gemv_kreduce adds both to y in a fixed order.
 template <int EPI>
 void launch_pf_gemm(const kmr_qweight& q, float* y, int ldy, int N, int K, int G, int M, void* ws,
                     const WsLayout& w, hipStream_t st) {
   PfGemmArgs g{};
   g.xs = at<const uint4>(ws, w.pxs); g.c2 = at<const float>(ws, w.pc2);
   g.packed = static_cast<const uint8_t*>(q.packed); g.sz = static_cast<const uint32_t*>(q.sz);
-  g.y = y; g.ldy = ldy; g.M = M; g.N = N; g.K = K; g.G = G;
+  g.y = y; g.ldy = ldy; g.M = M; g.N = N; g.K = K; g.G = G; g.kpart = at<float>(ws, w.pkp);
   const int rows = EPI == EPI_SILU ? kPfTileN / 2 : kPfTileN;
+  const dim3 grid((N + rows - 1) / rows, (M + kPfTileM - 1) / kPfTileM);
+  const bool split = EPI == EPI_ADD && grid.x * grid.y < 512 && (K / 128) % 8 == 0;
   allow_lds(k_pf_gemm<EPI>, pf_gemm_lds());
-  hipLaunchKernelGGL(k_pf_gemm<EPI>, dim3((N + rows - 1) / rows, (M + kPfTileM - 1) / kPfTileM), dim3(256),
-                     pf_gemm_lds(), st, g);
+  hipLaunchKernelGGL(k_pf_gemm<EPI>, dim3(grid.x, grid.y, split ? 2 : 1), dim3(256), pf_gemm_lds(), st, g);
+  if (split)
+    hipLaunchKernelGGL(k_gemv_kreduce, dim3((M * N + 255) / 256), dim3(256), 0, st, y, ldy,
+                       static_cast<const float*>(g.kpart), M, N, M);
 }
 
 // One decoder layer over the M tokens of a prompt chunk (cache row crow, cache

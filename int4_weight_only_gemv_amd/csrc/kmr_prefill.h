@@ -80,6 +80,10 @@ __global__ __launch_bounds__(64) void k_pf_stage(PfStageArgs a) {
 // is one more product over the K/128 blocks, on the fp32 matrix path
 // (v_mfma_f32_16x16x4_f32, four blocks per instruction), after the loop.
 // Each weight is thus read once per 128 tokens; a token's input once per 64 rows.
+// The loads run two blocks ahead of the products (two register sets), so a block's
+// global loads have the products of the block before to complete.  An EPI_ADD
+// product may split K in two (gridDim.z = 2) into partials that k_gemv_kreduce adds
+// to y, for outputs too few to give every compute unit a tile.
 constexpr int kPfTileM = 128;
 constexpr int kPfTileN = 64;
 
@@ -89,10 +93,17 @@ struct PfGemmArgs {
   const uint8_t* packed;   // [rows][K/2]
   const uint32_t* sz;      // [rows][K/G] (scale | zero << 16, bf16)
   float* y;                // [M][ldy]
+  float* kpart;            // split K (gridDim.z = 2, EPI_ADD): partials [2][M][N], added by k_gemv_kreduce
   int M, N, K, G, ldy;     // N outputs per token (EPI_SILU: weight rows are 2N)
 };
 
 __host__ __device__ inline size_t pf_gemm_lds() { return (size_t)2 * kPfTileM * 16 * 16; }
+
+// 16-byte load and LDS store as one vector access (a uint4 struct copy between
+// address spaces becomes a memcpy, which keeps register arrays out of registers).
+__device__ __forceinline__ u32x4_t load_vec16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ void store_vec16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+__device__ __forceinline__ uint4 as_uint4(u32x4_t v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
 __device__ __forceinline__ f32x4_t mfma16x16x4_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -107,6 +118,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(PfGemmArgs a) {
   const int wm = wave & 1, wn = wave >> 1;
   const int K = a.K, CH = K >> 5, NB = K >> 7, NG = K / a.G;
   const int m0 = blockIdx.y * kPfTileM;
+  // this wave's weight rows; rows past N (and tokens past M) read row 0 (token M - 1)
+  // and are never stored
   int wrow[2];
   bool wok[2];
   if (EPI == EPI_SILU) {
@@ -122,98 +135,103 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(PfGemmArgs a) {
       wrow[j] = wok[j] ? r : 0;
     }
   }
+  // split K: blockIdx.z takes the z-th of gridDim.z equal runs of 128-column blocks
+  const int nbz = NB / (int)gridDim.z, kb0 = (int)blockIdx.z * nbz;
   // staging: thread tid moves slot lj of tokens lt + 16 i (i < 8) of the tile
   const int lj = tid & 15, lt = tid >> 4;
-  auto load_a = [&](int kb, uint4 (&r)[8]) {
+  const uint4* asrc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = m0 + lt + 16 * i;
-      r[i] = t < a.M ? a.xs[((size_t)t * CH + 4 * kb) * 4 + lj] : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_a = [&](int buf, const uint4 (&r)[8]) {
-    uint4* d = sA + buf * (kPfTileM * 16);
+  for (int i = 0; i < 8; ++i) {
+    const int t = m0 + lt + 16 * i;
+    asrc[i] = a.xs + (size_t)(t < a.M ? t : a.M - 1) * CH * 4 + lj;
+  }
+  const uint8_t* bsrc[2];
+  const uint32_t* ssrc[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) d[(lt + 16 * i) * 16 + (lj ^ lt)] = r[i];
-  };
-  auto load_b = [&](int kb, uint4 (&cw)[2], uint32_t (&sw)[2]) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      cw[j] = wok[j] ? *reinterpret_cast<const uint4*>(a.packed + (size_t)wrow[j] * (K / 2) + 16 * (4 * kb + gq))
-                     : make_uint4(0, 0, 0, 0);
-      sw[j] = wok[j] ? a.sz[(size_t)wrow[j] * NG + ((kb << 7) / a.G)] : 0u;
-    }
-  };
-
+  for (int j = 0; j < 2; ++j) {
+    bsrc[j] = a.packed + (size_t)wrow[j] * (K / 2) + 16 * gq;
+    ssrc[j] = a.sz + (size_t)wrow[j] * NG;
+  }
+#define KMR_PF_LOAD(KB, RA, CW, SW)                                                    \
+  {                                                                                   \
+    const int kbl = (KB);                                                             \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) RA[i] = load_vec16(asrc[i] + 16 * kbl); \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                   \
+      CW[j] = load_vec16(bsrc[j] + 64 * kbl);                                         \
+      SW[j] = ssrc[j][(kbl << 7) / a.G];                                              \
+    }                                                                                 \
+  }
+#define KMR_PF_STORE(BUF, RA)                                                          \
+  {                                                                                   \
+    uint4* dst = sA + (BUF) * (kPfTileM * 16);                                        \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) store_vec16(dst + (lt + 16 * i) * 16 + (lj ^ lt), RA[i]); \
+  }
   f32x4_t acc[4][2];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[mb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint4 ar[8], cw[2];
-  uint32_t sw[2];
-  load_a(0, ar);
-  load_b(0, cw, sw);
-  store_a(0, ar);
-  __syncthreads();
-  for (int kb = 0; kb < NB; ++kb) {
-    const int buf = kb & 1;
-    const bool more = kb + 1 < NB;
-    uint4 ncw[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-    uint32_t nsw[2] = {0u, 0u};
-    if (more) {
-      load_a(kb + 1, ar);
-      load_b(kb + 1, ncw, nsw);
-    }
-    uint32_t p[2][16];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      dequant16(cw[j], p[j]);
-      // the bias off: even words 1024 + q -> q - 8, odd words 1024 + 16 q -> 16 (q - 8)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const half2_t h = __builtin_bit_cast(half2_t, p[j][i]);
-        const _Float16 off = (i & 1) ? (_Float16)1152.0f : (_Float16)1032.0f;
-        p[j][i] = __builtin_bit_cast(uint32_t, half2_t{h[0] - off, h[1] - off});
-      }
-    }
-    const uint4* At = sA + buf * (kPfTileM * 16) + (64 * wm) * 16;
-    f32x4_t d[4][2];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) d[mb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const uint4 xv = At[(16 * mb + n) * 16 + ((4 * gq + kt) ^ n)];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          d[mb][j] = mfma16x16x32(xv, make_uint4(p[j][4 * kt], p[j][4 * kt + 1], p[j][4 * kt + 2], p[j][4 * kt + 3]),
-                                  d[mb][j]);
-      }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float sc = bf16_lo(sw[j]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[mb][j][e] = __builtin_fmaf(sc, d[mb][j][e], acc[mb][j][e]);
-    }
-    if (more) {
-      store_a(buf ^ 1, ar);
-      cw[0] = ncw[0]; cw[1] = ncw[1];
-      sw[0] = nsw[0]; sw[1] = nsw[1];
-    }
-    __syncthreads();
+  // block kb: products from LDS buffer BUF and the codes in (CW, SW); the loads of
+  // block kb + 2 go to (RA, CW, SW) once the codes are dequantized, and block kb + 1
+  // (in RN since the block before) is written to the other buffer at the end.  The
+  // loads are unconditional (the last block again at the end): loads under a branch
+  // would make the compiler wait for every load in flight before the next store.
+  // (Written out twice for the two register sets: register arrays selected by an
+  // index, or passed by reference into a shared body, ended up in scratch memory.)
+#define KMR_PF_BLOCK(BUF, RA, CW, SW, RN)                                                             \
+  {                                                                                                  \
+    uint32_t p[2][16];                                                                               \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                  \
+      dequant16(as_uint4(CW[j]), p[j]);                                                              \
+      _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                               \
+        const half2_t hv = __builtin_bit_cast(half2_t, p[j][i]);                                     \
+        const _Float16 off = (i & 1) ? (_Float16)1152.0f : (_Float16)1032.0f;                        \
+        p[j][i] = __builtin_bit_cast(uint32_t, half2_t{hv[0] - off, hv[1] - off});                   \
+      }                                                                                              \
+    }                                                                                                \
+    const float sc0 = bf16_lo(SW[0]), sc1 = bf16_lo(SW[1]);                                          \
+    KMR_PF_LOAD(kb + 2 < kb0 + nbz ? kb + 2 : kb0 + nbz - 1, RA, CW, SW)                             \
+    __builtin_amdgcn_sched_barrier(0); /* (the loads stay ahead of the products) */               \
+    const uint4* At = sA + (BUF) * (kPfTileM * 16) + (64 * wm) * 16;                                 \
+    f32x4_t d[4][2];                                                                                 \
+    _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                                 \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) d[mb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};          \
+    _Pragma("unroll") for (int kt = 0; kt < 4; ++kt)                                                 \
+      _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                                             \
+        const uint4 xv = At[(16 * mb + n) * 16 + ((4 * gq + kt) ^ n)];                               \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j) d[mb][j] =                                     \
+            mfma16x16x32(xv, make_uint4(p[j][4 * kt], p[j][4 * kt + 1], p[j][4 * kt + 2], p[j][4 * kt + 3]), \
+                         d[mb][j]);                                                                  \
+      }                                                                                              \
+    _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                                 \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                                \
+        acc[mb][0][e] = __builtin_fmaf(sc0, d[mb][0][e], acc[mb][0][e]);                             \
+        acc[mb][1][e] = __builtin_fmaf(sc1, d[mb][1][e], acc[mb][1][e]);                             \
+      }                                                                                              \
+    KMR_PF_STORE((BUF) ^ 1, RN)                                                                      \
+    __syncthreads();                                                                                 \
   }
+  u32x4_t ra0[8], ra1[8], cw0[2], cw1[2];
+  uint32_t sw0[2], sw1[2];
+  KMR_PF_LOAD(kb0, ra0, cw0, sw0)
+  KMR_PF_LOAD(kb0 + 1, ra1, cw1, sw1)
+  KMR_PF_STORE(0, ra0)
+  __syncthreads();
+  // (nbz is a multiple of 4: the blocks go in pairs)
+  for (int kb = kb0; kb < kb0 + nbz; ++kb) {
+    KMR_PF_BLOCK(0, ra0, cw0, sw0, ra1)
+    ++kb;
+    KMR_PF_BLOCK(1, ra1, cw1, sw1, ra0)
+  }
+#undef KMR_PF_BLOCK
+#undef KMR_PF_STORE
+#undef KMR_PF_LOAD
   // zero points: acc[t][r] += sum_kb c2[t][kb] z[r][kb], four blocks per product
   // (lane (n, gq) supplies c2 of token n and z of weight row n at block 4 s + gq)
-  for (int s = 0; s < NB; s += 4) {
+  for (int s = kb0; s < kb0 + nbz; s += 4) {
     float zb[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) zb[j] = wok[j] ? bf16_hi(a.sz[(size_t)wrow[j] * NG + (((s + gq) << 7) / a.G)]) : 0.f;
+    for (int j = 0; j < 2; ++j) zb[j] = bf16_hi(ssrc[j][((s + gq) << 7) / a.G]);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int t = m0 + 64 * wm + 16 * mb + n;
@@ -223,6 +241,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(PfGemmArgs a) {
     }
   }
   // epilogue: lane (n, gq) holds tokens 16 mb + 4 gq + e of its wave for weight row n
+  const bool split = gridDim.z > 1;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -239,7 +258,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(PfGemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           if (wok[j]) {
-            if (EPI == EPI_STORE) yr[wrow[j]] = acc[mb][j][e];
+            if (EPI == EPI_ADD && split) a.kpart[((size_t)blockIdx.z * a.M + t) * a.N + wrow[j]] = acc[mb][j][e];
+            else if (EPI == EPI_STORE) yr[wrow[j]] = acc[mb][j][e];
             else yr[wrow[j]] += acc[mb][j][e];
           }
       }
