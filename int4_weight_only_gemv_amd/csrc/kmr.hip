@@ -583,9 +583,13 @@ void enqueue_prefill_layer(const kmr_config* c, const kmr_layer* L, int layer, c
   aa.q = qkv; aa.ldq = nqkv; aa.kc = kc; aa.vc = vc; aa.cpos = cpos; aa.o = ao; aa.ldo = Hq * D;
   aa.M = M; aa.Hkv = Hkv; aa.max_len = kv->max_len; aa.crow = crow;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
-  const int qpg = Hq / Hkv, tq = 64 / qpg;
-  const dim3 agrid((M + tq - 1) / tq, Hkv);
-#define KMR_PFATTN(DD, QQ) hipLaunchKernelGGL((k_pf_attn<DD, QQ>), agrid, dim3(256), 0, st, aa)
+  const int qpg = Hq / Hkv;
+  const dim3 agrid((M + kPfAttnTokens - 1) / kPfAttnTokens, Hkv);
+#define KMR_PFATTN(DD, QQ)                                                                            \
+  do {                                                                                                \
+    allow_lds(k_pf_attn<DD, QQ>, pf_attn_lds(DD, QQ));                                               \
+    hipLaunchKernelGGL((k_pf_attn<DD, QQ>), agrid, dim3(64 * QQ * pf_attn_groups(QQ)), pf_attn_lds(DD, QQ), st, aa); \
+  } while (0)
   if (D == 128) {
     if (qpg == 1) KMR_PFATTN(128, 1); else if (qpg == 2) KMR_PFATTN(128, 2); else KMR_PFATTN(128, 4);
   } else {

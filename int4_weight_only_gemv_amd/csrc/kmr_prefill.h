@@ -321,17 +321,20 @@ __global__ __launch_bounds__(256) void k_pf_qk(PfQkArgs a) {
 // ------------------------------------------------------------------ attention
 // Causal attention of a chunk's tokens (cache positions consecutive, cpos[t]) over
 // slots 0 .. cpos[t] of cache row crow, after k_pf_qk wrote the chunk's slots.
-// Work-group: kv head g and 16 (4 / QPG) tokens, four waves, wave = one q head of
-// the GQA group x 16 tokens.  K/V blocks of 32 slots go to LDS once for all four
-// waves (double-buffered; V transposed).  Per block, S^T = K Q^T on the matrix
-// cores leaves lane (n, gq) the scores of token n at slots 16 pb + 4 gq + e, so
-// each lane's running max, sum and output column belong to one token; the online
-// softmax rescales by 2^(m - m'), and O^T += V^T P^T takes the lane's own
-// probabilities as its operand (the product's k order is the slots the lane holds).
-// Operands are bf16 (the cache's precision for K and V); q and the probabilities
-// enter as a bf16 high part plus a bf16 low part, two products each, so that their
-// rounding stays near fp32.  Output o[t][h D + d] fp32, divided by the softmax sum.
+// Work-group: kv head g and 16 tokens; NGRP groups of QPG waves, wave = one q head of
+// the GQA group x the 16 tokens.  Group j takes the 32-slot K/V blocks j, j + NGRP,
+// ..., staging each in its own LDS buffers once for its QPG waves (double-buffered;
+// V transposed), and the groups' softmax states merge in LDS at the end.  Per block,
+// S^T = K Q^T on the matrix cores leaves lane (n, gq) the scores of token n at slots
+// 16 pb + 4 gq + e, so each lane's running max, sum and output column belong to one
+// token; the online softmax rescales by 2^(m - m'), and O^T += V^T P^T takes the
+// lane's own probabilities as its operand (the product's k order is the slots the
+// lane holds).  Operands are bf16 (the cache's precision for K and V); q and the
+// probabilities enter as a bf16 high part plus a bf16 low part, two products each,
+// so that their rounding stays near fp32.  Output o[t][h D + d] fp32, divided by the
+// softmax sum.
 constexpr int kPfKvBlock = 32;
+constexpr int kPfAttnTokens = 16;
 
 struct PfAttnArgs {
   const float* q;          // [M][ldq], q head h at h * D (after k_pf_qk)
@@ -348,24 +351,43 @@ __device__ __forceinline__ void split_bf16(float f, uint16_t& hi, uint16_t& lo) 
   lo = f32_to_bf16(f - bf16_to_f32(hi));
 }
 
+// Groups per work-group (each QPG waves) and the LDS the kernel takes.
+__host__ __device__ constexpr int pf_attn_groups(int QPG) { return QPG == 4 ? 2 : 4; }
+__host__ __device__ constexpr int pf_attn_vs() { return kPfKvBlock + 4; }   // V^T row stride (bf16)
+__host__ __device__ constexpr size_t pf_attn_group_lds(int D) {
+  return (size_t)2 * kPfKvBlock * D * 2 + (size_t)2 * D * pf_attn_vs() * 2;
+}
+// (the K/V buffers of every group, or the merge area [groups][QPG][D / 4 + 2][64]
+// floats that reuses them, whichever is larger)
+__host__ __device__ constexpr size_t pf_attn_lds(int D, int QPG) {
+  return pf_attn_groups(QPG) * pf_attn_group_lds(D) > (size_t)pf_attn_groups(QPG) * QPG * (D / 4 + 2) * 64 * 4
+             ? pf_attn_groups(QPG) * pf_attn_group_lds(D)
+             : (size_t)pf_attn_groups(QPG) * QPG * (D / 4 + 2) * 64 * 4;
+}
+
 template <int D, int QPG>
-__global__ __launch_bounds__(256) void k_pf_attn(PfAttnArgs a) {
-  constexpr int WPH = 4 / QPG;          // waves per q head
-  constexpr int TQ = 16 * WPH;          // tokens per work-group
-  constexpr int SL = D / 8;             // 16-byte slots per K row
-  constexpr int KS = D / 32;            // k steps of S^T
-  constexpr int DB = D / 16;            // 16-dim blocks of O^T
-  constexpr int VS = kPfKvBlock + 4;    // V^T row stride (bf16): 8-byte reads of 16 rows hit distinct banks
-  constexpr int KI = kPfKvBlock * SL / 256;   // K staging words per thread (2 or 1)
-  __shared__ __align__(16) uint4 sK[2][kPfKvBlock * SL];
-  __shared__ __align__(16) uint16_t sV[2][D * VS];
+__global__ __launch_bounds__(64 * QPG * pf_attn_groups(QPG)) void k_pf_attn(PfAttnArgs a) {
+  constexpr int NGRP = pf_attn_groups(QPG);
+  constexpr int GT = 64 * QPG;            // threads per group
+  constexpr int SL = D / 8;               // 16-byte slots per K row
+  constexpr int KS = D / 32;              // k steps of S^T
+  constexpr int DB = D / 16;              // 16-dim blocks of O^T
+  constexpr int VS = pf_attn_vs();        // 8-byte reads of 16 V^T rows hit distinct banks
+  constexpr int KN = kPfKvBlock * SL;     // 16-byte K words per block
+  constexpr int VN = (kPfKvBlock / 2) * SL;   // V items per block (two slots x 8 dims)
+  constexpr int KI = (KN + GT - 1) / GT, VI = (VN + GT - 1) / GT;
+  extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, gq = lane >> 4;
-  const int g = blockIdx.y, hq = g * QPG + wave / WPH;
-  const int t0 = blockIdx.x * TQ, tq = t0 + (wave % WPH) * 16 + n;
+  const int grp = wave / QPG, gw = wave % QPG, gt = tid - grp * GT;
+  uint4* sK = reinterpret_cast<uint4*>(smem + grp * pf_attn_group_lds(D));        // [2][KN]
+  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + grp * pf_attn_group_lds(D) + (size_t)2 * KN * 16);   // [2][D][VS]
+  const int g = blockIdx.y, hq = g * QPG + gw;
+  const int t0 = blockIdx.x * kPfAttnTokens, tq = t0 + n;
   const bool qok = tq < a.M;
   const int cq = a.cpos[qok ? tq : a.M - 1];
-  const int cmax = a.cpos[(t0 + TQ < a.M ? t0 + TQ : a.M) - 1];
+  const int cmax = a.cpos[(t0 + kPfAttnTokens < a.M ? t0 + kPfAttnTokens : a.M) - 1];
   const int nblk = cmax / kPfKvBlock + 1;
+  const int iters = (nblk + NGRP - 1) / NGRP;   // the same for every group (uniform barriers)
   const size_t head = ((size_t)a.crow * a.Hkv + g) * a.max_len;   // cache row of slot 0 of this kv head
 
   // q of token tq, head hq: dims 32 ks + 8 gq + i as bf16 high and low parts
@@ -391,41 +413,46 @@ __global__ __launch_bounds__(256) void k_pf_attn(PfAttnArgs a) {
     }
   }
 
-  // staging of block kb: K rows as 16-byte slots (slot c of slot row p at
-  // p * SL + (c ^ (p % SL))); V transposed, two slots per 32-bit word.  Slots past
-  // cmax are zero (they may hold anything, and 0 * NaN would reach the sums).
-  uint4 kr[KI], vr[2];
+  // staging of block kb by the group: K rows as 16-byte slots (slot c of slot row p at
+  // p * SL + (c ^ (p % SL))); V transposed, two slots per 32-bit word (item: slot pair
+  // pp, dims 8 c ..; consecutive threads take consecutive pairs, so their LDS words are
+  // adjacent).  Slots past cmax are zero (they may hold anything, and 0 * NaN would
+  // reach the sums).
+  u32x4_t kr[KI], vr[VI][2];
   auto load_kv = [&](int kb) {
     const int p0 = kb * kPfKvBlock;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int it = tid + 256 * i, p = it / SL, c = it % SL;
-      kr[i] = p0 + p <= cmax ? *reinterpret_cast<const uint4*>(a.kc + (head + p0 + p) * D + 8 * c)
-                             : make_uint4(0, 0, 0, 0);
+      const int it = gt + GT * i, p = it / SL, c = it % SL;
+      kr[i] = (it < KN && p0 + p <= cmax) ? load_vec16(a.kc + (head + p0 + p) * D + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    const int pp = tid / SL, c = tid % SL;   // slot pair pp (2 pp, 2 pp + 1), dims 8 c ..
-    if (pp < kPfKvBlock / 2) {
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int it = gt + GT * i, pp = it % (kPfKvBlock / 2), c = it / (kPfKvBlock / 2);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int p = p0 + 2 * pp + u;
-        vr[u] = p <= cmax ? *reinterpret_cast<const uint4*>(a.vc + (head + p) * D + 8 * c) : make_uint4(0, 0, 0, 0);
+        vr[i][u] = (it < VN && p <= cmax) ? load_vec16(a.vc + (head + p) * D + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
   };
   auto store_kv = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int it = tid + 256 * i, p = it / SL, c = it % SL;
-      sK[buf][p * SL + (c ^ (p % SL))] = kr[i];
+      const int it = gt + GT * i, p = it / SL, c = it % SL;
+      if (it < KN) store_vec16(sK + buf * KN + p * SL + (c ^ (p % SL)), kr[i]);
     }
-    const int pp = tid / SL, c = tid % SL;
-    if (pp < kPfKvBlock / 2) {
-      const uint32_t a0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
-      const uint32_t a1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint32_t*>(&sV[buf][(8 * c + 2 * i) * VS + 2 * pp]) = (a0[i] & 0xffffu) | (a1[i] << 16);
-        *reinterpret_cast<uint32_t*>(&sV[buf][(8 * c + 2 * i + 1) * VS + 2 * pp]) = (a0[i] >> 16) | (a1[i] & 0xffff0000u);
+    for (int i = 0; i < VI; ++i) {
+      const int it = gt + GT * i, pp = it % (kPfKvBlock / 2), c = it / (kPfKvBlock / 2);
+      if (it < VN) {
+        uint16_t* vb = sV + buf * (D * VS);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x0 = vr[i][0][w], x1 = vr[i][1][w];
+          *reinterpret_cast<uint32_t*>(vb + (8 * c + 2 * w) * VS + 2 * pp) = (x0 & 0xffffu) | (x1 << 16);
+          *reinterpret_cast<uint32_t*>(vb + (8 * c + 2 * w + 1) * VS + 2 * pp) = (x0 >> 16) | (x1 & 0xffff0000u);
+        }
       }
     }
   };
@@ -434,82 +461,129 @@ __global__ __launch_bounds__(256) void k_pf_attn(PfAttnArgs a) {
   f32x4_t ot[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) ot[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  load_kv(0);
-  store_kv(0);
+  if (grp < nblk) {
+    load_kv(grp);
+    store_kv(0);
+  }
   __syncthreads();
-  for (int kb = 0; kb < nblk; ++kb) {
-    const int buf = kb & 1;
-    const bool more = kb + 1 < nblk;
-    if (more) load_kv(kb + 1);
-    // S^T = K Q^T: lane (n, gq) gets slots 16 pb + 4 gq + e of token n
-    f32x4_t st[2];
+  for (int it = 0; it < iters; ++it) {
+    const int kb = grp + NGRP * it, buf = it & 1;
+    const bool live = kb < nblk, more = kb + NGRP < nblk;
+    if (more) load_kv(kb + NGRP);
+    if (live) {
+      // S^T = K Q^T: lane (n, gq) gets slots 16 pb + 4 gq + e of token n
+      f32x4_t st[2];
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
-      st[pb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int p = 16 * pb + n;
+      for (int pb = 0; pb < 2; ++pb) {
+        st[pb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int p = 16 * pb + n;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kf = sK[buf][p * SL + ((4 * ks + gq) ^ (p % SL))];
-        st[pb] = mfma16x16x32_bf16(kf, qh[ks], st[pb]);
-        st[pb] = mfma16x16x32_bf16(kf, ql[ks], st[pb]);
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 kf = as_uint4(load_vec16(sK + buf * KN + p * SL + ((4 * ks + gq) ^ (p % SL))));
+          st[pb] = mfma16x16x32_bf16(kf, qh[ks], st[pb]);
+          st[pb] = mfma16x16x32_bf16(kf, ql[ks], st[pb]);
+        }
       }
-    }
-    const int p0 = kb * kPfKvBlock;
-    float s[2][4], bm = -INFINITY;
+      const int p0 = kb * kPfKvBlock;
+      float s[2][4], bm = -INFINITY;
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb)
+      for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = p0 + 16 * pb + 4 * gq + e;
-        s[pb][e] = p <= cq ? st[pb][e] * a.scale_log2 : -INFINITY;
-        bm = fmaxf(bm, s[pb][e]);
+        for (int e = 0; e < 4; ++e) {
+          const int p = p0 + 16 * pb + 4 * gq + e;
+          s[pb][e] = p <= cq ? st[pb][e] * a.scale_log2 : -INFINITY;
+          bm = fmaxf(bm, s[pb][e]);
+        }
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      // a token's first block may hold none of its slots (the block past cq, for a
+      // token before the group's slots): m stays -inf and nothing is added
+      const float mn = fmaxf(m, bm);
+      const float al = mn == -INFINITY ? 1.f : exp2_fast(m - mn);
+      m = mn;
+      l *= al;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ot[db][e] *= al;
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float e0 = s[pb][2 * i] == -INFINITY ? 0.f : exp2_fast(s[pb][2 * i] - mn);
+          const float e1 = s[pb][2 * i + 1] == -INFINITY ? 0.f : exp2_fast(s[pb][2 * i + 1] - mn);
+          l += e0 + e1;
+          uint16_t h0, l0, h1, l1;
+          split_bf16(e0, h0, l0);
+          split_bf16(e1, h1, l1);
+          ph[2 * pb + i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          pl[2 * pb + i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+      const uint4 PH = make_uint4(ph[0], ph[1], ph[2], ph[3]), PL = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+      // O^T += V^T P^T: lane (n, gq) supplies V^T row 16 db + n at slots 4 gq .. + 3, 16 + 4 gq .. + 3
+      const uint16_t* vb = sV + buf * (D * VS);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint16_t* vrow = vb + (16 * db + n) * VS;
+        const uint2 w0 = *reinterpret_cast<const uint2*>(vrow + 4 * gq);
+        const uint2 w1 = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * gq);
+        const uint4 vf = make_uint4(w0.x, w0.y, w1.x, w1.y);
+        ot[db] = mfma16x16x32_bf16(vf, PH, ot[db]);
+        ot[db] = mfma16x16x32_bf16(vf, PL, ot[db]);
       }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m, bm);   // finite from the first block on (slot 0 <= cq)
-    const float al = exp2_fast(m - mn);
-    m = mn;
-    l *= al;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ot[db][e] *= al;
-    uint32_t ph[4], pl[4];
-#pragma unroll
-    for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const float e0 = exp2_fast(s[pb][2 * i] - mn), e1 = exp2_fast(s[pb][2 * i + 1] - mn);
-        l += e0 + e1;
-        uint16_t h0, l0, h1, l1;
-        split_bf16(e0, h0, l0);
-        split_bf16(e1, h1, l1);
-        ph[2 * pb + i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        pl[2 * pb + i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-      }
-    const uint4 PH = make_uint4(ph[0], ph[1], ph[2], ph[3]), PL = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-    // O^T += V^T P^T: lane (n, gq) supplies V^T row 16 db + n at slots 4 gq .. + 3, 16 + 4 gq .. + 3
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint16_t* vrow = &sV[buf][(16 * db + n) * VS];
-      const uint2 w0 = *reinterpret_cast<const uint2*>(vrow + 4 * gq);
-      const uint2 w1 = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * gq);
-      const uint4 vf = make_uint4(w0.x, w0.y, w1.x, w1.y);
-      ot[db] = mfma16x16x32_bf16(vf, PH, ot[db]);
-      ot[db] = mfma16x16x32_bf16(vf, PL, ot[db]);
     }
     if (more) store_kv(buf ^ 1);
     __syncthreads();
   }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (qok) {
-    const float il = 1.0f / l;
-    float* orow = a.o + (size_t)tq * a.ldo + (size_t)hq * D;
+  // merge the groups' states: groups 1.. write (m, l, O^T) per lane, group 0 combines
+  // (a group that saw no slot of a token has m = -inf and weight 0)
+  float* sm = reinterpret_cast<float*>(smem);   // [NGRP][QPG][DB * 4 + 2][64]
+  constexpr int F = DB * 4 + 2;
+  if (grp > 0) {
+    float* d = sm + ((size_t)(grp * QPG + gw) * F) * 64 + lane;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<float4*>(orow + 16 * db + 4 * gq) =
-          make_float4(ot[db][0] * il, ot[db][1] * il, ot[db][2] * il, ot[db][3] * il);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[(4 * db + e) * 64] = ot[db][e];
+    d[(F - 2) * 64] = m;
+    d[(F - 1) * 64] = l;
+  }
+  __syncthreads();
+  if (grp == 0) {
+    float mg[NGRP], wg[NGRP];
+    mg[0] = m;
+#pragma unroll
+    for (int j = 1; j < NGRP; ++j) mg[j] = sm[((size_t)(j * QPG + gw) * F + F - 2) * 64 + lane];
+    float M = mg[0];
+#pragma unroll
+    for (int j = 1; j < NGRP; ++j) M = fmaxf(M, mg[j]);
+#pragma unroll
+    for (int j = 0; j < NGRP; ++j) wg[j] = mg[j] == -INFINITY ? 0.f : exp2_fast(mg[j] - M);
+    float L = wg[0] * l;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ot[db][e] *= wg[0];
+#pragma unroll
+    for (int j = 1; j < NGRP; ++j) {
+      const float* src = sm + ((size_t)(j * QPG + gw) * F) * 64 + lane;
+      L += wg[j] * src[(F - 1) * 64];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ot[db][e] += wg[j] * src[(4 * db + e) * 64];
+    }
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    if (qok) {
+      const float il = 1.0f / L;
+      float* orow = a.o + (size_t)tq * a.ldo + (size_t)hq * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<float4*>(orow + 16 * db + 4 * gq) =
+            make_float4(ot[db][0] * il, ot[db][1] * il, ot[db][2] * il, ot[db][3] * il);
+    }
   }
 }
 
