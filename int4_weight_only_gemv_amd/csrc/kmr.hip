@@ -509,20 +509,22 @@ bool pf_gemm_fits(const kmr_config* c) {
          c->intermediate % 512 == 0;
 }
 
+// Staging of a chunk's GEMM input; kp (or null): split-K partials of the projection
+// that wrote x, added to x first.
 template <int PRO>
-void launch_pf_stage(const float* x, int ldx, const uint16_t* gain, int K, int M, float eps, void* ws,
+void launch_pf_stage(float* x, int ldx, const uint16_t* gain, const float* kp, int K, int M, float eps, void* ws,
                      const WsLayout& w, hipStream_t st) {
   PfStageArgs s{};
-  s.x = x; s.ldx = ldx; s.gain = gain; s.eps = eps; s.K = K; s.M = M;
+  s.x = x; s.ldx = ldx; s.gain = gain; s.kp = kp; s.eps = eps; s.K = K; s.M = M;
   s.xs = at<uint4>(ws, w.pxs); s.c2 = at<float>(ws, w.pc2); s.status = at<uint32_t>(ws, w.status);
-  hipLaunchKernelGGL(k_pf_stage<PRO>, dim3(M, (K / 32 + 63) / 64), dim3(64), 0, st, s);
+  hipLaunchKernelGGL(k_pf_stage<PRO>, dim3(M), dim3(256), 0, st, s);
 }
 
-// An EPI_ADD product whose tiles number fewer than two per compute unit's worth of
-// groups (512) splits K in two when each half keeps whole 4-block zero-point steps;
-// its partials go to the workspace and k_gemv_kreduce adds both to y in a fixed order.
+// An EPI_ADD product whose tiles number fewer than 512 splits K in two when each half
+// keeps whole 4-block zero-point steps: its partials go to the workspace (w.pkp) and
+// the caller's next staging of y adds them.  Returns whether it split.
 template <int EPI>
-void launch_pf_gemm(const kmr_qweight& q, float* y, int ldy, int N, int K, int G, int M, void* ws,
+bool launch_pf_gemm(const kmr_qweight& q, float* y, int ldy, int N, int K, int G, int M, void* ws,
                     const WsLayout& w, hipStream_t st) {
   PfGemmArgs g{};
   g.xs = at<const uint4>(ws, w.pxs); g.c2 = at<const float>(ws, w.pc2);
@@ -533,9 +535,7 @@ void launch_pf_gemm(const kmr_qweight& q, float* y, int ldy, int N, int K, int G
   const bool split = EPI == EPI_ADD && grid.x * grid.y < 512 && (K / 128) % 8 == 0;
   allow_lds(k_pf_gemm<EPI>, pf_gemm_lds());
   hipLaunchKernelGGL(k_pf_gemm<EPI>, dim3(grid.x, grid.y, split ? 2 : 1), dim3(256), pf_gemm_lds(), st, g);
-  if (split)
-    hipLaunchKernelGGL(k_gemv_kreduce, dim3((M * N + 255) / 256), dim3(256), 0, st, y, ldy,
-                       static_cast<const float*>(g.kpart), M, N, M);
+  return split;
 }
 
 // One decoder layer over the M tokens of a prompt chunk (cache row crow, cache
@@ -543,11 +543,16 @@ void launch_pf_gemm(const kmr_qweight& q, float* y, int ldy, int N, int K, int G
 // chunk when pf_gemm_fits (else as the decode path's GEMV tiles); the chunk's q/k/v
 // are normalized, rotated and written to the cache first, then every token attends
 // causally over slots 0 .. its own.
+// `pending`: x still owes the split-K partials of the previous down projection
+// (w.pkp); the layer's first staging adds them, and the layer leaves it set when its
+// own down projection split.
 void enqueue_prefill_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr_kv* kv, float* x,
-                           const int32_t* cpos, int M, int crow, void* ws, const WsLayout& w, hipStream_t st) {
+                           const int32_t* cpos, int M, int crow, void* ws, const WsLayout& w, hipStream_t st,
+                           bool& pending) {
   const int H = c->hidden, D = c->head_dim, Hq = c->n_heads, Hkv = c->n_kv_heads;
   const int nqkv = (Hq + 2 * Hkv) * D, I = c->intermediate, G = c->group_size;
   const bool mm = pf_gemm_fits(c);
+  const float* kp = at<const float>(ws, w.pkp);
   float* qkv = at<float>(ws, w.qkv);
   float* ao = at<float>(ws, w.attn_o);
   float* act = at<float>(ws, w.act);
@@ -564,7 +569,9 @@ void enqueue_prefill_layer(const kmr_config* c, const kmr_layer* L, int layer, c
   };
   // q, k, v
   if (mm) {
-    launch_pf_stage<PRO_RMSNORM>(x, H, static_cast<const uint16_t*>(L->in_norm), H, M, c->rms_eps, ws, w, st);
+    launch_pf_stage<PRO_RMSNORM>(x, H, static_cast<const uint16_t*>(L->in_norm), pending ? kp : nullptr, H, M,
+                                 c->rms_eps, ws, w, st);
+    pending = false;
     launch_pf_gemm<EPI_STORE>(L->qkv, qkv, nqkv, nqkv, H, G, M, ws, w, st);
   } else {
     launch_gemv<EPI_STORE, PRO_RMSNORM>(gemv(L->qkv, x, H, static_cast<const uint16_t*>(L->in_norm), qkv, nqkv,
@@ -597,18 +604,20 @@ void enqueue_prefill_layer(const kmr_config* c, const kmr_layer* L, int layer, c
   }
 #undef KMR_PFATTN
   // o projection (+ residual)
+  bool o_split = false;
   if (mm) {
-    launch_pf_stage<PRO_PLAIN>(ao, Hq * D, nullptr, Hq * D, M, c->rms_eps, ws, w, st);
-    launch_pf_gemm<EPI_ADD>(L->o, x, H, H, Hq * D, G, M, ws, w, st);
+    launch_pf_stage<PRO_PLAIN>(ao, Hq * D, nullptr, nullptr, Hq * D, M, c->rms_eps, ws, w, st);
+    o_split = launch_pf_gemm<EPI_ADD>(L->o, x, H, H, Hq * D, G, M, ws, w, st);
   } else {
     launch_gemv<EPI_ADD, PRO_PLAIN>(gemv(L->o, ao, Hq * D, nullptr, x, H, H, Hq * D), st);
   }
   // MLP
   if (mm) {
-    launch_pf_stage<PRO_RMSNORM>(x, H, static_cast<const uint16_t*>(L->post_norm), H, M, c->rms_eps, ws, w, st);
+    launch_pf_stage<PRO_RMSNORM>(x, H, static_cast<const uint16_t*>(L->post_norm), o_split ? kp : nullptr, H, M,
+                                 c->rms_eps, ws, w, st);
     launch_pf_gemm<EPI_SILU>(L->gate_up, act, I, I, H, G, M, ws, w, st);
-    launch_pf_stage<PRO_PLAIN>(act, I, nullptr, I, M, c->rms_eps, ws, w, st);
-    launch_pf_gemm<EPI_ADD>(L->down, x, H, H, I, G, M, ws, w, st);
+    launch_pf_stage<PRO_PLAIN>(act, I, nullptr, nullptr, I, M, c->rms_eps, ws, w, st);
+    pending = launch_pf_gemm<EPI_ADD>(L->down, x, H, H, I, G, M, ws, w, st);
   } else {
     launch_gemv<EPI_SILU, PRO_RMSNORM>(gemv(L->gate_up, x, H, static_cast<const uint16_t*>(L->post_norm), act, I,
                                             I, H), st);
@@ -1102,8 +1111,15 @@ int kmr_prefill(const kmr_config* cfg, const kmr_model* model, const kmr_kv* kv,
     hipLaunchKernelGGL(k_prefill_rows, dim3(1), dim3(KMR_PREFILL_CHUNK), 0, st, positions, n_tokens, t0, n, start,
                        pos_c, cpos_c);
     enqueue_prep(cfg, static_cast<const uint16_t*>(model->embed), token_ids + t0, nullptr, pos_c, x, n, ws, w, st);
+    bool pending = false;
     for (int l = 0; l < cfg->n_layers; ++l)
-      enqueue_prefill_layer(cfg, &model->layers[l], l, kv, x, cpos_c, n, row, ws, w, st);
+      enqueue_prefill_layer(cfg, &model->layers[l], l, kv, x, cpos_c, n, row, ws, w, st, pending);
+    // the last layer's split-K partials: only the last token's hidden state is read
+    // (by the lm_head after the last chunk); an earlier chunk's are dropped
+    if (pending && t0 + n == n_tokens)
+      hipLaunchKernelGGL(k_gemv_kreduce, dim3((cfg->hidden + 255) / 256), dim3(256), 0, st,
+                         x + (size_t)(n - 1) * cfg->hidden, cfg->hidden,
+                         at<const float>(ws, w.pkp) + (size_t)(n - 1) * cfg->hidden, n, cfg->hidden, 1);
   }
   // the next token from the last prompt token only
   LmArgs la{};

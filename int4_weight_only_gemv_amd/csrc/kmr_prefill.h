@@ -8,60 +8,103 @@
 
 namespace kmr {
 
+// 16-byte load and store as one vector access (a uint4 struct copy between address
+// spaces becomes a memcpy, which keeps register arrays out of registers).
+__device__ __forceinline__ u32x4_t load_vec16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ void store_vec16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+__device__ __forceinline__ uint4 as_uint4(u32x4_t v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
 // ------------------------------------------------------------------ staging
 // A chunk's GEMM input, token-major: row t of x (plain, or its RMSNorm with `gain`)
-// as fp16 magic-bias pairs (h[8w+i], h[8w+i+4]) with odd columns divided by 16,
-// xs[t][K/32][4] (16-byte words; the four words of a 32-column chunk together, so
-// the 128 columns of a quantization block are 256 contiguous bytes per token), and
-// the per-token sums of the staged values over each 128-column block,
-// c2[t][K/128] (the zero-point term's input).  Grid (M tokens, ceil(K/2048)), one
-// wave: lane = 32-column chunk.
+// as fp16 magic-bias pairs (h[8w+i], h[8w+i+4]) with odd columns divided by 16, one
+// 16-byte word per 8 columns, xs[t][K/8] (so the 128 columns of a quantization block
+// are 256 contiguous bytes per token), and the per-token sums of the staged values
+// over each 128-column block, c2[t][K/128] (the zero-point term's input).
+// With kp set, x first takes the two split-K partials of the projection that wrote it,
+// x += kp[0][t] + kp[1][t] (written back), the same sum k_gemv_kreduce forms.
+// One work-group of 256 threads per token; thread i takes the words i, i + 256, ...
 struct PfStageArgs {
-  const float* x;         // [M][ldx]
+  float* x;               // [M][ldx]
   const uint16_t* gain;   // [K] (PRO_RMSNORM)
-  uint4* xs;              // [M][K/32][4]
+  const float* kp;        // null, or split-K partials [2][M][K] to add to x first
+  uint4* xs;              // [M][K/8]
   float* c2;              // [M][K/128]
   uint32_t* status;       // KMR_STATUS_RANGE when a staged value leaves the fp16 range
   int M, K, ldx;
   float eps;
 };
 
+constexpr int kPfStageWords = 4;   // words per thread: K <= 8192
+
 template <int PRO>
-__global__ __launch_bounds__(64) void k_pf_stage(PfStageArgs a) {
+__global__ __launch_bounds__(256) void k_pf_stage(PfStageArgs a) {
   static_assert(PRO == PRO_PLAIN || PRO == PRO_RMSNORM, "plain or RMSNorm input");
-  const int t = blockIdx.x, K = a.K, CH = K >> 5, lane = threadIdx.x, c = blockIdx.y * 64 + lane;
-  const float* xr = a.x + (size_t)t * a.ldx;
-  const bool own = c < CH;
-  float e[32];
-  uint32_t gw[16];
+  __shared__ float s_ss[4];
+  const int t = blockIdx.x, K = a.K, NW = K >> 3, tid = threadIdx.x, lane = tid & 63;
+  float* xr = a.x + (size_t)t * a.ldx;
+  float v[kPfStageWords][8];
+  float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float4 v = own ? reinterpret_cast<const float4*>(xr + 32 * c)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    e[4 * i] = v.x; e[4 * i + 1] = v.y; e[4 * i + 2] = v.z; e[4 * i + 3] = v.w;
+  for (int i = 0; i < kPfStageWords; ++i) {
+    const int w = tid + 256 * i;
+    if (w < NW) {
+      const float4 lo = *reinterpret_cast<const float4*>(xr + 8 * w);
+      const float4 hi = *reinterpret_cast<const float4*>(xr + 8 * w + 4);
+      float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (a.kp) {
+        const float* p0 = a.kp + (size_t)t * K + 8 * w;
+        const float* p1 = a.kp + ((size_t)a.M + t) * K + 8 * w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] += p0[e] + p1[e];
+        *reinterpret_cast<float4*>(xr + 8 * w) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(xr + 8 * w + 4) = make_float4(f[4], f[5], f[6], f[7]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[i][e] = f[e];
+        ss += f[e] * f[e];
+      }
+    }
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    gw[i] = (PRO == PRO_RMSNORM && own) ? reinterpret_cast<const uint32_t*>(a.gain + 32 * c)[i] : 0u;
+  float iv = 1.f;
   if (PRO == PRO_RMSNORM) {
-    float ss = 0.f;
-    for (int k = lane * 4; k < K; k += 256) {
-      const float4 v = *reinterpret_cast<const float4*>(xr + k);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-    const float iv = 1.0f / sqrtf(wave_sum(ss) / (float)K + a.eps);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      e[2 * i] = (e[2 * i] * iv) * bf16_lo(gw[i]);
-      e[2 * i + 1] = (e[2 * i + 1] * iv) * bf16_hi(gw[i]);
-    }
+    ss = wave_sum(ss);
+    if (lane == 0) s_ss[tid >> 6] = ss;
+    __syncthreads();
+    iv = 1.0f / sqrtf(((s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3])) / (float)K + a.eps);
   }
-  uint4 spare[4];
-  const float2 C = stage_chunk(e, own ? a.xs + ((size_t)t * CH + c) * 4 : spare, 1, a.status);
-  // the 4 chunks of a 128-column block are lanes 4m .. 4m + 3
-  float s = C.y;
-  s += dpp<0xB1>(s);   // lane ^ 1
-  s += dpp<0x4E>(s);   // lane ^ 2
-  if ((lane & 3) == 0 && own) a.c2[(size_t)t * (CH >> 2) + (c >> 2)] = s;
+#pragma unroll
+  for (int i = 0; i < kPfStageWords; ++i) {
+    const int w = tid + 256 * i;
+    if (i * 256 >= NW) break;   // (uniform: whole rounds of 256 words)
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = w < NW ? v[i][e] : 0.f;
+    if (PRO == PRO_RMSNORM && w < NW) {
+      const uint4 gw = *reinterpret_cast<const uint4*>(a.gain + 8 * w);
+      const uint32_t g[4] = {gw.x, gw.y, gw.z, gw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = (f[2 * e] * iv) * bf16_lo(g[e]);
+        f[2 * e + 1] = (f[2 * e + 1] * iv) * bf16_hi(g[e]);
+      }
+    }
+    const _Float16 h0 = (_Float16)f[0], h4 = (_Float16)f[4], h2 = (_Float16)f[2], h6 = (_Float16)f[6];
+    const _Float16 h1 = (_Float16)(f[1] * 0.0625f), h5 = (_Float16)(f[5] * 0.0625f);
+    const _Float16 h3 = (_Float16)(f[3] * 0.0625f), h7 = (_Float16)(f[7] * 0.0625f);
+    const float ev = ((float)h0 + (float)h4) + ((float)h2 + (float)h6);
+    const float od = ((float)h1 + (float)h5) + ((float)h3 + (float)h7);
+    const float usum = ev + 16.0f * od;
+    if (w < NW) {
+      store_vec16(a.xs + (size_t)t * NW + w,
+                  u32x4_t{__builtin_bit_cast(uint32_t, half2_t{h0, h4}), __builtin_bit_cast(uint32_t, half2_t{h1, h5}),
+                          __builtin_bit_cast(uint32_t, half2_t{h2, h6}), __builtin_bit_cast(uint32_t, half2_t{h3, h7})});
+      if (!(fabsf(ev + od) + fabsf(usum) <= 3.0e38f)) raise_status(a.status, kStatusRange);
+    }
+    // a 128-column block is 16 consecutive words: one 16-lane row
+    const float bs = row16_sum(usum);
+    if ((lane & 15) == 0 && w < NW) a.c2[(size_t)t * (K >> 7) + (w >> 4)] = bs;
+  }
 }
 
 // ------------------------------------------------------------------ GEMM
@@ -82,28 +125,23 @@ __global__ __launch_bounds__(64) void k_pf_stage(PfStageArgs a) {
 // Each weight is thus read once per 128 tokens; a token's input once per 64 rows.
 // The loads run two blocks ahead of the products (two register sets), so a block's
 // global loads have the products of the block before to complete.  An EPI_ADD
-// product may split K in two (gridDim.z = 2) into partials that k_gemv_kreduce adds
-// to y, for outputs too few to give every compute unit a tile.
+// product may split K in two (gridDim.z = 2), for outputs too few to give every
+// compute unit a tile: its partials go to kpart, and the next staging of y adds them.
 constexpr int kPfTileM = 128;
 constexpr int kPfTileN = 64;
 
 struct PfGemmArgs {
-  const uint4* xs;         // staged input [M][K/32][4] (k_pf_stage)
+  const uint4* xs;         // staged input [M][K/8] (k_pf_stage)
   const float* c2;         // [M][K/128]
   const uint8_t* packed;   // [rows][K/2]
   const uint32_t* sz;      // [rows][K/G] (scale | zero << 16, bf16)
   float* y;                // [M][ldy]
-  float* kpart;            // split K (gridDim.z = 2, EPI_ADD): partials [2][M][N], added by k_gemv_kreduce
+  float* kpart;            // split K (gridDim.z = 2, EPI_ADD): partials [2][M][N], for k_pf_stage to add
   int M, N, K, G, ldy;     // N outputs per token (EPI_SILU: weight rows are 2N)
 };
 
 __host__ __device__ inline size_t pf_gemm_lds() { return (size_t)2 * kPfTileM * 16 * 16; }
 
-// 16-byte load and LDS store as one vector access (a uint4 struct copy between
-// address spaces becomes a memcpy, which keeps register arrays out of registers).
-__device__ __forceinline__ u32x4_t load_vec16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
-__device__ __forceinline__ void store_vec16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
-__device__ __forceinline__ uint4 as_uint4(u32x4_t v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
 __device__ __forceinline__ f32x4_t mfma16x16x4_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

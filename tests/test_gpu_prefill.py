@@ -153,3 +153,34 @@ def test_prefill_then_decode_continues_the_sequence(kmr, pair):
     log(f"prefill of {T - 1} tokens, then one decode step: logits max_rel={err:.3e}")
     assert err <= TOL
     _check_token(int(nxt.cpu()[0]), want)
+
+
+@pytest.mark.parametrize("heads,kv_heads,head_dim", [(16, 4, 64), (8, 8, 128), (8, 2, 128)],
+                         ids=["qpg4-d64", "qpg1-d128", "qpg4-d128"])
+def test_prefill_gqa_shapes_match_causal_forward(kmr, heads, kv_heads, head_dim):
+    """The prefill attention's other GQA group sizes (1 and 4 q heads per kv head: one
+    and four waves per group, four and two groups) and head_dim 128 at the reduced
+    width, 150 tokens from position 0 in two chunks (workspace for 128 tokens), against
+    the oracle's causal forward: last-token logits and every written K/V slot."""
+    w = synth.WORKLOADS["kv8"]
+    sec = (12, 10, 10) if head_dim == 64 else (24, 20, 20)
+    dims = dataclasses.replace(w.dims, n_heads=heads, n_kv_heads=kv_heads, head_dim=head_dim, group_size=128,
+                               mrope_section=sec)
+    pair = build_pair(dims, synth.base_seed(w) + heads * 100 + kv_heads, "host", with_globals=True)
+    T = 150
+    rng = np.random.default_rng(heads + kv_heads)
+    tokens = rng.integers(0, dims.vocab, T)
+    pos3 = np.sort(rng.integers(0, 300, size=(3, T)), axis=1).astype(np.int32)
+    log(f"prefill {T} tokens, {heads} q heads / {kv_heads} kv heads of {head_dim}, chunks of 128")
+    kv, kh, vh = make_caches(dims, synth.base_seed(w) + T, 2, w.max_len, "host")
+    got_next, got_logits = _run(kmr, pair, kv, 1, tokens, pos3, 0, 128)
+    x0 = prefill.bf16_values(pair.ora.g["embed"][tokens])
+    x_full, kvs = prefill.forward(dims, _np_layers(pair.ora), x0, pos3)
+    want = prefill.logits(dims, x_full[-1:], pair.ora.g["final_norm"], pair.ora.g["lm_head"])[0]
+    err = max_rel(got_logits[None], want[None])
+    log(f"  logits max_rel={err:.3e} next={got_next} oracle argmax={int(np.argmax(want))}")
+    assert err <= TOL
+    _check_token(got_next, want)
+    want_k = np.stack([prefill.to_bf16_bits(kb.transpose(1, 0, 2)) for kb, _ in kvs])
+    want_v = np.stack([prefill.to_bf16_bits(vb.transpose(1, 0, 2)) for _, vb in kvs])
+    _check_cache(kv, kh, vh, 1, 0, T, want_k, want_v)
