@@ -252,8 +252,9 @@ def bench_prefill(args):
            "config": {"workload": "prefill-512-tokens-28L-int4-g128", "tokens": T, "chunk": kmr.KMR_PREFILL_CHUNK},
            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": F16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tflops / F16_DENSE_PEAK_TFLOPS, 5), "traffic": None,
-                        "kernel": "per-phase kernels over 64-token chunks", "launches_per_step": None,
-                        "kernel_us_per_launch": None},
+                        "kernel": "whole prefill, one 512-token chunk: per layer 4 stagings, 4 matrix-core "
+                                  "int4 GEMMs (128-token x 64-row tiles), q/k norm + RoPE, causal flash attention",
+                        "launches_per_step": 10 * d.n_layers + 4, "kernel_us_per_launch": None},
            "cpu_baseline": None}
     print(json.dumps(out), flush=True)
 
