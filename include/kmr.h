@@ -198,8 +198,9 @@ int kmr_quantize_int4(const void* w_bf16, int32_t N, int32_t K, int32_t group, v
 
 /* Bytes of workspace the decode calls need for this config, batch and max_len. */
 size_t kmr_workspace_bytes(const kmr_config* cfg, int32_t batch, int32_t max_len);
-/* The workspace kmr_prefill needs for a prompt of n_tokens (a chunk of
- * min(n_tokens, KMR_PREFILL_CHUNK) rows); 0 for an invalid config or size. */
+/* The workspace kmr_prefill needs to run a prompt of n_tokens in chunks of
+ * min(n_tokens, KMR_PREFILL_CHUNK) tokens; 0 for an invalid config or size.  A
+ * workspace sized for fewer tokens makes kmr_prefill take smaller chunks. */
 size_t kmr_prefill_workspace_bytes(const kmr_config* cfg, int32_t n_tokens, int32_t max_len);
 
 /* Clears a workspace with a fill kernel on `stream`.  Call once after allocating
@@ -321,11 +322,16 @@ int kmr_decode_step_prefix(const kmr_config* cfg, const kmr_model* model, const 
  * attends causally to the slots up to its own.  No other slot or row is touched.
  * next_id [1] receives the argmax at the last token; logits [vocab] fp32 receives
  * that token's logits if not NULL.
- * The tokens run in chunks of at most KMR_PREFILL_CHUNK through the per-phase kernels
- * (every projection of a chunk as one batch; the attention of a chunk in two
- * passes, the new K/V slots of every token first, then the attention itself).
- * ws must hold kmr_prefill_workspace_bytes(cfg, n_tokens, max_len) bytes and
- * have been initialised once.  Returns KMR_EINVAL for a row outside the
+ * The tokens run in chunks through the layers: per layer and chunk, the q/k/v,
+ * o, gate/up and down projections as matrix-core int4 GEMMs over the whole chunk
+ * (group_size a multiple of 128 and hidden, n_heads*head_dim and intermediate
+ * multiples of 512; otherwise the decode path's GEMV tiles), the chunk's K/V slots
+ * written first and then causal attention over the row's slots 0 .. each token's
+ * own.  The chunk is min(n_tokens, KMR_PREFILL_CHUNK) tokens when the workspace
+ * holds its layout, else the largest of 256, 128, 64, 32, 16 tokens below that
+ * which it holds (KMR_ENOMEM if none).
+ * ws must hold kmr_prefill_workspace_bytes(cfg, n_tokens, max_len) bytes (or the
+ * bytes of a smaller chunk) and have been initialised once.  Returns KMR_EINVAL for a row outside the
  * cache, n_tokens < 1, or start + n_tokens > max_len, before anything is launched;
  * token ids outside [0, vocab) raise KMR_STATUS_TOKEN as in kmr_decode_step.
  * Nothing is synchronised.

@@ -419,12 +419,9 @@ bool fuse_attn_merge(int B, int ns) { return (size_t)B * ns <= 16; }
 
 // One decoder layer on x (fp32 [B][H]) using workspace buffers; the RoPE table
 // must already be in ws.cs.
-// fixed_row > 0: every row is a token of one prompt held in cache row fixed_row - 1
-// at its own cache position; the new slots of all rows are written before any row
-// attends (two attention passes), so that each token sees the ones before it.
 void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr_kv* kv, float* x,
                    const int32_t* cpos, int B, void* ws, const WsLayout& w, hipStream_t st,
-                   int prefix_splits = 0, int fixed_row = 0, bool inv = false) {
+                   int prefix_splits = 0, bool inv = false) {
   const int H = c->hidden, D = c->head_dim, Hq = c->n_heads, Hkv = c->n_kv_heads;
   const int nqkv = (Hq + 2 * Hkv) * D, I = c->intermediate, G = c->group_size;
   float* qkv = at<float>(ws, w.qkv);
@@ -457,12 +454,6 @@ void enqueue_layer(const kmr_config* c, const kmr_layer* L, int layer, const kmr
   a.Hq = Hq; a.Hkv = Hkv; a.M = kv->max_len; a.NS = w.ns_pp; a.eps = c->rms_eps;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   a.B = B; a.first_split = prefix_splits; a.prefix_row = 0;
-  a.fixed_row = fixed_row;
-  if (fixed_row) {
-    a.write_mode = 1;
-    launch_attn(c, a, B, st);
-    a.write_mode = 2;
-  }
   launch_attn(c, a, B, st);
 
   AttnPart ap{};
@@ -1018,7 +1009,7 @@ static int decode_step(const kmr_config* cfg, const kmr_model* model, const kmr_
   enqueue_prep(cfg, static_cast<const uint16_t*>(model->embed), token_ids, finished, positions, x,
                batch, ws, w, st);
   for (int l = 0; l < cfg->n_layers; ++l)
-    enqueue_layer(cfg, &model->layers[l], l, kv, x, cache_position, batch, ws, w, st, prefix_splits, 0, inv);
+    enqueue_layer(cfg, &model->layers[l], l, kv, x, cache_position, batch, ws, w, st, prefix_splits, inv);
   LmArgs la{};
   la.x = x; la.gain = static_cast<const uint16_t*>(model->final_norm);
   la.W = static_cast<const uint16_t*>(model->lm_head);

@@ -807,9 +807,6 @@ struct AttnArgs {
   int B;                   // rows
   int first_split;         // shared-prefix splits (0: none) ...
   int prefix_row;          // ... and the cache row that holds the prefix
-  int fixed_row;           // 0: row b reads and writes cache row b; r + 1: every row uses
-                           // cache row r (the tokens of one prompt, at their own positions)
-  int write_mode;          // 0: write the new slot and attend; 1: only write it; 2: only attend
 };
 
 // The attention of split s of kv head g for batch row b (cache position c), given
@@ -834,8 +831,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int g, int 
   const int row = wave * 4 + rr;    // 0..15
   const int d0 = li * DPL;
   const int ns = c / kAttnSplitPP + 1;
-  const int crow = a.fixed_row ? a.fixed_row - 1 : b;
-  const size_t head_base = ((size_t)crow * a.Hkv + g) * a.M;   // in rows of D
+  const size_t head_base = ((size_t)b * a.Hkv + g) * a.M;   // in rows of D
   const size_t pidx = ((size_t)b * a.Hkv + g) * a.NS + s;      // partial slot
   // ---- prologue: q', k', v of the current token for this lane's dims
   const float* qrow = a.qkv + (size_t)b * a.ldqkv;
@@ -878,7 +874,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int g, int 
     kf[e] = round_bf16(kf[e]);
     vf[e] = round_bf16(vf[e]);
   }
-  if (s == ns - 1 && row == 0 && a.write_mode != 2) {
+  if (s == ns - 1 && row == 0) {
     uint16_t* kd = a.kc + (head_base + c) * D + d0;
     uint16_t* vd = a.vc + (head_base + c) * D + d0;
 #pragma unroll
@@ -887,7 +883,6 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int g, int 
       vd[e] = f32_to_bf16(vf[e]);
     }
   }
-  if (a.write_mode == 1) return;   // (uniform over the group)
 
   // ---- online softmax over this split's positions
   float m[QPG], l[QPG], o[QPG][DPL];
@@ -1045,8 +1040,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int rr = lane >> 4, li = lane & 15;
   const int d0 = li * DPL;
   const int c = a.cpos[b];
-  const int crow = a.fixed_row ? a.fixed_row - 1 : b;
-  const size_t head_base = ((size_t)crow * a.Hkv + g) * a.M;   // in rows of D
+  const size_t head_base = ((size_t)b * a.Hkv + g) * a.M;   // in rows of D
   const size_t pidx = ((size_t)b * a.Hkv + g) * a.NS + s;      // partial slot
 
   if (c < 0 || c >= a.M) {
@@ -1060,14 +1054,13 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   if (s * kAttnSplitPP > c) return;
   // a split of the shared prefix of a row past it: k_attn_prefix writes its partial
   if (s < a.first_split && c >= a.first_split * kAttnSplitPP) return;
-  if (a.write_mode == 1 && s != c / kAttnSplitPP) return;   // only the new slot's split writes
 
   // ---- cache reads first
   uint32_t kr[IT][DPL / 2], vr[IT][DPL / 2];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int p = s * kAttnSplitPP + wave * (kAttnSplitPP / 4) + it * 4 + rr;
-    if (p < c && a.write_mode != 1) {
+    if (p < c) {
       const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kc + (head_base + p) * D + d0);
       const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vc + (head_base + p) * D + d0);
 #pragma unroll
