@@ -216,8 +216,10 @@ size_t kmr_prefill_workspace_bytes(const kmr_config* cfg, int32_t n_tokens, int3
 int kmr_workspace_init(void* ws, size_t ws_bytes, kmr_stream_t stream);
 
 /*
- * kmr_decode_layer -- one decoder layer for `batch` rows, in place on
- * hidden_inout (fp32 [batch][hidden]):
+ * kmr_decode_layer -- one decoder layer for `batch` rows (kaminari page, section 03
+ * "Architecture overview": the DecoderLayer of model/modules.py, fused-QKV attention
+ * with GQA and 3D M-RoPE, then the MLP; section 05 "The native model port"), in place
+ * on hidden_inout (fp32 [batch][hidden]):
  *   h = RMSNorm(x; in_norm); [q|k|v] = W_qkv h; per head q, k <- MRoPE(RMSNorm(.; q/k_norm));
  *   K/V of layer `layer`, row b, slot cache_position[b] <- bf16(k), bf16(v);
  *   o = attention of each q head over slots 0..cache_position[b] of its kv head
