@@ -203,6 +203,12 @@ size_t kmr_workspace_bytes(const kmr_config* cfg, int32_t batch, int32_t max_len
  * workspace sized for fewer tokens makes kmr_prefill take smaller chunks. */
 size_t kmr_prefill_workspace_bytes(const kmr_config* cfg, int32_t n_tokens, int32_t max_len);
 
+/* Diagnostic (no device work): 1 if kmr_decode_step would run this config at this
+ * batch on the XCD-local persistent kernel with n_groups work-groups (the number of
+ * compute units), 0 if not, -1 for an invalid config or size.  Lets a host-side test
+ * enumerate the shapes the kernel accepts and check its loaders' addresses. */
+int kmr_debug_stepx_fits(const kmr_config* cfg, int32_t batch, int32_t n_groups);
+
 /* Clears a workspace with a fill kernel on `stream`.  Call once after allocating
  * it, and again after a call that returned an error or raised KMR_STATUS_TIMEOUT;
  * the decode and prefill calls otherwise leave it ready for the next call.  One

@@ -644,9 +644,28 @@ bool stepx_fits(const kmr_config* c, int B, int nwg) {
   if (RPW <= 64 ? 64 % RPW != 0 : RPW % 64 != 0) return false;
   if (4 * GPX * QPG > 8 || QPG != 2) return false;   // split-merge weights in one wave
   if (GPX & (GPX - 1)) return false;                  // kv heads per XCD: a power of two
+  // The weight loaders' chunk assumptions (each loader covers its rows' columns
+  // only under these; the address model in tests/test_stepx_loaders.py checks them):
+  //  - QKV rows (wrows_load, one chunk per lane) and the gate/up rows (wrows_to_lds,
+  //    one chunk per lane, lanes past the row reload chunk 0): hidden <= 64 chunks;
+  if (H > 64 * 32 || H % 32 != 0) return false;
+  //  - O and down rows (wnarrow_load): the XCD's column slice (OX of n_heads*head_dim,
+  //    IX of intermediate) in at most kXNarrowCpl chunks per lane of an 8-lane group,
+  //    and 8 XCD slices that tile the row exactly;
+  if (OX % 32 != 0 || IX % 32 != 0 || OX / 32 > 8 * kXNarrowCpl || IX / 32 > 8 * kXNarrowCpl ||
+      kXcds * OX != c->n_heads * D || kXcds * IX != c->intermediate)
+    return false;
+  //  - a quantization group never straddles a chunk: G a power of two >= 32.
+  if (c->group_size < 32) return false;
+  //  - the matrix-core gate/up form (the constant-size instantiation only) takes
+  //    kGuMfmaRows act rows per group over exactly kGuMfmaK columns; its shape
+  //    match in launch_stepx_k implies IX = WPX * kGuMfmaRows and hidden = kGuMfmaK.
   const size_t lds = stepx_lds(4, H, RPW, D, QPG, GPX).total;
   return lds <= 160 * 1024;
 }
+
+static_assert(kFixI / kXcds == (kFixNwg / kXcds) * kGuMfmaRows && kFixH == kGuMfmaK,
+              "the constant-size gate/up tiles cover the XCD's act rows and the hidden width exactly");
 
 __global__ void k_xcc_probe(uint32_t* out) {
   if (threadIdx.x == 0) out[blockIdx.x] = __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u;
@@ -887,6 +906,11 @@ int kmr_quantize_int4(const void* w_bf16, int32_t N, int32_t K, int32_t group, v
 size_t kmr_workspace_bytes(const kmr_config* cfg, int32_t batch, int32_t max_len) {
   if (check_config(cfg) || batch <= 0 || batch > KMR_MAX_BATCH || max_len <= 0) return 0;
   return ws_layout(cfg, batch, max_len).total;
+}
+
+int kmr_debug_stepx_fits(const kmr_config* cfg, int32_t batch, int32_t n_groups) {
+  if (check_config(cfg) || batch < 1 || n_groups < 1) return -1;
+  return stepx_fits(cfg, batch, n_groups) ? 1 : 0;
 }
 
 size_t kmr_prefill_workspace_bytes(const kmr_config* cfg, int32_t n_tokens, int32_t max_len) {

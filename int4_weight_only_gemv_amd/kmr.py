@@ -79,6 +79,7 @@ _lib.kmr_workspace_bytes.restype = C.c_size_t
 _lib.kmr_prefill_workspace_bytes.argtypes = [C.POINTER(Config), _i32, _i32]
 _lib.kmr_prefill_workspace_bytes.restype = C.c_size_t
 _lib.kmr_workspace_init.argtypes = [_p, C.c_size_t, _p]
+_lib.kmr_debug_stepx_fits.argtypes = [C.POINTER(Config), _i32, _i32]
 _lib.kmr_decode_layer.argtypes = [C.POINTER(Config), C.POINTER(Layer), _i32, C.POINTER(KV), _p, _p,
                                   _p, _i32, _p, C.c_size_t, _p]
 _lib.kmr_decode_step.argtypes = [C.POINTER(Config), C.POINTER(Model), C.POINTER(KV), _p, _p, _p, _p,
@@ -98,7 +99,7 @@ _lib.kmr_strerror.restype = C.c_char_p
 _lib.kmr_last_error.restype = C.c_char_p
 
 EXPORTED = ["kmr_kv_alloc", "kmr_kv_copy_row", "kmr_quantize_int4", "kmr_workspace_bytes",
-            "kmr_prefill_workspace_bytes",
+            "kmr_prefill_workspace_bytes", "kmr_debug_stepx_fits",
             "kmr_workspace_init", "kmr_decode_layer", "kmr_decode_step", "kmr_decode_step_static",
             "kmr_decode_step_prefix",
             "kmr_prefill",
@@ -169,6 +170,11 @@ def workspace_bytes(cfg: Config, batch: int, max_len: int) -> int:
 
 def prefill_workspace_bytes(cfg: Config, n_tokens: int, max_len: int) -> int:
     return int(_lib.kmr_prefill_workspace_bytes(C.byref(cfg), n_tokens, max_len))
+
+
+def debug_stepx_fits(cfg: Config, batch: int, n_groups: int) -> int:
+    """kmr_debug_stepx_fits: 1 if the XCD-local persistent kernel takes this shape."""
+    return int(_lib.kmr_debug_stepx_fits(C.byref(cfg), batch, n_groups))
 
 
 class Workspace:
