@@ -384,9 +384,14 @@ struct PfAttnArgs {
   float scale_log2;        // log2(e) / sqrt(D)
 };
 
-__device__ __forceinline__ void split_bf16(float f, uint16_t& hi, uint16_t& lo) {
-  hi = f32_to_bf16(f);
-  lo = f32_to_bf16(f - bf16_to_f32(hi));
+// (a, b) as bf16 high parts and bf16 low parts (the residuals f - high), packed in pairs;
+// round to nearest even (v_cvt_pk_bf16_f32: one instruction per pair).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)a, (__bf16)b});
+  const float ra = a - __uint_as_float(h << 16), rb = b - __uint_as_float(h & 0xffff0000u);
+  hi = h;
+  lo = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)ra, (__bf16)rb});
 }
 
 // Groups per work-group (each QPG waves) and the LDS the kernel takes.
@@ -439,13 +444,7 @@ __global__ __launch_bounds__(64 * QPG * pf_attn_groups(QPG)) void k_pf_attn(PfAt
       const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
       uint32_t wh[4], wl[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint16_t h0, l0, h1, l1;
-        split_bf16(f[2 * i], h0, l0);
-        split_bf16(f[2 * i + 1], h1, l1);
-        wh[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        wl[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-      }
+      for (int i = 0; i < 4; ++i) split_bf16x2(f[2 * i], f[2 * i + 1], wh[i], wl[i]);
       qh[ks] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
       ql[ks] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
     }
@@ -454,27 +453,29 @@ __global__ __launch_bounds__(64 * QPG * pf_attn_groups(QPG)) void k_pf_attn(PfAt
   // staging of block kb by the group: K rows as 16-byte slots (slot c of slot row p at
   // p * SL + (c ^ (p % SL))); V transposed, two slots per 32-bit word (item: slot pair
   // pp, dims 8 c ..; consecutive threads take consecutive pairs, so their LDS words are
-  // adjacent).  Slots past cmax are zero (they may hold anything, and 0 * NaN would
-  // reach the sums).
-  u32x4_t kr[KI], vr[VI][2];
-  auto load_kv = [&](int kb) {
+  // adjacent).  A slot past cmax is loaded from slot cmax instead: a slot past the
+  // tile's last position may hold anything (a NaN there would reach the sums as
+  // 0 * NaN), while slot cmax holds finite data that every token's mask then gives
+  // weight 0.  Every load is issued unconditionally (a load under a branch makes the
+  // compiler wait for every load in flight before the next LDS store).
+  auto load_kv = [&](int kb, u32x4_t (&kr)[KI], u32x4_t (&vr)[VI][2]) {
     const int p0 = kb * kPfKvBlock;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int it = gt + GT * i, p = it / SL, c = it % SL;
-      kr[i] = (it < KN && p0 + p <= cmax) ? load_vec16(a.kc + (head + p0 + p) * D + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
+      const int it = gt + GT * i, p = it / SL, c = it % SL, q = p0 + p <= cmax ? p0 + p : cmax;
+      kr[i] = load_vec16(a.kc + (head + q) * D + 8 * (it < KN ? c : 0));
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int it = gt + GT * i, pp = it % (kPfKvBlock / 2), c = it / (kPfKvBlock / 2);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int p = p0 + 2 * pp + u;
-        vr[i][u] = (it < VN && p <= cmax) ? load_vec16(a.vc + (head + p) * D + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
+        const int p = p0 + 2 * pp + u, q = p <= cmax ? p : cmax;
+        vr[i][u] = load_vec16(a.vc + (head + q) * D + 8 * (it < VN ? c : 0));
       }
     }
   };
-  auto store_kv = [&](int buf) {
+  auto store_kv = [&](int buf, const u32x4_t (&kr)[KI], const u32x4_t (&vr)[VI][2]) {
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int it = gt + GT * i, p = it / SL, c = it % SL;
@@ -499,15 +500,19 @@ __global__ __launch_bounds__(64 * QPG * pf_attn_groups(QPG)) void k_pf_attn(PfAt
   f32x4_t ot[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) ot[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (grp < nblk) {
-    load_kv(grp);
-    store_kv(0);
-  }
+  // the group's blocks kb = grp + NGRP it, two in flight ahead of the products: block it
+  // is in LDS buffer it & 1, block it + 1 in the other register set since the block
+  // before, block it + 2's loads are issued into this set at the start of block it
+  u32x4_t kra[KI], vra[VI][2], krb[KI], vrb[VI][2];
+  load_kv(grp, kra, vra);
+  load_kv(grp + NGRP, krb, vrb);
+  store_kv(0, kra, vra);
   __syncthreads();
-  for (int it = 0; it < iters; ++it) {
-    const int kb = grp + NGRP * it, buf = it & 1;
-    const bool live = kb < nblk, more = kb + NGRP < nblk;
-    if (more) load_kv(kb + NGRP);
+  auto block = [&](int it, int buf, u32x4_t (&kc)[KI], u32x4_t (&vc)[VI][2], const u32x4_t (&kn)[KI],
+                   const u32x4_t (&vn)[VI][2]) {
+    const int kb = grp + NGRP * it;
+    const bool live = kb < nblk;
+    load_kv(kb + 2 * NGRP, kc, vc);
     if (live) {
       // S^T = K Q^T: lane (n, gq) gets slots 16 pb + 4 gq + e of token n
       f32x4_t st[2];
@@ -544,19 +549,16 @@ __global__ __launch_bounds__(64 * QPG * pf_attn_groups(QPG)) void k_pf_attn(PfAt
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int e = 0; e < 4; ++e) ot[db][e] *= al;
+      // (with mn = -inf every score here is -inf too: subtracting 0 keeps exp2(-inf) = 0)
+      const float mref = mn == -INFINITY ? 0.f : mn;
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const float e0 = s[pb][2 * i] == -INFINITY ? 0.f : exp2_fast(s[pb][2 * i] - mn);
-          const float e1 = s[pb][2 * i + 1] == -INFINITY ? 0.f : exp2_fast(s[pb][2 * i + 1] - mn);
+          const float e0 = exp2_fast(s[pb][2 * i] - mref), e1 = exp2_fast(s[pb][2 * i + 1] - mref);
           l += e0 + e1;
-          uint16_t h0, l0, h1, l1;
-          split_bf16(e0, h0, l0);
-          split_bf16(e1, h1, l1);
-          ph[2 * pb + i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          pl[2 * pb + i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+          split_bf16x2(e0, e1, ph[2 * pb + i], pl[2 * pb + i]);
         }
       const uint4 PH = make_uint4(ph[0], ph[1], ph[2], ph[3]), PL = make_uint4(pl[0], pl[1], pl[2], pl[3]);
       // O^T += V^T P^T: lane (n, gq) supplies V^T row 16 db + n at slots 4 gq .. + 3, 16 + 4 gq .. + 3
@@ -571,8 +573,12 @@ __global__ __launch_bounds__(64 * QPG * pf_attn_groups(QPG)) void k_pf_attn(PfAt
         ot[db] = mfma16x16x32_bf16(vf, PL, ot[db]);
       }
     }
-    if (more) store_kv(buf ^ 1);
+    store_kv(buf ^ 1, kn, vn);   // (after the group's last block: a buffer no one reads again)
     __syncthreads();
+  };
+  for (int it = 0; it < iters; it += 2) {
+    block(it, 0, kra, vra, krb, vrb);
+    if (it + 1 < iters) block(it + 1, 1, krb, vrb, kra, vra);   // (iters is the same for every group)
   }
   // merge the groups' states: groups 1.. write (m, l, O^T) per lane, group 0 combines
   // (a group that saw no slot of a token has m = -inf and weight 0)
