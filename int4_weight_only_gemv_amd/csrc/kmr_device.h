@@ -122,6 +122,25 @@ __device__ __forceinline__ f32x4_t mfma16x16x32_bf16(const uint4 a, const uint4 
                                                  c, 0, 0, 0);
 }
 
+// The same product shape with K = 16: lane l supplies a[l % 16][4 (l / 16) + e] and
+// b[4 (l / 16) + e][l % 16] as element e of its 4 bf16 (2 words); c as above
+// (v_mfma_f32_16x16x16_bf16).
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t mfma16x16x16_bf16(const uint2 a, const uint2 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b),
+                                                   c, 0, 0, 0);
+}
+
+// (a, b) as bf16 high parts and bf16 low parts (the residuals f - high), packed in pairs;
+// round to nearest even (v_cvt_pk_bf16_f32: one instruction per pair).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)a, (__bf16)b});
+  const float ra = a - __uint_as_float(h << 16), rb = b - __uint_as_float(h & 0xffff0000u);
+  hi = h;
+  lo = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)ra, (__bf16)rb});
+}
+
 // (a & mask) | bias as one v_and_or_b32.  A three-source VALU instruction takes no
 // 32-bit literal on this architecture, so with literal constants the compiler splits
 // it into v_and_b32 + v_or_b32.  The empty asm statements only hide the constants'

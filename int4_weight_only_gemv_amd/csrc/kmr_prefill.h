@@ -384,16 +384,6 @@ struct PfAttnArgs {
   float scale_log2;        // log2(e) / sqrt(D)
 };
 
-// (a, b) as bf16 high parts and bf16 low parts (the residuals f - high), packed in pairs;
-// round to nearest even (v_cvt_pk_bf16_f32: one instruction per pair).
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const uint32_t h = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)a, (__bf16)b});
-  const float ra = a - __uint_as_float(h << 16), rb = b - __uint_as_float(h & 0xffff0000u);
-  hi = h;
-  lo = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)ra, (__bf16)rb});
-}
-
 // Groups per work-group (each QPG waves) and the LDS the kernel takes.
 __host__ __device__ constexpr int pf_attn_groups(int QPG) { return QPG == 4 ? 2 : 4; }
 __host__ __device__ constexpr int pf_attn_vs() { return kPfKvBlock + 4; }   // V^T row stride (bf16)

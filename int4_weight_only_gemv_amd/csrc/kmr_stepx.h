@@ -60,13 +60,17 @@ __device__ __forceinline__ void xitem(int item, const int* s_ns, int GPX, int& b
   s = rem - gl * ns;
 }
 
-// K/V rows of attention item `item` (row b, local kv head, 128-position split):
-// 16-lane row `row` of wave `wave` takes positions s*128 + 4*row + {0..3}, this
-// lane DPL dims of each.  The loads are unconditional (slot clamped into the
-// cache) so that nothing waits for them here; the attention loop ignores slots
-// past the row's cache position and takes the new slot's k/v from the QKV phase.
+// K/V rows of attention item `item` (row b, local kv head, 128-position split), laid
+// out for the matrix-core products of the attention loop.  Wave w takes positions
+// s*128 + 16 w + {0..15}; lane (r, i) = (lane / 16, lane % 16) loads
+//   K: position s*128 + 16 w + i, dims 32 t + 8 r .. + 7 for t < D/32 (the first
+//      operand of the score product: row i, columns 8 r .. of each 32-dim step)
+//   V: positions s*128 + 16 w + 4 r + e, e < 4, dims DPL i .. + DPL - 1.
+// The loads are unconditional (slot clamped into the cache) so that nothing waits
+// for them here; the attention loop ignores slots past the row's cache position
+// and takes the new slot's k/v from the QKV phase.
 template <int DPL>
-__device__ __forceinline__ void attn_load_kv(uint32_t (&kr)[4][DPL / 2], uint32_t (&vr)[4][DPL / 2],
+__device__ __forceinline__ void attn_load_kv(uint32_t (&kr)[DPL / 2][4], uint32_t (&vr)[4][DPL / 2],
                                              const uint16_t* kc, const uint16_t* vc, int item,
                                              const int* s_ns, const int* s_c, int GPX, int x, int Hkv,
                                              int M, int D, int wave) {
@@ -74,23 +78,28 @@ __device__ __forceinline__ void attn_load_kv(uint32_t (&kr)[4][DPL / 2], uint32_
   int b, gl, s;
   xitem(item, s_ns, GPX, b, gl, s);
   const int g = x * GPX + gl;
-  const int lane = otid() & 63, row = wave * 4 + (lane >> 4), d0 = (lane & 15) * DPL;
+  const int lane = otid() & 63, rr = lane >> 4, li = lane & 15;
   const size_t head_base = ((size_t)b * Hkv + g) * M;
+  const int p0 = s * kXSplit + 16 * wave;
+  {
+    const int p = p0 + li < M ? p0 + li : M - 1;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    int p = s * kXSplit + 4 * row + it;
+    for (int t = 0; t < DPL / 2; ++t) {
+      const uint4 k4 = *reinterpret_cast<const uint4*>(kc + (head_base + p) * D + 32 * t + 8 * rr);
+      kr[t][0] = k4.x; kr[t][1] = k4.y; kr[t][2] = k4.z; kr[t][3] = k4.w;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    int p = p0 + 4 * rr + e;
     p = p < M ? p : M - 1;
-    // DPL bf16 = DPL * 2 bytes per lane, aligned to that size (d0 = lane * DPL)
+    // DPL bf16 = DPL * 2 bytes per lane, aligned to that size (DPL * li)
     if constexpr (DPL == 8) {
-      const uint4 k4 = *reinterpret_cast<const uint4*>(kc + (head_base + p) * D + d0);
-      const uint4 v4 = *reinterpret_cast<const uint4*>(vc + (head_base + p) * D + d0);
-      kr[it][0] = k4.x; kr[it][1] = k4.y; kr[it][2] = k4.z; kr[it][3] = k4.w;
-      vr[it][0] = v4.x; vr[it][1] = v4.y; vr[it][2] = v4.z; vr[it][3] = v4.w;
+      const uint4 v4 = *reinterpret_cast<const uint4*>(vc + (head_base + p) * D + DPL * li);
+      vr[e][0] = v4.x; vr[e][1] = v4.y; vr[e][2] = v4.z; vr[e][3] = v4.w;
     } else {
-      const uint2 k2 = *reinterpret_cast<const uint2*>(kc + (head_base + p) * D + d0);
-      const uint2 v2 = *reinterpret_cast<const uint2*>(vc + (head_base + p) * D + d0);
-      kr[it][0] = k2.x; kr[it][1] = k2.y;
-      vr[it][0] = v2.x; vr[it][1] = v2.y;
+      const uint2 v2 = *reinterpret_cast<const uint2*>(vc + (head_base + p) * D + DPL * li);
+      vr[e][0] = v2.x; vr[e][1] = v2.y;
     }
   }
 }
@@ -415,6 +424,12 @@ __device__ __forceinline__ void publish_staged_x(uint64_t* dst, long long stride
 //   xown  fp32 [BT][RPW]        this group's rows of the residual stream
 //   cs    float2 [BT][D/2]      RoPE cos/sin of each row
 //   red   float [128]
+// Float offset in the attention scratch of the q heads' bf16 splits (16-byte
+// aligned), after q/k/v, the wave states and their merge weights.
+__host__ __device__ inline int xattn_qb(int D, int QPG) {
+  return ((QPG + 2) * D + kStepWaves * QPG * (D + 2) + (kStepWaves + 2) * QPG + 3) & ~3;
+}
+
 struct StepXLds {
   size_t xs, cc, sums, xin, xown, cs, red, wgu, total;
 };
@@ -425,7 +440,7 @@ __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 15) & ~(size_t)15; return r; };
   const size_t pw = (size_t)QPG * (D + 2);
   // attention: q/k/v, then the wave states and their merge weights (disjoint)
-  size_t xin = (size_t)(QPG + 2) * D * 4 + (size_t)kStepWaves * pw * 4 + (size_t)(kStepWaves + 2) * QPG * 4;
+  size_t xin = (size_t)xattn_qb(D, QPG) * 4 + (size_t)2 * QPG * D * 2;
   const size_t merge = (size_t)BT * GPX * kXMergeChunk * pw * 4 +
                        (size_t)BT * GPX * QPG * (kXMergeChunk + 2) * 4;
   const size_t rs = (size_t)kXcds * BT * RPW * 4;
@@ -475,8 +490,9 @@ __device__ __forceinline__ void wrows_from_lds(WRows<kXGuRows, 1>& w, const uint
 // gate of act row r for r < 24, up of act row r - 24 after) form three 16-row tiles,
 // and wave w takes all of them over its 256 columns [256 w, 256 w + 256), two
 // groups of four 32-column chunks.  The codes stream into LDS a whole 128-byte line
-// per row and load: load i, lane l takes local row 8 i + l / 8, chunk 8 w + l % 8,
-// into slot i*64 + l.  The scale/zero words of the wave's 96 (row, group) pairs
+// per row and load: load i, lane l takes local row 8 i + l / 8, chunk
+// 8 w + ((l % 8) ^ (l / 8)), into slot i*64 + l (the XOR with the row's low bits puts
+// the 8 rows of one chunk that a tile read takes together in distinct LDS banks).  The scale/zero words of the wave's 96 (row, group) pairs
 // follow in two loads: slot p = 2 r + h holds local row r, group 2 w + h.
 constexpr int kGuMfmaK = 2048, kGuMfmaRows = 24;
 __device__ __forceinline__ void gu_tiles_to_lds(const uint8_t* packed, const uint32_t* sz, int lgG,
@@ -485,7 +501,7 @@ __device__ __forceinline__ void gu_tiles_to_lds(const uint8_t* packed, const uin
   const int lane = otid() & 63, wave = otid() >> 6, NG = kGuMfmaK >> lgG;
 #pragma unroll
   for (int i = 0; i < kXGuRows; ++i)
-    __builtin_amdgcn_global_load_lds(packed + (size_t)row[i] * (kGuMfmaK / 2) + 16 * (8 * wave + (lane & 7)),
+    __builtin_amdgcn_global_load_lds(packed + (size_t)row[i] * (kGuMfmaK / 2) + 16 * (8 * wave + ((lane & 7) ^ (lane >> 3))),
                                      codes + i * 64, 16, 0, 0);
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -538,15 +554,15 @@ __device__ __forceinline__ void gu_mfma_part(const uint4* codes, const uint32_t*
   for (int h = 0; h < 2; ++h) {
     const int c0 = 8 * wave + 4 * h;
     // every LDS read of this group first: the staged rows, then the three tiles'
-    // codes (local row 16 t + n, chunk c0 + gq: load 2 t + n / 8, lane 8 (n % 8) + 4 h + gq)
-    // and scale/zero words
+    // codes (local row 16 t + n, chunk c0 + gq: load 2 t + n / 8, lane
+    // 8 (n % 8) + ((4 h + gq) ^ (n % 8))) and scale/zero words
     uint4 xv[4], cw[3];
     uint32_t zz[3];
 #pragma unroll
     for (int q = 0; q < 4; ++q) xv[q] = xs[(bn * 4 + q) * CH + c0 + gq];
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
-      cw[t] = codes[(2 * t + (n >> 3)) * 64 + 8 * (n & 7) + 4 * h + gq];
+      cw[t] = codes[(2 * t + (n >> 3)) * 64 + 8 * (n & 7) + ((4 * h + gq) ^ (n & 7))];
       zz[t] = szw[2 * (16 * t + n) + h];
     }
 #pragma unroll
@@ -739,7 +755,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     uint16_t* vc = a.vc + (size_t)l * a.cacheB * Hkv * M * D;
     int total = 0;
     for (int b = 0; b < B; ++b) total += GPX * s_ns[b];
-    uint32_t kr[4][DPL / 2], vr[4][DPL / 2];
+    uint32_t kr[DPL / 2][4], vr[4][DPL / 2];
     // ================= QKV rows of this XCD's kv heads: RQ rows per group, 2 per wave
     {
       constexpr int NR = NRQ;
@@ -812,6 +828,9 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         }
         // q heads of kv head g (contiguous), then k, then v: one gather
         float* qv = xin;
+        float* s_w = xin + (QPG + 2) * D;                  // [8 waves][QPG][D + 2], after q/k/v
+        float* s_e = s_w + kStepWaves * QPG * (D + 2);     // [8][QPG] weights, [QPG] max, [QPG] sum
+        uint16_t* qb = reinterpret_cast<uint16_t*>(xin + xattn_qb(D, QPG));   // [2 QPG][D] q splits
         {
           auto addr = [](int i) { return (size_t)i; };
           auto place = [](int i) { return i; };
@@ -825,7 +844,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         KMR_TRACE_MARK(tev + 2);
         // per-head RMSNorm + RoPE of the q heads and k, and bf16 rounding of k and
         // v, once per group: wave h takes head h (q heads, then k, then v), lane l
-        // the rotate-half pair of dims (l, l + D/2), in place in LDS
+        // the rotate-half pair of dims (l, l + D/2), in place in LDS; q head h also as
+        // its bf16 high parts (row 2 h of qb) and low parts (row 2 h + 1)
         if (wave <= QPG + 1) {
           float* hv = qv + wave * D;
           const bool act = lane < HALF;
@@ -849,105 +869,107 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
             hv[lane] = x0;
             hv[lane + HALF] = x1;
           }
+          if (wave < QPG && act) {
+            uint32_t hi, lo;
+            split_bf16x2(x0, x1, hi, lo);
+            qb[2 * wave * D + lane] = (uint16_t)hi;
+            qb[2 * wave * D + lane + HALF] = (uint16_t)(hi >> 16);
+            qb[(2 * wave + 1) * D + lane] = (uint16_t)lo;
+            qb[(2 * wave + 1) * D + lane + HALF] = (uint16_t)(lo >> 16);
+          }
         }
         __syncthreads();
-        float q[QPG][DPL], kf[DPL], vf[DPL];
-#pragma unroll
-        for (int h = 0; h < QPG; ++h)
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) q[h][e] = qv[h * D + d0 + e];
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) {
-          kf[e] = qv[QPG * D + d0 + e];
-          vf[e] = qv[(QPG + 1) * D + d0 + e];
-        }
+        // the new slot's k and v: bf16 values held as fp32 in LDS
+        const float* nk = qv + QPG * D;
+        const float* nv = qv + (QPG + 1) * D;
+        auto bf16_pair = [](float lo, float hi) {   // (both already bf16 values)
+          return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+        };
         KMR_TRACE_MARK(l == 1 ? 59 : 64);
         if (s == ns - 1 && row == 0) {
           uint16_t* kd = kc + (head_base + c) * D + d0;
           uint16_t* vd = vc + (head_base + c) * D + d0;
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) { kd[e] = f32_to_bf16(kf[e]); vd[e] = f32_to_bf16(vf[e]); }
+          for (int e = 0; e < DPL; ++e) { kd[e] = f32_to_bf16(nk[d0 + e]); vd[e] = f32_to_bf16(nv[d0 + e]); }
         }
+        // The wave's 16 positions p0 + 0..15 on the matrix cores.  Scores S = K Q^T: K rows
+        // are the first operand (lane (rr, li) supplies position p0 + li), the second is
+        // the columns (q_0 high, q_0 low, q_1 high, q_1 low) of the q heads' bf16 splits
+        // (lanes of columns 4..15 repeat them; those columns are never read), and lane
+        // (rr, li) receives column li at positions p0 + 4 rr + e.
+        const int p0 = s * kXSplit + 16 * wave;
+        if (p0 + li == c) {
+#pragma unroll
+          for (int t = 0; t < DPL / 2; ++t)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              kr[t][w] = bf16_pair(nk[32 * t + 8 * rr + 2 * w], nk[32 * t + 8 * rr + 2 * w + 1]);
+        }
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < DPL / 2; ++t) {
+          const uint4 bq = *reinterpret_cast<const uint4*>(qb + (li & 3) * D + 32 * t + 8 * rr);
+          sacc = mfma16x16x32_bf16(make_uint4(kr[t][0], kr[t][1], kr[t][2], kr[t][3]), bq, sacc);
+        }
+        // head li / 2 (li < 4): high + low products, in log2 units; -inf past the cache
+        // position.  Then the wave's state per head: the max over its 16 positions, the
+        // weights relative to it and their sum (rows added (0 + 1) + (2 + 3)).
+        float sc[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float t = (sacc[e] + dpp<0xB1>(sacc[e])) * a.scale_log2;
+          sc[e] = p0 + 4 * rr + e <= c ? t : -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        {
+          float lo, hi;
+          lane_pair<16>(mx, lo, hi);
+          mx = fmaxf(lo, hi);
+          lane_pair<32>(mx, lo, hi);
+          mx = fmaxf(lo, hi);
+        }
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[e] = sc[e] != -INFINITY ? exp2_fast(sc[e] - mx) : 0.f;
+        float ls = (pe[0] + pe[1]) + (pe[2] + pe[3]);
+        {
+          float lo, hi;
+          lane_pair<16>(ls, lo, hi);
+          ls = lo + hi;
+          lane_pair<32>(ls, lo, hi);
+          ls = lo + hi;
+        }
+        // O = P V: the weights' bf16 splits are the first operand (row 2 h: head h's high
+        // parts, row 2 h + 1: the low parts; lane (rr, li) supplies row li at positions
+        // p0 + 4 rr + e), V the second (product dt: lane (rr, li) supplies dim DPL li + dt
+        // of those positions), and lanes 0..15 receive rows 0..3 at their DPL dims.
+        uint32_t wh[2], wl[2];
+        split_bf16x2(pe[0], pe[1], wh[0], wl[0]);
+        split_bf16x2(pe[2], pe[3], wh[1], wl[1]);
+        const uint2 pa = (li & 1) ? make_uint2(wl[0], wl[1]) : make_uint2(wh[0], wh[1]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (p0 + 4 * rr + e == c) {
+#pragma unroll
+            for (int w = 0; w < DPL / 2; ++w) vr[e][w] = bf16_pair(nv[d0 + 2 * w], nv[d0 + 2 * w + 1]);
+          }
         float m[QPG], lsum[QPG], o[QPG][DPL];
 #pragma unroll
-        for (int h = 0; h < QPG; ++h) {
-          m[h] = -INFINITY;
-          lsum[h] = 0.f;
+        for (int dt = 0; dt < DPL; ++dt) {
+          const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;   // dim dt of each position pair
+          const uint2 bv = make_uint2(__builtin_amdgcn_perm(vr[1][dt >> 1], vr[0][dt >> 1], sel),
+                                      __builtin_amdgcn_perm(vr[3][dt >> 1], vr[2][dt >> 1], sel));
+          const f32x4_t od = mfma16x16x16_bf16(pa, bv, f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
+          for (int h = 0; h < QPG; ++h) o[h][dt] = od[2 * h] + od[2 * h + 1];
         }
-        // the row's 4 positions as one block: their scores (log2 units; -inf past
-        // the cache position), then one update of the running max and one rescale
-        // of the state per head, then the 4 weighted value rows
-        float sc[QPG][4];
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int p = s * kXSplit + 4 * row + it;
-          float kk[DPL];
-          if (p == c) {
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) kk[e] = kf[e];
-          } else {
-#pragma unroll
-            for (int e = 0; e < DPL / 2; ++e) { kk[2 * e] = bf16_lo(kr[it][e]); kk[2 * e + 1] = bf16_hi(kr[it][e]); }
-          }
-#pragma unroll
-          for (int h = 0; h < QPG; ++h) {
-            float t = 0.f;
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) t += q[h][e] * kk[e];
-            t = row16_sum(t) * a.scale_log2;
-            sc[h][it] = p <= c ? t : -INFINITY;
-          }
-        }
-        float mb[QPG];
 #pragma unroll
         for (int h = 0; h < QPG; ++h) {
-          mb[h] = fmaxf(fmaxf(m[h], fmaxf(sc[h][0], sc[h][1])), fmaxf(sc[h][2], sc[h][3]));
-          // (-inf: no valid position yet, the state stays empty)
-          const float corr = mb[h] != -INFINITY ? exp2_fast(m[h] - mb[h]) : 1.f;
-          lsum[h] *= corr;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) o[h][e] *= corr;
-          m[h] = mb[h];
-        }
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int p = s * kXSplit + 4 * row + it;
-          float vv[DPL];
-          if (p == c) {
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) vv[e] = vf[e];
-          } else {
-#pragma unroll
-            for (int e = 0; e < DPL / 2; ++e) { vv[2 * e] = bf16_lo(vr[it][e]); vv[2 * e + 1] = bf16_hi(vr[it][e]); }
-          }
-#pragma unroll
-          for (int h = 0; h < QPG; ++h) {
-            const float pe = sc[h][it] != -INFINITY ? exp2_fast(sc[h][it] - mb[h]) : 0.f;
-            lsum[h] += pe;
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) o[h][e] += pe * vv[e];
-          }
+          m[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 2 * h));
+          lsum[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), 2 * h));
         }
         KMR_TRACE_MARK(l == 1 ? 60 : 64);
-        // merge the 4 rows of each wave: rows (0,1) and (2,3), then (01, 23)
-#pragma unroll
-        for (int h = 0; h < QPG; ++h) {
-          float mlo, mhi, llo, lhi, olo[DPL], ohi[DPL];
-          lane_pair<16>(m[h], mlo, mhi);
-          lane_pair<16>(lsum[h], llo, lhi);
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) lane_pair<16>(o[h][e], olo[e], ohi[e]);
-          lse_merge(mlo, llo, olo, mhi, lhi, ohi, DPL);
-          lane_pair<32>(mlo, m[h], mhi);
-          lane_pair<32>(llo, lsum[h], lhi);
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) lane_pair<32>(olo[e], o[h][e], ohi[e]);
-          lse_merge(m[h], lsum[h], o[h], mhi, lhi, ohi, DPL);
-        }
         KMR_TRACE_MARK(l == 1 ? 61 : 64);
-        float* s_w = xin + (QPG + 2) * D;  // [8 waves][QPG][D + 2], after q/k/v
         if (rr == 0) {
 #pragma unroll
           for (int h = 0; h < QPG; ++h) {
@@ -962,7 +984,6 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         __syncthreads();
         // merge the 8 wave states of each head: the log-sum-exp weights are
         // computed once per (wave, head), then each output is 8 multiply-adds
-        float* s_e = s_w + kStepWaves * QPG * (D + 2);   // [8][QPG] weights, [QPG] max, [QPG] sum
         static_assert(kStepWaves * QPG == 16, "one 16-lane row holds every (wave, head) state");
         if (wave == 0 && lane < 16) {
           // lane t = wave * QPG + head: the states of one head sit at lane ^ 2, ^ 4, ^ 8

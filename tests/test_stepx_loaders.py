@@ -119,15 +119,15 @@ def model_step_loads(H, Hq, Hkv, D, I, G, nwg):
     gu = Loads(2 * I, H, G)
     if fixed:
         # matrix-core tiles: load i, lane l: local row 8 i + l / 8 (gate rows, then up
-        # rows), chunk 8 wave + l % 8; scale/zero pairs p = 64 u + l < 96: (row p / 2,
-        # group 2 wave + p % 2)
+        # rows), chunk 8 wave + ((l % 8) ^ (l / 8)); scale/zero pairs p = 64 u + l < 96:
+        # (row p / 2, group 2 wave + p % 2)
         def grow_of(r):
             ar = np.where(r < GU_ROWS, r, r - GU_ROWS)
             return x * IX + j * GU_ROWS + ar + np.where(r < GU_ROWS, 0, I)
 
         for i in range(6):
             r = 8 * i + (ln >> 3)
-            gu.add(grow_of(r), 32 * (8 * wv + (ln & 7)), with_sz=False)
+            gu.add(grow_of(r), 32 * (8 * wv + ((ln & 7) ^ (ln >> 3))), with_sz=False)
         for u in range(2):
             p = 64 * u + ln
             gu.add_sz(grow_of(np.where(p < 96, p >> 1, 0)), 256 * wv + 128 * (ln & 1))
@@ -148,19 +148,41 @@ def model_step_loads(H, Hq, Hkv, D, I, G, nwg):
 
 
 def model_kv_loads(D, Hkv, M, B):
-    """Attention item loads: row b, kv head g, 128-slot split s, 16-lane row r of wave
-    w takes slots s*128 + 4 r + it (clamped into the cache), DPL dims from 16 (lane % 16)."""
+    """Attention item loads: row b, kv head g, 128-slot split s, lane (r, i) = (lane / 16,
+    lane % 16) of wave w.  K: slot s*128 + 16 w + i (clamped into the cache), 16 bytes at
+    dims 32 t + 8 r for t < D/32; V: slots s*128 + 16 w + 4 r + e (clamped), DPL dims from
+    DPL i.  Every (slot, dim) of a split's 128 slots must be read exactly once by each of
+    the K and V loads (before the clamp), and every load must stay inside the cache."""
     DPL = D // 16
-    s = np.arange(-(-M // 128))
-    w, ln, it = np.meshgrid(np.arange(WAVES), np.arange(LANES), np.arange(4), indexing="ij")
-    p = s[:, None] * 128 + (4 * (w * 4 + (ln >> 4)) + it).ravel()[None]
-    p = np.minimum(p, M - 1)
-    d0 = (ln & 15).ravel() * DPL
-    assert np.all(p >= 0) and np.all(p < M)
-    assert np.all(d0 + DPL <= D)
-    head = (np.arange(B)[:, None] * Hkv + np.arange(Hkv)[None]) * M
-    last = (head.max() + p.max()) * D + d0.max() + DPL
-    assert last <= B * Hkv * M * D
+    ns = -(-M // 128)
+    w, ln = np.meshgrid(np.arange(WAVES), np.arange(LANES), indexing="ij")
+    r, i = (ln >> 4).ravel(), (ln & 15).ravel()
+    w = w.ravel()
+    head = (np.arange(B)[:, None] * Hkv + np.arange(Hkv)[None]).ravel() * M
+    for s in range(ns):
+        # K
+        pk = s * 128 + 16 * w
+        pk = pk + i
+        kd = np.stack([32 * t + 8 * r for t in range(D // 32)])            # [t][lane]
+        cov = np.zeros((128, D), np.int32)
+        for t in range(D // 32):
+            for d in range(8):
+                np.add.at(cov, (pk - s * 128, kd[t] + d), 1)
+        assert np.all(cov == 1), "K: every (slot, dim) of the split once"
+        pkc = np.minimum(pk, M - 1)
+        assert np.all(kd + 8 <= D) and np.all(kd % 8 == 0)
+        # V
+        cov[:] = 0
+        for e in range(4):
+            pv = s * 128 + 16 * w + 4 * r + e
+            for d in range(DPL):
+                np.add.at(cov, (pv - s * 128, DPL * i + d), 1)
+        assert np.all(cov == 1), "V: every (slot, dim) of the split once"
+        pvc = np.minimum(s * 128 + 16 * w + 4 * r + 3, M - 1)
+        for p in (pkc, pvc):
+            assert np.all(p >= 0) and np.all(p < M)
+        last = (head.max() + max(pkc.max(), pvc.max())) * D + D
+        assert last <= B * Hkv * M * D
 
 
 GRID = list(itertools.product([512, 1024, 1536, 2048, 2560], [64, 128], [8, 16], [1024, 2048, 3072, 6144, 8192],
