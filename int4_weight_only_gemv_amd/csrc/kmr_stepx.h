@@ -128,6 +128,34 @@ __device__ __forceinline__ void wnarrow_load(WNarrow& w, const uint8_t* packed, 
   }
 }
 
+// The same weights streamed into LDS instead of registers: chunk t of thread i at
+// raw[t * kStepThreads + i] and sz[t * kStepThreads + i] (each wave's 64 lanes
+// contiguous, as the LDS DMA writes them).  Slots of chunks a lane does not load keep
+// stale data, which narrow_dot never uses for a published row.
+__device__ __forceinline__ void wnarrow_to_lds(const uint8_t* packed, const uint32_t* sz, int K, int lgG,
+                                               int k0, int KS, int row, bool ok, uint4* raw_l,
+                                               uint32_t* sz_l) {
+  const int tid = otid(), sub = tid & 7, wave = tid >> 6, CHs = KS >> 5, NG = K >> lgG;
+#pragma unroll
+  for (int t = 0; t < kXNarrowCpl; ++t) {
+    const int c = sub + 8 * t;
+    if (ok && c < CHs) {
+      __builtin_amdgcn_global_load_lds(packed + (size_t)row * (K / 2) + (k0 >> 1) + 16 * c,
+                                       raw_l + t * kStepThreads + wave * 64, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(sz + (size_t)row * NG + ((k0 + 32 * c) >> lgG),
+                                       sz_l + t * kStepThreads + wave * 64, 4, 0, 0);
+    }
+  }
+}
+__device__ __forceinline__ void wnarrow_from_lds(WNarrow& w, const uint4* raw_l, const uint32_t* sz_l) {
+  const int tid = otid();
+#pragma unroll
+  for (int t = 0; t < kXNarrowCpl; ++t) {
+    w.raw[t] = raw_l[t * kStepThreads + tid];
+    w.sz[t] = sz_l[t * kStepThreads + tid];
+  }
+}
+
 // out[b] = dot of the group's row with staged input row b over the slice; every
 // lane of the 8-lane group receives the sums.
 template <int BT, typename CS>
@@ -414,6 +442,12 @@ __device__ __forceinline__ void publish_staged_x(uint64_t* dst, long long stride
   }
 }
 
+// Float offset in the attention scratch of the q heads' bf16 splits (16-byte
+// aligned), after q/k/v, the wave states and their merge weights.
+__host__ __device__ inline int xattn_qb(int D, int QPG) {
+  return ((QPG + 2) * D + kStepWaves * QPG * (D + 2) + (kStepWaves + 2) * QPG + 3) & ~3;
+}
+
 // ------------------------------------------------------------------ LDS layout
 //   xs    uint4 [BT][4][H/32]   staged fp16 input pairs (every GEMV input <= H)
 //   cc    float2 [BT][H/32]     per-chunk (C1, C2) of the O input
@@ -424,14 +458,11 @@ __device__ __forceinline__ void publish_staged_x(uint64_t* dst, long long stride
 //   xown  fp32 [BT][RPW]        this group's rows of the residual stream
 //   cs    float2 [BT][D/2]      RoPE cos/sin of each row
 //   red   float [128]
-// Float offset in the attention scratch of the q heads' bf16 splits (16-byte
-// aligned), after q/k/v, the wave states and their merge weights.
-__host__ __device__ inline int xattn_qb(int D, int QPG) {
-  return ((QPG + 2) * D + kStepWaves * QPG * (D + 2) + (kStepWaves + 2) * QPG + 3) & ~3;
-}
-
+//   wgu   gate/up codes and scale/zero words, [8 waves][6 rows][64]
+//   wdn   (batch > 1) the group's down weights: uint4 [3][512] codes, u32 [3][512]
+//         scale/zero words
 struct StepXLds {
-  size_t xs, cc, sums, xin, xown, cs, red, wgu, total;
+  size_t xs, cc, sums, xin, xown, cs, red, wgu, wdn, total;
 };
 
 __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int QPG, int GPX) {
@@ -456,6 +487,7 @@ __host__ __device__ inline StepXLds stepx_lds(int BT, int H, int RPW, int D, int
   s.cs = take((size_t)BT * (D / 2) * 8);
   s.red = take(128 * 4);
   s.wgu = take((size_t)kStepWaves * kXGuRows * 64 * 20);   // gate/up codes (16 B) + scale/zero (4 B)
+  s.wdn = BT > 1 ? take((size_t)kXNarrowCpl * kStepThreads * 20) : 0;
   s.total = o;
   return s;
 }
@@ -651,6 +683,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   group_fail_reset();
   __syncthreads();
   uint4* xs = reinterpret_cast<uint4*>(smem + Ld.xs);
+  uint4* wdn_raw = reinterpret_cast<uint4*>(smem + Ld.wdn);
+  uint32_t* wdn_sz = reinterpret_cast<uint32_t*>(smem + Ld.wdn + (size_t)kXNarrowCpl * kStepThreads * 16);
   float2* cc = reinterpret_cast<float2*>(smem + Ld.cc);
   float* sums = reinterpret_cast<float*>(smem + Ld.sums);
   float* xin = reinterpret_cast<float*>(smem + Ld.xin);
@@ -1208,10 +1242,16 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       }
       KMR_TRACE_MARK(tev + 7);
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gate/up rows are in LDS
-      if constexpr (kAhead) {
+      // the down weights, requested now so that they have arrived before the act
+      // gather polls (at larger batches into LDS: held in registers across the
+      // gate/up product they would be spilled)
+      {
         const int orow = orow_at();
         const bool ook = ook_at(orow);
-        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, lgG, x * IX, IX, ook ? orow : 0, ook);
+        if constexpr (kAhead)
+          wnarrow_load(wd, Ly.d_p, Ly.d_s, I, lgG, x * IX, IX, ook ? orow : 0, ook);
+        else
+          wnarrow_to_lds(Ly.d_p, Ly.d_s, I, lgG, x * IX, IX, ook ? orow : 0, ook, wdn_raw, wdn_sz);
         g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
       }
       if constexpr (FIXED) {
@@ -1276,18 +1316,15 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     KMR_TRACE_MARK(tev + 8);
     // ================= down split-K over the XCD's slice, then RS_D
     {
-      if constexpr (!kAhead) {
-        g_next = staged_gain(a.layers[l + 1 < a.L ? l + 1 : l].in_norm, H, RPW, j * RPW);
-        const int orow = orow_at();
-        const bool ook = ook_at(orow);
-        wnarrow_load(wd, Ly.d_p, Ly.d_s, I, lgG, x * IX, IX, ook ? orow : 0, ook);
-      }
       if (!gather_staged<BT, 4 * BT>(lact, SA, IX, B, 0, ctag(ph + 5), xs, sums, lim)) {
         alive = false;
         break;
       }
       settle(g_next);
       KMR_TRACE_MARK(tev + 9);
+      // (each lane reads the slots its own wave's DMA wrote, complete once its gather
+      // poll has returned)
+      if constexpr (!kAhead) wnarrow_from_lds(wd, wdn_raw, wdn_sz);
       float out[BT];
       narrow_dot<BT>(wd, IX, B, xs, ChunkSums{sums, IX / 4}, out);
       const int sub = lane & 7;
