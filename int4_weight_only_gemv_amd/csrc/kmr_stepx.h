@@ -508,6 +508,31 @@ __device__ __forceinline__ void wrows_to_lds(const uint8_t* packed, const uint32
   }
 }
 
+// NR full rows of K <= 64*32 columns into LDS, one 32-column chunk per lane: row i
+// of this wave at codes[i * 64 + lane], its scale/zero word at szw[i * 64 + lane]
+// (slots of chunks past K, or of rows without ok, keep stale data: the dot products
+// skip the chunks, and such rows are never published).
+template <int NR>
+__device__ __forceinline__ void wrows_dma(const uint8_t* packed, const uint32_t* sz, int K, int lgG,
+                                          const int* row, const bool* ok, uint4* codes, uint32_t* szw) {
+  const int lane = otid() & 63, NG = K >> lgG;
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+    if (ok[i] && 32 * lane < K) {
+      __builtin_amdgcn_global_load_lds(packed + (size_t)row[i] * (K / 2) + 16 * lane, codes + i * 64, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(sz + (size_t)row[i] * NG + ((32 * lane) >> lgG), szw + i * 64, 4, 0, 0);
+    }
+}
+template <int NR>
+__device__ __forceinline__ void wrows_read(WRows<NR, 1>& w, const uint4* codes, const uint32_t* szw) {
+  const int lane = otid() & 63;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    w.raw[i][0] = codes[i * 64 + lane];
+    w.sz[i][0] = szw[i * 64 + lane];
+  }
+}
+
 __device__ __forceinline__ void wrows_from_lds(WRows<kXGuRows, 1>& w, const uint4* codes, const uint32_t* szw) {
   const int lane = otid() & 63;
 #pragma unroll
@@ -773,11 +798,21 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   // more than the latency saved.)
   constexpr bool kAhead = BT == 1;
   WRows<NRQ, 1> wq;
-  if constexpr (kAhead) {
+  // At larger batches the QKV rows go through LDS instead (held in registers they
+  // would be spilled): the first rows of each wave's gate/up slots, which are free
+  // from the end of one layer's gate/up product to the next layer's O phase.
+  uint4* wq_codes = reinterpret_cast<uint4*>(smem + Ld.wgu) + wave * kXGuRows * 64;
+  uint32_t* wq_sz = reinterpret_cast<uint32_t*>(smem + Ld.wgu + (size_t)kStepWaves * kXGuRows * 64 * 16) +
+                    wave * kXGuRows * 64;
+  static_assert(NRQ <= kXGuRows, "the QKV rows fit the gate/up slots");
+  {
     int row[NRQ], lr[NRQ];
     bool ok[NRQ];
     qkv_rows(row, lr, ok);
-    wrows_load(wq, a.layers[0].qkv_p, a.layers[0].qkv_s, H, lgG, row, ok);
+    if constexpr (kAhead)
+      wrows_load(wq, a.layers[0].qkv_p, a.layers[0].qkv_s, H, lgG, row, ok);
+    else
+      wrows_dma<NRQ>(a.layers[0].qkv_p, a.layers[0].qkv_s, H, lgG, row, ok, wq_codes, wq_sz);
   }
 
   for (int l = 0; l < a.L && alive; ++l) {
@@ -796,14 +831,13 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       int row[NR], lr[NR];
       bool ok[NR];
       qkv_rows(row, lr, ok);
-      if constexpr (!kAhead) {
-        wrows_load(wq, Ly.qkv_p, Ly.qkv_s, H, lgG, row, ok);
-        asm volatile("" ::: "memory");   // keep the weight requests ahead of the polls
-      }
       if (!gather_staged<BT, 4 * BT>(sx0, SX, H, B, NSS, ctag(ph), xs, sums, lim)) {
         alive = false;
         break;
       }
+      // (each lane reads the slots its own wave's DMA wrote, complete once its gather
+      // poll has returned)
+      if constexpr (!kAhead) wrows_read<NR>(wq, wq_codes, wq_sz);
       KMR_TRACE_MARK(tev + 0);
       // at batch 1 the K/V rows of the first attention item are requested now,
       // to be in flight during the QKV rows and their hand-off (the QKV rows,
@@ -1344,11 +1378,14 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         break;
       }
       if (l + 1 < a.L) {
-        if constexpr (kAhead) {
+        {
           int row[NRQ], lr[NRQ];
           bool ok[NRQ];
           qkv_rows(row, lr, ok);
-          wrows_load(wq, a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, lgG, row, ok);
+          if constexpr (kAhead)
+            wrows_load(wq, a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, lgG, row, ok);
+          else
+            wrows_dma<NRQ>(a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, lgG, row, ok, wq_codes, wq_sz);
         }
         publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, g_next, j, tag(ph + 6), plain, a.status);
       } else if (hx) {
