@@ -551,29 +551,33 @@ __device__ __forceinline__ void wrows_from_lds(WRows<kXGuRows, 1>& w, const uint
 // 8 w + ((l % 8) ^ (l / 8)), into slot i*64 + l (the XOR with the row's low bits puts
 // the 8 rows of one chunk that a tile read takes together in distinct LDS banks).  The scale/zero words of the wave's 96 (row, group) pairs
 // follow in two loads: slot p = 2 r + h holds local row r, group 2 w + h.
+// The same tile layout serves the group's 16 q/k/v rows (one tile, T = 1).
 constexpr int kGuMfmaK = 2048, kGuMfmaRows = 24;
+__host__ __device__ constexpr int gu_zloads(int T) { return (32 * T + 63) / 64; }
+template <int T = 3>
 __device__ __forceinline__ void gu_tiles_to_lds(const uint8_t* packed, const uint32_t* sz, int lgG,
-                                                const int (&row)[6], const int (&zrow)[2], uint4* codes,
-                                                uint32_t* szw) {
+                                                const int (&row)[2 * T], const int (&zrow)[gu_zloads(T)],
+                                                uint4* codes, uint32_t* szw) {
   const int lane = otid() & 63, wave = otid() >> 6, NG = kGuMfmaK >> lgG;
 #pragma unroll
-  for (int i = 0; i < kXGuRows; ++i)
+  for (int i = 0; i < 2 * T; ++i)
     __builtin_amdgcn_global_load_lds(packed + (size_t)row[i] * (kGuMfmaK / 2) + 16 * (8 * wave + ((lane & 7) ^ (lane >> 3))),
                                      codes + i * 64, 16, 0, 0);
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < gu_zloads(T); ++u)
     __builtin_amdgcn_global_load_lds(sz + (size_t)zrow[u] * NG + ((256 * wave + 128 * (lane & 1)) >> lgG),
                                      szw + u * 64, 4, 0, 0);
 }
 
-// This wave's part of the 48 gate/up dot products of each staged row b < B, over its
-// 256 columns, into part[(wave * BT + b) * 48 + local row].  Per tile and group the
+// This wave's part of the 16 T dot products (the 48 gate/up rows, or the 16 q/k/v
+// rows) of each staged row b < B, over its 256 columns, into
+// part[(wave * BT + b) * 16 T + local row].  Per tile and group the
 // four chunk products go through the matrix cores with the staged rows as the first
 // operand (row b of it; lanes of higher rows repeat row 0) and the weight tile as
 // the second, so lane n < 16 receives every batch row of weight row n.  The group's
 // scale and zero point then apply as in wave_dot_c, s (d - C1) + z C2, with the
 // staged constants of row b summed over the group's 16 eight-column words.
-template <int BT>
+template <int BT, int T = 3>
 __device__ __forceinline__ void gu_mfma_part(const uint4* codes, const uint32_t* szw, const uint4* xs,
                                              const float* sums, int B, float* part) {
   constexpr int CH = kGuMfmaK / 32, K4 = kGuMfmaK / 4;
@@ -602,9 +606,9 @@ __device__ __forceinline__ void gu_mfma_part(const uint4* codes, const uint32_t*
       C2[b][h] = su;
     }
   }
-  float acc[3][BT];
+  float acc[T][BT];
 #pragma unroll
-  for (int t = 0; t < 3; ++t)
+  for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int e = 0; e < BT; ++e) acc[t][e] = 0.f;
 #pragma unroll
@@ -613,17 +617,17 @@ __device__ __forceinline__ void gu_mfma_part(const uint4* codes, const uint32_t*
     // every LDS read of this group first: the staged rows, then the three tiles'
     // codes (local row 16 t + n, chunk c0 + gq: load 2 t + n / 8, lane
     // 8 (n % 8) + ((4 h + gq) ^ (n % 8))) and scale/zero words
-    uint4 xv[4], cw[3];
-    uint32_t zz[3];
+    uint4 xv[4], cw[T];
+    uint32_t zz[T];
 #pragma unroll
     for (int q = 0; q < 4; ++q) xv[q] = xs[(bn * 4 + q) * CH + c0 + gq];
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
+    for (int t = 0; t < T; ++t) {
       cw[t] = codes[(2 * t + (n >> 3)) * 64 + 8 * (n & 7) + ((4 * h + gq) ^ (n & 7))];
       zz[t] = szw[2 * (16 * t + n) + h];
     }
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
+    for (int t = 0; t < T; ++t) {
       uint32_t p[16];
       dequant16(cw[t], p);
       f32x4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -641,7 +645,7 @@ __device__ __forceinline__ void gu_mfma_part(const uint4* codes, const uint32_t*
     for (int e = 0; e < BT; ++e) {
       if (BT > 1 && e >= B) break;
 #pragma unroll
-      for (int t = 0; t < 3; ++t) part[(wave * BT + e) * 48 + 16 * t + n] = acc[t][e];
+      for (int t = 0; t < T; ++t) part[(wave * BT + e) * (16 * T) + 16 * t + n] = acc[t][e];
     }
   }
 }
@@ -805,15 +809,37 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   uint32_t* wq_sz = reinterpret_cast<uint32_t*>(smem + Ld.wgu + (size_t)kStepWaves * kXGuRows * 64 * 16) +
                     wave * kXGuRows * 64;
   static_assert(NRQ <= kXGuRows, "the QKV rows fit the gate/up slots");
-  {
-    int row[NRQ], lr[NRQ];
-    bool ok[NRQ];
-    qkv_rows(row, lr, ok);
-    if constexpr (kAhead)
-      wrows_load(wq, a.layers[0].qkv_p, a.layers[0].qkv_s, H, lgG, row, ok);
-    else
-      wrows_dma<NRQ>(a.layers[0].qkv_p, a.layers[0].qkv_s, H, lgG, row, ok, wq_codes, wq_sz);
-  }
+  // The constant-size instantiation takes the group's 16 q/k/v rows as one
+  // matrix-core tile, in the gate/up tile layout (every row valid: 32 groups of 16
+  // rows cover the XCD's 512); its partial sums go to wave 0's gate/up slots past the
+  // tile, which nothing else uses before the O phase.
+  static_assert(!FIXED || ((kFixHkv / kXcds) * (QPG + 2) * D == 16 * (kFixNwg / kXcds) && kFixH == kGuMfmaK),
+                "the constant-size q/k/v rows form one 16-row tile per group over kGuMfmaK columns");
+  auto qkv_row_of = [&](int r) {   // weight row of this group's local q/k/v row r
+    const int lr2 = j * RQ + r, gl = lr2 / ((QPG + 2) * D), t = lr2 - gl * (QPG + 2) * D, g = x * GPX + gl;
+    return t < QPG * D ? g * QPG * D + t
+         : t < (QPG + 1) * D ? Hq * D + g * D + (t - QPG * D)
+                             : Hq * D + Hkv * D + g * D + (t - (QPG + 1) * D);
+  };
+  auto qkv_request = [&](const StepLayer& L2) {
+    if constexpr (FIXED) {
+      int trow[2], zrow[gu_zloads(1)];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) trow[i] = qkv_row_of(8 * i + (lane >> 3));
+      zrow[0] = qkv_row_of(lane < 32 ? lane >> 1 : 0);   // (row, group) pair lane < 32
+      gu_tiles_to_lds<1>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, wq_codes, wq_sz);
+    } else {
+      int row[NRQ], lr[NRQ];
+      bool ok[NRQ];
+      qkv_rows(row, lr, ok);
+      if constexpr (kAhead)
+        wrows_load(wq, L2.qkv_p, L2.qkv_s, H, lgG, row, ok);
+      else
+        wrows_dma<NRQ>(L2.qkv_p, L2.qkv_s, H, lgG, row, ok, wq_codes, wq_sz);
+    }
+  };
+  float* qpart = reinterpret_cast<float*>(reinterpret_cast<uint4*>(smem + Ld.wgu) + 2 * 64);
+  qkv_request(a.layers[0]);
 
   for (int l = 0; l < a.L && alive; ++l) {
     const StepLayer& Ly = a.layers[l];
@@ -836,32 +862,50 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         break;
       }
       // (each lane reads the slots its own wave's DMA wrote, complete once its gather
-      // poll has returned)
-      if constexpr (!kAhead) wrows_read<NR>(wq, wq_codes, wq_sz);
+      // poll has returned; in the matrix-core form the gather's closing barrier makes
+      // every wave's slots visible)
+      if constexpr (!kAhead && !FIXED) wrows_read<NR>(wq, wq_codes, wq_sz);
       KMR_TRACE_MARK(tev + 0);
       // at batch 1 the K/V rows of the first attention item are requested now,
       // to be in flight during the QKV rows and their hand-off (the QKV rows,
       // requested a phase ago, are settled first)
       if constexpr (kAhead) {
+        if constexpr (!FIXED) {
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-          settle(wq.raw[i][0]);
-          settle(wq.sz[i][0]);
+          for (int i = 0; i < NR; ++i) {
+            settle(wq.raw[i][0]);
+            settle(wq.sz[i][0]);
+          }
         }
         if (j < total) attn_load_kv<DPL>(kr, vr, kc, vc, j, s_ns, s_c, GPX, x, Hkv, M, D, wave);
       }
-      float out[NR][BT];
-      wave_dot_c<BT, NR, 1>(wq, H, B, xs, ChunkSums{sums, H / 4}, out);
-      const float inv = row_inv<BT>(sums + BT * (H / 4), B, NSS, H, a.eps);
-      if (lane < B) {
+      if constexpr (FIXED) {
+        // wave partials [8][BT][16], then wave b sums batch row b's 16 rows
+        gu_mfma_part<BT, 1>(wq_codes, wq_sz, xs, sums, B, qpart);
+        __syncthreads();
+        if (wave < B) {
+          const float inv = staged_inv(sums + BT * (H / 4), wave, NSS, H, a.eps);
+          if (lane < 16) {
+            float v = 0.f;
 #pragma unroll
-        for (int i = 0; i < NR; ++i)
-          if (ok[i]) {
-            float v = out[i][0];
-#pragma unroll
-            for (int b = 1; b < BT; ++b) if (lane == b) v = out[i][b];
-            publish_l(lqkv + (size_t)lane * QX + lr[i], tag(ph + 1), v * inv, plain);
+            for (int w = 0; w < kStepWaves; ++w) v += qpart[(w * BT + wave) * 16 + lane];
+            publish_l(lqkv + (size_t)wave * QX + j * RQ + lane, tag(ph + 1), v * inv, plain);
           }
+        }
+      } else {
+        float out[NR][BT];
+        wave_dot_c<BT, NR, 1>(wq, H, B, xs, ChunkSums{sums, H / 4}, out);
+        const float inv = row_inv<BT>(sums + BT * (H / 4), B, NSS, H, a.eps);
+        if (lane < B) {
+#pragma unroll
+          for (int i = 0; i < NR; ++i)
+            if (ok[i]) {
+              float v = out[i][0];
+#pragma unroll
+              for (int b = 1; b < BT; ++b) if (lane == b) v = out[i][b];
+              publish_l(lqkv + (size_t)lane * QX + lr[i], tag(ph + 1), v * inv, plain);
+            }
+        }
       }
     }
     // K/V rows of this group's first attention item: requested right after its
@@ -1378,15 +1422,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         break;
       }
       if (l + 1 < a.L) {
-        {
-          int row[NRQ], lr[NRQ];
-          bool ok[NRQ];
-          qkv_rows(row, lr, ok);
-          if constexpr (kAhead)
-            wrows_load(wq, a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, lgG, row, ok);
-          else
-            wrows_dma<NRQ>(a.layers[l + 1].qkv_p, a.layers[l + 1].qkv_s, H, lgG, row, ok, wq_codes, wq_sz);
-        }
+        qkv_request(a.layers[l + 1]);
         publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, g_next, j, tag(ph + 6), plain, a.status);
       } else if (hx) {
         const int b = tid / RPW;

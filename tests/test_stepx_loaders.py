@@ -83,22 +83,34 @@ def model_step_loads(H, Hq, Hkv, D, I, G, nwg):
     x, j, wv, ln = np.meshgrid(np.arange(XCDS), np.arange(WPX), np.arange(WAVES), np.arange(LANES), indexing="ij")
     x, j, wv, ln = x.ravel(), j.ravel(), wv.ravel(), ln.ravel()
 
-    # q/k/v rows: two per wave (wrows_load, one 32-column chunk per lane, lane < H/32)
-    qkv = Loads((Hq + 2 * Hkv) * D, H, G)
-    used = []
-    for i in range(2):
-        rr = wv * 2 + i
-        lr = j * RQ + rr
-        ok = (rr < RQ) & (lr < QX) & (32 * ln < H)
+    def qkv_row(lr):   # weight row of the XCD's local q/k/v row lr
         gl = lr // ((QPG + 2) * D)
         t = lr - gl * (QPG + 2) * D
         g = x * GPX + gl
-        row = np.where(t < QPG * D, g * QPG * D + t,
-                       np.where(t < (QPG + 1) * D, Hq * D + g * D + (t - QPG * D),
-                                Hq * D + Hkv * D + g * D + (t - (QPG + 1) * D)))
-        qkv.add(row[ok], 32 * ln[ok])
-        used.append(np.ones(int(ok.sum()), bool))
-    qkv.check("qkv", used)
+        return np.where(t < QPG * D, g * QPG * D + t,
+                        np.where(t < (QPG + 1) * D, Hq * D + g * D + (t - QPG * D),
+                                 Hq * D + Hkv * D + g * D + (t - (QPG + 1) * D)))
+
+    qkv = Loads((Hq + 2 * Hkv) * D, H, G)
+    if fixed:
+        # matrix-core tile (gate/up layout, T = 1): load i < 2, lane l: local row
+        # 8 i + l / 8, chunk 8 wave + ((l % 8) ^ (l / 8)); scale/zero pair l < 32:
+        # (row l / 2, group 2 wave + l % 2), lanes past 32 repeat pair 0
+        assert RQ == 16
+        for i in range(2):
+            qkv.add(qkv_row(j * RQ + 8 * i + (ln >> 3)), 32 * (8 * wv + ((ln & 7) ^ (ln >> 3))), with_sz=False)
+        qkv.add_sz(qkv_row(j * RQ + np.where(ln < 32, ln >> 1, 0)), 256 * wv + 128 * (ln & 1))
+        qkv.check("qkv (matrix-core)")
+    else:
+        # two rows per wave (one 32-column chunk per lane, lane < H/32)
+        used = []
+        for i in range(2):
+            rr = wv * 2 + i
+            lr = j * RQ + rr
+            ok = (rr < RQ) & (lr < QX) & (32 * ln < H)
+            qkv.add(qkv_row(lr)[ok], 32 * ln[ok])
+            used.append(np.ones(int(ok.sum()), bool))
+        qkv.check("qkv", used)
 
     # o and down rows (wnarrow_load): output row j*RPW + 8 wave + lane/8 of the group,
     # the XCD's column slice, chunks (lane % 8) + 8 t
