@@ -554,17 +554,19 @@ __device__ __forceinline__ void wrows_from_lds(WRows<kXGuRows, 1>& w, const uint
 // The same tile layout serves the group's 16 q/k/v rows (one tile, T = 1).
 constexpr int kGuMfmaK = 2048, kGuMfmaRows = 24;
 __host__ __device__ constexpr int gu_zloads(int T) { return (32 * T + 63) / 64; }
-template <int T = 3>
+// (I0, I1: the code loads issued, [I0, I1) of the 2 T; Z0, Z1 likewise of the
+// scale/zero loads: a caller may split the stream in parts)
+template <int T = 3, int I0 = 0, int I1 = 2 * T, int Z0 = 0, int Z1 = gu_zloads(T)>
 __device__ __forceinline__ void gu_tiles_to_lds(const uint8_t* packed, const uint32_t* sz, int lgG,
                                                 const int (&row)[2 * T], const int (&zrow)[gu_zloads(T)],
                                                 uint4* codes, uint32_t* szw) {
   const int lane = otid() & 63, wave = otid() >> 6, NG = kGuMfmaK >> lgG;
 #pragma unroll
-  for (int i = 0; i < 2 * T; ++i)
+  for (int i = I0; i < I1; ++i)
     __builtin_amdgcn_global_load_lds(packed + (size_t)row[i] * (kGuMfmaK / 2) + 16 * (8 * wave + ((lane & 7) ^ (lane >> 3))),
                                      codes + i * 64, 16, 0, 0);
 #pragma unroll
-  for (int u = 0; u < gu_zloads(T); ++u)
+  for (int u = Z0; u < Z1; ++u)
     __builtin_amdgcn_global_load_lds(sz + (size_t)zrow[u] * NG + ((256 * wave + 128 * (lane & 1)) >> lgG),
                                      szw + u * 64, 4, 0, 0);
 }
@@ -1281,13 +1283,13 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     uint4* gu_codes = reinterpret_cast<uint4*>(smem + Ld.wgu) + wave * kXGuRows * 64;
     uint32_t* gu_sz = reinterpret_cast<uint32_t*>(smem + Ld.wgu + (size_t)kStepWaves * kXGuRows * 64 * 16) +
                       wave * kXGuRows * 64;
+    // matrix-core tiles: local row 16 t + lane % 16 of the group's gate/up rows
+    auto grow_of = [&](int r) {   // weight row of local row r (gate rows, then up rows)
+      const int ar = r < kGuMfmaRows ? r : r - kGuMfmaRows;
+      return x * IX + j * kGuMfmaRows + ar + (r < kGuMfmaRows ? 0 : I);
+    };
+    int trow[kXGuRows], zrow[2];
     if constexpr (FIXED) {
-      // matrix-core tiles: local row 16 t + lane % 16 of the group's gate/up rows
-      auto grow_of = [&](int r) {   // weight row of local row r (gate rows, then up rows)
-        const int ar = r < kGuMfmaRows ? r : r - kGuMfmaRows;
-        return x * IX + j * kGuMfmaRows + ar + (r < kGuMfmaRows ? 0 : I);
-      };
-      int trow[kXGuRows], zrow[2];
 #pragma unroll
       for (int i = 0; i < kXGuRows; ++i) trow[i] = grow_of(8 * i + (lane >> 3));
 #pragma unroll
@@ -1295,7 +1297,9 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         const int p = 64 * u + lane;   // (row, group) pair p < 96; the rest repeat pair 0
         zrow[u] = grow_of(p < 96 ? p >> 1 : 0);
       }
-      gu_tiles_to_lds(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, gu_codes, gu_sz);
+      // (the first half now, the rest once the reduce-scatter poll is in: a poll
+      // returns only after every load its wave issued before it)
+      gu_tiles_to_lds<3, 0, 3, 0, 1>(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, gu_codes, gu_sz);
     } else {
       wrows_to_lds(Ly.gu_p, Ly.gu_s, H, lgG, grow, gu_codes, gu_sz);
     }
@@ -1307,6 +1311,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         alive = false;
         break;
       }
+      if constexpr (FIXED) gu_tiles_to_lds<3, 3, 6, 1, 2>(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, gu_codes, gu_sz);
       publish_staged_x<BT>(sx1, SX, H, B, RPW, j * RPW, xn, hx, g_post, j, tag(ph + 4), plain, a.status);
     }
     KMR_TRACE_MARK(tev + 6);
