@@ -24,6 +24,8 @@
 // bit-identical copy of the residual stream: the same sums in the same order.
 #pragma once
 
+#include <type_traits>
+
 #include "kmr_step.h"
 
 namespace kmr {
@@ -823,14 +825,22 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
          : t < (QPG + 1) * D ? Hq * D + g * D + (t - QPG * D)
                              : Hq * D + Hkv * D + g * D + (t - (QPG + 1) * D);
   };
-  auto qkv_request = [&](const StepLayer& L2) {
+  // part 0: every load; in the matrix-core form part 1 is the first 8 rows and the
+  // scale/zero words, part 2 the other 8 rows (the other form requests all with part 2)
+  auto qkv_request = [&](const StepLayer& L2, auto part) {
+    constexpr int P = decltype(part)::value;
     if constexpr (FIXED) {
       int trow[2], zrow[gu_zloads(1)];
 #pragma unroll
       for (int i = 0; i < 2; ++i) trow[i] = qkv_row_of(8 * i + (lane >> 3));
       zrow[0] = qkv_row_of(lane < 32 ? lane >> 1 : 0);   // (row, group) pair lane < 32
-      gu_tiles_to_lds<1>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, wq_codes, wq_sz);
-    } else {
+      if constexpr (P == 0)
+        gu_tiles_to_lds<1>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, wq_codes, wq_sz);
+      else if constexpr (P == 1)
+        gu_tiles_to_lds<1, 0, 1, 0, 1>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, wq_codes, wq_sz);
+      else
+        gu_tiles_to_lds<1, 1, 2, 0, 0>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, wq_codes, wq_sz);
+    } else if constexpr (P != 1) {
       int row[NRQ], lr[NRQ];
       bool ok[NRQ];
       qkv_rows(row, lr, ok);
@@ -841,7 +851,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
     }
   };
   float* qpart = reinterpret_cast<float*>(reinterpret_cast<uint4*>(smem + Ld.wgu) + 2 * 64);
-  qkv_request(a.layers[0]);
+  qkv_request(a.layers[0], std::integral_constant<int, 0>());
 
   for (int l = 0; l < a.L && alive; ++l) {
     const StepLayer& Ly = a.layers[l];
@@ -1418,6 +1428,9 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         for (int b = 1; b < BT; ++b) if (sub == b) v = out[b];
         publish(a.pD + ((size_t)x * B + sub) * H + orow, tag(ph + 6), v * kStageUnscale);
       }
+      // half of the next layer's q/k/v rows, ahead of the reduce-scatter poll (the
+      // rest follows it)
+      if (l + 1 < a.L) qkv_request(a.layers[l + 1], std::integral_constant<int, 1>());
     }
     {
       float xn;
@@ -1427,7 +1440,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         break;
       }
       if (l + 1 < a.L) {
-        qkv_request(a.layers[l + 1]);
+        qkv_request(a.layers[l + 1], std::integral_constant<int, 2>());
         publish_staged_x<BT>(sx0, SX, H, B, RPW, j * RPW, xn, hx, g_next, j, tag(ph + 6), plain, a.status);
       } else if (hx) {
         const int b = tid / RPW;
