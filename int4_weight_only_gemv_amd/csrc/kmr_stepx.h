@@ -71,7 +71,7 @@ __device__ __forceinline__ void xitem(int item, const int* s_ns, int GPX, int& b
 // The loads are unconditional (slot clamped into the cache) so that nothing waits
 // for them here; the attention loop ignores slots past the row's cache position
 // and takes the new slot's k/v from the QKV phase.
-template <int DPL>
+template <int DPL, bool LK = true, bool LV = true>
 __device__ __forceinline__ void attn_load_kv(uint32_t (&kr)[DPL / 2][4], uint32_t (&vr)[4][DPL / 2],
                                              const uint16_t* kc, const uint16_t* vc, int item,
                                              const int* s_ns, const int* s_c, int GPX, int x, int Hkv,
@@ -83,7 +83,7 @@ __device__ __forceinline__ void attn_load_kv(uint32_t (&kr)[DPL / 2][4], uint32_
   const int lane = otid() & 63, rr = lane >> 4, li = lane & 15;
   const size_t head_base = ((size_t)b * Hkv + g) * M;
   const int p0 = s * kXSplit + 16 * wave;
-  {
+  if constexpr (LK) {
     const int p = p0 + li < M ? p0 + li : M - 1;
 #pragma unroll
     for (int t = 0; t < DPL / 2; ++t) {
@@ -93,6 +93,7 @@ __device__ __forceinline__ void attn_load_kv(uint32_t (&kr)[DPL / 2][4], uint32_
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
+    if constexpr (!LV) break;
     int p = p0 + 4 * rr + e;
     p = p < M ? p : M - 1;
     // DPL bf16 = DPL * 2 bytes per lane, aligned to that size (DPL * li)
@@ -878,9 +879,11 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       // every wave's slots visible)
       if constexpr (!kAhead && !FIXED) wrows_read<NR>(wq, wq_codes, wq_sz);
       KMR_TRACE_MARK(tev + 0);
-      // at batch 1 the K/V rows of the first attention item are requested now,
-      // to be in flight during the QKV rows and their hand-off (the QKV rows,
-      // requested a phase ago, are settled first)
+      // at batch 1 the K rows of the first attention item are requested now, to be
+      // in flight during the QKV rows and their hand-off (the QKV rows, requested a
+      // phase ago, are settled first); the V rows follow the q/k/v rows' publish
+      // (a wave issues no further instruction until its loads are accepted, so all
+      // 64 KB here would hold back the item groups' q/k/v rows, the hand-off's last)
       if constexpr (kAhead) {
         if constexpr (!FIXED) {
 #pragma unroll
@@ -889,7 +892,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
             settle(wq.sz[i][0]);
           }
         }
-        if (j < total) attn_load_kv<DPL>(kr, vr, kc, vc, j, s_ns, s_c, GPX, x, Hkv, M, D, wave);
+        if (j < total) attn_load_kv<DPL, true, false>(kr, vr, kc, vc, j, s_ns, s_c, GPX, x, Hkv, M, D, wave);
       }
       if constexpr (FIXED) {
         // wave partials [8][BT][16], then wave b sums batch row b's 16 rows
@@ -920,11 +923,15 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         }
       }
     }
-    // K/V rows of this group's first attention item: requested right after its
-    // q/k/v rows are out, so that their latency overlaps the hand-off
+    // K/V rows (at batch 1 the V rows) of this group's first attention item:
+    // requested right after its q/k/v rows are out, so that their latency overlaps
+    // the hand-off
     asm volatile("" ::: "memory");   // not ahead of the q/k/v stores
-    if constexpr (!kAhead)
+    if constexpr (!kAhead) {
       if (j < total) attn_load_kv<DPL>(kr, vr, kc, vc, j, s_ns, s_c, GPX, x, Hkv, M, D, wave);
+    } else {
+      if (j < total) attn_load_kv<DPL, false, true>(kr, vr, kc, vc, j, s_ns, s_c, GPX, x, Hkv, M, D, wave);
+    }
     KMR_TRACE_MARK(tev + 1);
     // O and down rows of this lane group (at larger batches recomputed where used:
     // held across the attention they would be spilled)
