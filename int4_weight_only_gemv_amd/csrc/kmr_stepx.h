@@ -456,12 +456,14 @@ __host__ __device__ inline int xattn_qb(int D, int QPG) {
 //   cc    float2 [BT][H/32]     per-chunk (C1, C2) of the O input
 //   sums  fp32 [BT][H/4], [BT][64]  per-word sums and sums of squares of a
 //                               gathered staged vector
-//   xin   fp32 scratch          attention q/k/v and wave states, split merge,
-//                               reduce-scatter partials, lm_head input
+//   xin   fp32 scratch          attention q/k/v, wave states and the q heads' bf16
+//                               splits, split merge, reduce-scatter partials,
+//                               lm_head input
 //   xown  fp32 [BT][RPW]        this group's rows of the residual stream
 //   cs    float2 [BT][D/2]      RoPE cos/sin of each row
 //   red   float [128]
-//   wgu   gate/up codes and scale/zero words, [8 waves][6 rows][64]
+//   wgu   gate/up codes and scale/zero words, [8 waves][6 rows][64] (also the q/k/v
+//         rows between the gate/up products, and the q/k/v tile's wave partials)
 //   wdn   (batch > 1) the group's down weights: uint4 [3][512] codes, u32 [3][512]
 //         scale/zero words
 struct StepXLds {
@@ -552,7 +554,8 @@ __device__ __forceinline__ void wrows_from_lds(WRows<kXGuRows, 1>& w, const uint
 // groups of four 32-column chunks.  The codes stream into LDS a whole 128-byte line
 // per row and load: load i, lane l takes local row 8 i + l / 8, chunk
 // 8 w + ((l % 8) ^ (l / 8)), into slot i*64 + l (the XOR with the row's low bits puts
-// the 8 rows of one chunk that a tile read takes together in distinct LDS banks).  The scale/zero words of the wave's 96 (row, group) pairs
+// the 8 rows of one chunk that a tile read takes together in distinct LDS banks).
+// The scale/zero words of the wave's 96 (row, group) pairs
 // follow in two loads: slot p = 2 r + h holds local row r, group 2 w + h.
 // The same tile layout serves the group's 16 q/k/v rows (one tile, T = 1).
 constexpr int kGuMfmaK = 2048, kGuMfmaRows = 24;
@@ -807,9 +810,10 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   // more than the latency saved.)
   constexpr bool kAhead = BT == 1;
   WRows<NRQ, 1> wq;
-  // At larger batches the QKV rows go through LDS instead (held in registers they
-  // would be spilled): the first rows of each wave's gate/up slots, which are free
-  // from the end of one layer's gate/up product to the next layer's O phase.
+  // The QKV rows go through LDS in the constant-size instantiation (the matrix-core
+  // tile) and at larger batches (held in registers they would be spilled): the first
+  // rows of each wave's gate/up slots, which are free from the end of one layer's
+  // gate/up product to the next layer's O phase.
   uint4* wq_codes = reinterpret_cast<uint4*>(smem + Ld.wgu) + wave * kXGuRows * 64;
   uint32_t* wq_sz = reinterpret_cast<uint32_t*>(smem + Ld.wgu + (size_t)kStepWaves * kXGuRows * 64 * 16) +
                     wave * kXGuRows * 64;
