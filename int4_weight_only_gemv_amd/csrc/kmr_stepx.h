@@ -562,11 +562,13 @@ constexpr int kGuMfmaK = 2048, kGuMfmaRows = 24;
 __host__ __device__ constexpr int gu_zloads(int T) { return (32 * T + 63) / 64; }
 // (I0, I1: the code loads issued, [I0, I1) of the 2 T; Z0, Z1 likewise of the
 // scale/zero loads: a caller may split the stream in parts)
+// (sw: the wave whose column slice is loaded, into that wave's slots codes/szw;
+// by default the calling wave)
 template <int T = 3, int I0 = 0, int I1 = 2 * T, int Z0 = 0, int Z1 = gu_zloads(T)>
 __device__ __forceinline__ void gu_tiles_to_lds(const uint8_t* packed, const uint32_t* sz, int lgG,
                                                 const int (&row)[2 * T], const int (&zrow)[gu_zloads(T)],
-                                                uint4* codes, uint32_t* szw) {
-  const int lane = otid() & 63, wave = otid() >> 6, NG = kGuMfmaK >> lgG;
+                                                uint4* codes, uint32_t* szw, int sw = -1) {
+  const int lane = otid() & 63, wave = sw < 0 ? otid() >> 6 : sw, NG = kGuMfmaK >> lgG;
 #pragma unroll
   for (int i = I0; i < I1; ++i)
     __builtin_amdgcn_global_load_lds(packed + (size_t)row[i] * (kGuMfmaK / 2) + 16 * (8 * wave + ((lane & 7) ^ (lane >> 3))),
@@ -814,9 +816,21 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   // tile) and at larger batches (held in registers they would be spilled): the first
   // rows of each wave's gate/up slots, which are free from the end of one layer's
   // gate/up product to the next layer's O phase.
-  uint4* wq_codes = reinterpret_cast<uint4*>(smem + Ld.wgu) + wave * kXGuRows * 64;
-  uint32_t* wq_sz = reinterpret_cast<uint32_t*>(smem + Ld.wgu + (size_t)kStepWaves * kXGuRows * 64 * 16) +
-                    wave * kXGuRows * 64;
+  // wave w's gate/up (and q/k/v tile) slots in LDS
+  auto slot_codes = [&](int w) { return reinterpret_cast<uint4*>(smem + Ld.wgu) + w * kXGuRows * 64; };
+  auto slot_sz = [&](int w) {
+    return reinterpret_cast<uint32_t*>(smem + Ld.wgu + (size_t)kStepWaves * kXGuRows * 64 * 16) + w * kXGuRows * 64;
+  };
+  uint4* wq_codes = slot_codes(wave);
+  uint32_t* wq_sz = slot_sz(wave);
+  // In the constant-size form a reduce-scatter poll covers B * 8 * kXcds words: at
+  // batch 1 wave 0 polls it.  It requests no weights just ahead of it (its poll would
+  // return only after those loads); wave kStepWaves / 2 requests wave 0's instead.
+  // That wave's own next poll, a gather that gives every wave words (K = 2048),
+  // returns after them, and the gather's closing barrier orders them before any tile
+  // read.  (At batch 4, four polling waves and four proxies measured slower.)
+  const bool xrs_poller = FIXED && BT == 1 && wave == 0;
+  const int xrs_proxy = FIXED && BT == 1 && wave == kStepWaves / 2 ? 0 : -1;
   static_assert(NRQ <= kXGuRows, "the QKV rows fit the gate/up slots");
   // The constant-size instantiation takes the group's 16 q/k/v rows as one
   // matrix-core tile, in the gate/up tile layout (every row valid: 32 groups of 16
@@ -841,8 +855,13 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       zrow[0] = qkv_row_of(lane < 32 ? lane >> 1 : 0);   // (row, group) pair lane < 32
       if constexpr (P == 0)
         gu_tiles_to_lds<1>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, wq_codes, wq_sz);
-      else if constexpr (P == 1)
-        gu_tiles_to_lds<1, 0, 1, 0, 1>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, wq_codes, wq_sz);
+      else if constexpr (P == 1) {
+        // (ahead of the reduce-scatter poll: its polling waves' share through another wave)
+        if (!xrs_poller) gu_tiles_to_lds<1, 0, 1, 0, 1>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, wq_codes, wq_sz);
+        if (xrs_proxy >= 0)
+          gu_tiles_to_lds<1, 0, 1, 0, 1>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, slot_codes(xrs_proxy),
+                                         slot_sz(xrs_proxy), xrs_proxy);
+      }
       else
         gu_tiles_to_lds<1, 1, 2, 0, 0>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, wq_codes, wq_sz);
     } else if constexpr (P != 1) {
@@ -1319,8 +1338,12 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         zrow[u] = grow_of(p < 96 ? p >> 1 : 0);
       }
       // (the first half now, the rest once the reduce-scatter poll is in: a poll
-      // returns only after every load its wave issued before it)
-      gu_tiles_to_lds<3, 0, 3, 0, 1>(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, gu_codes, gu_sz);
+      // returns only after every load its wave issued before it, so the waves that
+      // poll it request theirs through another wave)
+      if (!xrs_poller) gu_tiles_to_lds<3, 0, 3, 0, 1>(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, gu_codes, gu_sz);
+      if (xrs_proxy >= 0)
+        gu_tiles_to_lds<3, 0, 3, 0, 1>(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, slot_codes(xrs_proxy),
+                                       slot_sz(xrs_proxy), xrs_proxy);
     } else {
       wrows_to_lds(Ly.gu_p, Ly.gu_s, H, lgG, grow, gu_codes, gu_sz);
     }
