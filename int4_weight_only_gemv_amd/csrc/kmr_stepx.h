@@ -823,12 +823,14 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
   };
   uint4* wq_codes = slot_codes(wave);
   uint32_t* wq_sz = slot_sz(wave);
-  // In the constant-size form a reduce-scatter poll covers B * 8 * kXcds words: at
-  // batch 1 wave 0 polls it.  It requests no weights just ahead of it (its poll would
-  // return only after those loads); wave kStepWaves / 2 requests wave 0's instead.
-  // That wave's own next poll, a gather that gives every wave words (K = 2048),
-  // returns after them, and the gather's closing barrier orders them before any tile
-  // read.  (At batch 4, four polling waves and four proxies measured slower.)
+  // In the constant-size form every wave polls the reduce-scatters (at batch 1 wave
+  // w takes XCD w's partials of the group's 64 rows), and a poll returns only after
+  // every load its wave issued before it.  At batch 1 wave 0, whose lanes then reduce
+  // and publish the rows, requests no weights just ahead of those polls; wave
+  // kStepWaves / 2 requests wave 0's instead.  That wave's own next poll, a gather
+  // that gives every wave words (K = 2048), returns after them, and the gather's
+  // closing barrier orders them before any tile read.  (At batch 4, waves 0-3 with
+  // waves 4-7 as their proxies measured slower.)
   const bool xrs_poller = FIXED && BT == 1 && wave == 0;
   const int xrs_proxy = FIXED && BT == 1 && wave == kStepWaves / 2 ? 0 : -1;
   static_assert(NRQ <= kXGuRows, "the QKV rows fit the gate/up slots");
