@@ -38,6 +38,10 @@ constexpr uint32_t kStatusTopology = 8u;
 constexpr int kXMaxPerXcd = 64;     // work-groups per XCD
 constexpr int kXSsSlots = kXMaxPerXcd * 2;   // sums-of-squares slots of a staged row (<= 2 per group)
 constexpr int kXGuRows = 6;         // gate/up rows per wave (3 act values)
+// s_sleep(8) rounds (512 clocks each) between a group's q/k/v publish and its early
+// gate/up request when it has no attention item (batch 1): 6 to 10 measured alike
+// at the workload's positions, 4 and 12 measured as no early request at all.
+constexpr int kEarlyGuSleeps = 8;
 
 // Store of a tagged word that only groups of this XCD read.  A work-group-scope
 // store stays in the XCD's L2, where the device-scope polls of the XCD's other
@@ -932,6 +936,29 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
             publish_l(lqkv + (size_t)wave * QX + j * RQ + lane, tag(ph + 1), v * inv, plain);
           }
         }
+        if constexpr (BT == 1) {
+          // A group without an attention item requests its gate/up tiles now, into
+          // slots nothing reads before the gate/up product: the weights then arrive
+          // while the items run, when HBM is otherwise idle, and no later poll of
+          // this group waits behind them.  The wait first lets the item groups' K/V
+          // rows and q/k/v hand-off go ahead of the stream.
+          if (j >= total) {
+            for (int k = 0; k < kEarlyGuSleeps; ++k) __builtin_amdgcn_s_sleep(8);
+            auto grow_e = [&](int r) {   // as grow_of in the gate/up phase
+              const int ar = r < kGuMfmaRows ? r : r - kGuMfmaRows;
+              return x * IX + j * kGuMfmaRows + ar + (r < kGuMfmaRows ? 0 : I);
+            };
+            int trow_e[kXGuRows], zrow_e[2];
+#pragma unroll
+            for (int i = 0; i < kXGuRows; ++i) trow_e[i] = grow_e(8 * i + (lane >> 3));
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int p = 64 * u + lane;
+              zrow_e[u] = grow_e(p < 96 ? p >> 1 : 0);
+            }
+            gu_tiles_to_lds<3>(Ly.gu_p, Ly.gu_s, lgG, trow_e, zrow_e, slot_codes(wave), slot_sz(wave));
+          }
+        }
       } else {
         float out[NR][BT];
         wave_dot_c<BT, NR, 1>(wq, H, B, xs, ChunkSums{sums, H / 4}, out);
@@ -1342,8 +1369,9 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       // (the first half now, the rest once the reduce-scatter poll is in: a poll
       // returns only after every load its wave issued before it, so the waves that
       // poll it request theirs through another wave)
-      if (!xrs_poller) gu_tiles_to_lds<3, 0, 3, 0, 1>(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, gu_codes, gu_sz);
-      if (xrs_proxy >= 0)
+      const bool early = BT == 1 && j >= total;   // (requested after the q/k/v publish)
+      if (!xrs_poller && !early) gu_tiles_to_lds<3, 0, 3, 0, 1>(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, gu_codes, gu_sz);
+      if (xrs_proxy >= 0 && !early)
         gu_tiles_to_lds<3, 0, 3, 0, 1>(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, slot_codes(xrs_proxy),
                                        slot_sz(xrs_proxy), xrs_proxy);
     } else {
@@ -1357,7 +1385,10 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         alive = false;
         break;
       }
-      if constexpr (FIXED) gu_tiles_to_lds<3, 3, 6, 1, 2>(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, gu_codes, gu_sz);
+      if constexpr (FIXED) {
+        if (!(BT == 1 && j >= total))
+          gu_tiles_to_lds<3, 3, 6, 1, 2>(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, gu_codes, gu_sz);
+      }
       publish_staged_x<BT>(sx1, SX, H, B, RPW, j * RPW, xn, hx, g_post, j, tag(ph + 4), plain, a.status);
     }
     KMR_TRACE_MARK(tev + 6);
