@@ -862,7 +862,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       if constexpr (P == 0)
         gu_tiles_to_lds<1>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, wq_codes, wq_sz);
       else if constexpr (P == 1) {
-        // (ahead of the reduce-scatter poll: its polling waves' share through another wave)
+        // (ahead of the reduce-scatter poll: at batch 1 wave 0's share through wave 4)
         if (!xrs_poller) gu_tiles_to_lds<1, 0, 1, 0, 1>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, wq_codes, wq_sz);
         if (xrs_proxy >= 0)
           gu_tiles_to_lds<1, 0, 1, 0, 1>(L2.qkv_p, L2.qkv_s, lgG, trow, zrow, slot_codes(xrs_proxy),
@@ -1367,8 +1367,8 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         zrow[u] = grow_of(p < 96 ? p >> 1 : 0);
       }
       // (the first half now, the rest once the reduce-scatter poll is in: a poll
-      // returns only after every load its wave issued before it, so the waves that
-      // poll it request theirs through another wave)
+      // returns only after every load its wave issued before it; at batch 1 wave 0's
+      // through wave 4, and none here for a group that requested them early)
       const bool early = BT == 1 && j >= total;   // (requested after the q/k/v publish)
       if (!xrs_poller && !early) gu_tiles_to_lds<3, 0, 3, 0, 1>(Ly.gu_p, Ly.gu_s, lgG, trow, zrow, gu_codes, gu_sz);
       if (xrs_proxy >= 0 && !early)
