@@ -61,15 +61,24 @@ def algorithmic_bytes(dims, batch, cache_positions, with_lm=True):
     return total
 
 
+def _strip_comments(src):
+    """C/C++ source without its comments and trailing blanks (string literals
+    with comment markers inside are not expected in these files)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
 def kernel_source_hash():
-    """sha256 over the HIP sources (name + bytes, sorted): identifies the kernel
-    build that a stored counter summary was taken from."""
+    """sha256 over the HIP sources (name + text without comments, sorted):
+    identifies the kernel build that a stored counter summary was taken from, and
+    stays put when only comments change."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".h", ".hip")):
             h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                h.update(_strip_comments(f.read()).encode())
     return h.hexdigest()
 
 
