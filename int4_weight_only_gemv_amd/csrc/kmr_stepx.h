@@ -1070,10 +1070,24 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         };
         KMR_TRACE_MARK(l == 1 ? 59 : 64);
         if (s == ns - 1 && row == 0) {
+          // the new slot's k and v into the cache: nk and nv hold bf16 values as fp32,
+          // so each value's bf16 bits are its high half (two vector LDS reads and one
+          // store per tensor and lane, DPL dims at d0)
           uint16_t* kd = kc + (head_base + c) * D + d0;
           uint16_t* vd = vc + (head_base + c) * D + d0;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) { kd[e] = f32_to_bf16(nk[d0 + e]); vd[e] = f32_to_bf16(nv[d0 + e]); }
+          const float4* nk4 = reinterpret_cast<const float4*>(nk + d0);
+          const float4* nv4 = reinterpret_cast<const float4*>(nv + d0);
+          if constexpr (DPL == 8) {
+            const float4 k0 = nk4[0], k1 = nk4[1], v0 = nv4[0], v1 = nv4[1];
+            *reinterpret_cast<uint4*>(kd) = make_uint4(bf16_pair(k0.x, k0.y), bf16_pair(k0.z, k0.w),
+                                                       bf16_pair(k1.x, k1.y), bf16_pair(k1.z, k1.w));
+            *reinterpret_cast<uint4*>(vd) = make_uint4(bf16_pair(v0.x, v0.y), bf16_pair(v0.z, v0.w),
+                                                       bf16_pair(v1.x, v1.y), bf16_pair(v1.z, v1.w));
+          } else {
+            const float4 k0 = nk4[0], v0 = nv4[0];
+            *reinterpret_cast<uint2*>(kd) = make_uint2(bf16_pair(k0.x, k0.y), bf16_pair(k0.z, k0.w));
+            *reinterpret_cast<uint2*>(vd) = make_uint2(bf16_pair(v0.x, v0.y), bf16_pair(v0.z, v0.w));
+          }
         }
         // The wave's 16 positions p0 + 0..15 on the matrix cores.  Scores S = K Q^T: K rows
         // are the first operand (lane (rr, li) supplies position p0 + li), the second is
