@@ -1206,8 +1206,18 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         for (int i = tid; i < QPG * D; i += kStepThreads) {
           const int h = i / D, d = i - h * D;
           float Os = 0.f;
+          if constexpr (BT == 1) {
+            // (every wave state's value first: one after another they would each wait;
+            // at larger batches the registers measured dearer than the waits)
+            float ow[kStepWaves];
 #pragma unroll
-          for (int wv = 0; wv < kStepWaves; ++wv) Os += s_e[wv * QPG + h] * s_w[(wv * QPG + h) * (D + 2) + d];
+            for (int wv = 0; wv < kStepWaves; ++wv) ow[wv] = s_w[(wv * QPG + h) * (D + 2) + d];
+#pragma unroll
+            for (int wv = 0; wv < kStepWaves; ++wv) Os += s_e[wv * QPG + h] * ow[wv];
+          } else {
+#pragma unroll
+            for (int wv = 0; wv < kStepWaves; ++wv) Os += s_e[wv * QPG + h] * s_w[(wv * QPG + h) * (D + 2) + d];
+          }
           publish_l(pdst + h * (D + 2) + d, tag(ph + 2), Os, plain);
           if (d == 0) {
             publish_l(pdst + h * (D + 2) + D, tag(ph + 2), s_e[kStepWaves * QPG + h], plain);
@@ -1239,6 +1249,10 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
       int maxns = 0;
       for (int b = 0; b < B; ++b) maxns = s_ns[b] > maxns ? s_ns[b] : maxns;
       const int CW = kXMergeChunk * PW, words = B * GPX * CW;
+      // (at batch 1 the row's split count in a register, read once, not once per
+      // poll word)
+      const int ns1 = s_ns[0];
+      auto ns_of = [&](int bb) { return BT == 1 ? ns1 : s_ns[bb]; };
       for (int t0 = 0; t0 < maxns && alive; t0 += kXMergeChunk) {
         constexpr int PG = 8;
         bool ok = true;
@@ -1250,7 +1264,7 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           for (int q = 0; q < PG; ++q) {
             const int i = base + kStepThreads * q + tid;
             const int seg = i / CW, r1 = i - seg * CW, sl = r1 / PW, k = r1 - sl * PW;
-            hv[q] = i < words && t0 + sl < s_ns[seg >> lgGPX];
+            hv[q] = i < words && t0 + sl < ns_of(seg >> lgGPX);
             off[q] = hv[q] ? (uint32_t)((seg * NSX + t0 + sl) * PW + k) : 0u;
           }
           uint32_t spins = 0;
