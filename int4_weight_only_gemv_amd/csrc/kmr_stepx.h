@@ -1179,49 +1179,80 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           }
         }
         __syncthreads();
-        // merge the 8 wave states of each head: the log-sum-exp weights are
-        // computed once per (wave, head), then each output is 8 multiply-adds
-        static_assert(kStepWaves * QPG == 16, "one 16-lane row holds every (wave, head) state");
-        if (wave == 0 && lane < 16) {
-          // lane t = wave * QPG + head: the states of one head sit at lane ^ 2, ^ 4, ^ 8
-          const float mw = s_w[lane * (D + 2) + D], lw = s_w[lane * (D + 2) + D + 1];
-          float Mx = mw;
-          Mx = fmaxf(Mx, dpp<0x4E>(Mx));        // lane ^ 2
-          Mx = fmaxf(Mx, lane_xor4(Mx));        // lane ^ 4
-          Mx = fmaxf(Mx, row16_swap8(Mx));      // lane ^ 8
-          const float e = mw == -INFINITY ? 0.f : exp2_fast(mw - Mx);
-          float Ls = e * lw;
-          Ls += dpp<0x4E>(Ls);
-          Ls += lane_xor4(Ls);
-          Ls += row16_swap8(Ls);
-          s_e[lane] = e;
-          if (lane < QPG) {
-            s_e[kStepWaves * QPG + lane] = Mx;
-            s_e[(kStepWaves + 1) * QPG + lane] = Ls;
-          }
-        }
-        __syncthreads();
-        KMR_TRACE_MARK(l == 1 ? 62 : 64);
+        // Merge the 8 wave states of each head: log-sum-exp weights e = 2^(m - max m),
+        // then each output is 8 multiply-adds in wave order and the sum of the weighted
+        // sums is taken pairwise (products and sums without contraction, so that both
+        // forms below give the same bits).
         uint64_t* pdst = lpart + (((size_t)b * GPX + gl) * NSX + s) * PW;
-        for (int i = tid; i < QPG * D; i += kStepThreads) {
-          const int h = i / D, d = i - h * D;
-          float Os = 0.f;
-          if constexpr (BT == 1) {
-            // (every wave state's value first: one after another they would each wait;
-            // at larger batches the registers measured dearer than the waits)
-            float ow[kStepWaves];
+        if constexpr (BT == 1) {
+          // every publishing thread takes the weights of its head's 8 states itself: no
+          // one-wave step and no second barrier
+          KMR_TRACE_MARK(l == 1 ? 62 : 64);
+          for (int i = tid; i < QPG * D; i += kStepThreads) {
+            const int h = i / D, d = i - h * D;
+            float mw[kStepWaves], lw[kStepWaves], ow[kStepWaves];
 #pragma unroll
-            for (int wv = 0; wv < kStepWaves; ++wv) ow[wv] = s_w[(wv * QPG + h) * (D + 2) + d];
+            for (int wv = 0; wv < kStepWaves; ++wv) {
+              const float* st = s_w + (wv * QPG + h) * (D + 2);
+              ow[wv] = st[d];
+              mw[wv] = st[D];
+              lw[wv] = st[D + 1];
+            }
+            float Mx = mw[0];
 #pragma unroll
-            for (int wv = 0; wv < kStepWaves; ++wv) Os += s_e[wv * QPG + h] * ow[wv];
-          } else {
+            for (int wv = 1; wv < kStepWaves; ++wv) Mx = fmaxf(Mx, mw[wv]);
+            float e[kStepWaves];
 #pragma unroll
-            for (int wv = 0; wv < kStepWaves; ++wv) Os += s_e[wv * QPG + h] * s_w[(wv * QPG + h) * (D + 2) + d];
+            for (int wv = 0; wv < kStepWaves; ++wv) e[wv] = mw[wv] == -INFINITY ? 0.f : exp2_fast(mw[wv] - Mx);
+            float Os = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < kStepWaves; ++wv) Os = __builtin_fmaf(e[wv], ow[wv], Os);
+            publish_l(pdst + h * (D + 2) + d, tag(ph + 2), Os, plain);
+            if (d == 0) {
+#pragma clang fp contract(off)
+              float pl[kStepWaves];
+#pragma unroll
+              for (int wv = 0; wv < kStepWaves; ++wv) pl[wv] = e[wv] * lw[wv];
+              const float Ls = ((pl[0] + pl[1]) + (pl[2] + pl[3])) + ((pl[4] + pl[5]) + (pl[6] + pl[7]));
+              publish_l(pdst + h * (D + 2) + D, tag(ph + 2), Mx, plain);
+              publish_l(pdst + h * (D + 2) + D + 1, tag(ph + 2), Ls, plain);
+            }
           }
-          publish_l(pdst + h * (D + 2) + d, tag(ph + 2), Os, plain);
-          if (d == 0) {
-            publish_l(pdst + h * (D + 2) + D, tag(ph + 2), s_e[kStepWaves * QPG + h], plain);
-            publish_l(pdst + h * (D + 2) + D + 1, tag(ph + 2), s_e[(kStepWaves + 1) * QPG + h], plain);
+        } else {
+          // the weights once per (wave, head) in one wave, through LDS to every thread
+          static_assert(kStepWaves * QPG == 16, "one 16-lane row holds every (wave, head) state");
+          if (wave == 0 && lane < 16) {
+#pragma clang fp contract(off)
+            // lane t = wave * QPG + head: the states of one head sit at lane ^ 2, ^ 4, ^ 8
+            const float mw = s_w[lane * (D + 2) + D], lw = s_w[lane * (D + 2) + D + 1];
+            float Mx = mw;
+            Mx = fmaxf(Mx, dpp<0x4E>(Mx));        // lane ^ 2
+            Mx = fmaxf(Mx, lane_xor4(Mx));        // lane ^ 4
+            Mx = fmaxf(Mx, row16_swap8(Mx));      // lane ^ 8
+            const float e = mw == -INFINITY ? 0.f : exp2_fast(mw - Mx);
+            float Ls = e * lw;
+            Ls += dpp<0x4E>(Ls);
+            Ls += lane_xor4(Ls);
+            Ls += row16_swap8(Ls);
+            s_e[lane] = e;
+            if (lane < QPG) {
+              s_e[kStepWaves * QPG + lane] = Mx;
+              s_e[(kStepWaves + 1) * QPG + lane] = Ls;
+            }
+          }
+          __syncthreads();
+          KMR_TRACE_MARK(l == 1 ? 62 : 64);
+          for (int i = tid; i < QPG * D; i += kStepThreads) {
+            const int h = i / D, d = i - h * D;
+            float Os = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < kStepWaves; ++wv)
+              Os = __builtin_fmaf(s_e[wv * QPG + h], s_w[(wv * QPG + h) * (D + 2) + d], Os);
+            publish_l(pdst + h * (D + 2) + d, tag(ph + 2), Os, plain);
+            if (d == 0) {
+              publish_l(pdst + h * (D + 2) + D, tag(ph + 2), s_e[kStepWaves * QPG + h], plain);
+              publish_l(pdst + h * (D + 2) + D + 1, tag(ph + 2), s_e[(kStepWaves + 1) * QPG + h], plain);
+            }
           }
         }
         __syncthreads();
