@@ -260,9 +260,21 @@ __device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag,
   xn = 0.f;
   if (has_x) {
     float sum = 0.f;
+    if constexpr (BT == 1) {
+      // (the partials and the owned value read first: one after another each read
+      // would be waited for before the next)
+      float pv[kXcds];
 #pragma unroll
-    for (int y = 0; y < kXcds; ++y) sum += buf[(y * B + b) * RPW + r];
-    xn = xown[b * RPW + r] + sum;
+      for (int y = 0; y < kXcds; ++y) pv[y] = buf[y * RPW + r];
+      const float xo = xown[r];
+#pragma unroll
+      for (int y = 0; y < kXcds; ++y) sum += pv[y];
+      xn = xo + sum;
+    } else {
+#pragma unroll
+      for (int y = 0; y < kXcds; ++y) sum += buf[(y * B + b) * RPW + r];
+      xn = xown[b * RPW + r] + sum;
+    }
     xown[b * RPW + r] = xn;
   }
   return true;
