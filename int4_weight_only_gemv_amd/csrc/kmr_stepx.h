@@ -943,8 +943,16 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           const float inv = staged_inv(sums + BT * (H / 4), wave, NSS, H, a.eps);
           if (lane < 16) {
             float v = 0.f;
+            if constexpr (BT == 1) {
+              float pq[kStepWaves];   // (read first, then summed in wave order)
 #pragma unroll
-            for (int w = 0; w < kStepWaves; ++w) v += qpart[(w * BT + wave) * 16 + lane];
+              for (int w = 0; w < kStepWaves; ++w) pq[w] = qpart[w * 16 + lane];
+#pragma unroll
+              for (int w = 0; w < kStepWaves; ++w) v += pq[w];
+            } else {
+#pragma unroll
+              for (int w = 0; w < kStepWaves; ++w) v += qpart[(w * BT + wave) * 16 + lane];
+            }
             publish_l(lqkv + (size_t)wave * QX + j * RQ + lane, tag(ph + 1), v * inv, plain);
           }
         }
@@ -1495,10 +1503,25 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           const bool has = lane < kGuMfmaRows;
           float gt = 0.f, up = 0.f;
           if (has) {
+            if constexpr (BT == 1) {
+              // (every wave's partials read first, then summed in wave order)
+              float pg[kStepWaves], pu[kStepWaves];
 #pragma unroll
-            for (int w = 0; w < kStepWaves; ++w) {
-              gt += part[(w * BT + wave) * 48 + lane];
-              up += part[(w * BT + wave) * 48 + kGuMfmaRows + lane];
+              for (int w = 0; w < kStepWaves; ++w) {
+                pg[w] = part[w * 48 + lane];
+                pu[w] = part[w * 48 + kGuMfmaRows + lane];
+              }
+#pragma unroll
+              for (int w = 0; w < kStepWaves; ++w) {
+                gt += pg[w];
+                up += pu[w];
+              }
+            } else {
+#pragma unroll
+              for (int w = 0; w < kStepWaves; ++w) {
+                gt += part[(w * BT + wave) * 48 + lane];
+                up += part[(w * BT + wave) * 48 + kGuMfmaRows + lane];
+              }
             }
           }
           gt *= inv;
