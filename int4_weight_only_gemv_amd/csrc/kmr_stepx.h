@@ -259,22 +259,16 @@ __device__ __forceinline__ bool reduce_rows(const uint64_t* part, uint32_t ptag,
   has_x = tid < per && row0 + r < H;
   xn = 0.f;
   if (has_x) {
+    // (the partials and the owned value read first: one after another each read
+    // would be waited for before the next)
+    float pv[kXcds];
+#pragma unroll
+    for (int y = 0; y < kXcds; ++y) pv[y] = buf[((BT == 1 ? y : y * B + b)) * RPW + r];
+    const float xo = xown[b * RPW + r];
     float sum = 0.f;
-    if constexpr (BT == 1) {
-      // (the partials and the owned value read first: one after another each read
-      // would be waited for before the next)
-      float pv[kXcds];
 #pragma unroll
-      for (int y = 0; y < kXcds; ++y) pv[y] = buf[y * RPW + r];
-      const float xo = xown[r];
-#pragma unroll
-      for (int y = 0; y < kXcds; ++y) sum += pv[y];
-      xn = xo + sum;
-    } else {
-#pragma unroll
-      for (int y = 0; y < kXcds; ++y) sum += buf[(y * B + b) * RPW + r];
-      xn = xown[b * RPW + r] + sum;
-    }
+    for (int y = 0; y < kXcds; ++y) sum += pv[y];
+    xn = xo + sum;
     xown[b * RPW + r] = xn;
   }
   return true;
@@ -942,17 +936,11 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
         if (wave < B) {
           const float inv = staged_inv(sums + BT * (H / 4), wave, NSS, H, a.eps);
           if (lane < 16) {
-            float v = 0.f;
-            if constexpr (BT == 1) {
-              float pq[kStepWaves];   // (read first, then summed in wave order)
+            float v = 0.f, pq[kStepWaves];   // (read first, then summed in wave order)
 #pragma unroll
-              for (int w = 0; w < kStepWaves; ++w) pq[w] = qpart[w * 16 + lane];
+            for (int w = 0; w < kStepWaves; ++w) pq[w] = qpart[(w * BT + wave) * 16 + lane];
 #pragma unroll
-              for (int w = 0; w < kStepWaves; ++w) v += pq[w];
-            } else {
-#pragma unroll
-              for (int w = 0; w < kStepWaves; ++w) v += qpart[(w * BT + wave) * 16 + lane];
-            }
+            for (int w = 0; w < kStepWaves; ++w) v += pq[w];
             publish_l(lqkv + (size_t)wave * QX + j * RQ + lane, tag(ph + 1), v * inv, plain);
           }
         }
@@ -1503,25 +1491,17 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           const bool has = lane < kGuMfmaRows;
           float gt = 0.f, up = 0.f;
           if (has) {
-            if constexpr (BT == 1) {
-              // (every wave's partials read first, then summed in wave order)
-              float pg[kStepWaves], pu[kStepWaves];
+            // (every wave's partials read first, then summed in wave order)
+            float pg[kStepWaves], pu[kStepWaves];
 #pragma unroll
-              for (int w = 0; w < kStepWaves; ++w) {
-                pg[w] = part[w * 48 + lane];
-                pu[w] = part[w * 48 + kGuMfmaRows + lane];
-              }
+            for (int w = 0; w < kStepWaves; ++w) {
+              pg[w] = part[(w * BT + wave) * 48 + lane];
+              pu[w] = part[(w * BT + wave) * 48 + kGuMfmaRows + lane];
+            }
 #pragma unroll
-              for (int w = 0; w < kStepWaves; ++w) {
-                gt += pg[w];
-                up += pu[w];
-              }
-            } else {
-#pragma unroll
-              for (int w = 0; w < kStepWaves; ++w) {
-                gt += part[(w * BT + wave) * 48 + lane];
-                up += part[(w * BT + wave) * 48 + kGuMfmaRows + lane];
-              }
+            for (int w = 0; w < kStepWaves; ++w) {
+              gt += pg[w];
+              up += pu[w];
             }
           }
           gt *= inv;
