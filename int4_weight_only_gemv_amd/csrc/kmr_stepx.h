@@ -1252,10 +1252,11 @@ __global__ __launch_bounds__(kStepThreads) void k_stepx(const StepArgs a) {
           KMR_TRACE_MARK(l == 1 ? 62 : 64);
           for (int i = tid; i < QPG * D; i += kStepThreads) {
             const int h = i / D, d = i - h * D;
-            float Os = 0.f;
+            float Os = 0.f, ow[kStepWaves];
 #pragma unroll
-            for (int wv = 0; wv < kStepWaves; ++wv)
-              Os = __builtin_fmaf(s_e[wv * QPG + h], s_w[(wv * QPG + h) * (D + 2) + d], Os);
+            for (int wv = 0; wv < kStepWaves; ++wv) ow[wv] = s_w[(wv * QPG + h) * (D + 2) + d];
+#pragma unroll
+            for (int wv = 0; wv < kStepWaves; ++wv) Os = __builtin_fmaf(s_e[wv * QPG + h], ow[wv], Os);
             publish_l(pdst + h * (D + 2) + d, tag(ph + 2), Os, plain);
             if (d == 0) {
               publish_l(pdst + h * (D + 2) + D, tag(ph + 2), s_e[kStepWaves * QPG + h], plain);
